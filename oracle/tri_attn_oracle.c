@@ -1,0 +1,181 @@
+/*
+ * oracle/tri_attn_oracle.c -- THE ORACLE: a plain, slow, fp64 CPU reference for
+ * pair-biased triangle attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's
+ * CPU-baseline leg may load or run this code.  It shares nothing with the HIP path
+ * (no kernels, headers, helpers, tables or constants) and the product never calls it.
+ *
+ * What it computes (per batch b, query row i, query column j and head h):
+ *
+ *   s_k = (1/sqrt(D)) * sum_d q[b,i,j,h,d] * k[b,i,k,h,d] + bias[b,h,j,k] + mask[b,k]
+ *   out[b,i,j,h,:] = sum_k softmax_k(s)_k * v[b,i,k,h,:]
+ *
+ * Sources:
+ *   - "Fold-CP: A Context Parallelism Framework for Biomolecular Modeling", Table 1
+ *     (triangle attention, serial time B*H*N^3*D and space B*H*N^2*D: N^2 query
+ *     positions (i,j) against N keys per head, score tensor never stored) and
+ *     Figure 2(a) (the bias is the "triangular" one, indexed by the third edge (j,k)
+ *     and so shared by every row i; keys, values and bias travel round a ring and
+ *     the partial results are joined by a tiled-softmax merge).
+ *   - Table 1's caption: every ring pattern takes P steps; each step contributes one
+ *     contiguous key tile, so the key axis is cut into T tiles processed in order.
+ *   - The merge is the online-normaliser rule of "Online normalizer calculation for
+ *     softmax" (listed among Design-CP's prior work): a tile's state (m_t, l_t, a_t)
+ *     joins the running state (m, l, a) as
+ *        M = max(m, m_t),  l = e^(m-M) l + e^(m_t-M) l_t,  a = e^(m-M) a + e^(m_t-M) a_t.
+ * Readings where the pages are silent: 1/sqrt(D) scales q.k only; the mask is an
+ * additive [B,N] term over the key index; a tile whose keys are all -inf is the
+ * identity of the merge; a row with no finite score gives out = 0 and lse = -inf.
+ *
+ * All arithmetic is IEEE double, libm exp/log/sqrt, no fast-math and no contraction
+ * (built with -ffp-contract=off).  Inputs are widened exactly: binary32 as is,
+ * bfloat16 as the upper half of a binary32.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_DTYPE_FP32 0
+#define ORACLE_DTYPE_BF16 1
+
+#define ORACLE_OK 0
+#define ORACLE_ERR_ARG -1
+#define ORACLE_ERR_NOMEM -2
+
+/* Exact widening of one stored element to double. */
+static double widen(const void *base, int64_t idx, int dtype)
+{
+    if (dtype == ORACLE_DTYPE_FP32)
+        return (double)((const float *)base)[idx];
+    uint32_t bits = (uint32_t)((const uint16_t *)base)[idx] << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+/* Near-equal contiguous key tiles: the first N mod T tiles hold ceil(N/T) keys,
+ * the rest floor(N/T).  starts[] receives T+1 entries (starts[T] == N). */
+void oracle_even_tiles(int64_t N, int64_t T, int64_t *starts)
+{
+    for (int64_t t = 0; t <= T; ++t)
+        starts[t] = t * (N / T) + (t < N % T ? t : N % T);
+}
+
+/*
+ * q, k, v:   [B, I, N, H, D] of dtype;  bias: [B, H, N, N] of dtype;
+ * mask:      [B, N] binary32 additive, or NULL;
+ * tile_start: T+1 increasing key offsets, tile_start[0] = 0, tile_start[T] = N;
+ * first_tile: the ring step that runs first (tiles taken first_tile, first_tile+1, ... mod T);
+ * rows:      n_rows flat row indices (b*I + i)*N + j, or NULL for all B*I*N rows in order;
+ * out:       [n_rows, H, D] doubles;  lse: [n_rows, H] doubles (log-sum-exp of the scores), or NULL.
+ * Returns 0, or a negative code for bad arguments / no memory.
+ */
+int oracle_tri_attn(const void *q, const void *k, const void *v, const void *bias,
+                    const float *mask, int dtype,
+                    int64_t B, int64_t H, int64_t I, int64_t N, int64_t D,
+                    const int64_t *tile_start, int64_t T, int64_t first_tile,
+                    const int64_t *rows, int64_t n_rows,
+                    double *out, double *lse)
+{
+    if (!q || !k || !v || !bias || !out || !tile_start)
+        return ORACLE_ERR_ARG;
+    if (B < 1 || H < 1 || I < 1 || N < 1 || D < 1 || I > N || T < 1 || T > N)
+        return ORACLE_ERR_ARG;
+    if (dtype != ORACLE_DTYPE_FP32 && dtype != ORACLE_DTYPE_BF16)
+        return ORACLE_ERR_ARG;
+    if (tile_start[0] != 0 || tile_start[T] != N || first_tile < 0 || first_tile >= T)
+        return ORACLE_ERR_ARG;
+    int64_t widest = 0;
+    for (int64_t t = 0; t < T; ++t) {
+        if (tile_start[t + 1] <= tile_start[t])
+            return ORACLE_ERR_ARG;
+        if (tile_start[t + 1] - tile_start[t] > widest)
+            widest = tile_start[t + 1] - tile_start[t];
+    }
+    const int64_t total = rows ? n_rows : B * I * N;
+    if (rows) {
+        for (int64_t r = 0; r < n_rows; ++r)
+            if (rows[r] < 0 || rows[r] >= B * I * N)
+                return ORACLE_ERR_ARG;
+    }
+    const double inv_sqrt_d = 1.0 / sqrt((double)D);
+    int failed = 0;
+
+#pragma omp parallel
+    {
+        double *s = (double *)malloc((size_t)widest * sizeof(double));
+        double *a = (double *)malloc((size_t)D * sizeof(double));
+        double *a_t = (double *)malloc((size_t)D * sizeof(double));
+        const int ok = s && a && a_t;
+        if (!ok) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(dynamic, 8)
+        for (int64_t r = 0; r < total; ++r) {
+            if (!ok)
+                continue;
+            const int64_t flat = rows ? rows[r] : r;
+            const int64_t j = flat % N;
+            const int64_t bi = flat / N;        /* b*I + i */
+            const int64_t b = bi / I;
+            for (int64_t h = 0; h < H; ++h) {
+                const int64_t q_off = ((bi * N + j) * H + h) * D;
+                const int64_t bias_row = ((b * H + h) * N + j) * N;
+                double m = -INFINITY, l = 0.0;
+                for (int64_t d = 0; d < D; ++d)
+                    a[d] = 0.0;
+                for (int64_t step = 0; step < T; ++step) {
+                    const int64_t t = (first_tile + step) % T;
+                    const int64_t k0 = tile_start[t], k1 = tile_start[t + 1];
+                    /* scores of this key tile and their maximum */
+                    double m_t = -INFINITY;
+                    for (int64_t kk = k0; kk < k1; ++kk) {
+                        const int64_t k_off = ((bi * N + kk) * H + h) * D;
+                        double dot = 0.0;
+                        for (int64_t d = 0; d < D; ++d)
+                            dot += widen(q, q_off + d, dtype) * widen(k, k_off + d, dtype);
+                        double sc = dot * inv_sqrt_d + widen(bias, bias_row + kk, dtype);
+                        if (mask)
+                            sc += (double)mask[b * N + kk];
+                        s[kk - k0] = sc;
+                        if (sc > m_t)
+                            m_t = sc;
+                    }
+                    if (m_t == -INFINITY)
+                        continue;   /* every key of the tile dropped: identity of the merge */
+                    /* the tile's own softmax state relative to its maximum */
+                    double l_t = 0.0;
+                    for (int64_t d = 0; d < D; ++d)
+                        a_t[d] = 0.0;
+                    for (int64_t kk = k0; kk < k1; ++kk) {
+                        const double w = exp(s[kk - k0] - m_t);
+                        const int64_t v_off = ((bi * N + kk) * H + h) * D;
+                        l_t += w;
+                        for (int64_t d = 0; d < D; ++d)
+                            a_t[d] += w * widen(v, v_off + d, dtype);
+                    }
+                    /* merge the tile into the running state */
+                    const double M = m > m_t ? m : m_t;
+                    const double alpha = (m == -INFINITY) ? 0.0 : exp(m - M);
+                    const double beta = exp(m_t - M);
+                    l = alpha * l + beta * l_t;
+                    for (int64_t d = 0; d < D; ++d)
+                        a[d] = alpha * a[d] + beta * a_t[d];
+                    m = M;
+                }
+                double *o = out + (r * H + h) * D;
+                for (int64_t d = 0; d < D; ++d)
+                    o[d] = (l > 0.0) ? a[d] / l : 0.0;
+                if (lse)
+                    lse[r * H + h] = (l > 0.0) ? m + log(l) : -INFINITY;
+            }
+        }
+        free(s);
+        free(a);
+        free(a_t);
+    }
+    return failed ? ORACLE_ERR_NOMEM : ORACLE_OK;
+}

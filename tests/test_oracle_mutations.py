@@ -1,0 +1,122 @@
+"""Planted mistakes: each plausible slip in the oracle must fail at least one pin.
+
+A copy of the oracle's C source is edited (one textual mutation per case), built
+with gcc into a temporary directory, and run against the same checks that pin the
+real oracle (library SDPA special case, ring-step invariance, huge bias shifts,
+uniform and single-key closed forms).  The real oracle passes all of them; every
+mutant must fail at least one.  Everything runs on the CPU.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from tests.test_oracle_pins import rand_case, sdpa_reference
+
+MUTATIONS = {
+    "drop_1_over_sqrt_d": ("dot * inv_sqrt_d", "dot"),
+    "scale_bias_too": ("dot * inv_sqrt_d + widen(bias, bias_row + kk, dtype)",
+                       "(dot + widen(bias, bias_row + kk, dtype)) * inv_sqrt_d"),
+    "bias_transposed": ("const int64_t bias_row = ((b * H + h) * N + j) * N;",
+                        "const int64_t bias_row = ((b * H + h) * N) * N + j;"),
+    "bias_column_stride": ("widen(bias, bias_row + kk, dtype)", "widen(bias, bias_row - j * N + kk * N, dtype)"),
+    "mask_ignored": ("sc += (double)mask[b * N + kk];", "sc += 0.0;"),
+    "keys_from_row_j": ("const int64_t k_off = ((bi * N + kk) * H + h) * D;",
+                        "const int64_t k_off = (((b * I + kk % I) * N + (bi % I)) * H + h) * D;"),
+    "values_wrong_head": ("const int64_t v_off = ((bi * N + kk) * H + h) * D;",
+                          "const int64_t v_off = ((bi * N + kk) * H + (h + 1) % H) * D;"),
+    "merge_alpha_dropped": ("l = alpha * l + beta * l_t;", "l = l + beta * l_t;"),
+    "merge_beta_dropped": ("a[d] = alpha * a[d] + beta * a_t[d];", "a[d] = alpha * a[d] + a_t[d];"),
+    "merge_last_tile_wins": ("l = alpha * l + beta * l_t;", "l = l_t;"),
+    "no_max_subtraction": ("const double w = exp(s[kk - k0] - m_t);", "const double w = exp(s[kk - k0]);"),
+    "no_normalisation": ("o[d] = (l > 0.0) ? a[d] / l : 0.0;", "o[d] = a[d];"),
+    "masked_tile_not_skipped": ("if (m_t == -INFINITY)\n                        continue;",
+                                "if (0)\n                        continue;"),
+    "lse_without_max": ("lse[r * H + h] = (l > 0.0) ? m + log(l) : -INFINITY;",
+                        "lse[r * H + h] = (l > 0.0) ? log(l) : -INFINITY;"),
+    "bf16_low_half": ("uint32_t bits = (uint32_t)((const uint16_t *)base)[idx] << 16;",
+                      "uint32_t bits = (uint32_t)((const uint16_t *)base)[idx];"),
+    "dot_skips_last_d": ("for (int64_t d = 0; d < D; ++d)\n                            dot +=",
+                         "for (int64_t d = 0; d + 1 < D; ++d)\n                            dot +="),
+}
+
+
+def battery(lib_path) -> list[str]:
+    """Run the pins against the oracle at lib_path; return the names of those that fail."""
+    failed = []
+    run = lambda *a, **kw: oracle.tri_attn(*a, lib_path=lib_path, **kw)
+
+    def check(name, fn):
+        try:
+            fn()
+        except (AssertionError, ValueError, FloatingPointError):
+            failed.append(name)
+
+    rng = np.random.default_rng(21)
+    q, k, v, bias, mask = rand_case(rng, B=2, I=4, N=23, H=3, D=8, masked=(0, 5, 22), sigma_b=2.0)
+
+    def sdpa():
+        for T in (1, 5):
+            out, _ = run(q, k, v, bias, mask, n_key_tiles=T)
+            np.testing.assert_allclose(out, sdpa_reference(q, k, v, bias, mask), rtol=0, atol=1e-12)
+
+    def tiles():
+        base, base_lse = run(q, k, v, bias, mask, n_key_tiles=1)
+        for T in (2, 3, 7, 23):
+            for first in (0, T - 1):
+                out, lse = run(q, k, v, bias, mask, n_key_tiles=T, first_tile=first)
+                np.testing.assert_allclose(out, base, rtol=0, atol=1e-12)
+                np.testing.assert_allclose(lse, base_lse, rtol=0, atol=1e-12)
+
+    def shifts():
+        b = np.round(bias * 256) / 256
+        base, base_lse = run(q, k, v, b, mask, n_key_tiles=3)
+        out, lse = run(q, k, v, b + np.float32(800.0), mask, n_key_tiles=3)
+        assert np.all(np.isfinite(out))
+        np.testing.assert_allclose(out, base, rtol=0, atol=1e-10)
+        np.testing.assert_allclose(lse, base_lse + 800.0, rtol=0, atol=1e-10)
+
+    def closed_forms():
+        z = np.zeros_like(q)
+        zb = np.zeros_like(bias)
+        out, lse = run(z, z, v, zb, mask, n_key_tiles=4)
+        keep = mask[0] == 0
+        mean = v.astype(np.float64)[:, :, keep].mean(axis=2, keepdims=True)
+        np.testing.assert_allclose(out, np.broadcast_to(mean, out.shape), rtol=0, atol=1e-13)
+        np.testing.assert_allclose(lse, math.log(keep.sum()), rtol=0, atol=1e-13)
+        one = np.full_like(mask, -np.inf)
+        one[:, 0] = 0.0                              # only the first key survives
+        out, _ = run(q, k, v, bias, one, n_key_tiles=3)
+        np.testing.assert_array_equal(out, np.broadcast_to(v[:, :, :1].astype(np.float64), out.shape))
+
+    def bf16():
+        from workloads import bf16_bits_to_f32, f32_to_bf16_bits
+        qb, kb, vb, bb = (f32_to_bf16_bits(x) for x in (q, k, v, bias))
+        out, _ = run(qb, kb, vb, bb, mask, n_key_tiles=2)
+        ref = sdpa_reference(bf16_bits_to_f32(qb), bf16_bits_to_f32(kb), bf16_bits_to_f32(vb),
+                             bf16_bits_to_f32(bb), mask)
+        np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+
+    with np.errstate(all="ignore"):
+        for name, fn in [("sdpa", sdpa), ("tiles", tiles), ("shifts", shifts),
+                         ("closed_forms", closed_forms), ("bf16", bf16)]:
+            check(name, fn)
+    return failed
+
+
+def test_real_oracle_passes_battery(oracle_mod):
+    assert battery(oracle.load.__defaults__[0]) == []
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutant_is_caught(tmp_path, name):
+    old, new = MUTATIONS[name]
+    src = open(oracle.SOURCE).read()
+    assert src.count(old) == 1, f"mutation anchor for {name} not unique in the oracle source"
+    mutant_src = tmp_path / "mutant.c"
+    mutant_src.write_text(src.replace(old, new))
+    lib = oracle.build(force=True, source=str(mutant_src), target=str(tmp_path / "libmutant.so"))
+    failed = battery(lib)
+    assert failed, f"planted mistake '{name}' passed every pin"
