@@ -1,0 +1,117 @@
+/*
+ * tri_attn.h -- C ABI of the MI355X (gfx950) pair-biased triangle-attention library
+ * (libtri_attn.so).
+ *
+ * The operation (starting-node triangle attention; "Fold-CP: A Context Parallelism
+ * Framework for Biomolecular Modeling", Table 1 row "Triangle Attention", and
+ * Figure 2(a)): for every batch b, query row i, query column j and head h,
+ *
+ *     s_k               = q[b,i,j,h,:] . k[b,i,k,h,:] / sqrt(D) + bias[b,h,j,k] + mask[b,k]
+ *     out[b,i,j,h,:]    = sum_k softmax_k(s)_k * v[b,i,k,h,:]
+ *
+ * The bias is the "triangular" one: indexed by the third edge (j,k), it is shared by
+ * every row i.  The key axis is cut into n_key_tiles contiguous tiles -- one per ring
+ * step of the context-parallel schedule (Table 1's caption: every ring pattern takes
+ * P steps) -- and the tiles are joined, in ascending order, by the tiled online-softmax
+ * merge (running maximum, normaliser and accumulator; Figure 2(a) and (c)).  Tile t
+ * holds keys [t*(N/T) + min(t, N%T), (t+1)*(N/T) + min(t+1, N%T)): the first N mod T
+ * tiles take ceil(N/T) keys, the rest floor(N/T).  The tiling changes only rounding.
+ *
+ * Layouts: every tensor is dense and C-contiguous, elements as listed (last fastest):
+ *     q, k, v   [B, I, N, H, D]   dtype (see tri_attn_dtype)
+ *     bias      [B, H, N, N]      dtype, k innermost
+ *     mask      [B, N]            binary32, additive over the key index (0 keeps a key,
+ *                                 -inf drops it); may be NULL (no mask)
+ *     out       [B, I, N, H, D]   binary32 for both dtypes
+ * I is the number of query rows held by this call (I == N in tri_attn_fwd; 1 <= I <= N
+ * in tri_attn_fwd_rows, which serves one rank's row share: rows i in [0, I) of q, k, v,
+ * with the full j and k axes and the full bias).
+ *
+ * Results: a row whose keys are all -inf yields out = 0 (never NaN).  The bf16 path
+ * computes q.k and P.V on bf16 matrix cores with fp32 accumulation; softmax statistics
+ * are fp32 and the probabilities are rounded to bf16 (nearest even) only as the P.V
+ * operand.  The fp32 path computes in fp32 throughout.
+ *
+ * Ownership and memory: every pointer is a device pointer owned by the caller; the
+ * library keeps none of them after returning and allocates no device memory.  q, k, v,
+ * bias and mask are only read and may alias one another; out must not overlap any
+ * input.  q, k, v, bias and out must be 16-byte aligned, mask 4-byte aligned.
+ *
+ * Streams: calls only enqueue work on `stream` (a hipStream_t; NULL is the null
+ * stream) and return without synchronising.  A kernel fault surfaces at the caller's
+ * next synchronisation on that stream.
+ *
+ * Errors: every entry point returns a tri_attn_status and never throws, aborts or
+ * prints.  Arguments are checked in this order, before any device work: NULL
+ * pointers; sizes (all >= 1, I <= N, element counts fit int64); dtype; head size
+ * (the bf16 path needs D == 32, the fp32 path D <= 64; D <= 64 for bf16 on the
+ * general path); n_key_tiles in [1, N]; alignment; out overlapping an input.  A failed
+ * launch returns TRI_ATTN_ERR_HIP and records the HIP error code for
+ * tri_attn_last_hip_error() (per calling thread).
+ */
+#ifndef TRI_ATTN_H
+#define TRI_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element type of q, k, v and bias */
+typedef enum {
+    TRI_ATTN_FP32 = 0,   /* IEEE binary32 */
+    TRI_ATTN_BF16 = 1    /* bfloat16 (upper half of a binary32) */
+} tri_attn_dtype;
+
+typedef enum {
+    TRI_ATTN_OK = 0,
+    TRI_ATTN_ERR_NULL = -1,         /* a required pointer is NULL */
+    TRI_ATTN_ERR_SHAPE = -2,        /* a size < 1, I > N, or a size overflows int64 */
+    TRI_ATTN_ERR_DTYPE = -3,        /* dtype is not a tri_attn_dtype */
+    TRI_ATTN_ERR_UNSUPPORTED = -4,  /* head size D not served (D > 64) */
+    TRI_ATTN_ERR_ALIGN = -5,        /* a pointer is not aligned as required */
+    TRI_ATTN_ERR_TILES = -6,        /* n_key_tiles outside [1, N] */
+    TRI_ATTN_ERR_HIP = -7,          /* the HIP runtime refused the launch */
+    TRI_ATTN_ERR_ALIAS = -8         /* out overlaps an input */
+} tri_attn_status;
+
+/*
+ * Triangle attention over all N query rows (I == N).
+ *   q, k, v   [B, N, N, H, D] device, dtype      bias [B, H, N, N] device, dtype
+ *   mask      [B, N] device binary32 or NULL      out  [B, N, N, H, D] device binary32
+ *   n_key_tiles  number of ring-step key tiles, 1 <= n_key_tiles <= N
+ *   dtype        a tri_attn_dtype
+ *   stream       hipStream_t to enqueue on (NULL: null stream)
+ * Returns TRI_ATTN_OK or a negative tri_attn_status.
+ */
+int tri_attn_fwd(const void *q, const void *k, const void *v, const void *bias,
+                 const float *mask, float *out,
+                 int64_t B, int64_t H, int64_t N, int64_t D,
+                 int32_t n_key_tiles, int32_t dtype, void *stream);
+
+/*
+ * The same operation for one rank's share of query rows: q, k, v and out hold rows
+ * i in [0, I) ([B, I, N, H, D]); bias and mask keep their full [B, H, N, N] / [B, N]
+ * shapes ("Design-CP: Context Parallelism for Design of Protein Nanoparticles",
+ * abstract: 1D row-sharding of the pair representation).  1 <= I <= N.
+ */
+int tri_attn_fwd_rows(const void *q, const void *k, const void *v, const void *bias,
+                      const float *mask, float *out,
+                      int64_t B, int64_t H, int64_t I, int64_t N, int64_t D,
+                      int32_t n_key_tiles, int32_t dtype, void *stream);
+
+/* Static, NUL-terminated description of a tri_attn_status (unknown codes included). */
+const char *tri_attn_status_string(int status);
+
+/* HIP error code (hipError_t value) of this thread's last TRI_ATTN_ERR_HIP; 0 if none. */
+int tri_attn_last_hip_error(void);
+
+/* Library ABI version: major * 10000 + minor * 100 + patch. */
+int tri_attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TRI_ATTN_H */

@@ -1,0 +1,140 @@
+"""Pair-biased triangle attention on AMD MI355X (gfx950).
+
+Thin Python binding of ``libtri_attn.so`` (C ABI in ``include/tri_attn.h``).  Every
+step of the computation runs in the library's HIP kernels; this module only checks and
+marshals torch device tensors (torch provides device memory and streams) and raises
+when the library is missing -- there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libtri_attn.so")
+
+# tri_attn_dtype
+TRI_ATTN_FP32, TRI_ATTN_BF16 = 0, 1
+# tri_attn_status
+STATUS = {
+    0: "TRI_ATTN_OK", -1: "TRI_ATTN_ERR_NULL", -2: "TRI_ATTN_ERR_SHAPE", -3: "TRI_ATTN_ERR_DTYPE",
+    -4: "TRI_ATTN_ERR_UNSUPPORTED", -5: "TRI_ATTN_ERR_ALIGN", -6: "TRI_ATTN_ERR_TILES",
+    -7: "TRI_ATTN_ERR_HIP", -8: "TRI_ATTN_ERR_ALIAS",
+}
+EXPORTS = ("tri_attn_fwd", "tri_attn_fwd_rows", "tri_attn_status_string",
+           "tri_attn_last_hip_error", "tri_attn_version")
+
+
+class TriAttnError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libtri_attn.so (built by pair_biased_triangle_amd.build); raise if it is absent."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise ImportError(f"{path} is missing: build it with `python -m pair_biased_triangle_amd.build`")
+        L = ctypes.CDLL(path)
+        vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+        L.tri_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, vp]
+        L.tri_attn_fwd.restype = ctypes.c_int
+        L.tri_attn_fwd_rows.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, i32, vp]
+        L.tri_attn_fwd_rows.restype = ctypes.c_int
+        L.tri_attn_status_string.argtypes = [ctypes.c_int]
+        L.tri_attn_status_string.restype = ctypes.c_char_p
+        L.tri_attn_last_hip_error.argtypes = []
+        L.tri_attn_last_hip_error.restype = ctypes.c_int
+        L.tri_attn_version.argtypes = []
+        L.tri_attn_version.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return load_library().tri_attn_status_string(status).decode()
+
+
+def _check(rc: int):
+    if rc != 0:
+        msg = status_string(rc)
+        if rc == -7:
+            msg += f" (hipError {load_library().tri_attn_last_hip_error()})"
+        raise TriAttnError(rc, msg)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return TRI_ATTN_BF16
+    if t.dtype == torch.float32:
+        return TRI_ATTN_FP32
+    raise TypeError(f"q, k, v and bias must be bfloat16 or float32, got {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_handle(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _validate(q, k, v, bias, mask, out):
+    import torch
+    dt = _dtype_code(q)
+    for name, t in (("q", q), ("k", k), ("v", v), ("bias", bias)):
+        if t.dtype != q.dtype:
+            raise TypeError(f"{name} has dtype {t.dtype}, q has {q.dtype}")
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if q.dim() != 5 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share one [B, I, N, H, D] shape")
+    B, I, N, H, D = q.shape
+    if tuple(bias.shape) != (B, H, N, N):
+        raise ValueError(f"bias must be [B, H, N, N] = {(B, H, N, N)}, got {tuple(bias.shape)}")
+    if mask is not None:
+        if (mask.dtype != torch.float32 or tuple(mask.shape) != (B, N) or not mask.is_cuda
+                or not mask.is_contiguous()):
+            raise ValueError("mask must be a contiguous float32 device tensor of shape [B, N]")
+    if out is None:
+        out = torch.empty((B, I, N, H, D), dtype=torch.float32, device=q.device)
+    elif out.dtype != torch.float32 or tuple(out.shape) != (B, I, N, H, D) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 tensor shaped like q")
+    return dt, out
+
+
+def tri_attn_fwd_rows(q, k, v, bias, mask=None, *, n_key_tiles: int = 1, out=None, stream=None):
+    """Triangle attention for the query rows i held in q, k, v (one rank's row share).
+
+    q, k, v: [B, I, N, H, D] (bfloat16 or float32, device, contiguous); bias: [B, H, N, N]
+    of the same dtype; mask: [B, N] float32 additive or None.  Returns out [B, I, N, H, D]
+    float32 (written into ``out`` when given).  Enqueued on ``stream`` (default: torch's
+    current stream); nothing is synchronised.  Calls the C entry point tri_attn_fwd_rows.
+    """
+    L = load_library()
+    dt, out = _validate(q, k, v, bias, mask, out)
+    B, I, N, H, D = q.shape
+    _check(L.tri_attn_fwd_rows(_ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(mask), _ptr(out),
+                               B, H, I, N, D, int(n_key_tiles), dt, _stream_handle(stream)))
+    return out
+
+
+def tri_attn_fwd(q, k, v, bias, mask=None, *, n_key_tiles: int = 1, out=None, stream=None):
+    """Triangle attention over all N query rows: q, k, v are [B, N, N, H, D].  Calls the C
+    entry point tri_attn_fwd; otherwise as tri_attn_fwd_rows."""
+    L = load_library()
+    if q.dim() != 5 or q.shape[1] != q.shape[2]:
+        raise ValueError("tri_attn_fwd needs q of shape [B, N, N, H, D]; use tri_attn_fwd_rows for a row share")
+    dt, out = _validate(q, k, v, bias, mask, out)
+    B, _, N, H, D = q.shape
+    _check(L.tri_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(mask), _ptr(out),
+                          B, H, N, D, int(n_key_tiles), dt, _stream_handle(stream)))
+    return out

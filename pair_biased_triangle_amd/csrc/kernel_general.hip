@@ -1,0 +1,130 @@
+// Plain fp32 triangle-attention kernel for any head size D <= 64 and fp32 or bf16 inputs.
+//
+// One workgroup covers 64 query columns j of one (b, i, h); each thread owns one query
+// and keeps its q vector, running maximum, normaliser and fp32 accumulator in registers
+// (online softmax over key blocks; "Fold-CP", Figure 2(a): tiled-softmax merge).  Key
+// blocks of 32 never straddle a ring-step tile, so each tile is folded into the running
+// state exactly as one ring step would be.  K, V and the bias block (with the additive
+// key mask folded in) are staged through LDS.
+#include "launch.h"
+
+#include <cmath>
+
+namespace tri_attn {
+namespace {
+
+constexpr int GJ = 64;  // queries per workgroup, one per thread
+constexpr int GK = 32;  // keys per block
+
+template <bool BF16>
+__device__ __forceinline__ float load_elem(const void* base, int64_t idx) {
+    if constexpr (BF16) {
+        const uint32_t u = static_cast<uint32_t>(static_cast<const uint16_t*>(base)[idx]) << 16;
+        return __uint_as_float(u);
+    } else {
+        return static_cast<const float*>(base)[idx];
+    }
+}
+
+template <bool BF16, int DP>
+__global__ void __launch_bounds__(GJ) general_kernel(Problem p) {
+    const int64_t N = p.N, H = p.H, D = p.D, I = p.I;
+    const int64_t i = blockIdx.y;
+    const int64_t b = blockIdx.z / H, h = blockIdx.z % H;
+    const int64_t j0 = static_cast<int64_t>(blockIdx.x) * GJ;
+    const int tid = threadIdx.x;
+    const int64_t j = j0 + tid;
+    const int64_t row = (b * I + i) * N;  // index of (b, i, j=0) in the [B, I, N] grid
+
+    __shared__ float Ks[GK][DP + 1];
+    __shared__ float Vs[GK][DP + 1];
+    __shared__ float Bs[GJ][GK + 1];
+
+    float q[DP], acc[DP];
+#pragma unroll
+    for (int d = 0; d < DP; ++d) {
+        q[d] = (j < N && d < D) ? load_elem<BF16>(p.q, ((row + j) * H + h) * D + d) : 0.0f;
+        acc[d] = 0.0f;
+    }
+    const float scale = 1.0f / sqrtf(static_cast<float>(D));
+    float m = -INFINITY, l = 0.0f;
+
+    for (int t = 0; t < p.T; ++t) {
+        const int64_t ks = tile_start(t, N, p.T), ke = tile_start(t + 1, N, p.T);
+        for (int64_t kb = ks; kb < ke; kb += GK) {
+            const int nk = static_cast<int>(ke - kb < GK ? ke - kb : GK);
+            __syncthreads();
+            for (int e = tid; e < GK * DP; e += GJ) {
+                const int kk = e / DP, d = e % DP;
+                const bool ok = kk < nk && d < D;
+                const int64_t off = ((row + kb + kk) * H + h) * D + d;
+                Ks[kk][d] = ok ? load_elem<BF16>(p.k, off) : 0.0f;
+                Vs[kk][d] = ok ? load_elem<BF16>(p.v, off) : 0.0f;
+            }
+            for (int e = tid; e < GJ * GK; e += GJ) {
+                const int jj = e / GK, kk = e % GK;
+                const int64_t jg = j0 + jj;
+                float bv = -INFINITY;
+                if (kk < nk && jg < N) {
+                    bv = load_elem<BF16>(p.bias, ((b * H + h) * N + jg) * N + kb + kk);
+                    if (p.mask) bv += p.mask[b * N + kb + kk];
+                }
+                Bs[jj][kk] = bv;
+            }
+            __syncthreads();
+
+            float s[GK];
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kk = 0; kk < GK; ++kk) {
+                float dot = 0.0f;
+#pragma unroll
+                for (int d = 0; d < DP; ++d) dot = fmaf(q[d], Ks[kk][d], dot);
+                s[kk] = dot * scale + Bs[tid][kk];
+                mx = fmaxf(mx, s[kk]);
+            }
+            if (mx == -INFINITY) continue;  // every key of the block dropped for this query
+            const float mnew = fmaxf(m, mx);
+            const float alpha = expf(m - mnew);  // 0 while m is still -inf
+            l *= alpha;
+#pragma unroll
+            for (int d = 0; d < DP; ++d) acc[d] *= alpha;
+#pragma unroll
+            for (int kk = 0; kk < GK; ++kk) {
+                const float pk = expf(s[kk] - mnew);
+                l += pk;
+#pragma unroll
+                for (int d = 0; d < DP; ++d) acc[d] = fmaf(pk, Vs[kk][d], acc[d]);
+            }
+            m = mnew;
+        }
+    }
+    if (j < N) {
+        const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+        float* o = p.out + ((row + j) * H + h) * D;
+#pragma unroll
+        for (int d = 0; d < DP; ++d)
+            if (d < D) o[d] = acc[d] * inv;
+    }
+}
+
+template <bool BF16>
+hipError_t launch_dp(const Problem& p, hipStream_t stream) {
+    const dim3 grid(static_cast<unsigned>((p.N + GJ - 1) / GJ), static_cast<unsigned>(p.I),
+                    static_cast<unsigned>(p.B * p.H));
+    if (p.D <= 16)
+        hipLaunchKernelGGL((general_kernel<BF16, 16>), grid, dim3(GJ), 0, stream, p);
+    else if (p.D <= 32)
+        hipLaunchKernelGGL((general_kernel<BF16, 32>), grid, dim3(GJ), 0, stream, p);
+    else
+        hipLaunchKernelGGL((general_kernel<BF16, 64>), grid, dim3(GJ), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_general(const Problem& p, bool bf16, hipStream_t stream) {
+    return bf16 ? launch_dp<true>(p, stream) : launch_dp<false>(p, stream);
+}
+
+}  // namespace tri_attn
