@@ -1,0 +1,191 @@
+#!/usr/bin/env python3
+"""Benchmark: pair-biased triangle attention on one MI355X.
+
+One step = one call of the whole forward (tri_attn_fwd) on the single-GPU ceiling
+workload: B=1, N=2,700 tokens, H=4, D=32, bf16 inputs, last 60 keys masked, 8 ring-step
+key tiles (the 1x1 row of the Fold-CP page's Table 2 gives 2,700 tokens as one H100's
+maximum).  Inputs are synthetic and seeded (workloads/), resident in HBM before timing.
+
+Prints one JSON line.  `value` is TFLOP/s at the nominal 4*B*H*N^3*D FLOPs; `roofline`
+relates the kernel's live-measured average launch time to the bf16 dense MFMA peak;
+`cpu_baseline` times the fp64 oracle on a bounded sample of the same workload's rows.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "triangle-attention TFLOP/s (4·B·H·N³·D) and % bf16 MFMA peak, 1×MI355X"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak (AMD published)
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E (AMD published)
+DEFAULT_WORKLOAD = "single_gpu_n2700"
+KERNEL_NAME = "bf16_mfma_kernel"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+def kernel_source_digest() -> str:
+    """SHA-256 over the HIP sources of the library: stored traffic counters are only
+    reported while the kernels they were taken on are unchanged."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "pair_biased_triangle_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, or None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = rec.get(workload)
+    if not entry or entry.get("kernel_source_sha256") != kernel_source_digest():
+        return None
+    return int(entry["hbm_bytes_per_launch"])
+
+
+def to_dev(torch, a):
+    if a is None:
+        return None
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(a).cuda()
+
+
+def cpu_baseline(w, out_gpu, torch, target_s: float):
+    """Time the fp64 oracle on a bounded, deterministic sample of query rows of the same
+    workload; scale to TFLOP/s with the same nominal FLOPs per row.  Also reports the
+    largest |gpu - oracle| over the sample (parity spot check of the timed launch)."""
+    import oracle
+    cfg = w.cfg
+    rng = np.random.default_rng(1234)
+    total_rows = cfg.B * cfg.I * cfg.N
+    flops_per_row = 4.0 * cfg.H * cfg.N * cfg.D
+    probe = np.sort(rng.choice(total_rows, size=min(total_rows, 256), replace=False))
+    t0 = time.perf_counter()
+    oracle.tri_attn(w.q, w.k, w.v, w.bias, w.mask, n_key_tiles=cfg.n_key_tiles, rows=probe)
+    t_probe = time.perf_counter() - t0
+    n = int(min(total_rows, max(256, len(probe) * target_s / max(t_probe, 1e-6))))
+    rows = np.sort(rng.choice(total_rows, size=n, replace=False))
+    t0 = time.perf_counter()
+    ref, _ = oracle.tri_attn(w.q, w.k, w.v, w.bias, w.mask, n_key_tiles=cfg.n_key_tiles, rows=rows)
+    secs = time.perf_counter() - t0
+    got = out_gpu.view(-1, cfg.H, cfg.D)[torch.from_numpy(rows).cuda()].cpu().numpy().astype(np.float64)
+    err = float(np.max(np.abs(got - ref)))
+    return {
+        "value": round(n * flops_per_row / secs / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"{n} of {total_rows} query rows (b,i,j), all {cfg.H} heads and {cfg.N} keys each, "
+                  f"{secs:.1f} s wall, fp64",
+    }, err, n
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target wall time of the CPU baseline")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the multi-GPU sharding is described in DESIGN.md but not built.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import pair_biased_triangle_amd as P
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    P.load_library()
+    cfg = W.CONFIGS[args.workload]
+    w = W.make_inputs(cfg)
+    q, k, v, bias, mask = (to_dev(torch, x) for x in (w.q, w.k, w.v, w.bias, w.mask))
+    out = torch.empty((cfg.B, cfg.I, cfg.N, cfg.H, cfg.D), dtype=torch.float32, device="cuda")
+    fn = P.tri_attn_fwd if cfg.I == cfg.N else P.tri_attn_fwd_rows
+    step = lambda: fn(q, k, v, bias, mask, n_key_tiles=cfg.n_key_tiles, out=out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()          # the stream the kernel is launched on
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t0
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+
+    flops = cfg.flops
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+    traffic = measured_traffic(args.workload) if cfg.dtype == "bf16" else None
+    roofline = {
+        "bound": "mfma",
+        "achieved": round(tflops, 3),
+        "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "traffic": traffic,
+        "kernel": KERNEL_NAME if (cfg.dtype == "bf16" and cfg.D == 32) else "general_kernel",
+        "avg_launch_ms": round(ms_per_step, 4),
+        "algorithmic_flops_per_launch": flops,
+        "algorithmic_bytes_per_launch": cfg.algorithmic_bytes,
+        "hbm_gbs_algorithmic": round(cfg.algorithmic_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+    }
+    result = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded counter-based normal inputs, workloads/)",
+        "config": {"workload": cfg.name, "B": cfg.B, "I": cfg.I, "N": cfg.N, "H": cfg.H, "D": cfg.D,
+                   "n_key_tiles": cfg.n_key_tiles, "masked_keys": cfg.mask_last, "input_dtype": cfg.dtype,
+                   "out_dtype": "fp32"},
+        "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "wall_s_timed_region": round(wall_s, 4),
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu:
+        base, err, n = cpu_baseline(w, out, torch, args.cpu_seconds)
+        result["cpu_baseline"] = base
+        result["parity_sample"] = {"rows": n, "max_abs_err_vs_oracle": err, "bar": 1e-2 if cfg.dtype == "bf16" else 1e-5}
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -33,9 +33,16 @@
  * operand.  The fp32 path computes in fp32 throughout.
  *
  * Ownership and memory: every pointer is a device pointer owned by the caller; the
- * library keeps none of them after returning and allocates no device memory.  q, k, v,
- * bias and mask are only read and may alias one another; out must not overlap any
- * input.  q, k, v, bias and out must be 16-byte aligned, mask 4-byte aligned.
+ * library keeps none of them after returning.  q, k, v, bias and mask are only read and
+ * may alias one another; out must not overlap any input.  q, k, v, bias and out must be
+ * 16-byte aligned, mask 4-byte aligned.  The bf16 matrix-core path (D == 32) first
+ * converts the bias into an fp32 image of tri_attn_workspace_bytes() bytes: roughly
+ * 4 * B * H * N * N * (1 + 127/N) bytes.  tri_attn_fwd and tri_attn_fwd_rows obtain it
+ * stream-ordered on `stream` (hipMallocFromPoolAsync / hipFreeAsync) from a memory pool the
+ * library creates once per device; the pool keeps freed memory reserved for later calls
+ * (up to the largest workspace used) until the process ends.  tri_attn_fwd_rows_ws takes
+ * the workspace from the caller instead and allocates nothing.  The other paths need no
+ * workspace.
  *
  * Streams: calls only enqueue work on `stream` (a hipStream_t; NULL is the null
  * stream) and return without synchronising.  A kernel fault surfaces at the caller's
@@ -45,9 +52,9 @@
  * prints.  Arguments are checked in this order, before any device work: NULL
  * pointers; sizes (all >= 1, I <= N, element counts fit int64); dtype; head size
  * (the bf16 path needs D == 32, the fp32 path D <= 64; D <= 64 for bf16 on the
- * general path); n_key_tiles in [1, N]; alignment; out overlapping an input.  A failed
- * launch returns TRI_ATTN_ERR_HIP and records the HIP error code for
- * tri_attn_last_hip_error() (per calling thread).
+ * general path; I and B*H at most 65535); n_key_tiles in [1, N]; alignment; out
+ * overlapping an input.  A failed allocation or launch returns TRI_ATTN_ERR_HIP and
+ * records the HIP error code for tri_attn_last_hip_error() (per calling thread).
  */
 #ifndef TRI_ATTN_H
 #define TRI_ATTN_H
@@ -69,11 +76,12 @@ typedef enum {
     TRI_ATTN_ERR_NULL = -1,         /* a required pointer is NULL */
     TRI_ATTN_ERR_SHAPE = -2,        /* a size < 1, I > N, or a size overflows int64 */
     TRI_ATTN_ERR_DTYPE = -3,        /* dtype is not a tri_attn_dtype */
-    TRI_ATTN_ERR_UNSUPPORTED = -4,  /* head size D not served (D > 64) */
+    TRI_ATTN_ERR_UNSUPPORTED = -4,  /* D > 64, or I or B*H above 65535 */
     TRI_ATTN_ERR_ALIGN = -5,        /* a pointer is not aligned as required */
     TRI_ATTN_ERR_TILES = -6,        /* n_key_tiles outside [1, N] */
-    TRI_ATTN_ERR_HIP = -7,          /* the HIP runtime refused the launch */
-    TRI_ATTN_ERR_ALIAS = -8         /* out overlaps an input */
+    TRI_ATTN_ERR_HIP = -7,          /* the HIP runtime refused an allocation or launch */
+    TRI_ATTN_ERR_ALIAS = -8,        /* out (or the workspace) overlaps an input */
+    TRI_ATTN_ERR_WORKSPACE = -9     /* caller workspace smaller than tri_attn_workspace_bytes() */
 } tri_attn_status;
 
 /*
@@ -100,6 +108,28 @@ int tri_attn_fwd_rows(const void *q, const void *k, const void *v, const void *b
                       const float *mask, float *out,
                       int64_t B, int64_t H, int64_t I, int64_t N, int64_t D,
                       int32_t n_key_tiles, int32_t dtype, void *stream);
+
+/*
+ * Device workspace, in bytes, that the call with these sizes needs (0 when its path needs
+ * none), or a negative tri_attn_status for sizes the entry points would reject (same
+ * checks and order as they apply, minus the pointer checks).
+ */
+int64_t tri_attn_workspace_bytes(int64_t B, int64_t H, int64_t I, int64_t N, int64_t D,
+                                 int32_t n_key_tiles, int32_t dtype);
+
+/*
+ * tri_attn_fwd_rows with a caller-owned device workspace of workspace_bytes bytes
+ * (16-byte aligned, at least tri_attn_workspace_bytes(); it must not overlap any input
+ * or out).  The library allocates nothing in this call.  The workspace is overwritten and
+ * must not be touched by other work until the call's kernels have finished on `stream`.
+ * Extra errors: TRI_ATTN_ERR_WORKSPACE (too small or negative size), TRI_ATTN_ERR_NULL
+ * (NULL workspace where one is needed), TRI_ATTN_ERR_ALIGN, TRI_ATTN_ERR_ALIAS.
+ */
+int tri_attn_fwd_rows_ws(const void *q, const void *k, const void *v, const void *bias,
+                         const float *mask, float *out,
+                         int64_t B, int64_t H, int64_t I, int64_t N, int64_t D,
+                         int32_t n_key_tiles, int32_t dtype,
+                         void *workspace, int64_t workspace_bytes, void *stream);
 
 /* Static, NUL-terminated description of a tri_attn_status (unknown codes included). */
 const char *tri_attn_status_string(int status);

@@ -48,6 +48,8 @@ def _bind(path: str):
     L.oracle_tri_attn.restype = ctypes.c_int
     L.oracle_even_tiles.argtypes = [i64, i64, vp]
     L.oracle_even_tiles.restype = None
+    L.oracle_num_threads.argtypes = []
+    L.oracle_num_threads.restype = ctypes.c_int
     return L
 
 
@@ -67,6 +69,11 @@ def even_tiles(N: int, T: int, lib_path: str = _LIB_PATH) -> np.ndarray:
     starts = np.empty(T + 1, dtype=np.int64)
     load(lib_path).oracle_even_tiles(N, T, starts.ctypes.data)
     return starts
+
+
+def num_threads(lib_path: str = _LIB_PATH) -> int:
+    """OpenMP threads the oracle runs on."""
+    return int(load(lib_path).oracle_num_threads())
 
 
 def _dtype_of(a: np.ndarray) -> int:

@@ -33,6 +33,7 @@
  * bfloat16 as the upper half of a binary32.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -53,6 +54,12 @@ static double widen(const void *base, int64_t idx, int dtype)
     float f;
     memcpy(&f, &bits, sizeof f);
     return (double)f;
+}
+
+/* Number of OpenMP threads a parallel region of the oracle uses. */
+int oracle_num_threads(void)
+{
+    return omp_get_max_threads();
 }
 
 /* Near-equal contiguous key tiles: the first N mod T tiles hold ceil(N/T) keys,

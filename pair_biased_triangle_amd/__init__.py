@@ -19,10 +19,10 @@ TRI_ATTN_FP32, TRI_ATTN_BF16 = 0, 1
 STATUS = {
     0: "TRI_ATTN_OK", -1: "TRI_ATTN_ERR_NULL", -2: "TRI_ATTN_ERR_SHAPE", -3: "TRI_ATTN_ERR_DTYPE",
     -4: "TRI_ATTN_ERR_UNSUPPORTED", -5: "TRI_ATTN_ERR_ALIGN", -6: "TRI_ATTN_ERR_TILES",
-    -7: "TRI_ATTN_ERR_HIP", -8: "TRI_ATTN_ERR_ALIAS",
+    -7: "TRI_ATTN_ERR_HIP", -8: "TRI_ATTN_ERR_ALIAS", -9: "TRI_ATTN_ERR_WORKSPACE",
 }
-EXPORTS = ("tri_attn_fwd", "tri_attn_fwd_rows", "tri_attn_status_string",
-           "tri_attn_last_hip_error", "tri_attn_version")
+EXPORTS = ("tri_attn_fwd", "tri_attn_fwd_rows", "tri_attn_fwd_rows_ws", "tri_attn_workspace_bytes",
+           "tri_attn_status_string", "tri_attn_last_hip_error", "tri_attn_version")
 
 
 class TriAttnError(RuntimeError):
@@ -46,6 +46,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         L.tri_attn_fwd.restype = ctypes.c_int
         L.tri_attn_fwd_rows.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, i32, vp]
         L.tri_attn_fwd_rows.restype = ctypes.c_int
+        L.tri_attn_fwd_rows_ws.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, i32, vp, i64, vp]
+        L.tri_attn_fwd_rows_ws.restype = ctypes.c_int
+        L.tri_attn_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i32, i32]
+        L.tri_attn_workspace_bytes.restype = ctypes.c_int64
         L.tri_attn_status_string.argtypes = [ctypes.c_int]
         L.tri_attn_status_string.restype = ctypes.c_char_p
         L.tri_attn_last_hip_error.argtypes = []
@@ -137,4 +141,27 @@ def tri_attn_fwd(q, k, v, bias, mask=None, *, n_key_tiles: int = 1, out=None, st
     B, _, N, H, D = q.shape
     _check(L.tri_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(mask), _ptr(out),
                           B, H, N, D, int(n_key_tiles), dt, _stream_handle(stream)))
+    return out
+
+
+def workspace_bytes(B: int, H: int, I: int, N: int, D: int, n_key_tiles: int, dtype_code: int) -> int:
+    """Device workspace (bytes) tri_attn_fwd_rows_ws needs for these sizes (0 if none)."""
+    n = load_library().tri_attn_workspace_bytes(B, H, I, N, D, int(n_key_tiles), dtype_code)
+    if n < 0:
+        raise TriAttnError(int(n), status_string(int(n)))
+    return int(n)
+
+
+def tri_attn_fwd_rows_ws(q, k, v, bias, mask=None, *, workspace, n_key_tiles: int = 1, out=None, stream=None):
+    """tri_attn_fwd_rows with a caller-owned device workspace (a uint8 tensor of at least
+    workspace_bytes(...) bytes); the library allocates nothing.  Calls tri_attn_fwd_rows_ws."""
+    L = load_library()
+    dt, out = _validate(q, k, v, bias, mask, out)
+    B, I, N, H, D = q.shape
+    if workspace is None or not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(L.tri_attn_fwd_rows_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(mask), _ptr(out),
+                                  B, H, I, N, D, int(n_key_tiles), dt, _ptr(workspace), nbytes,
+                                  _stream_handle(stream)))
     return out

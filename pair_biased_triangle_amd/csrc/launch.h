@@ -19,8 +19,10 @@ struct Problem {
     int32_t T;           // key tiles (ring steps)
 };
 
-// bf16 inputs, D == 32: matrix-core kernel.
-hipError_t launch_bf16_mfma(const Problem& p, hipStream_t stream);
+// bf16 inputs, D == 32: matrix-core kernels.  `workspace` (16-byte aligned, at least
+// bf16_workspace_bytes(p) bytes) receives the converted bias image.
+size_t bf16_workspace_bytes(const Problem& p);
+hipError_t launch_bf16_mfma(const Problem& p, void* workspace, hipStream_t stream);
 
 // Any D <= 64, fp32 or bf16 inputs: plain fp32 kernel.
 hipError_t launch_general(const Problem& p, bool bf16, hipStream_t stream);

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "tri_attn.h")
 
 FP32, BF16 = 0, 1
-OK, E_NULL, E_SHAPE, E_DTYPE, E_UNSUP, E_ALIGN, E_TILES, E_HIP, E_ALIAS = 0, -1, -2, -3, -4, -5, -6, -7, -8
+OK, E_NULL, E_SHAPE, E_DTYPE, E_UNSUP, E_ALIGN, E_TILES, E_HIP, E_ALIAS, E_WS = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
 
 
 def declared_functions():
@@ -43,13 +43,13 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.tri_attn_version() == 10000
+    assert lib.tri_attn_version() == 10100
     seen = set()
-    for code in (OK, E_NULL, E_SHAPE, E_DTYPE, E_UNSUP, E_ALIGN, E_TILES, E_HIP, E_ALIAS):
+    for code in (OK, E_NULL, E_SHAPE, E_DTYPE, E_UNSUP, E_ALIGN, E_TILES, E_HIP, E_ALIAS, E_WS):
         s = P.status_string(code)
         assert s and s != "unknown status"
         seen.add(s)
-    assert len(seen) == 9
+    assert len(seen) == 10
     assert P.status_string(12345) == "unknown status"
     assert lib.tri_attn_last_hip_error() == 0
 
@@ -122,3 +122,46 @@ def test_out_overlapping_an_input(lib):
     assert call(lib, out=Q) == E_ALIAS
     assert call(lib, out=fake(0x10000000 * 4 + 64)) == E_ALIAS   # inside bias
     assert call(lib, mask=fake(0x10000000 * 6 + 1024)) == E_ALIAS  # mask inside out
+
+
+# ---------------------------------------------------------------------------
+# workspace
+# ---------------------------------------------------------------------------
+def test_workspace_bytes(lib):
+    # bf16 D=32: B*H*ceil(N/128)*(key blocks)*128*32*4; key blocks = sum over tiles of ceil(len/32)
+    assert lib.tri_attn_workspace_bytes(1, 4, 2700, 2700, 32, 8, BF16) == 4 * 22 * (8 * 11) * 128 * 32 * 4
+    assert lib.tri_attn_workspace_bytes(1, 4, 1024, 4096, 32, 8, BF16) == 4 * 32 * (8 * 16) * 128 * 32 * 4
+    assert lib.tri_attn_workspace_bytes(2, 3, 5, 7, 32, 3, BF16) == 6 * 1 * 3 * 128 * 32 * 4
+    assert lib.tri_attn_workspace_bytes(1, 4, 64, 64, 32, 1, FP32) == 0
+    assert lib.tri_attn_workspace_bytes(1, 4, 64, 64, 16, 1, BF16) == 0
+    assert lib.tri_attn_workspace_bytes(1, 4, 64, 64, 32, 0, BF16) == E_TILES
+    assert lib.tri_attn_workspace_bytes(1, 4, 65, 64, 32, 1, BF16) == E_SHAPE
+    assert P.workspace_bytes(1, 4, 2700, 2700, 32, 8, 1) == 4 * 22 * 88 * 16384
+
+
+WS = fake(0x70000000)
+
+
+def call_ws(lib, ws=WS, nbytes=1 << 30, **kw):
+    args = dict(q=Q, k=K, v=V, bias=BIAS, mask=None, out=OUT, B=1, H=4, I=64, N=64, D=32, T=1, dtype=BF16)
+    args.update(kw)
+    return lib.tri_attn_fwd_rows_ws(args["q"], args["k"], args["v"], args["bias"], args["mask"], args["out"],
+                                    args["B"], args["H"], args["I"], args["N"], args["D"], args["T"], args["dtype"],
+                                    ws, nbytes, None)
+
+
+def test_workspace_errors(lib):
+    need = lib.tri_attn_workspace_bytes(1, 4, 64, 64, 32, 1, BF16)
+    assert call_ws(lib, nbytes=need - 1) == E_WS
+    assert call_ws(lib, nbytes=-1) == E_WS
+    assert call_ws(lib, ws=None) == E_NULL
+    assert call_ws(lib, ws=fake(0x70000008)) == E_ALIGN
+    assert call_ws(lib, ws=fake(0x10000000 + 256)) == E_ALIAS        # inside q
+    assert call_ws(lib, ws=fake(0x10000000 * 6 - 64)) == E_ALIAS      # runs into out
+    assert call_ws(lib, q=None) == E_NULL                              # ordinary checks come first
+    assert call_ws(lib, T=65) == E_TILES
+
+
+def test_row_span_limit_of_matrix_core_path(lib):
+    # one (b, i) row of K holds N*H*D bf16 values; 32-bit byte offsets cap it below 2 GiB
+    assert call(lib, N=1 << 16, H=1 << 9) == E_UNSUP

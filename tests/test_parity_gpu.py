@@ -266,3 +266,52 @@ def test_binding_rejects_bad_tensors(torch_dev):
         P.tri_attn_fwd(q, q, q, bias.float())
     with pytest.raises(ValueError):
         P.tri_attn_fwd(q, q, q, bias[:, :, :, :4])
+
+
+def test_caller_workspace_matches_pool_workspace(torch_dev):
+    import pair_biased_triangle_amd as P
+    torch = torch_dev
+    cfg = W.custom_config(B=2, I=21, N=150, H=3, D=32, dtype="bf16", n_key_tiles=6, seed=14, mask_last=7)
+    w = W.make_inputs(cfg)
+    q, k, v, bias, mask = (to_dev(torch, x) for x in (w.q, w.k, w.v, w.bias, w.mask))
+    need = P.workspace_bytes(2, 3, 21, 150, 32, 6, P.TRI_ATTN_BF16)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    say("[parity] caller workspace vs library pool")
+    a = P.tri_attn_fwd_rows(q, k, v, bias, mask, n_key_tiles=6)
+    b = P.tri_attn_fwd_rows_ws(q, k, v, bias, mask, workspace=ws, n_key_tiles=6)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    with pytest.raises(P.TriAttnError) as e:
+        P.tri_attn_fwd_rows_ws(q, k, v, bias, mask, workspace=ws[: need - 16], n_key_tiles=6)
+    assert e.value.status == -9
+
+
+def test_score_jump_takes_exact_fallback(torch_dev):
+    """A key far above the first block's maximum (+120 nats) overflows the stale
+    reference; the workgroup must recompute with the exact running maximum."""
+    torch = torch_dev
+    cfg = W.custom_config(B=1, I=24, N=260, H=2, D=32, dtype="bf16", n_key_tiles=3, seed=15)
+    w = W.make_inputs(cfg)
+    b = W.bf16_bits_to_f32(w.bias)
+    b[0, 0, 5:40, 200] = 120.0
+    b[0, 1, 100:101, 250] = -1000.0
+    w.bias = W.f32_to_bf16_bits(b)
+    say("[parity] score jump above the first block")
+    out = run_gpu(torch, w, 3).cpu().numpy()
+    ref, _ = oracle.tri_attn(w.q, w.k, w.v, w.bias, w.mask, n_key_tiles=3)
+    compare(out, ref, TOL["bf16"], "score jump")
+    np.testing.assert_allclose(out[0, :, 5:40, 0], np.broadcast_to(W.bf16_bits_to_f32(w.v)[0, :, 200:201, 0], (24, 35, 32)),
+                               atol=1e-6)
+
+
+def test_masked_first_blocks(torch_dev):
+    """Keys masked at the front: the first block of every row has no finite score."""
+    torch = torch_dev
+    cfg = W.custom_config(B=1, I=16, N=200, H=4, D=32, dtype="bf16", n_key_tiles=4, seed=16)
+    w = W.make_inputs(cfg)
+    w.mask = np.zeros((1, 200), np.float32)
+    w.mask[0, :70] = -np.inf
+    say("[parity] masked leading keys")
+    out = run_gpu(torch, w, 4).cpu().numpy()
+    ref, _ = oracle.tri_attn(w.q, w.k, w.v, w.bias, w.mask, n_key_tiles=4)
+    compare(out, ref, TOL["bf16"], "masked leading keys")
