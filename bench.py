@@ -105,6 +105,8 @@ def main() -> int:
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target wall time of the CPU baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run 3 plain device copies of 1 GiB (reference dispatches for the HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -120,6 +122,15 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         return 1
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n, "dispatches": 3}))
+        return 0
     P.load_library()
     cfg = W.CONFIGS[args.workload]
     w = W.make_inputs(cfg)

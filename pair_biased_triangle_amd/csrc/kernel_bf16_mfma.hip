@@ -34,11 +34,12 @@
 // whole key loop with the exact running maximum refreshed on every block.
 //
 // Workgroup ids are remapped so that each XCD walks a contiguous range of (b, h, row
-// group, column block) with the column block fastest: a row group's K/V stream and the
-// bias strips stay hot in that XCD's L2.
+// group, column block) tiles of 4 row groups x 8 column blocks: the workgroups an XCD runs
+// together share each row group's K/V stream 8 ways and each bias tile 4 ways in its L2.
 #include "launch.h"
 
 #include <cmath>
+#include <cstddef>
 
 namespace tri_attn {
 namespace {
@@ -64,6 +65,18 @@ constexpr int TW = 2;                       // query tiles per wave
 constexpr int NWAVE = (R / RW) * (QT / TW);
 constexpr int NTHR = 64 * NWAVE;
 constexpr int NXCD = 8;
+#ifndef TRI_ATTN_STAGES
+#define TRI_ATTN_STAGES 3
+#endif
+#ifndef TRI_ATTN_TILE_RG
+#define TRI_ATTN_TILE_RG 4
+#endif
+#ifndef TRI_ATTN_TILE_JB
+#define TRI_ATTN_TILE_JB 8
+#endif
+constexpr int NSTAGE = TRI_ATTN_STAGES;     // key blocks in flight (LDS ring of stages)
+constexpr int TILE_RG = TRI_ATTN_TILE_RG;   // row groups x column blocks that one XCD
+constexpr int TILE_JB = TRI_ATTN_TILE_JB;   //   works on together (L2 reuse of K/V and bias)
 constexpr int IMG_FLOATS = BJ * BK;         // one bias tile of the image
 static_assert(NWAVE == R, "wave w stages K and V of row w");
 static_assert(IMG_FLOATS * 4 == 2 * NWAVE * 1024, "each wave stages two 1 KB pieces of the bias tile");
@@ -179,19 +192,28 @@ __device__ __forceinline__ void stage_block(const Ctx& cx, int n, Stage& st, int
     }
 }
 
+constexpr int ROW_BYTES = BK * D * 2;       // one staged row of K or V
+constexpr int TILE_BYTES = 32 * BK * 4;     // 32 rows of the staged bias tile
+constexpr int STAGE_BYTES = static_cast<int>(sizeof(Stage));
+constexpr int K_OFF = static_cast<int>(offsetof(Stage, k));
+constexpr int V_OFF = static_cast<int>(offsetof(Stage, v));
+constexpr int B_OFF = static_cast<int>(offsetof(Stage, bias));
+static_assert(RW == 2 && TW == 2, "the operand reads below address rows +ROW_BYTES and tiles +TILE_BYTES");
+
+// LDS byte offsets (inside stage 0) of this lane's operand reads for its first row / tile.
 struct Lane {
     int c, h2;
-    int k_off[2];          // byte offsets inside one staged row of K: A operand of S^T = K Q^T
-    int v_off[2][2];       // byte offsets inside one staged row of V: ds_read_b64_tr_b16 sources
-    int b_off[4];          // byte offsets inside a 32-row slab of the bias tile
+    uint32_t k[2];        // K operand of S^T = K Q^T, d-half m
+    uint32_t v[2][2];     // ds_read_b64_tr_b16 sources of the V^T operand, [key half m][sub]
+    uint32_t b[4];        // bias operand, 16-byte chunk a
 };
 
-__device__ __forceinline__ Lane lane_layout(int lane) {
+__device__ __forceinline__ Lane lane_layout(int lane, int row0, int tile0) {
     Lane L;
     L.c = lane & 31;
     L.h2 = lane >> 5;
 #pragma unroll
-    for (int m = 0; m < 2; ++m) L.k_off[m] = L.c * 64 + kv_chunk(L.c, 2 * m + L.h2) * 16;
+    for (int m = 0; m < 2; ++m) L.k[m] = K_OFF + row0 * ROW_BYTES + L.c * 64 + kv_chunk(L.c, 2 * m + L.h2) * 16;
     // transpose read: lane i of a 16-lane group reads keys kbase + i/4, d = dbase + 4*(i%4) .. +3
     // and receives d = dbase + i for keys kbase .. kbase + 3
     const int i = lane & 15, dbase = 16 * ((lane >> 4) & 1);
@@ -201,11 +223,84 @@ __device__ __forceinline__ Lane lane_layout(int lane) {
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub) {
             const int key = 16 * m + 8 * sub + 4 * L.h2 + (i >> 2);
-            L.v_off[m][sub] = key * 64 + kv_chunk(key, d0 >> 3) * 16 + (d0 & 7) * 2;
+            L.v[m][sub] = V_OFF + row0 * ROW_BYTES + key * 64 + kv_chunk(key, d0 >> 3) * 16 + (d0 & 7) * 2;
         }
 #pragma unroll
-    for (int a = 0; a < 4; ++a) L.b_off[a] = L.c * 128 + bias_chunk(L.c, 2 * a + L.h2) * 16;
+    for (int a = 0; a < 4; ++a)
+        L.b[a] = B_OFF + tile0 * TILE_BYTES + L.c * 128 + bias_chunk(L.c, 2 * a + L.h2) * 16;
     return L;
+}
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Operands of one staged block.  The reads are inline assembly that waits for its own
+// results (lgkmcnt) before returning: the compiler then sees no LDS read it would have to
+// order against the global->LDS copies still in flight into the other stages.
+struct VFrags {
+    bf16x8 vA[RW][2];
+};
+struct KCFrags {
+    bf16x8 kA[RW][2];
+    f32x16 C[TW];
+};
+
+__device__ __forceinline__ void load_v(uint32_t stage, const Lane& L, VFrags& f) {
+    u32x2 t[8];
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8\n\t"
+        "ds_read_b64_tr_b16 %1, %9\n\t"
+        "ds_read_b64_tr_b16 %2, %10\n\t"
+        "ds_read_b64_tr_b16 %3, %11\n\t"
+        "ds_read_b64_tr_b16 %4, %8 offset:2048\n\t"
+        "ds_read_b64_tr_b16 %5, %9 offset:2048\n\t"
+        "ds_read_b64_tr_b16 %6, %10 offset:2048\n\t"
+        "ds_read_b64_tr_b16 %7, %11 offset:2048\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3]), "=&v"(t[4]), "=&v"(t[5]), "=&v"(t[6]), "=&v"(t[7])
+        : "v"(stage + L.v[0][0]), "v"(stage + L.v[0][1]), "v"(stage + L.v[1][0]), "v"(stage + L.v[1][1]));
+    static_assert(ROW_BYTES == 2048, "row offset in the assembly above");
+#pragma unroll
+    for (int ri = 0; ri < RW; ++ri)
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const u32x2 lo = t[4 * ri + 2 * m], hi = t[4 * ri + 2 * m + 1];
+            const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
+            f.vA[ri][m] = __builtin_bit_cast(bf16x8, w);
+        }
+}
+
+__device__ __forceinline__ void load_kc(uint32_t stage, const Lane& L, KCFrags& f) {
+    u32x4 k[4], b[8];
+    asm volatile(
+        "ds_read_b128 %0, %12\n\t"
+        "ds_read_b128 %1, %13\n\t"
+        "ds_read_b128 %2, %12 offset:2048\n\t"
+        "ds_read_b128 %3, %13 offset:2048\n\t"
+        "ds_read_b128 %4, %14\n\t"
+        "ds_read_b128 %5, %15\n\t"
+        "ds_read_b128 %6, %16\n\t"
+        "ds_read_b128 %7, %17\n\t"
+        "ds_read_b128 %8, %14 offset:4096\n\t"
+        "ds_read_b128 %9, %15 offset:4096\n\t"
+        "ds_read_b128 %10, %16 offset:4096\n\t"
+        "ds_read_b128 %11, %17 offset:4096\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(b[0]), "=&v"(b[1]), "=&v"(b[2]), "=&v"(b[3]),
+          "=&v"(b[4]), "=&v"(b[5]), "=&v"(b[6]), "=&v"(b[7])
+        : "v"(stage + L.k[0]), "v"(stage + L.k[1]), "v"(stage + L.b[0]), "v"(stage + L.b[1]), "v"(stage + L.b[2]),
+          "v"(stage + L.b[3]));
+    static_assert(TILE_BYTES == 4096, "tile offset in the assembly above");
+#pragma unroll
+    for (int ri = 0; ri < RW; ++ri)
+#pragma unroll
+        for (int m = 0; m < 2; ++m) f.kA[ri][m] = __builtin_bit_cast(bf16x8, k[2 * ri + m]);
+#pragma unroll
+    for (int ti = 0; ti < TW; ++ti)
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) f.C[ti][4 * a + e] = __uint_as_float(b[4 * ti + a][e]);
 }
 
 struct State {
@@ -226,54 +321,16 @@ struct State {
     }
 };
 
-// V^T operands of the wave's rows.  ds_read_b64_tr_b16 carries no alias information, so
-// these reads are issued before the next block's copy (a read after it would wait for it).
-struct VFrags {
-    bf16x8 vA[RW][2];
-};
-
-__device__ __forceinline__ void load_v(const Stage& st, const Lane& L, int row0, VFrags& f) {
-    const char* vbase = reinterpret_cast<const char*>(&st.v[0][0][0]);
-#pragma unroll
-    for (int ri = 0; ri < RW; ++ri) {
-        const int rowb = (row0 + ri) * BK * D * 2;
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vbase + rowb + L.v_off[m][0]));
-            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vbase + rowb + L.v_off[m][1]));
-            f.vA[ri][m] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        }
-    }
-}
-
 template <bool EXACT_MAX>
-__device__ __forceinline__ void compute_block(const Stage& st, const Lane& L, int row0, int tile0, const VFrags& vf,
-                                              const bf16x8 (&qB)[RW][TW][2], State& s) {
-    const char* kbase = reinterpret_cast<const char*>(&st.k[0][0][0]);
-    const char* bbase = reinterpret_cast<const char*>(&st.bias[0][0]);
-    bf16x8 kA[RW][2];
-#pragma unroll
-    for (int ri = 0; ri < RW; ++ri)
-#pragma unroll
-        for (int m = 0; m < 2; ++m)
-            kA[ri][m] = *reinterpret_cast<const bf16x8*>(kbase + (row0 + ri) * BK * D * 2 + L.k_off[m]);
+__device__ __forceinline__ void compute_block(const KCFrags& kc, const VFrags& vf, const bf16x8 (&qB)[RW][TW][2],
+                                              State& s) {
     const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 #pragma unroll
     for (int ti = 0; ti < TW; ++ti) {
-        const char* brow = bbase + (tile0 + ti) * 32 * BK * 4;
-        f32x16 C;
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-            const f32x4 x = *reinterpret_cast<const f32x4*>(brow + L.b_off[a]);
-            C[4 * a + 0] = x[0];
-            C[4 * a + 1] = x[1];
-            C[4 * a + 2] = x[2];
-            C[4 * a + 3] = x[3];
-        }
 #pragma unroll
         for (int ri = 0; ri < RW; ++ri) {
-            f32x16 S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kA[ri][0], qB[ri][ti][0], C, 0, 0, 0);
-            S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kA[ri][1], qB[ri][ti][1], S, 0, 0, 0);
+            f32x16 S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kc.kA[ri][0], qB[ri][ti][0], kc.C[ti], 0, 0, 0);
+            S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kc.kA[ri][1], qB[ri][ti][1], S, 0, 0, 0);
             if constexpr (EXACT_MAX) {
                 float mx = S[0];
 #pragma unroll
@@ -309,30 +366,71 @@ __device__ __forceinline__ void compute_block(const Stage& st, const Lane& L, in
     }
 }
 
-__shared__ Stage g_stage0;
-__shared__ Stage g_stage1;
+__shared__ Stage g_stage[NSTAGE];
 __shared__ int g_redo;
 
-// One pass over every key block; the first block (all blocks when `exact`) refreshes the
-// reference maximum.
-__device__ __forceinline__ void key_loop(const Ctx& cx, const Lane& L, int wave, int lane, int row0, int tile0,
-                                         const bf16x8 (&qB)[RW][TW][2], State& s, int nblk, bool exact) {
-    stage_block(cx, 0, g_stage0, wave, lane);
-    __syncthreads();
-    for (int n = 0; n < nblk; ++n) {
-        const bool odd = n & 1;
-        // read this block's operands before the next block's copy is issued, so that no LDS
-        // read has to wait for the copy in flight
-        const Stage& st = odd ? g_stage1 : g_stage0;
-        VFrags vf;
-        load_v(st, L, row0, vf);
-        if (n + 1 < nblk) stage_block(cx, n + 1, odd ? g_stage0 : g_stage1, wave, lane);
-        if (exact || n == 0)
-            compute_block<true>(st, L, row0, tile0, vf, qB, s);
-        else
-            compute_block<false>(st, L, row0, tile0, vf, qB, s);
-        __syncthreads();
+constexpr int COPIES_PER_BLOCK = 6;         // global_load_lds issued per wave per staged block
+static_assert(NSTAGE == 3, "the barrier below keeps exactly one block of copies in flight");
+
+// Barrier after which every wave's copies except the most recent block's are complete
+// (the most recent block is still needed later, the one before it next).
+__device__ __forceinline__ void barrier_keep_newest() {
+    static_assert(COPIES_PER_BLOCK == 6, "vmcnt below");
+    asm volatile("s_waitcnt vmcnt(6)\n\ts_barrier" ::: "memory");
+}
+// Barrier after which every copy issued so far is complete.
+__device__ __forceinline__ void barrier_drain() { asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+__device__ __forceinline__ uint32_t stage_addr(int n) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(LDS_PTR(char, &g_stage[0]))) +
+           static_cast<uint32_t>(n % NSTAGE) * STAGE_BYTES;
+}
+
+// Prologue: copies of blocks 0 .. NSTAGE-2 in flight, block 0 complete everywhere.
+__device__ __forceinline__ void key_prologue(const Ctx& cx, int wave, int lane, int nblk) {
+    stage_block(cx, 0, g_stage[0], wave, lane);
+    if (nblk > 1) {
+        stage_block(cx, 1, g_stage[1], wave, lane);
+        barrier_keep_newest();
+    } else {
+        barrier_drain();
     }
+}
+
+// One step of the key loop: read block n's operands, issue the copy of block
+// n + NSTAGE - 1 into the stage block n - 1 used, compute block n, and leave block n + 1
+// complete for every wave.
+template <bool EXACT_MAX>
+__device__ __forceinline__ void key_step(const Ctx& cx, const Lane& L, int wave, int lane,
+                                         const bf16x8 (&qB)[RW][TW][2], State& s, int n, int nblk) {
+    const uint32_t st = stage_addr(n);
+    VFrags vf;
+    load_v(st, L, vf);
+    const bool issue = n + NSTAGE - 1 < nblk;
+    if (issue) stage_block(cx, n + NSTAGE - 1, g_stage[(n + NSTAGE - 1) % NSTAGE], wave, lane);
+    KCFrags kc;
+    load_kc(st, L, kc);
+    compute_block<EXACT_MAX>(kc, vf, qB, s);
+    if (issue)
+        barrier_keep_newest();
+    else
+        barrier_drain();
+}
+
+// Fast pass: block 0 fixes the reference at its exact maximum, the other blocks reuse it.
+// Each loop has a single compute path, so the accumulators stay in place across blocks.
+__device__ __forceinline__ void key_loop_fast(const Ctx& cx, const Lane& L, int wave, int lane,
+                                              const bf16x8 (&qB)[RW][TW][2], State& s, int nblk) {
+    key_prologue(cx, wave, lane, nblk);
+    key_step<true>(cx, L, wave, lane, qB, s, 0, nblk);
+    for (int n = 1; n < nblk; ++n) key_step<false>(cx, L, wave, lane, qB, s, n, nblk);
+}
+
+// Exact pass: the running maximum is refreshed on every block.
+__device__ __forceinline__ void key_loop_exact(const Ctx& cx, const Lane& L, int wave, int lane,
+                                               const bf16x8 (&qB)[RW][TW][2], State& s, int nblk) {
+    key_prologue(cx, wave, lane, nblk);
+    for (int n = 0; n < nblk; ++n) key_step<true>(cx, L, wave, lane, qB, s, n, nblk);
 }
 
 __global__ void __launch_bounds__(NTHR) bf16_mfma_kernel(Problem p, const float* img, int n_jb, int n_rg, int nblk,
@@ -342,17 +440,27 @@ __global__ void __launch_bounds__(NTHR) bf16_mfma_kernel(Problem p, const float*
     const int xcd = w % NXCD, slot = w / NXCD;
     const int base = total / NXCD, extra = total % NXCD;
     const int logical = xcd * base + (xcd < extra ? xcd : extra) + slot;
-    const int jb = logical % n_jb;
-    const int rg = (logical / n_jb) % n_rg;
+    // within one (b, h): strips of TILE_RG row groups, each cut into tiles of TILE_RG x
+    // TILE_JB (row group, column block) pairs, column block fastest inside a tile; the last
+    // strip and the last tile of a strip may be narrower
     const int bh = logical / (n_jb * n_rg);
+    const int rem = logical - bh * n_jb * n_rg;
+    const int strip = rem / (TILE_RG * n_jb);
+    const int nr = min(TILE_RG, n_rg - strip * TILE_RG);
+    const int o = rem - strip * TILE_RG * n_jb;
+    const int tile = o / (nr * TILE_JB);
+    const int nj = min(TILE_JB, n_jb - tile * TILE_JB);
+    const int o2 = o - tile * nr * TILE_JB;
+    const int rg = strip * TILE_RG + o2 / nj;
+    const int jb = tile * TILE_JB + o2 % nj;
     const int64_t b = bh / p.H, h = bh % p.H;
     const int64_t i0 = static_cast<int64_t>(rg) * R, j0 = static_cast<int64_t>(jb) * BJ;
 
     const int tid = threadIdx.x;
     const int wave = tid / 64, lane = tid % 64;
-    const Lane L = lane_layout(lane);
     const int row0 = (wave / (QT / TW)) * RW;       // first of this wave's rows in the group
     const int tile0 = (wave % (QT / TW)) * TW;      // first of this wave's query tiles
+    const Lane L = lane_layout(lane, row0, tile0);
 
     Ctx cx;
     {
@@ -389,10 +497,14 @@ __global__ void __launch_bounds__(NTHR) bf16_mfma_kernel(Problem p, const float*
             }
         }
 
+    // let the Q loads land before the key loop starts its copies, so that their first use
+    // does not wait for the copies as well (vmcnt(0); expcnt, lgkmcnt unconstrained)
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+
     State s;
     s.reset();
     if (tid == 0) g_redo = 0;
-    key_loop(cx, L, wave, lane, row0, tile0, qB, s, nblk, false);
+    key_loop_fast(cx, L, wave, lane, qB, s, nblk);
 
     // accept the pass only if every normaliser is in range and every accumulator finite
     bool bad = false;
@@ -410,7 +522,7 @@ __global__ void __launch_bounds__(NTHR) bf16_mfma_kernel(Problem p, const float*
     __syncthreads();
     if (g_redo) {
         s.reset();
-        key_loop(cx, L, wave, lane, row0, tile0, qB, s, nblk, true);
+        key_loop_exact(cx, L, wave, lane, qB, s, nblk);
     }
 
     // out = O / l; lanes l and l^32 hold disjoint keys of the same query.
