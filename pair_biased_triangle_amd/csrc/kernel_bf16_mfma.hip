@@ -22,7 +22,10 @@
 //        p   = 2^(S * log2(e)/sqrt(D) + nb),  nb = -m_ref * log2(e)/sqrt(D)
 //        O^T += V^T P^T        two v_mfma_f32_32x32x16_bf16 on the bf16-rounded p;
 //                              V^T comes from ds_read_b64_tr_b16 on the [key][d] tile
-//      The row sum is taken per lane with v_dot2_f32_bf16 on the rounded p.
+//      The row sum is taken per lane with v_dot2_f32_bf16 on the rounded p.  In the
+//      fixed-reference blocks the four units run as a software pipeline in which every
+//      group of four exponentials carries one matrix instruction of the neighbouring
+//      units (compute_block_pipe).
 //
 // Softmax reference.  The first key block sets m_ref to its exact row maximum (one
 // cross-lane step: in the 32x32 output layout lanes l and l^32 hold the 16 + 16 keys of
@@ -321,12 +324,13 @@ struct State {
     }
 };
 
-template <bool EXACT_MAX>
-__device__ __forceinline__ void compute_block(const KCFrags& kc, const VFrags& vf, const bf16x8 (&qB)[RW][TW][2],
-                                              State& s) {
+// The wave's two units (rows ri = 0, 1) of query tile TI for one key block.
+template <bool EXACT_MAX, int TI>
+__device__ __forceinline__ void compute_tile(const KCFrags& kc, const VFrags& vf, const bf16x8 (&qB)[RW][TW][2],
+                                             State& s) {
     const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
-#pragma unroll
-    for (int ti = 0; ti < TW; ++ti) {
+    constexpr int ti = TI;
+    {
 #pragma unroll
         for (int ri = 0; ri < RW; ++ri) {
             f32x16 S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kc.kA[ri][0], qB[ri][ti][0], kc.C[ti], 0, 0, 0);
@@ -364,6 +368,81 @@ __device__ __forceinline__ void compute_block(const KCFrags& kc, const VFrags& v
             s.O[ri][ti] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf.vA[ri][1], pb1, s.O[ri][ti], 0, 0, 0);
         }
     }
+}
+
+template <bool EXACT_MAX>
+__device__ __forceinline__ void compute_block(const KCFrags& kc, const VFrags& vf, const bf16x8 (&qB)[RW][TW][2],
+                                              State& s) {
+    static_assert(TW == 2, "two query tiles per wave");
+    compute_tile<EXACT_MAX, 0>(kc, vf, qB, s);
+    compute_tile<EXACT_MAX, 1>(kc, vf, qB, s);
+}
+
+// Fixed-reference block as an explicit software pipeline over the wave's four units
+// u = (tile u / 2, row u % 2).  Unit u's softmax runs in four chunks of 4 scores (4 FMA +
+// 4 v_exp_f32, the bf16 conversion and row sum after every second chunk), and each chunk
+// carries exactly one matrix instruction: the two halves of S for unit u + 1 during
+// chunks 0 and 1, the two halves of P.V for unit u - 1 during chunks 2 and 3.  On gfx950
+// a matrix instruction issued among transcendental instructions runs almost entirely in
+// their shadow, while one issued among plain VALU instructions mostly does not, so the
+// order is pinned with scheduling barriers.
+template <int U>
+__device__ __forceinline__ f32x16 s_half(const KCFrags& kc, const bf16x8 (&qB)[RW][TW][2], int m, const f32x16& acc) {
+    constexpr int ti = U / RW, ri = U % RW;
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(kc.kA[ri][m], qB[ri][ti][m], acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ void compute_block_pipe(const KCFrags& kc, const VFrags& vf, const bf16x8 (&qB)[RW][TW][2],
+                                                   State& s) {
+    static_assert(RW == 2 && TW == 2, "four units per wave");
+    const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+    f32x16 S[4];
+    bf16x8 P[4][2];
+    S[0] = s_half<0>(kc, qB, 0, kc.C[0]);
+    S[0] = s_half<0>(kc, qB, 1, S[0]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int ti = u / RW, ri = u % RW;
+        const float nb = s.nb[ri][ti];
+        float ls = s.lsum[ri][ti];
+        f32x16 p;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if (q == 0 && u + 1 < 4) {
+                if (u + 1 == 1) S[1] = s_half<1>(kc, qB, 0, kc.C[0]);
+                if (u + 1 == 2) S[2] = s_half<2>(kc, qB, 0, kc.C[1]);
+                if (u + 1 == 3) S[3] = s_half<3>(kc, qB, 0, kc.C[1]);
+            }
+            if (q == 1 && u + 1 < 4) {
+                if (u + 1 == 1) S[1] = s_half<1>(kc, qB, 1, S[1]);
+                if (u + 1 == 2) S[2] = s_half<2>(kc, qB, 1, S[2]);
+                if (u + 1 == 3) S[3] = s_half<3>(kc, qB, 1, S[3]);
+            }
+            if (q >= 2 && u > 0) {
+                const int pu = u - 1, pt = pu / RW, pr = pu % RW;
+                s.O[pr][pt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf.vA[pr][q - 2], P[pu][q - 2], s.O[pr][pt], 0, 0, 0);
+            }
+#pragma unroll
+            for (int r = 4 * q; r < 4 * q + 4; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(S[u][r], kScale, nb));
+            if (q == 1 || q == 3) {
+                const int h = q / 2;
+                const f32x8 ph = h == 0 ? __builtin_shufflevector(p, p, 0, 1, 2, 3, 4, 5, 6, 7)
+                                        : __builtin_shufflevector(p, p, 8, 9, 10, 11, 12, 13, 14, 15);
+                P[u][h] = __builtin_convertvector(ph, bf16x8);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const bf16x2 a = {P[u][h][2 * e], P[u][h][2 * e + 1]};
+                    ls = __builtin_amdgcn_fdot2_f32_bf16(a, ones, ls, false);
+                }
+                asm volatile("" : "+v"(ls));   // keep the row sums in this chunk
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        s.lsum[ri][ti] = ls;
+    }
+    s.O[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf.vA[1][0], P[3][0], s.O[1][1], 0, 0, 0);
+    s.O[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf.vA[1][1], P[3][1], s.O[1][1], 0, 0, 0);
 }
 
 __shared__ Stage g_stage[NSTAGE];
@@ -410,7 +489,10 @@ __device__ __forceinline__ void key_step(const Ctx& cx, const Lane& L, int wave,
     if (issue) stage_block(cx, n + NSTAGE - 1, g_stage[(n + NSTAGE - 1) % NSTAGE], wave, lane);
     KCFrags kc;
     load_kc(st, L, kc);
-    compute_block<EXACT_MAX>(kc, vf, qB, s);
+    if constexpr (!EXACT_MAX)
+        compute_block_pipe(kc, vf, qB, s);
+    else
+        compute_block<EXACT_MAX>(kc, vf, qB, s);
     if (issue)
         barrier_keep_newest();
     else
@@ -457,7 +539,7 @@ __global__ void __launch_bounds__(NTHR) bf16_mfma_kernel(Problem p, const float*
     const int64_t i0 = static_cast<int64_t>(rg) * R, j0 = static_cast<int64_t>(jb) * BJ;
 
     const int tid = threadIdx.x;
-    const int wave = tid / 64, lane = tid % 64;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;   // wave is uniform
     const int row0 = (wave / (QT / TW)) * RW;       // first of this wave's rows in the group
     const int tile0 = (wave % (QT / TW)) * TW;      // first of this wave's query tiles
     const Lane L = lane_layout(lane, row0, tile0);
