@@ -34,7 +34,7 @@
  *
  * Ownership and memory: every pointer is a device pointer owned by the caller; the
  * library keeps none of them after returning.  q, k, v, bias and mask are only read and
- * may alias one another; out must not overlap any input.  q, k, v, bias and out must be
+ * may alias one another; outputs must not overlap any input.  q, k, v, bias and out must be
  * 16-byte aligned, mask 4-byte aligned.  The bf16 matrix-core path (D == 32) first
  * converts the bias into an fp32 image of tri_attn_workspace_bytes() bytes: roughly
  * 4 * B * H * N * N * (1 + 127/N) bytes.  tri_attn_fwd and tri_attn_fwd_rows obtain it
@@ -51,10 +51,12 @@
  * Errors: every entry point returns a tri_attn_status and never throws, aborts or
  * prints.  Arguments are checked in this order, before any device work: NULL
  * pointers; sizes (all >= 1, I <= N, element counts fit int64); dtype; head size
- * (the bf16 path needs D == 32, the fp32 path D <= 64; D <= 64 for bf16 on the
- * general path; I and B*H at most 65535); n_key_tiles in [1, N]; alignment; out
- * overlapping an input.  A failed allocation or launch returns TRI_ATTN_ERR_HIP and
- * records the HIP error code for tri_attn_last_hip_error() (per calling thread).
+ * (D <= 64; the matrix-core path serves bf16 with D == 32, every other case runs on
+ * the general fp32 path); I and B*H at most 65535; n_key_tiles in [1, N]; I == N for
+ * the ending orientation; the key range of tri_attn_tile_state; alignment; an output
+ * overlapping an input or another output.  A failed allocation or launch returns
+ * TRI_ATTN_ERR_HIP and records the HIP error code for tri_attn_last_hip_error() (per
+ * calling thread).
  */
 #ifndef TRI_ATTN_H
 #define TRI_ATTN_H
@@ -76,12 +78,14 @@ typedef enum {
     TRI_ATTN_ERR_NULL = -1,         /* a required pointer is NULL */
     TRI_ATTN_ERR_SHAPE = -2,        /* a size < 1, I > N, or a size overflows int64 */
     TRI_ATTN_ERR_DTYPE = -3,        /* dtype is not a tri_attn_dtype */
-    TRI_ATTN_ERR_UNSUPPORTED = -4,  /* D > 64, or I or B*H above 65535 */
+    TRI_ATTN_ERR_UNSUPPORTED = -4,  /* D > 64, I or B*H above 65535, or (ending node, bf16,
+                                       D == 32) 32 * N * H * D * 2 above 2^31 - 1 */
     TRI_ATTN_ERR_ALIGN = -5,        /* a pointer is not aligned as required */
     TRI_ATTN_ERR_TILES = -6,        /* n_key_tiles outside [1, N] */
     TRI_ATTN_ERR_HIP = -7,          /* the HIP runtime refused an allocation or launch */
-    TRI_ATTN_ERR_ALIAS = -8,        /* out (or the workspace) overlaps an input */
-    TRI_ATTN_ERR_WORKSPACE = -9     /* caller workspace smaller than tri_attn_workspace_bytes() */
+    TRI_ATTN_ERR_ALIAS = -8,        /* an output (or the workspace) overlaps an input or another output */
+    TRI_ATTN_ERR_WORKSPACE = -9,    /* caller workspace smaller than tri_attn_workspace_bytes() */
+    TRI_ATTN_ERR_RANGE = -10        /* key range not within 0 <= key_begin < key_end <= N */
 } tri_attn_status;
 
 /*
@@ -130,6 +134,92 @@ int tri_attn_fwd_rows_ws(const void *q, const void *k, const void *v, const void
                          int64_t B, int64_t H, int64_t I, int64_t N, int64_t D,
                          int32_t n_key_tiles, int32_t dtype,
                          void *workspace, int64_t workspace_bytes, void *stream);
+
+/*
+ * Forward that also returns the natural-log normaliser of every query,
+ *     lse[b,i,j,h] = ln sum_k exp(s_k)       (-inf for a query with no finite score),
+ * the statistic a backward pass recomputes the probabilities from (p_k = exp(s_k - lse)).
+ * Arguments as tri_attn_fwd_rows; lse is device binary32 [B, I, N, H], 4-byte aligned,
+ * and must not overlap any input or out.
+ */
+int tri_attn_fwd_lse(const void *q, const void *k, const void *v, const void *bias,
+                     const float *mask, float *out, float *lse,
+                     int64_t B, int64_t H, int64_t I, int64_t N, int64_t D,
+                     int32_t n_key_tiles, int32_t dtype, void *stream);
+
+/*
+ * Ending-node orientation: attention along the columns of the pair tensor, with the
+ * triangular bias transposed ("Fold-CP", Figure 2(a): the bias is transposed across
+ * axes before the ring).  For every b, i, j, h:
+ *     s_k            = q[b,i,j,h,:] . k[b,k,j,h,:] / sqrt(D) + bias[b,h,k,i] + mask[b,k]
+ *     out[b,i,j,h,:] = sum_k softmax_k(s)_k * v[b,k,j,h,:]
+ * i.e. the starting-node operation on the tensors with their first two pair axes
+ * swapped (and the bias's last two), without moving any data.  Same layouts, tiling,
+ * numerics and rules as tri_attn_fwd (I == N); lse is optional ([B, N, N, H] or NULL).
+ */
+int tri_attn_fwd_ending(const void *q, const void *k, const void *v, const void *bias,
+                        const float *mask, float *out, float *lse,
+                        int64_t B, int64_t H, int64_t N, int64_t D,
+                        int32_t n_key_tiles, int32_t dtype, void *stream);
+
+/*
+ * Split-tile primitive: the partial softmax state of one ring step, the keys
+ * [key_begin, key_end) taken as a single tile ("Fold-CP", Table 1's caption and
+ * Figure 2(a)/(c): each ring step's tile is computed on its own and joined by the
+ * tiled-softmax merge).  For every query (b, i, j, h) of the orientation chosen by
+ * `ending` (0: starting node, rows i in [0, I); 1: ending node, I == N):
+ *     m   = a reference in natural-log units (any value; the GPU takes the maximum of
+ *           the range's first 32-key block, or the running maximum)
+ *     l   = sum_k exp(s_k - m)                          over the key range
+ *     acc = sum_k exp(s_k - m) * v_k                    [D] values, unnormalised
+ * A query with no finite score in the range gets m = -inf, l = 0, acc = 0 (the
+ * identity of the merge).  acc is device binary32 [B, I, N, H, D] (16-byte aligned),
+ * m and l device binary32 [B, I, N, H] (4-byte aligned); none may overlap an input or
+ * each other.  Other arguments and rules as tri_attn_fwd_rows.  Extra error:
+ * TRI_ATTN_ERR_RANGE.  States are joined with tri_attn_state_merge and turned into the
+ * output with tri_attn_state_finalize; merging every tile of a partition of [0, N) in
+ * any order gives tri_attn_fwd's result up to rounding.
+ */
+int tri_attn_tile_state(const void *q, const void *k, const void *v, const void *bias,
+                        const float *mask, float *acc, float *m, float *l,
+                        int64_t B, int64_t H, int64_t I, int64_t N, int64_t D,
+                        int64_t key_begin, int64_t key_end, int32_t ending,
+                        int32_t dtype, void *stream);
+
+/*
+ * The merge of two partial states, in place into the first, for `rows` queries of D
+ * values (rows = B * I * N * H for the states above; 1 <= D <= 64):
+ *     M = max(m, m_t);  a = exp(m - M), b = exp(m_t - M)
+ *     acc = a * acc + b * acc_t;  l = a * l + b * l_t;  m = M
+ * where a state with l == 0 contributes nothing.  All pointers are device binary32,
+ * 4-byte aligned; acc, m, l must not overlap acc_t, m_t, l_t.
+ */
+int tri_attn_state_merge(float *acc, float *m, float *l,
+                         const float *acc_t, const float *m_t, const float *l_t,
+                         int64_t rows, int64_t D, void *stream);
+
+/*
+ * out = acc / l (0 where l == 0) and, when lse is not NULL, lse = m + ln l (-inf where
+ * l == 0), for `rows` queries of D values.  out [rows, D] and lse [rows] are device
+ * binary32, 4-byte aligned, and must not overlap the state or each other.
+ */
+int tri_attn_state_finalize(const float *acc, const float *m, const float *l,
+                            float *out, float *lse, int64_t rows, int64_t D, void *stream);
+
+/*
+ * Attention with pair bias ("Fold-CP", Table 1 row "Attention with Pair Bias", and
+ * Figure 2(c)): one sequence of N tokens per batch element, biased by the pair
+ * representation,
+ *     s_k            = q[b,j,h,:] . k[b,k,h,:] / sqrt(D) + bias[b,h,j,k] + mask[b,k]
+ *     out[b,j,h,:]   = sum_k softmax_k(s)_k * v[b,k,h,:]
+ * q, k, v, out [B, N, H, D]; bias [B, H, N, N]; mask [B, N] or NULL; lse [B, N, H] or
+ * NULL.  It is the triangle operation with a single row (I == 1), with the same tiling,
+ * numerics and rules.
+ */
+int pair_bias_attn_fwd(const void *q, const void *k, const void *v, const void *bias,
+                       const float *mask, float *out, float *lse,
+                       int64_t B, int64_t H, int64_t N, int64_t D,
+                       int32_t n_key_tiles, int32_t dtype, void *stream);
 
 /* Static, NUL-terminated description of a tri_attn_status (unknown codes included). */
 const char *tri_attn_status_string(int status);

@@ -28,6 +28,17 @@
  * additive [B,N] term over the key index; a tile whose keys are all -inf is the
  * identity of the merge; a row with no finite score gives out = 0 and lse = -inf.
  *
+ * Ending-node orientation (oracle_tri_attn_ending): Figure 2(a) transposes the pair
+ * tensor across its axes before the ring; read plainly, the same attention then runs
+ * along columns with the triangular bias transposed:
+ *
+ *   s_k = (1/sqrt(D)) * sum_d q[b,i,j,h,d] * k[b,k,j,h,d] + bias[b,h,k,i] + mask[b,k]
+ *   out[b,i,j,h,:] = sum_k softmax_k(s)_k * v[b,k,j,h,:]
+ *
+ * Split tiles (oracle_tile_state): one ring step's own softmax state over a key range,
+ * (m_t, l_t, a_t) above with m_t the range's maximum score, unnormalised -- the
+ * quantity a rank holds between the ring steps of Figure 2(a).
+ *
  * All arithmetic is IEEE double, libm exp/log/sqrt, no fast-math and no contraction
  * (built with -ffp-contract=off).  Inputs are widened exactly: binary32 as is,
  * bfloat16 as the upper half of a binary32.
@@ -71,28 +82,33 @@ void oracle_even_tiles(int64_t N, int64_t T, int64_t *starts)
 }
 
 /*
- * q, k, v:   [B, I, N, H, D] of dtype;  bias: [B, H, N, N] of dtype;
- * mask:      [B, N] binary32 additive, or NULL;
- * tile_start: T+1 increasing key offsets, tile_start[0] = 0, tile_start[T] = N;
- * first_tile: the ring step that runs first (tiles taken first_tile, first_tile+1, ... mod T);
- * rows:      n_rows flat row indices (b*I + i)*N + j, or NULL for all B*I*N rows in order;
- * out:       [n_rows, H, D] doubles;  lse: [n_rows, H] doubles (log-sum-exp of the scores), or NULL.
- * Returns 0, or a negative code for bad arguments / no memory.
+ * Shared body.  ending == 0: starting node (rows i in [0, I)); ending == 1: ending node
+ * (I == N).  The tiles tile_start[0] < ... < tile_start[T] cover the keys taken into
+ * account (all N keys for a forward; one range for a state).  state == 0: out and lse
+ * receive the normalised result; state == 1: out receives the unnormalised accumulator
+ * a and lse the pair (m, l) as [.., H, 2], the merged state of the tiles with m the
+ * running maximum (m = -inf, l = 0, a = 0 when no score is finite).
  */
-int oracle_tri_attn(const void *q, const void *k, const void *v, const void *bias,
-                    const float *mask, int dtype,
-                    int64_t B, int64_t H, int64_t I, int64_t N, int64_t D,
-                    const int64_t *tile_start, int64_t T, int64_t first_tile,
-                    const int64_t *rows, int64_t n_rows,
-                    double *out, double *lse)
+static int tri_attn_impl(const void *q, const void *k, const void *v, const void *bias,
+                         const float *mask, int dtype,
+                         int64_t B, int64_t H, int64_t I, int64_t N, int64_t D,
+                         const int64_t *tile_start, int64_t T, int64_t first_tile,
+                         const int64_t *rows, int64_t n_rows,
+                         double *out, double *lse, int ending, int state)
 {
     if (!q || !k || !v || !bias || !out || !tile_start)
         return ORACLE_ERR_ARG;
     if (B < 1 || H < 1 || I < 1 || N < 1 || D < 1 || I > N || T < 1 || T > N)
         return ORACLE_ERR_ARG;
+    if (ending && I != N)
+        return ORACLE_ERR_ARG;
+    if (state && !lse)
+        return ORACLE_ERR_ARG;
     if (dtype != ORACLE_DTYPE_FP32 && dtype != ORACLE_DTYPE_BF16)
         return ORACLE_ERR_ARG;
-    if (tile_start[0] != 0 || tile_start[T] != N || first_tile < 0 || first_tile >= T)
+    if (tile_start[0] < 0 || tile_start[T] > N || first_tile < 0 || first_tile >= T)
+        return ORACLE_ERR_ARG;
+    if (!state && (tile_start[0] != 0 || tile_start[T] != N))
         return ORACLE_ERR_ARG;
     int64_t widest = 0;
     for (int64_t t = 0; t < T; ++t) {
@@ -127,10 +143,9 @@ int oracle_tri_attn(const void *q, const void *k, const void *v, const void *bia
             const int64_t flat = rows ? rows[r] : r;
             const int64_t j = flat % N;
             const int64_t bi = flat / N;        /* b*I + i */
-            const int64_t b = bi / I;
+            const int64_t b = bi / I, i = bi % I;
             for (int64_t h = 0; h < H; ++h) {
                 const int64_t q_off = ((bi * N + j) * H + h) * D;
-                const int64_t bias_row = ((b * H + h) * N + j) * N;
                 double m = -INFINITY, l = 0.0;
                 for (int64_t d = 0; d < D; ++d)
                     a[d] = 0.0;
@@ -140,11 +155,16 @@ int oracle_tri_attn(const void *q, const void *k, const void *v, const void *bia
                     /* scores of this key tile and their maximum */
                     double m_t = -INFINITY;
                     for (int64_t kk = k0; kk < k1; ++kk) {
-                        const int64_t k_off = ((bi * N + kk) * H + h) * D;
+                        /* starting node: key (i, kk), bias[b,h,j,kk];
+                         * ending node:   key (kk, j), bias[b,h,kk,i] */
+                        const int64_t k_off = ending ? (((b * N + kk) * N + j) * H + h) * D
+                                                     : ((bi * N + kk) * H + h) * D;
+                        const int64_t b_off = ending ? ((b * H + h) * N + kk) * N + i
+                                                     : ((b * H + h) * N + j) * N + kk;
                         double dot = 0.0;
                         for (int64_t d = 0; d < D; ++d)
                             dot += widen(q, q_off + d, dtype) * widen(k, k_off + d, dtype);
-                        double sc = dot * inv_sqrt_d + widen(bias, bias_row + kk, dtype);
+                        double sc = dot * inv_sqrt_d + widen(bias, b_off, dtype);
                         if (mask)
                             sc += (double)mask[b * N + kk];
                         s[kk - k0] = sc;
@@ -159,7 +179,8 @@ int oracle_tri_attn(const void *q, const void *k, const void *v, const void *bia
                         a_t[d] = 0.0;
                     for (int64_t kk = k0; kk < k1; ++kk) {
                         const double w = exp(s[kk - k0] - m_t);
-                        const int64_t v_off = ((bi * N + kk) * H + h) * D;
+                        const int64_t v_off = ending ? (((b * N + kk) * N + j) * H + h) * D
+                                                     : ((bi * N + kk) * H + h) * D;
                         l_t += w;
                         for (int64_t d = 0; d < D; ++d)
                             a_t[d] += w * widen(v, v_off + d, dtype);
@@ -174,6 +195,13 @@ int oracle_tri_attn(const void *q, const void *k, const void *v, const void *bia
                     m = M;
                 }
                 double *o = out + (r * H + h) * D;
+                if (state) {
+                    for (int64_t d = 0; d < D; ++d)
+                        o[d] = a[d];
+                    lse[(r * H + h) * 2] = m;
+                    lse[(r * H + h) * 2 + 1] = l;
+                    continue;
+                }
                 for (int64_t d = 0; d < D; ++d)
                     o[d] = (l > 0.0) ? a[d] / l : 0.0;
                 if (lse)
@@ -185,4 +213,59 @@ int oracle_tri_attn(const void *q, const void *k, const void *v, const void *bia
         free(a_t);
     }
     return failed ? ORACLE_ERR_NOMEM : ORACLE_OK;
+}
+
+/*
+ * Starting-node triangle attention.
+ * q, k, v:   [B, I, N, H, D] of dtype;  bias: [B, H, N, N] of dtype;
+ * mask:      [B, N] binary32 additive, or NULL;
+ * tile_start: T+1 increasing key offsets, tile_start[0] = 0, tile_start[T] = N;
+ * first_tile: the ring step that runs first (tiles taken first_tile, first_tile+1, ... mod T);
+ * rows:      n_rows flat row indices (b*I + i)*N + j, or NULL for all B*I*N rows in order;
+ * out:       [n_rows, H, D] doubles;  lse: [n_rows, H] doubles (log-sum-exp of the scores), or NULL.
+ * Returns 0, or a negative code for bad arguments / no memory.
+ */
+int oracle_tri_attn(const void *q, const void *k, const void *v, const void *bias,
+                    const float *mask, int dtype,
+                    int64_t B, int64_t H, int64_t I, int64_t N, int64_t D,
+                    const int64_t *tile_start, int64_t T, int64_t first_tile,
+                    const int64_t *rows, int64_t n_rows,
+                    double *out, double *lse)
+{
+    return tri_attn_impl(q, k, v, bias, mask, dtype, B, H, I, N, D, tile_start, T, first_tile,
+                         rows, n_rows, out, lse, 0, 0);
+}
+
+/*
+ * Ending-node triangle attention; q, k, v [B, N, N, H, D], flat rows (b*N + i)*N + j,
+ * everything else as oracle_tri_attn.
+ */
+int oracle_tri_attn_ending(const void *q, const void *k, const void *v, const void *bias,
+                           const float *mask, int dtype,
+                           int64_t B, int64_t H, int64_t N, int64_t D,
+                           const int64_t *tile_start, int64_t T, int64_t first_tile,
+                           const int64_t *rows, int64_t n_rows,
+                           double *out, double *lse)
+{
+    return tri_attn_impl(q, k, v, bias, mask, dtype, B, H, N, N, D, tile_start, T, first_tile,
+                         rows, n_rows, out, lse, 1, 0);
+}
+
+/*
+ * Softmax state of the keys [key_begin, key_end) as one tile, for either orientation
+ * (ending = 0 or 1): acc [n_rows, H, D] receives a_t, ml [n_rows, H, 2] the pair
+ * (m_t, l_t); m_t is the range's maximum score.
+ */
+int oracle_tile_state(const void *q, const void *k, const void *v, const void *bias,
+                      const float *mask, int dtype,
+                      int64_t B, int64_t H, int64_t I, int64_t N, int64_t D,
+                      int64_t key_begin, int64_t key_end, int ending,
+                      const int64_t *rows, int64_t n_rows,
+                      double *acc, double *ml)
+{
+    if (key_begin < 0 || key_end > N || key_begin >= key_end)
+        return ORACLE_ERR_ARG;
+    const int64_t range[2] = {key_begin, key_end};
+    return tri_attn_impl(q, k, v, bias, mask, dtype, B, H, I, N, D, range, 1, 0,
+                         rows, n_rows, acc, ml, ending != 0, 1);
 }

@@ -20,8 +20,11 @@ STATUS = {
     0: "TRI_ATTN_OK", -1: "TRI_ATTN_ERR_NULL", -2: "TRI_ATTN_ERR_SHAPE", -3: "TRI_ATTN_ERR_DTYPE",
     -4: "TRI_ATTN_ERR_UNSUPPORTED", -5: "TRI_ATTN_ERR_ALIGN", -6: "TRI_ATTN_ERR_TILES",
     -7: "TRI_ATTN_ERR_HIP", -8: "TRI_ATTN_ERR_ALIAS", -9: "TRI_ATTN_ERR_WORKSPACE",
+    -10: "TRI_ATTN_ERR_RANGE",
 }
 EXPORTS = ("tri_attn_fwd", "tri_attn_fwd_rows", "tri_attn_fwd_rows_ws", "tri_attn_workspace_bytes",
+           "tri_attn_fwd_lse", "tri_attn_fwd_ending", "tri_attn_tile_state", "tri_attn_state_merge",
+           "tri_attn_state_finalize", "pair_bias_attn_fwd",
            "tri_attn_status_string", "tri_attn_last_hip_error", "tri_attn_version")
 
 
@@ -48,6 +51,19 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         L.tri_attn_fwd_rows.restype = ctypes.c_int
         L.tri_attn_fwd_rows_ws.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, i32, vp, i64, vp]
         L.tri_attn_fwd_rows_ws.restype = ctypes.c_int
+        L.tri_attn_fwd_lse.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, i32, vp]
+        L.tri_attn_fwd_lse.restype = ctypes.c_int
+        L.tri_attn_fwd_ending.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, vp]
+        L.tri_attn_fwd_ending.restype = ctypes.c_int
+        L.tri_attn_tile_state.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64,
+                                          i32, i32, vp]
+        L.tri_attn_tile_state.restype = ctypes.c_int
+        L.tri_attn_state_merge.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, vp]
+        L.tri_attn_state_merge.restype = ctypes.c_int
+        L.tri_attn_state_finalize.argtypes = [vp, vp, vp, vp, vp, i64, i64, vp]
+        L.tri_attn_state_finalize.restype = ctypes.c_int
+        L.pair_bias_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, vp]
+        L.pair_bias_attn_fwd.restype = ctypes.c_int
         L.tri_attn_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i32, i32]
         L.tri_attn_workspace_bytes.restype = ctypes.c_int64
         L.tri_attn_status_string.argtypes = [ctypes.c_int]
@@ -165,3 +181,114 @@ def tri_attn_fwd_rows_ws(q, k, v, bias, mask=None, *, workspace, n_key_tiles: in
                                   B, H, I, N, D, int(n_key_tiles), dt, _ptr(workspace), nbytes,
                                   _stream_handle(stream)))
     return out
+
+
+def _per_query(out, shape, name, t):
+    """Check or allocate a float32 per-query array (one value per (b, ..., h))."""
+    import torch
+    if t is None:
+        return torch.empty(shape, dtype=torch.float32, device=out.device)
+    if t.dtype != torch.float32 or tuple(t.shape) != tuple(shape) or not t.is_contiguous() or not t.is_cuda:
+        raise ValueError(f"{name} must be a contiguous float32 device tensor of shape {tuple(shape)}")
+    return t
+
+
+def tri_attn_fwd_lse(q, k, v, bias, mask=None, *, n_key_tiles: int = 1, out=None, lse=None, stream=None):
+    """tri_attn_fwd_rows that also returns lse [B, I, N, H] (natural-log normaliser of every
+    query; -inf where no key survives).  Returns (out, lse).  Calls tri_attn_fwd_lse."""
+    L = load_library()
+    dt, out = _validate(q, k, v, bias, mask, out)
+    B, I, N, H, D = q.shape
+    lse = _per_query(out, (B, I, N, H), "lse", lse)
+    _check(L.tri_attn_fwd_lse(_ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(mask), _ptr(out), _ptr(lse),
+                              B, H, I, N, D, int(n_key_tiles), dt, _stream_handle(stream)))
+    return out, lse
+
+
+def tri_attn_fwd_ending(q, k, v, bias, mask=None, *, n_key_tiles: int = 1, out=None, lse=None,
+                        want_lse: bool = False, stream=None):
+    """Ending-node triangle attention (attention along columns, bias transposed):
+    out[b,i,j] = sum_k softmax_k(q[b,i,j].k[b,k,j]/sqrt(D) + bias[b,h,k,i] + mask[b,k]) v[b,k,j].
+    q, k, v: [B, N, N, H, D].  Returns out, or (out, lse) when want_lse or lse is given.
+    Calls tri_attn_fwd_ending."""
+    L = load_library()
+    if q.dim() != 5 or q.shape[1] != q.shape[2]:
+        raise ValueError("tri_attn_fwd_ending needs q of shape [B, N, N, H, D]")
+    dt, out = _validate(q, k, v, bias, mask, out)
+    B, _, N, H, D = q.shape
+    if want_lse or lse is not None:
+        lse = _per_query(out, (B, N, N, H), "lse", lse)
+    _check(L.tri_attn_fwd_ending(_ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(mask), _ptr(out), _ptr(lse),
+                                 B, H, N, D, int(n_key_tiles), dt, _stream_handle(stream)))
+    return (out, lse) if lse is not None else out
+
+
+def tri_attn_tile_state(q, k, v, bias, mask=None, *, key_begin: int, key_end: int, ending: bool = False,
+                        acc=None, m=None, l=None, stream=None):
+    """Partial softmax state of the keys [key_begin, key_end) as one ring step: returns
+    (acc [B, I, N, H, D] unnormalised, m [B, I, N, H] reference, l [B, I, N, H] normaliser).
+    Calls tri_attn_tile_state."""
+    L = load_library()
+    dt, acc = _validate(q, k, v, bias, mask, acc)
+    B, I, N, H, D = q.shape
+    m = _per_query(acc, (B, I, N, H), "m", m)
+    l = _per_query(acc, (B, I, N, H), "l", l)
+    _check(L.tri_attn_tile_state(_ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(mask), _ptr(acc), _ptr(m), _ptr(l),
+                                 B, H, I, N, D, int(key_begin), int(key_end), int(bool(ending)), dt,
+                                 _stream_handle(stream)))
+    return acc, m, l
+
+
+def _state_shape(acc, m, l):
+    import torch
+    for name, t in (("acc", acc), ("m", m), ("l", l)):
+        if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float32 device tensor")
+    if tuple(m.shape) != tuple(acc.shape[:-1]) or tuple(l.shape) != tuple(m.shape):
+        raise ValueError("m and l must have acc's shape without its last axis")
+    return m.numel(), acc.shape[-1]
+
+
+def tri_attn_state_merge(acc, m, l, acc_t, m_t, l_t, *, stream=None):
+    """Merge the state (acc_t, m_t, l_t) into (acc, m, l) in place.  Calls tri_attn_state_merge."""
+    L = load_library()
+    rows, D = _state_shape(acc, m, l)
+    if _state_shape(acc_t, m_t, l_t) != (rows, D) or acc_t.shape != acc.shape:
+        raise ValueError("both states must have the same shapes")
+    _check(L.tri_attn_state_merge(_ptr(acc), _ptr(m), _ptr(l), _ptr(acc_t), _ptr(m_t), _ptr(l_t), rows, D,
+                                  _stream_handle(stream)))
+    return acc, m, l
+
+
+def tri_attn_state_finalize(acc, m, l, *, out=None, lse=None, stream=None):
+    """out = acc / l (0 where l == 0) and lse = m + ln l.  Returns (out, lse).
+    Calls tri_attn_state_finalize."""
+    import torch
+    L = load_library()
+    rows, D = _state_shape(acc, m, l)
+    if out is None:
+        out = torch.empty_like(acc)
+    if lse is None:
+        lse = torch.empty_like(m)
+    _check(L.tri_attn_state_finalize(_ptr(acc), _ptr(m), _ptr(l), _ptr(out), _ptr(lse), rows, D,
+                                     _stream_handle(stream)))
+    return out, lse
+
+
+def pair_bias_attn_fwd(q, k, v, bias, mask=None, *, n_key_tiles: int = 1, out=None, lse=None,
+                       want_lse: bool = False, stream=None):
+    """Attention with pair bias: q, k, v [B, N, H, D], bias [B, H, N, N], mask [B, N] or None.
+    Returns out [B, N, H, D] float32, or (out, lse [B, N, H]).  Calls pair_bias_attn_fwd."""
+    L = load_library()
+    if q.dim() != 4:
+        raise ValueError("pair_bias_attn_fwd needs q, k, v of shape [B, N, H, D]")
+    B, N, H, D = q.shape
+    q5, k5, v5 = (t.view(B, 1, N, H, D) for t in (q, k, v))
+    out5 = None if out is None else out.view(B, 1, N, H, D)
+    dt, out5 = _validate(q5, k5, v5, bias, mask, out5)
+    if want_lse or lse is not None:
+        lse = _per_query(out5, (B, N, H), "lse", lse)
+    _check(L.pair_bias_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(mask), _ptr(out5), _ptr(lse),
+                                B, H, N, D, int(n_key_tiles), dt, _stream_handle(stream)))
+    out = out5.view(B, N, H, D)
+    return (out, lse) if lse is not None else out

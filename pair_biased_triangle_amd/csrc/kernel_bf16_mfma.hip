@@ -140,20 +140,22 @@ constexpr int IMG_THR = 256;
 __global__ void __launch_bounds__(IMG_THR) bias_image_kernel(Problem p, float* img, int n_jb, int nblk) {
     const int n = blockIdx.x, jb = blockIdx.y, bh = blockIdx.z;
     const int64_t b = bh / p.H;
-    const KeyBlock kbk = BlockPlan(p.N, p.T).block(n);
+    const KeyBlock kbk = BlockPlan(p.nkeys(), p.T).block(n);
+    const int64_t key0 = p.k0 + kbk.kb;        // absolute index of the block's first key
     const uint16_t* bg = static_cast<const uint16_t*>(p.bias);
     float* dst = img + ((static_cast<int64_t>(bh) * n_jb + jb) * nblk + n) * IMG_FLOATS;
     const int kk = threadIdx.x % BK;
     const bool key_ok = kk < kbk.nk;
-    const float mk = (p.mask && key_ok) ? p.mask[b * p.N + kbk.kb + kk] : 0.0f;
+    const float mk = (p.mask && key_ok) ? p.mask[b * p.N + key0 + kk] : 0.0f;
 #pragma unroll
     for (int s = 0; s < IMG_FLOATS / IMG_THR; ++s) {
         const int jj = (threadIdx.x + s * IMG_THR) / BK;
         const int64_t j = static_cast<int64_t>(jb) * BJ + jj;
         float val = -INFINITY;
         if (key_ok) {
-            const float bv = j < p.N ? __uint_as_float(static_cast<uint32_t>(bg[(bh * p.N + j) * p.N + kbk.kb + kk]) << 16)
-                                     : 0.0f;
+            // starting node bias[b, h, j, key]; ending node the transpose, bias[b, h, key, j]
+            const int64_t bi = p.ending ? (bh * p.N + key0 + kk) * p.N + j : (bh * p.N + j) * p.N + key0 + kk;
+            const float bv = j < p.N ? __uint_as_float(static_cast<uint32_t>(bg[bi]) << 16) : 0.0f;
             val = (bv + mk) * kSqrtD;
         }
         dst[jj * BK + bias_chunk(jj, kk / 4) * 4 + kk % 4] = val;
@@ -164,13 +166,13 @@ __global__ void __launch_bounds__(IMG_THR) bias_image_kernel(Problem p, float* i
 // 2. attention
 // ---------------------------------------------------------------------------------------
 struct Ctx {
-    const char* k_row;      // K of this wave's staged row: &k[b, i, 0, h, 0]
+    const char* k_row;      // K of this wave's staged line at the first key of the range
     const char* v_row;
     const float* img_wg;    // this workgroup's bias tiles, nblk consecutive 128 x 32 tiles
-    int row_bytes;          // bytes between consecutive keys (H * D * 2)
+    int64_t key_bytes;      // bytes between consecutive keys of a line
     int key_local[2];       // key of this lane's 16-byte slot in the two 1 KB pieces
     int part_bytes[2];      // byte offset of the slot's logical 16-byte part inside the key
-    int last_key;           // N - 1
+    int last_key;           // index of the last key of the range
     BlockPlan plan;
 };
 
@@ -179,12 +181,15 @@ struct Ctx {
 __device__ __forceinline__ void stage_block(const Ctx& cx, int n, Stage& st, int wave, int lane) {
     const KeyBlock kbk = cx.plan.block(n);
     const int kb = static_cast<int>(kbk.kb);
+    const char* kbase = cx.k_row + kbk.kb * cx.key_bytes;
+    const char* vbase = cx.v_row + kbk.kb * cx.key_bytes;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-        const int key = min(kb + cx.key_local[half], cx.last_key);   // padded keys read a real key (bias -inf)
-        const int off = key * cx.row_bytes + cx.part_bytes[half];
-        __builtin_amdgcn_global_load_lds(GLOBAL_PTR(void, cx.k_row + off), LDS_PTR(void, &st.k[wave][16 * half][0]), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(GLOBAL_PTR(void, cx.v_row + off), LDS_PTR(void, &st.v[wave][16 * half][0]), 16, 0, 0);
+        // padded keys read a real key (their bias is -inf); offsets from the block's first key
+        const int rel = min(kb + cx.key_local[half], cx.last_key) - kb;
+        const int off = rel * static_cast<int>(cx.key_bytes) + cx.part_bytes[half];
+        __builtin_amdgcn_global_load_lds(GLOBAL_PTR(void, kbase + off), LDS_PTR(void, &st.k[wave][16 * half][0]), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(GLOBAL_PTR(void, vbase + off), LDS_PTR(void, &st.v[wave][16 * half][0]), 16, 0, 0);
     }
     const float* src = cx.img_wg + static_cast<int64_t>(n) * IMG_FLOATS + lane * 4;
     float* flat = &st.bias[0][0];
@@ -515,8 +520,8 @@ __device__ __forceinline__ void key_loop_exact(const Ctx& cx, const Lane& L, int
     for (int n = 0; n < nblk; ++n) key_step<true>(cx, L, wave, lane, qB, s, n, nblk);
 }
 
-__global__ void __launch_bounds__(NTHR) bf16_mfma_kernel(Problem p, const float* img, int n_jb, int n_rg, int nblk,
-                                                         int total) {
+__global__ void __launch_bounds__(NTHR) bf16_mfma_kernel(Problem p, Strides sd, const float* img, int n_jb, int n_rg,
+                                                         int nblk, int total) {
     // XCD-aware remap: XCD x (= hardware id mod 8) walks a contiguous range of logical ids.
     const int w = blockIdx.x;
     const int xcd = w % NXCD, slot = w / NXCD;
@@ -537,6 +542,8 @@ __global__ void __launch_bounds__(NTHR) bf16_mfma_kernel(Problem p, const float*
     const int jb = tile * TILE_JB + o2 % nj;
     const int64_t b = bh / p.H, h = bh % p.H;
     const int64_t i0 = static_cast<int64_t>(rg) * R, j0 = static_cast<int64_t>(jb) * BJ;
+    const int64_t lines = p.ending ? p.N : p.I;      // rows i, or columns j for the ending node
+    const int64_t bh_off = b * sd.batch + h * D;      // element offset of (b, line 0, query 0, h)
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;   // wave is uniform
@@ -546,20 +553,20 @@ __global__ void __launch_bounds__(NTHR) bf16_mfma_kernel(Problem p, const float*
 
     Ctx cx;
     {
-        int64_t i = i0 + wave;                       // the row this wave stages
-        i = i < p.I ? i : p.I - 1;                   // padded rows read a real row (never stored)
-        const int64_t row_off = ((b * p.I + i) * p.N * p.H + h) * D * 2;
+        int64_t i = i0 + wave;                       // the line this wave stages
+        i = i < lines ? i : lines - 1;               // padded lines read a real line (never stored)
+        const int64_t row_off = (bh_off + i * sd.line + p.k0 * sd.key) * 2;
         cx.k_row = static_cast<const char*>(p.k) + row_off;
         cx.v_row = static_cast<const char*>(p.v) + row_off;
         cx.img_wg = img + (static_cast<int64_t>(bh) * n_jb + jb) * nblk * IMG_FLOATS;
-        cx.row_bytes = static_cast<int>(p.H * D * 2);
+        cx.key_bytes = sd.key * 2;
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
             cx.key_local[half] = 16 * half + (lane >> 2);
             cx.part_bytes[half] = kv_chunk(cx.key_local[half], lane & 3) * 16;   // logical part at this slot
         }
-        cx.last_key = static_cast<int>(p.N - 1);
-        cx.plan = BlockPlan(p.N, p.T);
+        cx.last_key = static_cast<int>(p.nkeys() - 1);
+        cx.plan = BlockPlan(p.nkeys(), p.T);
     }
 
     // Q^T operands (B of S^T = K Q^T): query j = tile*32 + c, d = 16m + 8*h2 .. +7.
@@ -572,9 +579,9 @@ __global__ void __launch_bounds__(NTHR) bf16_mfma_kernel(Problem p, const float*
 #pragma unroll
             for (int m = 0; m < 2; ++m) {
                 bf16x8 z = {};
-                if (i < p.I && j < p.N)
-                    z = *reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(p.q) +
-                                                         (((b * p.I + i) * p.N + j) * p.H + h) * D + 16 * m + 8 * L.h2);
+                if (i < lines && j < p.N)
+                    z = *reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(p.q) + bh_off + i * sd.line +
+                                                         j * sd.query + 16 * m + 8 * L.h2);
                 qB[ri][ti][m] = z;
             }
         }
@@ -607,24 +614,37 @@ __global__ void __launch_bounds__(NTHR) bf16_mfma_kernel(Problem p, const float*
         key_loop_exact(cx, L, wave, lane, qB, s, nblk);
     }
 
-    // out = O / l; lanes l and l^32 hold disjoint keys of the same query.
+    // out = O / l; lanes l and l^32 hold disjoint keys of the same query.  In state mode
+    // out receives O itself, with the reference (m_ref / sqrt(D): S carries a factor
+    // sqrt(D)) and l; the log-sum-exp is m_ref / sqrt(D) + ln l.
+    const bool state = p.st_m != nullptr;
 #pragma unroll
     for (int ri = 0; ri < RW; ++ri)
 #pragma unroll
         for (int ti = 0; ti < TW; ++ti) {
             const float lt = s.lsum[ri][ti] + __shfl_xor(s.lsum[ri][ti], 32);
             const int64_t i = i0 + row0 + ri, j = j0 + (tile0 + ti) * 32 + L.c;
-            if (i < p.I && j < p.N) {
-                float* o = p.out + (((b * p.I + i) * p.N + j) * p.H + h) * D;
+            if (i < lines && j < p.N) {
+                const int64_t qo = bh_off + i * sd.line + j * sd.query;
+                float* o = p.out + qo;
                 // correctly rounded O / l: a single surviving key returns its v exactly
 #pragma unroll
                 for (int a = 0; a < 4; ++a) {
                     f32x4 x;
-                    x[0] = lt > 0.0f ? s.O[ri][ti][4 * a + 0] / lt : 0.0f;
-                    x[1] = lt > 0.0f ? s.O[ri][ti][4 * a + 1] / lt : 0.0f;
-                    x[2] = lt > 0.0f ? s.O[ri][ti][4 * a + 2] / lt : 0.0f;
-                    x[3] = lt > 0.0f ? s.O[ri][ti][4 * a + 3] / lt : 0.0f;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float acc = s.O[ri][ti][4 * a + e];
+                        x[e] = state ? acc : (lt > 0.0f ? acc / lt : 0.0f);
+                    }
                     *reinterpret_cast<f32x4*>(o + 8 * a + 4 * L.h2) = x;
+                }
+                const float mnat = s.mref[ri][ti] * (1.0f / kSqrtD);
+                if (L.h2 == 0) {
+                    if (state) {
+                        p.st_m[qo / D] = lt > 0.0f ? mnat : -INFINITY;
+                        p.st_l[qo / D] = lt;
+                    }
+                    if (p.lse) p.lse[qo / D] = lt > 0.0f ? mnat + logf(lt) : -INFINITY;
                 }
             }
         }
@@ -634,18 +654,19 @@ __global__ void __launch_bounds__(NTHR) bf16_mfma_kernel(Problem p, const float*
 
 size_t bf16_workspace_bytes(const Problem& p) {
     const int64_t n_jb = (p.N + BJ - 1) / BJ;
-    const int64_t nblk = BlockPlan(p.N, p.T).count();
+    const int64_t nblk = BlockPlan(p.nkeys(), p.T).count();
     return static_cast<size_t>(p.B * p.H * n_jb * nblk) * IMG_FLOATS * sizeof(float);
 }
 
 hipError_t launch_bf16_mfma(const Problem& p, void* workspace, hipStream_t stream) {
     const int64_t n_jb = (p.N + BJ - 1) / BJ;
-    const int64_t n_rg = (p.I + R - 1) / R;
-    const int64_t nblk = BlockPlan(p.N, p.T).count();
+    const int64_t n_rg = ((p.ending ? p.N : p.I) + R - 1) / R;
+    const int64_t nblk = BlockPlan(p.nkeys(), p.T).count();
+    const Strides sd = strides_of(p);
     const int64_t total = n_jb * n_rg * p.B * p.H;
-    // one (b, i) row of K or V is addressed with 32-bit byte offsets
+    // the 32 keys of a block are addressed with 32-bit byte offsets from the block's first key
     if (total > 0x7FFFFFFF || nblk > 0x7FFFFFFF || n_jb > 65535 || p.B * p.H > 65535 ||
-        p.N * p.H * D * 2 > 0x7FFFFFFF)
+        BK * sd.key * 2 > 0x7FFFFFFF)
         return hipErrorInvalidConfiguration;
     float* img = static_cast<float*>(workspace);
     hipLaunchKernelGGL(bias_image_kernel, dim3(static_cast<unsigned>(nblk), static_cast<unsigned>(n_jb),
@@ -653,7 +674,7 @@ hipError_t launch_bf16_mfma(const Problem& p, void* workspace, hipStream_t strea
                        dim3(IMG_THR), 0, stream, p, img, static_cast<int>(n_jb), static_cast<int>(nblk));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(bf16_mfma_kernel, dim3(static_cast<unsigned>(total)), dim3(NTHR), 0, stream, p, img,
+    hipLaunchKernelGGL(bf16_mfma_kernel, dim3(static_cast<unsigned>(total)), dim3(NTHR), 0, stream, p, sd, img,
                        static_cast<int>(n_jb), static_cast<int>(n_rg), static_cast<int>(nblk), static_cast<int>(total));
     return hipGetLastError();
 }

@@ -1,11 +1,14 @@
 // Plain fp32 triangle-attention kernel for any head size D <= 64 and fp32 or bf16 inputs.
 //
-// One workgroup covers 64 query columns j of one (b, i, h); each thread owns one query
+// One workgroup covers 64 queries of one (b, line, h) -- a line is a row i for the
+// starting node and a column j for the ending node; each thread owns one query
 // and keeps its q vector, running maximum, normaliser and fp32 accumulator in registers
 // (online softmax over key blocks; "Fold-CP", Figure 2(a): tiled-softmax merge).  Key
 // blocks of 32 never straddle a ring-step tile, so each tile is folded into the running
 // state exactly as one ring step would be.  K, V and the bias block (with the additive
-// key mask folded in) are staged through LDS.
+// key mask folded in) are staged through LDS.  The same kernel writes the log-sum-exp of
+// each query, or a key range's unnormalised partial state (accumulator, running maximum,
+// normaliser) for the split-tile entry points.
 #include "launch.h"
 
 #include <cmath>
@@ -27,14 +30,14 @@ __device__ __forceinline__ float load_elem(const void* base, int64_t idx) {
 }
 
 template <bool BF16, int DP>
-__global__ void __launch_bounds__(GJ) general_kernel(Problem p) {
-    const int64_t N = p.N, H = p.H, D = p.D, I = p.I;
-    const int64_t i = blockIdx.y;
+__global__ void __launch_bounds__(GJ) general_kernel(Problem p, Strides st) {
+    const int64_t N = p.N, H = p.H, D = p.D, NK = p.nkeys();
+    const int64_t r = blockIdx.y;                 // line (row i, or column j for the ending node)
     const int64_t b = blockIdx.z / H, h = blockIdx.z % H;
     const int64_t j0 = static_cast<int64_t>(blockIdx.x) * GJ;
     const int tid = threadIdx.x;
-    const int64_t j = j0 + tid;
-    const int64_t row = (b * I + i) * N;  // index of (b, i, j=0) in the [B, I, N] grid
+    const int64_t j = j0 + tid;                   // this thread's query
+    const int64_t line = b * st.batch + r * st.line + h * D;   // element offset of (b, line r, head h)
 
     __shared__ float Ks[GK][DP + 1];
     __shared__ float Vs[GK][DP + 1];
@@ -43,31 +46,32 @@ __global__ void __launch_bounds__(GJ) general_kernel(Problem p) {
     float q[DP], acc[DP];
 #pragma unroll
     for (int d = 0; d < DP; ++d) {
-        q[d] = (j < N && d < D) ? load_elem<BF16>(p.q, ((row + j) * H + h) * D + d) : 0.0f;
+        q[d] = (j < N && d < D) ? load_elem<BF16>(p.q, line + j * st.query + d) : 0.0f;
         acc[d] = 0.0f;
     }
     const float scale = 1.0f / sqrtf(static_cast<float>(D));
     float m = -INFINITY, l = 0.0f;
 
     for (int t = 0; t < p.T; ++t) {
-        const int64_t ks = tile_start(t, N, p.T), ke = tile_start(t + 1, N, p.T);
+        const int64_t ks = p.k0 + tile_start(t, NK, p.T), ke = p.k0 + tile_start(t + 1, NK, p.T);
         for (int64_t kb = ks; kb < ke; kb += GK) {
             const int nk = static_cast<int>(ke - kb < GK ? ke - kb : GK);
             __syncthreads();
             for (int e = tid; e < GK * DP; e += GJ) {
                 const int kk = e / DP, d = e % DP;
                 const bool ok = kk < nk && d < D;
-                const int64_t off = ((row + kb + kk) * H + h) * D + d;
+                const int64_t off = line + (kb + kk) * st.key + d;
                 Ks[kk][d] = ok ? load_elem<BF16>(p.k, off) : 0.0f;
                 Vs[kk][d] = ok ? load_elem<BF16>(p.v, off) : 0.0f;
             }
             for (int e = tid; e < GJ * GK; e += GJ) {
                 const int jj = e / GK, kk = e % GK;
-                const int64_t jg = j0 + jj;
+                const int64_t jg = j0 + jj, key = kb + kk;
                 float bv = -INFINITY;
                 if (kk < nk && jg < N) {
-                    bv = load_elem<BF16>(p.bias, ((b * H + h) * N + jg) * N + kb + kk);
-                    if (p.mask) bv += p.mask[b * N + kb + kk];
+                    const int64_t bi = p.ending ? ((b * H + h) * N + key) * N + jg : ((b * H + h) * N + jg) * N + key;
+                    bv = load_elem<BF16>(p.bias, bi);
+                    if (p.mask) bv += p.mask[b * N + key];
                 }
                 Bs[jj][kk] = bv;
             }
@@ -100,24 +104,37 @@ __global__ void __launch_bounds__(GJ) general_kernel(Problem p) {
         }
     }
     if (j < N) {
-        const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-        float* o = p.out + ((row + j) * H + h) * D;
+        const int64_t qo = line + j * st.query;   // element offset of this query's D values
+        const int64_t so = qo / D;                // offset in the [B, I, N, H] per-query arrays
+        float* o = p.out + qo;
+        if (p.st_m) {                             // partial state: unnormalised accumulator
 #pragma unroll
-        for (int d = 0; d < DP; ++d)
-            if (d < D) o[d] = acc[d] * inv;
+            for (int d = 0; d < DP; ++d)
+                if (d < D) o[d] = acc[d];
+            p.st_m[so] = m;
+            p.st_l[so] = l;
+        } else {
+            const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+#pragma unroll
+            for (int d = 0; d < DP; ++d)
+                if (d < D) o[d] = acc[d] * inv;
+        }
+        if (p.lse) p.lse[so] = l > 0.0f ? m + logf(l) : -INFINITY;
     }
 }
 
 template <bool BF16>
 hipError_t launch_dp(const Problem& p, hipStream_t stream) {
-    const dim3 grid(static_cast<unsigned>((p.N + GJ - 1) / GJ), static_cast<unsigned>(p.I),
+    // lines: I rows (starting node) or N columns (ending node, I == N)
+    const dim3 grid(static_cast<unsigned>((p.N + GJ - 1) / GJ), static_cast<unsigned>(p.ending ? p.N : p.I),
                     static_cast<unsigned>(p.B * p.H));
+    const Strides st = strides_of(p);
     if (p.D <= 16)
-        hipLaunchKernelGGL((general_kernel<BF16, 16>), grid, dim3(GJ), 0, stream, p);
+        hipLaunchKernelGGL((general_kernel<BF16, 16>), grid, dim3(GJ), 0, stream, p, st);
     else if (p.D <= 32)
-        hipLaunchKernelGGL((general_kernel<BF16, 32>), grid, dim3(GJ), 0, stream, p);
+        hipLaunchKernelGGL((general_kernel<BF16, 32>), grid, dim3(GJ), 0, stream, p, st);
     else
-        hipLaunchKernelGGL((general_kernel<BF16, 64>), grid, dim3(GJ), 0, stream, p);
+        hipLaunchKernelGGL((general_kernel<BF16, 64>), grid, dim3(GJ), 0, stream, p, st);
     return hipGetLastError();
 }
 

@@ -8,16 +8,41 @@
 namespace tri_attn {
 
 // One call's problem, already validated by the entry point.
+//
+// Orientation.  The kernels work on "lines": attention problems that share the key axis
+// with their queries.  Starting node: line r is row i, queries are columns j, keys the
+// entries (i, k) of the same row, bias[b, h, j, k].  Ending node: line r is column j,
+// queries are rows i, keys the entries (k, j) of the same column, bias[b, h, k, i] (the
+// bias transposed: "Fold-CP", Figure 2(a), cross-axis transpose).  Both use the same
+// kernels with different strides (Strides below); the ending node needs I == N.
 struct Problem {
     const void* q;
     const void* k;
     const void* v;
     const void* bias;
     const float* mask;   // may be null
-    float* out;
+    float* out;          // normalised output, or the unnormalised accumulator (state mode)
     int64_t B, H, I, N, D;
-    int32_t T;           // key tiles (ring steps)
+    int32_t T;           // key tiles (ring steps) over the key range
+    int64_t k0 = 0;      // key range [k0, k0 + NK) (one ring step's keys in state mode)
+    int64_t NK = 0;      //   NK == 0 means all N keys
+    bool ending = false; // ending-node orientation
+    float* lse = nullptr;   // optional [B, I, N, H]: natural-log normaliser of each query
+    float* st_m = nullptr;  // state mode when non-null: reference (natural-log units) ...
+    float* st_l = nullptr;  //   ... and normaliser of each query; out gets the accumulator
+    __host__ __device__ int64_t nkeys() const { return NK > 0 ? NK : N; }
 };
+
+// Element strides of q, k, v and out ([B, I, N, H, D] storage) for a line r, a query
+// and a key; lse, st_m and st_l use the same offsets divided by D.
+struct Strides {
+    int64_t batch, line, query, key;
+};
+__host__ __device__ inline Strides strides_of(const Problem& p) {
+    const int64_t HD = p.H * p.D;
+    if (p.ending) return Strides{p.N * p.N * HD, HD, p.N * HD, p.N * HD};
+    return Strides{p.I * p.N * HD, p.N * HD, HD, HD};
+}
 
 // bf16 inputs, D == 32: matrix-core kernels.  `workspace` (16-byte aligned, at least
 // bf16_workspace_bytes(p) bytes) receives the converted bias image.
@@ -26,6 +51,13 @@ hipError_t launch_bf16_mfma(const Problem& p, void* workspace, hipStream_t strea
 
 // Any D <= 64, fp32 or bf16 inputs: plain fp32 kernel.
 hipError_t launch_general(const Problem& p, bool bf16, hipStream_t stream);
+
+// Partial softmax states (state mode above), rows = B * I * N * H queries of D values:
+// (acc, m, l) <- merge((acc, m, l), (acc_t, m_t, l_t)), and out = acc / l, lse = m + ln l.
+hipError_t launch_state_merge(float* acc, float* m, float* l, const float* acc_t, const float* m_t,
+                              const float* l_t, int64_t rows, int64_t D, hipStream_t stream);
+hipError_t launch_state_finalize(const float* acc, const float* m, const float* l, float* out, float* lse,
+                                 int64_t rows, int64_t D, hipStream_t stream);
 
 // Start of key tile t when N keys are cut into T near-equal contiguous tiles
 // (the first N mod T tiles hold one key more).

@@ -49,29 +49,64 @@ int check_sizes(int64_t B, int64_t H, int64_t I, int64_t N, int64_t D, int32_t n
     // grid limits: the general kernel puts rows i and (b, h) on grid y and z, the matrix-core
     // kernels put column blocks and (b, h) on grid y and z of the bias conversion
     if (I > 65535 || B * H > 65535) return TRI_ATTN_ERR_UNSUPPORTED;
-    // the matrix-core kernels address one (b, i) row of K or V with 32-bit byte offsets
-    if (uses_matrix_cores(dtype, D) && N * H * D * 2 > INT32_MAX) return TRI_ATTN_ERR_UNSUPPORTED;
     if (n_key_tiles < 1 || n_key_tiles > N) return TRI_ATTN_ERR_TILES;
     return TRI_ATTN_OK;
 }
 
-int check_pointers(const void* q, const void* k, const void* v, const void* bias, const float* mask, float* out,
-                   int64_t B, int64_t N, int64_t qkv_elems, int64_t bias_elems, int32_t dtype) {
-    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(bias, 16) || !aligned(out, 16) ||
-        (mask && !aligned(mask, 4)))
+// Everything one entry point asks for.
+struct Call {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* bias;
+    const float* mask;
+    float* out;
+    int64_t B, H, I, N, D;
+    int32_t T, dtype;
+    int64_t key_begin = 0, key_end = -1;   // key range (state mode); -1: all keys
+    bool ending = false;
+    float* lse = nullptr;
+    float* st_m = nullptr;
+    float* st_l = nullptr;
+    void* ws = nullptr;                    // caller workspace when ws_bytes >= 0
+    int64_t ws_bytes = -1;
+};
+
+struct Span {
+    const void* p;
+    int64_t bytes;
+};
+
+int check_pointers(const Call& c, int64_t qkv_elems, int64_t bias_elems) {
+    if (!aligned(c.q, 16) || !aligned(c.k, 16) || !aligned(c.v, 16) || !aligned(c.bias, 16) || !aligned(c.out, 16) ||
+        (c.mask && !aligned(c.mask, 4)) || (c.lse && !aligned(c.lse, 4)) || (c.st_m && !aligned(c.st_m, 4)) ||
+        (c.st_l && !aligned(c.st_l, 4)))
         return TRI_ATTN_ERR_ALIGN;
-    const int64_t esz = dtype == TRI_ATTN_BF16 ? 2 : 4;
-    const int64_t out_bytes = qkv_elems * 4;
-    if (overlaps(out, out_bytes, q, qkv_elems * esz) || overlaps(out, out_bytes, k, qkv_elems * esz) ||
-        overlaps(out, out_bytes, v, qkv_elems * esz) || overlaps(out, out_bytes, bias, bias_elems * esz) ||
-        (mask && overlaps(out, out_bytes, mask, B * N * 4)))
-        return TRI_ATTN_ERR_ALIAS;
+    const int64_t esz = c.dtype == TRI_ATTN_BF16 ? 2 : 4;
+    const int64_t per_query = qkv_elems / c.D * 4;   // bytes of one fp32 value per query
+    const Span inputs[] = {{c.q, qkv_elems * esz}, {c.k, qkv_elems * esz}, {c.v, qkv_elems * esz},
+                           {c.bias, bias_elems * esz}, {c.mask, c.B * c.N * 4}};
+    const Span outputs[] = {{c.out, qkv_elems * 4}, {c.lse, per_query}, {c.st_m, per_query}, {c.st_l, per_query}};
+    for (int a = 0; a < 4; ++a) {
+        if (!outputs[a].p) continue;
+        for (const Span& in : inputs)
+            if (in.p && overlaps(outputs[a].p, outputs[a].bytes, in.p, in.bytes)) return TRI_ATTN_ERR_ALIAS;
+        for (int o = a + 1; o < 4; ++o)
+            if (outputs[o].p && overlaps(outputs[a].p, outputs[a].bytes, outputs[o].p, outputs[o].bytes))
+                return TRI_ATTN_ERR_ALIAS;
+    }
     return TRI_ATTN_OK;
 }
 
-tri_attn::Problem make_problem(const void* q, const void* k, const void* v, const void* bias, const float* mask,
-                               float* out, int64_t B, int64_t H, int64_t I, int64_t N, int64_t D, int32_t T) {
-    return tri_attn::Problem{q, k, v, bias, mask, out, B, H, I, N, D, T};
+tri_attn::Problem make_problem(const Call& c) {
+    tri_attn::Problem p{c.q, c.k, c.v, c.bias, c.mask, c.out, c.B, c.H, c.I, c.N, c.D, c.T};
+    p.k0 = c.key_begin;
+    p.NK = c.key_end >= 0 ? c.key_end - c.key_begin : 0;
+    p.ending = c.ending;
+    p.lse = c.lse;
+    p.st_m = c.st_m;
+    p.st_l = c.st_l;
+    return p;
 }
 
 // Stream-ordered memory pool of the library, one per device, created on first use.  Its
@@ -106,33 +141,40 @@ hipError_t workspace_pool(hipMemPool_t* out) {
     return hipSuccess;
 }
 
-// ws == nullptr && ws_bytes < 0: allocate the workspace stream-ordered on `stream`.
-int run(const void* q, const void* k, const void* v, const void* bias, const float* mask, float* out, int64_t B,
-        int64_t H, int64_t I, int64_t N, int64_t D, int32_t n_key_tiles, int32_t dtype, void* ws, int64_t ws_bytes,
-        void* stream) {
-    if (!q || !k || !v || !bias || !out) return TRI_ATTN_ERR_NULL;
+int run(const Call& c, void* stream) {
+    if (!c.q || !c.k || !c.v || !c.bias || !c.out) return TRI_ATTN_ERR_NULL;
+    if ((c.st_m == nullptr) != (c.st_l == nullptr)) return TRI_ATTN_ERR_NULL;
     int64_t qkv_elems = 0, bias_elems = 0;
-    int st = check_sizes(B, H, I, N, D, n_key_tiles, dtype, &qkv_elems, &bias_elems);
+    int st = check_sizes(c.B, c.H, c.I, c.N, c.D, c.T, c.dtype, &qkv_elems, &bias_elems);
     if (st != TRI_ATTN_OK) return st;
-    st = check_pointers(q, k, v, bias, mask, out, B, N, qkv_elems, bias_elems, dtype);
+    if (c.ending && c.I != c.N) return TRI_ATTN_ERR_SHAPE;
+    if (c.key_end >= 0 && !(0 <= c.key_begin && c.key_begin < c.key_end && c.key_end <= c.N))
+        return TRI_ATTN_ERR_RANGE;
+    // the matrix-core kernel addresses the 32 keys of a block with 32-bit byte offsets; in
+    // the ending orientation consecutive keys are N * H * D elements apart
+    if (uses_matrix_cores(c.dtype, c.D) && c.ending && 32 * c.N * c.H * c.D * 2 > INT32_MAX)
+        return TRI_ATTN_ERR_UNSUPPORTED;
+    st = check_pointers(c, qkv_elems, bias_elems);
     if (st != TRI_ATTN_OK) return st;
 
-    const tri_attn::Problem p = make_problem(q, k, v, bias, mask, out, B, H, I, N, D, n_key_tiles);
+    const tri_attn::Problem p = make_problem(c);
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    if (!uses_matrix_cores(dtype, D)) {
-        const hipError_t e = tri_attn::launch_general(p, dtype == TRI_ATTN_BF16, s);
+    if (!uses_matrix_cores(c.dtype, c.D)) {
+        const hipError_t e = tri_attn::launch_general(p, c.dtype == TRI_ATTN_BF16, s);
         return e == hipSuccess ? TRI_ATTN_OK : hip_fail(e);
     }
     const int64_t need = static_cast<int64_t>(tri_attn::bf16_workspace_bytes(p));
-    if (ws_bytes >= 0) {  // caller-provided workspace
-        if (!ws) return TRI_ATTN_ERR_NULL;
-        if (!aligned(ws, 16)) return TRI_ATTN_ERR_ALIGN;
-        if (ws_bytes < need) return TRI_ATTN_ERR_WORKSPACE;
-        if (overlaps(ws, need, out, qkv_elems * 4) || overlaps(ws, need, q, qkv_elems * 2) ||
-            overlaps(ws, need, k, qkv_elems * 2) || overlaps(ws, need, v, qkv_elems * 2) ||
-            overlaps(ws, need, bias, bias_elems * 2) || (mask && overlaps(ws, need, mask, B * N * 4)))
-            return TRI_ATTN_ERR_ALIAS;
-        const hipError_t e = tri_attn::launch_bf16_mfma(p, ws, s);
+    if (c.ws_bytes >= 0) {  // caller-provided workspace
+        if (!c.ws) return TRI_ATTN_ERR_NULL;
+        if (!aligned(c.ws, 16)) return TRI_ATTN_ERR_ALIGN;
+        if (c.ws_bytes < need) return TRI_ATTN_ERR_WORKSPACE;
+        const Span others[] = {{c.out, qkv_elems * 4}, {c.q, qkv_elems * 2},  {c.k, qkv_elems * 2},
+                               {c.v, qkv_elems * 2},   {c.bias, bias_elems * 2}, {c.mask, c.B * c.N * 4},
+                               {c.lse, qkv_elems / c.D * 4}, {c.st_m, qkv_elems / c.D * 4},
+                               {c.st_l, qkv_elems / c.D * 4}};
+        for (const Span& o : others)
+            if (o.p && overlaps(c.ws, need, o.p, o.bytes)) return TRI_ATTN_ERR_ALIAS;
+        const hipError_t e = tri_attn::launch_bf16_mfma(p, c.ws, s);
         return e == hipSuccess ? TRI_ATTN_OK : hip_fail(e);
     }
     hipMemPool_t pool = nullptr;
@@ -148,19 +190,33 @@ int run(const void* q, const void* k, const void* v, const void* bias, const flo
     return TRI_ATTN_OK;
 }
 
+Call make_call(const void* q, const void* k, const void* v, const void* bias, const float* mask, float* out, int64_t B,
+               int64_t H, int64_t I, int64_t N, int64_t D, int32_t T, int32_t dtype) {
+    Call c{q, k, v, bias, mask, out, B, H, I, N, D, T, dtype};
+    return c;
+}
+
+int check_state_args(const float* a, const float* b, const float* c, int64_t rows, int64_t D) {
+    if (!a || !b || !c) return TRI_ATTN_ERR_NULL;
+    int64_t t;
+    if (rows < 1 || D < 1 || D > 64 || !mul_ok(rows, D, &t) || !mul_ok(t, 4, &t)) return TRI_ATTN_ERR_SHAPE;
+    if (!aligned(a, 4) || !aligned(b, 4) || !aligned(c, 4)) return TRI_ATTN_ERR_ALIGN;
+    return TRI_ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
 int tri_attn_fwd(const void* q, const void* k, const void* v, const void* bias, const float* mask, float* out,
                  int64_t B, int64_t H, int64_t N, int64_t D, int32_t n_key_tiles, int32_t dtype, void* stream) {
-    return run(q, k, v, bias, mask, out, B, H, N, N, D, n_key_tiles, dtype, nullptr, -1, stream);
+    return run(make_call(q, k, v, bias, mask, out, B, H, N, N, D, n_key_tiles, dtype), stream);
 }
 
 int tri_attn_fwd_rows(const void* q, const void* k, const void* v, const void* bias, const float* mask, float* out,
                       int64_t B, int64_t H, int64_t I, int64_t N, int64_t D, int32_t n_key_tiles, int32_t dtype,
                       void* stream) {
-    return run(q, k, v, bias, mask, out, B, H, I, N, D, n_key_tiles, dtype, nullptr, -1, stream);
+    return run(make_call(q, k, v, bias, mask, out, B, H, I, N, D, n_key_tiles, dtype), stream);
 }
 
 int64_t tri_attn_workspace_bytes(int64_t B, int64_t H, int64_t I, int64_t N, int64_t D, int32_t n_key_tiles,
@@ -169,8 +225,8 @@ int64_t tri_attn_workspace_bytes(int64_t B, int64_t H, int64_t I, int64_t N, int
     const int st = check_sizes(B, H, I, N, D, n_key_tiles, dtype, &qkv_elems, &bias_elems);
     if (st != TRI_ATTN_OK) return st;
     if (!uses_matrix_cores(dtype, D)) return 0;
-    const tri_attn::Problem p = make_problem(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, B, H, I, N, D,
-                                             n_key_tiles);
+    const tri_attn::Problem p =
+        make_problem(make_call(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, B, H, I, N, D, n_key_tiles, dtype));
     return static_cast<int64_t>(tri_attn::bf16_workspace_bytes(p));
 }
 
@@ -178,7 +234,81 @@ int tri_attn_fwd_rows_ws(const void* q, const void* k, const void* v, const void
                          float* out, int64_t B, int64_t H, int64_t I, int64_t N, int64_t D, int32_t n_key_tiles,
                          int32_t dtype, void* workspace, int64_t workspace_bytes, void* stream) {
     if (workspace_bytes < 0) return TRI_ATTN_ERR_WORKSPACE;
-    return run(q, k, v, bias, mask, out, B, H, I, N, D, n_key_tiles, dtype, workspace, workspace_bytes, stream);
+    Call c = make_call(q, k, v, bias, mask, out, B, H, I, N, D, n_key_tiles, dtype);
+    c.ws = workspace;
+    c.ws_bytes = workspace_bytes;
+    return run(c, stream);
+}
+
+int tri_attn_fwd_lse(const void* q, const void* k, const void* v, const void* bias, const float* mask, float* out,
+                     float* lse, int64_t B, int64_t H, int64_t I, int64_t N, int64_t D, int32_t n_key_tiles,
+                     int32_t dtype, void* stream) {
+    if (!lse) return TRI_ATTN_ERR_NULL;
+    Call c = make_call(q, k, v, bias, mask, out, B, H, I, N, D, n_key_tiles, dtype);
+    c.lse = lse;
+    return run(c, stream);
+}
+
+int tri_attn_fwd_ending(const void* q, const void* k, const void* v, const void* bias, const float* mask,
+                        float* out, float* lse, int64_t B, int64_t H, int64_t N, int64_t D, int32_t n_key_tiles,
+                        int32_t dtype, void* stream) {
+    Call c = make_call(q, k, v, bias, mask, out, B, H, N, N, D, n_key_tiles, dtype);
+    c.ending = true;
+    c.lse = lse;
+    return run(c, stream);
+}
+
+int tri_attn_tile_state(const void* q, const void* k, const void* v, const void* bias, const float* mask, float* acc,
+                        float* m, float* l, int64_t B, int64_t H, int64_t I, int64_t N, int64_t D, int64_t key_begin,
+                        int64_t key_end, int32_t ending, int32_t dtype, void* stream) {
+    if (!m || !l) return TRI_ATTN_ERR_NULL;
+    Call c = make_call(q, k, v, bias, mask, acc, B, H, I, N, D, 1, dtype);
+    c.key_begin = key_begin;
+    c.key_end = key_end < 0 ? 0 : key_end;   // a negative end is an empty (invalid) range
+    c.ending = ending != 0;
+    c.st_m = m;
+    c.st_l = l;
+    return run(c, stream);
+}
+
+int tri_attn_state_merge(float* acc, float* m, float* l, const float* acc_t, const float* m_t, const float* l_t,
+                         int64_t rows, int64_t D, void* stream) {
+    int st = check_state_args(acc, m, l, rows, D);
+    if (st != TRI_ATTN_OK) return st;
+    st = check_state_args(acc_t, m_t, l_t, rows, D);
+    if (st != TRI_ATTN_OK) return st;
+    const Span mine[] = {{acc, rows * D * 4}, {m, rows * 4}, {l, rows * 4}};
+    const Span theirs[] = {{acc_t, rows * D * 4}, {m_t, rows * 4}, {l_t, rows * 4}};
+    for (const Span& a : mine)
+        for (const Span& b : theirs)
+            if (overlaps(a.p, a.bytes, b.p, b.bytes)) return TRI_ATTN_ERR_ALIAS;
+    const hipError_t e =
+        tri_attn::launch_state_merge(acc, m, l, acc_t, m_t, l_t, rows, D, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? TRI_ATTN_OK : hip_fail(e);
+}
+
+int tri_attn_state_finalize(const float* acc, const float* m, const float* l, float* out, float* lse, int64_t rows,
+                            int64_t D, void* stream) {
+    int st = check_state_args(acc, m, l, rows, D);
+    if (st != TRI_ATTN_OK) return st;
+    if (!out) return TRI_ATTN_ERR_NULL;
+    if (!aligned(out, 4) || (lse && !aligned(lse, 4))) return TRI_ATTN_ERR_ALIGN;
+    const Span ins[] = {{acc, rows * D * 4}, {m, rows * 4}, {l, rows * 4}};
+    for (const Span& a : ins)
+        if (overlaps(out, rows * D * 4, a.p, a.bytes) || (lse && overlaps(lse, rows * 4, a.p, a.bytes)))
+            return TRI_ATTN_ERR_ALIAS;
+    if (lse && overlaps(out, rows * D * 4, lse, rows * 4)) return TRI_ATTN_ERR_ALIAS;
+    const hipError_t e = tri_attn::launch_state_finalize(acc, m, l, out, lse, rows, D, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? TRI_ATTN_OK : hip_fail(e);
+}
+
+int pair_bias_attn_fwd(const void* q, const void* k, const void* v, const void* bias, const float* mask, float* out,
+                       float* lse, int64_t B, int64_t H, int64_t N, int64_t D, int32_t n_key_tiles, int32_t dtype,
+                       void* stream) {
+    // one sequence per batch element: the [B, N, H, D] tensors are [B, 1, N, H, D]
+    Call c = make_call(q, k, v, bias, mask, out, B, H, 1, N, D, n_key_tiles, dtype);
+    c.lse = lse;
+    return run(c, stream);
 }
 
 const char* tri_attn_status_string(int status) {
@@ -187,18 +317,19 @@ const char* tri_attn_status_string(int status) {
         case TRI_ATTN_ERR_NULL: return "a required pointer is NULL";
         case TRI_ATTN_ERR_SHAPE: return "invalid sizes (each >= 1, I <= N, element counts within int64)";
         case TRI_ATTN_ERR_DTYPE: return "unknown dtype (expected TRI_ATTN_FP32 or TRI_ATTN_BF16)";
-        case TRI_ATTN_ERR_UNSUPPORTED: return "unsupported problem (head size D > 64, I or B*H above 65535, or a bf16 row of K/V over 2 GiB)";
+        case TRI_ATTN_ERR_UNSUPPORTED: return "unsupported problem (head size D > 64, I or B*H above 65535, or an ending-node bf16 key block beyond 32-bit offsets)";
         case TRI_ATTN_ERR_ALIGN: return "misaligned pointer (16 bytes for q, k, v, bias, out, workspace; 4 for mask)";
         case TRI_ATTN_ERR_TILES: return "n_key_tiles outside [1, N]";
         case TRI_ATTN_ERR_HIP: return "the HIP runtime refused an allocation or launch (see tri_attn_last_hip_error)";
-        case TRI_ATTN_ERR_ALIAS: return "out or the workspace overlaps an input";
+        case TRI_ATTN_ERR_ALIAS: return "an output or the workspace overlaps an input or another output";
         case TRI_ATTN_ERR_WORKSPACE: return "workspace smaller than tri_attn_workspace_bytes()";
+        case TRI_ATTN_ERR_RANGE: return "key range outside 0 <= key_begin < key_end <= N";
         default: return "unknown status";
     }
 }
 
 int tri_attn_last_hip_error(void) { return g_last_hip_error; }
 
-int tri_attn_version(void) { return 10100; }
+int tri_attn_version(void) { return 10200; }
 
 }  // extern "C"

@@ -16,13 +16,15 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "tri_attn.h")
 
 FP32, BF16 = 0, 1
-OK, E_NULL, E_SHAPE, E_DTYPE, E_UNSUP, E_ALIGN, E_TILES, E_HIP, E_ALIAS, E_WS = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
+OK, E_NULL, E_SHAPE, E_DTYPE, E_UNSUP, E_ALIGN, E_TILES, E_HIP, E_ALIAS, E_WS, E_RANGE = (
+    0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10)
+NAME = r"(?:tri_attn_\w+|pair_bias_attn_\w+)"
 
 
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(tri_attn_\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(" + NAME + r")\s*\(", text, flags=re.M)))
 
 
 @pytest.fixture(scope="module")
@@ -36,20 +38,22 @@ def test_header_declares_the_binding_exports():
 
 def test_library_exports_every_declared_symbol(lib):
     out = subprocess.run(["nm", "-D", "--defined-only", P.LIB_PATH], capture_output=True, text=True, check=True).stdout
-    exported = set(re.findall(r"\sT\s(tri_attn_\w+)$", out, flags=re.M))
+    exported = set(re.findall(r"\sT\s(" + NAME + r")$", out, flags=re.M))
     assert exported == set(declared_functions())
     for name in declared_functions():
         assert hasattr(lib, name)
 
 
 def test_version_and_status_strings(lib):
-    assert lib.tri_attn_version() == 10100
+    assert lib.tri_attn_version() == 10200
     seen = set()
-    for code in (OK, E_NULL, E_SHAPE, E_DTYPE, E_UNSUP, E_ALIGN, E_TILES, E_HIP, E_ALIAS, E_WS):
+    codes = (OK, E_NULL, E_SHAPE, E_DTYPE, E_UNSUP, E_ALIGN, E_TILES, E_HIP, E_ALIAS, E_WS, E_RANGE)
+    for code in codes:
         s = P.status_string(code)
         assert s and s != "unknown status"
+        assert P.STATUS[code]
         seen.add(s)
-    assert len(seen) == 10
+    assert len(seen) == len(codes)
     assert P.status_string(12345) == "unknown status"
     assert lib.tri_attn_last_hip_error() == 0
 
@@ -162,6 +166,93 @@ def test_workspace_errors(lib):
     assert call_ws(lib, T=65) == E_TILES
 
 
-def test_row_span_limit_of_matrix_core_path(lib):
-    # one (b, i) row of K holds N*H*D bf16 values; 32-bit byte offsets cap it below 2 GiB
-    assert call(lib, N=1 << 16, H=1 << 9) == E_UNSUP
+def test_ending_key_span_limit_of_matrix_core_path(lib):
+    # ending node: consecutive keys are N*H*D bf16 values apart; a 32-key block must stay
+    # within 32-bit byte offsets
+    assert lib.tri_attn_fwd_ending(Q, K, V, BIAS, None, OUT, None, 1, 128, 8192, 32, 1, BF16, None) == E_UNSUP
+    # the fp32 path has no such limit: the same sizes get as far as the alias check (out == k)
+    assert lib.tri_attn_fwd_ending(Q, K, V, BIAS, None, K, None, 1, 128, 8192, 32, 1, FP32, None) == E_ALIAS
+
+
+# ---------------------------------------------------------------------------
+# lse, ending node, ring-step states, pair-bias attention
+# ---------------------------------------------------------------------------
+LSE, M_, L_ = (fake(0x10000000 * (n + 8)) for n in range(3))
+
+
+def call_lse(lib, lse=LSE, **kw):
+    a = dict(q=Q, k=K, v=V, bias=BIAS, mask=None, out=OUT, B=1, H=4, I=64, N=64, D=32, T=1, dtype=BF16)
+    a.update(kw)
+    return lib.tri_attn_fwd_lse(a["q"], a["k"], a["v"], a["bias"], a["mask"], a["out"], lse,
+                                a["B"], a["H"], a["I"], a["N"], a["D"], a["T"], a["dtype"], None)
+
+
+def test_lse_errors(lib):
+    assert call_lse(lib, lse=None) == E_NULL
+    assert call_lse(lib, q=None) == E_NULL
+    assert call_lse(lib, lse=fake(0x10000000 * 8 + 2)) == E_ALIGN
+    assert call_lse(lib, lse=fake(0x10000000 + 4096)) == E_ALIAS           # inside q
+    assert call_lse(lib, lse=fake(0x10000000 * 6 + 4096)) == E_ALIAS       # inside out
+    assert call_lse(lib, T=0) == E_TILES
+    assert call_lse(lib, I=65) == E_SHAPE
+
+
+def test_ending_errors(lib):
+    f = lambda **kw: lib.tri_attn_fwd_ending(kw.get("q", Q), K, V, BIAS, None, kw.get("out", OUT), kw.get("lse"),
+                                             1, 4, kw.get("N", 64), 32, kw.get("T", 1), BF16, None)
+    assert f(q=None) == E_NULL
+    assert f(N=0) == E_SHAPE
+    assert f(T=65) == E_TILES
+    assert f(out=K) == E_ALIAS
+    assert f(lse=fake(0x10000000 * 6 + 64)) == E_ALIAS
+
+
+def call_state(lib, kb=0, ke=64, ending=0, m=M_, l=L_, acc=OUT, I=64, **kw):
+    return lib.tri_attn_tile_state(kw.get("q", Q), K, V, BIAS, None, acc, m, l, 1, 4, I, 64, 32, kb, ke, ending,
+                                   kw.get("dtype", BF16), None)
+
+
+@pytest.mark.parametrize("kb,ke", [(-1, 10), (5, 5), (10, 5), (0, 65), (64, 70), (0, -1)])
+def test_tile_state_key_range(lib, kb, ke):
+    assert call_state(lib, kb=kb, ke=ke) == E_RANGE
+
+
+def test_tile_state_errors(lib):
+    assert call_state(lib, m=None) == E_NULL
+    assert call_state(lib, l=None) == E_NULL
+    assert call_state(lib, q=None) == E_NULL
+    assert call_state(lib, ending=1, I=32) == E_SHAPE                     # the ending node needs I == N
+    assert call_state(lib, m=fake(0x10000000 * 9 + 2)) == E_ALIGN
+    assert call_state(lib, m=L_) == E_ALIAS                               # m and l share memory
+    assert call_state(lib, l=fake(0x10000000 * 6 + 128)) == E_ALIAS      # l inside acc
+    assert call_state(lib, dtype=5) == E_DTYPE
+
+
+def test_state_merge_errors(lib):
+    A, M1, L1, A2, M2, L2 = (fake(0x10000000 * (n + 1)) for n in range(6))
+    mg = lambda rows=100, D=32, **kw: lib.tri_attn_state_merge(kw.get("a", A), M1, L1, kw.get("a2", A2), M2, L2,
+                                                               rows, D, None)
+    assert mg(a=None) == E_NULL
+    assert mg(a2=None) == E_NULL
+    assert mg(rows=0) == E_SHAPE
+    assert mg(D=0) == E_SHAPE
+    assert mg(D=65) == E_SHAPE
+    assert mg(a=fake(0x10000002)) == E_ALIGN
+    assert mg(a2=fake(0x10000000 + 64)) == E_ALIAS
+    fin = lambda out=fake(0x70000000), lse=None: lib.tri_attn_state_finalize(A, M1, L1, out, lse, 100, 32, None)
+    assert fin(out=None) == E_NULL
+    assert fin(out=fake(0x10000000 + 256)) == E_ALIAS                     # out inside acc
+    assert fin(lse=fake(0x10000000 * 2)) == E_ALIAS                       # lse on m
+    assert fin(lse=fake(0x70000000 + 64)) == E_ALIAS                      # lse inside out
+    assert fin(lse=fake(0x70100002)) == E_ALIGN
+
+
+def test_pair_bias_errors(lib):
+    pb = lambda **kw: lib.pair_bias_attn_fwd(kw.get("q", Q), K, V, BIAS, None, kw.get("out", OUT), kw.get("lse"),
+                                             kw.get("B", 1), 4, kw.get("N", 64), kw.get("D", 32), kw.get("T", 1),
+                                             BF16, None)
+    assert pb(q=None) == E_NULL
+    assert pb(B=0) == E_SHAPE
+    assert pb(D=65) == E_UNSUP
+    assert pb(T=65) == E_TILES
+    assert pb(out=V) == E_ALIAS

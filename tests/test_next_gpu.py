@@ -1,0 +1,216 @@
+"""GPU parity of the entry points beyond the forward: the log-sum-exp output, the
+ending-node orientation, the split-tile primitive (ring-step states, their merge and
+finalisation) and attention with pair bias -- each through the C ABI against the fp64
+oracle on the same seeded inputs.
+
+Bars (absolute, every compared element): outputs as the forward (1e-5 fp32, 1e-2 bf16
+with fp32 accumulation); log-sum-exps and partial log-sum-exps the same bars.  States
+are compared through what does not depend on the reference m each side picked: the
+normalised partial output acc / l and the partial log-sum-exp m + ln l.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from tests.test_parity_gpu import TOL, compare, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch_dev():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import pair_biased_triangle_amd as P
+    P.load_library()
+    return torch
+
+
+def dev_inputs(torch, w):
+    return tuple(to_dev(torch, x) for x in (w.q, w.k, w.v, w.bias, w.mask))
+
+
+def small(dtype, B=1, I=64, N=64, H=4, D=32, T=3, seed=31, mask_last=5, sigma_bias=2.0):
+    return W.make_inputs(W.custom_config(B=B, I=I, N=N, H=H, D=D, dtype=dtype, n_key_tiles=T, seed=seed,
+                                         sigma_bias=sigma_bias, mask_last=mask_last))
+
+
+def compare_lse(got, expect, tol, what):
+    got = got.astype(np.float64)
+    fin = np.isfinite(expect)
+    assert np.array_equal(np.isfinite(got), fin), f"{what}: -inf pattern differs"
+    err = np.abs(got[fin] - expect[fin])
+    worst = float(err.max()) if err.size else 0.0
+    say(f"  {what}: max|err| = {worst:.3e} (bar {tol:g}) over {err.size} finite values")
+    assert worst <= tol, f"{what}: {worst:.3e} > {tol:g}"
+
+
+# ---------------------------------------------------------------------------
+# log-sum-exp
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype,D", [("bf16", 32), ("fp32", 32), ("bf16", 16)])
+def test_forward_lse(torch_dev, dtype, D):
+    import pair_biased_triangle_amd as P
+    w = small(dtype, I=40, N=130, D=D, T=4)
+    say(f"[next] lse {dtype} D={D}")
+    q, k, v, bias, mask = dev_inputs(torch_dev, w)
+    out, lse = P.tri_attn_fwd_lse(q, k, v, bias, mask, n_key_tiles=4)
+    plain = P.tri_attn_fwd_rows(q, k, v, bias, mask, n_key_tiles=4)
+    torch_dev.cuda.synchronize()
+    assert torch_dev.equal(out, plain), "the lse entry point changed the output"
+    ref, ref_lse = oracle.tri_attn(w.q, w.k, w.v, w.bias, w.mask, n_key_tiles=4)
+    compare(out.cpu().numpy(), ref, TOL[dtype], f"out {dtype}")
+    compare_lse(lse.cpu().numpy(), ref_lse, TOL[dtype], f"lse {dtype}")
+
+
+def test_lse_of_fully_masked_rows(torch_dev):
+    import pair_biased_triangle_amd as P
+    for dtype in ("bf16", "fp32"):
+        w = small(dtype, I=8, N=40, T=2, mask_last=0)
+        mask = np.zeros((1, 40), dtype=np.float32)
+        mask[0, :] = -np.inf
+        q, k, v, bias, _ = dev_inputs(torch_dev, w)
+        out, lse = P.tri_attn_fwd_lse(q, k, v, bias, to_dev(torch_dev, mask), n_key_tiles=2)
+        torch_dev.cuda.synchronize()
+        assert torch_dev.all(out == 0) and torch_dev.all(lse == -float("inf"))
+
+
+# ---------------------------------------------------------------------------
+# ending node
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype,N,D,T", [("bf16", 64, 32, 1), ("bf16", 150, 32, 5), ("fp32", 70, 32, 3),
+                                         ("fp32", 33, 48, 2), ("bf16", 9, 16, 9)])
+def test_ending_small_full(torch_dev, dtype, N, D, T):
+    import pair_biased_triangle_amd as P
+    w = small(dtype, B=2 if N < 100 else 1, I=N, N=N, D=D, T=T, mask_last=3)
+    say(f"[next] ending {dtype} N={N} D={D} T={T}")
+    q, k, v, bias, mask = dev_inputs(torch_dev, w)
+    out, lse = P.tri_attn_fwd_ending(q, k, v, bias, mask, n_key_tiles=T, want_lse=True)
+    torch_dev.cuda.synchronize()
+    ref, ref_lse = oracle.tri_attn(w.q, w.k, w.v, w.bias, w.mask, n_key_tiles=T, ending=True)
+    compare(out.cpu().numpy(), ref, TOL[dtype], f"ending out {dtype}")
+    compare_lse(lse.cpu().numpy(), ref_lse, TOL[dtype], f"ending lse {dtype}")
+
+
+def test_ending_large_sampled(torch_dev):
+    """N = 1024, bf16, the four-chain workload's inputs in the ending orientation."""
+    import pair_biased_triangle_amd as P
+    w = W.make_inputs("complex_n1024")
+    cfg = w.cfg
+    say("[next] ending complex_n1024 sampled")
+    q, k, v, bias, mask = dev_inputs(torch_dev, w)
+    out = P.tri_attn_fwd_ending(q, k, v, bias, mask, n_key_tiles=cfg.n_key_tiles)
+    torch_dev.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    N = cfg.N
+    edges = [0, 1, 31, 32, 127, 128, N // 2, N - 2, N - 1]
+    rows = [oracle.flat_rows(1, N, N, 0, i, j)[0] for i in edges for j in edges]
+    rows = np.unique(np.array(rows + list(rng.integers(0, N * N, size=300)), dtype=np.int64))
+    ref, _ = oracle.tri_attn(w.q, w.k, w.v, w.bias, w.mask, n_key_tiles=cfg.n_key_tiles, ending=True, rows=rows)
+    got = out.view(-1, cfg.H, cfg.D)[torch_dev.from_numpy(rows).cuda()].cpu().numpy()
+    compare(got, ref, TOL["bf16"], "ending complex_n1024")
+
+
+# ---------------------------------------------------------------------------
+# split-tile primitive
+# ---------------------------------------------------------------------------
+def normalised(acc, m, l):
+    l = l.astype(np.float64)
+    some = l > 0
+    safe = np.where(some, l, 1.0)
+    out = np.where(some[..., None], acc.astype(np.float64) / safe[..., None], 0.0)
+    lse = np.where(some, m.astype(np.float64) + np.log(safe), -np.inf)
+    return out, lse
+
+
+@pytest.mark.parametrize("dtype,ending", [("bf16", False), ("fp32", False), ("bf16", True), ("fp32", True)])
+def test_tile_states_and_ring_merge(torch_dev, dtype, ending):
+    import pair_biased_triangle_amd as P
+    N = 97
+    w = small(dtype, I=N if ending else 20, N=N, T=1, mask_last=4)
+    say(f"[next] ring-step states {dtype} ending={ending}")
+    q, k, v, bias, mask = dev_inputs(torch_dev, w)
+    bounds = [0, 13, 45, 46, 93, N]                 # ragged tiles, one of a single key, one fully masked
+    order = [2, 4, 0, 3, 1]                          # a ring that starts mid-axis
+    run = None
+    for t in order:
+        lo, hi = bounds[t], bounds[t + 1]
+        acc, m, l = P.tri_attn_tile_state(q, k, v, bias, mask, key_begin=lo, key_end=hi, ending=ending)
+        torch_dev.cuda.synchronize()
+        racc, rm, rl = oracle.tile_state(w.q, w.k, w.v, w.bias, w.mask, key_begin=lo, key_end=hi, ending=ending)
+        g_out, g_lse = normalised(acc.cpu().numpy(), m.cpu().numpy(), l.cpu().numpy())
+        r_out, r_lse = normalised(racc, rm, rl)
+        compare(g_out, r_out, TOL[dtype], f"tile [{lo},{hi}) partial output")
+        compare_lse(g_lse, r_lse, TOL[dtype], f"tile [{lo},{hi}) partial lse")
+        if run is None:
+            run = (acc.clone(), m.clone(), l.clone())
+        else:
+            P.tri_attn_state_merge(*run, acc, m, l)
+    out, lse = P.tri_attn_state_finalize(*run)
+    torch_dev.cuda.synchronize()
+    ref, ref_lse = oracle.tri_attn(w.q, w.k, w.v, w.bias, w.mask, ending=ending)
+    compare(out.cpu().numpy(), ref, TOL[dtype], "merged ring")
+    compare_lse(lse.cpu().numpy(), ref_lse, TOL[dtype], "merged ring lse")
+
+
+def test_state_merge_and_finalize_kernels(torch_dev):
+    """The merge and finalisation kernels on random fp32 states (empty states mixed in)
+    against the oracle module's merge rule in fp64 on the same values."""
+    import pair_biased_triangle_amd as P
+    rng = np.random.default_rng(17)
+    rows, D = 5000, 24
+    def state(empty_frac):
+        acc = rng.standard_normal((rows, D)).astype(np.float32)
+        m = (3 * rng.standard_normal(rows)).astype(np.float32)
+        l = rng.uniform(1.0, 50.0, rows).astype(np.float32)
+        empty = rng.random(rows) < empty_frac
+        acc[empty], m[empty], l[empty] = 0.0, -np.inf, 0.0
+        return acc, m, l
+    a, b = state(0.1), state(0.1)
+    for st in (a, b):                                # rows 0..9: both states present ...
+        st[1][:10] = np.float32(1.5)
+        st[2][:10] = np.float32(3.0)
+    b[1][:5] = np.float32(-2.0)                      # ... with equal references in 5..9
+    say("[next] state merge/finalize kernels")
+    ga = tuple(torch_dev.from_numpy(x.copy()).cuda() for x in a)
+    gb = tuple(torch_dev.from_numpy(x.copy()).cuda() for x in b)
+    P.tri_attn_state_merge(*ga, *gb)
+    out, lse = P.tri_attn_state_finalize(*ga)
+    torch_dev.cuda.synchronize()
+    e_acc, e_m, e_l = oracle.merge_states(*a, *b)
+    e_out, e_lse = oracle.finalize_states(e_acc, e_m, e_l)
+    np.testing.assert_allclose(ga[2].cpu().numpy(), e_l, rtol=2e-6, atol=0)
+    fin = np.isfinite(e_m)
+    np.testing.assert_array_equal(np.isfinite(ga[1].cpu().numpy()), fin)
+    np.testing.assert_allclose(ga[1].cpu().numpy()[fin], e_m[fin], rtol=0, atol=0)
+    np.testing.assert_allclose(out.cpu().numpy(), e_out, rtol=5e-6, atol=1e-6)
+    compare_lse(lse.cpu().numpy(), e_lse, 1e-5, "finalize lse")
+
+
+def test_tile_state_of_masked_range_is_empty(torch_dev):
+    import pair_biased_triangle_amd as P
+    for dtype in ("bf16", "fp32"):
+        w = small(dtype, I=16, N=70, T=1, mask_last=20)       # keys 50..69 dropped
+        q, k, v, bias, mask = dev_inputs(torch_dev, w)
+        acc, m, l = P.tri_attn_tile_state(q, k, v, bias, mask, key_begin=52, key_end=70)
+        torch_dev.cuda.synchronize()
+        assert torch_dev.all(acc == 0) and torch_dev.all(l == 0) and torch_dev.all(m == -float("inf"))
+
+
+# ---------------------------------------------------------------------------
+# attention with pair bias
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype,N,D,T,B", [("bf16", 300, 32, 4, 2), ("fp32", 130, 16, 1, 3), ("bf16", 2700, 32, 8, 1)])
+def test_pair_bias_attention(torch_dev, dtype, N, D, T, B):
+    import pair_biased_triangle_amd as P
+    w = small(dtype, B=B, I=1, N=N, D=D, T=T, mask_last=7)
+    say(f"[next] pair-bias attention {dtype} B={B} N={N} D={D} T={T}")
+    q, k, v, bias, mask = dev_inputs(torch_dev, w)
+    shp = (B, N, 4, D)
+    out, lse = P.pair_bias_attn_fwd(q.view(shp), k.view(shp), v.view(shp), bias, mask, n_key_tiles=T, want_lse=True)
+    torch_dev.cuda.synchronize()
+    ref, ref_lse = oracle.tri_attn(w.q, w.k, w.v, w.bias, w.mask, n_key_tiles=T)
+    compare(out.cpu().numpy(), ref[:, 0], TOL[dtype], f"pair-bias out {dtype}")
+    compare_lse(lse.cpu().numpy(), ref_lse[:, 0], TOL[dtype], f"pair-bias lse {dtype}")

@@ -2,8 +2,8 @@
 
 A copy of the oracle's C source is edited (one textual mutation per case), built
 with gcc into a temporary directory, and run against the same checks that pin the
-real oracle (library SDPA special case, ring-step invariance, huge bias shifts,
-uniform and single-key closed forms).  The real oracle passes all of them; every
+real oracle (library SDPA special case for both orientations, ring-step invariance,
+huge bias shifts, uniform and single-key closed forms, merged ring-step states).  The real oracle passes all of them; every
 mutant must fail at least one.  Everything runs on the CPU.
 """
 import math
@@ -17,16 +17,19 @@ from tests.test_oracle_pins import rand_case, sdpa_reference
 
 MUTATIONS = {
     "drop_1_over_sqrt_d": ("dot * inv_sqrt_d", "dot"),
-    "scale_bias_too": ("dot * inv_sqrt_d + widen(bias, bias_row + kk, dtype)",
-                       "(dot + widen(bias, bias_row + kk, dtype)) * inv_sqrt_d"),
-    "bias_transposed": ("const int64_t bias_row = ((b * H + h) * N + j) * N;",
-                        "const int64_t bias_row = ((b * H + h) * N) * N + j;"),
-    "bias_column_stride": ("widen(bias, bias_row + kk, dtype)", "widen(bias, bias_row - j * N + kk * N, dtype)"),
+    "scale_bias_too": ("dot * inv_sqrt_d + widen(bias, b_off, dtype)",
+                       "(dot + widen(bias, b_off, dtype)) * inv_sqrt_d"),
+    "bias_transposed": (": ((b * H + h) * N + j) * N + kk;", ": ((b * H + h) * N + kk) * N + j;"),
+    "bias_column_stride": (": ((b * H + h) * N + j) * N + kk;", ": ((b * H + h) * N + kk) * N;"),
     "mask_ignored": ("sc += (double)mask[b * N + kk];", "sc += 0.0;"),
-    "keys_from_row_j": ("const int64_t k_off = ((bi * N + kk) * H + h) * D;",
-                        "const int64_t k_off = (((b * I + kk % I) * N + (bi % I)) * H + h) * D;"),
-    "values_wrong_head": ("const int64_t v_off = ((bi * N + kk) * H + h) * D;",
-                          "const int64_t v_off = ((bi * N + kk) * H + (h + 1) % H) * D;"),
+    "keys_from_row_j": ("                                                     : ((bi * N + kk) * H + h) * D;\n"
+                        "                        const int64_t b_off",
+                        "                                                     : (((b * I + kk % I) * N + i) * H + h) * D;\n"
+                        "                        const int64_t b_off"),
+    "values_wrong_head": ("                                                     : ((bi * N + kk) * H + h) * D;\n"
+                          "                        l_t += w;",
+                          "                                                     : ((bi * N + kk) * H + (h + 1) % H) * D;\n"
+                          "                        l_t += w;"),
     "merge_alpha_dropped": ("l = alpha * l + beta * l_t;", "l = l + beta * l_t;"),
     "merge_beta_dropped": ("a[d] = alpha * a[d] + beta * a_t[d];", "a[d] = alpha * a[d] + a_t[d];"),
     "merge_last_tile_wins": ("l = alpha * l + beta * l_t;", "l = l_t;"),
@@ -40,7 +43,18 @@ MUTATIONS = {
                       "uint32_t bits = (uint32_t)((const uint16_t *)base)[idx];"),
     "dot_skips_last_d": ("for (int64_t d = 0; d < D; ++d)\n                            dot +=",
                          "for (int64_t d = 0; d + 1 < D; ++d)\n                            dot +="),
+    # ending-node orientation
+    "ending_bias_not_transposed": ("ending ? ((b * H + h) * N + kk) * N + i", "ending ? ((b * H + h) * N + i) * N + kk"),
+    "ending_keys_from_row": ("const int64_t k_off = ending ? (((b * N + kk) * N + j) * H + h) * D",
+                             "const int64_t k_off = ending ? (((b * N + i) * N + kk) * H + h) * D"),
+    "ending_values_from_row": ("const int64_t v_off = ending ? (((b * N + kk) * N + j) * H + h) * D",
+                               "const int64_t v_off = ending ? (((b * N + i) * N + kk) * H + h) * D"),
+    # one ring step's state
+    "state_normalised": ("                        o[d] = a[d];\n                    lse[(r * H + h) * 2] = m;",
+                         "                        o[d] = a[d] / l;\n                    lse[(r * H + h) * 2] = m;"),
+    "state_reference_dropped": ("lse[(r * H + h) * 2] = m;", "lse[(r * H + h) * 2] = 0.0;"),
 }
+
 
 
 def battery(lib_path) -> list[str]:
@@ -99,9 +113,39 @@ def battery(lib_path) -> list[str]:
                              bf16_bits_to_f32(bb), mask)
         np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
 
+    qe, ke, ve, be, me = rand_case(rng, B=1, I=9, N=9, H=2, D=8, masked=(0, 4), sigma_b=2.0)
+
+    def ending():
+        T = lambda x: np.ascontiguousarray(np.swapaxes(x, 1, 2))
+        ref = T(sdpa_reference(T(qe), T(ke), T(ve), np.ascontiguousarray(np.swapaxes(be, 2, 3)), me))
+        for n_tiles in (1, 4):
+            out, _ = run(qe, ke, ve, be, me, n_key_tiles=n_tiles, ending=True)
+            np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+
+    def states():
+        ref = sdpa_reference(q, k, v, bias, mask)
+        bounds = (0, 1, 6, 13, 23)
+        st = None
+        for lo, hi in zip(bounds[:-1], bounds[1:]):
+            acc, m, l = oracle.tile_state(q, k, v, bias, mask, key_begin=lo, key_end=hi, lib_path=lib_path)
+            # m is the range's maximum score: the largest weight is exactly 1
+            w_max = np.exp(np.zeros_like(m))
+            assert np.all((l >= w_max) | (l == 0))
+            st = (acc, m, l) if st is None else oracle.merge_states(*st, acc, m, l)
+        out, _ = oracle.finalize_states(*st)
+        np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+        for e in (False, True):
+            qq, kk_, vv, bb, mm = (qe, ke, ve, be, me)
+            acc, m, l = oracle.tile_state(qq, kk_, vv, bb, mm, key_begin=0, key_end=9, ending=e, lib_path=lib_path)
+            full, lse = run(qq, kk_, vv, bb, mm, ending=e)
+            out, lse2 = oracle.finalize_states(acc, m, l)
+            np.testing.assert_allclose(out, full, rtol=0, atol=1e-12)
+            np.testing.assert_allclose(lse2, lse, rtol=0, atol=1e-12)
+
     with np.errstate(all="ignore"):
         for name, fn in [("sdpa", sdpa), ("tiles", tiles), ("shifts", shifts),
-                         ("closed_forms", closed_forms), ("bf16", bf16)]:
+                         ("closed_forms", closed_forms), ("bf16", bf16), ("ending", ending),
+                         ("states", states)]:
             check(name, fn)
     return failed
 
