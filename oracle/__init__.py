@@ -13,7 +13,8 @@ What it computes and which passages it follows is stated at the top of the C fil
 triangle attention (Fold-CP, Table 1) with the triangular bias shared across rows
 (Fold-CP, Figure 2(a)), over T contiguous key tiles (one per ring step, Table 1's
 caption) joined by the online-normaliser merge; the ending-node orientation; one ring
-step's softmax state.  ``merge_states`` and ``finalize_states`` restate the merge rule
+step's softmax state; the backward (gradients of the definition).  ``merge_states`` and
+``finalize_states`` restate the merge rule
 in numpy for states kept outside the C loop.
 """
 from __future__ import annotations
@@ -56,6 +57,9 @@ def _bind(path: str):
                                     i64, i64, i64, i64, i64,
                                     i64, i64, ctypes.c_int, vp, i64, vp, vp]
     L.oracle_tile_state.restype = ctypes.c_int
+    L.oracle_tri_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_int,
+                                      i64, i64, i64, i64, i64, vp, vp, vp, vp]
+    L.oracle_tri_attn_bwd.restype = ctypes.c_int
     L.oracle_even_tiles.argtypes = [i64, i64, vp]
     L.oracle_even_tiles.restype = None
     L.oracle_num_threads.argtypes = []
@@ -179,6 +183,26 @@ def tile_state(q, k, v, bias, mask=None, *, key_begin: int, key_end: int, ending
     if rc != 0:
         raise ValueError(f"oracle rejected its arguments (code {rc})")
     return acc, ml[..., 0].copy(), ml[..., 1].copy()
+
+
+def tri_attn_bwd(q, k, v, bias, mask, dout, *, lib_path: str = _LIB_PATH):
+    """Gradients of starting-node triangle attention for the upstream gradient dout
+    ([B, I, N, H, D] float32), in fp64.  Returns (dq, dk, dv, dbias): dq, dk, dv
+    [B, I, N, H, D], dbias [B, H, N, N] summed over the rows i held."""
+    q, k, v, bias, mask, dt = _prepare(q, k, v, bias, mask)
+    dout = np.ascontiguousarray(dout, dtype=np.float32)
+    B, I, N, H, D = q.shape
+    if dout.shape != q.shape:
+        raise ValueError("dout must be shaped like q")
+    dq, dk, dv = (np.empty(q.shape, dtype=np.float64) for _ in range(3))
+    dbias = np.empty((B, H, N, N), dtype=np.float64)
+    rc = load(lib_path).oracle_tri_attn_bwd(
+        q.ctypes.data, k.ctypes.data, v.ctypes.data, bias.ctypes.data,
+        None if mask is None else mask.ctypes.data, dout.ctypes.data, dt, B, H, I, N, D,
+        dq.ctypes.data, dk.ctypes.data, dv.ctypes.data, dbias.ctypes.data)
+    if rc != 0:
+        raise ValueError(f"oracle rejected its arguments (code {rc})")
+    return dq, dk, dv, dbias
 
 
 def merge_states(acc, m, l, acc_t, m_t, l_t):

@@ -39,6 +39,10 @@
  * (m_t, l_t, a_t) above with m_t the range's maximum score, unnormalised -- the
  * quantity a rank holds between the ring steps of Figure 2(a).
  *
+ * Backward (oracle_tri_attn_bwd): Fold-CP trains through its context-parallel modules;
+ * the pages give no formula for the gradients, so the oracle takes the plain derivative
+ * of the definition (stated where the function is defined).
+ *
  * All arithmetic is IEEE double, libm exp/log/sqrt, no fast-math and no contraction
  * (built with -ffp-contract=off).  Inputs are widened exactly: binary32 as is,
  * bfloat16 as the upper half of a binary32.
@@ -268,4 +272,108 @@ int oracle_tile_state(const void *q, const void *k, const void *v, const void *b
     const int64_t range[2] = {key_begin, key_end};
     return tri_attn_impl(q, k, v, bias, mask, dtype, B, H, I, N, D, range, 1, 0,
                          rows, n_rows, acc, ml, ending != 0, 1);
+}
+
+/*
+ * Backward of starting-node triangle attention: the derivative of the definition above
+ * (softmax attention with an additive bias) with respect to q, k, v and the triangular
+ * bias, for an upstream gradient dout [B, I, N, H, D] (binary32).  The tiling of the key
+ * axis does not enter: the forward result it produces is the definition's.  Per (b,i,j,h):
+ *
+ *   p_k   = softmax_k(s)_k,          o = sum_k p_k v_k
+ *   dp_k  = dout . v_k,              delta = sum_k p_k dp_k  (= dout . o)
+ *   ds_k  = p_k (dp_k - delta)
+ *   dq_j += sum_k ds_k k_k / sqrt(D);   dk_k += ds_k q_j / sqrt(D);   dv_k += p_k dout_j
+ *   dbias[b,h,j,k] += ds_k              (summed over every row i: the bias is shared)
+ *
+ * A key with mask -inf has p_k = 0 and receives nothing; a row with no finite score
+ * contributes nothing.  dq, dk, dv [B, I, N, H, D] and dbias [B, H, N, N] are doubles,
+ * overwritten.  One OpenMP task per (b, h), so every sum over rows runs in one thread
+ * in row order.
+ */
+int oracle_tri_attn_bwd(const void *q, const void *k, const void *v, const void *bias,
+                        const float *mask, const float *dout, int dtype,
+                        int64_t B, int64_t H, int64_t I, int64_t N, int64_t D,
+                        double *dq, double *dk, double *dv, double *dbias)
+{
+    if (!q || !k || !v || !bias || !dout || !dq || !dk || !dv || !dbias)
+        return ORACLE_ERR_ARG;
+    if (B < 1 || H < 1 || I < 1 || N < 1 || D < 1 || I > N)
+        return ORACLE_ERR_ARG;
+    if (dtype != ORACLE_DTYPE_FP32 && dtype != ORACLE_DTYPE_BF16)
+        return ORACLE_ERR_ARG;
+    const double inv_sqrt_d = 1.0 / sqrt((double)D);
+    const int64_t n_elem = B * I * N * H * D;
+    for (int64_t e = 0; e < n_elem; ++e)
+        dq[e] = dk[e] = dv[e] = 0.0;
+    for (int64_t e = 0; e < B * H * N * N; ++e)
+        dbias[e] = 0.0;
+    int failed = 0;
+
+#pragma omp parallel
+    {
+        double *p = (double *)malloc((size_t)N * sizeof(double));
+        double *dp = (double *)malloc((size_t)N * sizeof(double));
+        const int ok = p && dp;
+        if (!ok) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t bh = 0; bh < B * H; ++bh) {
+            if (!ok)
+                continue;
+            const int64_t b = bh / H, h = bh % H;
+            for (int64_t i = 0; i < I; ++i) {
+                const int64_t line = (b * I + i) * N;     /* flat (b, i, j=0) */
+                for (int64_t j = 0; j < N; ++j) {
+                    const int64_t q_off = ((line + j) * H + h) * D;
+                    /* scores and their maximum */
+                    double mx = -INFINITY;
+                    for (int64_t kk = 0; kk < N; ++kk) {
+                        const int64_t k_off = ((line + kk) * H + h) * D;
+                        double dot = 0.0;
+                        for (int64_t d = 0; d < D; ++d)
+                            dot += widen(q, q_off + d, dtype) * widen(k, k_off + d, dtype);
+                        double sc = dot * inv_sqrt_d + widen(bias, ((b * H + h) * N + j) * N + kk, dtype);
+                        if (mask)
+                            sc += (double)mask[b * N + kk];
+                        p[kk] = sc;
+                        if (sc > mx)
+                            mx = sc;
+                    }
+                    if (mx == -INFINITY)
+                        continue;   /* no finite score: the row has no gradient */
+                    double l = 0.0;
+                    for (int64_t kk = 0; kk < N; ++kk) {
+                        p[kk] = exp(p[kk] - mx);
+                        l += p[kk];
+                    }
+                    double delta = 0.0;
+                    for (int64_t kk = 0; kk < N; ++kk) {
+                        p[kk] /= l;
+                        const int64_t v_off = ((line + kk) * H + h) * D;
+                        double dot = 0.0;
+                        for (int64_t d = 0; d < D; ++d)
+                            dot += (double)dout[q_off + d] * widen(v, v_off + d, dtype);
+                        dp[kk] = dot;
+                        delta += p[kk] * dot;
+                    }
+                    for (int64_t kk = 0; kk < N; ++kk) {
+                        const double ds = p[kk] * (dp[kk] - delta);
+                        const int64_t kv_off = ((line + kk) * H + h) * D;
+                        for (int64_t d = 0; d < D; ++d) {
+                            dq[q_off + d] += ds * widen(k, kv_off + d, dtype) * inv_sqrt_d;
+                            dk[kv_off + d] += ds * widen(q, q_off + d, dtype) * inv_sqrt_d;
+                            dv[kv_off + d] += p[kk] * (double)dout[q_off + d];
+                        }
+                        dbias[((b * H + h) * N + j) * N + kk] += ds;
+                    }
+                }
+            }
+        }
+        free(p);
+        free(dp);
+    }
+    return failed ? ORACLE_ERR_NOMEM : ORACLE_OK;
 }

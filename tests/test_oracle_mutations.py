@@ -3,7 +3,8 @@
 A copy of the oracle's C source is edited (one textual mutation per case), built
 with gcc into a temporary directory, and run against the same checks that pin the
 real oracle (library SDPA special case for both orientations, ring-step invariance,
-huge bias shifts, uniform and single-key closed forms, merged ring-step states).  The real oracle passes all of them; every
+huge bias shifts, uniform and single-key closed forms, merged ring-step states,
+autograd for the backward).  The real oracle passes all of them; every
 mutant must fail at least one.  Everything runs on the CPU.
 """
 import math
@@ -16,12 +17,14 @@ import oracle
 from tests.test_oracle_pins import rand_case, sdpa_reference
 
 MUTATIONS = {
-    "drop_1_over_sqrt_d": ("dot * inv_sqrt_d", "dot"),
+    "drop_1_over_sqrt_d": ("double sc = dot * inv_sqrt_d + widen(bias, b_off, dtype);",
+                           "double sc = dot + widen(bias, b_off, dtype);"),
     "scale_bias_too": ("dot * inv_sqrt_d + widen(bias, b_off, dtype)",
                        "(dot + widen(bias, b_off, dtype)) * inv_sqrt_d"),
     "bias_transposed": (": ((b * H + h) * N + j) * N + kk;", ": ((b * H + h) * N + kk) * N + j;"),
     "bias_column_stride": (": ((b * H + h) * N + j) * N + kk;", ": ((b * H + h) * N + kk) * N;"),
-    "mask_ignored": ("sc += (double)mask[b * N + kk];", "sc += 0.0;"),
+    "mask_ignored": ("sc += (double)mask[b * N + kk];\n                        s[kk - k0] = sc;",
+                     "sc += 0.0;\n                        s[kk - k0] = sc;"),
     "keys_from_row_j": ("                                                     : ((bi * N + kk) * H + h) * D;\n"
                         "                        const int64_t b_off",
                         "                                                     : (((b * I + kk % I) * N + i) * H + h) * D;\n"
@@ -41,8 +44,10 @@ MUTATIONS = {
                         "lse[r * H + h] = (l > 0.0) ? log(l) : -INFINITY;"),
     "bf16_low_half": ("uint32_t bits = (uint32_t)((const uint16_t *)base)[idx] << 16;",
                       "uint32_t bits = (uint32_t)((const uint16_t *)base)[idx];"),
-    "dot_skips_last_d": ("for (int64_t d = 0; d < D; ++d)\n                            dot +=",
-                         "for (int64_t d = 0; d + 1 < D; ++d)\n                            dot +="),
+    "dot_skips_last_d": ("for (int64_t d = 0; d < D; ++d)\n                            dot += widen(q, q_off + d, dtype) * "
+                         "widen(k, k_off + d, dtype);\n                        double sc = dot * inv_sqrt_d + widen(bias, b_off",
+                         "for (int64_t d = 0; d + 1 < D; ++d)\n                            dot += widen(q, q_off + d, dtype) * "
+                         "widen(k, k_off + d, dtype);\n                        double sc = dot * inv_sqrt_d + widen(bias, b_off"),
     # ending-node orientation
     "ending_bias_not_transposed": ("ending ? ((b * H + h) * N + kk) * N + i", "ending ? ((b * H + h) * N + i) * N + kk"),
     "ending_keys_from_row": ("const int64_t k_off = ending ? (((b * N + kk) * N + j) * H + h) * D",
@@ -53,6 +58,16 @@ MUTATIONS = {
     "state_normalised": ("                        o[d] = a[d];\n                    lse[(r * H + h) * 2] = m;",
                          "                        o[d] = a[d] / l;\n                    lse[(r * H + h) * 2] = m;"),
     "state_reference_dropped": ("lse[(r * H + h) * 2] = m;", "lse[(r * H + h) * 2] = 0.0;"),
+    # backward
+    "bwd_delta_dropped": ("const double ds = p[kk] * (dp[kk] - delta);", "const double ds = p[kk] * dp[kk];"),
+    "bwd_dq_unscaled": ("dq[q_off + d] += ds * widen(k, kv_off + d, dtype) * inv_sqrt_d;",
+                        "dq[q_off + d] += ds * widen(k, kv_off + d, dtype);"),
+    "bwd_dk_from_keys": ("dk[kv_off + d] += ds * widen(q, q_off + d, dtype) * inv_sqrt_d;",
+                         "dk[kv_off + d] += ds * widen(k, kv_off + d, dtype) * inv_sqrt_d;"),
+    "bwd_dv_weighted_by_ds": ("dv[kv_off + d] += p[kk] * (double)dout[q_off + d];",
+                              "dv[kv_off + d] += ds * (double)dout[q_off + d];"),
+    "bwd_dbias_not_summed_over_rows": ("dbias[((b * H + h) * N + j) * N + kk] += ds;",
+                                       "dbias[((b * H + h) * N + j) * N + kk] = ds;"),
 }
 
 
@@ -142,10 +157,17 @@ def battery(lib_path) -> list[str]:
             np.testing.assert_allclose(out, full, rtol=0, atol=1e-12)
             np.testing.assert_allclose(lse2, lse, rtol=0, atol=1e-12)
 
+    def backward():
+        from tests.test_oracle_bwd import autograd_reference
+        dout = rng.standard_normal(q.shape).astype(np.float32)
+        got = oracle.tri_attn_bwd(q, k, v, bias, mask, dout, lib_path=lib_path)
+        for g, r in zip(got, autograd_reference(q, k, v, bias, mask, dout)):
+            np.testing.assert_allclose(g, r, rtol=0, atol=1e-12)
+
     with np.errstate(all="ignore"):
         for name, fn in [("sdpa", sdpa), ("tiles", tiles), ("shifts", shifts),
                          ("closed_forms", closed_forms), ("bf16", bf16), ("ending", ending),
-                         ("states", states)]:
+                         ("states", states), ("backward", backward)]:
             check(name, fn)
     return failed
 
