@@ -207,6 +207,32 @@ int tri_attn_state_finalize(const float *acc, const float *m, const float *l,
                             float *out, float *lse, int64_t rows, int64_t D, void *stream);
 
 /*
+ * Backward of the starting-node operation: the gradients of the definition for an
+ * upstream gradient dout (Fold-CP trains through its context-parallel modules; the
+ * pages give no formula, so these are the plain derivatives).  With
+ * p_k = exp(s_k - lse[b,i,j,h]), delta = dout[b,i,j,h,:] . out[b,i,j,h,:],
+ * dp_k = dout[b,i,j,h,:] . v[b,i,k,h,:] and ds_k = p_k (dp_k - delta):
+ *     dq[b,i,j,h,:] = sum_k ds_k k[b,i,k,h,:] / sqrt(D)
+ *     dk[b,i,k,h,:] = sum_j ds_k q[b,i,j,h,:] / sqrt(D)
+ *     dv[b,i,k,h,:] = sum_j p_k dout[b,i,j,h,:]
+ *     dbias[b,h,j,k] = sum_i ds_k            (summed over the I rows held by the call; the
+ *                                             row shares of several calls add up)
+ *   q, k, v [B, I, N, H, D], bias [B, H, N, N] (dtype), mask [B, N] or NULL: the forward's
+ *   inputs;  out [B, I, N, H, D] and lse [B, I, N, H]: the forward's results
+ *   (tri_attn_fwd_lse);  dout [B, I, N, H, D] binary32;
+ *   dq, dk, dv [B, I, N, H, D] and dbias [B, H, N, N]: binary32 results, overwritten.
+ * fp32 arithmetic for both dtypes, any D <= 64; deterministic (every sum is taken by one
+ * thread in a fixed order, no atomics).  A query with lse = -inf contributes nothing.
+ * q, k, v, bias 16-byte aligned, the other pointers 4-byte aligned; no result may
+ * overlap an input or another result.  No workspace.  Same error rules as the forward.
+ */
+int tri_attn_bwd(const void *q, const void *k, const void *v, const void *bias,
+                 const float *mask, const float *out, const float *lse, const float *dout,
+                 float *dq, float *dk, float *dv, float *dbias,
+                 int64_t B, int64_t H, int64_t I, int64_t N, int64_t D,
+                 int32_t dtype, void *stream);
+
+/*
  * Attention with pair bias ("Fold-CP", Table 1 row "Attention with Pair Bias", and
  * Figure 2(c)): one sequence of N tokens per batch element, biased by the pair
  * representation,

@@ -24,7 +24,7 @@ STATUS = {
 }
 EXPORTS = ("tri_attn_fwd", "tri_attn_fwd_rows", "tri_attn_fwd_rows_ws", "tri_attn_workspace_bytes",
            "tri_attn_fwd_lse", "tri_attn_fwd_ending", "tri_attn_tile_state", "tri_attn_state_merge",
-           "tri_attn_state_finalize", "pair_bias_attn_fwd",
+           "tri_attn_state_finalize", "pair_bias_attn_fwd", "tri_attn_bwd",
            "tri_attn_status_string", "tri_attn_last_hip_error", "tri_attn_version")
 
 
@@ -64,6 +64,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         L.tri_attn_state_finalize.restype = ctypes.c_int
         L.pair_bias_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, vp]
         L.pair_bias_attn_fwd.restype = ctypes.c_int
+        L.tri_attn_bwd.argtypes = [vp] * 12 + [i64, i64, i64, i64, i64, i32, vp]
+        L.tri_attn_bwd.restype = ctypes.c_int
         L.tri_attn_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i32, i32]
         L.tri_attn_workspace_bytes.restype = ctypes.c_int64
         L.tri_attn_status_string.argtypes = [ctypes.c_int]
@@ -292,3 +294,60 @@ def pair_bias_attn_fwd(q, k, v, bias, mask=None, *, n_key_tiles: int = 1, out=No
                                 B, H, N, D, int(n_key_tiles), dt, _stream_handle(stream)))
     out = out5.view(B, N, H, D)
     return (out, lse) if lse is not None else out
+
+
+def tri_attn_bwd(q, k, v, bias, mask, out, lse, dout, *, stream=None):
+    """Gradients of the starting-node operation for the upstream gradient dout.
+
+    q, k, v, bias, mask: the forward's inputs; out, lse: its results (tri_attn_fwd_lse);
+    dout: float32 shaped like q.  Returns (dq, dk, dv, dbias), float32; dbias [B, H, N, N]
+    is summed over the rows i held.  Calls tri_attn_bwd.
+    """
+    import torch
+    L = load_library()
+    dt, out = _validate(q, k, v, bias, mask, out)
+    B, I, N, H, D = q.shape
+    lse = _per_query(out, (B, I, N, H), "lse", lse)
+    if dout.dtype != torch.float32 or tuple(dout.shape) != tuple(q.shape) or not dout.is_contiguous():
+        raise ValueError("dout must be a contiguous float32 tensor shaped like q")
+    dq, dk, dv = (torch.empty(q.shape, dtype=torch.float32, device=q.device) for _ in range(3))
+    dbias = torch.empty((B, H, N, N), dtype=torch.float32, device=q.device)
+    _check(L.tri_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(mask), _ptr(out), _ptr(lse), _ptr(dout),
+                          _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbias), B, H, I, N, D, dt, _stream_handle(stream)))
+    return dq, dk, dv, dbias
+
+
+def _autograd_function():
+    import torch
+
+    class TriangleAttention(torch.autograd.Function):
+        """Starting-node triangle attention as a differentiable torch op: forward through
+        tri_attn_fwd_lse, backward through tri_attn_bwd (the mask is a constant)."""
+
+        @staticmethod
+        def forward(ctx, q, k, v, bias, mask, n_key_tiles):
+            out, lse = tri_attn_fwd_lse(q, k, v, bias, mask, n_key_tiles=n_key_tiles)
+            ctx.save_for_backward(q, k, v, bias, out, lse)
+            ctx.mask = mask
+            return out
+
+        @staticmethod
+        def backward(ctx, dout):
+            q, k, v, bias, out, lse = ctx.saved_tensors
+            dq, dk, dv, dbias = tri_attn_bwd(q, k, v, bias, ctx.mask, out, lse,
+                                             dout.to(torch.float32).contiguous())
+            return dq.to(q.dtype), dk.to(k.dtype), dv.to(v.dtype), dbias.to(bias.dtype), None, None
+
+    return TriangleAttention
+
+
+_TRI_FN = None
+
+
+def triangle_attention(q, k, v, bias, mask=None, *, n_key_tiles: int = 1):
+    """Differentiable starting-node triangle attention ([B, I, N, H, D] inputs; returns
+    float32 out).  Gradients flow to q, k, v and bias."""
+    global _TRI_FN
+    if _TRI_FN is None:
+        _TRI_FN = _autograd_function()
+    return _TRI_FN.apply(q, k, v, bias, mask, int(n_key_tiles))

@@ -59,6 +59,25 @@ hipError_t launch_state_merge(float* acc, float* m, float* l, const float* acc_t
 hipError_t launch_state_finalize(const float* acc, const float* m, const float* l, float* out, float* lse,
                                  int64_t rows, int64_t D, hipStream_t stream);
 
+// Backward (starting node): gradients for the upstream gradient dout, from the forward's
+// out and lse.  dq, dk, dv like q; dbias [B, H, N, N] summed over the I rows held.
+struct BwdProblem {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* bias;
+    const float* mask;   // may be null
+    const float* out;
+    const float* lse;
+    const float* dout;
+    float* dq;
+    float* dk;
+    float* dv;
+    float* dbias;
+    int64_t B, H, I, N, D;
+};
+hipError_t launch_backward(const BwdProblem& p, bool bf16, hipStream_t stream);
+
 // Start of key tile t when N keys are cut into T near-equal contiguous tiles
 // (the first N mod T tiles hold one key more).
 __host__ __device__ inline int64_t tile_start(int64_t t, int64_t N, int64_t T) {

@@ -302,6 +302,33 @@ int tri_attn_state_finalize(const float* acc, const float* m, const float* l, fl
     return e == hipSuccess ? TRI_ATTN_OK : hip_fail(e);
 }
 
+int tri_attn_bwd(const void* q, const void* k, const void* v, const void* bias, const float* mask, const float* out,
+                 const float* lse, const float* dout, float* dq, float* dk, float* dv, float* dbias, int64_t B,
+                 int64_t H, int64_t I, int64_t N, int64_t D, int32_t dtype, void* stream) {
+    if (!q || !k || !v || !bias || !out || !lse || !dout || !dq || !dk || !dv || !dbias) return TRI_ATTN_ERR_NULL;
+    int64_t qkv_elems = 0, bias_elems = 0;
+    const int st = check_sizes(B, H, I, N, D, 1, dtype, &qkv_elems, &bias_elems);
+    if (st != TRI_ATTN_OK) return st;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(bias, 16) || (mask && !aligned(mask, 4)) ||
+        !aligned(out, 4) || !aligned(lse, 4) || !aligned(dout, 4) || !aligned(dq, 4) || !aligned(dk, 4) ||
+        !aligned(dv, 4) || !aligned(dbias, 4))
+        return TRI_ATTN_ERR_ALIGN;
+    const int64_t esz = dtype == TRI_ATTN_BF16 ? 2 : 4;
+    const Span inputs[] = {{q, qkv_elems * esz},   {k, qkv_elems * esz},  {v, qkv_elems * esz},
+                           {bias, bias_elems * esz}, {mask, B * N * 4},     {out, qkv_elems * 4},
+                           {lse, qkv_elems / D * 4}, {dout, qkv_elems * 4}};
+    const Span outputs[] = {{dq, qkv_elems * 4}, {dk, qkv_elems * 4}, {dv, qkv_elems * 4}, {dbias, bias_elems * 4}};
+    for (int a = 0; a < 4; ++a) {
+        for (const Span& in : inputs)
+            if (in.p && overlaps(outputs[a].p, outputs[a].bytes, in.p, in.bytes)) return TRI_ATTN_ERR_ALIAS;
+        for (int o = a + 1; o < 4; ++o)
+            if (overlaps(outputs[a].p, outputs[a].bytes, outputs[o].p, outputs[o].bytes)) return TRI_ATTN_ERR_ALIAS;
+    }
+    const tri_attn::BwdProblem p{q, k, v, bias, mask, out, lse, dout, dq, dk, dv, dbias, B, H, I, N, D};
+    const hipError_t e = tri_attn::launch_backward(p, dtype == TRI_ATTN_BF16, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? TRI_ATTN_OK : hip_fail(e);
+}
+
 int pair_bias_attn_fwd(const void* q, const void* k, const void* v, const void* bias, const float* mask, float* out,
                        float* lse, int64_t B, int64_t H, int64_t N, int64_t D, int32_t n_key_tiles, int32_t dtype,
                        void* stream) {

@@ -256,3 +256,24 @@ def test_pair_bias_errors(lib):
     assert pb(D=65) == E_UNSUP
     assert pb(T=65) == E_TILES
     assert pb(out=V) == E_ALIAS
+
+
+def test_backward_errors(lib):
+    OUTB, LSEB, DOUT, DQ, DK, DV, DB = (fake(0x10000000 * (n + 12)) for n in range(7))
+    def bw(**kw):
+        a = dict(q=Q, k=K, v=V, bias=BIAS, mask=None, out=OUTB, lse=LSEB, dout=DOUT, dq=DQ, dk=DK, dv=DV, db=DB,
+                 B=1, H=4, I=64, N=64, D=32, dtype=BF16)
+        a.update(kw)
+        return lib.tri_attn_bwd(a["q"], a["k"], a["v"], a["bias"], a["mask"], a["out"], a["lse"], a["dout"],
+                                a["dq"], a["dk"], a["dv"], a["db"], a["B"], a["H"], a["I"], a["N"], a["D"],
+                                a["dtype"], None)
+    for name in ("q", "k", "v", "bias", "out", "lse", "dout", "dq", "dk", "dv", "db"):
+        assert bw(**{name: None}) == E_NULL, name
+    assert bw(I=65) == E_SHAPE
+    assert bw(dtype=3) == E_DTYPE
+    assert bw(D=65) == E_UNSUP
+    assert bw(q=fake(0x10000004)) == E_ALIGN
+    assert bw(dq=fake(0x10000000 * 15 + 2)) == E_ALIGN
+    assert bw(dq=Q) == E_ALIAS                                 # a result on an input
+    assert bw(dk=DQ) == E_ALIAS                                # two results share memory
+    assert bw(db=fake(0x10000000 * 12 + 512)) == E_ALIAS      # dbias inside out
