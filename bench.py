@@ -10,7 +10,18 @@ Prints one JSON line.  `value` is TFLOP/s at the nominal 4*B*H*N^3*D FLOPs; `roo
 relates the kernel's live-measured average launch time to the bf16 dense MFMA peak;
 `cpu_baseline` times the fp64 oracle on a bounded sample of the same workload's rows.
 
+`--pass` measures the other entry points on the same workload, one JSON line each:
+  bwd        tri_attn_bwd (dq, dk, dv, row-summed dbias) from the forward's out and lse;
+             algorithmic FLOPs 10*B*H*I*N^2*D (the S recompute, dP, dQ, dK, dV products),
+             fp32 vector arithmetic -> roofline against the fp32 vector peak
+  ending     tri_attn_fwd_ending (same FLOPs as the forward, bf16 MFMA peak)
+  pair_bias  pair_bias_attn_fwd on the workload's first row (I = 1): bound by reading
+             the bias -> roofline in GB/s against HBM
+  ring       one tri_attn_tile_state per key tile, tri_attn_state_merge after each, then
+             tri_attn_state_finalize (the split-tile path), against the bf16 MFMA peak
+
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME] [--no-cpu]
+                    [--pass fwd|bwd|ending|pair_bias|ring]
 """
 from __future__ import annotations
 
@@ -29,6 +40,7 @@ sys.path.insert(0, ROOT)
 METRIC = "triangle-attention TFLOP/s (4·B·H·N³·D) and % bf16 MFMA peak, 1×MI355X"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak (AMD published)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E (AMD published)
+PEAK_FP32_TFLOPS = 157.3       # MI355X fp32 vector (AMD published)
 DEFAULT_WORKLOAD = "single_gpu_n2700"
 KERNEL_NAME = "bf16_mfma_kernel"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
@@ -97,6 +109,94 @@ def cpu_baseline(w, out_gpu, torch, target_s: float):
     }, err, n
 
 
+def timed(torch, step, steps, warmup):
+    """HIP events on the launch stream around `steps` calls after `warmup` untimed ones;
+    returns (ms per step, wall seconds of the timed region)."""
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / steps, time.perf_counter() - t0
+
+
+def other_pass(args, torch, P, W, cfg) -> dict:
+    """The entry points beyond the forward, timed on the same workload's inputs."""
+    w = W.make_inputs(cfg)
+    q, k, v, bias, mask = (to_dev(torch, x) for x in (w.q, w.k, w.v, w.bias, w.mask))
+    B, I, N, H, D, T = cfg.B, cfg.I, cfg.N, cfg.H, cfg.D, cfg.n_key_tiles
+    fwd_flops = cfg.flops
+    extra = {}
+    if args.which == "bwd":
+        out, lse = P.tri_attn_fwd_lse(q, k, v, bias, mask, n_key_tiles=T)
+        dout = torch.randn(q.shape, dtype=torch.float32, device="cuda", generator=torch.Generator("cuda").manual_seed(1))
+        step = lambda: P.tri_attn_bwd(q, k, v, bias, mask, out, lse, dout)
+        work, unit, peak, bound = 2.5 * fwd_flops, "TFLOP/s", PEAK_FP32_TFLOPS, "alu"
+        metric = "triangle-attention backward TFLOP/s (10·B·H·I·N²·D: S recompute, dP, dQ, dK, dV)"
+        kernels = "bwd_dq_kernel + bwd_dkdv_kernel + bwd_dbias_kernel (fp32 vector)"
+        dtype = "f32"
+    elif args.which == "ending":
+        if I != N:
+            raise SystemExit("the ending orientation needs a workload with I == N")
+        step = lambda: P.tri_attn_fwd_ending(q, k, v, bias, mask, n_key_tiles=T)
+        work, unit, peak, bound = fwd_flops, "TFLOP/s", PEAK_BF16_TFLOPS, "mfma"
+        metric = "ending-node triangle-attention TFLOP/s (4·B·H·N³·D)"
+        kernels = "bias_image_kernel (transposed bias) + bf16_mfma_kernel"
+        dtype = cfg.dtype
+    elif args.which == "pair_bias":
+        shp = (B, N, H, D)
+        q1, k1, v1 = (x[:, 0].contiguous().view(shp) for x in (q, k, v))
+        step = lambda: P.pair_bias_attn_fwd(q1, k1, v1, bias, mask, n_key_tiles=T)
+        s_in = cfg.in_bytes
+        work = 3 * B * N * H * D * s_in + B * H * N * N * s_in + (4 * B * N if mask is not None else 0) + 4 * B * N * H * D
+        unit, peak, bound = "GB/s", PEAK_HBM_GBS, "hbm"
+        metric = "attention with pair bias GB/s (q, k, v, bias read once, out written once)"
+        kernels = "bias_image_kernel + bf16_mfma_kernel with one row"
+        extra["flops_per_call"] = 4.0 * B * H * N * N * D
+        dtype = cfg.dtype
+    else:   # ring
+        bounds = [t * (N // T) + min(t, N % T) for t in range(T + 1)]   # the forward's tiles
+        acc = torch.empty((B, I, N, H, D), dtype=torch.float32, device="cuda")
+        m = torch.empty((B, I, N, H), dtype=torch.float32, device="cuda")
+        l = torch.empty_like(m)
+        acc_t, m_t, l_t = torch.empty_like(acc), torch.empty_like(m), torch.empty_like(l)
+        out = torch.empty_like(acc)
+
+        def step():
+            P.tri_attn_tile_state(q, k, v, bias, mask, key_begin=bounds[0], key_end=bounds[1], acc=acc, m=m, l=l)
+            for t in range(1, T):
+                P.tri_attn_tile_state(q, k, v, bias, mask, key_begin=bounds[t], key_end=bounds[t + 1],
+                                      acc=acc_t, m=m_t, l=l_t)
+                P.tri_attn_state_merge(acc, m, l, acc_t, m_t, l_t)
+            P.tri_attn_state_finalize(acc, m, l, out=out)
+        work, unit, peak, bound = fwd_flops, "TFLOP/s", PEAK_BF16_TFLOPS, "mfma"
+        metric = f"split-tile ring TFLOP/s ({T} tile states + merges + finalize, 4·B·H·I·N²·D)"
+        kernels = "per tile: bias_image_kernel + bf16_mfma_kernel (state mode); state_merge_kernel; state_finalize_kernel"
+        dtype = cfg.dtype
+    ms, wall = timed(torch, step, args.steps, args.warmup)
+    rate = work / (ms * 1e-3) / (1e12 if unit == "TFLOP/s" else 1e9)
+    res = {
+        "metric": metric, "value": round(rate, 3), "unit": unit, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": dtype, "data": "synthetic (seeded counter-based normal inputs, workloads/)",
+        "config": {"workload": cfg.name, "pass": args.which, "B": B, "I": I if args.which != "pair_bias" else 1,
+                   "N": N, "H": H, "D": D, "n_key_tiles": T, "masked_keys": cfg.mask_last, "input_dtype": cfg.dtype},
+        "wall_s_timed_region": round(wall, 4),
+        "roofline": {"bound": bound, "achieved": round(rate, 3), "peak": peak, "unit": unit,
+                     "frac": round(rate / peak, 4), "traffic": None, "kernels": kernels,
+                     "avg_pass_ms": round(ms, 4)},
+        "cpu_baseline": None,
+    }
+    res.update(extra)
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -105,6 +205,7 @@ def main() -> int:
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target wall time of the CPU baseline")
+    ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd", "ending", "pair_bias", "ring"])
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 3 plain device copies of 1 GiB (reference dispatches for the HBM byte counters)")
     args = ap.parse_args()
@@ -133,6 +234,9 @@ def main() -> int:
         return 0
     P.load_library()
     cfg = W.CONFIGS[args.workload]
+    if args.which != "fwd":
+        print(json.dumps(other_pass(args, torch, P, W, cfg)), flush=True)
+        return 0
     w = W.make_inputs(cfg)
     q, k, v, bias, mask = (to_dev(torch, x) for x in (w.q, w.k, w.v, w.bias, w.mask))
     out = torch.empty((cfg.B, cfg.I, cfg.N, cfg.H, cfg.D), dtype=torch.float32, device="cuda")

@@ -5,8 +5,8 @@
 // sum_k e^(s_k - m).  Any finite reference gives the same merged result; a state with
 // l == 0 (no finite score) is the identity of the merge.
 //
-// One thread per query; D consecutive floats per query, so a wave covers 64 * D * 4
-// contiguous bytes.  Both kernels are HBM-bound (they read and write every state once).
+// Both kernels are HBM-bound: they read and write every state once, with coalesced
+// accesses (see below).
 #include "launch.h"
 
 #include <cmath>
@@ -14,46 +14,87 @@
 namespace tri_attn {
 namespace {
 
-constexpr int ST_THR = 256;
+constexpr int ST_THR = 256;   // threads per workgroup
+constexpr int ST_Q = 64;      // queries per workgroup
 
+// A workgroup owns ST_Q consecutive queries.  Their per-query factors are formed once in
+// LDS; then every thread walks the workgroup's ST_Q * D contiguous floats with a stride
+// of ST_THR, so each wave reads and writes 256 consecutive bytes per access.  The per-query
+// values m and l are read and rewritten by the same thread, on either side of the barriers.
 __global__ void __launch_bounds__(ST_THR) state_merge_kernel(float* acc, float* m, float* l, const float* acc_t,
                                                              const float* m_t, const float* l_t, int64_t rows,
                                                              int D) {
-    const int64_t q = static_cast<int64_t>(blockIdx.x) * ST_THR + threadIdx.x;
-    if (q >= rows) return;
-    const float la = l[q], lb = l_t[q];
-    if (!(lb > 0.0f)) return;                 // incoming tile holds no finite score
-    float* a = acc + q * D;
-    const float* at = acc_t + q * D;
-    if (!(la > 0.0f)) {                       // running state empty: take the tile's state
-        for (int d = 0; d < D; ++d) a[d] = at[d];
-        m[q] = m_t[q];
-        l[q] = lb;
-        return;
+    __shared__ float fa[ST_Q], fb[ST_Q];
+    const int64_t q0 = static_cast<int64_t>(blockIdx.x) * ST_Q;
+    const int nq = static_cast<int>(rows - q0 < ST_Q ? rows - q0 : ST_Q);
+    const int tid = threadIdx.x;
+    float mm = 0.0f, ll = 0.0f;
+    if (tid < nq) {
+        const int64_t q = q0 + tid;
+        const float la = l[q], lb = l_t[q];
+        float alpha, beta;
+        if (!(lb > 0.0f)) {                   // incoming tile holds no finite score: keep the state
+            alpha = 1.0f;
+            beta = 0.0f;
+            mm = m[q];
+            ll = la;
+        } else if (!(la > 0.0f)) {            // running state empty: take the tile's state
+            alpha = 0.0f;
+            beta = 1.0f;
+            mm = m_t[q];
+            ll = lb;
+        } else {
+            const float ma = m[q], mb = m_t[q];
+            mm = fmaxf(ma, mb);
+            alpha = expf(ma - mm);
+            beta = expf(mb - mm);
+            ll = alpha * la + beta * lb;
+        }
+        fa[tid] = alpha;
+        fb[tid] = beta;
     }
-    const float ma = m[q], mb = m_t[q];
-    const float mm = fmaxf(ma, mb);
-    const float alpha = expf(ma - mm), beta = expf(mb - mm);
-    for (int d = 0; d < D; ++d) a[d] = alpha * a[d] + beta * at[d];
-    m[q] = mm;
-    l[q] = alpha * la + beta * lb;
+    __syncthreads();
+    const int64_t e0 = q0 * D;
+    const int ne = nq * D;
+    for (int e = tid; e < ne; e += ST_THR) {
+        const int qq = e / D;
+        const float a = fa[qq], b = fb[qq];
+        if (b == 0.0f) continue;              // an empty tile leaves the accumulator as it is
+        const float bt = b * acc_t[e0 + e];
+        acc[e0 + e] = a == 0.0f ? bt : a * acc[e0 + e] + bt;
+    }
+    if (tid < nq) {
+        m[q0 + tid] = mm;
+        l[q0 + tid] = ll;
+    }
 }
 
 __global__ void __launch_bounds__(ST_THR) state_finalize_kernel(const float* acc, const float* m, const float* l,
                                                                 float* out, float* lse, int64_t rows, int D) {
-    const int64_t q = static_cast<int64_t>(blockIdx.x) * ST_THR + threadIdx.x;
-    if (q >= rows) return;
-    const float lq = l[q];
-    const bool some = lq > 0.0f;
-    for (int d = 0; d < D; ++d) out[q * D + d] = some ? acc[q * D + d] / lq : 0.0f;
-    if (lse) lse[q] = some ? m[q] + logf(lq) : -INFINITY;
+    __shared__ float inv[ST_Q];
+    const int64_t q0 = static_cast<int64_t>(blockIdx.x) * ST_Q;
+    const int nq = static_cast<int>(rows - q0 < ST_Q ? rows - q0 : ST_Q);
+    const int tid = threadIdx.x;
+    if (tid < nq) {
+        const float lq = l[q0 + tid];
+        const bool some = lq > 0.0f;
+        inv[tid] = lq;
+        if (lse) lse[q0 + tid] = some ? m[q0 + tid] + logf(lq) : -INFINITY;
+    }
+    __syncthreads();
+    const int64_t e0 = q0 * D;
+    const int ne = nq * D;
+    for (int e = tid; e < ne; e += ST_THR) {
+        const float lq = inv[e / D];
+        out[e0 + e] = lq > 0.0f ? acc[e0 + e] / lq : 0.0f;
+    }
 }
 
 }  // namespace
 
 hipError_t launch_state_merge(float* acc, float* m, float* l, const float* acc_t, const float* m_t,
                               const float* l_t, int64_t rows, int64_t D, hipStream_t stream) {
-    const int64_t blocks = (rows + ST_THR - 1) / ST_THR;
+    const int64_t blocks = (rows + ST_Q - 1) / ST_Q;
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(state_merge_kernel, dim3(static_cast<unsigned>(blocks)), dim3(ST_THR), 0, stream, acc, m, l,
                        acc_t, m_t, l_t, rows, static_cast<int>(D));
@@ -62,7 +103,7 @@ hipError_t launch_state_merge(float* acc, float* m, float* l, const float* acc_t
 
 hipError_t launch_state_finalize(const float* acc, const float* m, const float* l, float* out, float* lse,
                                  int64_t rows, int64_t D, hipStream_t stream) {
-    const int64_t blocks = (rows + ST_THR - 1) / ST_THR;
+    const int64_t blocks = (rows + ST_Q - 1) / ST_Q;
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(state_finalize_kernel, dim3(static_cast<unsigned>(blocks)), dim3(ST_THR), 0, stream, acc, m,
                        l, out, lse, rows, static_cast<int>(D));
