@@ -97,7 +97,8 @@ constexpr float kLo = 5.421010862427522e-20f;  // 2^-64
 constexpr float kHi = 1.8446744073709552e19f;  // 2^64
 
 __host__ __device__ constexpr int kv_chunk(int key, int part) { return part ^ ((key >> 1) & 3); }
-__host__ __device__ constexpr int bias_chunk(int j, int part) { return part ^ (j & 7); }
+__host__ __device__ constexpr int bias_chunk(int j, int part) { return img_chunk(j, part); }
+static_assert(IMG_BJ == BJ && IMG_BK == BK, "the image layout published in launch.h");
 
 // Key block n of the tile-ordered sequence: tiles ascending, 32-key blocks inside each.
 struct KeyBlock {
@@ -656,6 +657,18 @@ size_t bf16_workspace_bytes(const Problem& p) {
     const int64_t n_jb = (p.N + BJ - 1) / BJ;
     const int64_t nblk = BlockPlan(p.nkeys(), p.T).count();
     return static_cast<size_t>(p.B * p.H * n_jb * nblk) * IMG_FLOATS * sizeof(float);
+}
+
+int64_t bias_image_blocks(const Problem& p) { return BlockPlan(p.nkeys(), p.T).count(); }
+
+hipError_t launch_bias_image(const Problem& p, float* img, hipStream_t stream) {
+    const int64_t n_jb = (p.N + BJ - 1) / BJ;
+    const int64_t nblk = BlockPlan(p.nkeys(), p.T).count();
+    if (nblk > 0x7FFFFFFF || n_jb > 65535 || p.B * p.H > 65535) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(bias_image_kernel, dim3(static_cast<unsigned>(nblk), static_cast<unsigned>(n_jb),
+                                               static_cast<unsigned>(p.B * p.H)),
+                       dim3(IMG_THR), 0, stream, p, img, static_cast<int>(n_jb), static_cast<int>(nblk));
+    return hipGetLastError();
 }
 
 hipError_t launch_bf16_mfma(const Problem& p, void* workspace, hipStream_t stream) {

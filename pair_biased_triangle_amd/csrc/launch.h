@@ -44,21 +44,6 @@ __host__ __device__ inline Strides strides_of(const Problem& p) {
     return Strides{p.I * p.N * HD, p.N * HD, HD, HD};
 }
 
-// bf16 inputs, D == 32: matrix-core kernels.  `workspace` (16-byte aligned, at least
-// bf16_workspace_bytes(p) bytes) receives the converted bias image.
-size_t bf16_workspace_bytes(const Problem& p);
-hipError_t launch_bf16_mfma(const Problem& p, void* workspace, hipStream_t stream);
-
-// Any D <= 64, fp32 or bf16 inputs: plain fp32 kernel.
-hipError_t launch_general(const Problem& p, bool bf16, hipStream_t stream);
-
-// Partial softmax states (state mode above), rows = B * I * N * H queries of D values:
-// (acc, m, l) <- merge((acc, m, l), (acc_t, m_t, l_t)), and out = acc / l, lse = m + ln l.
-hipError_t launch_state_merge(float* acc, float* m, float* l, const float* acc_t, const float* m_t,
-                              const float* l_t, int64_t rows, int64_t D, hipStream_t stream);
-hipError_t launch_state_finalize(const float* acc, const float* m, const float* l, float* out, float* lse,
-                                 int64_t rows, int64_t D, hipStream_t stream);
-
 // Backward (starting node): gradients for the upstream gradient dout, from the forward's
 // out and lse.  dq, dk, dv like q; dbias [B, H, N, N] summed over the I rows held.
 struct BwdProblem {
@@ -77,6 +62,38 @@ struct BwdProblem {
     int64_t B, H, I, N, D;
 };
 hipError_t launch_backward(const BwdProblem& p, bool bf16, hipStream_t stream);
+
+// bf16 inputs, D == 32: matrix-core kernels.  `workspace` (16-byte aligned, at least
+// bf16_workspace_bytes(p) bytes) receives the converted bias image.
+size_t bf16_workspace_bytes(const Problem& p);
+hipError_t launch_bf16_mfma(const Problem& p, void* workspace, hipStream_t stream);
+
+// The bias image on its own.  Layout: per (b, h), column block jb of IMG_BJ query columns
+// and key block n (key blocks follow the key tiles, see BlockPlan), one IMG_BJ x IMG_BK
+// fp32 tile at img + ((b*H + h) * n_jb + jb) * nblk + n) * IMG_BJ * IMG_BK holding
+// (bias + mask) * sqrt(D), -inf past the block's last key; row jj (a query column) has its
+// 16-byte chunk `part` (keys 4*part .. 4*part+3) at position img_chunk(jj, part).
+constexpr int IMG_BJ = 128;
+constexpr int IMG_BK = 32;
+__host__ __device__ constexpr int img_chunk(int jj, int part) { return part ^ (jj & 7); }
+int64_t bias_image_blocks(const Problem& p);   // nblk
+hipError_t launch_bias_image(const Problem& p, float* img, hipStream_t stream);
+
+// Backward on matrix cores (bf16, D == 32).  Workspace: the bias image (keys in one tile),
+// dout rounded to bf16 and delta = dout . out per query; bwd_mfma_workspace_bytes() bytes.
+size_t bwd_mfma_workspace_bytes(const BwdProblem& p);
+hipError_t launch_backward_mfma(const BwdProblem& p, void* workspace, hipStream_t stream);
+
+// Any D <= 64, fp32 or bf16 inputs: plain fp32 kernel.
+hipError_t launch_general(const Problem& p, bool bf16, hipStream_t stream);
+
+// Partial softmax states (state mode above), rows = B * I * N * H queries of D values:
+// (acc, m, l) <- merge((acc, m, l), (acc_t, m_t, l_t)), and out = acc / l, lse = m + ln l.
+hipError_t launch_state_merge(float* acc, float* m, float* l, const float* acc_t, const float* m_t,
+                              const float* l_t, int64_t rows, int64_t D, hipStream_t stream);
+hipError_t launch_state_finalize(const float* acc, const float* m, const float* l, float* out, float* lse,
+                                 int64_t rows, int64_t D, hipStream_t stream);
+
 
 // Start of key tile t when N keys are cut into T near-equal contiguous tiles
 // (the first N mod T tiles hold one key more).

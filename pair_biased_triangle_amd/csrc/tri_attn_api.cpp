@@ -325,8 +325,25 @@ int tri_attn_bwd(const void* q, const void* k, const void* v, const void* bias, 
             if (overlaps(outputs[a].p, outputs[a].bytes, outputs[o].p, outputs[o].bytes)) return TRI_ATTN_ERR_ALIAS;
     }
     const tri_attn::BwdProblem p{q, k, v, bias, mask, out, lse, dout, dq, dk, dv, dbias, B, H, I, N, D};
-    const hipError_t e = tri_attn::launch_backward(p, dtype == TRI_ATTN_BF16, static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? TRI_ATTN_OK : hip_fail(e);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    // matrix cores for bf16 with D == 32 when the fp32 tensors allow 16-byte accesses
+    const bool mfma = uses_matrix_cores(dtype, D) && aligned(out, 16) && aligned(dout, 16) && aligned(dq, 16) &&
+                      aligned(dk, 16) && aligned(dv, 16);
+    if (!mfma) {
+        const hipError_t e = tri_attn::launch_backward(p, dtype == TRI_ATTN_BF16, s);
+        return e == hipSuccess ? TRI_ATTN_OK : hip_fail(e);
+    }
+    hipMemPool_t pool = nullptr;
+    hipError_t e = workspace_pool(&pool);
+    if (e != hipSuccess) return hip_fail(e);
+    void* own = nullptr;
+    e = hipMallocFromPoolAsync(&own, tri_attn::bwd_mfma_workspace_bytes(p), pool, s);
+    if (e != hipSuccess) return hip_fail(e);
+    e = tri_attn::launch_backward_mfma(p, own, s);
+    const hipError_t ef = hipFreeAsync(own, s);
+    if (e != hipSuccess) return hip_fail(e);
+    if (ef != hipSuccess) return hip_fail(ef);
+    return TRI_ATTN_OK;
 }
 
 int pair_bias_attn_fwd(const void* q, const void* k, const void* v, const void* bias, const float* mask, float* out,

@@ -1,13 +1,15 @@
 """GPU parity of the backward (tri_attn_bwd) against the fp64 oracle's gradients.
 
-Two bars, both stated relative to the largest reference gradient of the tensor
-(gradients of the bias are sums over every row i and grow with I):
+Bars, stated relative to the largest reference gradient of the tensor (gradients of
+the bias are sums over every row i and grow with I):
   * the kernels alone, fed the oracle's exact forward statistics (out, lse rounded to
-    fp32): max |gpu - oracle| <= 1e-4 * max(1, max|oracle|) -- fp32 arithmetic over sums
-    of up to N*I terms;
-  * end to end, from the GPU's own forward (tri_attn_fwd_lse): the fp32 path keeps the
-    same bar; the bf16 path inherits the forward's error (probabilities rounded to bf16,
-    |out| and |lse| errors up to ~5e-3), so its bar is 2e-2 * max(1, max|oracle|).
+    fp32): the fp32 path (fp32 inputs, or bf16 with D != 32) computes in fp32 throughout,
+    max |gpu - oracle| <= 1e-4 * max(1, max|oracle|) over sums of up to N*I terms; the
+    matrix-core path (bf16, D == 32) rounds dout, P and dS to bf16 as product operands
+    (relative 2^-9 each), so its bar is the bf16 one, 1e-2 * max(1, max|oracle|);
+  * end to end, from the GPU's own forward (tri_attn_fwd_lse): the fp32 path keeps 1e-4;
+    the bf16 path also inherits the forward's error (|out| and |lse| errors up to
+    ~5e-3), so its bar is 2e-2 * max(1, max|oracle|).
 """
 import numpy as np
 import pytest
@@ -54,9 +56,11 @@ def gpu_bwd(torch, w, dout, out, lse):
     return [t.cpu().numpy() for t in g]
 
 
-@pytest.mark.parametrize("dtype,I,N,D", [("bf16", 20, 130, 32), ("fp32", 9, 70, 16), ("fp32", 5, 33, 64),
-                                         ("bf16", 3, 200, 48)])
-def test_kernels_with_exact_statistics(torch_dev, dtype, I, N, D):
+@pytest.mark.parametrize("dtype,I,N,D,bar", [("bf16", 20, 130, 32, 1e-2), ("bf16", 7, 33, 32, 1e-2),
+                                             ("bf16", 2, 300, 32, 1e-2), ("fp32", 9, 70, 16, 1e-4),
+                                             ("fp32", 5, 33, 64, 1e-4), ("bf16", 3, 200, 48, 1e-4),
+                                             ("fp32", 4, 40, 32, 1e-4)])
+def test_kernels_with_exact_statistics(torch_dev, dtype, I, N, D, bar):
     w, dout = case(dtype, I, N, D)
     say(f"[bwd] exact statistics {dtype} I={I} N={N} D={D}")
     out, lse = oracle.tri_attn(w.q, w.k, w.v, w.bias, w.mask)
@@ -64,7 +68,7 @@ def test_kernels_with_exact_statistics(torch_dev, dtype, I, N, D):
                   torch_dev.from_numpy(lse.astype(np.float32)).cuda())
     ref = oracle.tri_attn_bwd(w.q, w.k, w.v, w.bias, w.mask, dout)
     for n, g, r in zip(NAMES, got, ref):
-        compare_rel(g, r, 1e-4, f"{n} {dtype}")
+        compare_rel(g, r, bar, f"{n} {dtype} D={D}")
 
 
 @pytest.mark.parametrize("dtype,I,N,D,bar", [("bf16", 24, 160, 32, 2e-2), ("fp32", 12, 96, 32, 1e-4)])
@@ -80,9 +84,10 @@ def test_end_to_end(torch_dev, dtype, I, N, D, bar):
         compare_rel(g, r, bar, f"{n} {dtype}")
 
 
-def test_masked_rows_and_keys(torch_dev):
+@pytest.mark.parametrize("dtype,bar", [("fp32", 1e-4), ("bf16", 1e-2)])
+def test_masked_rows_and_keys(torch_dev, dtype, bar):
     """Dropped keys get no gradient; a batch element whose keys are all dropped gets none."""
-    w, dout = case("fp32", 6, 40, 32, B=2, mask_last=0)
+    w, dout = case(dtype, 6, 40, 32, B=2, mask_last=0)
     mask = np.zeros((2, 40), dtype=np.float32)
     mask[0, [3, 17, 39]] = -np.inf
     mask[1, :] = -np.inf
@@ -100,13 +105,14 @@ def test_masked_rows_and_keys(torch_dev):
     assert np.all(dbias[0][..., [3, 17, 39]] == 0)
     ref = oracle.tri_attn_bwd(w.q, w.k, w.v, w.bias, mask, dout)
     for n, a, r in zip(NAMES, (dq, dk, dv, dbias), ref):
-        compare_rel(a, r, 1e-4, f"masked {n}")
+        compare_rel(a, r, bar, f"masked {n} {dtype}")
 
 
-def test_row_shares_add_up(torch_dev):
+@pytest.mark.parametrize("dtype,bar", [("fp32", 1e-4), ("bf16", 1e-2)])
+def test_row_shares_add_up(torch_dev, dtype, bar):
     """dbias of a row share is that share's sum: two halves add to the whole."""
     import pair_biased_triangle_amd as P
-    w, dout = case("bf16", 16, 64, 32, seed=71)
+    w, dout = case(dtype, 16, 64, 32, seed=71)
     out, lse = oracle.tri_attn(w.q, w.k, w.v, w.bias, w.mask)
     t = torch_dev
     parts = []
@@ -118,7 +124,7 @@ def test_row_shares_add_up(torch_dev):
                            t.from_numpy(sl(lse).astype(np.float32)).cuda(), t.from_numpy(sl(dout)).cuda())
         parts.append(g[3].cpu().numpy().astype(np.float64))
     ref = oracle.tri_attn_bwd(w.q, w.k, w.v, w.bias, w.mask, dout)[3]
-    compare_rel(parts[0] + parts[1], ref, 1e-4, "dbias of two row shares")
+    compare_rel(parts[0] + parts[1], ref, bar, f"dbias of two row shares {dtype}")
 
 
 def test_autograd_function(torch_dev):
