@@ -12,8 +12,9 @@ relates the kernel's live-measured average launch time to the bf16 dense MFMA pe
 
 `--pass` measures the other entry points on the same workload, one JSON line each:
   bwd        tri_attn_bwd (dq, dk, dv, row-summed dbias) from the forward's out and lse;
-             algorithmic FLOPs 10*B*H*I*N^2*D (the S recompute, dP, dQ, dK, dV products),
-             fp32 vector arithmetic -> roofline against the fp32 vector peak
+             algorithmic FLOPs 10*B*H*I*N^2*D (the S recompute, dP, dQ, dK, dV products);
+             bf16 with D = 32 runs on matrix cores (bf16 MFMA peak), other cases in fp32
+             vector arithmetic (fp32 vector peak)
   ending     tri_attn_fwd_ending (same FLOPs as the forward, bf16 MFMA peak)
   pair_bias  pair_bias_attn_fwd on the workload's first row (I = 1): bound by reading
              the bias -> roofline in GB/s against HBM
@@ -137,10 +138,15 @@ def other_pass(args, torch, P, W, cfg) -> dict:
         out, lse = P.tri_attn_fwd_lse(q, k, v, bias, mask, n_key_tiles=T)
         dout = torch.randn(q.shape, dtype=torch.float32, device="cuda", generator=torch.Generator("cuda").manual_seed(1))
         step = lambda: P.tri_attn_bwd(q, k, v, bias, mask, out, lse, dout)
-        work, unit, peak, bound = 2.5 * fwd_flops, "TFLOP/s", PEAK_FP32_TFLOPS, "alu"
         metric = "triangle-attention backward TFLOP/s (10·B·H·I·N²·D: S recompute, dP, dQ, dK, dV)"
-        kernels = "bwd_dq_kernel + bwd_dkdv_kernel + bwd_dbias_kernel (fp32 vector)"
-        dtype = "f32"
+        if cfg.dtype == "bf16" and D == 32:     # the matrix-core backward
+            work, unit, peak, bound = 2.5 * fwd_flops, "TFLOP/s", PEAK_BF16_TFLOPS, "mfma"
+            kernels = "bwd_prep_kernel + bwd_dq_mfma + bwd_dkdv_mfma + bwd_dbias_mfma (bf16 MFMA, fp32 accumulate)"
+            dtype = "bf16"
+        else:
+            work, unit, peak, bound = 2.5 * fwd_flops, "TFLOP/s", PEAK_FP32_TFLOPS, "alu"
+            kernels = "bwd_dq_kernel + bwd_dkdv_kernel + bwd_dbias_kernel (fp32 vector)"
+            dtype = "f32"
     elif args.which == "ending":
         if I != N:
             raise SystemExit("the ending orientation needs a workload with I == N")

@@ -45,6 +45,9 @@ constexpr float kSqrtD = 5.656854249492381f;
 constexpr float kScale = kLog2e / kSqrtD;        // S units (q.k + sqrt(D) bias) -> log2 units
 constexpr float kInvSqrtD = 0.17677669529663687f;
 constexpr int TILE_BYTES = 32 * D * 2;           // one wave's 32 x 32 bf16 tile in LDS
+#ifndef TRI_ATTN_DBIAS_AHEAD
+#define TRI_ATTN_DBIAS_AHEAD 3
+#endif
 
 #define LDS_ADDR(p) static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)(p)))
 
@@ -122,12 +125,24 @@ __device__ __forceinline__ void to_bf16(const f32x16& x, bf16x8& lo, bf16x8& hi)
 __device__ __forceinline__ float neg_lse2(float lse) { return lse == -INFINITY ? -INFINITY : -lse * kLog2e; }
 
 // ---------------------------------------------------------------------------------------
-__global__ void __launch_bounds__(256) bwd_prep_kernel(const float* dout, const float* out, __bf16* g16, float* delta,
-                                                       int64_t nq) {
-    const int64_t q = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-    if (q >= nq) return;
-    const f32x4* g = reinterpret_cast<const f32x4*>(dout + q * D);
-    const f32x4* o = reinterpret_cast<const f32x4*>(out + q * D);
+// One thread per (b, i, h, j) with j padded to NP: dout of query (b, i, j, h) rounded to
+// bf16, delta = dout . out, and lse / delta also written transposed, [b, i, h, j], so that
+// a lane can read 4 consecutive queries with one 16-byte load; padded j get lse = -inf
+// (no probability) and delta = 0.
+__global__ void __launch_bounds__(256) bwd_prep_kernel(BwdProblem p, __bf16* g16, float* delta, float* lseT,
+                                                       float* deltaT, int64_t NP) {
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    const int64_t total = p.B * p.I * p.H * NP;
+    if (t >= total) return;
+    const int64_t j = t % NP, lh = t / NP, h = lh % p.H, line = lh / p.H;   // line = b * I + i
+    if (j >= p.N) {
+        lseT[t] = -INFINITY;
+        deltaT[t] = 0.0f;
+        return;
+    }
+    const int64_t q = (line * p.N + j) * p.H + h;
+    const f32x4* g = reinterpret_cast<const f32x4*>(p.dout + q * D);
+    const f32x4* o = reinterpret_cast<const f32x4*>(p.out + q * D);
     float dl = 0.0f;
 #pragma unroll
     for (int a = 0; a < D / 8; ++a) {
@@ -138,6 +153,8 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(const float* dout, const 
         *reinterpret_cast<bf16x8*>(g16 + q * D + 8 * a) = __builtin_convertvector(gg, bf16x8);
     }
     delta[q] = dl;
+    deltaT[t] = dl;
+    lseT[t] = p.lse[q];
 }
 
 // ---------------------------------------------------------------------------------------
@@ -170,36 +187,46 @@ __global__ void __launch_bounds__(NTHR) bwd_dq_mfma(BwdProblem p, const float* i
     const uint32_t tile = LDS_ADDR(lds) + wave * TILE_BYTES;
     const float* img_row = img + (bh * n_jb + jb) * static_cast<int64_t>(nblk) * IMG_BJ * IMG_BK + jj * IMG_BK;
 
-    f32x16 dQ = {};
-    for (int n = 0; n < nblk; ++n) {
+    // operands of key block n: K, V rows (lane = key) and the bias image chunks of this query
+    struct Blk {
+        bf16x8 kA[2], vA[2];
+        f32x4 c[4];
+    };
+    auto fetch = [&](int n, Blk& X) {
         const int64_t key = static_cast<int64_t>(n) * IMG_BK + c;
         const int64_t ko = (row + (key < N ? key : N - 1)) * HD + h * D;   // padded keys: bias -inf
-        bf16x8 kA[2], vA[2];
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-            kA[m] = frag(k, ko + 16 * m + 8 * h2, true);
-            vA[m] = frag(v, ko + 16 * m + 8 * h2, true);
+            X.kA[m] = frag(k, ko + 16 * m + 8 * h2, true);
+            X.vA[m] = frag(v, ko + 16 * m + 8 * h2, true);
         }
-        f32x16 C;
         const float* t = img_row + static_cast<int64_t>(n) * IMG_BJ * IMG_BK;
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-            const f32x4 x = *reinterpret_cast<const f32x4*>(t + img_chunk(jj, 2 * a + h2) * 4);
+        for (int a = 0; a < 4; ++a) X.c[a] = *reinterpret_cast<const f32x4*>(t + img_chunk(jj, 2 * a + h2) * 4);
+    };
+    f32x16 dQ = {};
+    Blk cur, nxt;
+    fetch(0, cur);
+    for (int n = 0; n < nblk; ++n) {
+        if (n + 1 < nblk) fetch(n + 1, nxt);              // next block's loads fly during this block
+        f32x16 C;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) C[4 * a + e] = x[e];
-        }
-        f32x16 S = mfma(kA[0], qB[0], C);
-        S = mfma(kA[1], qB[1], S);
-        f32x16 dP = mfma(vA[0], gB[0], f32x16{});
-        dP = mfma(vA[1], gB[1], dP);
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) C[4 * a + e] = cur.c[a][e];
+        f32x16 S = mfma(cur.kA[0], qB[0], C);
+        S = mfma(cur.kA[1], qB[1], S);
+        f32x16 dP = mfma(cur.vA[0], gB[0], f32x16{});
+        dP = mfma(cur.vA[1], gB[1], dP);
         f32x16 dS;
 #pragma unroll
         for (int r = 0; r < 16; ++r) dS[r] = __builtin_amdgcn_exp2f(fmaf(S[r], kScale, nb)) * (dP[r] - dl);
         bf16x8 s0, s1, kT0, kT1;
         to_bf16(dS, s0, s1);
-        transpose_tile(tile, L, kA[0], kA[1], kT0, kT1);
+        transpose_tile(tile, L, cur.kA[0], cur.kA[1], kT0, kT1);
         dQ = mfma(kT0, s0, dQ);
         dQ = mfma(kT1, s1, dQ);
+        cur = nxt;
     }
     if (jok) {
         float* o = p.dq + qo;
@@ -214,20 +241,29 @@ __global__ void __launch_bounds__(NTHR) bwd_dq_mfma(BwdProblem p, const float* i
 }
 
 // ---------------------------------------------------------------------------------------
-__global__ void __launch_bounds__(NTHR, 2) bwd_dkdv_mfma(BwdProblem p, const __bf16* g16, const float* delta) {
-    __shared__ __attribute__((aligned(16))) char lds[NWAVE * 2 * TILE_BYTES];
+// imgT: the bias image of the transposed bias without the mask (built in the ending
+// orientation), so that tile (key block of IMG_BJ, query block of IMG_BK) row kk holds
+// bias[b, h, q, key] * sqrt(D) for 32 consecutive queries q (-inf past the last query):
+// the accumulator input of S for a lane that owns a key.  Dropped keys are zeroed at the end.
+__global__ void __launch_bounds__(NTHR, 2) bwd_dkdv_mfma(BwdProblem p, const float* imgT, const __bf16* g16,
+                                                         const float* lseT, const float* deltaT, int n_kb,
+                                                         int nqblk, int64_t NP) {
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int c = lane & 31, h2 = lane >> 5;
     const int64_t N = p.N, H = p.H, HD = H * D;
     const int64_t bh = blockIdx.z, b = bh / H, h = bh % H, i = blockIdx.y;
-    const int64_t key = static_cast<int64_t>(blockIdx.x) * (NWAVE * 32) + wave * 32 + c;
+    const int kb = blockIdx.x;                            // block of IMG_BJ keys
+    const int kk = wave * 32 + c;                         // key inside the block
+    const int64_t key = static_cast<int64_t>(kb) * IMG_BJ + kk;
     const bool kok = key < N;
     const int64_t row = (b * p.I + i) * N;
     const __bf16* q = static_cast<const __bf16*>(p.q);
     const __bf16* k = static_cast<const __bf16*>(p.k);
     const __bf16* v = static_cast<const __bf16*>(p.v);
-    const uint16_t* bias = static_cast<const uint16_t*>(p.bias);
     const int64_t ko = (row + key) * HD + h * D;
+    const float* lse_l = lseT + ((b * p.I + i) * H + h) * NP + 4 * h2;
+    const float* dl_l = deltaT + ((b * p.I + i) * H + h) * NP + 4 * h2;
+    const float* img_row = imgT + (bh * n_kb + kb) * static_cast<int64_t>(nqblk) * IMG_BJ * IMG_BK + kk * IMG_BK;
 
     bf16x8 kB[2], vB[2];
 #pragma unroll
@@ -235,54 +271,71 @@ __global__ void __launch_bounds__(NTHR, 2) bwd_dkdv_mfma(BwdProblem p, const __b
         kB[m] = frag(k, ko + 16 * m + 8 * h2, kok);
         vB[m] = frag(v, ko + 16 * m + 8 * h2, kok);
     }
-    const float mk = !kok ? -INFINITY : (p.mask ? p.mask[b * N + key] : 0.0f);
+    const bool dropped = !kok || (p.mask && p.mask[b * N + (kok ? key : 0)] == -INFINITY);
     const TileLane L = tile_lane(lane);
+    __shared__ __attribute__((aligned(16))) char lds[NWAVE * 2 * TILE_BYTES];
     const uint32_t tile_g = LDS_ADDR(lds) + wave * 2 * TILE_BYTES, tile_q = tile_g + TILE_BYTES;
 
-    f32x16 dK = {}, dV = {};
-    for (int64_t qb = 0; qb < N; qb += 32) {
-        const int64_t jq = qb + c;                        // this lane's row of the A operands
+    // operands of query block n: Q, dO rows (lane = query), and for this lane's key the
+    // accumulator input, lse and delta of the 16 query rows 8a + 4h2 + e of its registers
+    struct Blk {
+        bf16x8 qA[2], gA[2];
+        f32x4 c[4], nl[4], dl[4];
+    };
+    auto fetch = [&](int n, Blk& X) {
+        const int64_t qb = static_cast<int64_t>(n) * IMG_BK;
+        const int64_t jq = qb + c;
         const bool jok = jq < N;
         const int64_t qo = (row + jq) * HD + h * D;
-        bf16x8 qA[2], gA[2];
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-            qA[m] = frag(q, qo + 16 * m + 8 * h2, jok);
-            gA[m] = frag(g16, qo + 16 * m + 8 * h2, jok);
+            X.qA[m] = frag(q, qo + 16 * m + 8 * h2, jok);
+            X.gA[m] = frag(g16, qo + 16 * m + 8 * h2, jok);
         }
-        // C for the 16 query rows of this lane's accumulator registers
-        f32x16 C;
+        const float* t = img_row + static_cast<int64_t>(n) * IMG_BJ * IMG_BK;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int64_t jr = qb + 8 * (r / 4) + 4 * h2 + (r % 4);
-            const float bv = jr < N ? bf16_to_f32(bias[(bh * N + jr) * N + (kok ? key : 0)]) : 0.0f;
-            C[r] = jr < N ? (bv + mk) * kSqrtD : -INFINITY;
+        for (int a = 0; a < 4; ++a) {
+            X.c[a] = *reinterpret_cast<const f32x4*>(t + img_chunk(kk, 2 * a + h2) * 4);
+            X.nl[a] = *reinterpret_cast<const f32x4*>(lse_l + qb + 8 * a);
+            X.dl[a] = *reinterpret_cast<const f32x4*>(dl_l + qb + 8 * a);
         }
+    };
+    f32x16 dK = {}, dV = {};
+    Blk cur, nxt;
+    fetch(0, cur);
+    for (int n = 0; n < nqblk; ++n) {
+        if (n + 1 < nqblk) fetch(n + 1, nxt);             // next block's loads fly during this block
+        const bf16x8 (&qA)[2] = cur.qA;
+        const bf16x8 (&gA)[2] = cur.gA;
+        f32x16 C, nl, dl;
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                C[4 * a + e] = cur.c[a][e];
+                nl[4 * a + e] = cur.nl[a][e];
+                dl[4 * a + e] = cur.dl[a][e];
+            }
         f32x16 S = mfma(qA[0], kB[0], C);
         S = mfma(qA[1], kB[1], S);
         f32x16 dP = mfma(gA[0], vB[0], f32x16{});
         dP = mfma(gA[1], vB[1], dP);
-        // P overwrites S and dS overwrites dP, row by row with that row's lse and delta
+        // P overwrites S and dS overwrites dP
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int64_t jr = qb + 8 * (r / 4) + 4 * h2 + (r % 4);
-            const bool ok = jr < N;
-            const float nb = ok ? neg_lse2(p.lse[(row + jr) * H + h]) : -INFINITY;
-            const float dl = ok ? delta[(row + jr) * H + h] : 0.0f;
-            S[r] = __builtin_amdgcn_exp2f(fmaf(S[r], kScale, nb));
-            dP[r] = S[r] * (dP[r] - dl);
+            S[r] = __builtin_amdgcn_exp2f(fmaf(S[r], kScale, neg_lse2(nl[r])));
+            dP[r] = S[r] * (dP[r] - dl[r]);
         }
-        const f32x16& P = S;
-        const f32x16& dS = dP;
         bf16x8 p0, p1, s0, s1, gT0, gT1, qT0, qT1;
-        to_bf16(P, p0, p1);
-        to_bf16(dS, s0, s1);
+        to_bf16(S, p0, p1);
+        to_bf16(dP, s0, s1);
         transpose_tile(tile_g, L, gA[0], gA[1], gT0, gT1);
         transpose_tile(tile_q, L, qA[0], qA[1], qT0, qT1);
         dV = mfma(gT0, p0, dV);
         dV = mfma(gT1, p1, dV);
         dK = mfma(qT0, s0, dK);
         dK = mfma(qT1, s1, dK);
+        cur = nxt;
     }
     if (kok) {
 #pragma unroll
@@ -290,8 +343,8 @@ __global__ void __launch_bounds__(NTHR, 2) bwd_dkdv_mfma(BwdProblem p, const __b
             f32x4 xk, xv;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                xk[e] = dK[4 * a + e] * kInvSqrtD;
-                xv[e] = dV[4 * a + e];
+                xk[e] = dropped ? 0.0f : dK[4 * a + e] * kInvSqrtD;
+                xv[e] = dropped ? 0.0f : dV[4 * a + e];
             }
             *reinterpret_cast<f32x4*>(p.dk + ko + 8 * a + 4 * h2) = xk;
             *reinterpret_cast<f32x4*>(p.dv + ko + 8 * a + 4 * h2) = xv;
@@ -331,26 +384,49 @@ __global__ void __launch_bounds__(NTHR) bwd_dbias_mfma(BwdProblem p, const float
             for (int e = 0; e < 4; ++e) C[4 * a + e] = x[e];
         }
     }
-    f32x16 acc = {};
-    for (int64_t i = 0; i < p.I; ++i) {
+    // operands of row i: K, V (this wave's keys), Q, dO (its queries), lse and delta
+    struct Row {
+        bf16x8 kA[2], vA[2], qB[2], gB[2];
+        float lse, dl;
+    };
+    auto fetch = [&](int64_t i, Row& R) {
         const int64_t row = (b * p.I + i) * N;
         const int64_t ko = (row + kc) * HD + h * D, qo = (row + j) * HD + h * D;
-        bf16x8 kA[2], vA[2], qB[2], gB[2];
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-            kA[m] = frag(k, ko + 16 * m + 8 * h2, true);
-            vA[m] = frag(v, ko + 16 * m + 8 * h2, true);
-            qB[m] = frag(q, qo + 16 * m + 8 * h2, jok);
-            gB[m] = frag(g16, qo + 16 * m + 8 * h2, jok);
+            R.kA[m] = frag(k, ko + 16 * m + 8 * h2, true);
+            R.vA[m] = frag(v, ko + 16 * m + 8 * h2, true);
+            R.qB[m] = frag(q, qo + 16 * m + 8 * h2, jok);
+            R.gB[m] = frag(g16, qo + 16 * m + 8 * h2, jok);
         }
-        const float nb = jok ? neg_lse2(p.lse[(row + j) * H + h]) : -INFINITY;
-        const float dl = jok ? delta[(row + j) * H + h] : 0.0f;
-        f32x16 S = mfma(kA[0], qB[0], C);
-        S = mfma(kA[1], qB[1], S);
-        f32x16 dP = mfma(vA[0], gB[0], f32x16{});
-        dP = mfma(vA[1], gB[1], dP);
+        R.lse = jok ? p.lse[(row + j) * H + h] : -INFINITY;
+        R.dl = jok ? delta[(row + j) * H + h] : 0.0f;
+    };
+    f32x16 acc = {};
+    auto row_step = [&](const Row& R) {
+        const float nb = neg_lse2(R.lse);
+        f32x16 S = mfma(R.kA[0], R.qB[0], C);
+        S = mfma(R.kA[1], R.qB[1], S);
+        f32x16 dP = mfma(R.vA[0], R.gB[0], f32x16{});
+        dP = mfma(R.vA[1], R.gB[1], dP);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[r] = fmaf(__builtin_amdgcn_exp2f(fmaf(S[r], kScale, nb)), dP[r] - dl, acc[r]);
+        for (int r = 0; r < 16; ++r) acc[r] = fmaf(__builtin_amdgcn_exp2f(fmaf(S[r], kScale, nb)), dP[r] - R.dl, acc[r]);
+    };
+    // a ring of AHEAD + 1 rows: while row i is computed, rows i+1 .. i+AHEAD are loading
+    // (row r lives in slot r % (AHEAD + 1); the loop is unrolled so every slot is static)
+    constexpr int AHEAD = TRI_ATTN_DBIAS_AHEAD;
+    Row ring[AHEAD + 1];
+#pragma unroll
+    for (int t = 0; t < AHEAD; ++t)
+        if (t < p.I) fetch(t, ring[t]);
+    for (int64_t i = 0; i < p.I; i += AHEAD + 1) {
+#pragma unroll
+        for (int u = 0; u <= AHEAD; ++u) {
+            if (i + u < p.I) {
+                if (i + u + AHEAD < p.I) fetch(i + u + AHEAD, ring[(u + AHEAD) % (AHEAD + 1)]);
+                row_step(ring[u]);
+            }
+        }
     }
     if (jok) {
         float* o = p.dbias + (bh * N + j) * N;
@@ -364,33 +440,59 @@ __global__ void __launch_bounds__(NTHR) bwd_dbias_mfma(BwdProblem p, const float
 
 }  // namespace
 
-size_t bwd_mfma_workspace_bytes(const BwdProblem& p) {
-    Problem f{p.q, p.k, p.v, p.bias, p.mask, nullptr, p.B, p.H, p.I, p.N, p.D, 1};
-    const size_t img = bf16_workspace_bytes(f);
-    const size_t nq = static_cast<size_t>(p.B * p.I * p.N * p.H);
-    return img + nq * D * 2 + nq * 4;
+namespace {
+struct BwdLayout {
+    Problem fwd, tr;        // image problems: the bias, and its transpose without the mask
+    int64_t NP, nq;
+    size_t img, imgT, g16, delta, lseT, deltaT, total;   // byte offsets / total
+};
+
+BwdLayout bwd_layout(const BwdProblem& p) {
+    BwdLayout L;
+    L.fwd = Problem{p.q, p.k, p.v, p.bias, p.mask, nullptr, p.B, p.H, p.I, p.N, p.D, 1};
+    L.tr = Problem{p.q, p.k, p.v, p.bias, nullptr, nullptr, p.B, p.H, p.N, p.N, p.D, 1};
+    L.tr.ending = true;
+    L.NP = (p.N + IMG_BK - 1) / IMG_BK * IMG_BK;
+    L.nq = p.B * p.I * p.N * p.H;
+    const size_t per_line = static_cast<size_t>(p.B * p.I * p.H * L.NP) * 4;
+    L.img = 0;
+    L.imgT = L.img + bf16_workspace_bytes(L.fwd);
+    L.g16 = L.imgT + bf16_workspace_bytes(L.tr);
+    L.delta = L.g16 + static_cast<size_t>(L.nq) * D * 2;
+    L.lseT = L.delta + (static_cast<size_t>(L.nq) * 4 + 15) / 16 * 16;
+    L.deltaT = L.lseT + per_line;
+    L.total = L.deltaT + per_line;
+    return L;
 }
+}  // namespace
+
+size_t bwd_mfma_workspace_bytes(const BwdProblem& p) { return bwd_layout(p).total; }
 
 hipError_t launch_backward_mfma(const BwdProblem& p, void* workspace, hipStream_t stream) {
-    Problem f{p.q, p.k, p.v, p.bias, p.mask, nullptr, p.B, p.H, p.I, p.N, p.D, 1};
+    const BwdLayout Ly = bwd_layout(p);
     const int64_t n_jb = (p.N + IMG_BJ - 1) / IMG_BJ;
-    const int64_t nblk = bias_image_blocks(f);
-    const int64_t nq = p.B * p.I * p.N * p.H;
+    const int64_t nblk = bias_image_blocks(Ly.fwd);      // 32-key blocks
     char* ws = static_cast<char*>(workspace);
-    float* img = reinterpret_cast<float*>(ws);
-    __bf16* g16 = reinterpret_cast<__bf16*>(ws + bf16_workspace_bytes(f));
-    float* delta = reinterpret_cast<float*>(ws + bf16_workspace_bytes(f) + static_cast<size_t>(nq) * D * 2);
-    if (p.D != D || (nq + 255) / 256 > 0x7FFFFFFF || (p.N + 63) / 64 > 65535) return hipErrorInvalidConfiguration;
-    hipError_t e = launch_bias_image(f, img, stream);
+    float* img = reinterpret_cast<float*>(ws + Ly.img);
+    float* imgT = reinterpret_cast<float*>(ws + Ly.imgT);
+    __bf16* g16 = reinterpret_cast<__bf16*>(ws + Ly.g16);
+    float* delta = reinterpret_cast<float*>(ws + Ly.delta);
+    float* lseT = reinterpret_cast<float*>(ws + Ly.lseT);
+    float* deltaT = reinterpret_cast<float*>(ws + Ly.deltaT);
+    const int64_t n_prep = p.B * p.I * p.H * Ly.NP;
+    if (p.D != D || (n_prep + 255) / 256 > 0x7FFFFFFF || (p.N + 63) / 64 > 65535) return hipErrorInvalidConfiguration;
+    hipError_t e = launch_bias_image(Ly.fwd, img, stream);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd_prep_kernel, dim3(static_cast<unsigned>((nq + 255) / 256)), dim3(256), 0, stream, p.dout,
-                       p.out, g16, delta, nq);
+    if ((e = launch_bias_image(Ly.tr, imgT, stream)) != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_prep_kernel, dim3(static_cast<unsigned>((n_prep + 255) / 256)), dim3(256), 0, stream, p, g16,
+                       delta, lseT, deltaT, Ly.NP);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const dim3 lines(static_cast<unsigned>(n_jb), static_cast<unsigned>(p.I), static_cast<unsigned>(p.B * p.H));
     hipLaunchKernelGGL(bwd_dq_mfma, lines, dim3(NTHR), 0, stream, p, img, g16, delta, static_cast<int>(n_jb),
                        static_cast<int>(nblk));
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd_dkdv_mfma, lines, dim3(NTHR), 0, stream, p, g16, delta);
+    hipLaunchKernelGGL(bwd_dkdv_mfma, lines, dim3(NTHR), 0, stream, p, imgT, g16, lseT, deltaT,
+                       static_cast<int>(n_jb), static_cast<int>(nblk), Ly.NP);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const unsigned nt = static_cast<unsigned>((p.N + 63) / 64);
     hipLaunchKernelGGL(bwd_dbias_mfma, dim3(nt, nt, static_cast<unsigned>(p.B * p.H)), dim3(NTHR), 0, stream, p, img,
