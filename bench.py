@@ -47,15 +47,17 @@ KERNEL_NAME = "bf16_mfma_kernel"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 
+KERNEL_SOURCES = ("kernel_bf16_mfma.hip", "launch.h")   # what the forward's kernels are built from
+
+
 def kernel_source_digest() -> str:
-    """SHA-256 over the HIP sources of the library: stored traffic counters are only
+    """SHA-256 over the sources of the forward's kernels: stored traffic counters are only
     reported while the kernels they were taken on are unchanged."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "pair_biased_triangle_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".h", ".cpp")):
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
 
 
