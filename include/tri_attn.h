@@ -30,14 +30,18 @@
  * Results: a row whose keys are all -inf yields out = 0 (never NaN).  The bf16 path
  * computes q.k and P.V on bf16 matrix cores with fp32 accumulation; softmax statistics
  * are fp32 and the probabilities are rounded to bf16 (nearest even) only as the P.V
- * operand.  The fp32 path computes in fp32 throughout.
+ * operand.  It takes bias + mask relative to each query's largest bias + mask over the
+ * call's keys (softmax does not change when all scores of a query move together),
+ * times sqrt(D) and rounded to fp16: every such value is <= 0, those below the fp16 range
+ * become -inf (weight 0).  The fp32 path computes in fp32 throughout.
  *
  * Ownership and memory: every pointer is a device pointer owned by the caller; the
  * library keeps none of them after returning.  q, k, v, bias and mask are only read and
  * may alias one another; outputs must not overlap any input.  q, k, v, bias and out must be
  * 16-byte aligned, mask 4-byte aligned.  The bf16 matrix-core path (D == 32) first
- * converts the bias into an fp32 image of tri_attn_workspace_bytes() bytes: roughly
- * 4 * B * H * N * N * (1 + 127/N) bytes.  tri_attn_fwd and tri_attn_fwd_rows obtain it
+ * converts the bias into an fp16 image plus one fp32 reference per query, together
+ * tri_attn_workspace_bytes() bytes: roughly 2 * B * H * N * N * (1 + 255/N) bytes.
+ * tri_attn_fwd and tri_attn_fwd_rows obtain it
  * stream-ordered on `stream` (hipMallocFromPoolAsync / hipFreeAsync) from a memory pool the
  * library creates once per device; the pool keeps freed memory reserved for later calls
  * (up to the largest workspace used) until the process ends.  tri_attn_fwd_rows_ws takes

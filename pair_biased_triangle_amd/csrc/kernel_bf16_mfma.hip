@@ -2,43 +2,46 @@
 //
 // Per batch b and head h the rows i are independent attention problems that share one
 // N x N "triangular" bias bias[b,h,j,k] ("Fold-CP", Table 1 "Triangle Attention" and
-// Figure 2(a)).  A workgroup owns R = 8 rows i and BJ = 128 query columns j of one
-// (b, h) and streams the key axis in blocks of 32 keys.  Key blocks follow the ring-step
-// tiles (Table 1's caption): they start at every tile start and are cut short at every
-// tile end, so each tile is folded into the running softmax state as one ring step
-// (the running state is the merged state of the tiles seen so far).
+// Figure 2(a)).  A workgroup owns R lines (rows i) and BJ query columns j of one (b, h)
+// and streams the key axis in blocks of 32 keys.  Key blocks follow the ring-step tiles
+// (Table 1's caption): they start at every tile start and are cut short at every tile
+// end, so each tile is folded into the running softmax state as one ring step (the
+// running state is the merged state of the tiles seen so far).
 //
 // Two kernels run per call:
-//   1. bias_image_kernel: converts the bias once into the fp32 image the main kernel
-//      stages verbatim: per (b, h, column block, key block) a 128 x 32 tile holding
-//      (bias + mask) * sqrt(D), -inf for keys past the tile end, 16-byte chunks swizzled
-//      against LDS bank conflicts.  Every row i of the workgroup reuses it from LDS.
-//   2. bf16_mfma_kernel: per key block the workgroup copies K and V of its 8 rows
+//   1. bias_image16_kernel: per query j it finds the reference r_j, the largest
+//      bias + mask over the call's keys, and writes the fp16 image the main kernel stages
+//      verbatim: per (b, h, column block, key block) a BJ x 32 tile of
+//      (bias + mask - r_j) * log2(e), -inf for keys past the tile end.  Softmax does not
+//      change when every score of a query moves by the same amount, and relative to r_j
+//      every value is <= 0, so fp16 keeps 11 bits where the weights are large and a value
+//      too negative for fp16 becomes -inf, whose weight is 0 anyway.
+//   2. bf16_mfma_kernel: per key block the workgroup copies K and V of its R lines
 //      ([key][d], natural layout) and the bias tile straight from global memory into
-//      LDS (global_load_lds_dwordx4, double buffered, no registers on the way).  Each
-//      of the 8 waves owns 2 rows x 2 query tiles of 32 and runs, per (row, tile):
-//        S^T = K Q^T + C       two v_mfma_f32_32x32x16_bf16, C = the bias tile, so
-//                              S = sqrt(D) * (q.k / sqrt(D) + bias + mask) in fp32
-//        p   = 2^(S * log2(e)/sqrt(D) + nb),  nb = -m_ref * log2(e)/sqrt(D)
+//      LDS (global_load_lds_dwordx4, a ring of stages, no registers on the way).  Each
+//      of the 8 waves owns 2 lines x 2 query tiles of 32 and runs, per (line, tile):
+//        S^T = K Q^T           two v_mfma_f32_32x32x16_bf16
+//        x   = S * log2(e)/sqrt(D) + c      one v_fma_mix_f32 per score: c is the fp16
+//                              image value, taken from its half register as it is
+//        p   = 2^x             (x is the score minus r_j, in log2 units)
 //        O^T += V^T P^T        two v_mfma_f32_32x32x16_bf16 on the bf16-rounded p;
 //                              V^T comes from ds_read_b64_tr_b16 on the [key][d] tile
-//      The row sum is taken per lane with v_dot2_f32_bf16 on the rounded p.  In the
-//      fixed-reference blocks the four units run as a software pipeline in which every
-//      group of four exponentials carries one matrix instruction of the neighbouring
-//      units (compute_block_pipe).
+//      The row sum is taken per lane with v_dot2_f32_bf16 on the rounded p.  The four
+//      units run as a software pipeline in which every group of four exponentials carries
+//      one matrix instruction of the neighbouring units (compute_block_pipe).
 //
-// Softmax reference.  The first key block sets m_ref to its exact row maximum (one
-// cross-lane step: in the 32x32 output layout lanes l and l^32 hold the 16 + 16 keys of
-// one query).  Later blocks keep that reference -- O and l share it, so the result is
-// exact whatever it is -- and need no maximum, no cross-lane step and no branch.  At the
+// Softmax reference.  r_j is the reference of the fast pass: the scores are not shifted
+// by their running maximum -- O and l share the reference, so the result is exact
+// whatever it is -- so no block needs a maximum, a cross-lane step or a branch.  At the
 // end every lane checks that its normaliser lies in [2^-64, 2^64] and its accumulator is
-// finite; if any lane of the workgroup fails (scores that jump far above the first
-// block's maximum, or rows whose keys are all masked), the workgroup recomputes its
-// whole key loop with the exact running maximum refreshed on every block.
+// finite; if any lane of the workgroup fails (q.k far from 0, or rows whose keys are all
+// masked), the workgroup recomputes its whole key loop with the exact running maximum m
+// (log2 units) refreshed on every block.  The natural log of the normaliser adds the
+// reference back: lse = r_j + m ln 2 + ln l (m = 0 in the fast pass).
 //
-// Workgroup ids are remapped so that each XCD walks a contiguous range of (b, h, row
-// group, column block) tiles of 4 row groups x 8 column blocks: the workgroups an XCD runs
-// together share each row group's K/V stream 8 ways and each bias tile 4 ways in its L2.
+// Workgroup ids are remapped so that each XCD walks a contiguous range of (b, h, line
+// group, column block) tiles: the workgroups an XCD runs together share each line
+// group's K/V stream and each bias tile in its L2.
 #include "launch.h"
 
 #include <cmath>
@@ -48,57 +51,79 @@ namespace tri_attn {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 #define GLOBAL_PTR(T, p) ((const __attribute__((address_space(1))) T*)(p))
 
 constexpr int D = 32;
 constexpr int BK = 32;                      // keys per block
-constexpr int R = 8;                        // rows i per workgroup
-constexpr int QT = 4;                       // 32-wide query tiles per workgroup
-constexpr int BJ = 32 * QT;                 // query columns per workgroup
-constexpr int RW = 2;                       // rows per wave
-constexpr int TW = 2;                       // query tiles per wave
-constexpr int NWAVE = (R / RW) * (QT / TW);
+#ifndef TRI_ATTN_ROWS
+#define TRI_ATTN_ROWS 4
+#endif
+constexpr int R = TRI_ATTN_ROWS;            // lines per workgroup
+constexpr int NWAVE = 8;
 constexpr int NTHR = 64 * NWAVE;
+constexpr int RW = 2;                       // lines per wave
+constexpr int TW = 2;                       // query tiles per wave
+constexpr int QT = NWAVE * RW * TW / R;     // 32-wide query tiles per workgroup
+constexpr int BJ = 32 * QT;                 // query columns per workgroup
 constexpr int NXCD = 8;
+static_assert(R == 4 || R == 8, "4 lines x 256 columns or 8 lines x 128 columns");
+static_assert((R / RW) * (QT / TW) == NWAVE, "every wave owns RW x TW units");
 #ifndef TRI_ATTN_STAGES
-#define TRI_ATTN_STAGES 3
+#define TRI_ATTN_STAGES 4
 #endif
 #ifndef TRI_ATTN_TILE_RG
-#define TRI_ATTN_TILE_RG 4
+#define TRI_ATTN_TILE_RG (32 / TRI_ATTN_ROWS)
 #endif
 #ifndef TRI_ATTN_TILE_JB
-#define TRI_ATTN_TILE_JB 8
+#define TRI_ATTN_TILE_JB (TRI_ATTN_ROWS)
 #endif
 constexpr int NSTAGE = TRI_ATTN_STAGES;     // key blocks in flight (LDS ring of stages)
-constexpr int TILE_RG = TRI_ATTN_TILE_RG;   // row groups x column blocks that one XCD
+constexpr int TILE_RG = TRI_ATTN_TILE_RG;   // line groups x column blocks that one XCD
 constexpr int TILE_JB = TRI_ATTN_TILE_JB;   //   works on together (L2 reuse of K/V and bias)
-constexpr int IMG_FLOATS = BJ * BK;         // one bias tile of the image
-static_assert(NWAVE == R, "wave w stages K and V of row w");
-static_assert(IMG_FLOATS * 4 == 2 * NWAVE * 1024, "each wave stages two 1 KB pieces of the bias tile");
+constexpr int IMG_HALVES = BJ * BK;         // one fp16 bias tile of the image
+
+// Every staged piece is 1 KB: 16 keys of one line's K or V (64-byte rows), or 16 query
+// rows of the bias tile (64-byte rows of 32 fp16).  Wave w stages KV_PER_WAVE K/V pieces
+// and BIAS_PER_WAVE bias pieces.
+constexpr int KV_PER_WAVE = 4 * R / NWAVE;
+constexpr int BIAS_PER_WAVE = BJ * BK * 2 / 1024 / NWAVE;
+constexpr int COPIES_PER_BLOCK = KV_PER_WAVE + BIAS_PER_WAVE;   // global_load_lds per wave per block
+static_assert(KV_PER_WAVE * NWAVE == 4 * R && BIAS_PER_WAVE * NWAVE * 1024 == BJ * BK * 2, "whole pieces");
 
 struct Stage {
-    __bf16 k[R][BK][D];    // 64-byte rows, 16-byte chunks swizzled by kv_chunk()
+    __bf16 k[R][BK][D];      // 64-byte rows, 16-byte chunks swizzled by kv_chunk()
     __bf16 v[R][BK][D];
-    float bias[BJ][BK];    // 128-byte rows, 16-byte chunks swizzled by bias_chunk()
+    _Float16 bias[BJ][BK];   // 64-byte rows (one query), 16-byte chunks swizzled by kv_chunk()
 };
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kSqrtD = 5.656854249492381f;   // sqrt(32)
-constexpr float kScale = kLog2e / kSqrtD;      // S units -> log2 units
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kSqrtD = 5.656854249492381f;   // sqrt(32), the scale of the backward's fp32 image
+constexpr float kScale = 1.4426950408889634f / 5.656854249492381f;   // log2(e) / sqrt(32): q.k -> log2 units
 constexpr float kLo = 5.421010862427522e-20f;  // 2^-64
 constexpr float kHi = 1.8446744073709552e19f;  // 2^64
 
-__host__ __device__ constexpr int kv_chunk(int key, int part) { return part ^ ((key >> 1) & 3); }
-__host__ __device__ constexpr int bias_chunk(int j, int part) { return img_chunk(j, part); }
-static_assert(IMG_BJ == BJ && IMG_BK == BK, "the image layout published in launch.h");
+// Position of a 16-byte chunk inside a 64-byte LDS row (K, V: row = key; bias: row = query).
+__host__ __device__ constexpr int kv_chunk(int row, int part) { return part ^ ((row >> 1) & 3); }
+
+// Order of the 32 keys of a block inside a bias row: lane (c, h2) of the 32x32 MFMA
+// output holds keys 8a + 4*h2 + e (a, e = 0..3) of query c in registers 4a + e, so the
+// row stores key 8a + 4*h2 + e at position 16*h2 + 4a + e and the lane's 16 values are
+// the contiguous 16-byte parts 2*h2 and 2*h2 + 1.  Position 8*part + t holds this key:
+__host__ __device__ constexpr int part_key(int part, int t) {
+    return 8 * (2 * (part & 1) + (t >> 2)) + 4 * (part >> 1) + (t & 3);
+}
 
 // Key block n of the tile-ordered sequence: tiles ascending, 32-key blocks inside each.
 struct KeyBlock {
@@ -134,9 +159,10 @@ struct BlockPlan {
 };
 
 // ---------------------------------------------------------------------------------------
-// 1. bias image
+// 1a. fp32 bias image of the backward kernels (layout in launch.h)
 // ---------------------------------------------------------------------------------------
 constexpr int IMG_THR = 256;
+constexpr int IMG_FLOATS = IMG_BJ * IMG_BK;
 
 __global__ void __launch_bounds__(IMG_THR) bias_image_kernel(Problem p, float* img, int n_jb, int nblk) {
     const int n = blockIdx.x, jb = blockIdx.y, bh = blockIdx.z;
@@ -145,13 +171,13 @@ __global__ void __launch_bounds__(IMG_THR) bias_image_kernel(Problem p, float* i
     const int64_t key0 = p.k0 + kbk.kb;        // absolute index of the block's first key
     const uint16_t* bg = static_cast<const uint16_t*>(p.bias);
     float* dst = img + ((static_cast<int64_t>(bh) * n_jb + jb) * nblk + n) * IMG_FLOATS;
-    const int kk = threadIdx.x % BK;
+    const int kk = threadIdx.x % IMG_BK;
     const bool key_ok = kk < kbk.nk;
     const float mk = (p.mask && key_ok) ? p.mask[b * p.N + key0 + kk] : 0.0f;
 #pragma unroll
     for (int s = 0; s < IMG_FLOATS / IMG_THR; ++s) {
-        const int jj = (threadIdx.x + s * IMG_THR) / BK;
-        const int64_t j = static_cast<int64_t>(jb) * BJ + jj;
+        const int jj = (threadIdx.x + s * IMG_THR) / IMG_BK;
+        const int64_t j = static_cast<int64_t>(jb) * IMG_BJ + jj;
         float val = -INFINITY;
         if (key_ok) {
             // starting node bias[b, h, j, key]; ending node the transpose, bias[b, h, key, j]
@@ -159,7 +185,76 @@ __global__ void __launch_bounds__(IMG_THR) bias_image_kernel(Problem p, float* i
             const float bv = j < p.N ? __uint_as_float(static_cast<uint32_t>(bg[bi]) << 16) : 0.0f;
             val = (bv + mk) * kSqrtD;
         }
-        dst[jj * BK + bias_chunk(jj, kk / 4) * 4 + kk % 4] = val;
+        dst[jj * IMG_BK + img_chunk(jj, kk / 4) * 4 + kk % 4] = val;
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// 1b. fp16 bias image of the forward kernel, relative to each query's largest bias
+// ---------------------------------------------------------------------------------------
+constexpr int IMG16_Q = 64;                 // queries per workgroup of the image kernel
+static_assert(BJ % IMG16_Q == 0, "an image workgroup fills part of one column block");
+
+// Value of bias + mask for query j and absolute key `key` (starting node bias[b,h,j,key],
+// ending node bias[b,h,key,j]).
+__device__ __forceinline__ float biased(const Problem& p, const uint16_t* bg, int64_t b, int64_t bh, int64_t j,
+                                        int64_t key) {
+    const int64_t bi = p.ending ? (bh * p.N + key) * p.N + j : (bh * p.N + j) * p.N + key;
+    const float bv = __uint_as_float(static_cast<uint32_t>(bg[bi]) << 16);
+    return p.mask ? bv + p.mask[b * p.N + key] : bv;
+}
+
+// Thread t handles query jj of the workgroup's 64 and the 8 keys of part pt of every key
+// block.  Starting node: the 4 threads of a query are neighbours, so a query row's 32
+// keys are read as 64 contiguous bytes; ending node: a wave holds 64 consecutive queries,
+// which for one key are 128 contiguous bytes.
+__global__ void __launch_bounds__(256) bias_image16_kernel(Problem p, _Float16* img, float* ref, int n_jb, int nblk) {
+    __shared__ float red[4][IMG16_Q];
+    const int g = blockIdx.x, bh = blockIdx.y;
+    const int64_t b = bh / p.H;
+    const int t = threadIdx.x;
+    const int jj = p.ending ? (t & 63) : (t >> 2);
+    const int pt = p.ending ? (t >> 6) : (t & 3);
+    const int64_t j = static_cast<int64_t>(g) * IMG16_Q + jj;   // query (columns past N are padding)
+    const bool real = j < p.N;
+    const BlockPlan plan(p.nkeys(), p.T);
+    const uint16_t* bg = static_cast<const uint16_t*>(p.bias);
+
+    // pass 1: r_j = max over the key range of bias + mask (0 if every key is masked)
+    float mx = -INFINITY;
+    if (real) {
+        for (int n = 0; n < nblk; ++n) {
+            const KeyBlock kbk = plan.block(n);
+            const int64_t key0 = p.k0 + kbk.kb;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int kk = part_key(pt, e);
+                if (kk < kbk.nk) mx = fmaxf(mx, biased(p, bg, b, bh, j, key0 + kk));
+            }
+        }
+    }
+    red[pt][jj] = mx;
+    __syncthreads();
+    float r = fmaxf(fmaxf(red[0][jj], red[1][jj]), fmaxf(red[2][jj], red[3][jj]));
+    if (!(r > -INFINITY)) r = 0.0f;
+    if (pt == 0) ref[static_cast<int64_t>(bh) * n_jb * BJ + j] = r;
+
+    // pass 2: the tiles.  Padding queries get 0 for every existing key.
+    const int jb = static_cast<int>(j / BJ), jl = static_cast<int>(j % BJ);
+    _Float16* dst = img + (static_cast<int64_t>(bh) * n_jb + jb) * nblk * static_cast<int64_t>(IMG_HALVES) + jl * BK +
+                    kv_chunk(jl, pt) * 8;
+    for (int n = 0; n < nblk; ++n) {
+        const KeyBlock kbk = plan.block(n);
+        const int64_t key0 = p.k0 + kbk.kb;
+        f16x8 x;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int kk = part_key(pt, e);
+            float val = -INFINITY;
+            if (kk < kbk.nk) val = real ? (biased(p, bg, b, bh, j, key0 + kk) - r) * kLog2e : 0.0f;
+            x[e] = static_cast<_Float16>(val);
+        }
+        *reinterpret_cast<f16x8*>(dst + static_cast<int64_t>(n) * IMG_HALVES) = x;
     }
 }
 
@@ -167,54 +262,60 @@ __global__ void __launch_bounds__(IMG_THR) bias_image_kernel(Problem p, float* i
 // 2. attention
 // ---------------------------------------------------------------------------------------
 struct Ctx {
-    const char* k_row;      // K of this wave's staged line at the first key of the range
-    const char* v_row;
-    const float* img_wg;    // this workgroup's bias tiles, nblk consecutive 128 x 32 tiles
-    int64_t key_bytes;      // bytes between consecutive keys of a line
-    int key_local[2];       // key of this lane's 16-byte slot in the two 1 KB pieces
-    int part_bytes[2];      // byte offset of the slot's logical 16-byte part inside the key
-    int last_key;           // index of the last key of the range
+    const char* kv_row[KV_PER_WAVE];   // K or V of a staged line at the first key of the range
+    uint32_t kv_lds[KV_PER_WAVE];      // LDS byte offset of the piece inside a stage
+    int key_local[KV_PER_WAVE];        // key of this lane's 16-byte slot in the piece
+    int part_bytes[KV_PER_WAVE];       // byte offset of the slot's logical 16-byte part inside the key
+    const _Float16* img_wg;            // this workgroup's bias tiles, nblk consecutive BJ x 32 tiles
+    int64_t key_bytes;                 // bytes between consecutive keys of a line
+    int last_key;                      // index of the last key of the range
     BlockPlan plan;
 };
 
-// Wave w copies K and V of staged row w (two 1 KB pieces each) and two 1 KB pieces of the
-// bias tile; lane l of a piece carries 16 bytes.
-__device__ __forceinline__ void stage_block(const Ctx& cx, int n, Stage& st, int wave, int lane) {
-    const KeyBlock kbk = cx.plan.block(n);
-    const int kb = static_cast<int>(kbk.kb);
-    const char* kbase = cx.k_row + kbk.kb * cx.key_bytes;
-    const char* vbase = cx.v_row + kbk.kb * cx.key_bytes;
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-        // padded keys read a real key (their bias is -inf); offsets from the block's first key
-        const int rel = min(kb + cx.key_local[half], cx.last_key) - kb;
-        const int off = rel * static_cast<int>(cx.key_bytes) + cx.part_bytes[half];
-        __builtin_amdgcn_global_load_lds(GLOBAL_PTR(void, kbase + off), LDS_PTR(void, &st.k[wave][16 * half][0]), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(GLOBAL_PTR(void, vbase + off), LDS_PTR(void, &st.v[wave][16 * half][0]), 16, 0, 0);
-    }
-    const float* src = cx.img_wg + static_cast<int64_t>(n) * IMG_FLOATS + lane * 4;
-    float* flat = &st.bias[0][0];
-#pragma unroll
-    for (int piece = 0; piece < 2; ++piece) {
-        const int base = (2 * wave + piece) * 256;              // 256 floats = 1 KB
-        __builtin_amdgcn_global_load_lds(GLOBAL_PTR(void, src + base), LDS_PTR(void, flat + base), 16, 0, 0);
-    }
-}
-
-constexpr int ROW_BYTES = BK * D * 2;       // one staged row of K or V
-constexpr int TILE_BYTES = 32 * BK * 4;     // 32 rows of the staged bias tile
+constexpr int ROW_BYTES = BK * D * 2;       // one staged line of K or V
+constexpr int TILE_BYTES = 32 * BK * 2;     // 32 query rows of the staged bias tile
 constexpr int STAGE_BYTES = static_cast<int>(sizeof(Stage));
 constexpr int K_OFF = static_cast<int>(offsetof(Stage, k));
 constexpr int V_OFF = static_cast<int>(offsetof(Stage, v));
 constexpr int B_OFF = static_cast<int>(offsetof(Stage, bias));
-static_assert(RW == 2 && TW == 2, "the operand reads below address rows +ROW_BYTES and tiles +TILE_BYTES");
+static_assert(RW == 2 && TW == 2, "the operand reads below address lines +ROW_BYTES and tiles +TILE_BYTES");
 
-// LDS byte offsets (inside stage 0) of this lane's operand reads for its first row / tile.
+__shared__ Stage g_stage[NSTAGE];
+__shared__ int g_redo;
+
+__device__ __forceinline__ uint32_t stage_addr(int n) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(LDS_PTR(char, &g_stage[0]))) +
+           static_cast<uint32_t>(n % NSTAGE) * STAGE_BYTES;
+}
+
+// Wave w copies its K/V pieces and its bias pieces of block n; lane l of a piece carries
+// 16 bytes into bytes 16 l .. 16 l + 15 of the piece.
+__device__ __forceinline__ void stage_block(const Ctx& cx, int n, int wave, int lane) {
+    const KeyBlock kbk = cx.plan.block(n);
+    const int kb = static_cast<int>(kbk.kb);
+    char* lds = reinterpret_cast<char*>(&g_stage[n % NSTAGE]);
+#pragma unroll
+    for (int t = 0; t < KV_PER_WAVE; ++t) {
+        // padded keys read a real key (their bias is -inf); offsets from the block's first key
+        const int rel = min(kb + cx.key_local[t], cx.last_key) - kb;
+        const int off = rel * static_cast<int>(cx.key_bytes) + cx.part_bytes[t];
+        const char* src = cx.kv_row[t] + kbk.kb * cx.key_bytes + off;
+        __builtin_amdgcn_global_load_lds(GLOBAL_PTR(void, src), LDS_PTR(void, lds + cx.kv_lds[t]), 16, 0, 0);
+    }
+    const char* src = reinterpret_cast<const char*>(cx.img_wg + static_cast<int64_t>(n) * IMG_HALVES) + lane * 16;
+#pragma unroll
+    for (int t = 0; t < BIAS_PER_WAVE; ++t) {
+        const int base = (BIAS_PER_WAVE * wave + t) * 1024;
+        __builtin_amdgcn_global_load_lds(GLOBAL_PTR(void, src + base), LDS_PTR(void, lds + B_OFF + base), 16, 0, 0);
+    }
+}
+
+// LDS byte offsets (inside stage 0) of this lane's operand reads for its first line / tile.
 struct Lane {
     int c, h2;
     uint32_t k[2];        // K operand of S^T = K Q^T, d-half m
     uint32_t v[2][2];     // ds_read_b64_tr_b16 sources of the V^T operand, [key half m][sub]
-    uint32_t b[4];        // bias operand, 16-byte chunk a
+    uint32_t b[2];        // bias operand, 16-byte part 2*h2 + h
 };
 
 __device__ __forceinline__ Lane lane_layout(int lane, int row0, int tile0) {
@@ -235,13 +336,9 @@ __device__ __forceinline__ Lane lane_layout(int lane, int row0, int tile0) {
             L.v[m][sub] = V_OFF + row0 * ROW_BYTES + key * 64 + kv_chunk(key, d0 >> 3) * 16 + (d0 & 7) * 2;
         }
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
-        L.b[a] = B_OFF + tile0 * TILE_BYTES + L.c * 128 + bias_chunk(L.c, 2 * a + L.h2) * 16;
+    for (int h = 0; h < 2; ++h) L.b[h] = B_OFF + tile0 * TILE_BYTES + L.c * 64 + kv_chunk(L.c, 2 * L.h2 + h) * 16;
     return L;
 }
-
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Operands of one staged block.  The reads are inline assembly that waits for its own
 // results (lgkmcnt) before returning: the compiler then sees no LDS read it would have to
@@ -251,7 +348,7 @@ struct VFrags {
 };
 struct KCFrags {
     bf16x8 kA[RW][2];
-    f32x16 C[TW];
+    u32x4 c16[TW][2];     // bias tile of query tile ti: fp16 registers 8h .. 8h+7 in c16[ti][h]
 };
 
 __device__ __forceinline__ void load_v(uint32_t stage, const Lane& L, VFrags& f) {
@@ -268,7 +365,7 @@ __device__ __forceinline__ void load_v(uint32_t stage, const Lane& L, VFrags& f)
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3]), "=&v"(t[4]), "=&v"(t[5]), "=&v"(t[6]), "=&v"(t[7])
         : "v"(stage + L.v[0][0]), "v"(stage + L.v[0][1]), "v"(stage + L.v[1][0]), "v"(stage + L.v[1][1]));
-    static_assert(ROW_BYTES == 2048, "row offset in the assembly above");
+    static_assert(ROW_BYTES == 2048, "line offset in the assembly above");
 #pragma unroll
     for (int ri = 0; ri < RW; ++ri)
 #pragma unroll
@@ -280,118 +377,112 @@ __device__ __forceinline__ void load_v(uint32_t stage, const Lane& L, VFrags& f)
 }
 
 __device__ __forceinline__ void load_kc(uint32_t stage, const Lane& L, KCFrags& f) {
-    u32x4 k[4], b[8];
+    u32x4 k[4];
     asm volatile(
-        "ds_read_b128 %0, %12\n\t"
-        "ds_read_b128 %1, %13\n\t"
-        "ds_read_b128 %2, %12 offset:2048\n\t"
-        "ds_read_b128 %3, %13 offset:2048\n\t"
-        "ds_read_b128 %4, %14\n\t"
-        "ds_read_b128 %5, %15\n\t"
-        "ds_read_b128 %6, %16\n\t"
-        "ds_read_b128 %7, %17\n\t"
-        "ds_read_b128 %8, %14 offset:4096\n\t"
-        "ds_read_b128 %9, %15 offset:4096\n\t"
-        "ds_read_b128 %10, %16 offset:4096\n\t"
-        "ds_read_b128 %11, %17 offset:4096\n\t"
+        "ds_read_b128 %0, %8\n\t"
+        "ds_read_b128 %1, %9\n\t"
+        "ds_read_b128 %2, %8 offset:2048\n\t"
+        "ds_read_b128 %3, %9 offset:2048\n\t"
+        "ds_read_b128 %4, %10\n\t"
+        "ds_read_b128 %5, %11\n\t"
+        "ds_read_b128 %6, %10 offset:2048\n\t"
+        "ds_read_b128 %7, %11 offset:2048\n\t"
         "s_waitcnt lgkmcnt(0)"
-        : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(b[0]), "=&v"(b[1]), "=&v"(b[2]), "=&v"(b[3]),
-          "=&v"(b[4]), "=&v"(b[5]), "=&v"(b[6]), "=&v"(b[7])
-        : "v"(stage + L.k[0]), "v"(stage + L.k[1]), "v"(stage + L.b[0]), "v"(stage + L.b[1]), "v"(stage + L.b[2]),
-          "v"(stage + L.b[3]));
-    static_assert(TILE_BYTES == 4096, "tile offset in the assembly above");
+        : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(f.c16[0][0]), "=&v"(f.c16[0][1]),
+          "=&v"(f.c16[1][0]), "=&v"(f.c16[1][1])
+        : "v"(stage + L.k[0]), "v"(stage + L.k[1]), "v"(stage + L.b[0]), "v"(stage + L.b[1]));
+    static_assert(TILE_BYTES == 2048, "tile offset in the assembly above");
 #pragma unroll
     for (int ri = 0; ri < RW; ++ri)
 #pragma unroll
         for (int m = 0; m < 2; ++m) f.kA[ri][m] = __builtin_bit_cast(bf16x8, k[2 * ri + m]);
-#pragma unroll
-    for (int ti = 0; ti < TW; ++ti)
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) f.C[ti][4 * a + e] = __uint_as_float(b[4 * ti + a][e]);
+}
+
+// Score register r of query tile ti in log2 units relative to r_j: the image value for
+// register r is half r % 2 of word (r % 8) / 2 of c16[ti][r / 8]; the conversion from
+// fp16 folds into v_fma_mix_f32.
+__device__ __forceinline__ float score_log2(const KCFrags& kc, int ti, const f32x16& S, int r) {
+    const uint32_t word = kc.c16[ti][r >> 3][(r & 7) >> 1];   // a scalar copy: bit_cast of a vector element reads element 0
+    const f16x2 h = __builtin_bit_cast(f16x2, word);
+    return fmaf(S[r], kScale, static_cast<float>(h[r & 1]));
 }
 
 struct State {
     f32x16 O[RW][TW];
-    float mref[RW][TW];
-    float nb[RW][TW];
+    float mref[RW][TW];    // reference of O and l, log2 units relative to r_j
     float lsum[RW][TW];
-    __device__ void reset() {
+    __device__ void reset(float m0) {
 #pragma unroll
         for (int ri = 0; ri < RW; ++ri)
 #pragma unroll
             for (int ti = 0; ti < TW; ++ti) {
                 O[ri][ti] = f32x16{};
-                mref[ri][ti] = -INFINITY;
-                nb[ri][ti] = 0.0f;
+                mref[ri][ti] = m0;
                 lsum[ri][ti] = 0.0f;
             }
     }
 };
 
-// The wave's two units (rows ri = 0, 1) of query tile TI for one key block.
-template <bool EXACT_MAX, int TI>
-__device__ __forceinline__ void compute_tile(const KCFrags& kc, const VFrags& vf, const bf16x8 (&qB)[RW][TW][2],
-                                             State& s) {
+// The wave's two units (lines ri = 0, 1) of query tile TI for one key block, with the
+// exact running maximum.
+template <int TI>
+__device__ __forceinline__ void compute_tile_exact(const KCFrags& kc, const VFrags& vf, const bf16x8 (&qB)[RW][TW][2],
+                                                   State& s) {
     const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
     constexpr int ti = TI;
-    {
 #pragma unroll
-        for (int ri = 0; ri < RW; ++ri) {
-            f32x16 S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kc.kA[ri][0], qB[ri][ti][0], kc.C[ti], 0, 0, 0);
-            S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kc.kA[ri][1], qB[ri][ti][1], S, 0, 0, 0);
-            if constexpr (EXACT_MAX) {
-                float mx = S[0];
+    for (int ri = 0; ri < RW; ++ri) {
+        f32x16 S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kc.kA[ri][0], qB[ri][ti][0], f32x16{}, 0, 0, 0);
+        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kc.kA[ri][1], qB[ri][ti][1], S, 0, 0, 0);
+        f32x16 x;
 #pragma unroll
-                for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[r]);
-                mx = fmaxf(mx, __shfl_xor(mx, 32));
-                const float mold = s.mref[ri][ti];
-                const float mnew = fmaxf(mold, mx);
-                const float alpha = mold == -INFINITY ? 0.0f : exp2f((mold - mnew) * kScale);
-                s.lsum[ri][ti] *= alpha;
+        for (int r = 0; r < 16; ++r) x[r] = score_log2(kc, ti, S, r);
+        float mx = x[0];
 #pragma unroll
-                for (int r = 0; r < 16; ++r) s.O[ri][ti][r] *= alpha;
-                s.mref[ri][ti] = mnew;
-                s.nb[ri][ti] = mnew == -INFINITY ? 0.0f : -mnew * kScale;
-            }
-            const float nb = s.nb[ri][ti];
-            f32x16 P;
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, x[r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mold = s.mref[ri][ti];
+        const float mnew = fmaxf(mold, mx);
+        const float alpha = mold == -INFINITY ? 0.0f : exp2f(mold - mnew);
+        s.lsum[ri][ti] *= alpha;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) P[r] = __builtin_amdgcn_exp2f(fmaf(S[r], kScale, nb));
-            const bf16x8 pb0 = __builtin_convertvector(__builtin_shufflevector(P, P, 0, 1, 2, 3, 4, 5, 6, 7), bf16x8);
-            const bf16x8 pb1 = __builtin_convertvector(__builtin_shufflevector(P, P, 8, 9, 10, 11, 12, 13, 14, 15), bf16x8);
-            float ls = s.lsum[ri][ti];
+        for (int r = 0; r < 16; ++r) s.O[ri][ti][r] *= alpha;
+        s.mref[ri][ti] = mnew;
+        const float sh = mnew == -INFINITY ? 0.0f : mnew;
+        f32x16 P;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const bf16x2 a0 = {pb0[2 * e], pb0[2 * e + 1]};
-                const bf16x2 a1 = {pb1[2 * e], pb1[2 * e + 1]};
-                ls = __builtin_amdgcn_fdot2_f32_bf16(a0, ones, ls, false);
-                ls = __builtin_amdgcn_fdot2_f32_bf16(a1, ones, ls, false);
-            }
-            s.lsum[ri][ti] = ls;
-            s.O[ri][ti] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf.vA[ri][0], pb0, s.O[ri][ti], 0, 0, 0);
-            s.O[ri][ti] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf.vA[ri][1], pb1, s.O[ri][ti], 0, 0, 0);
+        for (int r = 0; r < 16; ++r) P[r] = __builtin_amdgcn_exp2f(x[r] - sh);
+        const bf16x8 pb0 = __builtin_convertvector(__builtin_shufflevector(P, P, 0, 1, 2, 3, 4, 5, 6, 7), bf16x8);
+        const bf16x8 pb1 = __builtin_convertvector(__builtin_shufflevector(P, P, 8, 9, 10, 11, 12, 13, 14, 15), bf16x8);
+        float ls = s.lsum[ri][ti];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const bf16x2 a0 = {pb0[2 * e], pb0[2 * e + 1]};
+            const bf16x2 a1 = {pb1[2 * e], pb1[2 * e + 1]};
+            ls = __builtin_amdgcn_fdot2_f32_bf16(a0, ones, ls, false);
+            ls = __builtin_amdgcn_fdot2_f32_bf16(a1, ones, ls, false);
         }
+        s.lsum[ri][ti] = ls;
+        s.O[ri][ti] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf.vA[ri][0], pb0, s.O[ri][ti], 0, 0, 0);
+        s.O[ri][ti] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf.vA[ri][1], pb1, s.O[ri][ti], 0, 0, 0);
     }
 }
 
-template <bool EXACT_MAX>
-__device__ __forceinline__ void compute_block(const KCFrags& kc, const VFrags& vf, const bf16x8 (&qB)[RW][TW][2],
-                                              State& s) {
+__device__ __forceinline__ void compute_block_exact(const KCFrags& kc, const VFrags& vf, const bf16x8 (&qB)[RW][TW][2],
+                                                    State& s) {
     static_assert(TW == 2, "two query tiles per wave");
-    compute_tile<EXACT_MAX, 0>(kc, vf, qB, s);
-    compute_tile<EXACT_MAX, 1>(kc, vf, qB, s);
+    compute_tile_exact<0>(kc, vf, qB, s);
+    compute_tile_exact<1>(kc, vf, qB, s);
 }
 
-// Fixed-reference block as an explicit software pipeline over the wave's four units
-// u = (tile u / 2, row u % 2).  Unit u's softmax runs in four chunks of 4 scores (4 FMA +
-// 4 v_exp_f32, the bf16 conversion and row sum after every second chunk), and each chunk
-// carries exactly one matrix instruction: the two halves of S for unit u + 1 during
-// chunks 0 and 1, the two halves of P.V for unit u - 1 during chunks 2 and 3.  On gfx950
-// a matrix instruction issued among transcendental instructions runs almost entirely in
-// their shadow, while one issued among plain VALU instructions mostly does not, so the
-// order is pinned with scheduling barriers.
+// Fast-pass block (reference r_j) as an explicit software pipeline over the wave's four
+// units u = (tile u / 2, line u % 2).  Unit u's softmax runs in four chunks of 4 scores
+// (4 v_fma_mix_f32 + 4 v_exp_f32, the bf16 conversion and row sum after every second
+// chunk), and each chunk carries exactly one matrix instruction: the two halves of S for
+// unit u + 1 during chunks 0 and 1, the two halves of P.V for unit u - 1 during chunks 2
+// and 3.  On gfx950 a matrix instruction issued among transcendental instructions runs
+// almost entirely in their shadow, while one issued among plain VALU instructions mostly
+// does not, so the order is pinned with scheduling barriers.
 template <int U>
 __device__ __forceinline__ f32x16 s_half(const KCFrags& kc, const bf16x8 (&qB)[RW][TW][2], int m, const f32x16& acc) {
     constexpr int ti = U / RW, ri = U % RW;
@@ -404,21 +495,21 @@ __device__ __forceinline__ void compute_block_pipe(const KCFrags& kc, const VFra
     const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
     f32x16 S[4];
     bf16x8 P[4][2];
-    S[0] = s_half<0>(kc, qB, 0, kc.C[0]);
+    const f32x16 zero = {};
+    S[0] = s_half<0>(kc, qB, 0, zero);
     S[0] = s_half<0>(kc, qB, 1, S[0]);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
         const int ti = u / RW, ri = u % RW;
-        const float nb = s.nb[ri][ti];
         float ls = s.lsum[ri][ti];
         f32x16 p;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             if (q == 0 && u + 1 < 4) {
-                if (u + 1 == 1) S[1] = s_half<1>(kc, qB, 0, kc.C[0]);
-                if (u + 1 == 2) S[2] = s_half<2>(kc, qB, 0, kc.C[1]);
-                if (u + 1 == 3) S[3] = s_half<3>(kc, qB, 0, kc.C[1]);
+                if (u + 1 == 1) S[1] = s_half<1>(kc, qB, 0, zero);
+                if (u + 1 == 2) S[2] = s_half<2>(kc, qB, 0, zero);
+                if (u + 1 == 3) S[3] = s_half<3>(kc, qB, 0, zero);
             }
             if (q == 1 && u + 1 < 4) {
                 if (u + 1 == 1) S[1] = s_half<1>(kc, qB, 1, S[1]);
@@ -430,7 +521,7 @@ __device__ __forceinline__ void compute_block_pipe(const KCFrags& kc, const VFra
                 s.O[pr][pt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf.vA[pr][q - 2], P[pu][q - 2], s.O[pr][pt], 0, 0, 0);
             }
 #pragma unroll
-            for (int r = 4 * q; r < 4 * q + 4; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(S[u][r], kScale, nb));
+            for (int r = 4 * q; r < 4 * q + 4; ++r) p[r] = __builtin_amdgcn_exp2f(score_log2(kc, ti, S[u], r));
             if (q == 1 || q == 3) {
                 const int h = q / 2;
                 const f32x8 ph = h == 0 ? __builtin_shufflevector(p, p, 0, 1, 2, 3, 4, 5, 6, 7)
@@ -451,35 +542,28 @@ __device__ __forceinline__ void compute_block_pipe(const KCFrags& kc, const VFra
     s.O[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf.vA[1][1], P[3][1], s.O[1][1], 0, 0, 0);
 }
 
-__shared__ Stage g_stage[NSTAGE];
-__shared__ int g_redo;
+static_assert(NSTAGE == 3 || NSTAGE == 4, "ring of three or four stages");
 
-constexpr int COPIES_PER_BLOCK = 6;         // global_load_lds issued per wave per staged block
-static_assert(NSTAGE == 3, "the barrier below keeps exactly one block of copies in flight");
-
-// Barrier after which every wave's copies except the most recent block's are complete
-// (the most recent block is still needed later, the one before it next).
+// Barrier after which every wave's copies except those of the NSTAGE - 2 most recent
+// blocks are complete (those are needed later, the one before them next).
 __device__ __forceinline__ void barrier_keep_newest() {
-    static_assert(COPIES_PER_BLOCK == 6, "vmcnt below");
-    asm volatile("s_waitcnt vmcnt(6)\n\ts_barrier" ::: "memory");
+    constexpr int keep = COPIES_PER_BLOCK * (NSTAGE - 2);
+    static_assert(keep == 4 || keep == 5 || keep == 8 || keep == 10, "vmcnt for this ring");
+    if constexpr (keep == 4) asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
+    if constexpr (keep == 5) asm volatile("s_waitcnt vmcnt(5)\n\ts_barrier" ::: "memory");
+    if constexpr (keep == 8) asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+    if constexpr (keep == 10) asm volatile("s_waitcnt vmcnt(10)\n\ts_barrier" ::: "memory");
 }
 // Barrier after which every copy issued so far is complete.
 __device__ __forceinline__ void barrier_drain() { asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-__device__ __forceinline__ uint32_t stage_addr(int n) {
-    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(LDS_PTR(char, &g_stage[0]))) +
-           static_cast<uint32_t>(n % NSTAGE) * STAGE_BYTES;
-}
-
 // Prologue: copies of blocks 0 .. NSTAGE-2 in flight, block 0 complete everywhere.
 __device__ __forceinline__ void key_prologue(const Ctx& cx, int wave, int lane, int nblk) {
-    stage_block(cx, 0, g_stage[0], wave, lane);
-    if (nblk > 1) {
-        stage_block(cx, 1, g_stage[1], wave, lane);
+    for (int n = 0; n < NSTAGE - 1 && n < nblk; ++n) stage_block(cx, n, wave, lane);
+    if (nblk >= NSTAGE - 1)
         barrier_keep_newest();
-    } else {
+    else
         barrier_drain();
-    }
 }
 
 // One step of the key loop: read block n's operands, issue the copy of block
@@ -492,26 +576,25 @@ __device__ __forceinline__ void key_step(const Ctx& cx, const Lane& L, int wave,
     VFrags vf;
     load_v(st, L, vf);
     const bool issue = n + NSTAGE - 1 < nblk;
-    if (issue) stage_block(cx, n + NSTAGE - 1, g_stage[(n + NSTAGE - 1) % NSTAGE], wave, lane);
+    if (issue) stage_block(cx, n + NSTAGE - 1, wave, lane);
     KCFrags kc;
     load_kc(st, L, kc);
     if constexpr (!EXACT_MAX)
         compute_block_pipe(kc, vf, qB, s);
     else
-        compute_block<EXACT_MAX>(kc, vf, qB, s);
+        compute_block_exact(kc, vf, qB, s);
     if (issue)
         barrier_keep_newest();
     else
         barrier_drain();
 }
 
-// Fast pass: block 0 fixes the reference at its exact maximum, the other blocks reuse it.
-// Each loop has a single compute path, so the accumulators stay in place across blocks.
+// Fast pass: every block with the reference r_j.  Each loop has a single compute path,
+// so the accumulators stay in place across blocks.
 __device__ __forceinline__ void key_loop_fast(const Ctx& cx, const Lane& L, int wave, int lane,
                                               const bf16x8 (&qB)[RW][TW][2], State& s, int nblk) {
     key_prologue(cx, wave, lane, nblk);
-    key_step<true>(cx, L, wave, lane, qB, s, 0, nblk);
-    for (int n = 1; n < nblk; ++n) key_step<false>(cx, L, wave, lane, qB, s, n, nblk);
+    for (int n = 0; n < nblk; ++n) key_step<false>(cx, L, wave, lane, qB, s, n, nblk);
 }
 
 // Exact pass: the running maximum is refreshed on every block.
@@ -521,15 +604,15 @@ __device__ __forceinline__ void key_loop_exact(const Ctx& cx, const Lane& L, int
     for (int n = 0; n < nblk; ++n) key_step<true>(cx, L, wave, lane, qB, s, n, nblk);
 }
 
-__global__ void __launch_bounds__(NTHR) bf16_mfma_kernel(Problem p, Strides sd, const float* img, int n_jb, int n_rg,
-                                                         int nblk, int total) {
+__global__ void __launch_bounds__(NTHR) bf16_mfma_kernel(Problem p, Strides sd, const _Float16* img, const float* ref,
+                                                         int n_jb, int n_rg, int nblk, int total) {
     // XCD-aware remap: XCD x (= hardware id mod 8) walks a contiguous range of logical ids.
     const int w = blockIdx.x;
     const int xcd = w % NXCD, slot = w / NXCD;
     const int base = total / NXCD, extra = total % NXCD;
     const int logical = xcd * base + (xcd < extra ? xcd : extra) + slot;
-    // within one (b, h): strips of TILE_RG row groups, each cut into tiles of TILE_RG x
-    // TILE_JB (row group, column block) pairs, column block fastest inside a tile; the last
+    // within one (b, h): strips of TILE_RG line groups, each cut into tiles of TILE_RG x
+    // TILE_JB (line group, column block) pairs, column block fastest inside a tile; the last
     // strip and the last tile of a strip may be narrower
     const int bh = logical / (n_jb * n_rg);
     const int rem = logical - bh * n_jb * n_rg;
@@ -548,24 +631,27 @@ __global__ void __launch_bounds__(NTHR) bf16_mfma_kernel(Problem p, Strides sd, 
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;   // wave is uniform
-    const int row0 = (wave / (QT / TW)) * RW;       // first of this wave's rows in the group
+    const int row0 = (wave / (QT / TW)) * RW;       // first of this wave's lines in the group
     const int tile0 = (wave % (QT / TW)) * TW;      // first of this wave's query tiles
     const Lane L = lane_layout(lane, row0, tile0);
 
     Ctx cx;
     {
-        int64_t i = i0 + wave;                       // the line this wave stages
-        i = i < lines ? i : lines - 1;               // padded lines read a real line (never stored)
-        const int64_t row_off = (bh_off + i * sd.line + p.k0 * sd.key) * 2;
-        cx.k_row = static_cast<const char*>(p.k) + row_off;
-        cx.v_row = static_cast<const char*>(p.v) + row_off;
-        cx.img_wg = img + (static_cast<int64_t>(bh) * n_jb + jb) * nblk * IMG_FLOATS;
         cx.key_bytes = sd.key * 2;
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            cx.key_local[half] = 16 * half + (lane >> 2);
-            cx.part_bytes[half] = kv_chunk(cx.key_local[half], lane & 3) * 16;   // logical part at this slot
+        for (int t = 0; t < KV_PER_WAVE; ++t) {
+            // piece pi: line pi / 4, K (0) or V (1) = (pi / 2) % 2, keys 16 * (pi % 2) .. +15
+            const int pi = KV_PER_WAVE * wave + t;
+            const int line = pi >> 2, kv = (pi >> 1) & 1, half = pi & 1;
+            int64_t i = i0 + line;
+            i = i < lines ? i : lines - 1;           // padded lines read a real line (never stored)
+            const int64_t row_off = (bh_off + i * sd.line + p.k0 * sd.key) * 2;
+            cx.kv_row[t] = static_cast<const char*>(kv ? p.v : p.k) + row_off;
+            cx.kv_lds[t] = (kv ? V_OFF : K_OFF) + line * ROW_BYTES + half * 1024;
+            cx.key_local[t] = 16 * half + (lane >> 2);
+            cx.part_bytes[t] = kv_chunk(cx.key_local[t], lane & 3) * 16;   // logical part at this slot
         }
+        cx.img_wg = img + (static_cast<int64_t>(bh) * n_jb + jb) * nblk * static_cast<int64_t>(IMG_HALVES);
         cx.last_key = static_cast<int>(p.nkeys() - 1);
         cx.plan = BlockPlan(p.nkeys(), p.T);
     }
@@ -592,7 +678,7 @@ __global__ void __launch_bounds__(NTHR) bf16_mfma_kernel(Problem p, Strides sd, 
     __builtin_amdgcn_s_waitcnt(0x0F70);
 
     State s;
-    s.reset();
+    s.reset(0.0f);
     if (tid == 0) g_redo = 0;
     key_loop_fast(cx, L, wave, lane, qB, s, nblk);
 
@@ -611,13 +697,13 @@ __global__ void __launch_bounds__(NTHR) bf16_mfma_kernel(Problem p, Strides sd, 
     if (__any(bad) && lane == 0) g_redo = 1;
     __syncthreads();
     if (g_redo) {
-        s.reset();
+        s.reset(-INFINITY);
         key_loop_exact(cx, L, wave, lane, qB, s, nblk);
     }
 
     // out = O / l; lanes l and l^32 hold disjoint keys of the same query.  In state mode
-    // out receives O itself, with the reference (m_ref / sqrt(D): S carries a factor
-    // sqrt(D)) and l; the log-sum-exp is m_ref / sqrt(D) + ln l.
+    // out receives O itself, with the reference in natural-log units (r_j + m ln 2) and l;
+    // the log-sum-exp is that reference plus ln l.
     const bool state = p.st_m != nullptr;
 #pragma unroll
     for (int ri = 0; ri < RW; ++ri)
@@ -639,8 +725,8 @@ __global__ void __launch_bounds__(NTHR) bf16_mfma_kernel(Problem p, Strides sd, 
                     }
                     *reinterpret_cast<f32x4*>(o + 8 * a + 4 * L.h2) = x;
                 }
-                const float mnat = s.mref[ri][ti] * (1.0f / kSqrtD);
-                if (L.h2 == 0) {
+                if (L.h2 == 0 && (state || p.lse)) {
+                    const float mnat = s.mref[ri][ti] * kLn2 + ref[static_cast<int64_t>(bh) * n_jb * BJ + j];
                     if (state) {
                         p.st_m[qo / D] = lt > 0.0f ? mnat : -INFINITY;
                         p.st_l[qo / D] = lt;
@@ -651,10 +737,28 @@ __global__ void __launch_bounds__(NTHR) bf16_mfma_kernel(Problem p, Strides sd, 
         }
 }
 
+// Workspace of the forward: the fp16 image, then the references r_j (fp32, padded to
+// whole column blocks), 256-byte aligned.
+struct FwdLayout {
+    int64_t n_jb, nblk;
+    size_t img_bytes, ref_off, total;
+};
+FwdLayout fwd_layout(const Problem& p) {
+    FwdLayout L;
+    L.n_jb = (p.N + BJ - 1) / BJ;
+    L.nblk = BlockPlan(p.nkeys(), p.T).count();
+    L.img_bytes = static_cast<size_t>(p.B * p.H * L.n_jb * L.nblk) * IMG_HALVES * 2;
+    L.ref_off = (L.img_bytes + 255) / 256 * 256;
+    L.total = L.ref_off + static_cast<size_t>(p.B * p.H * L.n_jb) * BJ * 4;
+    return L;
+}
+
 }  // namespace
 
-size_t bf16_workspace_bytes(const Problem& p) {
-    const int64_t n_jb = (p.N + BJ - 1) / BJ;
+size_t bf16_workspace_bytes(const Problem& p) { return fwd_layout(p).total; }
+
+size_t bias_image_bytes(const Problem& p) {
+    const int64_t n_jb = (p.N + IMG_BJ - 1) / IMG_BJ;
     const int64_t nblk = BlockPlan(p.nkeys(), p.T).count();
     return static_cast<size_t>(p.B * p.H * n_jb * nblk) * IMG_FLOATS * sizeof(float);
 }
@@ -662,7 +766,7 @@ size_t bf16_workspace_bytes(const Problem& p) {
 int64_t bias_image_blocks(const Problem& p) { return BlockPlan(p.nkeys(), p.T).count(); }
 
 hipError_t launch_bias_image(const Problem& p, float* img, hipStream_t stream) {
-    const int64_t n_jb = (p.N + BJ - 1) / BJ;
+    const int64_t n_jb = (p.N + IMG_BJ - 1) / IMG_BJ;
     const int64_t nblk = BlockPlan(p.nkeys(), p.T).count();
     if (nblk > 0x7FFFFFFF || n_jb > 65535 || p.B * p.H > 65535) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(bias_image_kernel, dim3(static_cast<unsigned>(nblk), static_cast<unsigned>(n_jb),
@@ -672,23 +776,24 @@ hipError_t launch_bias_image(const Problem& p, float* img, hipStream_t stream) {
 }
 
 hipError_t launch_bf16_mfma(const Problem& p, void* workspace, hipStream_t stream) {
-    const int64_t n_jb = (p.N + BJ - 1) / BJ;
+    const FwdLayout Ly = fwd_layout(p);
     const int64_t n_rg = ((p.ending ? p.N : p.I) + R - 1) / R;
-    const int64_t nblk = BlockPlan(p.nkeys(), p.T).count();
     const Strides sd = strides_of(p);
-    const int64_t total = n_jb * n_rg * p.B * p.H;
+    const int64_t total = Ly.n_jb * n_rg * p.B * p.H;
+    const int64_t n_qg = Ly.n_jb * (BJ / IMG16_Q);
     // the 32 keys of a block are addressed with 32-bit byte offsets from the block's first key
-    if (total > 0x7FFFFFFF || nblk > 0x7FFFFFFF || n_jb > 65535 || p.B * p.H > 65535 ||
+    if (total > 0x7FFFFFFF || Ly.nblk > 0x7FFFFFFF || n_qg > 0x7FFFFFFF || p.B * p.H > 65535 ||
         BK * sd.key * 2 > 0x7FFFFFFF)
         return hipErrorInvalidConfiguration;
-    float* img = static_cast<float*>(workspace);
-    hipLaunchKernelGGL(bias_image_kernel, dim3(static_cast<unsigned>(nblk), static_cast<unsigned>(n_jb),
-                                               static_cast<unsigned>(p.B * p.H)),
-                       dim3(IMG_THR), 0, stream, p, img, static_cast<int>(n_jb), static_cast<int>(nblk));
+    _Float16* img = static_cast<_Float16*>(workspace);
+    float* ref = reinterpret_cast<float*>(static_cast<char*>(workspace) + Ly.ref_off);
+    hipLaunchKernelGGL(bias_image16_kernel, dim3(static_cast<unsigned>(n_qg), static_cast<unsigned>(p.B * p.H)),
+                       dim3(256), 0, stream, p, img, ref, static_cast<int>(Ly.n_jb), static_cast<int>(Ly.nblk));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(bf16_mfma_kernel, dim3(static_cast<unsigned>(total)), dim3(NTHR), 0, stream, p, sd, img,
-                       static_cast<int>(n_jb), static_cast<int>(n_rg), static_cast<int>(nblk), static_cast<int>(total));
+    hipLaunchKernelGGL(bf16_mfma_kernel, dim3(static_cast<unsigned>(total)), dim3(NTHR), 0, stream, p, sd, img, ref,
+                       static_cast<int>(Ly.n_jb), static_cast<int>(n_rg), static_cast<int>(Ly.nblk),
+                       static_cast<int>(total));
     return hipGetLastError();
 }
 

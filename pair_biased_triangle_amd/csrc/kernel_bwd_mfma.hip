@@ -456,8 +456,8 @@ BwdLayout bwd_layout(const BwdProblem& p) {
     L.nq = p.B * p.I * p.N * p.H;
     const size_t per_line = static_cast<size_t>(p.B * p.I * p.H * L.NP) * 4;
     L.img = 0;
-    L.imgT = L.img + bf16_workspace_bytes(L.fwd);
-    L.g16 = L.imgT + bf16_workspace_bytes(L.tr);
+    L.imgT = L.img + bias_image_bytes(L.fwd);
+    L.g16 = L.imgT + bias_image_bytes(L.tr);
     L.delta = L.g16 + static_cast<size_t>(L.nq) * D * 2;
     L.lseT = L.delta + (static_cast<size_t>(L.nq) * 4 + 15) / 16 * 16;
     L.deltaT = L.lseT + per_line;

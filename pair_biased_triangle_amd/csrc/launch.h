@@ -63,12 +63,12 @@ struct BwdProblem {
 };
 hipError_t launch_backward(const BwdProblem& p, bool bf16, hipStream_t stream);
 
-// bf16 inputs, D == 32: matrix-core kernels.  `workspace` (16-byte aligned, at least
-// bf16_workspace_bytes(p) bytes) receives the converted bias image.
+// bf16 inputs, D == 32: matrix-core forward.  `workspace` (16-byte aligned, at least
+// bf16_workspace_bytes(p) bytes) receives its fp16 bias image and per-query references.
 size_t bf16_workspace_bytes(const Problem& p);
 hipError_t launch_bf16_mfma(const Problem& p, void* workspace, hipStream_t stream);
 
-// The bias image on its own.  Layout: per (b, h), column block jb of IMG_BJ query columns
+// The fp32 bias image of the backward kernels.  Layout: per (b, h), column block jb of IMG_BJ query columns
 // and key block n (key blocks follow the key tiles, see BlockPlan), one IMG_BJ x IMG_BK
 // fp32 tile at img + ((b*H + h) * n_jb + jb) * nblk + n) * IMG_BJ * IMG_BK holding
 // (bias + mask) * sqrt(D), -inf past the block's last key; row jj (a query column) has its
@@ -77,6 +77,7 @@ constexpr int IMG_BJ = 128;
 constexpr int IMG_BK = 32;
 __host__ __device__ constexpr int img_chunk(int jj, int part) { return part ^ (jj & 7); }
 int64_t bias_image_blocks(const Problem& p);   // nblk
+size_t bias_image_bytes(const Problem& p);
 hipError_t launch_bias_image(const Problem& p, float* img, hipStream_t stream);
 
 // Backward on matrix cores (bf16, D == 32).  Workspace: the bias image (keys in one tile),

@@ -132,15 +132,21 @@ def test_out_overlapping_an_input(lib):
 # workspace
 # ---------------------------------------------------------------------------
 def test_workspace_bytes(lib):
-    # bf16 D=32: B*H*ceil(N/128)*(key blocks)*128*32*4; key blocks = sum over tiles of ceil(len/32)
-    assert lib.tri_attn_workspace_bytes(1, 4, 2700, 2700, 32, 8, BF16) == 4 * 22 * (8 * 11) * 128 * 32 * 4
-    assert lib.tri_attn_workspace_bytes(1, 4, 1024, 4096, 32, 8, BF16) == 4 * 32 * (8 * 16) * 128 * 32 * 4
-    assert lib.tri_attn_workspace_bytes(2, 3, 5, 7, 32, 3, BF16) == 6 * 1 * 3 * 128 * 32 * 4
+    # bf16 D=32: the fp16 image, B*H*ceil(N/256)*(key blocks)*256*32*2 bytes (key blocks = sum
+    # over tiles of ceil(len/32)), padded to 256 bytes, then one fp32 reference per
+    # (b, h, query column padded to a multiple of 256)
+    def need(B, H, N, blocks):
+        img = B * H * -(-N // 256) * blocks * 256 * 32 * 2
+        return -(-img // 256) * 256 + B * H * -(-N // 256) * 256 * 4
+    assert lib.tri_attn_workspace_bytes(1, 4, 2700, 2700, 32, 8, BF16) == need(1, 4, 2700, 8 * 11)
+    assert lib.tri_attn_workspace_bytes(1, 4, 1024, 4096, 32, 8, BF16) == need(1, 4, 4096, 8 * 16)
+    assert lib.tri_attn_workspace_bytes(2, 3, 5, 7, 32, 3, BF16) == need(2, 3, 7, 3)
+    assert need(1, 4, 2700, 88) == 4 * 11 * 88 * 16384 + 4 * 11 * 1024
     assert lib.tri_attn_workspace_bytes(1, 4, 64, 64, 32, 1, FP32) == 0
     assert lib.tri_attn_workspace_bytes(1, 4, 64, 64, 16, 1, BF16) == 0
     assert lib.tri_attn_workspace_bytes(1, 4, 64, 64, 32, 0, BF16) == E_TILES
     assert lib.tri_attn_workspace_bytes(1, 4, 65, 64, 32, 1, BF16) == E_SHAPE
-    assert P.workspace_bytes(1, 4, 2700, 2700, 32, 8, 1) == 4 * 22 * 88 * 16384
+    assert P.workspace_bytes(1, 4, 2700, 2700, 32, 8, 1) == need(1, 4, 2700, 88)
 
 
 WS = fake(0x70000000)

@@ -286,9 +286,10 @@ def test_caller_workspace_matches_pool_workspace(torch_dev):
     assert e.value.status == -9
 
 
-def test_score_jump_takes_exact_fallback(torch_dev):
-    """A key far above the first block's maximum (+120 nats) overflows the stale
-    reference; the workgroup must recompute with the exact running maximum."""
+def test_bias_jump_is_exact(torch_dev):
+    """A bias far above the rest of its row (+120 nats) and one far below (-1000): the
+    bf16 path takes bias + mask relative to each query's largest value, so both stay
+    exact; the large key's value is returned."""
     torch = torch_dev
     cfg = W.custom_config(B=1, I=24, N=260, H=2, D=32, dtype="bf16", n_key_tiles=3, seed=15)
     w = W.make_inputs(cfg)
@@ -296,11 +297,30 @@ def test_score_jump_takes_exact_fallback(torch_dev):
     b[0, 0, 5:40, 200] = 120.0
     b[0, 1, 100:101, 250] = -1000.0
     w.bias = W.f32_to_bf16_bits(b)
-    say("[parity] score jump above the first block")
+    say("[parity] bias jump above the rest of the row")
     out = run_gpu(torch, w, 3).cpu().numpy()
     ref, _ = oracle.tri_attn(w.q, w.k, w.v, w.bias, w.mask, n_key_tiles=3)
     compare(out, ref, TOL["bf16"], "score jump")
     np.testing.assert_allclose(out[0, :, 5:40, 0], np.broadcast_to(W.bf16_bits_to_f32(w.v)[0, :, 200:201, 0], (24, 35, 32)),
+                               atol=1e-6)
+
+
+def test_qk_jump_takes_exact_fallback(torch_dev):
+    """q.k of one key about 90 nats above the rest overflows the fast pass's reference
+    (the normaliser leaves [2^-64, 2^64]); the workgroup recomputes with the exact running
+    maximum and returns that key's value."""
+    torch = torch_dev
+    cfg = W.custom_config(B=1, I=24, N=260, H=2, D=32, dtype="bf16", n_key_tiles=3, seed=25)
+    w = W.make_inputs(cfg)
+    q, k = W.bf16_bits_to_f32(w.q), W.bf16_bits_to_f32(w.k)
+    q[0, :, 5:40, 0, :] = 4.0
+    k[0, :, 200, 0, :] = 4.0
+    w.q, w.k = W.f32_to_bf16_bits(q), W.f32_to_bf16_bits(k)
+    say("[parity] q.k jump past the fast pass's range")
+    out = run_gpu(torch, w, 3).cpu().numpy()
+    ref, _ = oracle.tri_attn(w.q, w.k, w.v, w.bias, w.mask, n_key_tiles=3)
+    compare(out, ref, TOL["bf16"], "q.k jump")
+    np.testing.assert_allclose(out[0, :, 5:40, 0], W.bf16_bits_to_f32(w.v)[0, :, 200:201, 0].repeat(35, axis=1),
                                atol=1e-6)
 
 
