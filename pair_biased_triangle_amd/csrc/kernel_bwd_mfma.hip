@@ -353,88 +353,221 @@ __global__ void __launch_bounds__(NTHR, 2) bwd_dkdv_mfma(BwdProblem p, const flo
 }
 
 // ---------------------------------------------------------------------------------------
-// Workgroup: 64 queries x 64 keys of one (b, h); wave w takes queries (w & 1) * 32 and
-// keys (w >> 1) * 32 of it.
-__global__ void __launch_bounds__(NTHR) bwd_dbias_mfma(BwdProblem p, const float* img, const __bf16* g16,
-                                                       const float* delta, int n_jb, int nblk) {
-    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int c = lane & 31, h2 = lane >> 5;
-    const int64_t N = p.N, H = p.H, HD = H * D;
-    const int64_t bh = blockIdx.z, b = bh / H, h = bh % H;
-    const int64_t j = static_cast<int64_t>(blockIdx.y) * 64 + (wave & 1) * 32 + c;
-    const int64_t k0 = static_cast<int64_t>(blockIdx.x) * 64 + (wave >> 1) * 32;
-    if (k0 >= N) return;                                  // a wave past the last key (no barriers here)
-    const bool jok = j < N;
-    const int64_t kc = k0 + c < N ? k0 + c : N - 1;       // padded keys read a real key (bias -inf)
-    const __bf16* q = static_cast<const __bf16*>(p.q);
-    const __bf16* k = static_cast<const __bf16*>(p.k);
-    const __bf16* v = static_cast<const __bf16*>(p.v);
+// dbias[b, h, j, k] = sum over the rows i held of dS[i, j, k].  A workgroup of 8 waves owns
+// DB_Q = 128 queries x DB_K = 128 keys of one (b, h) and streams the rows i through a ring
+// of LDS stages: per row the waves copy Q, dO (its queries), K, V (its keys), lse and delta
+// straight from global memory into a stage (global_load_lds_dwordx4), and wave w computes
+// queries 32 (w % 4) .. +31 against keys 64 (w / 4) .. +63 (two 32 x 32 units) from LDS:
+//   S^T = K Q^T + C,  dP^T = V dO^T,  acc += P^T (dP^T - delta)
+// The bias tile C stays in registers for the whole loop.  Every sum over i runs in one
+// lane in row order: deterministic.
+constexpr int DB_Q = 128;
+constexpr int DB_K = 128;
+constexpr int DB_WAVES = 8;
+constexpr int DB_THR = 64 * DB_WAVES;
+#ifndef TRI_ATTN_DB_STAGES
+#define TRI_ATTN_DB_STAGES 4
+#endif
+constexpr int DB_STAGES = TRI_ATTN_DB_STAGES;
+#ifndef TRI_ATTN_DB_TILE_J
+#define TRI_ATTN_DB_TILE_J 4
+#endif
+#ifndef TRI_ATTN_DB_TILE_K
+#define TRI_ATTN_DB_TILE_K 8
+#endif
+constexpr int DB_TILE_J = TRI_ATTN_DB_TILE_J;   // query tiles x key tiles one XCD works on together
+constexpr int DB_TILE_K = TRI_ATTN_DB_TILE_K;
+constexpr int NP_ALIGN = 128;                   // lse / delta rows padded to whole query tiles
+static_assert(DB_Q % NP_ALIGN == 0 || NP_ALIGN % DB_Q == 0, "a query tile never crosses the padding");
 
-    // bias (+ mask) * sqrt(D) of this lane's query for the 16 keys of its registers
-    f32x16 C;
+struct DbStage {
+    __bf16 q[DB_Q][D];     // 64-byte rows, 16-byte chunks swizzled by kv_chunk()
+    __bf16 g[DB_Q][D];     // dO rounded to bf16
+    __bf16 k[DB_K][D];
+    __bf16 v[DB_K][D];
+    float lse[DB_Q];
+    float dl[DB_Q];
+};
+constexpr int DB_STAGE_BYTES = static_cast<int>(sizeof(DbStage));
+constexpr int DB_Q_OFF = static_cast<int>(offsetof(DbStage, q));
+constexpr int DB_G_OFF = static_cast<int>(offsetof(DbStage, g));
+constexpr int DB_K_OFF = static_cast<int>(offsetof(DbStage, k));
+constexpr int DB_V_OFF = static_cast<int>(offsetof(DbStage, v));
+constexpr int DB_L_OFF = static_cast<int>(offsetof(DbStage, lse));
+// per wave and row: 4 pieces of 1 KB (16 rows of Q, dO, K or V) and 128 bytes of lse / delta
+constexpr int DB_COPIES = 5;
+static_assert(4 * DB_WAVES * 1024 == 4 * DB_Q * D * 2 && DB_Q == DB_K, "pieces of the four tensors");
+static_assert(DB_WAVES * 128 == 2 * DB_Q * 4, "lse / delta pieces");
+__shared__ DbStage g_db[DB_STAGES];
+
+#define GPTR(p) ((const __attribute__((address_space(1))) void*)(p))
+#define LPTR(p) ((__attribute__((address_space(3))) void*)(p))
+
+struct DbCtx {
+    const char* src[4];        // this wave's four pieces: row base of (b, i = 0, pos, h), part applied
+    uint32_t dst[4];           // byte offset of each piece inside a stage
+    int64_t row_step;          // bytes between rows i of one tensor
+    const char* ls_src;        // lse / delta piece of row 0 (lanes 0 .. 7), or null
+    int64_t ls_step;           // bytes between rows i of lseT
+    uint32_t ls_dst;
+};
+
+__device__ __forceinline__ void db_stage(const DbCtx& cx, int64_t i, int slot, int lane) {
+    char* base = reinterpret_cast<char*>(&g_db[slot]);
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+        __builtin_amdgcn_global_load_lds(GPTR(cx.src[t] + i * cx.row_step), LPTR(base + cx.dst[t]), 16, 0, 0);
+    if (lane < 8) __builtin_amdgcn_global_load_lds(GPTR(cx.ls_src + i * cx.ls_step), LPTR(base + cx.ls_dst), 16, 0, 0);
+}
+
+__device__ __forceinline__ void db_barrier_keep() {
+    static_assert(DB_STAGES == 3 || DB_STAGES == 4, "three or four stages");
+    if constexpr (DB_STAGES == 3) asm volatile("s_waitcnt vmcnt(5)\n\ts_barrier" ::: "memory");
+    if constexpr (DB_STAGES == 4) asm volatile("s_waitcnt vmcnt(10)\n\ts_barrier" ::: "memory");
+}
+__device__ __forceinline__ void db_barrier_drain() { asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+__global__ void __launch_bounds__(DB_THR) bwd_dbias_lds(BwdProblem p, const float* img, const __bf16* g16,
+                                                        const float* lseT, const float* deltaT, int n_jb, int nblk,
+                                                        int64_t NP, int n_t, int total) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int c = lane & 31, h2 = lane >> 5;
+    // XCD-aware remap: XCD x walks a contiguous range of logical ids; inside one (b, h)
+    // strips of DB_TILE_J query tiles, cut into tiles of DB_TILE_J x DB_TILE_K, key tile fastest
+    const int w = blockIdx.x;
+    const int xcd = w % 8, slot = w / 8;
+    const int base = total / 8, extra = total % 8;
+    const int logical = xcd * base + (xcd < extra ? xcd : extra) + slot;
+    const int bh = logical / (n_t * n_t);
+    const int rem = logical - bh * n_t * n_t;
+    const int strip = rem / (DB_TILE_J * n_t);
+    const int nr = min(DB_TILE_J, n_t - strip * DB_TILE_J);
+    const int o = rem - strip * DB_TILE_J * n_t;
+    const int tile = o / (nr * DB_TILE_K);
+    const int nk = min(DB_TILE_K, n_t - tile * DB_TILE_K);
+    const int o2 = o - tile * nr * DB_TILE_K;
+    const int jt = strip * DB_TILE_J + o2 / nk;
+    const int kt = tile * DB_TILE_K + o2 % nk;
+    const int64_t N = p.N, H = p.H, HD = H * D;
+    const int64_t b = bh / H, h = bh % H;
+    const int64_t j0 = static_cast<int64_t>(jt) * DB_Q, k0 = static_cast<int64_t>(kt) * DB_K;
+
+    DbCtx cx;
     {
-        const int jb = static_cast<int>(j / IMG_BJ), jj = static_cast<int>(j % IMG_BJ);
-        const int n = static_cast<int>(k0 / IMG_BK);
-        const float* t = img + ((bh * n_jb + (jok ? jb : 0)) * static_cast<int64_t>(nblk) + n) * IMG_BJ * IMG_BK +
-                         jj * IMG_BK;
+        // piece pi = 4 w + t: tensor pi / 8 (Q, dO, K, V), rows 16 (pi % 8) .. +15; lane l
+        // carries row l / 4, 16-byte slot l % 4, which holds logical part kv_chunk(row, slot)
+        const __bf16* tens[4] = {static_cast<const __bf16*>(p.q), g16, static_cast<const __bf16*>(p.k),
+                                 static_cast<const __bf16*>(p.v)};
+        const uint32_t offs[4] = {DB_Q_OFF, DB_G_OFF, DB_K_OFF, DB_V_OFF};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int pi = 4 * wave + t, ten = pi >> 3, r = 16 * (pi & 7) + (lane >> 2);
+            int64_t pos = (ten < 2 ? j0 : k0) + r;
+            pos = pos < N ? pos : N - 1;                      // padded rows read a real one
+            const int part = kv_chunk(r, lane & 3);
+            cx.src[t] = reinterpret_cast<const char*>(tens[ten] + (b * p.I * N + pos) * HD + h * D + 8 * part);
+            cx.dst[t] = offs[ten] + (pi & 7) * 1024;
+        }
+        cx.row_step = N * HD * 2;
+        // lse / delta: wave w < 4 copies lse of queries 32 w .. +31, wave w >= 4 delta of 32 (w - 4)
+        const float* ls = wave < 4 ? lseT : deltaT;
+        cx.ls_src = reinterpret_cast<const char*>(ls + (b * p.I * H + h) * NP + j0 + 32 * (wave & 3) + 4 * (lane & 7));
+        cx.ls_step = H * NP * 4;
+        cx.ls_dst = DB_L_OFF + 128 * wave;
+    }
+
+    const int qt = wave & 3, kp = wave >> 2;
+    const int64_t j = j0 + 32 * qt + c;
+    const bool jok = j < N;
+    // bias (+ mask) * sqrt(D) of this lane's query for the 16 keys of each unit's registers
+    f32x16 C[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int64_t kb = k0 + 64 * kp + 32 * u;             // a multiple of 32: one image key block
+        if (kb >= N) {
+            C[u] = f32x16{} - INFINITY;
+            continue;
+        }
+        const int jb = static_cast<int>((jok ? j : 0) / IMG_BJ), jj = static_cast<int>((jok ? j : 0) % IMG_BJ);
+        const float* t = img + ((bh * n_jb + jb) * static_cast<int64_t>(nblk) + kb / IMG_BK) * IMG_BJ * IMG_BK + jj * IMG_BK;
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
             const f32x4 x = *reinterpret_cast<const f32x4*>(t + img_chunk(jj, 2 * a + h2) * 4);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) C[4 * a + e] = x[e];
+            for (int e = 0; e < 4; ++e) C[u][4 * a + e] = x[e];
         }
     }
-    // operands of row i: K, V (this wave's keys), Q, dO (its queries), lse and delta
-    struct Row {
-        bf16x8 kA[2], vA[2], qB[2], gB[2];
+    // LDS byte offsets of this lane's operand reads (stage 0); unit 1 is 32 rows (+2048) on
+    const int kr = 64 * kp + c, qr = 32 * qt + c;
+    uint32_t ok[2], oq[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+        ok[m] = kr * 64 + kv_chunk(kr, 2 * m + h2) * 16;
+        oq[m] = qr * 64 + kv_chunk(qr, 2 * m + h2) * 16;
+    }
+    const uint32_t ol = DB_L_OFF + qr * 4;
+    const uint32_t st0 = LDS_ADDR(&g_db[0]);
+
+    f32x16 acc[2] = {};
+    const int64_t I = p.I;
+    // prologue: rows 0 .. DB_STAGES - 2 in flight, row 0 complete everywhere
+    for (int64_t r = 0; r < DB_STAGES - 1 && r < I; ++r) db_stage(cx, r, static_cast<int>(r), lane);
+    if (I >= DB_STAGES - 1)
+        db_barrier_keep();
+    else
+        db_barrier_drain();
+    for (int64_t i = 0; i < I; ++i) {
+        const uint32_t st = st0 + static_cast<uint32_t>(i % DB_STAGES) * DB_STAGE_BYTES;
+        const bool issue = i + DB_STAGES - 1 < I;
+        if (issue) db_stage(cx, i + DB_STAGES - 1, static_cast<int>((i + DB_STAGES - 1) % DB_STAGES), lane);
+        u32x4 kk[4], vv[4], qq[2], gg[2];
         float lse, dl;
-    };
-    auto fetch = [&](int64_t i, Row& R) {
-        const int64_t row = (b * p.I + i) * N;
-        const int64_t ko = (row + kc) * HD + h * D, qo = (row + j) * HD + h * D;
+        asm volatile(
+            "ds_read_b128 %0, %14 offset:%c18\n\t"
+            "ds_read_b128 %1, %15 offset:%c18\n\t"
+            "ds_read_b128 %2, %14 offset:%c19\n\t"
+            "ds_read_b128 %3, %15 offset:%c19\n\t"
+            "ds_read_b128 %4, %14 offset:%c20\n\t"
+            "ds_read_b128 %5, %15 offset:%c20\n\t"
+            "ds_read_b128 %6, %14 offset:%c21\n\t"
+            "ds_read_b128 %7, %15 offset:%c21\n\t"
+            "ds_read_b128 %8, %16 offset:%c22\n\t"
+            "ds_read_b128 %9, %17 offset:%c22\n\t"
+            "ds_read_b128 %10, %16 offset:%c23\n\t"
+            "ds_read_b128 %11, %17 offset:%c23\n\t"
+            "ds_read_b32 %12, %24\n\t"
+            "ds_read_b32 %13, %24 offset:%c25\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(kk[0]), "=&v"(kk[1]), "=&v"(kk[2]), "=&v"(kk[3]), "=&v"(vv[0]), "=&v"(vv[1]), "=&v"(vv[2]),
+              "=&v"(vv[3]), "=&v"(qq[0]), "=&v"(qq[1]), "=&v"(gg[0]), "=&v"(gg[1]), "=&v"(lse), "=&v"(dl)
+            : "v"(st + ok[0]), "v"(st + ok[1]), "v"(st + oq[0]), "v"(st + oq[1]), "i"(DB_K_OFF), "i"(DB_K_OFF + 2048),
+              "i"(DB_V_OFF), "i"(DB_V_OFF + 2048), "i"(DB_Q_OFF), "i"(DB_G_OFF), "v"(st + ol), "i"(DB_Q * 4));
+        const float nb = neg_lse2(lse);
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            R.kA[m] = frag(k, ko + 16 * m + 8 * h2, true);
-            R.vA[m] = frag(v, ko + 16 * m + 8 * h2, true);
-            R.qB[m] = frag(q, qo + 16 * m + 8 * h2, jok);
-            R.gB[m] = frag(g16, qo + 16 * m + 8 * h2, jok);
+        for (int u = 0; u < 2; ++u) {
+            f32x16 S = mfma(__builtin_bit_cast(bf16x8, kk[2 * u]), __builtin_bit_cast(bf16x8, qq[0]), C[u]);
+            S = mfma(__builtin_bit_cast(bf16x8, kk[2 * u + 1]), __builtin_bit_cast(bf16x8, qq[1]), S);
+            f32x16 dP = mfma(__builtin_bit_cast(bf16x8, vv[2 * u]), __builtin_bit_cast(bf16x8, gg[0]), f32x16{});
+            dP = mfma(__builtin_bit_cast(bf16x8, vv[2 * u + 1]), __builtin_bit_cast(bf16x8, gg[1]), dP);
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                acc[u][r] = fmaf(__builtin_amdgcn_exp2f(fmaf(S[r], kScale, nb)), dP[r] - dl, acc[u][r]);
         }
-        R.lse = jok ? p.lse[(row + j) * H + h] : -INFINITY;
-        R.dl = jok ? delta[(row + j) * H + h] : 0.0f;
-    };
-    f32x16 acc = {};
-    auto row_step = [&](const Row& R) {
-        const float nb = neg_lse2(R.lse);
-        f32x16 S = mfma(R.kA[0], R.qB[0], C);
-        S = mfma(R.kA[1], R.qB[1], S);
-        f32x16 dP = mfma(R.vA[0], R.gB[0], f32x16{});
-        dP = mfma(R.vA[1], R.gB[1], dP);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[r] = fmaf(__builtin_amdgcn_exp2f(fmaf(S[r], kScale, nb)), dP[r] - R.dl, acc[r]);
-    };
-    // a ring of AHEAD + 1 rows: while row i is computed, rows i+1 .. i+AHEAD are loading
-    // (row r lives in slot r % (AHEAD + 1); the loop is unrolled so every slot is static)
-    constexpr int AHEAD = TRI_ATTN_DBIAS_AHEAD;
-    Row ring[AHEAD + 1];
-#pragma unroll
-    for (int t = 0; t < AHEAD; ++t)
-        if (t < p.I) fetch(t, ring[t]);
-    for (int64_t i = 0; i < p.I; i += AHEAD + 1) {
-#pragma unroll
-        for (int u = 0; u <= AHEAD; ++u) {
-            if (i + u < p.I) {
-                if (i + u + AHEAD < p.I) fetch(i + u + AHEAD, ring[(u + AHEAD) % (AHEAD + 1)]);
-                row_step(ring[u]);
-            }
-        }
+        if (issue)
+            db_barrier_keep();
+        else
+            db_barrier_drain();
     }
     if (jok) {
-        float* o = p.dbias + (bh * N + j) * N;
+        float* out = p.dbias + (bh * N + j) * N;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int64_t kk = k0 + 8 * (r / 4) + 4 * h2 + (r % 4);
-            if (kk < N) o[kk] = acc[r];
-        }
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t kk = k0 + 64 * kp + 32 * u + 8 * (r / 4) + 4 * h2 + (r % 4);
+                if (kk < N) out[kk] = acc[u][r];
+            }
     }
 }
 
@@ -452,7 +585,7 @@ BwdLayout bwd_layout(const BwdProblem& p) {
     L.fwd = Problem{p.q, p.k, p.v, p.bias, p.mask, nullptr, p.B, p.H, p.I, p.N, p.D, 1};
     L.tr = Problem{p.q, p.k, p.v, p.bias, nullptr, nullptr, p.B, p.H, p.N, p.N, p.D, 1};
     L.tr.ending = true;
-    L.NP = (p.N + IMG_BK - 1) / IMG_BK * IMG_BK;
+    L.NP = (p.N + NP_ALIGN - 1) / NP_ALIGN * NP_ALIGN;
     L.nq = p.B * p.I * p.N * p.H;
     const size_t per_line = static_cast<size_t>(p.B * p.I * p.H * L.NP) * 4;
     L.img = 0;
@@ -494,9 +627,12 @@ hipError_t launch_backward_mfma(const BwdProblem& p, void* workspace, hipStream_
     hipLaunchKernelGGL(bwd_dkdv_mfma, lines, dim3(NTHR), 0, stream, p, imgT, g16, lseT, deltaT,
                        static_cast<int>(n_jb), static_cast<int>(nblk), Ly.NP);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    const unsigned nt = static_cast<unsigned>((p.N + 63) / 64);
-    hipLaunchKernelGGL(bwd_dbias_mfma, dim3(nt, nt, static_cast<unsigned>(p.B * p.H)), dim3(NTHR), 0, stream, p, img,
-                       g16, delta, static_cast<int>(n_jb), static_cast<int>(nblk));
+    const int64_t n_t = (p.N + DB_Q - 1) / DB_Q;
+    const int64_t total = n_t * n_t * p.B * p.H;
+    if (total > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(bwd_dbias_lds, dim3(static_cast<unsigned>(total)), dim3(DB_THR), 0, stream, p, img, g16, lseT,
+                       deltaT, static_cast<int>(n_jb), static_cast<int>(nblk), Ly.NP, static_cast<int>(n_t),
+                       static_cast<int>(total));
     return hipGetLastError();
 }
 
