@@ -8,9 +8,9 @@
 // end, so each tile is folded into the running softmax state as one ring step (the
 // running state is the merged state of the tiles seen so far).
 //
-// Two kernels run per call:
-//   1. bias_image16_kernel: per query j it finds the reference r_j, the largest
-//      bias + mask over the call's keys, and writes the fp16 image the main kernel stages
+// Three kernels run per call:
+//   1. bias_ref_kernel, bias_image16_kernel: per query j the reference r_j, the largest
+//      bias + mask over the call's keys, then the fp16 image the main kernel stages
 //      verbatim: per (b, h, column block, key block) a BJ x 32 tile of
 //      (bias + mask - r_j) * log2(e), -inf for keys past the tile end.  Softmax does not
 //      change when every score of a query moves by the same amount, and relative to r_j
@@ -204,58 +204,91 @@ __device__ __forceinline__ float biased(const Problem& p, const uint16_t* bg, in
     return p.mask ? bv + p.mask[b * p.N + key] : bv;
 }
 
-// Thread t handles query jj of the workgroup's 64 and the 8 keys of part pt of every key
-// block.  Starting node: the 4 threads of a query are neighbours, so a query row's 32
-// keys are read as 64 contiguous bytes; ending node: a wave holds 64 consecutive queries,
-// which for one key are 128 contiguous bytes.
-__global__ void __launch_bounds__(256) bias_image16_kernel(Problem p, _Float16* img, float* ref, int n_jb, int nblk) {
-    __shared__ float red[4][IMG16_Q];
-    const int g = blockIdx.x, bh = blockIdx.y;
-    const int64_t b = bh / p.H;
+// r_j = max over the call's keys of bias + mask, written as REF_KS partial maxima per query
+// (padding queries and queries whose keys are all masked give -inf).  Starting node: a
+// query's biases are a contiguous row, so one wave walks it with coalesced reads (one
+// partial).  Ending node: they are a column, so a wave holds 64 consecutive queries and the
+// keys are split into REF_KS chunks, each a partial maximum, over 4 waves of a workgroup.
+constexpr int REF_KS = 16;
+__global__ void __launch_bounds__(256) bias_ref_kernel(Problem p, float* part, int64_t nqp) {
+    const int64_t bh = blockIdx.z, b = bh / p.H, BH = gridDim.z;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t NK = p.nkeys();
+    const uint16_t* bg = static_cast<const uint16_t*>(p.bias);
+    if (!p.ending) {
+        const int64_t j = static_cast<int64_t>(blockIdx.x) * 4 + wave;
+        if (j >= nqp) return;
+        float mx = -INFINITY;
+        if (j < p.N) {
+            const uint16_t* row = bg + (bh * p.N + j) * p.N + p.k0;
+            const float* mrow = p.mask ? p.mask + b * p.N + p.k0 : nullptr;
+#pragma unroll 8
+            for (int64_t k = lane; k < NK; k += 64) {
+                const float bv = __uint_as_float(static_cast<uint32_t>(row[k]) << 16);
+                mx = fmaxf(mx, mrow ? bv + mrow[k] : bv);
+            }
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+        if (lane == 0) part[bh * nqp + j] = mx;
+        return;
+    }
+    __shared__ float red[4][64];
+    const int64_t j = static_cast<int64_t>(blockIdx.x) * 64 + lane;
+    const int64_t chunk = (NK + REF_KS - 1) / REF_KS;
+    const int64_t lo = blockIdx.y * chunk, hi = min(NK, lo + chunk);
+    float mx = -INFINITY;
+    if (j < p.N) {
+#pragma unroll 8
+        for (int64_t k = lo + wave; k < hi; k += 4) {
+            const int64_t key = p.k0 + k;
+            const float bv = __uint_as_float(static_cast<uint32_t>(bg[(bh * p.N + key) * p.N + j]) << 16);
+            mx = fmaxf(mx, p.mask ? bv + p.mask[b * p.N + key] : bv);
+        }
+    }
+    red[wave][lane] = mx;
+    __syncthreads();
+    if (wave == 0)
+        part[(static_cast<int64_t>(blockIdx.y) * BH + bh) * nqp + j] =
+            fmaxf(fmaxf(red[0][lane], red[1][lane]), fmaxf(red[2][lane], red[3][lane]));
+}
+
+// One workgroup per (64 queries, key block, (b, h)); thread t handles query jj of the 64
+// and the 8 keys of part pt of the block.  Starting node: the 4 threads of a query are
+// neighbours, so a query row's 32 keys are read as 64 contiguous bytes; ending node: a
+// wave holds 64 consecutive queries, which for one key are 128 contiguous bytes.  r_j is
+// the largest of the n_part partial maxima (0 if every key is masked); with several
+// partials the workgroups of key block 0 also store r_j for the epilogue.
+__global__ void __launch_bounds__(256) bias_image16_kernel(Problem p, const float* part, int n_part, _Float16* img,
+                                                           float* ref, int n_jb, int nblk) {
+    const int g = blockIdx.x, n = blockIdx.y;
+    const int64_t bh = blockIdx.z, b = bh / p.H, BH = gridDim.z;
     const int t = threadIdx.x;
     const int jj = p.ending ? (t & 63) : (t >> 2);
     const int pt = p.ending ? (t >> 6) : (t & 3);
     const int64_t j = static_cast<int64_t>(g) * IMG16_Q + jj;   // query (columns past N are padding)
     const bool real = j < p.N;
-    const BlockPlan plan(p.nkeys(), p.T);
+    const int64_t nqp = static_cast<int64_t>(n_jb) * BJ;
     const uint16_t* bg = static_cast<const uint16_t*>(p.bias);
 
-    // pass 1: r_j = max over the key range of bias + mask (0 if every key is masked)
-    float mx = -INFINITY;
-    if (real) {
-        for (int n = 0; n < nblk; ++n) {
-            const KeyBlock kbk = plan.block(n);
-            const int64_t key0 = p.k0 + kbk.kb;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int kk = part_key(pt, e);
-                if (kk < kbk.nk) mx = fmaxf(mx, biased(p, bg, b, bh, j, key0 + kk));
-            }
-        }
-    }
-    red[pt][jj] = mx;
-    __syncthreads();
-    float r = fmaxf(fmaxf(red[0][jj], red[1][jj]), fmaxf(red[2][jj], red[3][jj]));
+    float r = -INFINITY;
+    for (int ks = 0; ks < n_part; ++ks) r = fmaxf(r, part[(ks * BH + bh) * nqp + j]);
     if (!(r > -INFINITY)) r = 0.0f;
-    if (pt == 0) ref[static_cast<int64_t>(bh) * n_jb * BJ + j] = r;
+    if (n_part > 1 && n == 0 && pt == 0) ref[bh * nqp + j] = r;
 
-    // pass 2: the tiles.  Padding queries get 0 for every existing key.
+    const KeyBlock kbk = BlockPlan(p.nkeys(), p.T).block(n);
+    const int64_t key0 = p.k0 + kbk.kb;
     const int jb = static_cast<int>(j / BJ), jl = static_cast<int>(j % BJ);
-    _Float16* dst = img + (static_cast<int64_t>(bh) * n_jb + jb) * nblk * static_cast<int64_t>(IMG_HALVES) + jl * BK +
-                    kv_chunk(jl, pt) * 8;
-    for (int n = 0; n < nblk; ++n) {
-        const KeyBlock kbk = plan.block(n);
-        const int64_t key0 = p.k0 + kbk.kb;
-        f16x8 x;
+    f16x8 x;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int kk = part_key(pt, e);
-            float val = -INFINITY;
-            if (kk < kbk.nk) val = real ? (biased(p, bg, b, bh, j, key0 + kk) - r) * kLog2e : 0.0f;
-            x[e] = static_cast<_Float16>(val);
-        }
-        *reinterpret_cast<f16x8*>(dst + static_cast<int64_t>(n) * IMG_HALVES) = x;
+    for (int e = 0; e < 8; ++e) {
+        const int kk = part_key(pt, e);
+        float val = -INFINITY;
+        if (kk < kbk.nk) val = real ? (biased(p, bg, b, bh, j, key0 + kk) - r) * kLog2e : 0.0f;
+        x[e] = static_cast<_Float16>(val);
     }
+    *reinterpret_cast<f16x8*>(img + ((bh * n_jb + jb) * nblk + n) * static_cast<int64_t>(IMG_HALVES) + jl * BK +
+                              kv_chunk(jl, pt) * 8) = x;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -738,18 +771,24 @@ __global__ void __launch_bounds__(NTHR) bf16_mfma_kernel(Problem p, Strides sd, 
 }
 
 // Workspace of the forward: the fp16 image, then the references r_j (fp32, padded to
-// whole column blocks), 256-byte aligned.
+// whole column blocks), then for the ending node REF_KS partial maxima per query; each
+// part 256-byte aligned.  The starting node's single partial is r_j itself.
 struct FwdLayout {
-    int64_t n_jb, nblk;
-    size_t img_bytes, ref_off, total;
+    int64_t n_jb, nblk, nqp;
+    int n_part;
+    size_t img_bytes, ref_off, part_off, total;
 };
 FwdLayout fwd_layout(const Problem& p) {
     FwdLayout L;
     L.n_jb = (p.N + BJ - 1) / BJ;
+    L.nqp = L.n_jb * BJ;
     L.nblk = BlockPlan(p.nkeys(), p.T).count();
+    L.n_part = p.ending ? REF_KS : 1;
     L.img_bytes = static_cast<size_t>(p.B * p.H * L.n_jb * L.nblk) * IMG_HALVES * 2;
     L.ref_off = (L.img_bytes + 255) / 256 * 256;
-    L.total = L.ref_off + static_cast<size_t>(p.B * p.H * L.n_jb) * BJ * 4;
+    const size_t ref_bytes = static_cast<size_t>(p.B * p.H * L.nqp) * 4;
+    L.part_off = L.ref_off + (ref_bytes + 255) / 256 * 256;
+    L.total = p.ending ? L.part_off + ref_bytes * REF_KS : L.ref_off + ref_bytes;
     return L;
 }
 
@@ -782,15 +821,22 @@ hipError_t launch_bf16_mfma(const Problem& p, void* workspace, hipStream_t strea
     const int64_t total = Ly.n_jb * n_rg * p.B * p.H;
     const int64_t n_qg = Ly.n_jb * (BJ / IMG16_Q);
     // the 32 keys of a block are addressed with 32-bit byte offsets from the block's first key
-    if (total > 0x7FFFFFFF || Ly.nblk > 0x7FFFFFFF || n_qg > 0x7FFFFFFF || p.B * p.H > 65535 ||
+    if (total > 0x7FFFFFFF || Ly.nblk > 65535 || Ly.nqp / 4 > 0x7FFFFFFF || p.B * p.H > 65535 ||
         BK * sd.key * 2 > 0x7FFFFFFF)
         return hipErrorInvalidConfiguration;
     _Float16* img = static_cast<_Float16*>(workspace);
     float* ref = reinterpret_cast<float*>(static_cast<char*>(workspace) + Ly.ref_off);
-    hipLaunchKernelGGL(bias_image16_kernel, dim3(static_cast<unsigned>(n_qg), static_cast<unsigned>(p.B * p.H)),
-                       dim3(256), 0, stream, p, img, ref, static_cast<int>(Ly.n_jb), static_cast<int>(Ly.nblk));
+    float* part = Ly.n_part > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + Ly.part_off) : ref;
+    const unsigned bhs = static_cast<unsigned>(p.B * p.H);
+    const dim3 ref_grid = p.ending ? dim3(static_cast<unsigned>(Ly.nqp / 64), REF_KS, bhs)
+                                   : dim3(static_cast<unsigned>(Ly.nqp / 4), 1, bhs);
+    hipLaunchKernelGGL(bias_ref_kernel, ref_grid, dim3(256), 0, stream, p, part, Ly.nqp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(bias_image16_kernel, dim3(static_cast<unsigned>(n_qg), static_cast<unsigned>(Ly.nblk), bhs),
+                       dim3(256), 0, stream, p, part, Ly.n_part, img, ref, static_cast<int>(Ly.n_jb),
+                       static_cast<int>(Ly.nblk));
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(bf16_mfma_kernel, dim3(static_cast<unsigned>(total)), dim3(NTHR), 0, stream, p, sd, img, ref,
                        static_cast<int>(Ly.n_jb), static_cast<int>(n_rg), static_cast<int>(Ly.nblk),
                        static_cast<int>(total));
