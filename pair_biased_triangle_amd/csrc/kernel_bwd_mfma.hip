@@ -158,89 +158,6 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdProblem p, __bf16* g16
 }
 
 // ---------------------------------------------------------------------------------------
-__global__ void __launch_bounds__(NTHR) bwd_dq_mfma(BwdProblem p, const float* img, const __bf16* g16,
-                                                    const float* delta, int n_jb, int nblk) {
-    __shared__ __attribute__((aligned(16))) char lds[NWAVE * TILE_BYTES];
-    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int c = lane & 31, h2 = lane >> 5;
-    const int64_t N = p.N, H = p.H, HD = H * D;
-    const int64_t bh = blockIdx.z, b = bh / H, h = bh % H, i = blockIdx.y;
-    const int jb = blockIdx.x;
-    const int jj = wave * 32 + c;                         // query inside the 128-query block
-    const int64_t j = static_cast<int64_t>(jb) * IMG_BJ + jj;
-    const bool jok = j < N;
-    const int64_t row = (b * p.I + i) * N;                // flat (b, i, 0)
-    const __bf16* q = static_cast<const __bf16*>(p.q);
-    const __bf16* k = static_cast<const __bf16*>(p.k);
-    const __bf16* v = static_cast<const __bf16*>(p.v);
-    const int64_t qo = (row + j) * HD + h * D;
-
-    bf16x8 qB[2], gB[2];
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-        qB[m] = frag(q, qo + 16 * m + 8 * h2, jok);
-        gB[m] = frag(g16, qo + 16 * m + 8 * h2, jok);
-    }
-    const float nb = jok ? neg_lse2(p.lse[(row + j) * H + h]) : -INFINITY;
-    const float dl = jok ? delta[(row + j) * H + h] : 0.0f;
-    const TileLane L = tile_lane(lane);
-    const uint32_t tile = LDS_ADDR(lds) + wave * TILE_BYTES;
-    const float* img_row = img + (bh * n_jb + jb) * static_cast<int64_t>(nblk) * IMG_BJ * IMG_BK + jj * IMG_BK;
-
-    // operands of key block n: K, V rows (lane = key) and the bias image chunks of this query
-    struct Blk {
-        bf16x8 kA[2], vA[2];
-        f32x4 c[4];
-    };
-    auto fetch = [&](int n, Blk& X) {
-        const int64_t key = static_cast<int64_t>(n) * IMG_BK + c;
-        const int64_t ko = (row + (key < N ? key : N - 1)) * HD + h * D;   // padded keys: bias -inf
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            X.kA[m] = frag(k, ko + 16 * m + 8 * h2, true);
-            X.vA[m] = frag(v, ko + 16 * m + 8 * h2, true);
-        }
-        const float* t = img_row + static_cast<int64_t>(n) * IMG_BJ * IMG_BK;
-#pragma unroll
-        for (int a = 0; a < 4; ++a) X.c[a] = *reinterpret_cast<const f32x4*>(t + img_chunk(jj, 2 * a + h2) * 4);
-    };
-    f32x16 dQ = {};
-    Blk cur, nxt;
-    fetch(0, cur);
-    for (int n = 0; n < nblk; ++n) {
-        if (n + 1 < nblk) fetch(n + 1, nxt);              // next block's loads fly during this block
-        f32x16 C;
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) C[4 * a + e] = cur.c[a][e];
-        f32x16 S = mfma(cur.kA[0], qB[0], C);
-        S = mfma(cur.kA[1], qB[1], S);
-        f32x16 dP = mfma(cur.vA[0], gB[0], f32x16{});
-        dP = mfma(cur.vA[1], gB[1], dP);
-        f32x16 dS;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) dS[r] = __builtin_amdgcn_exp2f(fmaf(S[r], kScale, nb)) * (dP[r] - dl);
-        bf16x8 s0, s1, kT0, kT1;
-        to_bf16(dS, s0, s1);
-        transpose_tile(tile, L, cur.kA[0], cur.kA[1], kT0, kT1);
-        dQ = mfma(kT0, s0, dQ);
-        dQ = mfma(kT1, s1, dQ);
-        cur = nxt;
-    }
-    if (jok) {
-        float* o = p.dq + qo;
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-            f32x4 x;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) x[e] = dQ[4 * a + e] * kInvSqrtD;
-            *reinterpret_cast<f32x4*>(o + 8 * a + 4 * h2) = x;
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------------------
 // imgT: the bias image of the transposed bias without the mask (built in the ending
 // orientation), so that tile (key block of IMG_BJ, query block of IMG_BK) row kk holds
 // bias[b, h, q, key] * sqrt(D) for 32 consecutive queries q (-inf past the last query):
@@ -352,6 +269,237 @@ __global__ void __launch_bounds__(NTHR, 2) bwd_dkdv_mfma(BwdProblem p, const flo
     }
 }
 
+#define GPTR(p) ((const __attribute__((address_space(1))) void*)(p))
+#define LPTR(p) ((__attribute__((address_space(3))) void*)(p))
+__device__ __forceinline__ void db_barrier_drain() { asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// ---------------------------------------------------------------------------------------
+// dq, in the forward's shape: a workgroup of 8 waves owns DQ_R = 4 lines (rows i) x 128
+// query columns of one (b, h) and streams 32-key blocks through a ring of LDS stages (K,
+// V of its lines and the 128 x 32 tile of the fp32 bias image, copied by
+// global_load_lds).  Wave w owns line w / 2 and query tiles 2 (w % 2), +1; Q and dO of its
+// queries stay in registers.  Per unit and block:
+//   S^T = K Q^T + C,  dP^T = V dO^T,  dS^T = P^T (dP^T - delta),  dQ^T += K^T dS^T
+// with K^T read transposed from the staged [key][d] tile (ds_read_b64_tr_b16).
+constexpr int DQ_R = 4;
+constexpr int DQ_WAVES = 8;
+constexpr int DQ_THR = 64 * DQ_WAVES;
+#ifndef TRI_ATTN_DQ_STAGES
+#define TRI_ATTN_DQ_STAGES 4
+#endif
+constexpr int DQ_STAGES = TRI_ATTN_DQ_STAGES;
+constexpr int DQ_TILE_RG = 8;               // line groups x column blocks one XCD works on together
+constexpr int DQ_TILE_JB = 4;
+struct DqStage {
+    __bf16 k[DQ_R][32][D];     // 64-byte rows, 16-byte chunks swizzled by kv_chunk()
+    __bf16 v[DQ_R][32][D];
+    float bias[IMG_BJ][IMG_BK];   // the image tile as stored: 128-byte rows, chunks img_chunk()
+};
+constexpr int DQ_STAGE_BYTES = static_cast<int>(sizeof(DqStage));
+constexpr int DQ_K_OFF = static_cast<int>(offsetof(DqStage, k));
+constexpr int DQ_V_OFF = static_cast<int>(offsetof(DqStage, v));
+constexpr int DQ_B_OFF = static_cast<int>(offsetof(DqStage, bias));
+constexpr int DQ_LINE_BYTES = 32 * D * 2;
+constexpr int DQ_CTILE_BYTES = 32 * IMG_BK * 4;
+static_assert(DQ_LINE_BYTES == 2048 && DQ_CTILE_BYTES == 4096 && DQ_V_OFF - DQ_K_OFF == 8192, "offsets below");
+static_assert(DQ_R * 2 * 2 == 2 * DQ_WAVES && IMG_BJ * IMG_BK * 4 == 2 * DQ_WAVES * 1024, "two K/V, two bias pieces per wave");
+__shared__ DqStage g_dq[DQ_STAGES];
+
+struct DqCtx {
+    const char* kv_row[2];     // K or V of the staged line at key 0
+    uint32_t kv_lds[2];
+    int key_local[2];
+    int part_bytes[2];
+    const float* img_wg;       // this workgroup's image tiles, nblk consecutive 128 x 32 tiles
+    int64_t key_bytes;
+    int last_key;
+};
+
+__device__ __forceinline__ void dq_stage(const DqCtx& cx, int n, int wave, int lane) {
+    char* lds = reinterpret_cast<char*>(&g_dq[n % DQ_STAGES]);
+    const int kb = 32 * n;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const int rel = min(kb + cx.key_local[t], cx.last_key) - kb;   // padded keys read a real key
+        const char* src = cx.kv_row[t] + static_cast<int64_t>(kb) * cx.key_bytes + rel * cx.key_bytes + cx.part_bytes[t];
+        __builtin_amdgcn_global_load_lds(GPTR(src), LPTR(lds + cx.kv_lds[t]), 16, 0, 0);
+    }
+    const char* src = reinterpret_cast<const char*>(cx.img_wg + static_cast<int64_t>(n) * IMG_BJ * IMG_BK) + lane * 16;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const int base = (2 * wave + t) * 1024;
+        __builtin_amdgcn_global_load_lds(GPTR(src + base), LPTR(lds + DQ_B_OFF + base), 16, 0, 0);
+    }
+}
+
+__device__ __forceinline__ void dq_barrier_keep() {
+    static_assert(DQ_STAGES == 3 || DQ_STAGES == 4, "three or four stages");
+    if constexpr (DQ_STAGES == 3) asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
+    if constexpr (DQ_STAGES == 4) asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+}
+
+__global__ void __launch_bounds__(DQ_THR) bwd_dq_lds(BwdProblem p, const float* img, const __bf16* g16,
+                                                     const float* delta, int n_jb, int n_rg, int nblk, int total) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int c = lane & 31, h2 = lane >> 5;
+    // XCD-aware remap (as in the forward): strips of DQ_TILE_RG line groups cut into tiles
+    // of DQ_TILE_RG x DQ_TILE_JB, column block fastest
+    const int w = blockIdx.x;
+    const int xcd = w % 8, slot = w / 8;
+    const int base = total / 8, extra = total % 8;
+    const int logical = xcd * base + (xcd < extra ? xcd : extra) + slot;
+    const int bh = logical / (n_jb * n_rg);
+    const int rem = logical - bh * n_jb * n_rg;
+    const int strip = rem / (DQ_TILE_RG * n_jb);
+    const int nr = min(DQ_TILE_RG, n_rg - strip * DQ_TILE_RG);
+    const int o = rem - strip * DQ_TILE_RG * n_jb;
+    const int tile = o / (nr * DQ_TILE_JB);
+    const int nj = min(DQ_TILE_JB, n_jb - tile * DQ_TILE_JB);
+    const int o2 = o - tile * nr * DQ_TILE_JB;
+    const int rg = strip * DQ_TILE_RG + o2 / nj;
+    const int jb = tile * DQ_TILE_JB + o2 % nj;
+    const int64_t N = p.N, H = p.H, HD = H * D, I = p.I;
+    const int64_t b = bh / H, h = bh % H;
+    const int64_t i0 = static_cast<int64_t>(rg) * DQ_R, j0 = static_cast<int64_t>(jb) * IMG_BJ;
+
+    DqCtx cx;
+    {
+        cx.key_bytes = HD * 2;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            // piece 2 w + t: line w / 2, K (w even) or V (w odd), keys 16 t .. +15
+            const int line = wave >> 1, kv = wave & 1;
+            int64_t i = i0 + line;
+            i = i < I ? i : I - 1;                       // padded lines read a real line (never stored)
+            cx.kv_row[t] = reinterpret_cast<const char*>(static_cast<const __bf16*>(kv ? p.v : p.k) +
+                                                         ((b * I + i) * N) * HD + h * D);
+            cx.kv_lds[t] = (kv ? DQ_V_OFF : DQ_K_OFF) + line * DQ_LINE_BYTES + t * 1024;
+            cx.key_local[t] = 16 * t + (lane >> 2);
+            cx.part_bytes[t] = kv_chunk(cx.key_local[t], lane & 3) * 16;
+        }
+        cx.img_wg = img + (static_cast<int64_t>(bh) * n_jb + jb) * nblk * static_cast<int64_t>(IMG_BJ * IMG_BK);
+        cx.last_key = static_cast<int>(N - 1);
+    }
+
+    const int line = wave >> 1, t0 = 2 * (wave & 1);
+    const int64_t i = i0 + line;
+    const bool iok = i < I;
+    const __bf16* q = static_cast<const __bf16*>(p.q);
+    bf16x8 qB[2][2], gB[2][2];
+    float nb[2], dl[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int64_t j = j0 + 32 * (t0 + u) + c;
+        const bool ok = iok && j < N;
+        const int64_t qo = ((b * I + i) * N + j) * HD + h * D;
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            qB[u][m] = frag(q, qo + 16 * m + 8 * h2, ok);
+            gB[u][m] = frag(g16, qo + 16 * m + 8 * h2, ok);
+        }
+        const int64_t qi = ((b * I + i) * N + j) * H + h;
+        nb[u] = ok ? neg_lse2(p.lse[qi]) : -INFINITY;
+        dl[u] = ok ? delta[qi] : 0.0f;
+    }
+    // LDS byte offsets (stage 0) of this lane's reads: K and V rows (A of S and dP), the
+    // transposed K reads (A of dQ), the bias chunks of its first tile (second tile +4096)
+    uint32_t ak[2], at[4], ac[4];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) ak[m] = DQ_K_OFF + line * DQ_LINE_BYTES + c * 64 + kv_chunk(c, 2 * m + h2) * 16;
+    {
+        const int ii = lane & 15, d0 = 16 * ((lane >> 4) & 1) + 4 * (ii & 3);
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int sub = 0; sub < 2; ++sub) {
+                const int key = 16 * m + 8 * sub + 4 * h2 + (ii >> 2);
+                at[2 * m + sub] = DQ_K_OFF + line * DQ_LINE_BYTES + key * 64 + kv_chunk(key, d0 >> 3) * 16 + (d0 & 7) * 2;
+            }
+    }
+#pragma unroll
+    for (int a = 0; a < 4; ++a) ac[a] = DQ_B_OFF + t0 * DQ_CTILE_BYTES + c * 128 + img_chunk(c, 2 * a + h2) * 16;
+    const uint32_t st0 = LDS_ADDR(&g_dq[0]);
+
+    f32x16 dQ[2] = {};
+    for (int n = 0; n < DQ_STAGES - 1 && n < nblk; ++n) dq_stage(cx, n, wave, lane);
+    if (nblk >= DQ_STAGES - 1)
+        dq_barrier_keep();
+    else
+        db_barrier_drain();
+    for (int n = 0; n < nblk; ++n) {
+        const uint32_t st = st0 + static_cast<uint32_t>(n % DQ_STAGES) * DQ_STAGE_BYTES;
+        const bool issue = n + DQ_STAGES - 1 < nblk;
+        if (issue) dq_stage(cx, n + DQ_STAGES - 1, wave, lane);
+        u32x4 kk[2], vv[2], cc[8];
+        u32x2 tt[4];
+        asm volatile(
+            "ds_read_b128 %0, %16\n\t"
+            "ds_read_b128 %1, %17\n\t"
+            "ds_read_b128 %2, %16 offset:8192\n\t"
+            "ds_read_b128 %3, %17 offset:8192\n\t"
+            "ds_read_b64_tr_b16 %4, %18\n\t"
+            "ds_read_b64_tr_b16 %5, %19\n\t"
+            "ds_read_b64_tr_b16 %6, %20\n\t"
+            "ds_read_b64_tr_b16 %7, %21\n\t"
+            "ds_read_b128 %8, %22\n\t"
+            "ds_read_b128 %9, %23\n\t"
+            "ds_read_b128 %10, %24\n\t"
+            "ds_read_b128 %11, %25\n\t"
+            "ds_read_b128 %12, %22 offset:4096\n\t"
+            "ds_read_b128 %13, %23 offset:4096\n\t"
+            "ds_read_b128 %14, %24 offset:4096\n\t"
+            "ds_read_b128 %15, %25 offset:4096\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(kk[0]), "=&v"(kk[1]), "=&v"(vv[0]), "=&v"(vv[1]), "=&v"(tt[0]), "=&v"(tt[1]), "=&v"(tt[2]),
+              "=&v"(tt[3]), "=&v"(cc[0]), "=&v"(cc[1]), "=&v"(cc[2]), "=&v"(cc[3]), "=&v"(cc[4]), "=&v"(cc[5]),
+              "=&v"(cc[6]), "=&v"(cc[7])
+            : "v"(st + ak[0]), "v"(st + ak[1]), "v"(st + at[0]), "v"(st + at[1]), "v"(st + at[2]), "v"(st + at[3]),
+              "v"(st + ac[0]), "v"(st + ac[1]), "v"(st + ac[2]), "v"(st + ac[3]));
+        bf16x8 kT[2];
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+            kT[m] = __builtin_bit_cast(bf16x8, u32x4{tt[2 * m][0], tt[2 * m][1], tt[2 * m + 1][0], tt[2 * m + 1][1]});
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            f32x16 C;
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) C[4 * a + e] = __uint_as_float(cc[4 * u + a][e]);
+            f32x16 S = mfma(__builtin_bit_cast(bf16x8, kk[0]), qB[u][0], C);
+            S = mfma(__builtin_bit_cast(bf16x8, kk[1]), qB[u][1], S);
+            f32x16 dP = mfma(__builtin_bit_cast(bf16x8, vv[0]), gB[u][0], f32x16{});
+            dP = mfma(__builtin_bit_cast(bf16x8, vv[1]), gB[u][1], dP);
+            f32x16 dS;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) dS[r] = __builtin_amdgcn_exp2f(fmaf(S[r], kScale, nb[u])) * (dP[r] - dl[u]);
+            bf16x8 s0, s1;
+            to_bf16(dS, s0, s1);
+            dQ[u] = mfma(kT[0], s0, dQ[u]);
+            dQ[u] = mfma(kT[1], s1, dQ[u]);
+        }
+        if (issue)
+            dq_barrier_keep();
+        else
+            db_barrier_drain();
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int64_t j = j0 + 32 * (t0 + u) + c;
+        if (iok && j < N) {
+            float* o = p.dq + ((b * I + i) * N + j) * HD + h * D;
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                f32x4 x;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) x[e] = dQ[u][4 * a + e] * kInvSqrtD;
+                *reinterpret_cast<f32x4*>(o + 8 * a + 4 * h2) = x;
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------------------
 // dbias[b, h, j, k] = sum over the rows i held of dS[i, j, k].  A workgroup of 8 waves owns
 // DB_Q = 128 queries x DB_K = 128 keys of one (b, h) and streams the rows i through a ring
@@ -400,8 +548,6 @@ static_assert(4 * DB_WAVES * 1024 == 4 * DB_Q * D * 2 && DB_Q == DB_K, "pieces o
 static_assert(DB_WAVES * 128 == 2 * DB_Q * 4, "lse / delta pieces");
 __shared__ DbStage g_db[DB_STAGES];
 
-#define GPTR(p) ((const __attribute__((address_space(1))) void*)(p))
-#define LPTR(p) ((__attribute__((address_space(3))) void*)(p))
 
 struct DbCtx {
     const char* src[4];        // this wave's four pieces: row base of (b, i = 0, pos, h), part applied
@@ -425,7 +571,6 @@ __device__ __forceinline__ void db_barrier_keep() {
     if constexpr (DB_STAGES == 3) asm volatile("s_waitcnt vmcnt(5)\n\ts_barrier" ::: "memory");
     if constexpr (DB_STAGES == 4) asm volatile("s_waitcnt vmcnt(10)\n\ts_barrier" ::: "memory");
 }
-__device__ __forceinline__ void db_barrier_drain() { asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 __global__ void __launch_bounds__(DB_THR) bwd_dbias_lds(BwdProblem p, const float* img, const __bf16* g16,
                                                         const float* lseT, const float* deltaT, int n_jb, int nblk,
@@ -621,9 +766,15 @@ hipError_t launch_backward_mfma(const BwdProblem& p, void* workspace, hipStream_
                        delta, lseT, deltaT, Ly.NP);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const dim3 lines(static_cast<unsigned>(n_jb), static_cast<unsigned>(p.I), static_cast<unsigned>(p.B * p.H));
-    hipLaunchKernelGGL(bwd_dq_mfma, lines, dim3(NTHR), 0, stream, p, img, g16, delta, static_cast<int>(n_jb),
-                       static_cast<int>(nblk));
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    {
+        const int64_t n_rg = (p.I + DQ_R - 1) / DQ_R;
+        const int64_t total = n_jb * n_rg * p.B * p.H;
+        if (total > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL(bwd_dq_lds, dim3(static_cast<unsigned>(total)), dim3(DQ_THR), 0, stream, p, img, g16, delta,
+                           static_cast<int>(n_jb), static_cast<int>(n_rg), static_cast<int>(nblk),
+                           static_cast<int>(total));
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     hipLaunchKernelGGL(bwd_dkdv_mfma, lines, dim3(NTHR), 0, stream, p, imgT, g16, lseT, deltaT,
                        static_cast<int>(n_jb), static_cast<int>(nblk), Ly.NP);
     if ((e = hipGetLastError()) != hipSuccess) return e;
