@@ -143,7 +143,7 @@ def other_pass(args, torch, P, W, cfg) -> dict:
         metric = "triangle-attention backward TFLOP/s (10·B·H·I·N²·D: S recompute, dP, dQ, dK, dV)"
         if cfg.dtype == "bf16" and D == 32:     # the matrix-core backward
             work, unit, peak, bound = 2.5 * fwd_flops, "TFLOP/s", PEAK_BF16_TFLOPS, "mfma"
-            kernels = "bwd_prep_kernel + bwd_dq_lds + bwd_dkdv_mfma + bwd_dbias_lds (bf16 MFMA, fp32 accumulate)"
+            kernels = "bwd_prep_kernel + bwd_dq_lds + bwd_dkdv_lds + bwd_dbias_lds (bf16 MFMA, fp32 accumulate)"
             dtype = "bf16"
         else:
             work, unit, peak, bound = 2.5 * fwd_flops, "TFLOP/s", PEAK_FP32_TFLOPS, "alu"

@@ -3,20 +3,21 @@
 // plain fp32 version used for every other case).
 //
 // Four kernels, each owning the sums it produces (no atomics, deterministic):
-//   bwd_prep_kernel   dout -> bf16 copy (the operand of the dP and dV products) and
-//                     delta = dout . out per query, in fp32.
-//   bwd_dq_mfma       one wave per (b, i, h, 32 queries), looping over 32-key blocks in
-//                     the forward's orientation (lane = query):
-//                       S^T  = K Q^T + C          C = the forward's bias image tile
-//                       dP^T = V dO^T
-//                       dS^T = P^T (dP^T - delta),  P^T = exp(S^T - lse)
-//                       dQ^T += K^T dS^T          K^T by an LDS transposed read
-//   bwd_dkdv_mfma     one wave per (b, i, h, 32 keys), looping over 32-query blocks in the
-//                     other orientation (lane = key), so that P and dS come out of the
-//                     accumulator layout as the B operands of
-//                       dV^T += dO^T P,  dK^T += Q^T dS     (dO^T, Q^T by transposed reads)
-//   bwd_dbias_mfma    one wave per (b, h, 32 queries, 32 keys), looping over every row i:
-//                       dbias^T += dS^T of row i (the bias is shared by all rows)
+//   bwd_prep_kernel   dout -> bf16 copy (the operand of the dP and dV products),
+//                     delta = dout . out per query, and delta and nb = -lse log2(e)
+//                     transposed to [b, i, h, j] (rows padded to whole 128-query tiles).
+//   bwd_dq_lds        4 lines x 128 queries per workgroup, 32-key blocks streamed through
+//                     an LDS ring (the forward's shape):
+//                       S^T = K Q^T + C,  dP^T = V dO^T,  dS^T = P^T (dP^T - delta),
+//                       dQ^T += K^T dS^T
+//   bwd_dkdv_lds      4 lines x 128 keys per workgroup, 32-query blocks streamed, in the
+//                     orientation in which P and dS leave the accumulator as B operands:
+//                       S = Q K^T + C,  dP = dO V^T,  dV^T += dO^T P,  dK^T += Q^T dS
+//   bwd_dbias_lds     128 queries x 128 keys of one (b, h) per workgroup, rows i streamed:
+//                       dbias^T += dS^T of every row i (the bias is shared by all rows)
+// Every streaming kernel copies its operands straight from global memory into a ring of
+// LDS stages (global_load_lds_dwordx4, one barrier per block) and reads them from there;
+// transposed operands come from ds_read_b64_tr_b16 on the natural [row][d] tiles.
 // Operand layouts are those of v_mfma_f32_32x32x16_bf16 (see kernel_bf16_mfma.hip): A and
 // B hold one row / column per lane with 8 consecutive k-values per half-wave; the
 // 32x32 fp32 result gives lane l column l % 32 and, in register r, row
@@ -38,16 +39,10 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int D = 32;
-constexpr int NWAVE = 4;
-constexpr int NTHR = 64 * NWAVE;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kSqrtD = 5.656854249492381f;
 constexpr float kScale = kLog2e / kSqrtD;        // S units (q.k + sqrt(D) bias) -> log2 units
 constexpr float kInvSqrtD = 0.17677669529663687f;
-constexpr int TILE_BYTES = 32 * D * 2;           // one wave's 32 x 32 bf16 tile in LDS
-#ifndef TRI_ATTN_DBIAS_AHEAD
-#define TRI_ATTN_DBIAS_AHEAD 3
-#endif
 
 #define LDS_ADDR(p) static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)(p)))
 
@@ -62,59 +57,8 @@ __device__ __forceinline__ bf16x8 frag(const __bf16* base, int64_t off, bool ok)
     return z;
 }
 
-__device__ __forceinline__ float bf16_to_f32(uint16_t u) { return __uint_as_float(static_cast<uint32_t>(u) << 16); }
-
 // 16-byte chunk `part` (d = 8*part .. +7) of tile row `row` sits at chunk kv_chunk(row, part)
 __host__ __device__ constexpr int kv_chunk(int row, int part) { return part ^ ((row >> 1) & 3); }
-
-// Per-lane LDS offsets inside one tile: the two row-major chunks this lane writes (row
-// l%32, d-halves m = 0, 1) and the sources of the transposed reads.  A transposed read
-// gives lane l row d = l%32 of the tile's transpose at tile rows {4h2 + b, 8 + 4h2 + b}
-// + 16m (b = 0..3, h2 = l/32): the row order of the accumulator layout above.
-struct TileLane {
-    uint32_t wr[2];
-    uint32_t tr[2][2];
-};
-
-__device__ __forceinline__ TileLane tile_lane(int lane) {
-    TileLane L;
-    const int c = lane & 31, h2 = lane >> 5;
-#pragma unroll
-    for (int m = 0; m < 2; ++m) L.wr[m] = c * 64 + kv_chunk(c, 2 * m + h2) * 16;
-    const int i = lane & 15, d0 = 16 * ((lane >> 4) & 1) + 4 * (i & 3);
-#pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-        for (int sub = 0; sub < 2; ++sub) {
-            const int row = 16 * m + 8 * sub + 4 * h2 + (i >> 2);
-            L.tr[m][sub] = row * 64 + kv_chunk(row, d0 >> 3) * 16 + (d0 & 7) * 2;
-        }
-    return L;
-}
-
-// Write a tile held as row fragments (lane row l%32, d-halves w0, w1) to this wave's LDS
-// tile at `base` and read back its transpose as A operands t0, t1.  The writes and reads
-// wait for themselves, so the tile may be rewritten right after.
-__device__ __forceinline__ void transpose_tile(uint32_t base, const TileLane& L, bf16x8 w0, bf16x8 w1, bf16x8& t0,
-                                               bf16x8& t1) {
-    u32x2 r0, r1, r2, r3;
-    asm volatile(
-        "ds_write_b128 %4, %6\n\t"
-        "ds_write_b128 %5, %7\n\t"
-        "s_waitcnt lgkmcnt(0)\n\t"
-        "ds_read_b64_tr_b16 %0, %8\n\t"
-        "ds_read_b64_tr_b16 %1, %9\n\t"
-        "ds_read_b64_tr_b16 %2, %10\n\t"
-        "ds_read_b64_tr_b16 %3, %11\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
-        : "v"(base + L.wr[0]), "v"(base + L.wr[1]), "v"(__builtin_bit_cast(u32x4, w0)),
-          "v"(__builtin_bit_cast(u32x4, w1)), "v"(base + L.tr[0][0]), "v"(base + L.tr[0][1]),
-          "v"(base + L.tr[1][0]), "v"(base + L.tr[1][1])
-        : "memory");
-    t0 = __builtin_bit_cast(bf16x8, u32x4{r0[0], r0[1], r1[0], r1[1]});
-    t1 = __builtin_bit_cast(bf16x8, u32x4{r2[0], r2[1], r3[0], r3[1]});
-}
 
 __device__ __forceinline__ void to_bf16(const f32x16& x, bf16x8& lo, bf16x8& hi) {
     lo = __builtin_convertvector(__builtin_shufflevector(x, x, 0, 1, 2, 3, 4, 5, 6, 7), bf16x8);
@@ -126,17 +70,17 @@ __device__ __forceinline__ float neg_lse2(float lse) { return lse == -INFINITY ?
 
 // ---------------------------------------------------------------------------------------
 // One thread per (b, i, h, j) with j padded to NP: dout of query (b, i, j, h) rounded to
-// bf16, delta = dout . out, and lse / delta also written transposed, [b, i, h, j], so that
-// a lane can read 4 consecutive queries with one 16-byte load; padded j get lse = -inf
-// (no probability) and delta = 0.
-__global__ void __launch_bounds__(256) bwd_prep_kernel(BwdProblem p, __bf16* g16, float* delta, float* lseT,
+// bf16, delta = dout . out, and, transposed to [b, i, h, j] so that the row-streaming
+// kernels copy whole rows, delta and nb = -lse log2(e) (the shift of the score in log2
+// units; -inf for a query without any finite score, and for the padded j, whose delta is 0).
+__global__ void __launch_bounds__(256) bwd_prep_kernel(BwdProblem p, __bf16* g16, float* delta, float* nbT,
                                                        float* deltaT, int64_t NP) {
     const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
     const int64_t total = p.B * p.I * p.H * NP;
     if (t >= total) return;
     const int64_t j = t % NP, lh = t / NP, h = lh % p.H, line = lh / p.H;   // line = b * I + i
     if (j >= p.N) {
-        lseT[t] = -INFINITY;
+        nbT[t] = -INFINITY;
         deltaT[t] = 0.0f;
         return;
     }
@@ -154,119 +98,7 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdProblem p, __bf16* g16
     }
     delta[q] = dl;
     deltaT[t] = dl;
-    lseT[t] = p.lse[q];
-}
-
-// ---------------------------------------------------------------------------------------
-// imgT: the bias image of the transposed bias without the mask (built in the ending
-// orientation), so that tile (key block of IMG_BJ, query block of IMG_BK) row kk holds
-// bias[b, h, q, key] * sqrt(D) for 32 consecutive queries q (-inf past the last query):
-// the accumulator input of S for a lane that owns a key.  Dropped keys are zeroed at the end.
-__global__ void __launch_bounds__(NTHR, 2) bwd_dkdv_mfma(BwdProblem p, const float* imgT, const __bf16* g16,
-                                                         const float* lseT, const float* deltaT, int n_kb,
-                                                         int nqblk, int64_t NP) {
-    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int c = lane & 31, h2 = lane >> 5;
-    const int64_t N = p.N, H = p.H, HD = H * D;
-    const int64_t bh = blockIdx.z, b = bh / H, h = bh % H, i = blockIdx.y;
-    const int kb = blockIdx.x;                            // block of IMG_BJ keys
-    const int kk = wave * 32 + c;                         // key inside the block
-    const int64_t key = static_cast<int64_t>(kb) * IMG_BJ + kk;
-    const bool kok = key < N;
-    const int64_t row = (b * p.I + i) * N;
-    const __bf16* q = static_cast<const __bf16*>(p.q);
-    const __bf16* k = static_cast<const __bf16*>(p.k);
-    const __bf16* v = static_cast<const __bf16*>(p.v);
-    const int64_t ko = (row + key) * HD + h * D;
-    const float* lse_l = lseT + ((b * p.I + i) * H + h) * NP + 4 * h2;
-    const float* dl_l = deltaT + ((b * p.I + i) * H + h) * NP + 4 * h2;
-    const float* img_row = imgT + (bh * n_kb + kb) * static_cast<int64_t>(nqblk) * IMG_BJ * IMG_BK + kk * IMG_BK;
-
-    bf16x8 kB[2], vB[2];
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-        kB[m] = frag(k, ko + 16 * m + 8 * h2, kok);
-        vB[m] = frag(v, ko + 16 * m + 8 * h2, kok);
-    }
-    const bool dropped = !kok || (p.mask && p.mask[b * N + (kok ? key : 0)] == -INFINITY);
-    const TileLane L = tile_lane(lane);
-    __shared__ __attribute__((aligned(16))) char lds[NWAVE * 2 * TILE_BYTES];
-    const uint32_t tile_g = LDS_ADDR(lds) + wave * 2 * TILE_BYTES, tile_q = tile_g + TILE_BYTES;
-
-    // operands of query block n: Q, dO rows (lane = query), and for this lane's key the
-    // accumulator input, lse and delta of the 16 query rows 8a + 4h2 + e of its registers
-    struct Blk {
-        bf16x8 qA[2], gA[2];
-        f32x4 c[4], nl[4], dl[4];
-    };
-    auto fetch = [&](int n, Blk& X) {
-        const int64_t qb = static_cast<int64_t>(n) * IMG_BK;
-        const int64_t jq = qb + c;
-        const bool jok = jq < N;
-        const int64_t qo = (row + jq) * HD + h * D;
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            X.qA[m] = frag(q, qo + 16 * m + 8 * h2, jok);
-            X.gA[m] = frag(g16, qo + 16 * m + 8 * h2, jok);
-        }
-        const float* t = img_row + static_cast<int64_t>(n) * IMG_BJ * IMG_BK;
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-            X.c[a] = *reinterpret_cast<const f32x4*>(t + img_chunk(kk, 2 * a + h2) * 4);
-            X.nl[a] = *reinterpret_cast<const f32x4*>(lse_l + qb + 8 * a);
-            X.dl[a] = *reinterpret_cast<const f32x4*>(dl_l + qb + 8 * a);
-        }
-    };
-    f32x16 dK = {}, dV = {};
-    Blk cur, nxt;
-    fetch(0, cur);
-    for (int n = 0; n < nqblk; ++n) {
-        if (n + 1 < nqblk) fetch(n + 1, nxt);             // next block's loads fly during this block
-        const bf16x8 (&qA)[2] = cur.qA;
-        const bf16x8 (&gA)[2] = cur.gA;
-        f32x16 C, nl, dl;
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                C[4 * a + e] = cur.c[a][e];
-                nl[4 * a + e] = cur.nl[a][e];
-                dl[4 * a + e] = cur.dl[a][e];
-            }
-        f32x16 S = mfma(qA[0], kB[0], C);
-        S = mfma(qA[1], kB[1], S);
-        f32x16 dP = mfma(gA[0], vB[0], f32x16{});
-        dP = mfma(gA[1], vB[1], dP);
-        // P overwrites S and dS overwrites dP
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            S[r] = __builtin_amdgcn_exp2f(fmaf(S[r], kScale, neg_lse2(nl[r])));
-            dP[r] = S[r] * (dP[r] - dl[r]);
-        }
-        bf16x8 p0, p1, s0, s1, gT0, gT1, qT0, qT1;
-        to_bf16(S, p0, p1);
-        to_bf16(dP, s0, s1);
-        transpose_tile(tile_g, L, gA[0], gA[1], gT0, gT1);
-        transpose_tile(tile_q, L, qA[0], qA[1], qT0, qT1);
-        dV = mfma(gT0, p0, dV);
-        dV = mfma(gT1, p1, dV);
-        dK = mfma(qT0, s0, dK);
-        dK = mfma(qT1, s1, dK);
-        cur = nxt;
-    }
-    if (kok) {
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-            f32x4 xk, xv;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                xk[e] = dropped ? 0.0f : dK[4 * a + e] * kInvSqrtD;
-                xv[e] = dropped ? 0.0f : dV[4 * a + e];
-            }
-            *reinterpret_cast<f32x4*>(p.dk + ko + 8 * a + 4 * h2) = xk;
-            *reinterpret_cast<f32x4*>(p.dv + ko + 8 * a + 4 * h2) = xv;
-        }
-    }
+    nbT[t] = neg_lse2(p.lse[q]);
 }
 
 #define GPTR(p) ((const __attribute__((address_space(1))) void*)(p))
@@ -501,6 +333,272 @@ __global__ void __launch_bounds__(DQ_THR) bwd_dq_lds(BwdProblem p, const float* 
 }
 
 // ---------------------------------------------------------------------------------------
+// dk, dv: a workgroup of 8 waves owns DK_R = 4 lines x 128 keys of one (b, h) and streams
+// 32-query blocks through a ring of LDS stages: Q and dO of its lines, the 128 x 32 tile
+// of imgT and nb = -lse log2(e), delta of the block's queries.  imgT is the bias image of
+// the transposed bias without the mask (built in the ending orientation): row kk of a tile
+// holds bias[b, h, q, key] sqrt(D) for 32 consecutive queries q (-inf past the last
+// query).  Wave w owns line w / 2 and key tiles 2 (w % 2), +1 (lane = key; K and V of its
+// keys stay in registers).  Per unit and block, in the orientation in which P and dS leave
+// the accumulator as the B operands of the next products:
+//   S = Q K^T + C,  dP = dO V^T,  dS = P (dP - delta),  dV^T += dO^T P,  dK^T += Q^T dS
+// with Q^T, dO^T read transposed from the staged [query][d] tiles.  A dropped key
+// (masked, or past the end) gets zero gradients.
+constexpr int DK_R = 4;
+constexpr int DK_WAVES = 8;
+constexpr int DK_THR = 64 * DK_WAVES;
+#ifndef TRI_ATTN_DK_STAGES
+#define TRI_ATTN_DK_STAGES 4
+#endif
+constexpr int DK_STAGES = TRI_ATTN_DK_STAGES;
+constexpr int DK_TILE_RG = 8;
+constexpr int DK_TILE_KB = 4;
+struct DkStage {
+    __bf16 q[DK_R][32][D];        // 64-byte rows, 16-byte chunks swizzled by kv_chunk()
+    __bf16 g[DK_R][32][D];        // dO rounded to bf16
+    float bias[IMG_BJ][IMG_BK];   // the imgT tile as stored: 128-byte rows, chunks img_chunk()
+    float nb[DK_R][32];
+    float dl[DK_R][32];
+};
+constexpr int DK_STAGE_BYTES = static_cast<int>(sizeof(DkStage));
+constexpr int DK_Q_OFF = static_cast<int>(offsetof(DkStage, q));
+constexpr int DK_G_OFF = static_cast<int>(offsetof(DkStage, g));
+constexpr int DK_B_OFF = static_cast<int>(offsetof(DkStage, bias));
+constexpr int DK_N_OFF = static_cast<int>(offsetof(DkStage, nb));
+static_assert(DK_G_OFF - DK_Q_OFF == 8192 && offsetof(DkStage, dl) - offsetof(DkStage, nb) == 512, "offsets below");
+__shared__ DkStage g_dk[DK_STAGES];
+
+__device__ __forceinline__ void dk_barrier_keep() {
+    static_assert(DK_STAGES == 3 || DK_STAGES == 4, "three or four stages");
+    if constexpr (DK_STAGES == 3) asm volatile("s_waitcnt vmcnt(5)\n\ts_barrier" ::: "memory");
+    if constexpr (DK_STAGES == 4) asm volatile("s_waitcnt vmcnt(10)\n\ts_barrier" ::: "memory");
+}
+
+struct DkCtx {
+    const char* qg_row[2];     // Q or dO of the staged line at query 0
+    uint32_t qg_lds[2];
+    int q_local[2];
+    int part_bytes[2];
+    const float* img_wg;       // this workgroup's imgT tiles, nqblk consecutive 128 x 32 tiles
+    const char* ls_src;        // nb or delta piece of query block 0 (lanes 0 .. 7)
+    uint32_t ls_dst;
+    int64_t q_bytes;
+    int last_q;
+};
+
+__device__ __forceinline__ void dk_stage(const DkCtx& cx, int n, int wave, int lane) {
+    char* lds = reinterpret_cast<char*>(&g_dk[n % DK_STAGES]);
+    const int qb = 32 * n;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const int rel = min(qb + cx.q_local[t], cx.last_q) - qb;    // padded queries read a real one
+        const char* src = cx.qg_row[t] + static_cast<int64_t>(qb) * cx.q_bytes + rel * cx.q_bytes + cx.part_bytes[t];
+        __builtin_amdgcn_global_load_lds(GPTR(src), LPTR(lds + cx.qg_lds[t]), 16, 0, 0);
+    }
+    const char* src = reinterpret_cast<const char*>(cx.img_wg + static_cast<int64_t>(n) * IMG_BJ * IMG_BK) + lane * 16;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const int base = (2 * wave + t) * 1024;
+        __builtin_amdgcn_global_load_lds(GPTR(src + base), LPTR(lds + DK_B_OFF + base), 16, 0, 0);
+    }
+    if (lane < 8) __builtin_amdgcn_global_load_lds(GPTR(cx.ls_src + qb * 4), LPTR(lds + cx.ls_dst), 16, 0, 0);
+}
+
+__global__ void __launch_bounds__(DK_THR) bwd_dkdv_lds(BwdProblem p, const float* imgT, const __bf16* g16,
+                                                       const float* nbT, const float* deltaT, int n_kb, int n_rg,
+                                                       int nqblk, int64_t NP, int total) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int c = lane & 31, h2 = lane >> 5;
+    const int w = blockIdx.x;
+    const int xcd = w % 8, slot = w / 8;
+    const int base = total / 8, extra = total % 8;
+    const int logical = xcd * base + (xcd < extra ? xcd : extra) + slot;
+    const int bh = logical / (n_kb * n_rg);
+    const int rem = logical - bh * n_kb * n_rg;
+    const int strip = rem / (DK_TILE_RG * n_kb);
+    const int nr = min(DK_TILE_RG, n_rg - strip * DK_TILE_RG);
+    const int o = rem - strip * DK_TILE_RG * n_kb;
+    const int tile = o / (nr * DK_TILE_KB);
+    const int nk = min(DK_TILE_KB, n_kb - tile * DK_TILE_KB);
+    const int o2 = o - tile * nr * DK_TILE_KB;
+    const int rg = strip * DK_TILE_RG + o2 / nk;
+    const int kb = tile * DK_TILE_KB + o2 % nk;
+    const int64_t N = p.N, H = p.H, HD = H * D, I = p.I;
+    const int64_t b = bh / H, h = bh % H;
+    const int64_t i0 = static_cast<int64_t>(rg) * DK_R, k0 = static_cast<int64_t>(kb) * IMG_BJ;
+
+    DkCtx cx;
+    {
+        cx.q_bytes = HD * 2;
+        const int sline = wave >> 1, qg = wave & 1;   // pieces of wave w: line w / 2, Q (w even) or dO, both halves
+        int64_t i = i0 + sline;
+        i = i < I ? i : I - 1;                         // padded lines read a real line (never stored)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            cx.qg_row[t] = reinterpret_cast<const char*>((qg ? g16 : static_cast<const __bf16*>(p.q)) +
+                                                         ((b * I + i) * N) * HD + h * D);
+            cx.qg_lds[t] = (qg ? DK_G_OFF : DK_Q_OFF) + sline * 2048 + t * 1024;
+            cx.q_local[t] = 16 * t + (lane >> 2);
+            cx.part_bytes[t] = kv_chunk(cx.q_local[t], lane & 3) * 16;
+        }
+        cx.img_wg = imgT + (static_cast<int64_t>(bh) * n_kb + kb) * nqblk * static_cast<int64_t>(IMG_BJ * IMG_BK);
+        // nb of line w (w < 4) or delta of line w - 4, 32 floats of the block in lanes 0 .. 7
+        int64_t il = i0 + (wave & 3);
+        il = il < I ? il : I - 1;
+        cx.ls_src = reinterpret_cast<const char*>((wave < 4 ? nbT : deltaT) + ((b * I + il) * H + h) * NP + 4 * (lane & 7));
+        cx.ls_dst = DK_N_OFF + 128 * wave;
+        cx.last_q = static_cast<int>(N - 1);
+    }
+
+    const int line = wave >> 1, t0 = 2 * (wave & 1);
+    const int64_t i = i0 + line;
+    const bool iok = i < I;
+    const __bf16* kp = static_cast<const __bf16*>(p.k);
+    const __bf16* vp = static_cast<const __bf16*>(p.v);
+    bf16x8 kB[2][2], vB[2][2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int64_t key = k0 + 32 * (t0 + u) + c;
+        const int64_t ko = ((b * I + i) * N + key) * HD + h * D;
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            kB[u][m] = frag(kp, ko + 16 * m + 8 * h2, iok && key < N);
+            vB[u][m] = frag(vp, ko + 16 * m + 8 * h2, iok && key < N);
+        }
+    }
+    // LDS byte offsets (stage 0) of this lane's reads: Q and dO rows (A of S and dP), the
+    // transposed reads of Q and dO (A of dK, dV), the bias chunks of its first key tile
+    // (second tile +4096), and nb / delta of its 16 query rows 8a + 4 h2 + e
+    uint32_t aq[2], at[4], ac[4];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) aq[m] = DK_Q_OFF + line * 2048 + c * 64 + kv_chunk(c, 2 * m + h2) * 16;
+    {
+        const int ii = lane & 15, d0 = 16 * ((lane >> 4) & 1) + 4 * (ii & 3);
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int sub = 0; sub < 2; ++sub) {
+                const int row = 16 * m + 8 * sub + 4 * h2 + (ii >> 2);
+                at[2 * m + sub] = DK_Q_OFF + line * 2048 + row * 64 + kv_chunk(row, d0 >> 3) * 16 + (d0 & 7) * 2;
+            }
+    }
+#pragma unroll
+    for (int a = 0; a < 4; ++a) ac[a] = DK_B_OFF + t0 * 4096 + c * 128 + img_chunk(c, 2 * a + h2) * 16;
+    const uint32_t an = DK_N_OFF + line * 128 + 16 * h2;
+    const uint32_t st0 = LDS_ADDR(&g_dk[0]);
+
+    f32x16 dK[2] = {}, dV[2] = {};
+    for (int n = 0; n < DK_STAGES - 1 && n < nqblk; ++n) dk_stage(cx, n, wave, lane);
+    if (nqblk >= DK_STAGES - 1)
+        dk_barrier_keep();
+    else
+        db_barrier_drain();
+    for (int n = 0; n < nqblk; ++n) {
+        const uint32_t st = st0 + static_cast<uint32_t>(n % DK_STAGES) * DK_STAGE_BYTES;
+        const bool issue = n + DK_STAGES - 1 < nqblk;
+        if (issue) dk_stage(cx, n + DK_STAGES - 1, wave, lane);
+        u32x4 qq[2], gg[2], nn[4], dd[4];
+        u32x2 tq[4], tg[4];
+        asm volatile(
+            "ds_read_b128 %0, %20\n\t"
+            "ds_read_b128 %1, %21\n\t"
+            "ds_read_b128 %2, %20 offset:8192\n\t"
+            "ds_read_b128 %3, %21 offset:8192\n\t"
+            "ds_read_b64_tr_b16 %4, %22\n\t"
+            "ds_read_b64_tr_b16 %5, %23\n\t"
+            "ds_read_b64_tr_b16 %6, %24\n\t"
+            "ds_read_b64_tr_b16 %7, %25\n\t"
+            "ds_read_b64_tr_b16 %8, %22 offset:8192\n\t"
+            "ds_read_b64_tr_b16 %9, %23 offset:8192\n\t"
+            "ds_read_b64_tr_b16 %10, %24 offset:8192\n\t"
+            "ds_read_b64_tr_b16 %11, %25 offset:8192\n\t"
+            "ds_read_b128 %12, %26\n\t"
+            "ds_read_b128 %13, %26 offset:32\n\t"
+            "ds_read_b128 %14, %26 offset:64\n\t"
+            "ds_read_b128 %15, %26 offset:96\n\t"
+            "ds_read_b128 %16, %26 offset:512\n\t"
+            "ds_read_b128 %17, %26 offset:544\n\t"
+            "ds_read_b128 %18, %26 offset:576\n\t"
+            "ds_read_b128 %19, %26 offset:608\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(qq[0]), "=&v"(qq[1]), "=&v"(gg[0]), "=&v"(gg[1]), "=&v"(tq[0]), "=&v"(tq[1]), "=&v"(tq[2]),
+              "=&v"(tq[3]), "=&v"(tg[0]), "=&v"(tg[1]), "=&v"(tg[2]), "=&v"(tg[3]), "=&v"(nn[0]), "=&v"(nn[1]),
+              "=&v"(nn[2]), "=&v"(nn[3]), "=&v"(dd[0]), "=&v"(dd[1]), "=&v"(dd[2]), "=&v"(dd[3])
+            : "v"(st + aq[0]), "v"(st + aq[1]), "v"(st + at[0]), "v"(st + at[1]), "v"(st + at[2]), "v"(st + at[3]),
+              "v"(st + an));
+        bf16x8 qT[2], gT[2];
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            qT[m] = __builtin_bit_cast(bf16x8, u32x4{tq[2 * m][0], tq[2 * m][1], tq[2 * m + 1][0], tq[2 * m + 1][1]});
+            gT[m] = __builtin_bit_cast(bf16x8, u32x4{tg[2 * m][0], tg[2 * m][1], tg[2 * m + 1][0], tg[2 * m + 1][1]});
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            u32x4 cc[4];
+            asm volatile(
+                "ds_read_b128 %0, %4\n\t"
+                "ds_read_b128 %1, %5\n\t"
+                "ds_read_b128 %2, %6\n\t"
+                "ds_read_b128 %3, %7\n\t"
+                "s_waitcnt lgkmcnt(0)"
+                : "=&v"(cc[0]), "=&v"(cc[1]), "=&v"(cc[2]), "=&v"(cc[3])
+                : "v"(st + ac[0] + 4096 * u), "v"(st + ac[1] + 4096 * u), "v"(st + ac[2] + 4096 * u),
+                  "v"(st + ac[3] + 4096 * u));
+            f32x16 S;
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) S[4 * a + e] = __uint_as_float(cc[a][e]);
+            S = mfma(__builtin_bit_cast(bf16x8, qq[0]), kB[u][0], S);
+            S = mfma(__builtin_bit_cast(bf16x8, qq[1]), kB[u][1], S);
+            f32x16 dP = mfma(__builtin_bit_cast(bf16x8, gg[0]), vB[u][0], f32x16{});
+            dP = mfma(__builtin_bit_cast(bf16x8, gg[1]), vB[u][1], dP);
+            // register r = 4a + e holds query row 8a + 4 h2 + e: nb and delta from nn[a][e], dd[a][e]
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * a + e;
+                    S[r] = __builtin_amdgcn_exp2f(fmaf(S[r], kScale, __uint_as_float(nn[a][e])));
+                    dP[r] = S[r] * (dP[r] - __uint_as_float(dd[a][e]));
+                }
+            bf16x8 p0, p1, s0, s1;
+            to_bf16(S, p0, p1);
+            to_bf16(dP, s0, s1);
+            dV[u] = mfma(gT[0], p0, dV[u]);
+            dV[u] = mfma(gT[1], p1, dV[u]);
+            dK[u] = mfma(qT[0], s0, dK[u]);
+            dK[u] = mfma(qT[1], s1, dK[u]);
+        }
+        if (issue)
+            dk_barrier_keep();
+        else
+            db_barrier_drain();
+    }
+    if (iok) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int64_t key = k0 + 32 * (t0 + u) + c;
+            if (key >= N) continue;
+            const bool dropped = p.mask && p.mask[b * N + key] == -INFINITY;
+            const int64_t ko = ((b * I + i) * N + key) * HD + h * D;
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                f32x4 xk, xv;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    xk[e] = dropped ? 0.0f : dK[u][4 * a + e] * kInvSqrtD;
+                    xv[e] = dropped ? 0.0f : dV[u][4 * a + e];
+                }
+                *reinterpret_cast<f32x4*>(p.dk + ko + 8 * a + 4 * h2) = xk;
+                *reinterpret_cast<f32x4*>(p.dv + ko + 8 * a + 4 * h2) = xv;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------
 // dbias[b, h, j, k] = sum over the rows i held of dS[i, j, k].  A workgroup of 8 waves owns
 // DB_Q = 128 queries x DB_K = 128 keys of one (b, h) and streams the rows i through a ring
 // of LDS stages: per row the waves copy Q, dO (its queries), K, V (its keys), lse and delta
@@ -554,7 +652,7 @@ struct DbCtx {
     uint32_t dst[4];           // byte offset of each piece inside a stage
     int64_t row_step;          // bytes between rows i of one tensor
     const char* ls_src;        // lse / delta piece of row 0 (lanes 0 .. 7), or null
-    int64_t ls_step;           // bytes between rows i of lseT
+    int64_t ls_step;           // bytes between rows i of nbT
     uint32_t ls_dst;
 };
 
@@ -573,7 +671,7 @@ __device__ __forceinline__ void db_barrier_keep() {
 }
 
 __global__ void __launch_bounds__(DB_THR) bwd_dbias_lds(BwdProblem p, const float* img, const __bf16* g16,
-                                                        const float* lseT, const float* deltaT, int n_jb, int nblk,
+                                                        const float* nbT, const float* deltaT, int n_jb, int nblk,
                                                         int64_t NP, int n_t, int total) {
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -616,7 +714,7 @@ __global__ void __launch_bounds__(DB_THR) bwd_dbias_lds(BwdProblem p, const floa
         }
         cx.row_step = N * HD * 2;
         // lse / delta: wave w < 4 copies lse of queries 32 w .. +31, wave w >= 4 delta of 32 (w - 4)
-        const float* ls = wave < 4 ? lseT : deltaT;
+        const float* ls = wave < 4 ? nbT : deltaT;
         cx.ls_src = reinterpret_cast<const char*>(ls + (b * p.I * H + h) * NP + j0 + 32 * (wave & 3) + 4 * (lane & 7));
         cx.ls_step = H * NP * 4;
         cx.ls_dst = DB_L_OFF + 128 * wave;
@@ -688,7 +786,7 @@ __global__ void __launch_bounds__(DB_THR) bwd_dbias_lds(BwdProblem p, const floa
               "=&v"(vv[3]), "=&v"(qq[0]), "=&v"(qq[1]), "=&v"(gg[0]), "=&v"(gg[1]), "=&v"(lse), "=&v"(dl)
             : "v"(st + ok[0]), "v"(st + ok[1]), "v"(st + oq[0]), "v"(st + oq[1]), "i"(DB_K_OFF), "i"(DB_K_OFF + 2048),
               "i"(DB_V_OFF), "i"(DB_V_OFF + 2048), "i"(DB_Q_OFF), "i"(DB_G_OFF), "v"(st + ol), "i"(DB_Q * 4));
-        const float nb = neg_lse2(lse);
+        const float nb = lse;   // already -lse log2(e)
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             f32x16 S = mfma(__builtin_bit_cast(bf16x8, kk[2 * u]), __builtin_bit_cast(bf16x8, qq[0]), C[u]);
@@ -722,7 +820,7 @@ namespace {
 struct BwdLayout {
     Problem fwd, tr;        // image problems: the bias, and its transpose without the mask
     int64_t NP, nq;
-    size_t img, imgT, g16, delta, lseT, deltaT, total;   // byte offsets / total
+    size_t img, imgT, g16, delta, nbT, deltaT, total;   // byte offsets / total
 };
 
 BwdLayout bwd_layout(const BwdProblem& p) {
@@ -737,8 +835,8 @@ BwdLayout bwd_layout(const BwdProblem& p) {
     L.imgT = L.img + bias_image_bytes(L.fwd);
     L.g16 = L.imgT + bias_image_bytes(L.tr);
     L.delta = L.g16 + static_cast<size_t>(L.nq) * D * 2;
-    L.lseT = L.delta + (static_cast<size_t>(L.nq) * 4 + 15) / 16 * 16;
-    L.deltaT = L.lseT + per_line;
+    L.nbT = L.delta + (static_cast<size_t>(L.nq) * 4 + 15) / 16 * 16;
+    L.deltaT = L.nbT + per_line;
     L.total = L.deltaT + per_line;
     return L;
 }
@@ -755,7 +853,7 @@ hipError_t launch_backward_mfma(const BwdProblem& p, void* workspace, hipStream_
     float* imgT = reinterpret_cast<float*>(ws + Ly.imgT);
     __bf16* g16 = reinterpret_cast<__bf16*>(ws + Ly.g16);
     float* delta = reinterpret_cast<float*>(ws + Ly.delta);
-    float* lseT = reinterpret_cast<float*>(ws + Ly.lseT);
+    float* nbT = reinterpret_cast<float*>(ws + Ly.nbT);
     float* deltaT = reinterpret_cast<float*>(ws + Ly.deltaT);
     const int64_t n_prep = p.B * p.I * p.H * Ly.NP;
     if (p.D != D || (n_prep + 255) / 256 > 0x7FFFFFFF || (p.N + 63) / 64 > 65535) return hipErrorInvalidConfiguration;
@@ -763,9 +861,8 @@ hipError_t launch_backward_mfma(const BwdProblem& p, void* workspace, hipStream_
     if (e != hipSuccess) return e;
     if ((e = launch_bias_image(Ly.tr, imgT, stream)) != hipSuccess) return e;
     hipLaunchKernelGGL(bwd_prep_kernel, dim3(static_cast<unsigned>((n_prep + 255) / 256)), dim3(256), 0, stream, p, g16,
-                       delta, lseT, deltaT, Ly.NP);
+                       delta, nbT, deltaT, Ly.NP);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    const dim3 lines(static_cast<unsigned>(n_jb), static_cast<unsigned>(p.I), static_cast<unsigned>(p.B * p.H));
     {
         const int64_t n_rg = (p.I + DQ_R - 1) / DQ_R;
         const int64_t total = n_jb * n_rg * p.B * p.H;
@@ -775,13 +872,19 @@ hipError_t launch_backward_mfma(const BwdProblem& p, void* workspace, hipStream_
                            static_cast<int>(total));
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(bwd_dkdv_mfma, lines, dim3(NTHR), 0, stream, p, imgT, g16, lseT, deltaT,
-                       static_cast<int>(n_jb), static_cast<int>(nblk), Ly.NP);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    {
+        const int64_t n_rg = (p.I + DK_R - 1) / DK_R;
+        const int64_t total = n_jb * n_rg * p.B * p.H;
+        if (total > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL(bwd_dkdv_lds, dim3(static_cast<unsigned>(total)), dim3(DK_THR), 0, stream, p, imgT, g16, nbT,
+                           deltaT, static_cast<int>(n_jb), static_cast<int>(n_rg), static_cast<int>(nblk), Ly.NP,
+                           static_cast<int>(total));
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     const int64_t n_t = (p.N + DB_Q - 1) / DB_Q;
     const int64_t total = n_t * n_t * p.B * p.H;
     if (total > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(bwd_dbias_lds, dim3(static_cast<unsigned>(total)), dim3(DB_THR), 0, stream, p, img, g16, lseT,
+    hipLaunchKernelGGL(bwd_dbias_lds, dim3(static_cast<unsigned>(total)), dim3(DB_THR), 0, stream, p, img, g16, nbT,
                        deltaT, static_cast<int>(n_jb), static_cast<int>(nblk), Ly.NP, static_cast<int>(n_t),
                        static_cast<int>(total));
     return hipGetLastError();
