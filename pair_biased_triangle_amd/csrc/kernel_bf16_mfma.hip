@@ -195,15 +195,6 @@ __global__ void __launch_bounds__(IMG_THR) bias_image_kernel(Problem p, float* i
 constexpr int IMG16_Q = 64;                 // queries per workgroup of the image kernel
 static_assert(BJ % IMG16_Q == 0, "an image workgroup fills part of one column block");
 
-// Value of bias + mask for query j and absolute key `key` (starting node bias[b,h,j,key],
-// ending node bias[b,h,key,j]).
-__device__ __forceinline__ float biased(const Problem& p, const uint16_t* bg, int64_t b, int64_t bh, int64_t j,
-                                        int64_t key) {
-    const int64_t bi = p.ending ? (bh * p.N + key) * p.N + j : (bh * p.N + j) * p.N + key;
-    const float bv = __uint_as_float(static_cast<uint32_t>(bg[bi]) << 16);
-    return p.mask ? bv + p.mask[b * p.N + key] : bv;
-}
-
 // r_j = max over the call's keys of bias + mask, written as REF_KS partial maxima per query
 // (padding queries and queries whose keys are all masked give -inf).  Starting node: a
 // query's biases are a contiguous row, so one wave walks it with coalesced reads (one
@@ -222,8 +213,28 @@ __global__ void __launch_bounds__(256) bias_ref_kernel(Problem p, float* part, i
         if (j < p.N) {
             const uint16_t* row = bg + (bh * p.N + j) * p.N + p.k0;
             const float* mrow = p.mask ? p.mask + b * p.N + p.k0 : nullptr;
+            int64_t k0 = 0;
+            if ((reinterpret_cast<uintptr_t>(row) & 7) == 0 && (!mrow || (reinterpret_cast<uintptr_t>(mrow) & 15) == 0)) {
+                // aligned row: 4 keys per lane and load, 256 keys per wave step
+                const int64_t n4 = NK / 256 * 256;
+#pragma unroll 4
+                for (int64_t k = 4 * lane; k < n4; k += 256) {
+                    const uint2 w2 = *reinterpret_cast<const uint2*>(row + k);
+                    float x[4] = {__uint_as_float(w2.x << 16), __uint_as_float(w2.x & 0xFFFF0000u),
+                                  __uint_as_float(w2.y << 16), __uint_as_float(w2.y & 0xFFFF0000u)};
+                    if (mrow) {
+                        const float4 m4 = *reinterpret_cast<const float4*>(mrow + k);
+                        x[0] += m4.x;
+                        x[1] += m4.y;
+                        x[2] += m4.z;
+                        x[3] += m4.w;
+                    }
+                    mx = fmaxf(mx, fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+                }
+                k0 = n4;
+            }
 #pragma unroll 8
-            for (int64_t k = lane; k < NK; k += 64) {
+            for (int64_t k = k0 + lane; k < NK; k += 64) {
                 const float bv = __uint_as_float(static_cast<uint32_t>(row[k]) << 16);
                 mx = fmaxf(mx, mrow ? bv + mrow[k] : bv);
             }
@@ -253,15 +264,16 @@ __global__ void __launch_bounds__(256) bias_ref_kernel(Problem p, float* part, i
             fmaxf(fmaxf(red[0][lane], red[1][lane]), fmaxf(red[2][lane], red[3][lane]));
 }
 
-// One workgroup per (64 queries, key block, (b, h)); thread t handles query jj of the 64
-// and the 8 keys of part pt of the block.  Starting node: the 4 threads of a query are
-// neighbours, so a query row's 32 keys are read as 64 contiguous bytes; ending node: a
+// One workgroup per (64 queries, IMG16_NB key blocks, (b, h)); thread t handles query jj of
+// the 64 and the 8 keys of part pt of each block.  Starting node: the 4 threads of a query
+// are neighbours, so a query row's 32 keys are read as 64 contiguous bytes; ending node: a
 // wave holds 64 consecutive queries, which for one key are 128 contiguous bytes.  r_j is
 // the largest of the n_part partial maxima (0 if every key is masked); with several
-// partials the workgroups of key block 0 also store r_j for the epilogue.
+// partials the workgroups of the first blocks also store r_j for the epilogue.
+constexpr int IMG16_NB = 4;
 __global__ void __launch_bounds__(256) bias_image16_kernel(Problem p, const float* part, int n_part, _Float16* img,
                                                            float* ref, int n_jb, int nblk) {
-    const int g = blockIdx.x, n = blockIdx.y;
+    const int g = blockIdx.x, n0 = blockIdx.y * IMG16_NB;
     const int64_t bh = blockIdx.z, b = bh / p.H, BH = gridDim.z;
     const int t = threadIdx.x;
     const int jj = p.ending ? (t & 63) : (t >> 2);
@@ -274,21 +286,97 @@ __global__ void __launch_bounds__(256) bias_image16_kernel(Problem p, const floa
     float r = -INFINITY;
     for (int ks = 0; ks < n_part; ++ks) r = fmaxf(r, part[(ks * BH + bh) * nqp + j]);
     if (!(r > -INFINITY)) r = 0.0f;
-    if (n_part > 1 && n == 0 && pt == 0) ref[bh * nqp + j] = r;
+    if (n_part > 1 && n0 == 0 && pt == 0) ref[bh * nqp + j] = r;
 
-    const KeyBlock kbk = BlockPlan(p.nkeys(), p.T).block(n);
-    const int64_t key0 = p.k0 + kbk.kb;
+    const BlockPlan plan(p.nkeys(), p.T);
     const int jb = static_cast<int>(j / BJ), jl = static_cast<int>(j % BJ);
-    f16x8 x;
+    _Float16* dst = img + (bh * n_jb + jb) * nblk * static_cast<int64_t>(IMG_HALVES) + jl * BK + kv_chunk(jl, pt) * 8;
+    if (!p.ending) {
+        // Starting node: the workgroup's blocks cover the contiguous keys k0 + kbeg .. + span
+        // of 64 query rows.  Wave w copies rows w, w + 4, ... into LDS with each lane taking
+        // keys 2l, 2l + 1 (256 contiguous bytes of a row per step), already relative to r_j,
+        // then every thread gathers its 16-byte parts from LDS.
+        __shared__ _Float16 rowbuf[IMG16_Q][IMG16_NB * BK + 2];
+        __shared__ float rref[IMG16_Q];
+        const int lane = t & 63, wv = t >> 6;
+        if (pt == 0) rref[jj] = r;
+        const KeyBlock first = plan.block(n0);
+        const int nlast = min(n0 + IMG16_NB, nblk) - 1;
+        const KeyBlock last = plan.block(nlast);
+        const int64_t kbeg = first.kb;
+        const int span = static_cast<int>(last.kb + last.nk - kbeg);   // <= IMG16_NB * BK
+        float mk[2];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const int kk = part_key(pt, e);
-        float val = -INFINITY;
-        if (kk < kbk.nk) val = real ? (biased(p, bg, b, bh, j, key0 + kk) - r) * kLog2e : 0.0f;
-        x[e] = static_cast<_Float16>(val);
+        for (int h = 0; h < 2; ++h) {
+            const int kk = 2 * lane + h;
+            mk[h] = (p.mask && kk < span) ? p.mask[b * p.N + p.k0 + kbeg + kk] : 0.0f;
+        }
+        __syncthreads();
+        const int64_t jq0 = static_cast<int64_t>(g) * IMG16_Q;
+        for (int rr = wv; rr < IMG16_Q; rr += 4) {
+            const int64_t jr = jq0 + rr;
+            const uint16_t* rowp = bg + (bh * p.N + (jr < p.N ? jr : 0)) * p.N + p.k0 + kbeg;
+            const float rj = rref[rr];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int kk = 2 * lane + h;
+                float x = 0.0f;
+                if (jr < p.N && kk < span) x = (__uint_as_float(static_cast<uint32_t>(rowp[kk]) << 16) + mk[h] - rj) * kLog2e;
+                if (kk < IMG16_NB * BK) rowbuf[rr][kk] = static_cast<_Float16>(x);
+            }
+        }
+        __syncthreads();
+        for (int u = 0; u < IMG16_NB; ++u) {
+            const int n = n0 + u;
+            if (n >= nblk) break;
+            const KeyBlock kbk = plan.block(n);
+            const int off = static_cast<int>(kbk.kb - kbeg);
+            f16x8 x;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int kk = part_key(pt, e);
+                x[e] = kk < kbk.nk ? rowbuf[jj][off + kk] : static_cast<_Float16>(-INFINITY);
+            }
+            *reinterpret_cast<f16x8*>(dst + static_cast<int64_t>(n) * IMG_HALVES) = x;
+        }
+        return;
     }
-    *reinterpret_cast<f16x8*>(img + ((bh * n_jb + jb) * nblk + n) * static_cast<int64_t>(IMG_HALVES) + jl * BK +
-                              kv_chunk(jl, pt) * 8) = x;
+    // the query's biases at key k0 + k: base[k * kstride] (a row, or a column for the ending node)
+    const int64_t kstride = p.ending ? p.N : 1;
+    const uint16_t* base = bg + (p.ending ? (bh * p.N + p.k0) * p.N + (real ? j : 0) : (bh * p.N + (real ? j : 0)) * p.N + p.k0);
+    const float* mbase = p.mask ? p.mask + b * p.N + p.k0 : nullptr;
+    int64_t koff[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) koff[e] = part_key(pt, e) * kstride;
+    float val[IMG16_NB][8];
+#pragma unroll
+    for (int u = 0; u < IMG16_NB; ++u) {
+        const int n = n0 + u;
+        const KeyBlock kbk = plan.block(n < nblk ? n : nblk - 1);
+        const uint16_t* bp = base + kbk.kb * kstride;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int kk = part_key(pt, e);
+            float x = -INFINITY;
+            if (n < nblk && kk < kbk.nk) {
+                x = 0.0f;
+                if (real) {
+                    x = __uint_as_float(static_cast<uint32_t>(bp[koff[e]]) << 16);
+                    if (mbase) x += mbase[kbk.kb + kk];
+                    x = (x - r) * kLog2e;
+                }
+            }
+            val[u][e] = x;
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < IMG16_NB; ++u) {
+        if (n0 + u >= nblk) break;
+        f16x8 x;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = static_cast<_Float16>(val[u][e]);
+        *reinterpret_cast<f16x8*>(dst + static_cast<int64_t>(n0 + u) * IMG_HALVES) = x;
+    }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -590,10 +678,10 @@ __device__ __forceinline__ void barrier_keep_newest() {
 // Barrier after which every copy issued so far is complete.
 __device__ __forceinline__ void barrier_drain() { asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// Prologue: copies of blocks 0 .. NSTAGE-2 in flight, block 0 complete everywhere.
-__device__ __forceinline__ void key_prologue(const Ctx& cx, int wave, int lane, int nblk) {
-    for (int n = 0; n < NSTAGE - 1 && n < nblk; ++n) stage_block(cx, n, wave, lane);
-    if (nblk >= NSTAGE - 1)
+// Prologue: copies of blocks nb0 .. nb0 + NSTAGE-2 in flight, block nb0 complete everywhere.
+__device__ __forceinline__ void key_prologue(const Ctx& cx, int wave, int lane, int nb0, int nb1) {
+    for (int n = nb0; n < nb0 + NSTAGE - 1 && n < nb1; ++n) stage_block(cx, n, wave, lane);
+    if (nb1 - nb0 >= NSTAGE - 1)
         barrier_keep_newest();
     else
         barrier_drain();
@@ -622,19 +710,19 @@ __device__ __forceinline__ void key_step(const Ctx& cx, const Lane& L, int wave,
         barrier_drain();
 }
 
-// Fast pass: every block with the reference r_j.  Each loop has a single compute path,
-// so the accumulators stay in place across blocks.
+// Fast pass over key blocks nb0 .. nb1-1: every block with the reference r_j.  Each loop
+// has a single compute path, so the accumulators stay in place across blocks.
 __device__ __forceinline__ void key_loop_fast(const Ctx& cx, const Lane& L, int wave, int lane,
-                                              const bf16x8 (&qB)[RW][TW][2], State& s, int nblk) {
-    key_prologue(cx, wave, lane, nblk);
-    for (int n = 0; n < nblk; ++n) key_step<false>(cx, L, wave, lane, qB, s, n, nblk);
+                                              const bf16x8 (&qB)[RW][TW][2], State& s, int nb0, int nb1) {
+    key_prologue(cx, wave, lane, nb0, nb1);
+    for (int n = nb0; n < nb1; ++n) key_step<false>(cx, L, wave, lane, qB, s, n, nb1);
 }
 
 // Exact pass: the running maximum is refreshed on every block.
 __device__ __forceinline__ void key_loop_exact(const Ctx& cx, const Lane& L, int wave, int lane,
-                                               const bf16x8 (&qB)[RW][TW][2], State& s, int nblk) {
-    key_prologue(cx, wave, lane, nblk);
-    for (int n = 0; n < nblk; ++n) key_step<true>(cx, L, wave, lane, qB, s, n, nblk);
+                                               const bf16x8 (&qB)[RW][TW][2], State& s, int nb0, int nb1) {
+    key_prologue(cx, wave, lane, nb0, nb1);
+    for (int n = nb0; n < nb1; ++n) key_step<true>(cx, L, wave, lane, qB, s, n, nb1);
 }
 
 __global__ void __launch_bounds__(NTHR) bf16_mfma_kernel(Problem p, Strides sd, const _Float16* img, const float* ref,
@@ -710,10 +798,22 @@ __global__ void __launch_bounds__(NTHR) bf16_mfma_kernel(Problem p, Strides sd, 
     // does not wait for the copies as well (vmcnt(0); expcnt, lgkmcnt unconstrained)
     __builtin_amdgcn_s_waitcnt(0x0F70);
 
+    // split-key mode (gridDim.y > 1): this workgroup folds key blocks nb0 .. nb1-1 into a
+    // partial state; the launch points out, st_m, st_l at split 0's partials
+    const int split = blockIdx.y, n_split = gridDim.y;
+    const int nb0 = static_cast<int>(static_cast<int64_t>(split) * nblk / n_split);
+    const int nb1 = static_cast<int>(static_cast<int64_t>(split + 1) * nblk / n_split);
+    if (n_split > 1) {
+        const int64_t rows = p.B * p.I * p.N * p.H;
+        p.out += split * rows * D;
+        p.st_m += split * rows;
+        p.st_l += split * rows;
+    }
+
     State s;
     s.reset(0.0f);
     if (tid == 0) g_redo = 0;
-    key_loop_fast(cx, L, wave, lane, qB, s, nblk);
+    key_loop_fast(cx, L, wave, lane, qB, s, nb0, nb1);
 
     // accept the pass only if every normaliser is in range and every accumulator finite
     bool bad = false;
@@ -731,7 +831,7 @@ __global__ void __launch_bounds__(NTHR) bf16_mfma_kernel(Problem p, Strides sd, 
     __syncthreads();
     if (g_redo) {
         s.reset(-INFINITY);
-        key_loop_exact(cx, L, wave, lane, qB, s, nblk);
+        key_loop_exact(cx, L, wave, lane, qB, s, nb0, nb1);
     }
 
     // out = O / l; lanes l and l^32 hold disjoint keys of the same query.  In state mode
@@ -771,12 +871,20 @@ __global__ void __launch_bounds__(NTHR) bf16_mfma_kernel(Problem p, Strides sd, 
 }
 
 // Workspace of the forward: the fp16 image, then the references r_j (fp32, padded to
-// whole column blocks), then for the ending node REF_KS partial maxima per query; each
-// part 256-byte aligned.  The starting node's single partial is r_j itself.
+// whole column blocks), then for the ending node REF_KS partial maxima per query, then in
+// split-key mode the partial states (acc, m, l of every query, per split); each part
+// 256-byte aligned.  The starting node's single partial maximum is r_j itself.
+//
+// Split-key mode: a call whose grid would leave most of the chip idle (attention with
+// pair bias is one line; small N) cuts the key blocks into up to MAX_SPLIT ranges run side
+// by side, each of at least MIN_SPLIT_BLOCKS blocks, and joins them with the merge rule.
+constexpr int MAX_SPLIT = 16;
+constexpr int MIN_SPLIT_BLOCKS = 8;
+constexpr int64_t FILL_WGS = 512;           // two workgroups per compute unit
 struct FwdLayout {
-    int64_t n_jb, nblk, nqp;
-    int n_part;
-    size_t img_bytes, ref_off, part_off, total;
+    int64_t n_jb, nblk, nqp, n_rg, wgs, rows;
+    int n_part, n_split;
+    size_t img_bytes, ref_off, part_off, split_off, total;
 };
 FwdLayout fwd_layout(const Problem& p) {
     FwdLayout L;
@@ -784,11 +892,22 @@ FwdLayout fwd_layout(const Problem& p) {
     L.nqp = L.n_jb * BJ;
     L.nblk = BlockPlan(p.nkeys(), p.T).count();
     L.n_part = p.ending ? REF_KS : 1;
+    L.n_rg = ((p.ending ? p.N : p.I) + R - 1) / R;
+    L.wgs = L.n_jb * L.n_rg * p.B * p.H;
+    L.rows = p.B * p.I * p.N * p.H;
+    L.n_split = 1;
+    if (p.st_m == nullptr && L.wgs < FILL_WGS) {
+        const int64_t want = (FILL_WGS + L.wgs - 1) / L.wgs, most = L.nblk / MIN_SPLIT_BLOCKS;
+        L.n_split = static_cast<int>(min(min(want, most), static_cast<int64_t>(MAX_SPLIT)));
+        if (L.n_split < 2) L.n_split = 1;
+    }
     L.img_bytes = static_cast<size_t>(p.B * p.H * L.n_jb * L.nblk) * IMG_HALVES * 2;
     L.ref_off = (L.img_bytes + 255) / 256 * 256;
     const size_t ref_bytes = static_cast<size_t>(p.B * p.H * L.nqp) * 4;
     L.part_off = L.ref_off + (ref_bytes + 255) / 256 * 256;
-    L.total = p.ending ? L.part_off + ref_bytes * REF_KS : L.ref_off + ref_bytes;
+    L.split_off = p.ending ? L.part_off + (ref_bytes * REF_KS + 255) / 256 * 256 : L.part_off;
+    L.total = L.n_split > 1 ? L.split_off + static_cast<size_t>(L.n_split * L.rows) * (D + 2) * 4
+                            : (p.ending ? L.part_off + ref_bytes * REF_KS : L.ref_off + ref_bytes);
     return L;
 }
 
@@ -816,9 +935,9 @@ hipError_t launch_bias_image(const Problem& p, float* img, hipStream_t stream) {
 
 hipError_t launch_bf16_mfma(const Problem& p, void* workspace, hipStream_t stream) {
     const FwdLayout Ly = fwd_layout(p);
-    const int64_t n_rg = ((p.ending ? p.N : p.I) + R - 1) / R;
+    const int64_t n_rg = Ly.n_rg;
     const Strides sd = strides_of(p);
-    const int64_t total = Ly.n_jb * n_rg * p.B * p.H;
+    const int64_t total = Ly.wgs;
     const int64_t n_qg = Ly.n_jb * (BJ / IMG16_Q);
     // the 32 keys of a block are addressed with 32-bit byte offsets from the block's first key
     if (total > 0x7FFFFFFF || Ly.nblk > 65535 || Ly.nqp / 4 > 0x7FFFFFFF || p.B * p.H > 65535 ||
@@ -833,14 +952,31 @@ hipError_t launch_bf16_mfma(const Problem& p, void* workspace, hipStream_t strea
     hipLaunchKernelGGL(bias_ref_kernel, ref_grid, dim3(256), 0, stream, p, part, Ly.nqp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(bias_image16_kernel, dim3(static_cast<unsigned>(n_qg), static_cast<unsigned>(Ly.nblk), bhs),
+    hipLaunchKernelGGL(bias_image16_kernel,
+                       dim3(static_cast<unsigned>(n_qg), static_cast<unsigned>((Ly.nblk + IMG16_NB - 1) / IMG16_NB), bhs),
                        dim3(256), 0, stream, p, part, Ly.n_part, img, ref, static_cast<int>(Ly.n_jb),
                        static_cast<int>(Ly.nblk));
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(bf16_mfma_kernel, dim3(static_cast<unsigned>(total)), dim3(NTHR), 0, stream, p, sd, img, ref,
-                       static_cast<int>(Ly.n_jb), static_cast<int>(n_rg), static_cast<int>(Ly.nblk),
-                       static_cast<int>(total));
-    return hipGetLastError();
+    if (Ly.n_split == 1) {
+        hipLaunchKernelGGL(bf16_mfma_kernel, dim3(static_cast<unsigned>(total)), dim3(NTHR), 0, stream, p, sd, img, ref,
+                           static_cast<int>(Ly.n_jb), static_cast<int>(n_rg), static_cast<int>(Ly.nblk),
+                           static_cast<int>(total));
+        return hipGetLastError();
+    }
+    // split-key mode: partial states of every split, then one join into out (and lse)
+    float* acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + Ly.split_off);
+    float* sm = acc + Ly.n_split * Ly.rows * D;
+    float* sl = sm + Ly.n_split * Ly.rows;
+    Problem q = p;
+    q.out = acc;
+    q.st_m = sm;
+    q.st_l = sl;
+    q.lse = nullptr;
+    hipLaunchKernelGGL(bf16_mfma_kernel, dim3(static_cast<unsigned>(total), static_cast<unsigned>(Ly.n_split)),
+                       dim3(NTHR), 0, stream, q, sd, img, ref, static_cast<int>(Ly.n_jb), static_cast<int>(n_rg),
+                       static_cast<int>(Ly.nblk), static_cast<int>(total));
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    return launch_state_combine(acc, sm, sl, Ly.n_split, Ly.rows, D, p.out, p.lse, stream);
 }
 
 }  // namespace tri_attn

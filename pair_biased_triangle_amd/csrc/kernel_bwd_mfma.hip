@@ -666,6 +666,7 @@ __device__ __forceinline__ void db_stage(const DbCtx& cx, int64_t i, int slot, i
 
 __device__ __forceinline__ void db_barrier_keep() {
     static_assert(DB_STAGES == 3 || DB_STAGES == 4, "three or four stages");
+    static_assert(DB_COPIES == 5, "vmcnt below: the copies of the DB_STAGES - 2 newest rows stay in flight");
     if constexpr (DB_STAGES == 3) asm volatile("s_waitcnt vmcnt(5)\n\ts_barrier" ::: "memory");
     if constexpr (DB_STAGES == 4) asm volatile("s_waitcnt vmcnt(10)\n\ts_barrier" ::: "memory");
 }

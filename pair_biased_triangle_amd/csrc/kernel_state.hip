@@ -90,6 +90,47 @@ __global__ void __launch_bounds__(ST_THR) state_finalize_kernel(const float* acc
     }
 }
 
+// Join n_split partial states stored split after split (acc [n_split][rows][D], m and l
+// [n_split][rows]) into out = acc / l and lse = m + ln l of the merged state, in one pass:
+// the merge rule applied to all splits at once, m* = max m_s, l = sum e^(m_s - m*) l_s.
+// A workgroup owns CB_Q queries, so that small joins still spread over the chip.
+constexpr int MAX_COMBINE = 16;
+constexpr int CB_Q = 16;
+constexpr int CB_THR = 128;
+__global__ void __launch_bounds__(CB_THR) state_combine_kernel(const float* acc, const float* m, const float* l,
+                                                               int n_split, int64_t rows, int D, float* out,
+                                                               float* lse) {
+    __shared__ float fac[MAX_COMBINE][CB_Q];
+    const int64_t q0 = static_cast<int64_t>(blockIdx.x) * CB_Q;
+    const int nq = static_cast<int>(rows - q0 < CB_Q ? rows - q0 : CB_Q);
+    const int tid = threadIdx.x;
+    if (tid < nq) {
+        const int64_t q = q0 + tid;
+        float mx = -INFINITY;
+        for (int s = 0; s < n_split; ++s)
+            if (l[s * rows + q] > 0.0f) mx = fmaxf(mx, m[s * rows + q]);
+        float lt = 0.0f;
+        for (int s = 0; s < n_split; ++s) {
+            const float ls = l[s * rows + q];
+            const float f = ls > 0.0f ? expf(m[s * rows + q] - mx) : 0.0f;
+            fac[s][tid] = f;
+            lt += f * ls;
+        }
+        const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+        for (int s = 0; s < n_split; ++s) fac[s][tid] *= inv;
+        if (lse) lse[q] = lt > 0.0f ? mx + logf(lt) : -INFINITY;
+    }
+    __syncthreads();
+    const int64_t e0 = q0 * D;
+    const int ne = nq * D;
+    for (int e = tid; e < ne; e += CB_THR) {
+        const int qq = e / D;
+        float x = 0.0f;
+        for (int s = 0; s < n_split; ++s) x = fmaf(fac[s][qq], acc[s * rows * D + e0 + e], x);
+        out[e0 + e] = x;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_state_merge(float* acc, float* m, float* l, const float* acc_t, const float* m_t,
@@ -107,6 +148,15 @@ hipError_t launch_state_finalize(const float* acc, const float* m, const float* 
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(state_finalize_kernel, dim3(static_cast<unsigned>(blocks)), dim3(ST_THR), 0, stream, acc, m,
                        l, out, lse, rows, static_cast<int>(D));
+    return hipGetLastError();
+}
+
+hipError_t launch_state_combine(const float* acc, const float* m, const float* l, int n_split, int64_t rows,
+                                int64_t D, float* out, float* lse, hipStream_t stream) {
+    const int64_t blocks = (rows + CB_Q - 1) / CB_Q;
+    if (blocks > 0x7FFFFFFF || n_split < 1 || n_split > MAX_COMBINE) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(state_combine_kernel, dim3(static_cast<unsigned>(blocks)), dim3(CB_THR), 0, stream, acc, m, l,
+                       n_split, rows, static_cast<int>(D), out, lse);
     return hipGetLastError();
 }
 

@@ -94,6 +94,10 @@ hipError_t launch_state_merge(float* acc, float* m, float* l, const float* acc_t
                               const float* l_t, int64_t rows, int64_t D, hipStream_t stream);
 hipError_t launch_state_finalize(const float* acc, const float* m, const float* l, float* out, float* lse,
                                  int64_t rows, int64_t D, hipStream_t stream);
+// n_split partial states stored one after another ([n_split][rows][D], [n_split][rows])
+// joined into out = acc / l and lse = m + ln l of their merge (n_split <= 16).
+hipError_t launch_state_combine(const float* acc, const float* m, const float* l, int n_split, int64_t rows,
+                                int64_t D, float* out, float* lse, hipStream_t stream);
 
 
 // Start of key tile t when N keys are cut into T near-equal contiguous tiles

@@ -65,6 +65,35 @@ def test_forward_lse(torch_dev, dtype, D):
     compare_lse(lse.cpu().numpy(), ref_lse, TOL[dtype], f"lse {dtype}")
 
 
+@pytest.mark.parametrize("jump", [False, True])
+def test_split_key_mode(torch_dev, jump):
+    """A grid of a few workgroups (8 lines of N = 1024, two heads) runs in split-key mode:
+    the key blocks are cut into ranges folded side by side, whose states the merge rule
+    joins.  With q.k of one key far above the rest, the range holding that key takes the
+    exact pass while the others keep the fast one."""
+    import pair_biased_triangle_amd as P
+    w = small("bf16", I=8, N=1024, H=2, T=3, seed=41, mask_last=70)
+    if jump:
+        q, k = W.bf16_bits_to_f32(w.q), W.bf16_bits_to_f32(w.k)
+        q[0, :, 100:140, 1, :] = 4.0
+        k[0, :, 700, 1, :] = 4.0
+        w.q, w.k = W.f32_to_bf16_bits(q), W.f32_to_bf16_bits(k)
+    # the workspace holds the partial states only in split-key mode
+    blocks = 3 * -(-342 // 32)
+    image_and_refs = 2 * 4 * blocks * 256 * 32 * 2 + 2 * 4 * 256 * 4
+    assert P.workspace_bytes(1, 2, 8, 1024, 32, 3, 1) > image_and_refs
+    say(f"[next] split-key mode, jump={jump}")
+    qd, kd, vd, bias, mask = dev_inputs(torch_dev, w)
+    out, lse = P.tri_attn_fwd_lse(qd, kd, vd, bias, mask, n_key_tiles=3)
+    torch_dev.cuda.synchronize()
+    ref, ref_lse = oracle.tri_attn(w.q, w.k, w.v, w.bias, w.mask, n_key_tiles=3)
+    compare(out.cpu().numpy(), ref, TOL["bf16"], "out, split-key mode")
+    compare_lse(lse.cpu().numpy(), ref_lse, TOL["bf16"], "lse, split-key mode")
+    if jump:
+        np.testing.assert_allclose(out.cpu().numpy()[0, :, 100:140, 1],
+                                   W.bf16_bits_to_f32(w.v)[0, :, 700:701, 1].repeat(40, axis=1), atol=1e-6)
+
+
 def test_lse_of_fully_masked_rows(torch_dev):
     import pair_biased_triangle_amd as P
     for dtype in ("bf16", "fp32"):
