@@ -155,7 +155,7 @@ def other_pass(args, torch, P, W, cfg) -> dict:
         step = lambda: P.tri_attn_fwd_ending(q, k, v, bias, mask, n_key_tiles=T)
         work, unit, peak, bound = fwd_flops, "TFLOP/s", PEAK_BF16_TFLOPS, "mfma"
         metric = "ending-node triangle-attention TFLOP/s (4·B·H·N³·D)"
-        kernels = "bias_image_kernel (transposed bias) + bf16_mfma_kernel"
+        kernels = "bias_ref_kernel + bias_image16_kernel (transposed bias) + bf16_mfma_kernel"
         dtype = cfg.dtype
     elif args.which == "pair_bias":
         shp = (B, N, H, D)
@@ -165,7 +165,7 @@ def other_pass(args, torch, P, W, cfg) -> dict:
         work = 3 * B * N * H * D * s_in + B * H * N * N * s_in + (4 * B * N if mask is not None else 0) + 4 * B * N * H * D
         unit, peak, bound = "GB/s", PEAK_HBM_GBS, "hbm"
         metric = "attention with pair bias GB/s (q, k, v, bias read once, out written once)"
-        kernels = "bias_image_kernel + bf16_mfma_kernel with one row"
+        kernels = "bias_ref_kernel + bias_image16_kernel + bf16_mfma_kernel (one row, split-key) + state_combine_kernel"
         extra["flops_per_call"] = 4.0 * B * H * N * N * D
         dtype = cfg.dtype
     else:   # ring
@@ -173,19 +173,19 @@ def other_pass(args, torch, P, W, cfg) -> dict:
         acc = torch.empty((B, I, N, H, D), dtype=torch.float32, device="cuda")
         m = torch.empty((B, I, N, H), dtype=torch.float32, device="cuda")
         l = torch.empty_like(m)
-        acc_t, m_t, l_t = torch.empty_like(acc), torch.empty_like(m), torch.empty_like(l)
         out = torch.empty_like(acc)
 
         def step():
+            # one ring: the first step's state, every later step folded into it in place
             P.tri_attn_tile_state(q, k, v, bias, mask, key_begin=bounds[0], key_end=bounds[1], acc=acc, m=m, l=l)
             for t in range(1, T):
-                P.tri_attn_tile_state(q, k, v, bias, mask, key_begin=bounds[t], key_end=bounds[t + 1],
-                                      acc=acc_t, m=m_t, l=l_t)
-                P.tri_attn_state_merge(acc, m, l, acc_t, m_t, l_t)
+                P.tri_attn_tile_state_update(q, k, v, bias, mask, key_begin=bounds[t], key_end=bounds[t + 1],
+                                             acc=acc, m=m, l=l)
             P.tri_attn_state_finalize(acc, m, l, out=out)
         work, unit, peak, bound = fwd_flops, "TFLOP/s", PEAK_BF16_TFLOPS, "mfma"
-        metric = f"split-tile ring TFLOP/s ({T} tile states + merges + finalize, 4·B·H·I·N²·D)"
-        kernels = "per tile: bias_image_kernel + bf16_mfma_kernel (state mode); state_merge_kernel; state_finalize_kernel"
+        metric = f"split-tile ring TFLOP/s ({T} ring steps folded into one state + finalize, 4·B·H·I·N²·D)"
+        kernels = ("per step: bias_ref_kernel + bias_image16_kernel + bf16_mfma_kernel (state mode, the later steps "
+                   "merging into the running state); state_finalize_kernel")
         dtype = cfg.dtype
     ms, wall = timed(torch, step, args.steps, args.warmup)
     rate = work / (ms * 1e-3) / (1e12 if unit == "TFLOP/s" else 1e9)

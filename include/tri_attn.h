@@ -191,6 +191,22 @@ int tri_attn_tile_state(const void *q, const void *k, const void *v, const void 
                         int32_t dtype, void *stream);
 
 /*
+ * One ring step folded into a running state: the partial state of the keys
+ * [key_begin, key_end) (as tri_attn_tile_state computes it) merged in place into the
+ * state (acc, m, l) the caller passes, with the rule of tri_attn_state_merge.  The state
+ * must hold a valid partial state, for instance the previous step's, or l = 0 (the
+ * identity: acc and m are then not read).  Same arguments, layouts and errors as
+ * tri_attn_tile_state; acc, m and l are read and written.  Equivalent to
+ * tri_attn_tile_state into a scratch state followed by tri_attn_state_merge, without the
+ * scratch state's round trip through memory.
+ */
+int tri_attn_tile_state_update(const void *q, const void *k, const void *v, const void *bias,
+                               const float *mask, float *acc, float *m, float *l,
+                               int64_t B, int64_t H, int64_t I, int64_t N, int64_t D,
+                               int64_t key_begin, int64_t key_end, int32_t ending,
+                               int32_t dtype, void *stream);
+
+/*
  * The merge of two partial states, in place into the first, for `rows` queries of D
  * values (rows = B * I * N * H for the states above; 1 <= D <= 64):
  *     M = max(m, m_t);  a = exp(m - M), b = exp(m_t - M)

@@ -23,7 +23,8 @@ STATUS = {
     -10: "TRI_ATTN_ERR_RANGE",
 }
 EXPORTS = ("tri_attn_fwd", "tri_attn_fwd_rows", "tri_attn_fwd_rows_ws", "tri_attn_workspace_bytes",
-           "tri_attn_fwd_lse", "tri_attn_fwd_ending", "tri_attn_tile_state", "tri_attn_state_merge",
+           "tri_attn_fwd_lse", "tri_attn_fwd_ending", "tri_attn_tile_state", "tri_attn_tile_state_update",
+           "tri_attn_state_merge",
            "tri_attn_state_finalize", "pair_bias_attn_fwd", "tri_attn_bwd",
            "tri_attn_status_string", "tri_attn_last_hip_error", "tri_attn_version")
 
@@ -58,6 +59,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         L.tri_attn_tile_state.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64,
                                           i32, i32, vp]
         L.tri_attn_tile_state.restype = ctypes.c_int
+        L.tri_attn_tile_state_update.argtypes = L.tri_attn_tile_state.argtypes
+        L.tri_attn_tile_state_update.restype = ctypes.c_int
         L.tri_attn_state_merge.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, vp]
         L.tri_attn_state_merge.restype = ctypes.c_int
         L.tri_attn_state_finalize.argtypes = [vp, vp, vp, vp, vp, i64, i64, vp]
@@ -238,6 +241,21 @@ def tri_attn_tile_state(q, k, v, bias, mask=None, *, key_begin: int, key_end: in
     _check(L.tri_attn_tile_state(_ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(mask), _ptr(acc), _ptr(m), _ptr(l),
                                  B, H, I, N, D, int(key_begin), int(key_end), int(bool(ending)), dt,
                                  _stream_handle(stream)))
+    return acc, m, l
+
+
+def tri_attn_tile_state_update(q, k, v, bias, mask=None, *, key_begin: int, key_end: int, acc, m, l,
+                               ending: bool = False, stream=None):
+    """Fold the keys [key_begin, key_end), as one ring step, into the running state
+    (acc, m, l) in place (l = 0 is the empty state).  Calls tri_attn_tile_state_update."""
+    L = load_library()
+    dt, acc = _validate(q, k, v, bias, mask, acc)
+    B, I, N, H, D = q.shape
+    m = _per_query(acc, (B, I, N, H), "m", m)
+    l = _per_query(acc, (B, I, N, H), "l", l)
+    _check(L.tri_attn_tile_state_update(_ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(mask), _ptr(acc), _ptr(m),
+                                        _ptr(l), B, H, I, N, D, int(key_begin), int(key_end), int(bool(ending)), dt,
+                                        _stream_handle(stream)))
     return acc, m, l
 
 

@@ -844,7 +844,34 @@ __global__ void __launch_bounds__(NTHR) bf16_mfma_kernel(Problem p, Strides sd, 
         for (int ti = 0; ti < TW; ++ti) {
             const float lt = s.lsum[ri][ti] + __shfl_xor(s.lsum[ri][ti], 32);
             const int64_t i = i0 + row0 + ri, j = j0 + (tile0 + ti) * 32 + L.c;
-            if (i < lines && j < p.N) {
+            if (i < lines && j < p.N && state && p.update) {
+                // fold this range's state into the running one (merge rule, natural-log units)
+                const int64_t qo = bh_off + i * sd.line + j * sd.query;
+                float* o = p.out + qo;
+                const float m1 = s.mref[ri][ti] * kLn2 + ref[static_cast<int64_t>(bh) * n_jb * BJ + j];
+                const float m0 = p.st_m[qo / D], l0 = p.st_l[qo / D];
+                if (lt > 0.0f) {
+                    float a0 = 0.0f, a1 = 1.0f, mm = m1;
+                    if (l0 > 0.0f) {
+                        mm = fmaxf(m0, m1);
+                        a0 = expf(m0 - mm);
+                        a1 = expf(m1 - mm);
+                    }
+#pragma unroll
+                    for (int a = 0; a < 4; ++a) {
+                        f32x4* op = reinterpret_cast<f32x4*>(o + 8 * a + 4 * L.h2);
+                        f32x4 x = {};
+                        if (a0 != 0.0f) x = *op;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) x[e] = fmaf(a0, x[e], a1 * s.O[ri][ti][4 * a + e]);
+                        *op = x;
+                    }
+                    if (L.h2 == 0) {
+                        p.st_m[qo / D] = mm;
+                        p.st_l[qo / D] = a0 * l0 + a1 * lt;
+                    }
+                }
+            } else if (i < lines && j < p.N) {
                 const int64_t qo = bh_off + i * sd.line + j * sd.query;
                 float* o = p.out + qo;
                 // correctly rounded O / l: a single surviving key returns its v exactly

@@ -107,7 +107,22 @@ __global__ void __launch_bounds__(GJ) general_kernel(Problem p, Strides st) {
         const int64_t qo = line + j * st.query;   // element offset of this query's D values
         const int64_t so = qo / D;                // offset in the [B, I, N, H] per-query arrays
         float* o = p.out + qo;
-        if (p.st_m) {                             // partial state: unnormalised accumulator
+        if (p.st_m && p.update) {                 // fold into the running state (merge rule)
+            const float m0 = p.st_m[so], l0 = p.st_l[so];
+            if (l > 0.0f) {
+                float a0 = 0.0f, a1 = 1.0f, mm = m;
+                if (l0 > 0.0f) {
+                    mm = fmaxf(m0, m);
+                    a0 = expf(m0 - mm);
+                    a1 = expf(m - mm);
+                }
+#pragma unroll
+                for (int d = 0; d < DP; ++d)
+                    if (d < D) o[d] = a0 == 0.0f ? a1 * acc[d] : fmaf(a0, o[d], a1 * acc[d]);
+                p.st_m[so] = mm;
+                p.st_l[so] = a0 * l0 + a1 * l;
+            }
+        } else if (p.st_m) {                      // partial state: unnormalised accumulator
 #pragma unroll
             for (int d = 0; d < DP; ++d)
                 if (d < D) o[d] = acc[d];

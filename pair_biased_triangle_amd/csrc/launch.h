@@ -30,6 +30,7 @@ struct Problem {
     float* lse = nullptr;   // optional [B, I, N, H]: natural-log normaliser of each query
     float* st_m = nullptr;  // state mode when non-null: reference (natural-log units) ...
     float* st_l = nullptr;  //   ... and normaliser of each query; out gets the accumulator
+    bool update = false;    // state mode: fold into the state already in out, st_m, st_l
     __host__ __device__ int64_t nkeys() const { return NK > 0 ? NK : N; }
 };
 

@@ -68,6 +68,7 @@ struct Call {
     float* lse = nullptr;
     float* st_m = nullptr;
     float* st_l = nullptr;
+    bool update = false;                   // state mode: fold into the given state
     void* ws = nullptr;                    // caller workspace when ws_bytes >= 0
     int64_t ws_bytes = -1;
 };
@@ -106,6 +107,7 @@ tri_attn::Problem make_problem(const Call& c) {
     p.lse = c.lse;
     p.st_m = c.st_m;
     p.st_l = c.st_l;
+    p.update = c.update;
     return p;
 }
 
@@ -271,6 +273,20 @@ int tri_attn_tile_state(const void* q, const void* k, const void* v, const void*
     return run(c, stream);
 }
 
+int tri_attn_tile_state_update(const void* q, const void* k, const void* v, const void* bias, const float* mask,
+                               float* acc, float* m, float* l, int64_t B, int64_t H, int64_t I, int64_t N, int64_t D,
+                               int64_t key_begin, int64_t key_end, int32_t ending, int32_t dtype, void* stream) {
+    if (!m || !l) return TRI_ATTN_ERR_NULL;
+    Call c = make_call(q, k, v, bias, mask, acc, B, H, I, N, D, 1, dtype);
+    c.key_begin = key_begin;
+    c.key_end = key_end < 0 ? 0 : key_end;
+    c.ending = ending != 0;
+    c.st_m = m;
+    c.st_l = l;
+    c.update = true;
+    return run(c, stream);
+}
+
 int tri_attn_state_merge(float* acc, float* m, float* l, const float* acc_t, const float* m_t, const float* l_t,
                          int64_t rows, int64_t D, void* stream) {
     int st = check_state_args(acc, m, l, rows, D);
@@ -374,6 +390,6 @@ const char* tri_attn_status_string(int status) {
 
 int tri_attn_last_hip_error(void) { return g_last_hip_error; }
 
-int tri_attn_version(void) { return 10200; }
+int tri_attn_version(void) { return 10300; }
 
 }  // extern "C"

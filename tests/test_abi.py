@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.tri_attn_version() == 10200
+    assert lib.tri_attn_version() == 10300
     seen = set()
     codes = (OK, E_NULL, E_SHAPE, E_DTYPE, E_UNSUP, E_ALIGN, E_TILES, E_HIP, E_ALIAS, E_WS, E_RANGE)
     for code in codes:
@@ -213,17 +213,23 @@ def test_ending_errors(lib):
     assert f(lse=fake(0x10000000 * 6 + 64)) == E_ALIAS
 
 
-def call_state(lib, kb=0, ke=64, ending=0, m=M_, l=L_, acc=OUT, I=64, **kw):
-    return lib.tri_attn_tile_state(kw.get("q", Q), K, V, BIAS, None, acc, m, l, 1, 4, I, 64, 32, kb, ke, ending,
-                                   kw.get("dtype", BF16), None)
+STATE_ENTRIES = ("tri_attn_tile_state", "tri_attn_tile_state_update")
 
 
+def call_state(lib, kb=0, ke=64, ending=0, m=M_, l=L_, acc=OUT, I=64, entry="tri_attn_tile_state", **kw):
+    return getattr(lib, entry)(kw.get("q", Q), K, V, BIAS, None, acc, m, l, 1, 4, I, 64, 32, kb, ke, ending,
+                               kw.get("dtype", BF16), None)
+
+
+@pytest.mark.parametrize("entry", STATE_ENTRIES)
 @pytest.mark.parametrize("kb,ke", [(-1, 10), (5, 5), (10, 5), (0, 65), (64, 70), (0, -1)])
-def test_tile_state_key_range(lib, kb, ke):
-    assert call_state(lib, kb=kb, ke=ke) == E_RANGE
+def test_tile_state_key_range(lib, kb, ke, entry):
+    assert call_state(lib, kb=kb, ke=ke, entry=entry) == E_RANGE
 
 
-def test_tile_state_errors(lib):
+@pytest.mark.parametrize("entry", STATE_ENTRIES)
+def test_tile_state_errors(lib, entry):
+    call_state = lambda lib, **kw: globals()["call_state"](lib, entry=entry, **kw)
     assert call_state(lib, m=None) == E_NULL
     assert call_state(lib, l=None) == E_NULL
     assert call_state(lib, q=None) == E_NULL

@@ -184,6 +184,31 @@ def test_tile_states_and_ring_merge(torch_dev, dtype, ending):
     compare_lse(lse.cpu().numpy(), ref_lse, TOL[dtype], "merged ring lse")
 
 
+@pytest.mark.parametrize("dtype,ending,N,I", [("bf16", False, 97, 20), ("fp32", False, 97, 20), ("bf16", True, 97, 97),
+                                              ("fp32", True, 97, 97), ("bf16", False, 600, 12)])
+def test_ring_by_state_updates(torch_dev, dtype, ending, N, I):
+    """The ring folded step by step into one running state with tri_attn_tile_state_update,
+    starting from the empty state (l = 0), then finalised: tri_attn_fwd's result."""
+    import pair_biased_triangle_amd as P
+    w = small(dtype, I=I, N=N, T=1, mask_last=4)
+    say(f"[next] ring by state updates {dtype} ending={ending} N={N}")
+    q, k, v, bias, mask = dev_inputs(torch_dev, w)
+    t = torch_dev
+    acc = t.full((1, I, N, 4, 32), 7.0, dtype=t.float32, device="cuda")    # not read while l = 0
+    m = t.full((1, I, N, 4), 3.0, dtype=t.float32, device="cuda")
+    l = t.zeros((1, I, N, 4), dtype=t.float32, device="cuda")
+    bounds = [0, 13, 45, 46, 93, N] if N == 97 else [0, 150, 151, 420, N]
+    order = [2, 4, 0, 3, 1] if N == 97 else [3, 1, 0, 2]
+    for tt in order:
+        P.tri_attn_tile_state_update(q, k, v, bias, mask, key_begin=bounds[tt], key_end=bounds[tt + 1],
+                                     ending=ending, acc=acc, m=m, l=l)
+    out, lse = P.tri_attn_state_finalize(acc, m, l)
+    t.cuda.synchronize()
+    ref, ref_lse = oracle.tri_attn(w.q, w.k, w.v, w.bias, w.mask, ending=ending)
+    compare(out.cpu().numpy(), ref, TOL[dtype], "ring by updates")
+    compare_lse(lse.cpu().numpy(), ref_lse, TOL[dtype], "ring by updates lse")
+
+
 def test_state_merge_and_finalize_kernels(torch_dev):
     """The merge and finalisation kernels on random fp32 states (empty states mixed in)
     against the oracle module's merge rule in fp64 on the same values."""
