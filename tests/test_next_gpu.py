@@ -72,7 +72,8 @@ def test_split_key_mode(torch_dev, jump):
     joins.  With q.k of one key far above the rest, the range holding that key takes the
     exact pass while the others keep the fast one."""
     import pair_biased_triangle_amd as P
-    w = small("bf16", I=8, N=1024, H=2, T=3, seed=41, mask_last=70)
+    w = small("bf16", B=2, I=8, N=1024, H=2, T=3, seed=41, mask_last=70)
+    w.mask[1, :] = -np.inf                           # batch element 1: every key masked (out 0, lse -inf)
     if jump:
         q, k = W.bf16_bits_to_f32(w.q), W.bf16_bits_to_f32(w.k)
         q[0, :, 100:140, 1, :] = 4.0
@@ -80,8 +81,8 @@ def test_split_key_mode(torch_dev, jump):
         w.q, w.k = W.f32_to_bf16_bits(q), W.f32_to_bf16_bits(k)
     # the workspace holds the partial states only in split-key mode
     blocks = 3 * -(-342 // 32)
-    image_and_refs = 2 * 4 * blocks * 256 * 32 * 2 + 2 * 4 * 256 * 4
-    assert P.workspace_bytes(1, 2, 8, 1024, 32, 3, 1) > image_and_refs
+    image_and_refs = 4 * 4 * blocks * 256 * 32 * 2 + 4 * 4 * 256 * 4
+    assert P.workspace_bytes(2, 2, 8, 1024, 32, 3, 1) > image_and_refs
     say(f"[next] split-key mode, jump={jump}")
     qd, kd, vd, bias, mask = dev_inputs(torch_dev, w)
     out, lse = P.tri_attn_fwd_lse(qd, kd, vd, bias, mask, n_key_tiles=3)
@@ -89,6 +90,13 @@ def test_split_key_mode(torch_dev, jump):
     ref, ref_lse = oracle.tri_attn(w.q, w.k, w.v, w.bias, w.mask, n_key_tiles=3)
     compare(out.cpu().numpy(), ref, TOL["bf16"], "out, split-key mode")
     compare_lse(lse.cpu().numpy(), ref_lse, TOL["bf16"], "lse, split-key mode")
+    assert np.all(out.cpu().numpy()[1] == 0) and np.all(np.isneginf(lse.cpu().numpy()[1]))
+    # the caller-workspace entry point runs the same split-key launch
+    ws = torch_dev.empty(P.workspace_bytes(2, 2, 8, 1024, 32, 3, 1), dtype=torch_dev.uint8, device="cuda")
+    a = P.tri_attn_fwd_rows(qd, kd, vd, bias, mask, n_key_tiles=3)
+    b = P.tri_attn_fwd_rows_ws(qd, kd, vd, bias, mask, workspace=ws, n_key_tiles=3)
+    torch_dev.cuda.synchronize()
+    assert torch_dev.equal(a, b) and torch_dev.equal(a, out)
     if jump:
         np.testing.assert_allclose(out.cpu().numpy()[0, :, 100:140, 1],
                                    W.bf16_bits_to_f32(w.v)[0, :, 700:701, 1].repeat(40, axis=1), atol=1e-6)
