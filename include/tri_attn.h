@@ -40,12 +40,15 @@
  * may alias one another; outputs must not overlap any input.  q, k, v, bias and out must be
  * 16-byte aligned, mask 4-byte aligned.  The bf16 matrix-core path (D == 32) first
  * converts the bias into an fp16 image plus one fp32 reference per query, together
- * tri_attn_workspace_bytes() bytes: roughly 2 * B * H * N * N * (1 + 255/N) bytes.
- * tri_attn_fwd and tri_attn_fwd_rows obtain it
+ * tri_attn_workspace_bytes() bytes: roughly 2 * B * H * N * N * (1 + 255/N) bytes, plus,
+ * for calls too small to fill the GPU (fewer than 512 workgroups of 4 rows x 256 columns
+ * and at least 16 key blocks), the partial softmax states of up to 16 key ranges that run
+ * side by side and are then joined (16 * 34 * B * I * N * H bytes at most).  Every entry
+ * point except tri_attn_fwd_rows_ws, and the matrix-core backward, obtains its workspace
  * stream-ordered on `stream` (hipMallocFromPoolAsync / hipFreeAsync) from a memory pool the
  * library creates once per device; the pool keeps freed memory reserved for later calls
  * (up to the largest workspace used) until the process ends.  tri_attn_fwd_rows_ws takes
- * the workspace from the caller instead and allocates nothing.  The other paths need no
+ * the workspace from the caller instead and allocates nothing.  The fp32 paths need no
  * workspace.
  *
  * Streams: calls only enqueue work on `stream` (a hipStream_t; NULL is the null
@@ -172,8 +175,10 @@ int tri_attn_fwd_ending(const void *q, const void *k, const void *v, const void 
  * Figure 2(a)/(c): each ring step's tile is computed on its own and joined by the
  * tiled-softmax merge).  For every query (b, i, j, h) of the orientation chosen by
  * `ending` (0: starting node, rows i in [0, I); 1: ending node, I == N):
- *     m   = a reference in natural-log units (any value; the GPU takes the maximum of
- *           the range's first 32-key block, or the running maximum)
+ *     m   = a reference in natural-log units (any value; the matrix-core path takes the
+ *           query's largest bias + mask over the range, plus the range's exact running
+ *           maximum of the scores where that reference leaves l out of range; the fp32
+ *           path takes the running maximum)
  *     l   = sum_k exp(s_k - m)                          over the key range
  *     acc = sum_k exp(s_k - m) * v_k                    [D] values, unnormalised
  * A query with no finite score in the range gets m = -inf, l = 0, acc = 0 (the
@@ -241,10 +246,14 @@ int tri_attn_state_finalize(const float *acc, const float *m, const float *l,
  *   inputs;  out [B, I, N, H, D] and lse [B, I, N, H]: the forward's results
  *   (tri_attn_fwd_lse);  dout [B, I, N, H, D] binary32;
  *   dq, dk, dv [B, I, N, H, D] and dbias [B, H, N, N]: binary32 results, overwritten.
- * fp32 arithmetic for both dtypes, any D <= 64; deterministic (every sum is taken by one
- * thread in a fixed order, no atomics).  A query with lse = -inf contributes nothing.
- * q, k, v, bias 16-byte aligned, the other pointers 4-byte aligned; no result may
- * overlap an input or another result.  No workspace.  Same error rules as the forward.
+ * bf16 inputs with D == 32 and out, dout, dq, dk, dv 16-byte aligned run on matrix
+ * cores: dout, p and ds are rounded to bf16 as product operands, sums are fp32, and a
+ * workspace (bias images, bf16 dout, per-query statistics) comes from the library pool as
+ * described above.  Every other case computes in fp32, any D <= 64, with no workspace.
+ * Both are deterministic (every sum is taken by one thread in a fixed order, no atomics).
+ * A query with lse = -inf contributes nothing.  q, k, v, bias 16-byte aligned, the other
+ * pointers 4-byte aligned; no result may overlap an input or another result.  Same error
+ * rules as the forward.
  */
 int tri_attn_bwd(const void *q, const void *k, const void *v, const void *bias,
                  const float *mask, const float *out, const float *lse, const float *dout,
