@@ -18,7 +18,8 @@ relates the kernel's live-measured average launch time to the bf16 dense MFMA pe
   ending     tri_attn_fwd_ending (same FLOPs as the forward, bf16 MFMA peak)
   pair_bias  pair_bias_attn_fwd on the workload's first row (I = 1): bound by reading
              the bias -> roofline in GB/s against HBM
-  ring       one tri_attn_tile_state per key tile, tri_attn_state_merge after each, then
+  ring       tri_attn_tile_state on the first key tile, tri_attn_tile_state_update on each
+             later one (the step folded into the running state), then
              tri_attn_state_finalize (the split-tile path), against the bf16 MFMA peak
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME] [--no-cpu]
