@@ -125,36 +125,22 @@ __host__ __device__ constexpr int part_key(int part, int t) {
     return 8 * (2 * (part & 1) + (t >> 2)) + 4 * (part >> 1) + (t & 3);
 }
 
-// Key block n of the tile-ordered sequence: tiles ascending, 32-key blocks inside each.
+// Key block n of the call's key range: keys 32n .. 32n + 31, the last block partial.  The
+// method's T key tiles are folded into the running state in ascending key order, and the
+// merge rule is associative, so folding 32-key blocks in the same order computes the same
+// state: blocks run across tile boundaries and no tile's end pads a block.
 struct KeyBlock {
     int64_t kb;
     int nk;
 };
 struct BlockPlan {
     int64_t N;
-    int T, extra, nb_big, nb_small;
-    int64_t big, small;
     BlockPlan() = default;
-    __host__ __device__ BlockPlan(int64_t n, int t) : N(n), T(t) {
-        small = N / T;
-        big = small + 1;
-        extra = static_cast<int>(N % T);
-        nb_big = static_cast<int>((big + BK - 1) / BK);
-        nb_small = static_cast<int>((small + BK - 1) / BK);
-    }
-    __host__ __device__ int64_t count() const {
-        return static_cast<int64_t>(extra) * nb_big + static_cast<int64_t>(T - extra) * nb_small;
-    }
+    __host__ __device__ explicit BlockPlan(int64_t n) : N(n) {}
+    __host__ __device__ int64_t count() const { return (N + BK - 1) / BK; }
     __host__ __device__ KeyBlock block(int n) const {
-        int64_t t, loc, len;
-        if (n < extra * nb_big) {
-            t = n / nb_big; loc = n % nb_big; len = big;
-        } else {
-            const int n2 = n - extra * nb_big;
-            t = extra + n2 / nb_small; loc = n2 % nb_small; len = small;
-        }
-        const int64_t rest = len - loc * BK;
-        return {tile_start(t, N, T) + loc * BK, static_cast<int>(rest < BK ? rest : BK)};
+        const int64_t kb = static_cast<int64_t>(n) * BK, rest = N - kb;
+        return {kb, static_cast<int>(rest < BK ? rest : BK)};
     }
 };
 
@@ -167,7 +153,7 @@ constexpr int IMG_FLOATS = IMG_BJ * IMG_BK;
 __global__ void __launch_bounds__(IMG_THR) bias_image_kernel(Problem p, float* img, int n_jb, int nblk) {
     const int n = blockIdx.x, jb = blockIdx.y, bh = blockIdx.z;
     const int64_t b = bh / p.H;
-    const KeyBlock kbk = BlockPlan(p.nkeys(), p.T).block(n);
+    const KeyBlock kbk = BlockPlan(p.nkeys()).block(n);
     const int64_t key0 = p.k0 + kbk.kb;        // absolute index of the block's first key
     const uint16_t* bg = static_cast<const uint16_t*>(p.bias);
     float* dst = img + ((static_cast<int64_t>(bh) * n_jb + jb) * nblk + n) * IMG_FLOATS;
@@ -288,7 +274,7 @@ __global__ void __launch_bounds__(256) bias_image16_kernel(Problem p, const floa
     if (!(r > -INFINITY)) r = 0.0f;
     if (n_part > 1 && n0 == 0 && pt == 0) ref[bh * nqp + j] = r;
 
-    const BlockPlan plan(p.nkeys(), p.T);
+    const BlockPlan plan(p.nkeys());
     const int jb = static_cast<int>(j / BJ), jl = static_cast<int>(j % BJ);
     _Float16* dst = img + (bh * n_jb + jb) * nblk * static_cast<int64_t>(IMG_HALVES) + jl * BK + kv_chunk(jl, pt) * 8;
     if (!p.ending) {
@@ -774,7 +760,7 @@ __global__ void __launch_bounds__(NTHR) bf16_mfma_kernel(Problem p, Strides sd, 
         }
         cx.img_wg = img + (static_cast<int64_t>(bh) * n_jb + jb) * nblk * static_cast<int64_t>(IMG_HALVES);
         cx.last_key = static_cast<int>(p.nkeys() - 1);
-        cx.plan = BlockPlan(p.nkeys(), p.T);
+        cx.plan = BlockPlan(p.nkeys());
     }
 
     // Q^T operands (B of S^T = K Q^T): query j = tile*32 + c, d = 16m + 8*h2 .. +7.
@@ -917,7 +903,7 @@ FwdLayout fwd_layout(const Problem& p) {
     FwdLayout L;
     L.n_jb = (p.N + BJ - 1) / BJ;
     L.nqp = L.n_jb * BJ;
-    L.nblk = BlockPlan(p.nkeys(), p.T).count();
+    L.nblk = BlockPlan(p.nkeys()).count();
     L.n_part = p.ending ? REF_KS : 1;
     L.n_rg = ((p.ending ? p.N : p.I) + R - 1) / R;
     L.wgs = L.n_jb * L.n_rg * p.B * p.H;
@@ -944,15 +930,15 @@ size_t bf16_workspace_bytes(const Problem& p) { return fwd_layout(p).total; }
 
 size_t bias_image_bytes(const Problem& p) {
     const int64_t n_jb = (p.N + IMG_BJ - 1) / IMG_BJ;
-    const int64_t nblk = BlockPlan(p.nkeys(), p.T).count();
+    const int64_t nblk = BlockPlan(p.nkeys()).count();
     return static_cast<size_t>(p.B * p.H * n_jb * nblk) * IMG_FLOATS * sizeof(float);
 }
 
-int64_t bias_image_blocks(const Problem& p) { return BlockPlan(p.nkeys(), p.T).count(); }
+int64_t bias_image_blocks(const Problem& p) { return BlockPlan(p.nkeys()).count(); }
 
 hipError_t launch_bias_image(const Problem& p, float* img, hipStream_t stream) {
     const int64_t n_jb = (p.N + IMG_BJ - 1) / IMG_BJ;
-    const int64_t nblk = BlockPlan(p.nkeys(), p.T).count();
+    const int64_t nblk = BlockPlan(p.nkeys()).count();
     if (nblk > 0x7FFFFFFF || n_jb > 65535 || p.B * p.H > 65535) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(bias_image_kernel, dim3(static_cast<unsigned>(nblk), static_cast<unsigned>(n_jb),
                                                static_cast<unsigned>(p.B * p.H)),

@@ -70,7 +70,7 @@ size_t bf16_workspace_bytes(const Problem& p);
 hipError_t launch_bf16_mfma(const Problem& p, void* workspace, hipStream_t stream);
 
 // The fp32 bias image of the backward kernels.  Layout: per (b, h), column block jb of IMG_BJ query columns
-// and key block n (key blocks follow the key tiles, see BlockPlan), one IMG_BJ x IMG_BK
+// and key block n (keys 32n .. 32n + 31 of the call's range), one IMG_BJ x IMG_BK
 // fp32 tile at img + ((b*H + h) * n_jb + jb) * nblk + n) * IMG_BJ * IMG_BK holding
 // (bias + mask) * sqrt(D), -inf past the block's last key; row jj (a query column) has its
 // 16-byte chunk `part` (keys 4*part .. 4*part+3) at position img_chunk(jj, part).

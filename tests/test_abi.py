@@ -132,21 +132,22 @@ def test_out_overlapping_an_input(lib):
 # workspace
 # ---------------------------------------------------------------------------
 def test_workspace_bytes(lib):
-    # bf16 D=32: the fp16 image, B*H*ceil(N/256)*(key blocks)*256*32*2 bytes (key blocks = sum
-    # over tiles of ceil(len/32)), padded to 256 bytes, then one fp32 reference per
+    # bf16 D=32: the fp16 image, B*H*ceil(N/256)*ceil(N/32)*256*32*2 bytes (32-key blocks over
+    # the whole key range, whatever T), padded to 256 bytes, then one fp32 reference per
     # (b, h, query column padded to a multiple of 256)
     def need(B, H, N, blocks):
         img = B * H * -(-N // 256) * blocks * 256 * 32 * 2
         return -(-img // 256) * 256 + B * H * -(-N // 256) * 256 * 4
-    assert lib.tri_attn_workspace_bytes(1, 4, 2700, 2700, 32, 8, BF16) == need(1, 4, 2700, 8 * 11)
-    assert lib.tri_attn_workspace_bytes(1, 4, 1024, 4096, 32, 8, BF16) == need(1, 4, 4096, 8 * 16)
-    assert lib.tri_attn_workspace_bytes(2, 3, 5, 7, 32, 3, BF16) == need(2, 3, 7, 3)
-    assert need(1, 4, 2700, 88) == 4 * 11 * 88 * 16384 + 4 * 11 * 1024
+    assert lib.tri_attn_workspace_bytes(1, 4, 2700, 2700, 32, 8, BF16) == need(1, 4, 2700, 85)
+    assert lib.tri_attn_workspace_bytes(1, 4, 2700, 2700, 32, 200, BF16) == need(1, 4, 2700, 85)
+    assert lib.tri_attn_workspace_bytes(1, 4, 1024, 4096, 32, 8, BF16) == need(1, 4, 4096, 128)
+    assert lib.tri_attn_workspace_bytes(2, 3, 5, 7, 32, 3, BF16) == need(2, 3, 7, 1)
+    assert need(1, 4, 2700, 85) == 4 * 11 * 85 * 16384 + 4 * 11 * 1024
     assert lib.tri_attn_workspace_bytes(1, 4, 64, 64, 32, 1, FP32) == 0
     assert lib.tri_attn_workspace_bytes(1, 4, 64, 64, 16, 1, BF16) == 0
     assert lib.tri_attn_workspace_bytes(1, 4, 64, 64, 32, 0, BF16) == E_TILES
     assert lib.tri_attn_workspace_bytes(1, 4, 65, 64, 32, 1, BF16) == E_SHAPE
-    assert P.workspace_bytes(1, 4, 2700, 2700, 32, 8, 1) == need(1, 4, 2700, 88)
+    assert P.workspace_bytes(1, 4, 2700, 2700, 32, 8, 1) == need(1, 4, 2700, 85)
 
 
 WS = fake(0x70000000)
