@@ -373,6 +373,7 @@ struct Ctx {
     uint32_t kv_lds[KV_PER_WAVE];      // LDS byte offset of the piece inside a stage
     int key_local[KV_PER_WAVE];        // key of this lane's 16-byte slot in the piece
     int part_bytes[KV_PER_WAVE];       // byte offset of the slot's logical 16-byte part inside the key
+    uint32_t lane_off[KV_PER_WAVE];    // key_local * key_bytes + part_bytes: the slot's source offset in a block
     const _Float16* img_wg;            // this workgroup's bias tiles, nblk consecutive BJ x 32 tiles
     int64_t key_bytes;                 // bytes between consecutive keys of a line
     int last_key;                      // index of the last key of the range
@@ -399,21 +400,28 @@ __device__ __forceinline__ uint32_t stage_addr(int n) {
 // 16 bytes into bytes 16 l .. 16 l + 15 of the piece.
 __device__ __forceinline__ void stage_block(const Ctx& cx, int n, int wave, int lane) {
     const KeyBlock kbk = cx.plan.block(n);
-    const int kb = static_cast<int>(kbk.kb);
+    const int lim = cx.last_key - static_cast<int>(kbk.kb);      // last real key of the block, block-relative
     char* lds = reinterpret_cast<char*>(&g_stage[n % NSTAGE]);
+    // Sources are a wave-uniform base (the piece's line at the block's first key) plus a
+    // 32-bit lane offset, so the copies take the scalar-base address form.  The empty asm
+    // statements keep the compiler from folding the loop-invariant lane offsets into
+    // 64-bit vector pointers, which costs 64-bit vector arithmetic per block.
 #pragma unroll
     for (int t = 0; t < KV_PER_WAVE; ++t) {
-        // padded keys read a real key (their bias is -inf); offsets from the block's first key
-        const int rel = min(kb + cx.key_local[t], cx.last_key) - kb;
-        const int off = rel * static_cast<int>(cx.key_bytes) + cx.part_bytes[t];
-        const char* src = cx.kv_row[t] + kbk.kb * cx.key_bytes + off;
-        __builtin_amdgcn_global_load_lds(GLOBAL_PTR(void, src), LDS_PTR(void, lds + cx.kv_lds[t]), 16, 0, 0);
+        uint32_t off = cx.lane_off[t];
+        if (lim < BK - 1)        // the last, partial block: padded keys read the last real key (bias -inf)
+            off = static_cast<uint32_t>(min(cx.key_local[t], lim) * static_cast<int>(cx.key_bytes) + cx.part_bytes[t]);
+        asm volatile("" : "+v"(off));
+        const char* base = cx.kv_row[t] + kbk.kb * cx.key_bytes;
+        __builtin_amdgcn_global_load_lds(GLOBAL_PTR(void, base + off), LDS_PTR(void, lds + cx.kv_lds[t]), 16, 0, 0);
     }
-    const char* src = reinterpret_cast<const char*>(cx.img_wg + static_cast<int64_t>(n) * IMG_HALVES) + lane * 16;
+    const char* tile = reinterpret_cast<const char*>(cx.img_wg + static_cast<int64_t>(n) * IMG_HALVES);
 #pragma unroll
     for (int t = 0; t < BIAS_PER_WAVE; ++t) {
         const int base = (BIAS_PER_WAVE * wave + t) * 1024;
-        __builtin_amdgcn_global_load_lds(GLOBAL_PTR(void, src + base), LDS_PTR(void, lds + B_OFF + base), 16, 0, 0);
+        uint32_t off = static_cast<uint32_t>(lane * 16 + base);
+        asm volatile("" : "+v"(off));
+        __builtin_amdgcn_global_load_lds(GLOBAL_PTR(void, tile + off), LDS_PTR(void, lds + B_OFF + base), 16, 0, 0);
     }
 }
 
@@ -449,7 +457,8 @@ __device__ __forceinline__ Lane lane_layout(int lane, int row0, int tile0) {
 
 // Operands of one staged block.  The reads are inline assembly that waits for its own
 // results (lgkmcnt) before returning: the compiler then sees no LDS read it would have to
-// order against the global->LDS copies still in flight into the other stages.
+// order against the global->LDS copies still in flight into the other stages (ordinary
+// LDS loads get a full vmcnt(0) wait in front of them, which would drain the ring).
 struct VFrags {
     bf16x8 vA[RW][2];
 };
@@ -458,51 +467,44 @@ struct KCFrags {
     u32x4 c16[TW][2];     // bias tile of query tile ti: fp16 registers 8h .. 8h+7 in c16[ti][h]
 };
 
-__device__ __forceinline__ void load_v(uint32_t stage, const Lane& L, VFrags& f) {
+// Both operand sets of a block in one assembly block: sixteen reads and a single wait, so
+// the block pays one LDS round trip instead of two.
+__device__ __forceinline__ void load_vkc(uint32_t stage, const Lane& L, VFrags& fv, KCFrags& fk) {
     u32x2 t[8];
+    u32x4 k[4];
     asm volatile(
-        "ds_read_b64_tr_b16 %0, %8\n\t"
-        "ds_read_b64_tr_b16 %1, %9\n\t"
-        "ds_read_b64_tr_b16 %2, %10\n\t"
-        "ds_read_b64_tr_b16 %3, %11\n\t"
-        "ds_read_b64_tr_b16 %4, %8 offset:2048\n\t"
-        "ds_read_b64_tr_b16 %5, %9 offset:2048\n\t"
-        "ds_read_b64_tr_b16 %6, %10 offset:2048\n\t"
-        "ds_read_b64_tr_b16 %7, %11 offset:2048\n\t"
+        "ds_read_b64_tr_b16 %0, %16\n\t"
+        "ds_read_b64_tr_b16 %1, %17\n\t"
+        "ds_read_b64_tr_b16 %2, %18\n\t"
+        "ds_read_b64_tr_b16 %3, %19\n\t"
+        "ds_read_b64_tr_b16 %4, %16 offset:2048\n\t"
+        "ds_read_b64_tr_b16 %5, %17 offset:2048\n\t"
+        "ds_read_b64_tr_b16 %6, %18 offset:2048\n\t"
+        "ds_read_b64_tr_b16 %7, %19 offset:2048\n\t"
+        "ds_read_b128 %8, %20\n\t"
+        "ds_read_b128 %9, %21\n\t"
+        "ds_read_b128 %10, %20 offset:2048\n\t"
+        "ds_read_b128 %11, %21 offset:2048\n\t"
+        "ds_read_b128 %12, %22\n\t"
+        "ds_read_b128 %13, %23\n\t"
+        "ds_read_b128 %14, %22 offset:2048\n\t"
+        "ds_read_b128 %15, %23 offset:2048\n\t"
         "s_waitcnt lgkmcnt(0)"
-        : "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3]), "=&v"(t[4]), "=&v"(t[5]), "=&v"(t[6]), "=&v"(t[7])
-        : "v"(stage + L.v[0][0]), "v"(stage + L.v[0][1]), "v"(stage + L.v[1][0]), "v"(stage + L.v[1][1]));
-    static_assert(ROW_BYTES == 2048, "line offset in the assembly above");
+        : "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3]), "=&v"(t[4]), "=&v"(t[5]), "=&v"(t[6]), "=&v"(t[7]),
+          "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(fk.c16[0][0]), "=&v"(fk.c16[0][1]),
+          "=&v"(fk.c16[1][0]), "=&v"(fk.c16[1][1])
+        : "v"(stage + L.v[0][0]), "v"(stage + L.v[0][1]), "v"(stage + L.v[1][0]), "v"(stage + L.v[1][1]),
+          "v"(stage + L.k[0]), "v"(stage + L.k[1]), "v"(stage + L.b[0]), "v"(stage + L.b[1]));
+    static_assert(ROW_BYTES == 2048 && TILE_BYTES == 2048, "line and tile offsets in the assembly above");
 #pragma unroll
     for (int ri = 0; ri < RW; ++ri)
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
             const u32x2 lo = t[4 * ri + 2 * m], hi = t[4 * ri + 2 * m + 1];
             const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
-            f.vA[ri][m] = __builtin_bit_cast(bf16x8, w);
+            fv.vA[ri][m] = __builtin_bit_cast(bf16x8, w);
+            fk.kA[ri][m] = __builtin_bit_cast(bf16x8, k[2 * ri + m]);
         }
-}
-
-__device__ __forceinline__ void load_kc(uint32_t stage, const Lane& L, KCFrags& f) {
-    u32x4 k[4];
-    asm volatile(
-        "ds_read_b128 %0, %8\n\t"
-        "ds_read_b128 %1, %9\n\t"
-        "ds_read_b128 %2, %8 offset:2048\n\t"
-        "ds_read_b128 %3, %9 offset:2048\n\t"
-        "ds_read_b128 %4, %10\n\t"
-        "ds_read_b128 %5, %11\n\t"
-        "ds_read_b128 %6, %10 offset:2048\n\t"
-        "ds_read_b128 %7, %11 offset:2048\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(f.c16[0][0]), "=&v"(f.c16[0][1]),
-          "=&v"(f.c16[1][0]), "=&v"(f.c16[1][1])
-        : "v"(stage + L.k[0]), "v"(stage + L.k[1]), "v"(stage + L.b[0]), "v"(stage + L.b[1]));
-    static_assert(TILE_BYTES == 2048, "tile offset in the assembly above");
-#pragma unroll
-    for (int ri = 0; ri < RW; ++ri)
-#pragma unroll
-        for (int m = 0; m < 2; ++m) f.kA[ri][m] = __builtin_bit_cast(bf16x8, k[2 * ri + m]);
 }
 
 // Score register r of query tile ti in log2 units relative to r_j: the image value for
@@ -596,8 +598,11 @@ __device__ __forceinline__ f32x16 s_half(const KCFrags& kc, const bf16x8 (&qB)[R
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(kc.kA[ri][m], qB[ri][ti][m], acc, 0, 0, 0);
 }
 
+// `between` runs after the first unit's score instructions are issued (the block's copies:
+// their address work then overlaps the matrix latency).
+template <typename Between>
 __device__ __forceinline__ void compute_block_pipe(const KCFrags& kc, const VFrags& vf, const bf16x8 (&qB)[RW][TW][2],
-                                                   State& s) {
+                                                   State& s, Between between) {
     static_assert(RW == 2 && TW == 2, "four units per wave");
     const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
     f32x16 S[4];
@@ -605,6 +610,8 @@ __device__ __forceinline__ void compute_block_pipe(const KCFrags& kc, const VFra
     const f32x16 zero = {};
     S[0] = s_half<0>(kc, qB, 0, zero);
     S[0] = s_half<0>(kc, qB, 1, S[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    between();
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -681,15 +688,17 @@ __device__ __forceinline__ void key_step(const Ctx& cx, const Lane& L, int wave,
                                          const bf16x8 (&qB)[RW][TW][2], State& s, int n, int nblk) {
     const uint32_t st = stage_addr(n);
     VFrags vf;
-    load_v(st, L, vf);
-    const bool issue = n + NSTAGE - 1 < nblk;
-    if (issue) stage_block(cx, n + NSTAGE - 1, wave, lane);
     KCFrags kc;
-    load_kc(st, L, kc);
-    if constexpr (!EXACT_MAX)
-        compute_block_pipe(kc, vf, qB, s);
-    else
+    load_vkc(st, L, vf, kc);
+    const bool issue = n + NSTAGE - 1 < nblk;
+    if constexpr (!EXACT_MAX) {
+        compute_block_pipe(kc, vf, qB, s, [&] {
+            if (issue) stage_block(cx, n + NSTAGE - 1, wave, lane);
+        });
+    } else {
+        if (issue) stage_block(cx, n + NSTAGE - 1, wave, lane);
         compute_block_exact(kc, vf, qB, s);
+    }
     if (issue)
         barrier_keep_newest();
     else
@@ -757,6 +766,7 @@ __global__ void __launch_bounds__(NTHR) bf16_mfma_kernel(Problem p, Strides sd, 
             cx.kv_lds[t] = (kv ? V_OFF : K_OFF) + line * ROW_BYTES + half * 1024;
             cx.key_local[t] = 16 * half + (lane >> 2);
             cx.part_bytes[t] = kv_chunk(cx.key_local[t], lane & 3) * 16;   // logical part at this slot
+            cx.lane_off[t] = static_cast<uint32_t>(cx.key_local[t] * cx.key_bytes + cx.part_bytes[t]);
         }
         cx.img_wg = img + (static_cast<int64_t>(bh) * n_jb + jb) * nblk * static_cast<int64_t>(IMG_HALVES);
         cx.last_key = static_cast<int>(p.nkeys() - 1);
