@@ -220,8 +220,8 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              "the multi-GPU sharding is described in DESIGN.md but not built.", file=sys.stderr)
+        print(f"bench.py: the path runs on one GPU (asked for --gpus {args.gpus}); "
+              "sharding across GPUs is not implemented.", file=sys.stderr)
         return 2
 
     import torch
@@ -252,10 +252,19 @@ def main() -> int:
     fn = P.tri_attn_fwd if cfg.I == cfg.N else P.tri_attn_fwd_rows
     step = lambda: fn(q, k, v, bias, mask, n_key_tiles=cfg.n_key_tiles, out=out)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
     stream = torch.cuda.current_stream()          # the stream the kernel is launched on
+    cold_ms = None
+    for u in range(args.warmup):
+        if u == 0:                                 # the first call, caches not yet warm: timed on its own
+            c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            c0.record(stream)
+            step()
+            c1.record(stream)
+            torch.cuda.synchronize()
+            cold_ms = c0.elapsed_time(c1)
+        else:
+            step()
+    torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     ev0.record(stream)
@@ -265,6 +274,17 @@ def main() -> int:
     torch.cuda.synchronize()
     wall_s = time.perf_counter() - t0
     ms_per_step = ev0.elapsed_time(ev1) / args.steps
+
+    # after the timed region: the same number of calls, each between its own pair of events
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a, b in pairs:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    per = sorted(a.elapsed_time(b) for a, b in pairs)
+    per_call = {"calls": len(per), "median_ms": round(per[len(per) // 2], 4), "min_ms": round(per[0], 4),
+                "max_ms": round(per[-1], 4), "cold_first_call_ms": None if cold_ms is None else round(cold_ms, 4)}
 
     flops = cfg.flops
     tflops = flops / (ms_per_step * 1e-3) / 1e12
@@ -302,6 +322,7 @@ def main() -> int:
         "wall_s_timed_region": round(wall_s, 4),
         "roofline": roofline,
         "cpu_baseline": None,
+        "per_call": per_call,
     }
     if not args.no_cpu:
         base, err, n = cpu_baseline(w, out, torch, args.cpu_seconds)
