@@ -73,32 +73,39 @@ __device__ __forceinline__ float neg_lse2(float lse) { return lse == -INFINITY ?
 // bf16, delta = dout . out, and, transposed to [b, i, h, j] so that the row-streaming
 // kernels copy whole rows, delta and nb = -lse log2(e) (the shift of the score in log2
 // units; -inf for a query without any finite score, and for the padded j, whose delta is 0).
+// Eight lanes per query: lane `part` reads elements 4 part .. 4 part + 3 of dout and out,
+// so a wave reads 1 KB of contiguous rows per load; the partial dot products meet in three
+// shuffle steps.  Threads run over (line, query padded to NP, head, part); the padded
+// queries only write the padding of the transposed rows.
+constexpr int PREP_PARTS = D / 4;
 __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdProblem p, __bf16* g16, float* delta, float* nbT,
                                                        float* deltaT, int64_t NP) {
     const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-    const int64_t total = p.B * p.I * p.H * NP;
+    const int64_t total = p.B * p.I * NP * p.H * PREP_PARTS;   // whole groups of 8 lanes
     if (t >= total) return;
-    const int64_t j = t % NP, lh = t / NP, h = lh % p.H, line = lh / p.H;   // line = b * I + i
-    if (j >= p.N) {
-        nbT[t] = -INFINITY;
-        deltaT[t] = 0.0f;
-        return;
-    }
-    const int64_t q = (line * p.N + j) * p.H + h;
-    const f32x4* g = reinterpret_cast<const f32x4*>(p.dout + q * D);
-    const f32x4* o = reinterpret_cast<const f32x4*>(p.out + q * D);
+    const int part = static_cast<int>(t % PREP_PARTS);
+    const int64_t qh = t / PREP_PARTS, h = qh % p.H, lj = qh / p.H, j = lj % NP, line = lj / NP;
+    const bool real = j < p.N;
+    const int64_t q = (line * p.N + (real ? j : 0)) * p.H + h;
     float dl = 0.0f;
+    if (real) {
+        const f32x4 g = *reinterpret_cast<const f32x4*>(p.dout + q * D + 4 * part);
+        const f32x4 o = *reinterpret_cast<const f32x4*>(p.out + q * D + 4 * part);
 #pragma unroll
-    for (int a = 0; a < D / 8; ++a) {
-        const f32x4 g0 = g[2 * a], g1 = g[2 * a + 1], o0 = o[2 * a], o1 = o[2 * a + 1];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dl = fmaf(g0[e], o0[e], fmaf(g1[e], o1[e], dl));
-        const f32x8 gg = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
-        *reinterpret_cast<bf16x8*>(g16 + q * D + 8 * a) = __builtin_convertvector(gg, bf16x8);
+        for (int e = 0; e < 4; ++e) dl = fmaf(g[e], o[e], dl);
+        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+        *reinterpret_cast<bf16x4*>(g16 + q * D + 4 * part) = __builtin_convertvector(g, bf16x4);
     }
-    delta[q] = dl;
-    deltaT[t] = dl;
-    nbT[t] = neg_lse2(p.lse[q]);
+    static_assert(PREP_PARTS == 8, "three shuffle steps");
+    dl += __shfl_xor(dl, 1);
+    dl += __shfl_xor(dl, 2);
+    dl += __shfl_xor(dl, 4);
+    if (part == 0) {
+        const int64_t tt = (line * p.H + h) * NP + j;   // [b, i, h, j]
+        if (real) delta[q] = dl;
+        deltaT[tt] = dl;
+        nbT[tt] = real ? neg_lse2(p.lse[q]) : -INFINITY;
+    }
 }
 
 #define GPTR(p) ((const __attribute__((address_space(1))) void*)(p))
@@ -856,7 +863,7 @@ hipError_t launch_backward_mfma(const BwdProblem& p, void* workspace, hipStream_
     float* delta = reinterpret_cast<float*>(ws + Ly.delta);
     float* nbT = reinterpret_cast<float*>(ws + Ly.nbT);
     float* deltaT = reinterpret_cast<float*>(ws + Ly.deltaT);
-    const int64_t n_prep = p.B * p.I * p.H * Ly.NP;
+    const int64_t n_prep = p.B * p.I * p.H * Ly.NP * PREP_PARTS;
     if (p.D != D || (n_prep + 255) / 256 > 0x7FFFFFFF || (p.N + 63) / 64 > 65535) return hipErrorInvalidConfiguration;
     hipError_t e = launch_bias_image(Ly.fwd, img, stream);
     if (e != hipSuccess) return e;
