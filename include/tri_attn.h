@@ -40,8 +40,9 @@
  * may alias one another; outputs must not overlap any input.  q, k, v, bias and out must be
  * 16-byte aligned, mask 4-byte aligned.  The bf16 matrix-core path (D == 32) first
  * converts the bias into an fp16 image plus one fp32 reference per query, together
- * tri_attn_workspace_bytes() bytes: roughly 2 * B * H * N * N * (1 + 255/N) bytes, plus,
- * for calls too small to fill the GPU (fewer than 512 workgroups of 4 rows x 256 columns
+ * tri_attn_workspace_bytes() bytes: roughly 2 * B * H * N * N bytes (queries padded to a
+ * multiple of 128, keys to a multiple of 32), plus,
+ * for calls too small to fill the GPU (fewer than 512 workgroups of 4 rows x 128 columns
  * and at least 16 key blocks), the partial softmax states of up to 16 key ranges that run
  * side by side and are then joined (16 * 34 * B * I * N * H bytes at most).  Every entry
  * point except tri_attn_fwd_rows_ws, and the matrix-core backward, obtains its workspace

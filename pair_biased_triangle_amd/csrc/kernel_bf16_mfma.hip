@@ -3,23 +3,23 @@
 // Per batch b and head h the rows i are independent attention problems that share one
 // N x N "triangular" bias bias[b,h,j,k] ("Fold-CP", Table 1 "Triangle Attention" and
 // Figure 2(a)).  A workgroup owns R lines (rows i) and BJ query columns j of one (b, h)
-// and streams the key axis in blocks of 32 keys.  Key blocks follow the ring-step tiles
-// (Table 1's caption): they start at every tile start and are cut short at every tile
-// end, so each tile is folded into the running softmax state as one ring step (the
-// running state is the merged state of the tiles seen so far).
+// and streams the call's keys in contiguous blocks of 32 in ascending order.  The ring
+// steps (Table 1's caption, Figure 2) fold the key tiles into the running softmax state
+// with an associative merge, so folding the 32-key blocks in the same order gives the same
+// state: blocks run across tile boundaries and only the last block is partial.
 //
 // Three kernels run per call:
 //   1. bias_ref_kernel, bias_image16_kernel: per query j the reference r_j, the largest
 //      bias + mask over the call's keys, then the fp16 image the main kernel stages
 //      verbatim: per (b, h, column block, key block) a BJ x 32 tile of
-//      (bias + mask - r_j) * log2(e), -inf for keys past the tile end.  Softmax does not
+//      (bias + mask - r_j) * log2(e), -inf for keys past the last one.  Softmax does not
 //      change when every score of a query moves by the same amount, and relative to r_j
 //      every value is <= 0, so fp16 keeps 11 bits where the weights are large and a value
 //      too negative for fp16 becomes -inf, whose weight is 0 anyway.
 //   2. bf16_mfma_kernel: per key block the workgroup copies K and V of its R lines
 //      ([key][d], natural layout) and the bias tile straight from global memory into
 //      LDS (global_load_lds_dwordx4, a ring of stages, no registers on the way).  Each
-//      of the 8 waves owns 2 lines x 2 query tiles of 32 and runs, per (line, tile):
+//      wave owns 2 lines x 2 query tiles of 32 and runs, per (line, tile):
 //        S^T = K Q^T           two v_mfma_f32_32x32x16_bf16
 //        x   = S * log2(e)/sqrt(D) + c      one v_fma_mix_f32 per score: c is the fp16
 //                              image value, taken from its half register as it is
@@ -39,9 +39,13 @@
 // (log2 units) refreshed on every block.  The natural log of the normaliser adds the
 // reference back: lse = r_j + m ln 2 + ln l (m = 0 in the fast pass).
 //
-// Workgroup ids are remapped so that each XCD walks a contiguous range of (b, h, line
-// group, column block) tiles: the workgroups an XCD runs together share each line
-// group's K/V stream and each bias tile in its L2.
+// Shape: 4 waves own 4 lines x 128 query columns, with a ring of 3 stages of 24 KB, so
+// two workgroups (72 KB of LDS each) share a compute unit.  Each waits only at its own
+// barrier, so one workgroup's burst of operand reads after its barrier overlaps the
+// other's arithmetic (with 8 waves and one workgroup per unit, every wave waits on the
+// same burst).  Workgroup ids are remapped so that each XCD walks a contiguous range of
+// (b, h, line group, column block) tiles: the workgroups an XCD runs together share each
+// line group's K/V stream and each bias tile in its L2.
 #include "launch.h"
 
 #include <cmath>
@@ -70,23 +74,26 @@ constexpr int BK = 32;                      // keys per block
 #define TRI_ATTN_ROWS 4
 #endif
 constexpr int R = TRI_ATTN_ROWS;            // lines per workgroup
-constexpr int NWAVE = 8;
+#ifndef TRI_ATTN_WAVES
+#define TRI_ATTN_WAVES 4
+#endif
+constexpr int NWAVE = TRI_ATTN_WAVES;       // waves per workgroup
 constexpr int NTHR = 64 * NWAVE;
 constexpr int RW = 2;                       // lines per wave
 constexpr int TW = 2;                       // query tiles per wave
 constexpr int QT = NWAVE * RW * TW / R;     // 32-wide query tiles per workgroup
 constexpr int BJ = 32 * QT;                 // query columns per workgroup
 constexpr int NXCD = 8;
-static_assert(R == 4 || R == 8, "4 lines x 256 columns or 8 lines x 128 columns");
+static_assert(R == 4 || R == 8, "4 or 8 lines per workgroup");
 static_assert((R / RW) * (QT / TW) == NWAVE, "every wave owns RW x TW units");
 #ifndef TRI_ATTN_STAGES
-#define TRI_ATTN_STAGES 4
+#define TRI_ATTN_STAGES 3
 #endif
 #ifndef TRI_ATTN_TILE_RG
 #define TRI_ATTN_TILE_RG (32 / TRI_ATTN_ROWS)
 #endif
 #ifndef TRI_ATTN_TILE_JB
-#define TRI_ATTN_TILE_JB (TRI_ATTN_ROWS)
+#define TRI_ATTN_TILE_JB 8
 #endif
 constexpr int NSTAGE = TRI_ATTN_STAGES;     // key blocks in flight (LDS ring of stages)
 constexpr int TILE_RG = TRI_ATTN_TILE_RG;   // line groups x column blocks that one XCD
@@ -662,11 +669,8 @@ static_assert(NSTAGE == 3 || NSTAGE == 4, "ring of three or four stages");
 // blocks are complete (those are needed later, the one before them next).
 __device__ __forceinline__ void barrier_keep_newest() {
     constexpr int keep = COPIES_PER_BLOCK * (NSTAGE - 2);
-    static_assert(keep == 4 || keep == 5 || keep == 8 || keep == 10, "vmcnt for this ring");
-    if constexpr (keep == 4) asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
-    if constexpr (keep == 5) asm volatile("s_waitcnt vmcnt(5)\n\ts_barrier" ::: "memory");
-    if constexpr (keep == 8) asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
-    if constexpr (keep == 10) asm volatile("s_waitcnt vmcnt(10)\n\ts_barrier" ::: "memory");
+    static_assert(keep >= 1 && keep <= 63, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%c0)\n\ts_barrier" ::"i"(keep) : "memory");
 }
 // Barrier after which every copy issued so far is complete.
 __device__ __forceinline__ void barrier_drain() { asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory"); }
@@ -720,7 +724,7 @@ __device__ __forceinline__ void key_loop_exact(const Ctx& cx, const Lane& L, int
     for (int n = nb0; n < nb1; ++n) key_step<true>(cx, L, wave, lane, qB, s, n, nb1);
 }
 
-__global__ void __launch_bounds__(NTHR) bf16_mfma_kernel(Problem p, Strides sd, const _Float16* img, const float* ref,
+__global__ void __launch_bounds__(NTHR, 2) bf16_mfma_kernel(Problem p, Strides sd, const _Float16* img, const float* ref,
                                                          int n_jb, int n_rg, int nblk, int total) {
     // XCD-aware remap: XCD x (= hardware id mod 8) walks a contiguous range of logical ids.
     const int w = blockIdx.x;

@@ -132,17 +132,17 @@ def test_out_overlapping_an_input(lib):
 # workspace
 # ---------------------------------------------------------------------------
 def test_workspace_bytes(lib):
-    # bf16 D=32: the fp16 image, B*H*ceil(N/256)*ceil(N/32)*256*32*2 bytes (32-key blocks over
-    # the whole key range, whatever T), padded to 256 bytes, then one fp32 reference per
-    # (b, h, query column padded to a multiple of 256)
+    # bf16 D=32: the fp16 image, B*H*ceil(N/128)*ceil(N/32)*128*32*2 bytes (128-column
+    # blocks; 32-key blocks over the whole key range, whatever T), padded to 256 bytes, then
+    # one fp32 reference per (b, h, query column padded to a multiple of 128)
     def need(B, H, N, blocks):
-        img = B * H * -(-N // 256) * blocks * 256 * 32 * 2
-        return -(-img // 256) * 256 + B * H * -(-N // 256) * 256 * 4
+        img = B * H * -(-N // 128) * blocks * 128 * 32 * 2
+        return -(-img // 256) * 256 + B * H * -(-N // 128) * 128 * 4
     assert lib.tri_attn_workspace_bytes(1, 4, 2700, 2700, 32, 8, BF16) == need(1, 4, 2700, 85)
     assert lib.tri_attn_workspace_bytes(1, 4, 2700, 2700, 32, 200, BF16) == need(1, 4, 2700, 85)
     assert lib.tri_attn_workspace_bytes(1, 4, 1024, 4096, 32, 8, BF16) == need(1, 4, 4096, 128)
     assert lib.tri_attn_workspace_bytes(2, 3, 5, 7, 32, 3, BF16) == need(2, 3, 7, 1)
-    assert need(1, 4, 2700, 85) == 4 * 11 * 85 * 16384 + 4 * 11 * 1024
+    assert need(1, 4, 2700, 85) == 4 * 22 * 85 * 8192 + 4 * 22 * 512
     assert lib.tri_attn_workspace_bytes(1, 4, 64, 64, 32, 1, FP32) == 0
     assert lib.tri_attn_workspace_bytes(1, 4, 64, 64, 16, 1, BF16) == 0
     assert lib.tri_attn_workspace_bytes(1, 4, 64, 64, 32, 0, BF16) == E_TILES
