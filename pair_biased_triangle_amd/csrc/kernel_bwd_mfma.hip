@@ -6,11 +6,11 @@
 //   bwd_prep_kernel   dout -> bf16 copy (the operand of the dP and dV products),
 //                     delta = dout . out per query, and delta and nb = -lse log2(e)
 //                     transposed to [b, i, h, j] (rows padded to whole 128-query tiles).
-//   bwd_dq_lds        4 lines x 128 queries per workgroup, 32-key blocks streamed through
+//   bwd_dq_lds        2 lines x 128 queries per workgroup, 32-key blocks streamed through
 //                     an LDS ring (the forward's shape):
 //                       S^T = K Q^T + C,  dP^T = V dO^T,  dS^T = P^T (dP^T - delta),
 //                       dQ^T += K^T dS^T
-//   bwd_dkdv_lds      4 lines x 128 keys per workgroup, 32-query blocks streamed, in the
+//   bwd_dkdv_lds      2 lines x 128 keys per workgroup, 32-query blocks streamed, in the
 //                     orientation in which P and dS leave the accumulator as B operands:
 //                       S = Q K^T + C,  dP = dO V^T,  dV^T += dO^T P,  dK^T += Q^T dS
 //   bwd_dbias_lds     128 queries x 128 keys of one (b, h) per workgroup, rows i streamed:
@@ -113,21 +113,27 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdProblem p, __bf16* g16
 __device__ __forceinline__ void db_barrier_drain() { asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // ---------------------------------------------------------------------------------------
-// dq, in the forward's shape: a workgroup of 8 waves owns DQ_R = 4 lines (rows i) x 128
-// query columns of one (b, h) and streams 32-key blocks through a ring of LDS stages (K,
+// dq, in the forward's shape: a workgroup of 4 waves owns DQ_R = 2 lines (rows i) x 128
+// query columns of one (b, h) and streams 32-key blocks through a ring of 3 LDS stages (K,
 // V of its lines and the 128 x 32 tile of the fp32 bias image, copied by
-// global_load_lds).  Wave w owns line w / 2 and query tiles 2 (w % 2), +1; Q and dO of its
-// queries stay in registers.  Per unit and block:
+// global_load_lds); two workgroups share a compute unit.  Wave w owns line w / 2 and query
+// tiles 2 (w % 2), +1; Q and dO of its queries stay in registers.  Per unit and block:
 //   S^T = K Q^T + C,  dP^T = V dO^T,  dS^T = P^T (dP^T - delta),  dQ^T += K^T dS^T
 // with K^T read transposed from the staged [key][d] tile (ds_read_b64_tr_b16).
-constexpr int DQ_R = 4;
-constexpr int DQ_WAVES = 8;
-constexpr int DQ_THR = 64 * DQ_WAVES;
-#ifndef TRI_ATTN_DQ_STAGES
-#define TRI_ATTN_DQ_STAGES 4
+#ifndef TRI_ATTN_DQ_WAVES
+#define TRI_ATTN_DQ_WAVES 4
 #endif
+#ifndef TRI_ATTN_DQ_STAGES
+#define TRI_ATTN_DQ_STAGES 3
+#endif
+#ifndef TRI_ATTN_DQ_TILE_RG
+#define TRI_ATTN_DQ_TILE_RG 16
+#endif
+constexpr int DQ_WAVES = TRI_ATTN_DQ_WAVES;
+constexpr int DQ_R = DQ_WAVES / 2;          // lines per workgroup: two waves per line
+constexpr int DQ_THR = 64 * DQ_WAVES;
 constexpr int DQ_STAGES = TRI_ATTN_DQ_STAGES;
-constexpr int DQ_TILE_RG = 8;               // line groups x column blocks one XCD works on together
+constexpr int DQ_TILE_RG = TRI_ATTN_DQ_TILE_RG;   // line groups x column blocks one XCD works on together
 constexpr int DQ_TILE_JB = 4;
 struct DqStage {
     __bf16 k[DQ_R][32][D];     // 64-byte rows, 16-byte chunks swizzled by kv_chunk()
@@ -140,8 +146,11 @@ constexpr int DQ_V_OFF = static_cast<int>(offsetof(DqStage, v));
 constexpr int DQ_B_OFF = static_cast<int>(offsetof(DqStage, bias));
 constexpr int DQ_LINE_BYTES = 32 * D * 2;
 constexpr int DQ_CTILE_BYTES = 32 * IMG_BK * 4;
-static_assert(DQ_LINE_BYTES == 2048 && DQ_CTILE_BYTES == 4096 && DQ_V_OFF - DQ_K_OFF == 8192, "offsets below");
-static_assert(DQ_R * 2 * 2 == 2 * DQ_WAVES && IMG_BJ * IMG_BK * 4 == 2 * DQ_WAVES * 1024, "two K/V, two bias pieces per wave");
+constexpr int DQ_BIAS_PER_WAVE = IMG_BJ * IMG_BK * 4 / 1024 / DQ_WAVES;
+constexpr int DQ_COPIES = 2 + DQ_BIAS_PER_WAVE;   // global_load_lds per wave per block
+static_assert(DQ_LINE_BYTES == 2048 && DQ_CTILE_BYTES == 4096, "offsets below");
+static_assert(DQ_R * 2 * 2 == 2 * DQ_WAVES && DQ_BIAS_PER_WAVE * DQ_WAVES * 1024 == IMG_BJ * IMG_BK * 4,
+              "two K/V pieces and whole bias pieces per wave");
 __shared__ DqStage g_dq[DQ_STAGES];
 
 struct DqCtx {
@@ -165,19 +174,20 @@ __device__ __forceinline__ void dq_stage(const DqCtx& cx, int n, int wave, int l
     }
     const char* src = reinterpret_cast<const char*>(cx.img_wg + static_cast<int64_t>(n) * IMG_BJ * IMG_BK) + lane * 16;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        const int base = (2 * wave + t) * 1024;
+    for (int t = 0; t < DQ_BIAS_PER_WAVE; ++t) {
+        const int base = (DQ_BIAS_PER_WAVE * wave + t) * 1024;
         __builtin_amdgcn_global_load_lds(GPTR(src + base), LPTR(lds + DQ_B_OFF + base), 16, 0, 0);
     }
 }
 
+// barrier after which every wave's copies except those of the DQ_STAGES - 2 newest blocks are complete
 __device__ __forceinline__ void dq_barrier_keep() {
-    static_assert(DQ_STAGES == 3 || DQ_STAGES == 4, "three or four stages");
-    if constexpr (DQ_STAGES == 3) asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
-    if constexpr (DQ_STAGES == 4) asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+    constexpr int keep = DQ_COPIES * (DQ_STAGES - 2);
+    static_assert(keep >= 1 && keep <= 63, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%c0)\n\ts_barrier" ::"i"(keep) : "memory");
 }
 
-__global__ void __launch_bounds__(DQ_THR) bwd_dq_lds(BwdProblem p, const float* img, const __bf16* g16,
+__global__ void __launch_bounds__(DQ_THR, 2) bwd_dq_lds(BwdProblem p, const float* img, const __bf16* g16,
                                                      const float* delta, int n_jb, int n_rg, int nblk, int total) {
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -275,8 +285,8 @@ __global__ void __launch_bounds__(DQ_THR) bwd_dq_lds(BwdProblem p, const float* 
         asm volatile(
             "ds_read_b128 %0, %16\n\t"
             "ds_read_b128 %1, %17\n\t"
-            "ds_read_b128 %2, %16 offset:8192\n\t"
-            "ds_read_b128 %3, %17 offset:8192\n\t"
+            "ds_read_b128 %2, %16 offset:%c26\n\t"
+            "ds_read_b128 %3, %17 offset:%c26\n\t"
             "ds_read_b64_tr_b16 %4, %18\n\t"
             "ds_read_b64_tr_b16 %5, %19\n\t"
             "ds_read_b64_tr_b16 %6, %20\n\t"
@@ -294,7 +304,7 @@ __global__ void __launch_bounds__(DQ_THR) bwd_dq_lds(BwdProblem p, const float* 
               "=&v"(tt[3]), "=&v"(cc[0]), "=&v"(cc[1]), "=&v"(cc[2]), "=&v"(cc[3]), "=&v"(cc[4]), "=&v"(cc[5]),
               "=&v"(cc[6]), "=&v"(cc[7])
             : "v"(st + ak[0]), "v"(st + ak[1]), "v"(st + at[0]), "v"(st + at[1]), "v"(st + at[2]), "v"(st + at[3]),
-              "v"(st + ac[0]), "v"(st + ac[1]), "v"(st + ac[2]), "v"(st + ac[3]));
+              "v"(st + ac[0]), "v"(st + ac[1]), "v"(st + ac[2]), "v"(st + ac[3]), "i"(DQ_V_OFF - DQ_K_OFF));
         bf16x8 kT[2];
 #pragma unroll
         for (int m = 0; m < 2; ++m)
@@ -340,8 +350,8 @@ __global__ void __launch_bounds__(DQ_THR) bwd_dq_lds(BwdProblem p, const float* 
 }
 
 // ---------------------------------------------------------------------------------------
-// dk, dv: a workgroup of 8 waves owns DK_R = 4 lines x 128 keys of one (b, h) and streams
-// 32-query blocks through a ring of LDS stages: Q and dO of its lines, the 128 x 32 tile
+// dk, dv: a workgroup of 4 waves owns DK_R = 2 lines x 128 keys of one (b, h) and streams
+// 32-query blocks through a ring of 3 LDS stages (two workgroups per compute unit): Q and dO of its lines, the 128 x 32 tile
 // of imgT and nb = -lse log2(e), delta of the block's queries.  imgT is the bias image of
 // the transposed bias without the mask (built in the ending orientation): row kk of a tile
 // holds bias[b, h, q, key] sqrt(D) for 32 consecutive queries q (-inf past the last
@@ -351,14 +361,20 @@ __global__ void __launch_bounds__(DQ_THR) bwd_dq_lds(BwdProblem p, const float* 
 //   S = Q K^T + C,  dP = dO V^T,  dS = P (dP - delta),  dV^T += dO^T P,  dK^T += Q^T dS
 // with Q^T, dO^T read transposed from the staged [query][d] tiles.  A dropped key
 // (masked, or past the end) gets zero gradients.
-constexpr int DK_R = 4;
-constexpr int DK_WAVES = 8;
-constexpr int DK_THR = 64 * DK_WAVES;
-#ifndef TRI_ATTN_DK_STAGES
-#define TRI_ATTN_DK_STAGES 4
+#ifndef TRI_ATTN_DK_WAVES
+#define TRI_ATTN_DK_WAVES 4
 #endif
+#ifndef TRI_ATTN_DK_STAGES
+#define TRI_ATTN_DK_STAGES 3
+#endif
+#ifndef TRI_ATTN_DK_TILE_RG
+#define TRI_ATTN_DK_TILE_RG 16
+#endif
+constexpr int DK_WAVES = TRI_ATTN_DK_WAVES;
+constexpr int DK_R = DK_WAVES / 2;          // lines per workgroup: two waves per line
+constexpr int DK_THR = 64 * DK_WAVES;
 constexpr int DK_STAGES = TRI_ATTN_DK_STAGES;
-constexpr int DK_TILE_RG = 8;
+constexpr int DK_TILE_RG = TRI_ATTN_DK_TILE_RG;
 constexpr int DK_TILE_KB = 4;
 struct DkStage {
     __bf16 q[DK_R][32][D];        // 64-byte rows, 16-byte chunks swizzled by kv_chunk()
@@ -372,13 +388,18 @@ constexpr int DK_Q_OFF = static_cast<int>(offsetof(DkStage, q));
 constexpr int DK_G_OFF = static_cast<int>(offsetof(DkStage, g));
 constexpr int DK_B_OFF = static_cast<int>(offsetof(DkStage, bias));
 constexpr int DK_N_OFF = static_cast<int>(offsetof(DkStage, nb));
-static_assert(DK_G_OFF - DK_Q_OFF == 8192 && offsetof(DkStage, dl) - offsetof(DkStage, nb) == 512, "offsets below");
+constexpr int DK_GQ = DK_G_OFF - DK_Q_OFF;                                     // dO tile after the Q tile
+constexpr int DK_DN = static_cast<int>(offsetof(DkStage, dl) - offsetof(DkStage, nb));   // delta rows after nb rows
+constexpr int DK_BIAS_PER_WAVE = IMG_BJ * IMG_BK * 4 / 1024 / DK_WAVES;
+constexpr int DK_COPIES = 2 + DK_BIAS_PER_WAVE + 1;   // Q/dO pieces, bias pieces, the nb or delta piece
+static_assert(DK_BIAS_PER_WAVE * DK_WAVES * 1024 == IMG_BJ * IMG_BK * 4 && 2 * DK_R == DK_WAVES, "pieces per wave");
 __shared__ DkStage g_dk[DK_STAGES];
 
+// barrier after which every wave's copies except those of the DK_STAGES - 2 newest blocks are complete
 __device__ __forceinline__ void dk_barrier_keep() {
-    static_assert(DK_STAGES == 3 || DK_STAGES == 4, "three or four stages");
-    if constexpr (DK_STAGES == 3) asm volatile("s_waitcnt vmcnt(5)\n\ts_barrier" ::: "memory");
-    if constexpr (DK_STAGES == 4) asm volatile("s_waitcnt vmcnt(10)\n\ts_barrier" ::: "memory");
+    constexpr int keep = DK_COPIES * (DK_STAGES - 2);
+    static_assert(keep >= 1 && keep <= 63, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%c0)\n\ts_barrier" ::"i"(keep) : "memory");
 }
 
 struct DkCtx {
@@ -404,14 +425,14 @@ __device__ __forceinline__ void dk_stage(const DkCtx& cx, int n, int wave, int l
     }
     const char* src = reinterpret_cast<const char*>(cx.img_wg + static_cast<int64_t>(n) * IMG_BJ * IMG_BK) + lane * 16;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        const int base = (2 * wave + t) * 1024;
+    for (int t = 0; t < DK_BIAS_PER_WAVE; ++t) {
+        const int base = (DK_BIAS_PER_WAVE * wave + t) * 1024;
         __builtin_amdgcn_global_load_lds(GPTR(src + base), LPTR(lds + DK_B_OFF + base), 16, 0, 0);
     }
     if (lane < 8) __builtin_amdgcn_global_load_lds(GPTR(cx.ls_src + qb * 4), LPTR(lds + cx.ls_dst), 16, 0, 0);
 }
 
-__global__ void __launch_bounds__(DK_THR) bwd_dkdv_lds(BwdProblem p, const float* imgT, const __bf16* g16,
+__global__ void __launch_bounds__(DK_THR, 2) bwd_dkdv_lds(BwdProblem p, const float* imgT, const __bf16* g16,
                                                        const float* nbT, const float* deltaT, int n_kb, int n_rg,
                                                        int nqblk, int64_t NP, int total) {
     const int tid = threadIdx.x;
@@ -450,10 +471,10 @@ __global__ void __launch_bounds__(DK_THR) bwd_dkdv_lds(BwdProblem p, const float
             cx.part_bytes[t] = kv_chunk(cx.q_local[t], lane & 3) * 16;
         }
         cx.img_wg = imgT + (static_cast<int64_t>(bh) * n_kb + kb) * nqblk * static_cast<int64_t>(IMG_BJ * IMG_BK);
-        // nb of line w (w < 4) or delta of line w - 4, 32 floats of the block in lanes 0 .. 7
-        int64_t il = i0 + (wave & 3);
+        // nb of line w (w < DK_R) or delta of line w - DK_R, 32 floats of the block in lanes 0 .. 7
+        int64_t il = i0 + wave % DK_R;
         il = il < I ? il : I - 1;
-        cx.ls_src = reinterpret_cast<const char*>((wave < 4 ? nbT : deltaT) + ((b * I + il) * H + h) * NP + 4 * (lane & 7));
+        cx.ls_src = reinterpret_cast<const char*>((wave < DK_R ? nbT : deltaT) + ((b * I + il) * H + h) * NP + 4 * (lane & 7));
         cx.ls_dst = DK_N_OFF + 128 * wave;
         cx.last_q = static_cast<int>(N - 1);
     }
@@ -510,30 +531,30 @@ __global__ void __launch_bounds__(DK_THR) bwd_dkdv_lds(BwdProblem p, const float
         asm volatile(
             "ds_read_b128 %0, %20\n\t"
             "ds_read_b128 %1, %21\n\t"
-            "ds_read_b128 %2, %20 offset:8192\n\t"
-            "ds_read_b128 %3, %21 offset:8192\n\t"
+            "ds_read_b128 %2, %20 offset:%c27\n\t"
+            "ds_read_b128 %3, %21 offset:%c27\n\t"
             "ds_read_b64_tr_b16 %4, %22\n\t"
             "ds_read_b64_tr_b16 %5, %23\n\t"
             "ds_read_b64_tr_b16 %6, %24\n\t"
             "ds_read_b64_tr_b16 %7, %25\n\t"
-            "ds_read_b64_tr_b16 %8, %22 offset:8192\n\t"
-            "ds_read_b64_tr_b16 %9, %23 offset:8192\n\t"
-            "ds_read_b64_tr_b16 %10, %24 offset:8192\n\t"
-            "ds_read_b64_tr_b16 %11, %25 offset:8192\n\t"
+            "ds_read_b64_tr_b16 %8, %22 offset:%c27\n\t"
+            "ds_read_b64_tr_b16 %9, %23 offset:%c27\n\t"
+            "ds_read_b64_tr_b16 %10, %24 offset:%c27\n\t"
+            "ds_read_b64_tr_b16 %11, %25 offset:%c27\n\t"
             "ds_read_b128 %12, %26\n\t"
             "ds_read_b128 %13, %26 offset:32\n\t"
             "ds_read_b128 %14, %26 offset:64\n\t"
             "ds_read_b128 %15, %26 offset:96\n\t"
-            "ds_read_b128 %16, %26 offset:512\n\t"
-            "ds_read_b128 %17, %26 offset:544\n\t"
-            "ds_read_b128 %18, %26 offset:576\n\t"
-            "ds_read_b128 %19, %26 offset:608\n\t"
+            "ds_read_b128 %16, %26 offset:%c28\n\t"
+            "ds_read_b128 %17, %26 offset:%c29\n\t"
+            "ds_read_b128 %18, %26 offset:%c30\n\t"
+            "ds_read_b128 %19, %26 offset:%c31\n\t"
             "s_waitcnt lgkmcnt(0)"
             : "=&v"(qq[0]), "=&v"(qq[1]), "=&v"(gg[0]), "=&v"(gg[1]), "=&v"(tq[0]), "=&v"(tq[1]), "=&v"(tq[2]),
               "=&v"(tq[3]), "=&v"(tg[0]), "=&v"(tg[1]), "=&v"(tg[2]), "=&v"(tg[3]), "=&v"(nn[0]), "=&v"(nn[1]),
               "=&v"(nn[2]), "=&v"(nn[3]), "=&v"(dd[0]), "=&v"(dd[1]), "=&v"(dd[2]), "=&v"(dd[3])
             : "v"(st + aq[0]), "v"(st + aq[1]), "v"(st + at[0]), "v"(st + at[1]), "v"(st + at[2]), "v"(st + at[3]),
-              "v"(st + an));
+              "v"(st + an), "i"(DK_GQ), "i"(DK_DN), "i"(DK_DN + 32), "i"(DK_DN + 64), "i"(DK_DN + 96));
         bf16x8 qT[2], gT[2];
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
