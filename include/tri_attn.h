@@ -15,7 +15,10 @@
  * P steps) -- and the tiles are joined, in ascending order, by the tiled online-softmax
  * merge (running maximum, normaliser and accumulator; Figure 2(a) and (c)).  Tile t
  * holds keys [t*(N/T) + min(t, N%T), (t+1)*(N/T) + min(t+1, N%T)): the first N mod T
- * tiles take ceil(N/T) keys, the rest floor(N/T).  The tiling changes only rounding.
+ * tiles take ceil(N/T) keys, the rest floor(N/T).  The tiling changes only rounding:
+ * the merge is associative, so the bf16 matrix-core path folds 32-key blocks in the same
+ * ascending order across tile boundaries and its result does not depend on T at all; the
+ * fp32 path folds tile by tile.
  *
  * Layouts: every tensor is dense and C-contiguous, elements as listed (last fastest):
  *     q, k, v   [B, I, N, H, D]   dtype (see tri_attn_dtype)
