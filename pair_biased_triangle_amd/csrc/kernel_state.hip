@@ -16,11 +16,16 @@ namespace {
 
 constexpr int ST_THR = 256;   // threads per workgroup
 constexpr int ST_Q = 64;      // queries per workgroup
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// VEC: D % 4 == 0 and the accumulators 16-byte aligned, so four consecutive floats belong
+// to one query and each lane moves 16 bytes per access (a wave 1 KB); else one float.
 
 // A workgroup owns ST_Q consecutive queries.  Their per-query factors are formed once in
 // LDS; then every thread walks the workgroup's ST_Q * D contiguous floats with a stride
 // of ST_THR, so each wave reads and writes 256 consecutive bytes per access.  The per-query
 // values m and l are read and rewritten by the same thread, on either side of the barriers.
+template <bool VEC>
 __global__ void __launch_bounds__(ST_THR) state_merge_kernel(float* acc, float* m, float* l, const float* acc_t,
                                                              const float* m_t, const float* l_t, int64_t rows,
                                                              int D) {
@@ -56,12 +61,27 @@ __global__ void __launch_bounds__(ST_THR) state_merge_kernel(float* acc, float* 
     __syncthreads();
     const int64_t e0 = q0 * D;
     const int ne = nq * D;
-    for (int e = tid; e < ne; e += ST_THR) {
-        const int qq = e / D;
-        const float a = fa[qq], b = fb[qq];
-        if (b == 0.0f) continue;              // an empty tile leaves the accumulator as it is
-        const float bt = b * acc_t[e0 + e];
-        acc[e0 + e] = a == 0.0f ? bt : a * acc[e0 + e] + bt;
+    if constexpr (VEC) {
+        f32x4* a4 = reinterpret_cast<f32x4*>(acc + e0);
+        const f32x4* t4 = reinterpret_cast<const f32x4*>(acc_t + e0);
+        for (int e = tid; e < ne / 4; e += ST_THR) {
+            const int qq = 4 * e / D;
+            const float a = fa[qq], b = fb[qq];
+            if (b == 0.0f) continue;          // an empty tile leaves the accumulator as it is
+            const f32x4 t = t4[e];
+            f32x4 x = a == 0.0f ? f32x4{} : a4[e];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) x[c] = a == 0.0f ? b * t[c] : a * x[c] + b * t[c];
+            a4[e] = x;
+        }
+    } else {
+        for (int e = tid; e < ne; e += ST_THR) {
+            const int qq = e / D;
+            const float a = fa[qq], b = fb[qq];
+            if (b == 0.0f) continue;          // an empty tile leaves the accumulator as it is
+            const float bt = b * acc_t[e0 + e];
+            acc[e0 + e] = a == 0.0f ? bt : a * acc[e0 + e] + bt;
+        }
     }
     if (tid < nq) {
         m[q0 + tid] = mm;
@@ -69,6 +89,7 @@ __global__ void __launch_bounds__(ST_THR) state_merge_kernel(float* acc, float* 
     }
 }
 
+template <bool VEC>
 __global__ void __launch_bounds__(ST_THR) state_finalize_kernel(const float* acc, const float* m, const float* l,
                                                                 float* out, float* lse, int64_t rows, int D) {
     __shared__ float inv[ST_Q];
@@ -84,9 +105,22 @@ __global__ void __launch_bounds__(ST_THR) state_finalize_kernel(const float* acc
     __syncthreads();
     const int64_t e0 = q0 * D;
     const int ne = nq * D;
-    for (int e = tid; e < ne; e += ST_THR) {
-        const float lq = inv[e / D];
-        out[e0 + e] = lq > 0.0f ? acc[e0 + e] / lq : 0.0f;
+    if constexpr (VEC) {
+        const f32x4* a4 = reinterpret_cast<const f32x4*>(acc + e0);
+        f32x4* o4 = reinterpret_cast<f32x4*>(out + e0);
+        for (int e = tid; e < ne / 4; e += ST_THR) {
+            const float lq = inv[4 * e / D];
+            const f32x4 x = a4[e];
+            f32x4 y;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) y[c] = lq > 0.0f ? x[c] / lq : 0.0f;
+            o4[e] = y;
+        }
+    } else {
+        for (int e = tid; e < ne; e += ST_THR) {
+            const float lq = inv[e / D];
+            out[e0 + e] = lq > 0.0f ? acc[e0 + e] / lq : 0.0f;
+        }
     }
 }
 
@@ -133,12 +167,22 @@ __global__ void __launch_bounds__(CB_THR) state_combine_kernel(const float* acc,
 
 }  // namespace
 
+namespace {
+bool vec_ok(int64_t D, const void* a, const void* b) {
+    return D % 4 == 0 && reinterpret_cast<uintptr_t>(a) % 16 == 0 && reinterpret_cast<uintptr_t>(b) % 16 == 0;
+}
+}  // namespace
+
 hipError_t launch_state_merge(float* acc, float* m, float* l, const float* acc_t, const float* m_t,
                               const float* l_t, int64_t rows, int64_t D, hipStream_t stream) {
     const int64_t blocks = (rows + ST_Q - 1) / ST_Q;
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(state_merge_kernel, dim3(static_cast<unsigned>(blocks)), dim3(ST_THR), 0, stream, acc, m, l,
-                       acc_t, m_t, l_t, rows, static_cast<int>(D));
+    if (vec_ok(D, acc, acc_t))
+        hipLaunchKernelGGL(state_merge_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(ST_THR), 0, stream, acc,
+                           m, l, acc_t, m_t, l_t, rows, static_cast<int>(D));
+    else
+        hipLaunchKernelGGL(state_merge_kernel<false>, dim3(static_cast<unsigned>(blocks)), dim3(ST_THR), 0, stream, acc,
+                           m, l, acc_t, m_t, l_t, rows, static_cast<int>(D));
     return hipGetLastError();
 }
 
@@ -146,8 +190,12 @@ hipError_t launch_state_finalize(const float* acc, const float* m, const float* 
                                  int64_t rows, int64_t D, hipStream_t stream) {
     const int64_t blocks = (rows + ST_Q - 1) / ST_Q;
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(state_finalize_kernel, dim3(static_cast<unsigned>(blocks)), dim3(ST_THR), 0, stream, acc, m,
-                       l, out, lse, rows, static_cast<int>(D));
+    if (vec_ok(D, acc, out))
+        hipLaunchKernelGGL(state_finalize_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(ST_THR), 0, stream,
+                           acc, m, l, out, lse, rows, static_cast<int>(D));
+    else
+        hipLaunchKernelGGL(state_finalize_kernel<false>, dim3(static_cast<unsigned>(blocks)), dim3(ST_THR), 0, stream,
+                           acc, m, l, out, lse, rows, static_cast<int>(D));
     return hipGetLastError();
 }
 
