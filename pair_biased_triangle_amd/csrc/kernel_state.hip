@@ -131,6 +131,7 @@ __global__ void __launch_bounds__(ST_THR) state_finalize_kernel(const float* acc
 constexpr int MAX_COMBINE = 16;
 constexpr int CB_Q = 16;
 constexpr int CB_THR = 128;
+template <bool VEC>
 __global__ void __launch_bounds__(CB_THR) state_combine_kernel(const float* acc, const float* m, const float* l,
                                                                int n_split, int64_t rows, int D, float* out,
                                                                float* lse) {
@@ -157,11 +158,24 @@ __global__ void __launch_bounds__(CB_THR) state_combine_kernel(const float* acc,
     __syncthreads();
     const int64_t e0 = q0 * D;
     const int ne = nq * D;
-    for (int e = tid; e < ne; e += CB_THR) {
-        const int qq = e / D;
-        float x = 0.0f;
-        for (int s = 0; s < n_split; ++s) x = fmaf(fac[s][qq], acc[s * rows * D + e0 + e], x);
-        out[e0 + e] = x;
+    if constexpr (VEC) {
+        for (int e = tid; e < ne / 4; e += CB_THR) {
+            const int qq = 4 * e / D;
+            f32x4 x = {};
+            for (int s = 0; s < n_split; ++s) {
+                const f32x4 a = reinterpret_cast<const f32x4*>(acc + s * rows * D + e0)[e];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) x[c] = fmaf(fac[s][qq], a[c], x[c]);
+            }
+            reinterpret_cast<f32x4*>(out + e0)[e] = x;
+        }
+    } else {
+        for (int e = tid; e < ne; e += CB_THR) {
+            const int qq = e / D;
+            float x = 0.0f;
+            for (int s = 0; s < n_split; ++s) x = fmaf(fac[s][qq], acc[s * rows * D + e0 + e], x);
+            out[e0 + e] = x;
+        }
     }
 }
 
@@ -203,8 +217,13 @@ hipError_t launch_state_combine(const float* acc, const float* m, const float* l
                                 int64_t D, float* out, float* lse, hipStream_t stream) {
     const int64_t blocks = (rows + CB_Q - 1) / CB_Q;
     if (blocks > 0x7FFFFFFF || n_split < 1 || n_split > MAX_COMBINE) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(state_combine_kernel, dim3(static_cast<unsigned>(blocks)), dim3(CB_THR), 0, stream, acc, m, l,
-                       n_split, rows, static_cast<int>(D), out, lse);
+    // every split's accumulator block is rows * D floats: 16-byte aligned when D % 4 == 0
+    if (vec_ok(D, acc, out))
+        hipLaunchKernelGGL(state_combine_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(CB_THR), 0, stream,
+                           acc, m, l, n_split, rows, static_cast<int>(D), out, lse);
+    else
+        hipLaunchKernelGGL(state_combine_kernel<false>, dim3(static_cast<unsigned>(blocks)), dim3(CB_THR), 0, stream,
+                           acc, m, l, n_split, rows, static_cast<int>(D), out, lse);
     return hipGetLastError();
 }
 

@@ -217,12 +217,15 @@ def test_ring_by_state_updates(torch_dev, dtype, ending, N, I):
     compare_lse(lse.cpu().numpy(), ref_lse, TOL[dtype], "ring by updates lse")
 
 
-def test_state_merge_and_finalize_kernels(torch_dev):
+@pytest.mark.parametrize("D,shift", [(24, 0), (6, 0), (24, 1)], ids=["vector", "D6_scalar", "offset_scalar"])
+def test_state_merge_and_finalize_kernels(torch_dev, D, shift):
     """The merge and finalisation kernels on random fp32 states (empty states mixed in)
-    against the oracle module's merge rule in fp64 on the same values."""
+    against the oracle module's merge rule in fp64 on the same values.  D % 4 == 0 with
+    16-byte aligned accumulators takes the 16-byte path; D = 6, or accumulators that start
+    4 bytes past a 16-byte boundary (shift), take the one-float path."""
     import pair_biased_triangle_amd as P
     rng = np.random.default_rng(17)
-    rows, D = 5000, 24
+    rows = 5000
     def state(empty_frac):
         acc = rng.standard_normal((rows, D)).astype(np.float32)
         m = (3 * rng.standard_normal(rows)).astype(np.float32)
@@ -236,8 +239,16 @@ def test_state_merge_and_finalize_kernels(torch_dev):
         st[2][:10] = np.float32(3.0)
     b[1][:5] = np.float32(-2.0)                      # ... with equal references in 5..9
     say("[next] state merge/finalize kernels")
-    ga = tuple(torch_dev.from_numpy(x.copy()).cuda() for x in a)
-    gb = tuple(torch_dev.from_numpy(x.copy()).cuda() for x in b)
+    def dev(x):
+        if x.ndim == 1 or shift == 0:
+            return torch_dev.from_numpy(x.copy()).cuda()
+        buf = torch_dev.empty(x.size + shift, dtype=torch_dev.float32, device="cuda")
+        t = buf[shift:].view(x.shape)
+        t.copy_(torch_dev.from_numpy(x))
+        assert t.data_ptr() % 16 == 4 * shift
+        return t
+    ga = tuple(dev(x) for x in a)
+    gb = tuple(dev(x) for x in b)
     P.tri_attn_state_merge(*ga, *gb)
     out, lse = P.tri_attn_state_finalize(*ga)
     torch_dev.cuda.synchronize()
