@@ -41,7 +41,8 @@
  * Ownership and memory: every pointer is a device pointer owned by the caller; the
  * library keeps none of them after returning.  q, k, v, bias and mask are only read and
  * may alias one another; outputs must not overlap any input.  q, k, v, bias and out must be
- * 16-byte aligned, mask 4-byte aligned.  The bf16 matrix-core path (D == 32) first
+ * 16-byte aligned, mask 4-byte aligned.  The bf16 matrix-core path (D == 32; one-row calls
+ * with even N aside, see pair_bias_attn_fwd) first
  * converts the bias into an fp16 image plus one fp32 reference per query, together
  * tri_attn_workspace_bytes() bytes: roughly 2 * B * H * N * N bytes (queries padded to a
  * multiple of 128, keys to a multiple of 32), plus,
@@ -272,8 +273,12 @@ int tri_attn_bwd(const void *q, const void *k, const void *v, const void *bias,
  *     s_k            = q[b,j,h,:] . k[b,k,h,:] / sqrt(D) + bias[b,h,j,k] + mask[b,k]
  *     out[b,j,h,:]   = sum_k softmax_k(s)_k * v[b,k,h,:]
  * q, k, v, out [B, N, H, D]; bias [B, H, N, N]; mask [B, N] or NULL; lse [B, N, H] or
- * NULL.  It is the triangle operation with a single row (I == 1), with the same tiling,
- * numerics and rules.
+ * NULL.  It is the triangle operation with a single row (I == 1), with the same tiling
+ * and rules.  With one row every bias value is used once, so for bf16, D == 32 and even N
+ * the call (like any one-row tri_attn_fwd_rows call) runs a single-pass kernel that reads
+ * the raw bias once with the exact running maximum instead of the fp16 image; its
+ * workspace holds only the partial states of key ranges run side by side (none when one
+ * range suffices).  Odd N takes the image path.
  */
 int pair_bias_attn_fwd(const void *q, const void *k, const void *v, const void *bias,
                        const float *mask, float *out, float *lse,

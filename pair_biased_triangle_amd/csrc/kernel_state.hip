@@ -162,6 +162,7 @@ __global__ void __launch_bounds__(CB_THR) state_combine_kernel(const float* acc,
         for (int e = tid; e < ne / 4; e += CB_THR) {
             const int qq = 4 * e / D;
             f32x4 x = {};
+#pragma unroll 4
             for (int s = 0; s < n_split; ++s) {
                 const f32x4 a = reinterpret_cast<const f32x4*>(acc + s * rows * D + e0)[e];
 #pragma unroll

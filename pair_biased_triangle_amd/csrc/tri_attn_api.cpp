@@ -8,12 +8,24 @@
 #include <mutex>
 
 #include "launch.h"
+#include "pair_bias.h"
 
 namespace {
 
 thread_local int g_last_hip_error = 0;
 
 bool uses_matrix_cores(int32_t dtype, int64_t D) { return dtype == TRI_ATTN_BF16 && D == 32; }
+
+// Matrix-core forward: one line without state output (attention with pair bias) reads the
+// raw bias once in the single-pass kernel; everything else goes through the fp16 image.
+size_t mfma_workspace_bytes(const tri_attn::Problem& p) {
+    return tri_attn::pair_bias_direct_applies(p) ? tri_attn::pair_bias_direct_workspace_bytes(p)
+                                                 : tri_attn::bf16_workspace_bytes(p);
+}
+hipError_t launch_mfma(const tri_attn::Problem& p, void* ws, hipStream_t s) {
+    return tri_attn::pair_bias_direct_applies(p) ? tri_attn::launch_pair_bias_direct(p, ws, s)
+                                                 : tri_attn::launch_bf16_mfma(p, ws, s);
+}
 
 bool mul_ok(int64_t a, int64_t b, int64_t* out) {
     if (a < 0 || b < 0) return false;
@@ -165,7 +177,7 @@ int run(const Call& c, void* stream) {
         const hipError_t e = tri_attn::launch_general(p, c.dtype == TRI_ATTN_BF16, s);
         return e == hipSuccess ? TRI_ATTN_OK : hip_fail(e);
     }
-    const int64_t need = static_cast<int64_t>(tri_attn::bf16_workspace_bytes(p));
+    const int64_t need = static_cast<int64_t>(mfma_workspace_bytes(p));
     if (c.ws_bytes >= 0) {  // caller-provided workspace
         if (!c.ws) return TRI_ATTN_ERR_NULL;
         if (!aligned(c.ws, 16)) return TRI_ATTN_ERR_ALIGN;
@@ -176,7 +188,11 @@ int run(const Call& c, void* stream) {
                                {c.st_l, qkv_elems / c.D * 4}};
         for (const Span& o : others)
             if (o.p && overlaps(c.ws, need, o.p, o.bytes)) return TRI_ATTN_ERR_ALIAS;
-        const hipError_t e = tri_attn::launch_bf16_mfma(p, c.ws, s);
+        const hipError_t e = launch_mfma(p, c.ws, s);
+        return e == hipSuccess ? TRI_ATTN_OK : hip_fail(e);
+    }
+    if (need == 0) {  // nothing to allocate
+        const hipError_t e = launch_mfma(p, nullptr, s);
         return e == hipSuccess ? TRI_ATTN_OK : hip_fail(e);
     }
     hipMemPool_t pool = nullptr;
@@ -185,7 +201,7 @@ int run(const Call& c, void* stream) {
     void* own = nullptr;
     e = hipMallocFromPoolAsync(&own, static_cast<size_t>(need), pool, s);
     if (e != hipSuccess) return hip_fail(e);
-    e = tri_attn::launch_bf16_mfma(p, own, s);
+    e = launch_mfma(p, own, s);
     const hipError_t ef = hipFreeAsync(own, s);
     if (e != hipSuccess) return hip_fail(e);
     if (ef != hipSuccess) return hip_fail(ef);
@@ -229,7 +245,7 @@ int64_t tri_attn_workspace_bytes(int64_t B, int64_t H, int64_t I, int64_t N, int
     if (!uses_matrix_cores(dtype, D)) return 0;
     const tri_attn::Problem p =
         make_problem(make_call(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, B, H, I, N, D, n_key_tiles, dtype));
-    return static_cast<int64_t>(tri_attn::bf16_workspace_bytes(p));
+    return static_cast<int64_t>(mfma_workspace_bytes(p));
 }
 
 int tri_attn_fwd_rows_ws(const void* q, const void* k, const void* v, const void* bias, const float* mask,

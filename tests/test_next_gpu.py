@@ -275,7 +275,10 @@ def test_tile_state_of_masked_range_is_empty(torch_dev):
 # ---------------------------------------------------------------------------
 # attention with pair bias
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("dtype,N,D,T,B", [("bf16", 300, 32, 4, 2), ("fp32", 130, 16, 1, 3), ("bf16", 2700, 32, 8, 1)])
+# bf16 with D = 32 and even N: the single-pass kernel (N = 100: one key range, N = 300 and
+# 2700: ranges joined by the combine); odd N goes through the fp16 image; fp32 the general path
+@pytest.mark.parametrize("dtype,N,D,T,B", [("bf16", 300, 32, 4, 2), ("fp32", 130, 16, 1, 3), ("bf16", 2700, 32, 8, 1),
+                                           ("bf16", 100, 32, 3, 3), ("bf16", 301, 32, 2, 1)])
 def test_pair_bias_attention(torch_dev, dtype, N, D, T, B):
     import pair_biased_triangle_amd as P
     w = small(dtype, B=B, I=1, N=N, D=D, T=T, mask_last=7)
@@ -287,3 +290,28 @@ def test_pair_bias_attention(torch_dev, dtype, N, D, T, B):
     ref, ref_lse = oracle.tri_attn(w.q, w.k, w.v, w.bias, w.mask, n_key_tiles=T)
     compare(out.cpu().numpy(), ref[:, 0], TOL[dtype], f"pair-bias out {dtype}")
     compare_lse(lse.cpu().numpy(), ref_lse[:, 0], TOL[dtype], f"pair-bias lse {dtype}")
+
+
+@pytest.mark.parametrize("N", [100, 640])
+def test_pair_bias_single_pass_extremes(torch_dev, N):
+    """The single-pass kernel keeps the exact running maximum: a bias jump of +60 on one key
+    of some queries makes that key take all the weight, a batch element with every key
+    masked gives out 0 and lse -inf, and the rest still matches the oracle."""
+    import pair_biased_triangle_amd as P
+    w = small("bf16", B=2, I=1, N=N, D=32, T=1, mask_last=5)
+    w.mask[1, :] = -np.inf
+    bias = W.bf16_bits_to_f32(w.bias)
+    bias[0, 2, 10:40, N // 3] += 60.0
+    w.bias = W.f32_to_bf16_bits(bias)
+    say(f"[next] pair-bias single pass, extremes, N={N}")
+    q, k, v, b, mask = dev_inputs(torch_dev, w)
+    shp = (2, N, 4, 32)
+    out, lse = P.pair_bias_attn_fwd(q.view(shp), k.view(shp), v.view(shp), b, mask, want_lse=True)
+    torch_dev.cuda.synchronize()
+    ref, ref_lse = oracle.tri_attn(w.q, w.k, w.v, w.bias, w.mask, n_key_tiles=1)
+    o, l = out.cpu().numpy(), lse.cpu().numpy()
+    compare(o, ref[:, 0], TOL["bf16"], "pair-bias single pass out")
+    compare_lse(l, ref_lse[:, 0], TOL["bf16"], "pair-bias single pass lse")
+    assert np.all(o[1] == 0) and np.all(np.isneginf(l[1]))
+    vv = W.bf16_bits_to_f32(w.v)[0, 0, N // 3, 2]                     # the value row of the dominant key
+    np.testing.assert_allclose(o[0, 10:40, 2], np.broadcast_to(vv, (30, 32)), atol=1e-6)
