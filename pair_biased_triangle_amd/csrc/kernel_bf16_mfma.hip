@@ -838,61 +838,93 @@ __global__ void __launch_bounds__(NTHR, 2) bf16_mfma_kernel(Problem p, Strides s
     // out receives O itself, with the reference in natural-log units (r_j + m ln 2) and l;
     // the log-sum-exp is that reference plus ln l.
     const bool state = p.st_m != nullptr;
+    float lt[RW][TW];
+#pragma unroll
+    for (int ri = 0; ri < RW; ++ri)
+#pragma unroll
+        for (int ti = 0; ti < TW; ++ti) lt[ri][ti] = s.lsum[ri][ti] + __shfl_xor(s.lsum[ri][ti], 32);
+    if (state && p.update) {
+        // fold this range's state into the running one (merge rule, natural-log units).  Every
+        // old value is loaded before anything is stored, so all of them are in flight at once
+        // (loads after stores to the same array would each wait for the one before).
+        f32x4 old[RW][TW][4];
+        float m0[RW][TW], l0[RW][TW];
+#pragma unroll
+        for (int ri = 0; ri < RW; ++ri)
+#pragma unroll
+            for (int ti = 0; ti < TW; ++ti) {
+                const int64_t i = i0 + row0 + ri, j = j0 + (tile0 + ti) * 32 + L.c;
+                const bool ok = i < lines && j < p.N;
+                const int64_t qo = bh_off + (ok ? i * sd.line + j * sd.query : 0);
+                m0[ri][ti] = ok ? p.st_m[qo / D] : -INFINITY;
+                l0[ri][ti] = ok ? p.st_l[qo / D] : 0.0f;
+#pragma unroll
+                for (int a = 0; a < 4; ++a)
+                    old[ri][ti][a] = ok ? *reinterpret_cast<const f32x4*>(p.out + qo + 8 * a + 4 * L.h2) : f32x4{};
+            }
+#pragma unroll
+        for (int ri = 0; ri < RW; ++ri)
+#pragma unroll
+            for (int ti = 0; ti < TW; ++ti) {
+                const int64_t i = i0 + row0 + ri, j = j0 + (tile0 + ti) * 32 + L.c;
+                if (!(i < lines && j < p.N) || !(lt[ri][ti] > 0.0f)) continue;   // an empty range changes nothing
+                const int64_t qo = bh_off + i * sd.line + j * sd.query;
+                const float m1 = s.mref[ri][ti] * kLn2 + ref[static_cast<int64_t>(bh) * n_jb * BJ + j];
+                float a0 = 0.0f, a1 = 1.0f, mm = m1;
+                if (l0[ri][ti] > 0.0f) {
+                    mm = fmaxf(m0[ri][ti], m1);
+                    a0 = expf(m0[ri][ti] - mm);
+                    a1 = expf(m1 - mm);
+                }
+#pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    const f32x4 o0 = a0 != 0.0f ? old[ri][ti][a] : f32x4{};
+                    f32x4 x;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) x[e] = fmaf(a0, o0[e], a1 * s.O[ri][ti][4 * a + e]);
+                    *reinterpret_cast<f32x4*>(p.out + qo + 8 * a + 4 * L.h2) = x;
+                }
+                if (L.h2 == 0) {
+                    p.st_m[qo / D] = mm;
+                    p.st_l[qo / D] = a0 * l0[ri][ti] + a1 * lt[ri][ti];
+                }
+            }
+        return;
+    }
+    // the references r_j of this lane's two queries, loaded before any store
+    float rj[TW];
+#pragma unroll
+    for (int ti = 0; ti < TW; ++ti) {
+        const int64_t j = j0 + (tile0 + ti) * 32 + L.c;
+        rj[ti] = ((state || p.lse) && j < p.N) ? ref[static_cast<int64_t>(bh) * n_jb * BJ + j] : 0.0f;
+    }
 #pragma unroll
     for (int ri = 0; ri < RW; ++ri)
 #pragma unroll
         for (int ti = 0; ti < TW; ++ti) {
-            const float lt = s.lsum[ri][ti] + __shfl_xor(s.lsum[ri][ti], 32);
             const int64_t i = i0 + row0 + ri, j = j0 + (tile0 + ti) * 32 + L.c;
-            if (i < lines && j < p.N && state && p.update) {
-                // fold this range's state into the running one (merge rule, natural-log units)
-                const int64_t qo = bh_off + i * sd.line + j * sd.query;
-                float* o = p.out + qo;
-                const float m1 = s.mref[ri][ti] * kLn2 + ref[static_cast<int64_t>(bh) * n_jb * BJ + j];
-                const float m0 = p.st_m[qo / D], l0 = p.st_l[qo / D];
-                if (lt > 0.0f) {
-                    float a0 = 0.0f, a1 = 1.0f, mm = m1;
-                    if (l0 > 0.0f) {
-                        mm = fmaxf(m0, m1);
-                        a0 = expf(m0 - mm);
-                        a1 = expf(m1 - mm);
-                    }
+            if (!(i < lines && j < p.N)) continue;
+            const float lq = lt[ri][ti];
+            const int64_t qo = bh_off + i * sd.line + j * sd.query;
+            float* o = p.out + qo;
+            // correctly rounded O / l: a single surviving key returns its v exactly
 #pragma unroll
-                    for (int a = 0; a < 4; ++a) {
-                        f32x4* op = reinterpret_cast<f32x4*>(o + 8 * a + 4 * L.h2);
-                        f32x4 x = {};
-                        if (a0 != 0.0f) x = *op;
+            for (int a = 0; a < 4; ++a) {
+                f32x4 x;
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) x[e] = fmaf(a0, x[e], a1 * s.O[ri][ti][4 * a + e]);
-                        *op = x;
-                    }
-                    if (L.h2 == 0) {
-                        p.st_m[qo / D] = mm;
-                        p.st_l[qo / D] = a0 * l0 + a1 * lt;
-                    }
+                for (int e = 0; e < 4; ++e) {
+                    const float acc = s.O[ri][ti][4 * a + e];
+                    x[e] = state ? acc : (lq > 0.0f ? acc / lq : 0.0f);
                 }
-            } else if (i < lines && j < p.N) {
-                const int64_t qo = bh_off + i * sd.line + j * sd.query;
-                float* o = p.out + qo;
-                // correctly rounded O / l: a single surviving key returns its v exactly
-#pragma unroll
-                for (int a = 0; a < 4; ++a) {
-                    f32x4 x;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float acc = s.O[ri][ti][4 * a + e];
-                        x[e] = state ? acc : (lt > 0.0f ? acc / lt : 0.0f);
-                    }
-                    *reinterpret_cast<f32x4*>(o + 8 * a + 4 * L.h2) = x;
+                *reinterpret_cast<f32x4*>(o + 8 * a + 4 * L.h2) = x;
+            }
+            if (L.h2 == 0 && (state || p.lse)) {
+                const float mnat = s.mref[ri][ti] * kLn2 + rj[ti];
+                if (state) {
+                    p.st_m[qo / D] = lq > 0.0f ? mnat : -INFINITY;
+                    p.st_l[qo / D] = lq;
                 }
-                if (L.h2 == 0 && (state || p.lse)) {
-                    const float mnat = s.mref[ri][ti] * kLn2 + ref[static_cast<int64_t>(bh) * n_jb * BJ + j];
-                    if (state) {
-                        p.st_m[qo / D] = lt > 0.0f ? mnat : -INFINITY;
-                        p.st_l[qo / D] = lt;
-                    }
-                    if (p.lse) p.lse[qo / D] = lt > 0.0f ? mnat + logf(lt) : -INFINITY;
-                }
+                if (p.lse) p.lse[qo / D] = lq > 0.0f ? mnat + logf(lq) : -INFINITY;
             }
         }
 }
