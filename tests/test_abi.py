@@ -150,6 +150,26 @@ def test_workspace_bytes(lib):
     assert P.workspace_bytes(1, 4, 2700, 2700, 32, 8, 1) == need(1, 4, 2700, 85)
 
 
+def test_workspace_bytes_of_one_row_calls(lib):
+    # one row (attention with pair bias), bf16, D=32, even N: the single-pass kernel's key-range
+    # states, S splits of [rows][D] accumulators plus m and l per row (S so that about 512
+    # workgroups of 128 queries run, at most 16, each split at least 4 key blocks); none
+    # when one range suffices; odd N goes through the fp16 image
+    def single_pass(B, H, N):
+        n_qb, nblk, rows = -(-N // 128), -(-N // 32), B * N * H
+        s = min(-(-512 // (B * H * n_qb)), nblk // 4, 16)
+        if s < 2:
+            return 0
+        return s * rows * 32 * 4 + -(-(s * rows * 4) // 256) * 256 + s * rows * 4
+    assert single_pass(1, 4, 2700) == 6 * 10800 * 32 * 4 + 259328 + 6 * 10800 * 4
+    assert lib.tri_attn_workspace_bytes(1, 4, 1, 2700, 32, 8, BF16) == single_pass(1, 4, 2700)
+    assert lib.tri_attn_workspace_bytes(3, 4, 1, 100, 32, 3, BF16) == 0 == single_pass(3, 4, 100)
+    assert lib.tri_attn_workspace_bytes(2, 4, 1, 300, 32, 4, BF16) == single_pass(2, 4, 300) > 0
+    odd = lib.tri_attn_workspace_bytes(1, 4, 1, 301, 32, 2, BF16)
+    assert odd == 4 * 3 * 10 * 128 * 32 * 2 + 4 * 3 * 128 * 4        # image (3 column blocks x 10 key blocks) + r_j
+    assert P.workspace_bytes(1, 4, 1, 2700, 32, 8, 1) == single_pass(1, 4, 2700)
+
+
 WS = fake(0x70000000)
 
 
