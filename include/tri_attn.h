@@ -45,8 +45,8 @@
  * with even N aside, see pair_bias_attn_fwd) first
  * converts the bias into an fp16 image plus one fp32 reference per query, together
  * tri_attn_workspace_bytes() bytes: roughly 2 * B * H * N * N bytes (queries padded to a
- * multiple of 128, keys to a multiple of 32), plus,
- * for calls too small to fill the GPU (fewer than 512 workgroups of 4 rows x 128 columns
+ * multiple of 256, keys to a multiple of 32), plus,
+ * for calls too small to fill the GPU (fewer than 512 workgroups of 2 rows x 256 columns
  * and at least 16 key blocks), the partial softmax states of up to 16 key ranges that run
  * side by side and are then joined (16 * 34 * B * I * N * H bytes at most).  Every entry
  * point except tri_attn_fwd_rows_ws, and the matrix-core backward, obtains its workspace

@@ -39,7 +39,7 @@
 // (log2 units) refreshed on every block.  The natural log of the normaliser adds the
 // reference back: lse = r_j + m ln 2 + ln l (m = 0 in the fast pass).
 //
-// Shape: 4 waves own 4 lines x 128 query columns, with a ring of 3 stages of 24 KB, so
+// Shape: 4 waves own 2 lines x 256 query columns, with a ring of 3 stages of 24 KB, so
 // two workgroups (72 KB of LDS each) share a compute unit.  Each waits only at its own
 // barrier, so one workgroup's burst of operand reads after its barrier overlaps the
 // other's arithmetic (with 8 waves and one workgroup per unit, every wave waits on the
@@ -71,7 +71,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int D = 32;
 constexpr int BK = 32;                      // keys per block
 #ifndef TRI_ATTN_ROWS
-#define TRI_ATTN_ROWS 4
+#define TRI_ATTN_ROWS 2
 #endif
 constexpr int R = TRI_ATTN_ROWS;            // lines per workgroup
 #ifndef TRI_ATTN_WAVES
@@ -84,7 +84,7 @@ constexpr int TW = 2;                       // query tiles per wave
 constexpr int QT = NWAVE * RW * TW / R;     // 32-wide query tiles per workgroup
 constexpr int BJ = 32 * QT;                 // query columns per workgroup
 constexpr int NXCD = 8;
-static_assert(R == 4 || R == 8, "4 or 8 lines per workgroup");
+static_assert(R == 2 || R == 4 || R == 8, "2, 4 or 8 lines per workgroup");
 static_assert((R / RW) * (QT / TW) == NWAVE, "every wave owns RW x TW units");
 #ifndef TRI_ATTN_STAGES
 #define TRI_ATTN_STAGES 3
