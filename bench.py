@@ -19,8 +19,9 @@ relates the kernel's live-measured average launch time to the bf16 dense MFMA pe
   pair_bias  pair_bias_attn_fwd on the workload's first row (I = 1): bound by reading
              the bias -> roofline in GB/s against HBM
   ring       tri_attn_tile_state on the first key tile, tri_attn_tile_state_update on each
-             later one (the step folded into the running state), then
-             tri_attn_state_finalize (the split-tile path), against the bf16 MFMA peak
+             middle one (the step folded into the running state), tri_attn_tile_state_final
+             on the last (folded and written out): the split-tile path, against the bf16
+             MFMA peak
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME] [--no-cpu]
                     [--pass fwd|bwd|ending|pair_bias|ring]
@@ -179,14 +180,18 @@ def other_pass(args, torch, P, W, cfg) -> dict:
         def step():
             # one ring: the first step's state, every later step folded into it in place
             P.tri_attn_tile_state(q, k, v, bias, mask, key_begin=bounds[0], key_end=bounds[1], acc=acc, m=m, l=l)
-            for t in range(1, T):
+            for t in range(1, T - 1):
                 P.tri_attn_tile_state_update(q, k, v, bias, mask, key_begin=bounds[t], key_end=bounds[t + 1],
                                              acc=acc, m=m, l=l)
-            P.tri_attn_state_finalize(acc, m, l, out=out)
+            if T > 1:
+                P.tri_attn_tile_state_final(q, k, v, bias, mask, key_begin=bounds[T - 1], key_end=bounds[T],
+                                            acc=acc, m=m, l=l, out=out)
+            else:
+                P.tri_attn_state_finalize(acc, m, l, out=out)
         work, unit, peak, bound = fwd_flops, "TFLOP/s", PEAK_BF16_TFLOPS, "mfma"
-        metric = f"split-tile ring TFLOP/s ({T} ring steps folded into one state + finalize, 4·B·H·I·N²·D)"
-        kernels = ("per step: bias_ref_kernel + bias_image16_kernel + bf16_mfma_kernel (state mode, the later steps "
-                   "merging into the running state); state_finalize_kernel")
+        metric = f"split-tile ring TFLOP/s ({T} ring steps folded into one state, the last one finalised, 4·B·H·I·N²·D)"
+        kernels = ("per step: bias_ref_kernel + bias_image16_kernel + bf16_mfma_kernel (state mode; the middle steps "
+                   "merge into the running state, the last one writes out)")
         dtype = cfg.dtype
     ms, wall = timed(torch, step, args.steps, args.warmup)
     rate = work / (ms * 1e-3) / (1e12 if unit == "TFLOP/s" else 1e9)

@@ -217,6 +217,23 @@ int tri_attn_tile_state_update(const void *q, const void *k, const void *v, cons
                                int32_t dtype, void *stream);
 
 /*
+ * The last ring step: the keys [key_begin, key_end) folded into the state (acc, m, l) as
+ * tri_attn_tile_state_update does, and the result finalised straight into out
+ * (out = acc / l, 0 where l == 0) and, when lse is not NULL, lse = m + ln l (-inf where
+ * l == 0), as tri_attn_state_finalize would.  acc, m and l are only read.  Equivalent to
+ * tri_attn_tile_state_update followed by tri_attn_state_finalize, without writing the
+ * state back and reading it again.  out [B, I, N, H, D] fp32, 16-byte aligned; lse
+ * [B, I, N, H] or NULL; neither may overlap an input or the state.  Other arguments,
+ * layouts and errors as tri_attn_tile_state.
+ */
+int tri_attn_tile_state_final(const void *q, const void *k, const void *v, const void *bias,
+                              const float *mask, const float *acc, const float *m, const float *l,
+                              float *out, float *lse,
+                              int64_t B, int64_t H, int64_t I, int64_t N, int64_t D,
+                              int64_t key_begin, int64_t key_end, int32_t ending,
+                              int32_t dtype, void *stream);
+
+/*
  * The merge of two partial states, in place into the first, for `rows` queries of D
  * values (rows = B * I * N * H for the states above; 1 <= D <= 64):
  *     M = max(m, m_t);  a = exp(m - M), b = exp(m_t - M)

@@ -24,7 +24,7 @@ STATUS = {
 }
 EXPORTS = ("tri_attn_fwd", "tri_attn_fwd_rows", "tri_attn_fwd_rows_ws", "tri_attn_workspace_bytes",
            "tri_attn_fwd_lse", "tri_attn_fwd_ending", "tri_attn_tile_state", "tri_attn_tile_state_update",
-           "tri_attn_state_merge",
+           "tri_attn_tile_state_final", "tri_attn_state_merge",
            "tri_attn_state_finalize", "pair_bias_attn_fwd", "tri_attn_bwd",
            "tri_attn_status_string", "tri_attn_last_hip_error", "tri_attn_version")
 
@@ -61,6 +61,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         L.tri_attn_tile_state.restype = ctypes.c_int
         L.tri_attn_tile_state_update.argtypes = L.tri_attn_tile_state.argtypes
         L.tri_attn_tile_state_update.restype = ctypes.c_int
+        L.tri_attn_tile_state_final.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
+                                                i64, i32, i32, vp]
+        L.tri_attn_tile_state_final.restype = ctypes.c_int
         L.tri_attn_state_merge.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, vp]
         L.tri_attn_state_merge.restype = ctypes.c_int
         L.tri_attn_state_finalize.argtypes = [vp, vp, vp, vp, vp, i64, i64, vp]
@@ -257,6 +260,25 @@ def tri_attn_tile_state_update(q, k, v, bias, mask=None, *, key_begin: int, key_
                                         _ptr(l), B, H, I, N, D, int(key_begin), int(key_end), int(bool(ending)), dt,
                                         _stream_handle(stream)))
     return acc, m, l
+
+
+def tri_attn_tile_state_final(q, k, v, bias, mask=None, *, key_begin: int, key_end: int, acc, m, l,
+                              ending: bool = False, out=None, lse=None, want_lse: bool = False, stream=None):
+    """The last ring step: fold the keys [key_begin, key_end) into the state (acc, m, l),
+    which is only read, and return the finalised out [B, I, N, H, D] (and lse [B, I, N, H]
+    when asked).  Calls tri_attn_tile_state_final."""
+    L = load_library()
+    dt, acc = _validate(q, k, v, bias, mask, acc)
+    _, out = _validate(q, k, v, bias, mask, out)
+    B, I, N, H, D = q.shape
+    m = _per_query(acc, (B, I, N, H), "m", m)
+    l = _per_query(acc, (B, I, N, H), "l", l)
+    if want_lse or lse is not None:
+        lse = _per_query(acc, (B, I, N, H), "lse", lse)
+    _check(L.tri_attn_tile_state_final(_ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(mask), _ptr(acc), _ptr(m), _ptr(l),
+                                       _ptr(out), _ptr(lse), B, H, I, N, D, int(key_begin), int(key_end),
+                                       int(bool(ending)), dt, _stream_handle(stream)))
+    return (out, lse) if lse is not None else out
 
 
 def _state_shape(acc, m, l):

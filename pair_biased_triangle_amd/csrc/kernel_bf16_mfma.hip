@@ -862,31 +862,47 @@ __global__ void __launch_bounds__(NTHR, 2) bf16_mfma_kernel(Problem p, Strides s
                 for (int a = 0; a < 4; ++a)
                     old[ri][ti][a] = ok ? *reinterpret_cast<const f32x4*>(p.out + qo + 8 * a + 4 * L.h2) : f32x4{};
             }
+        const bool fin = p.fin != nullptr;      // final step: write the folded result as out and lse
 #pragma unroll
         for (int ri = 0; ri < RW; ++ri)
 #pragma unroll
             for (int ti = 0; ti < TW; ++ti) {
                 const int64_t i = i0 + row0 + ri, j = j0 + (tile0 + ti) * 32 + L.c;
-                if (!(i < lines && j < p.N) || !(lt[ri][ti] > 0.0f)) continue;   // an empty range changes nothing
+                if (!(i < lines && j < p.N)) continue;
+                const bool some = lt[ri][ti] > 0.0f;
+                if (!some && !fin) continue;    // an empty range leaves the state as it is
                 const int64_t qo = bh_off + i * sd.line + j * sd.query;
                 const float m1 = s.mref[ri][ti] * kLn2 + ref[static_cast<int64_t>(bh) * n_jb * BJ + j];
-                float a0 = 0.0f, a1 = 1.0f, mm = m1;
-                if (l0[ri][ti] > 0.0f) {
-                    mm = fmaxf(m0[ri][ti], m1);
-                    a0 = expf(m0[ri][ti] - mm);
-                    a1 = expf(m1 - mm);
+                float a0 = 1.0f, a1 = 0.0f, mm = m0[ri][ti];   // empty range: the old state as it is
+                if (some) {
+                    a0 = 0.0f;
+                    a1 = 1.0f;
+                    mm = m1;
+                    if (l0[ri][ti] > 0.0f) {
+                        mm = fmaxf(m0[ri][ti], m1);
+                        a0 = expf(m0[ri][ti] - mm);
+                        a1 = expf(m1 - mm);
+                    }
                 }
+                const float ln = a0 * l0[ri][ti] + a1 * lt[ri][ti];
 #pragma unroll
                 for (int a = 0; a < 4; ++a) {
                     const f32x4 o0 = a0 != 0.0f ? old[ri][ti][a] : f32x4{};
                     f32x4 x;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) x[e] = fmaf(a0, o0[e], a1 * s.O[ri][ti][4 * a + e]);
-                    *reinterpret_cast<f32x4*>(p.out + qo + 8 * a + 4 * L.h2) = x;
+                    for (int e = 0; e < 4; ++e) {
+                        x[e] = fmaf(a0, o0[e], a1 * s.O[ri][ti][4 * a + e]);
+                        if (fin) x[e] = ln > 0.0f ? x[e] / ln : 0.0f;
+                    }
+                    *reinterpret_cast<f32x4*>((fin ? p.fin : p.out) + qo + 8 * a + 4 * L.h2) = x;
                 }
                 if (L.h2 == 0) {
-                    p.st_m[qo / D] = mm;
-                    p.st_l[qo / D] = a0 * l0[ri][ti] + a1 * lt[ri][ti];
+                    if (!fin) {
+                        p.st_m[qo / D] = mm;
+                        p.st_l[qo / D] = ln;
+                    } else if (p.lse) {
+                        p.lse[qo / D] = ln > 0.0f ? mm + logf(ln) : -INFINITY;
+                    }
                 }
             }
         return;

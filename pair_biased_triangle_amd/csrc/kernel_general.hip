@@ -107,6 +107,30 @@ __global__ void __launch_bounds__(GJ) general_kernel(Problem p, Strides st) {
         const int64_t qo = line + j * st.query;   // element offset of this query's D values
         const int64_t so = qo / D;                // offset in the [B, I, N, H] per-query arrays
         float* o = p.out + qo;
+        if (p.st_m && p.update && p.fin) {        // final step: the folded state, normalised
+            const float m0 = p.st_m[so], l0 = p.st_l[so];
+            float a0 = 1.0f, a1 = 0.0f, mm = m0;   // empty range: the old state as it is
+            if (l > 0.0f) {
+                a0 = 0.0f;
+                a1 = 1.0f;
+                mm = m;
+                if (l0 > 0.0f) {
+                    mm = fmaxf(m0, m);
+                    a0 = expf(m0 - mm);
+                    a1 = expf(m - mm);
+                }
+            }
+            const float ln = a0 * l0 + a1 * l;
+            float* f = p.fin + qo;
+#pragma unroll
+            for (int d = 0; d < DP; ++d)
+                if (d < D) {
+                    const float x = a0 == 0.0f ? a1 * acc[d] : fmaf(a0, o[d], a1 * acc[d]);
+                    f[d] = ln > 0.0f ? x / ln : 0.0f;
+                }
+            if (p.lse) p.lse[so] = ln > 0.0f ? mm + logf(ln) : -INFINITY;
+            return;
+        }
         if (p.st_m && p.update) {                 // fold into the running state (merge rule)
             const float m0 = p.st_m[so], l0 = p.st_l[so];
             if (l > 0.0f) {

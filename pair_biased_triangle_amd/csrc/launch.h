@@ -31,6 +31,8 @@ struct Problem {
     float* st_m = nullptr;  // state mode when non-null: reference (natural-log units) ...
     float* st_l = nullptr;  //   ... and normaliser of each query; out gets the accumulator
     bool update = false;    // state mode: fold into the state already in out, st_m, st_l
+    float* fin = nullptr;   // with update: write the folded result here as the final output
+                            // (fin = acc / l, lse = m + ln l) and leave the state untouched
     __host__ __device__ int64_t nkeys() const { return NK > 0 ? NK : N; }
 };
 

@@ -81,6 +81,7 @@ struct Call {
     float* st_m = nullptr;
     float* st_l = nullptr;
     bool update = false;                   // state mode: fold into the given state
+    float* fin = nullptr;                  // with update: final output (state only read)
     void* ws = nullptr;                    // caller workspace when ws_bytes >= 0
     int64_t ws_bytes = -1;
 };
@@ -93,18 +94,20 @@ struct Span {
 int check_pointers(const Call& c, int64_t qkv_elems, int64_t bias_elems) {
     if (!aligned(c.q, 16) || !aligned(c.k, 16) || !aligned(c.v, 16) || !aligned(c.bias, 16) || !aligned(c.out, 16) ||
         (c.mask && !aligned(c.mask, 4)) || (c.lse && !aligned(c.lse, 4)) || (c.st_m && !aligned(c.st_m, 4)) ||
-        (c.st_l && !aligned(c.st_l, 4)))
+        (c.st_l && !aligned(c.st_l, 4)) || (c.fin && !aligned(c.fin, 16)))
         return TRI_ATTN_ERR_ALIGN;
     const int64_t esz = c.dtype == TRI_ATTN_BF16 ? 2 : 4;
     const int64_t per_query = qkv_elems / c.D * 4;   // bytes of one fp32 value per query
     const Span inputs[] = {{c.q, qkv_elems * esz}, {c.k, qkv_elems * esz}, {c.v, qkv_elems * esz},
                            {c.bias, bias_elems * esz}, {c.mask, c.B * c.N * 4}};
-    const Span outputs[] = {{c.out, qkv_elems * 4}, {c.lse, per_query}, {c.st_m, per_query}, {c.st_l, per_query}};
-    for (int a = 0; a < 4; ++a) {
+    const Span outputs[] = {{c.out, qkv_elems * 4}, {c.lse, per_query}, {c.st_m, per_query}, {c.st_l, per_query},
+                            {c.fin, qkv_elems * 4}};
+    constexpr int n_out = 5;
+    for (int a = 0; a < n_out; ++a) {
         if (!outputs[a].p) continue;
         for (const Span& in : inputs)
             if (in.p && overlaps(outputs[a].p, outputs[a].bytes, in.p, in.bytes)) return TRI_ATTN_ERR_ALIAS;
-        for (int o = a + 1; o < 4; ++o)
+        for (int o = a + 1; o < n_out; ++o)
             if (outputs[o].p && overlaps(outputs[a].p, outputs[a].bytes, outputs[o].p, outputs[o].bytes))
                 return TRI_ATTN_ERR_ALIAS;
     }
@@ -120,6 +123,7 @@ tri_attn::Problem make_problem(const Call& c) {
     p.st_m = c.st_m;
     p.st_l = c.st_l;
     p.update = c.update;
+    p.fin = c.fin;
     return p;
 }
 
@@ -303,6 +307,24 @@ int tri_attn_tile_state_update(const void* q, const void* k, const void* v, cons
     return run(c, stream);
 }
 
+int tri_attn_tile_state_final(const void* q, const void* k, const void* v, const void* bias, const float* mask,
+                              const float* acc, const float* m, const float* l, float* out, float* lse, int64_t B,
+                              int64_t H, int64_t I, int64_t N, int64_t D, int64_t key_begin, int64_t key_end,
+                              int32_t ending, int32_t dtype, void* stream) {
+    if (!m || !l || !out) return TRI_ATTN_ERR_NULL;
+    // the state is only read here; the kernels take it through the state pointers
+    Call c = make_call(q, k, v, bias, mask, const_cast<float*>(acc), B, H, I, N, D, 1, dtype);
+    c.key_begin = key_begin;
+    c.key_end = key_end < 0 ? 0 : key_end;
+    c.ending = ending != 0;
+    c.st_m = const_cast<float*>(m);
+    c.st_l = const_cast<float*>(l);
+    c.update = true;
+    c.fin = out;
+    c.lse = lse;
+    return run(c, stream);
+}
+
 int tri_attn_state_merge(float* acc, float* m, float* l, const float* acc_t, const float* m_t, const float* l_t,
                          int64_t rows, int64_t D, void* stream) {
     int st = check_state_args(acc, m, l, rows, D);
@@ -406,6 +428,6 @@ const char* tri_attn_status_string(int status) {
 
 int tri_attn_last_hip_error(void) { return g_last_hip_error; }
 
-int tri_attn_version(void) { return 10300; }
+int tri_attn_version(void) { return 10400; }
 
 }  // extern "C"

@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.tri_attn_version() == 10300
+    assert lib.tri_attn_version() == 10400
     seen = set()
     codes = (OK, E_NULL, E_SHAPE, E_DTYPE, E_UNSUP, E_ALIGN, E_TILES, E_HIP, E_ALIAS, E_WS, E_RANGE)
     for code in codes:
@@ -259,6 +259,34 @@ def test_tile_state_errors(lib, entry):
     assert call_state(lib, m=L_) == E_ALIAS                               # m and l share memory
     assert call_state(lib, l=fake(0x10000000 * 6 + 128)) == E_ALIAS      # l inside acc
     assert call_state(lib, dtype=5) == E_DTYPE
+
+
+FOUT, FLSE = fake(0x10000000 * 20), fake(0x10000000 * 21)
+
+
+def call_final(lib, kb=0, ke=64, m=M_, l=L_, acc=OUT, out=FOUT, lse=None, I=64, ending=0, **kw):
+    return lib.tri_attn_tile_state_final(kw.get("q", Q), K, V, BIAS, None, acc, m, l, out, lse, 1, 4, I, 64, 32, kb, ke,
+                                         ending, kw.get("dtype", BF16), None)
+
+
+@pytest.mark.parametrize("kb,ke", [(-1, 10), (5, 5), (10, 5), (0, 65), (64, 70), (0, -1)])
+def test_tile_state_final_key_range(lib, kb, ke):
+    assert call_final(lib, kb=kb, ke=ke) == E_RANGE
+
+
+def test_tile_state_final_errors(lib):
+    assert call_final(lib, m=None) == E_NULL
+    assert call_final(lib, l=None) == E_NULL
+    assert call_final(lib, out=None) == E_NULL
+    assert call_final(lib, q=None) == E_NULL
+    assert call_final(lib, ending=1, I=32) == E_SHAPE
+    assert call_final(lib, out=fake(0x10000000 * 20 + 8)) == E_ALIGN        # out needs 16 bytes
+    assert call_final(lib, lse=fake(0x10000000 * 21 + 2)) == E_ALIGN
+    assert call_final(lib, out=fake(0x10000000 * 6 + 256)) == E_ALIAS       # out inside acc
+    assert call_final(lib, out=fake(0x10000000 + 4096)) == E_ALIAS          # out inside q
+    assert call_final(lib, lse=fake(0x10000000 * 9)) == E_ALIAS             # lse on m
+    assert call_final(lib, lse=fake(0x10000000 * 20 + 64)) == E_ALIAS       # lse inside out
+    assert call_final(lib, dtype=5) == E_DTYPE
 
 
 def test_state_merge_errors(lib):

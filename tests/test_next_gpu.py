@@ -217,6 +217,61 @@ def test_ring_by_state_updates(torch_dev, dtype, ending, N, I):
     compare_lse(lse.cpu().numpy(), ref_lse, TOL[dtype], "ring by updates lse")
 
 
+@pytest.mark.parametrize("dtype,ending,N,I", [("bf16", False, 97, 20), ("fp32", False, 97, 20), ("bf16", True, 97, 97),
+                                              ("fp32", True, 97, 97), ("bf16", False, 600, 12)])
+def test_ring_with_final_step(torch_dev, dtype, ending, N, I):
+    """The ring folded by updates except its last step, which tri_attn_tile_state_final
+    folds and finalises in one call: tri_attn_fwd's result and lse, with the state left
+    as it was.  The first range's keys are all masked for N = 97 (an empty step)."""
+    import pair_biased_triangle_amd as P
+    w = small(dtype, I=I, N=N, T=1, mask_last=4)
+    if N == 97:
+        w.mask[0, 0:13] = -np.inf
+    say(f"[next] ring with a final step {dtype} ending={ending} N={N}")
+    q, k, v, bias, mask = dev_inputs(torch_dev, w)
+    t = torch_dev
+    acc = t.full((1, I, N, 4, 32), 7.0, dtype=t.float32, device="cuda")    # not read while l = 0
+    m = t.full((1, I, N, 4), 3.0, dtype=t.float32, device="cuda")
+    l = t.zeros((1, I, N, 4), dtype=t.float32, device="cuda")
+    bounds = [0, 13, 45, 46, 93, N] if N == 97 else [0, 150, 151, 420, N]
+    order = [2, 4, 3, 1, 0] if N == 97 else [3, 1, 0, 2]
+    for tt in order[:-1]:
+        P.tri_attn_tile_state_update(q, k, v, bias, mask, key_begin=bounds[tt], key_end=bounds[tt + 1],
+                                     ending=ending, acc=acc, m=m, l=l)
+    state = [x.clone() for x in (acc, m, l)]
+    last = order[-1]
+    out, lse = P.tri_attn_tile_state_final(q, k, v, bias, mask, key_begin=bounds[last], key_end=bounds[last + 1],
+                                           ending=ending, acc=acc, m=m, l=l, want_lse=True)
+    t.cuda.synchronize()
+    assert all(t.equal(a, b) for a, b in zip(state, (acc, m, l))), "the final step wrote the state"
+    ref, ref_lse = oracle.tri_attn(w.q, w.k, w.v, w.bias, w.mask, ending=ending)
+    compare(out.cpu().numpy(), ref, TOL[dtype], "ring with a final step")
+    compare_lse(lse.cpu().numpy(), ref_lse, TOL[dtype], "ring with a final step, lse")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_final_step_from_empty_state(torch_dev, dtype):
+    """tri_attn_tile_state_final on the empty state (l = 0) over the whole key range is the
+    forward itself; over a fully masked range it gives out 0 and lse -inf."""
+    import pair_biased_triangle_amd as P
+    w = small(dtype, I=9, N=70, T=1, mask_last=10)
+    say(f"[next] final step from the empty state {dtype}")
+    q, k, v, bias, mask = dev_inputs(torch_dev, w)
+    t = torch_dev
+    acc = t.full((1, 9, 70, 4, 32), float("nan"), dtype=t.float32, device="cuda")   # never read while l = 0
+    m = t.full((1, 9, 70, 4), float("nan"), dtype=t.float32, device="cuda")
+    l = t.zeros((1, 9, 70, 4), dtype=t.float32, device="cuda")
+    out, lse = P.tri_attn_tile_state_final(q, k, v, bias, mask, key_begin=0, key_end=70, acc=acc, m=m, l=l,
+                                           want_lse=True)
+    o2, l2 = P.tri_attn_tile_state_final(q, k, v, bias, mask, key_begin=60, key_end=70, acc=acc, m=m, l=l,
+                                         want_lse=True)
+    t.cuda.synchronize()
+    ref, ref_lse = oracle.tri_attn(w.q, w.k, w.v, w.bias, w.mask)
+    compare(out.cpu().numpy(), ref, TOL[dtype], "final step from the empty state")
+    compare_lse(lse.cpu().numpy(), ref_lse, TOL[dtype], "final step from the empty state, lse")
+    assert t.all(o2 == 0) and t.all(t.isneginf(l2))
+
+
 @pytest.mark.parametrize("D,shift", [(24, 0), (6, 0), (24, 1)], ids=["vector", "D6_scalar", "offset_scalar"])
 def test_state_merge_and_finalize_kernels(torch_dev, D, shift):
     """The merge and finalisation kernels on random fp32 states (empty states mixed in)
