@@ -1008,16 +1008,9 @@ hipError_t launch_bias_image(const Problem& p, float* img, hipStream_t stream) {
     return hipGetLastError();
 }
 
-hipError_t launch_bf16_mfma(const Problem& p, void* workspace, hipStream_t stream) {
-    const FwdLayout Ly = fwd_layout(p);
-    const int64_t n_rg = Ly.n_rg;
-    const Strides sd = strides_of(p);
-    const int64_t total = Ly.wgs;
-    const int64_t n_qg = Ly.n_jb * (BJ / IMG16_Q);
-    // the 32 keys of a block are addressed with 32-bit byte offsets from the block's first key
-    if (total > 0x7FFFFFFF || Ly.nblk > 65535 || Ly.nqp / 4 > 0x7FFFFFFF || p.B * p.H > 65535 ||
-        BK * sd.key * 2 > 0x7FFFFFFF)
-        return hipErrorInvalidConfiguration;
+namespace {
+// The bias prepass: r_j (bias_ref_kernel), then the fp16 image (bias_image16_kernel).
+hipError_t launch_prepass(const Problem& p, const FwdLayout& Ly, void* workspace, int64_t n_qg, hipStream_t stream) {
     _Float16* img = static_cast<_Float16*>(workspace);
     float* ref = reinterpret_cast<float*>(static_cast<char*>(workspace) + Ly.ref_off);
     float* part = Ly.n_part > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + Ly.part_off) : ref;
@@ -1031,7 +1024,42 @@ hipError_t launch_bf16_mfma(const Problem& p, void* workspace, hipStream_t strea
                        dim3(static_cast<unsigned>(n_qg), static_cast<unsigned>((Ly.nblk + IMG16_NB - 1) / IMG16_NB), bhs),
                        dim3(256), 0, stream, p, part, Ly.n_part, img, ref, static_cast<int>(Ly.n_jb),
                        static_cast<int>(Ly.nblk));
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    return hipGetLastError();
+}
+}  // namespace
+
+Prepass16 prepass16_layout(const Problem& p) {
+    const FwdLayout L = fwd_layout(p);
+    Prepass16 q;
+    q.cols = BJ;
+    q.n_jb = L.n_jb;
+    q.nqp = L.nqp;
+    q.nblk = L.nblk;
+    q.ref_off = L.ref_off;
+    q.bytes = L.ref_off + static_cast<size_t>(p.B * p.H * L.nqp) * 4;
+    return q;
+}
+
+hipError_t launch_prepass16(const Problem& p, void* workspace, hipStream_t stream) {
+    if (p.ending || p.B * p.H > 65535 || fwd_layout(p).nblk > 65535) return hipErrorInvalidConfiguration;
+    const FwdLayout Ly = fwd_layout(p);
+    return launch_prepass(p, Ly, workspace, Ly.n_jb * (BJ / IMG16_Q), stream);
+}
+
+hipError_t launch_bf16_mfma(const Problem& p, void* workspace, hipStream_t stream) {
+    const FwdLayout Ly = fwd_layout(p);
+    const int64_t n_rg = Ly.n_rg;
+    const Strides sd = strides_of(p);
+    const int64_t total = Ly.wgs;
+    const int64_t n_qg = Ly.n_jb * (BJ / IMG16_Q);
+    // the 32 keys of a block are addressed with 32-bit byte offsets from the block's first key
+    if (total > 0x7FFFFFFF || Ly.nblk > 65535 || Ly.nqp / 4 > 0x7FFFFFFF || p.B * p.H > 65535 ||
+        BK * sd.key * 2 > 0x7FFFFFFF)
+        return hipErrorInvalidConfiguration;
+    _Float16* img = static_cast<_Float16*>(workspace);
+    float* ref = reinterpret_cast<float*>(static_cast<char*>(workspace) + Ly.ref_off);
+    hipError_t e = launch_prepass(p, Ly, workspace, n_qg, stream);
+    if (e != hipSuccess) return e;
     if (Ly.n_split == 1) {
         hipLaunchKernelGGL(bf16_mfma_kernel, dim3(static_cast<unsigned>(total)), dim3(NTHR), 0, stream, p, sd, img, ref,
                            static_cast<int>(Ly.n_jb), static_cast<int>(n_rg), static_cast<int>(Ly.nblk),

@@ -2,17 +2,25 @@
 // (the gradients of the definition; see kernel_backward.hip for the formulas and the
 // plain fp32 version used for every other case).
 //
-// Four kernels, each owning the sums it produces (no atomics, deterministic):
+// The bias reaches the kernels in two forms.  dq and dk/dv read it as fp16 relative to
+// each query's reference r_j (the forward's prepass, and bias_imageT16_kernel for its
+// transpose): x = (q.k + (r_j - lse) sqrt(D)) log2(e)/sqrt(D) + (bias + mask - r_j) log2(e)
+// is the score minus lse in log2 units, with (r_j - lse) sqrt(D) seeding the matrix
+// accumulator and the image taken by one v_fma_mix_f32.  dbias keeps the fp32 image
+// (bias + mask) sqrt(D) in registers for its whole loop.
+//
+// Kernels, each owning the sums it produces (no atomics, deterministic):
 //   bwd_prep_kernel   dout -> bf16 copy (the operand of the dP and dV products),
-//                     delta = dout . out per query, and delta and nb = -lse log2(e)
-//                     transposed to [b, i, h, j] (rows padded to whole 128-query tiles).
+//                     delta = dout . out per query, and delta, nb = -lse log2(e) and
+//                     nb' = (r_j - lse) sqrt(D) transposed to [b, i, h, j] (rows padded to
+//                     whole 128-query tiles).
 //   bwd_dq_lds        2 lines x 128 queries per workgroup, 32-key blocks streamed through
 //                     an LDS ring (the forward's shape):
-//                       S^T = K Q^T + C,  dP^T = V dO^T,  dS^T = P^T (dP^T - delta),
+//                       S^T = K Q^T + nb',  dP^T = V dO^T,  dS^T = P^T (dP^T - delta),
 //                       dQ^T += K^T dS^T
 //   bwd_dkdv_lds      2 lines x 128 keys per workgroup, 32-query blocks streamed, in the
 //                     orientation in which P and dS leave the accumulator as B operands:
-//                       S = Q K^T + C,  dP = dO V^T,  dV^T += dO^T P,  dK^T += Q^T dS
+//                       S = Q K^T + nb',  dP = dO V^T,  dV^T += dO^T P,  dK^T += Q^T dS
 //   bwd_dbias_lds     128 queries x 128 keys of one (b, h) per workgroup, rows i streamed:
 //                       dbias^T += dS^T of every row i (the bias is shared by all rows)
 // Every streaming kernel copies its operands straight from global memory into a ring of
@@ -37,6 +45,8 @@ typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int D = 32;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -60,6 +70,18 @@ __device__ __forceinline__ bf16x8 frag(const __bf16* base, int64_t off, bool ok)
 // 16-byte chunk `part` (d = 8*part .. +7) of tile row `row` sits at chunk kv_chunk(row, part)
 __host__ __device__ constexpr int kv_chunk(int row, int part) { return part ^ ((row >> 1) & 3); }
 
+// fp16 bias tiles (64-byte rows of 32 columns): the 32 columns of a row are stored in the
+// order of the 32x32 MFMA result registers, so a lane's 16 values are the two 16-byte parts
+// 2*h2 and 2*h2 + 1 of its row; position 8*part + t of a row holds column part_col(part, t)
+__host__ __device__ constexpr int part_col(int part, int t) {
+    return 8 * (2 * (part & 1) + (t >> 2)) + 4 * (part >> 1) + (t & 3);
+}
+// fp16 value of register r (0..15) of a lane from its two parts h0 (registers 0..7) and h1
+__device__ __forceinline__ float half_of(const u32x4& h0, const u32x4& h1, int r) {
+    const uint32_t word = (r < 8 ? h0 : h1)[(r & 7) >> 1];
+    return static_cast<float>(__builtin_bit_cast(f16x2, word)[r & 1]);
+}
+
 __device__ __forceinline__ void to_bf16(const f32x16& x, bf16x8& lo, bf16x8& hi) {
     lo = __builtin_convertvector(__builtin_shufflevector(x, x, 0, 1, 2, 3, 4, 5, 6, 7), bf16x8);
     hi = __builtin_convertvector(__builtin_shufflevector(x, x, 8, 9, 10, 11, 12, 13, 14, 15), bf16x8);
@@ -79,7 +101,8 @@ __device__ __forceinline__ float neg_lse2(float lse) { return lse == -INFINITY ?
 // queries only write the padding of the transposed rows.
 constexpr int PREP_PARTS = D / 4;
 __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdProblem p, __bf16* g16, float* delta, float* nbT,
-                                                       float* deltaT, int64_t NP) {
+                                                       float* deltaT, int64_t NP, const float* ref16, int64_t nqp16,
+                                                       float* nbT2) {
     const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
     const int64_t total = p.B * p.I * NP * p.H * PREP_PARTS;   // whole groups of 8 lanes
     if (t >= total) return;
@@ -104,7 +127,12 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdProblem p, __bf16* g16
         const int64_t tt = (line * p.H + h) * NP + j;   // [b, i, h, j]
         if (real) delta[q] = dl;
         deltaT[tt] = dl;
-        nbT[tt] = real ? neg_lse2(p.lse[q]) : -INFINITY;
+        const float lse = real ? p.lse[q] : -INFINITY;
+        nbT[tt] = neg_lse2(lse);
+        // (r_j - lse) sqrt(D): with the fp16 image relative to r_j, the score in log2 units is
+        // (q.k + this) * log2(e)/sqrt(D) + image
+        const int64_t b = line / p.I;
+        nbT2[tt] = lse == -INFINITY ? -INFINITY : (ref16[(b * p.H + h) * nqp16 + j] - lse) * kSqrtD;
     }
 }
 
@@ -114,17 +142,17 @@ __device__ __forceinline__ void db_barrier_drain() { asm volatile("s_waitcnt vmc
 
 // ---------------------------------------------------------------------------------------
 // dq, in the forward's shape: a workgroup of 4 waves owns DQ_R = 2 lines (rows i) x 128
-// query columns of one (b, h) and streams 32-key blocks through a ring of 3 LDS stages (K,
-// V of its lines and the 128 x 32 tile of the fp32 bias image, copied by
+// query columns of one (b, h) and streams 32-key blocks through a ring of 4 LDS stages of
+// 16 KB (K, V of its lines and its 128 rows of the forward's fp16 image tile, copied by
 // global_load_lds); two workgroups share a compute unit.  Wave w owns line w / 2 and query
 // tiles 2 (w % 2), +1; Q and dO of its queries stay in registers.  Per unit and block:
-//   S^T = K Q^T + C,  dP^T = V dO^T,  dS^T = P^T (dP^T - delta),  dQ^T += K^T dS^T
+//   S^T = K Q^T + nb',  dP^T = V dO^T,  dS^T = P^T (dP^T - delta),  dQ^T += K^T dS^T
 // with K^T read transposed from the staged [key][d] tile (ds_read_b64_tr_b16).
 #ifndef TRI_ATTN_DQ_WAVES
 #define TRI_ATTN_DQ_WAVES 4
 #endif
 #ifndef TRI_ATTN_DQ_STAGES
-#define TRI_ATTN_DQ_STAGES 3
+#define TRI_ATTN_DQ_STAGES 4
 #endif
 #ifndef TRI_ATTN_DQ_TILE_RG
 #define TRI_ATTN_DQ_TILE_RG 16
@@ -138,18 +166,18 @@ constexpr int DQ_TILE_JB = 4;
 struct DqStage {
     __bf16 k[DQ_R][32][D];     // 64-byte rows, 16-byte chunks swizzled by kv_chunk()
     __bf16 v[DQ_R][32][D];
-    float bias[IMG_BJ][IMG_BK];   // the image tile as stored: 128-byte rows, chunks img_chunk()
+    _Float16 bias[IMG_BJ][32];    // 128 queries of the fp16 image tile (relative to r_j) as stored
 };
 constexpr int DQ_STAGE_BYTES = static_cast<int>(sizeof(DqStage));
 constexpr int DQ_K_OFF = static_cast<int>(offsetof(DqStage, k));
 constexpr int DQ_V_OFF = static_cast<int>(offsetof(DqStage, v));
 constexpr int DQ_B_OFF = static_cast<int>(offsetof(DqStage, bias));
 constexpr int DQ_LINE_BYTES = 32 * D * 2;
-constexpr int DQ_CTILE_BYTES = 32 * IMG_BK * 4;
-constexpr int DQ_BIAS_PER_WAVE = IMG_BJ * IMG_BK * 4 / 1024 / DQ_WAVES;
+constexpr int DQ_CTILE_BYTES = 32 * 32 * 2;           // 32 query rows of the fp16 tile
+constexpr int DQ_BIAS_PER_WAVE = IMG_BJ * 32 * 2 / 1024 / DQ_WAVES;
 constexpr int DQ_COPIES = 2 + DQ_BIAS_PER_WAVE;   // global_load_lds per wave per block
-static_assert(DQ_LINE_BYTES == 2048 && DQ_CTILE_BYTES == 4096, "offsets below");
-static_assert(DQ_R * 2 * 2 == 2 * DQ_WAVES && DQ_BIAS_PER_WAVE * DQ_WAVES * 1024 == IMG_BJ * IMG_BK * 4,
+static_assert(DQ_LINE_BYTES == 2048 && DQ_CTILE_BYTES == 2048, "offsets below");
+static_assert(DQ_R * 2 * 2 == 2 * DQ_WAVES && DQ_BIAS_PER_WAVE * DQ_WAVES * 1024 == IMG_BJ * 32 * 2,
               "two K/V pieces and whole bias pieces per wave");
 __shared__ DqStage g_dq[DQ_STAGES];
 
@@ -158,7 +186,8 @@ struct DqCtx {
     uint32_t kv_lds[2];
     int key_local[2];
     int part_bytes[2];
-    const float* img_wg;       // this workgroup's image tiles, nblk consecutive 128 x 32 tiles
+    const _Float16* img_wg;    // this workgroup's 128 rows of the fp16 image tile of key block 0
+    int64_t img_blk;           // halves between the tiles of consecutive key blocks
     int64_t key_bytes;
     int last_key;
 };
@@ -172,7 +201,7 @@ __device__ __forceinline__ void dq_stage(const DqCtx& cx, int n, int wave, int l
         const char* src = cx.kv_row[t] + static_cast<int64_t>(kb) * cx.key_bytes + rel * cx.key_bytes + cx.part_bytes[t];
         __builtin_amdgcn_global_load_lds(GPTR(src), LPTR(lds + cx.kv_lds[t]), 16, 0, 0);
     }
-    const char* src = reinterpret_cast<const char*>(cx.img_wg + static_cast<int64_t>(n) * IMG_BJ * IMG_BK) + lane * 16;
+    const char* src = reinterpret_cast<const char*>(cx.img_wg + n * cx.img_blk) + lane * 16;
 #pragma unroll
     for (int t = 0; t < DQ_BIAS_PER_WAVE; ++t) {
         const int base = (DQ_BIAS_PER_WAVE * wave + t) * 1024;
@@ -187,8 +216,9 @@ __device__ __forceinline__ void dq_barrier_keep() {
     asm volatile("s_waitcnt vmcnt(%c0)\n\ts_barrier" ::"i"(keep) : "memory");
 }
 
-__global__ void __launch_bounds__(DQ_THR, 2) bwd_dq_lds(BwdProblem p, const float* img, const __bf16* g16,
-                                                     const float* delta, int n_jb, int n_rg, int nblk, int total) {
+__global__ void __launch_bounds__(DQ_THR, 2) bwd_dq_lds(BwdProblem p, const _Float16* img16, const float* ref16,
+                                                     Prepass16 pre, const __bf16* g16, const float* delta, int n_jb,
+                                                     int n_rg, int nblk, int total) {
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c = lane & 31, h2 = lane >> 5;
@@ -227,7 +257,11 @@ __global__ void __launch_bounds__(DQ_THR, 2) bwd_dq_lds(BwdProblem p, const floa
             cx.key_local[t] = 16 * t + (lane >> 2);
             cx.part_bytes[t] = kv_chunk(cx.key_local[t], lane & 3) * 16;
         }
-        cx.img_wg = img + (static_cast<int64_t>(bh) * n_jb + jb) * nblk * static_cast<int64_t>(IMG_BJ * IMG_BK);
+        // the prepass tiles hold pre.cols queries; this block's 128 are rows (jb % sub) * 128 on
+        const int sub = pre.cols / IMG_BJ;
+        cx.img_blk = static_cast<int64_t>(pre.cols) * 32;
+        cx.img_wg = img16 + (static_cast<int64_t>(bh) * pre.n_jb + jb / sub) * pre.nblk * cx.img_blk +
+                    (jb % sub) * IMG_BJ * 32;
         cx.last_key = static_cast<int>(N - 1);
     }
 
@@ -248,12 +282,14 @@ __global__ void __launch_bounds__(DQ_THR, 2) bwd_dq_lds(BwdProblem p, const floa
             gB[u][m] = frag(g16, qo + 16 * m + 8 * h2, ok);
         }
         const int64_t qi = ((b * I + i) * N + j) * H + h;
-        nb[u] = ok ? neg_lse2(p.lse[qi]) : -INFINITY;
+        const float lse = ok ? p.lse[qi] : -INFINITY;
+        // (r_j - lse) sqrt(D) seeds the score accumulator: see bwd_prep_kernel
+        nb[u] = lse == -INFINITY ? -INFINITY : (ref16[bh * pre.nqp + j] - lse) * kSqrtD;
         dl[u] = ok ? delta[qi] : 0.0f;
     }
     // LDS byte offsets (stage 0) of this lane's reads: K and V rows (A of S and dP), the
     // transposed K reads (A of dQ), the bias chunks of its first tile (second tile +4096)
-    uint32_t ak[2], at[4], ac[4];
+    uint32_t ak[2], at[4], ac[2];
 #pragma unroll
     for (int m = 0; m < 2; ++m) ak[m] = DQ_K_OFF + line * DQ_LINE_BYTES + c * 64 + kv_chunk(c, 2 * m + h2) * 16;
     {
@@ -267,8 +303,13 @@ __global__ void __launch_bounds__(DQ_THR, 2) bwd_dq_lds(BwdProblem p, const floa
             }
     }
 #pragma unroll
-    for (int a = 0; a < 4; ++a) ac[a] = DQ_B_OFF + t0 * DQ_CTILE_BYTES + c * 128 + img_chunk(c, 2 * a + h2) * 16;
+    for (int h = 0; h < 2; ++h) ac[h] = DQ_B_OFF + t0 * DQ_CTILE_BYTES + c * 64 + kv_chunk(c, 2 * h2 + h) * 16;
     const uint32_t st0 = LDS_ADDR(&g_dq[0]);
+    f32x16 nbs[2];                    // score accumulator seeds: (r_j - lse) sqrt(D) in every register
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) nbs[u][r] = nb[u];
 
     f32x16 dQ[2] = {};
     for (int n = 0; n < DQ_STAGES - 1 && n < nblk; ++n) dq_stage(cx, n, wave, lane);
@@ -280,49 +321,41 @@ __global__ void __launch_bounds__(DQ_THR, 2) bwd_dq_lds(BwdProblem p, const floa
         const uint32_t st = st0 + static_cast<uint32_t>(n % DQ_STAGES) * DQ_STAGE_BYTES;
         const bool issue = n + DQ_STAGES - 1 < nblk;
         if (issue) dq_stage(cx, n + DQ_STAGES - 1, wave, lane);
-        u32x4 kk[2], vv[2], cc[8];
+        u32x4 kk[2], vv[2], cc[4];
         u32x2 tt[4];
         asm volatile(
-            "ds_read_b128 %0, %16\n\t"
-            "ds_read_b128 %1, %17\n\t"
-            "ds_read_b128 %2, %16 offset:%c26\n\t"
-            "ds_read_b128 %3, %17 offset:%c26\n\t"
-            "ds_read_b64_tr_b16 %4, %18\n\t"
-            "ds_read_b64_tr_b16 %5, %19\n\t"
-            "ds_read_b64_tr_b16 %6, %20\n\t"
-            "ds_read_b64_tr_b16 %7, %21\n\t"
-            "ds_read_b128 %8, %22\n\t"
-            "ds_read_b128 %9, %23\n\t"
-            "ds_read_b128 %10, %24\n\t"
-            "ds_read_b128 %11, %25\n\t"
-            "ds_read_b128 %12, %22 offset:4096\n\t"
-            "ds_read_b128 %13, %23 offset:4096\n\t"
-            "ds_read_b128 %14, %24 offset:4096\n\t"
-            "ds_read_b128 %15, %25 offset:4096\n\t"
+            "ds_read_b128 %0, %12\n\t"
+            "ds_read_b128 %1, %13\n\t"
+            "ds_read_b128 %2, %12 offset:%c20\n\t"
+            "ds_read_b128 %3, %13 offset:%c20\n\t"
+            "ds_read_b64_tr_b16 %4, %14\n\t"
+            "ds_read_b64_tr_b16 %5, %15\n\t"
+            "ds_read_b64_tr_b16 %6, %16\n\t"
+            "ds_read_b64_tr_b16 %7, %17\n\t"
+            "ds_read_b128 %8, %18\n\t"
+            "ds_read_b128 %9, %19\n\t"
+            "ds_read_b128 %10, %18 offset:%c21\n\t"
+            "ds_read_b128 %11, %19 offset:%c21\n\t"
             "s_waitcnt lgkmcnt(0)"
             : "=&v"(kk[0]), "=&v"(kk[1]), "=&v"(vv[0]), "=&v"(vv[1]), "=&v"(tt[0]), "=&v"(tt[1]), "=&v"(tt[2]),
-              "=&v"(tt[3]), "=&v"(cc[0]), "=&v"(cc[1]), "=&v"(cc[2]), "=&v"(cc[3]), "=&v"(cc[4]), "=&v"(cc[5]),
-              "=&v"(cc[6]), "=&v"(cc[7])
+              "=&v"(tt[3]), "=&v"(cc[0]), "=&v"(cc[1]), "=&v"(cc[2]), "=&v"(cc[3])
             : "v"(st + ak[0]), "v"(st + ak[1]), "v"(st + at[0]), "v"(st + at[1]), "v"(st + at[2]), "v"(st + at[3]),
-              "v"(st + ac[0]), "v"(st + ac[1]), "v"(st + ac[2]), "v"(st + ac[3]), "i"(DQ_V_OFF - DQ_K_OFF));
+              "v"(st + ac[0]), "v"(st + ac[1]), "i"(DQ_V_OFF - DQ_K_OFF), "i"(DQ_CTILE_BYTES));
         bf16x8 kT[2];
 #pragma unroll
         for (int m = 0; m < 2; ++m)
             kT[m] = __builtin_bit_cast(bf16x8, u32x4{tt[2 * m][0], tt[2 * m][1], tt[2 * m + 1][0], tt[2 * m + 1][1]});
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-            f32x16 C;
-#pragma unroll
-            for (int a = 0; a < 4; ++a)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) C[4 * a + e] = __uint_as_float(cc[4 * u + a][e]);
-            f32x16 S = mfma(__builtin_bit_cast(bf16x8, kk[0]), qB[u][0], C);
+            f32x16 S = mfma(__builtin_bit_cast(bf16x8, kk[0]), qB[u][0], nbs[u]);
             S = mfma(__builtin_bit_cast(bf16x8, kk[1]), qB[u][1], S);
             f32x16 dP = mfma(__builtin_bit_cast(bf16x8, vv[0]), gB[u][0], f32x16{});
             dP = mfma(__builtin_bit_cast(bf16x8, vv[1]), gB[u][1], dP);
             f32x16 dS;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) dS[r] = __builtin_amdgcn_exp2f(fmaf(S[r], kScale, nb[u])) * (dP[r] - dl[u]);
+            for (int r = 0; r < 16; ++r)
+                dS[r] = __builtin_amdgcn_exp2f(fmaf(S[r], kScale, half_of(cc[2 * u], cc[2 * u + 1], r))) *
+                        (dP[r] - dl[u]);
             bf16x8 s0, s1;
             to_bf16(dS, s0, s1);
             dQ[u] = mfma(kT[0], s0, dQ[u]);
@@ -351,21 +384,20 @@ __global__ void __launch_bounds__(DQ_THR, 2) bwd_dq_lds(BwdProblem p, const floa
 
 // ---------------------------------------------------------------------------------------
 // dk, dv: a workgroup of 4 waves owns DK_R = 2 lines x 128 keys of one (b, h) and streams
-// 32-query blocks through a ring of 3 LDS stages (two workgroups per compute unit): Q and dO of its lines, the 128 x 32 tile
-// of imgT and nb = -lse log2(e), delta of the block's queries.  imgT is the bias image of
-// the transposed bias without the mask (built in the ending orientation): row kk of a tile
-// holds bias[b, h, q, key] sqrt(D) for 32 consecutive queries q (-inf past the last
-// query).  Wave w owns line w / 2 and key tiles 2 (w % 2), +1 (lane = key; K and V of its
-// keys stay in registers).  Per unit and block, in the orientation in which P and dS leave
-// the accumulator as the B operands of the next products:
-//   S = Q K^T + C,  dP = dO V^T,  dS = P (dP - delta),  dV^T += dO^T P,  dK^T += Q^T dS
+// 32-query blocks through a ring of 4 LDS stages (two workgroups per compute unit): Q and
+// dO of its lines, the 128 x 32 fp16 transposed tile (bias_imageT16_kernel: row = key, 32
+// queries, relative to each query's r_q) and nb' = (r_q - lse) sqrt(D), delta of the
+// block's queries.  Wave w owns line w / 2 and key tiles 2 (w % 2), +1 (lane = key; K and
+// V of its keys stay in registers).  Per unit and block, in the orientation in which P and
+// dS leave the accumulator as the B operands of the next products:
+//   S = Q K^T + nb',  dP = dO V^T,  dS = P (dP - delta),  dV^T += dO^T P,  dK^T += Q^T dS
 // with Q^T, dO^T read transposed from the staged [query][d] tiles.  A dropped key
 // (masked, or past the end) gets zero gradients.
 #ifndef TRI_ATTN_DK_WAVES
 #define TRI_ATTN_DK_WAVES 4
 #endif
 #ifndef TRI_ATTN_DK_STAGES
-#define TRI_ATTN_DK_STAGES 3
+#define TRI_ATTN_DK_STAGES 4
 #endif
 #ifndef TRI_ATTN_DK_TILE_RG
 #define TRI_ATTN_DK_TILE_RG 16
@@ -379,7 +411,7 @@ constexpr int DK_TILE_KB = 4;
 struct DkStage {
     __bf16 q[DK_R][32][D];        // 64-byte rows, 16-byte chunks swizzled by kv_chunk()
     __bf16 g[DK_R][32][D];        // dO rounded to bf16
-    float bias[IMG_BJ][IMG_BK];   // the imgT tile as stored: 128-byte rows, chunks img_chunk()
+    _Float16 bias[IMG_BJ][32];    // the fp16 transposed tile: row = key, 32 queries (part_col order)
     float nb[DK_R][32];
     float dl[DK_R][32];
 };
@@ -390,9 +422,9 @@ constexpr int DK_B_OFF = static_cast<int>(offsetof(DkStage, bias));
 constexpr int DK_N_OFF = static_cast<int>(offsetof(DkStage, nb));
 constexpr int DK_GQ = DK_G_OFF - DK_Q_OFF;                                     // dO tile after the Q tile
 constexpr int DK_DN = static_cast<int>(offsetof(DkStage, dl) - offsetof(DkStage, nb));   // delta rows after nb rows
-constexpr int DK_BIAS_PER_WAVE = IMG_BJ * IMG_BK * 4 / 1024 / DK_WAVES;
+constexpr int DK_BIAS_PER_WAVE = IMG_BJ * 32 * 2 / 1024 / DK_WAVES;
 constexpr int DK_COPIES = 2 + DK_BIAS_PER_WAVE + 1;   // Q/dO pieces, bias pieces, the nb or delta piece
-static_assert(DK_BIAS_PER_WAVE * DK_WAVES * 1024 == IMG_BJ * IMG_BK * 4 && 2 * DK_R == DK_WAVES, "pieces per wave");
+static_assert(DK_BIAS_PER_WAVE * DK_WAVES * 1024 == IMG_BJ * 32 * 2 && 2 * DK_R == DK_WAVES, "pieces per wave");
 __shared__ DkStage g_dk[DK_STAGES];
 
 // barrier after which every wave's copies except those of the DK_STAGES - 2 newest blocks are complete
@@ -407,7 +439,7 @@ struct DkCtx {
     uint32_t qg_lds[2];
     int q_local[2];
     int part_bytes[2];
-    const float* img_wg;       // this workgroup's imgT tiles, nqblk consecutive 128 x 32 tiles
+    const _Float16* img_wg;    // this workgroup's fp16 transposed tiles, nqblk consecutive 128 x 32 tiles
     const char* ls_src;        // nb or delta piece of query block 0 (lanes 0 .. 7)
     uint32_t ls_dst;
     int64_t q_bytes;
@@ -423,7 +455,7 @@ __device__ __forceinline__ void dk_stage(const DkCtx& cx, int n, int wave, int l
         const char* src = cx.qg_row[t] + static_cast<int64_t>(qb) * cx.q_bytes + rel * cx.q_bytes + cx.part_bytes[t];
         __builtin_amdgcn_global_load_lds(GPTR(src), LPTR(lds + cx.qg_lds[t]), 16, 0, 0);
     }
-    const char* src = reinterpret_cast<const char*>(cx.img_wg + static_cast<int64_t>(n) * IMG_BJ * IMG_BK) + lane * 16;
+    const char* src = reinterpret_cast<const char*>(cx.img_wg + static_cast<int64_t>(n) * IMG_BJ * 32) + lane * 16;
 #pragma unroll
     for (int t = 0; t < DK_BIAS_PER_WAVE; ++t) {
         const int base = (DK_BIAS_PER_WAVE * wave + t) * 1024;
@@ -432,8 +464,8 @@ __device__ __forceinline__ void dk_stage(const DkCtx& cx, int n, int wave, int l
     if (lane < 8) __builtin_amdgcn_global_load_lds(GPTR(cx.ls_src + qb * 4), LPTR(lds + cx.ls_dst), 16, 0, 0);
 }
 
-__global__ void __launch_bounds__(DK_THR, 2) bwd_dkdv_lds(BwdProblem p, const float* imgT, const __bf16* g16,
-                                                       const float* nbT, const float* deltaT, int n_kb, int n_rg,
+__global__ void __launch_bounds__(DK_THR, 2) bwd_dkdv_lds(BwdProblem p, const _Float16* imgT16, const __bf16* g16,
+                                                       const float* nbT2, const float* deltaT, int n_kb, int n_rg,
                                                        int nqblk, int64_t NP, int total) {
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -470,11 +502,11 @@ __global__ void __launch_bounds__(DK_THR, 2) bwd_dkdv_lds(BwdProblem p, const fl
             cx.q_local[t] = 16 * t + (lane >> 2);
             cx.part_bytes[t] = kv_chunk(cx.q_local[t], lane & 3) * 16;
         }
-        cx.img_wg = imgT + (static_cast<int64_t>(bh) * n_kb + kb) * nqblk * static_cast<int64_t>(IMG_BJ * IMG_BK);
+        cx.img_wg = imgT16 + (static_cast<int64_t>(bh) * n_kb + kb) * nqblk * static_cast<int64_t>(IMG_BJ * 32);
         // nb of line w (w < DK_R) or delta of line w - DK_R, 32 floats of the block in lanes 0 .. 7
         int64_t il = i0 + wave % DK_R;
         il = il < I ? il : I - 1;
-        cx.ls_src = reinterpret_cast<const char*>((wave < DK_R ? nbT : deltaT) + ((b * I + il) * H + h) * NP + 4 * (lane & 7));
+        cx.ls_src = reinterpret_cast<const char*>((wave < DK_R ? nbT2 : deltaT) + ((b * I + il) * H + h) * NP + 4 * (lane & 7));
         cx.ls_dst = DK_N_OFF + 128 * wave;
         cx.last_q = static_cast<int>(N - 1);
     }
@@ -498,7 +530,7 @@ __global__ void __launch_bounds__(DK_THR, 2) bwd_dkdv_lds(BwdProblem p, const fl
     // LDS byte offsets (stage 0) of this lane's reads: Q and dO rows (A of S and dP), the
     // transposed reads of Q and dO (A of dK, dV), the bias chunks of its first key tile
     // (second tile +4096), and nb / delta of its 16 query rows 8a + 4 h2 + e
-    uint32_t aq[2], at[4], ac[4];
+    uint32_t aq[2], at[4], ac[2];
 #pragma unroll
     for (int m = 0; m < 2; ++m) aq[m] = DK_Q_OFF + line * 2048 + c * 64 + kv_chunk(c, 2 * m + h2) * 16;
     {
@@ -512,7 +544,7 @@ __global__ void __launch_bounds__(DK_THR, 2) bwd_dkdv_lds(BwdProblem p, const fl
             }
     }
 #pragma unroll
-    for (int a = 0; a < 4; ++a) ac[a] = DK_B_OFF + t0 * 4096 + c * 128 + img_chunk(c, 2 * a + h2) * 16;
+    for (int h = 0; h < 2; ++h) ac[h] = DK_B_OFF + t0 * 2048 + c * 64 + kv_chunk(c, 2 * h2 + h) * 16;
     const uint32_t an = DK_N_OFF + line * 128 + 16 * h2;
     const uint32_t st0 = LDS_ADDR(&g_dk[0]);
 
@@ -563,21 +595,19 @@ __global__ void __launch_bounds__(DK_THR, 2) bwd_dkdv_lds(BwdProblem p, const fl
         }
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-            u32x4 cc[4];
+            u32x4 cc[2];
             asm volatile(
-                "ds_read_b128 %0, %4\n\t"
-                "ds_read_b128 %1, %5\n\t"
-                "ds_read_b128 %2, %6\n\t"
-                "ds_read_b128 %3, %7\n\t"
+                "ds_read_b128 %0, %2\n\t"
+                "ds_read_b128 %1, %3\n\t"
                 "s_waitcnt lgkmcnt(0)"
-                : "=&v"(cc[0]), "=&v"(cc[1]), "=&v"(cc[2]), "=&v"(cc[3])
-                : "v"(st + ac[0] + 4096 * u), "v"(st + ac[1] + 4096 * u), "v"(st + ac[2] + 4096 * u),
-                  "v"(st + ac[3] + 4096 * u));
+                : "=&v"(cc[0]), "=&v"(cc[1])
+                : "v"(st + ac[0] + 2048 * u), "v"(st + ac[1] + 2048 * u));
+            // the score accumulator starts from (r_q - lse) sqrt(D) of each query row
             f32x16 S;
 #pragma unroll
             for (int a = 0; a < 4; ++a)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) S[4 * a + e] = __uint_as_float(cc[a][e]);
+                for (int e = 0; e < 4; ++e) S[4 * a + e] = __uint_as_float(nn[a][e]);
             S = mfma(__builtin_bit_cast(bf16x8, qq[0]), kB[u][0], S);
             S = mfma(__builtin_bit_cast(bf16x8, qq[1]), kB[u][1], S);
             f32x16 dP = mfma(__builtin_bit_cast(bf16x8, gg[0]), vB[u][0], f32x16{});
@@ -588,7 +618,7 @@ __global__ void __launch_bounds__(DK_THR, 2) bwd_dkdv_lds(BwdProblem p, const fl
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = 4 * a + e;
-                    S[r] = __builtin_amdgcn_exp2f(fmaf(S[r], kScale, __uint_as_float(nn[a][e])));
+                    S[r] = __builtin_amdgcn_exp2f(fmaf(S[r], kScale, half_of(cc[0], cc[1], r)));
                     dP[r] = S[r] * (dP[r] - __uint_as_float(dd[a][e]));
                 }
             bf16x8 p0, p1, s0, s1;
@@ -846,26 +876,64 @@ __global__ void __launch_bounds__(DB_THR) bwd_dbias_lds(BwdProblem p, const floa
 }  // namespace
 
 namespace {
+// fp16 transposed bias tile of dk/dv: per (b, h, key tile kt of 128 keys, query block n of
+// 32 queries) a 128 x 32 tile at ((b*H + h) * n_kt + kt) * nqb + n; row kk is key
+// 128 kt + kk, its 32 queries q in part_col order with 16-byte parts swizzled by kv_chunk,
+// each value (bias[b, h, q, key] + mask[b, key] - r_q) log2(e) relative to the query's r_q
+// (the forward prepass's reference), -inf past the last key or query.  A thread owns one
+// key and two parts; the 128 threads of a part read 128 consecutive keys of one bias row.
+__global__ void __launch_bounds__(256) bias_imageT16_kernel(BwdProblem p, const float* ref16, int64_t nqp16,
+                                                            _Float16* out, int n_kt, int nqb) {
+    const int tile = blockIdx.x, n = tile % nqb, kt = tile / nqb;
+    const int64_t bh = blockIdx.y, b = bh / p.H;
+    const int t = threadIdx.x, kk = t & 127;
+    const int64_t key = static_cast<int64_t>(kt) * IMG_BJ + kk;
+    const bool kok = key < p.N;
+    const uint16_t* bias = static_cast<const uint16_t*>(p.bias);
+    const float mk = (kok && p.mask) ? p.mask[b * p.N + key] : 0.0f;
+    _Float16* dst = out + ((bh * n_kt + kt) * nqb + n) * static_cast<int64_t>(IMG_BJ * 32) + kk * 32;
+#pragma unroll
+    for (int pi = 0; pi < 2; ++pi) {
+        const int part = (t >> 7) + 2 * pi;
+        f16x8 v;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int64_t q = static_cast<int64_t>(n) * 32 + part_col(part, e);
+            float x = -INFINITY;
+            if (kok && q < p.N) {
+                const float bv = __uint_as_float(static_cast<uint32_t>(bias[(bh * p.N + q) * p.N + key]) << 16);
+                x = (bv + mk - ref16[bh * nqp16 + q]) * kLog2e;
+            }
+            v[e] = static_cast<_Float16>(x);
+        }
+        *reinterpret_cast<f16x8*>(dst + kv_chunk(kk, part) * 8) = v;
+    }
+}
+
 struct BwdLayout {
-    Problem fwd, tr;        // image problems: the bias, and its transpose without the mask
+    Problem fwd;            // the image problem: the bias and mask over all keys
+    Prepass16 pre;          // the forward's prepass: fp16 image and r_j (dq, dk/dv)
     int64_t NP, nq;
-    size_t img, imgT, g16, delta, nbT, deltaT, total;   // byte offsets / total
+    size_t img, pre16, imgT16, g16, delta, nbT, nbT2, deltaT, total;   // byte offsets / total
 };
 
 BwdLayout bwd_layout(const BwdProblem& p) {
     BwdLayout L;
     L.fwd = Problem{p.q, p.k, p.v, p.bias, p.mask, nullptr, p.B, p.H, p.I, p.N, p.D, 1};
-    L.tr = Problem{p.q, p.k, p.v, p.bias, nullptr, nullptr, p.B, p.H, p.N, p.N, p.D, 1};
-    L.tr.ending = true;
+    L.pre = prepass16_layout(L.fwd);
     L.NP = (p.N + NP_ALIGN - 1) / NP_ALIGN * NP_ALIGN;
     L.nq = p.B * p.I * p.N * p.H;
     const size_t per_line = static_cast<size_t>(p.B * p.I * p.H * L.NP) * 4;
+    const int64_t n_kt = (p.N + IMG_BJ - 1) / IMG_BJ, nqb = (p.N + 31) / 32;
+    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
     L.img = 0;
-    L.imgT = L.img + bias_image_bytes(L.fwd);
-    L.g16 = L.imgT + bias_image_bytes(L.tr);
-    L.delta = L.g16 + static_cast<size_t>(L.nq) * D * 2;
-    L.nbT = L.delta + (static_cast<size_t>(L.nq) * 4 + 15) / 16 * 16;
-    L.deltaT = L.nbT + per_line;
+    L.pre16 = up(L.img + bias_image_bytes(L.fwd));
+    L.imgT16 = up(L.pre16 + L.pre.bytes);
+    L.g16 = up(L.imgT16 + static_cast<size_t>(p.B * p.H * n_kt * nqb) * IMG_BJ * 32 * 2);
+    L.delta = up(L.g16 + static_cast<size_t>(L.nq) * D * 2);
+    L.nbT = up(L.delta + static_cast<size_t>(L.nq) * 4);
+    L.nbT2 = L.nbT + per_line;
+    L.deltaT = L.nbT2 + per_line;
     L.total = L.deltaT + per_line;
     return L;
 }
@@ -879,25 +947,35 @@ hipError_t launch_backward_mfma(const BwdProblem& p, void* workspace, hipStream_
     const int64_t nblk = bias_image_blocks(Ly.fwd);      // 32-key blocks
     char* ws = static_cast<char*>(workspace);
     float* img = reinterpret_cast<float*>(ws + Ly.img);
-    float* imgT = reinterpret_cast<float*>(ws + Ly.imgT);
+    _Float16* img16 = reinterpret_cast<_Float16*>(ws + Ly.pre16);
+    const float* ref16 = reinterpret_cast<const float*>(ws + Ly.pre16 + Ly.pre.ref_off);
+    _Float16* imgT16 = reinterpret_cast<_Float16*>(ws + Ly.imgT16);
     __bf16* g16 = reinterpret_cast<__bf16*>(ws + Ly.g16);
     float* delta = reinterpret_cast<float*>(ws + Ly.delta);
     float* nbT = reinterpret_cast<float*>(ws + Ly.nbT);
+    float* nbT2 = reinterpret_cast<float*>(ws + Ly.nbT2);
     float* deltaT = reinterpret_cast<float*>(ws + Ly.deltaT);
     const int64_t n_prep = p.B * p.I * p.H * Ly.NP * PREP_PARTS;
-    if (p.D != D || (n_prep + 255) / 256 > 0x7FFFFFFF || (p.N + 63) / 64 > 65535) return hipErrorInvalidConfiguration;
-    hipError_t e = launch_bias_image(Ly.fwd, img, stream);
+    const int64_t n_kt = (p.N + IMG_BJ - 1) / IMG_BJ, nqb = (p.N + 31) / 32;
+    if (p.D != D || (n_prep + 255) / 256 > 0x7FFFFFFF || (p.N + 63) / 64 > 65535 || n_kt * nqb > 0x7FFFFFFF ||
+        p.B * p.H > 65535 || Ly.pre.cols % IMG_BJ != 0)
+        return hipErrorInvalidConfiguration;
+    hipError_t e = launch_prepass16(Ly.fwd, ws + Ly.pre16, stream);
     if (e != hipSuccess) return e;
-    if ((e = launch_bias_image(Ly.tr, imgT, stream)) != hipSuccess) return e;
+    if ((e = launch_bias_image(Ly.fwd, img, stream)) != hipSuccess) return e;
+    hipLaunchKernelGGL(bias_imageT16_kernel, dim3(static_cast<unsigned>(n_kt * nqb), static_cast<unsigned>(p.B * p.H)),
+                       dim3(256), 0, stream, p, ref16, Ly.pre.nqp, imgT16, static_cast<int>(n_kt),
+                       static_cast<int>(nqb));
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(bwd_prep_kernel, dim3(static_cast<unsigned>((n_prep + 255) / 256)), dim3(256), 0, stream, p, g16,
-                       delta, nbT, deltaT, Ly.NP);
+                       delta, nbT, deltaT, Ly.NP, ref16, Ly.pre.nqp, nbT2);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     {
         const int64_t n_rg = (p.I + DQ_R - 1) / DQ_R;
         const int64_t total = n_jb * n_rg * p.B * p.H;
         if (total > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-        hipLaunchKernelGGL(bwd_dq_lds, dim3(static_cast<unsigned>(total)), dim3(DQ_THR), 0, stream, p, img, g16, delta,
-                           static_cast<int>(n_jb), static_cast<int>(n_rg), static_cast<int>(nblk),
+        hipLaunchKernelGGL(bwd_dq_lds, dim3(static_cast<unsigned>(total)), dim3(DQ_THR), 0, stream, p, img16, ref16,
+                           Ly.pre, g16, delta, static_cast<int>(n_jb), static_cast<int>(n_rg), static_cast<int>(nblk),
                            static_cast<int>(total));
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
@@ -905,8 +983,8 @@ hipError_t launch_backward_mfma(const BwdProblem& p, void* workspace, hipStream_
         const int64_t n_rg = (p.I + DK_R - 1) / DK_R;
         const int64_t total = n_jb * n_rg * p.B * p.H;
         if (total > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-        hipLaunchKernelGGL(bwd_dkdv_lds, dim3(static_cast<unsigned>(total)), dim3(DK_THR), 0, stream, p, imgT, g16, nbT,
-                           deltaT, static_cast<int>(n_jb), static_cast<int>(n_rg), static_cast<int>(nblk), Ly.NP,
+        hipLaunchKernelGGL(bwd_dkdv_lds, dim3(static_cast<unsigned>(total)), dim3(DK_THR), 0, stream, p, imgT16, g16,
+                           nbT2, deltaT, static_cast<int>(n_jb), static_cast<int>(n_rg), static_cast<int>(nblk), Ly.NP,
                            static_cast<int>(total));
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }

@@ -71,6 +71,20 @@ hipError_t launch_backward(const BwdProblem& p, bool bf16, hipStream_t stream);
 size_t bf16_workspace_bytes(const Problem& p);
 hipError_t launch_bf16_mfma(const Problem& p, void* workspace, hipStream_t stream);
 
+// The forward's bias prepass on its own (starting orientation, the call's whole key range),
+// for the backward: into `workspace` (bytes long, 256-byte aligned) the fp16 image of
+// (bias + mask - r_j) * log2(e), one cols x 32 tile per (b, h, column block jb, key block n)
+// at ((b*H + h) * n_jb + jb) * nblk + n (row jj = query jb*cols + jj, its 32 keys in the
+// matrix-core register order, 16-byte parts swizzled by row), then r_j as fp32 at
+// ref_off + ((b*H + h) * nqp + j) * 4 (nqp = n_jb * cols).
+struct Prepass16 {
+    size_t ref_off, bytes;
+    int64_t n_jb, nqp, nblk;
+    int cols;
+};
+Prepass16 prepass16_layout(const Problem& p);
+hipError_t launch_prepass16(const Problem& p, void* workspace, hipStream_t stream);
+
 // The fp32 bias image of the backward kernels.  Layout: per (b, h), column block jb of IMG_BJ query columns
 // and key block n (keys 32n .. 32n + 31 of the call's range), one IMG_BJ x IMG_BK
 // fp32 tile at img + ((b*H + h) * n_jb + jb) * nblk + n) * IMG_BJ * IMG_BK holding
