@@ -658,19 +658,21 @@ __global__ void __launch_bounds__(DK_THR, 2) bwd_dkdv_lds(BwdProblem p, const _F
 
 // ---------------------------------------------------------------------------------------
 // dbias[b, h, j, k] = sum over the rows i held of dS[i, j, k].  A workgroup of 8 waves owns
-// DB_Q = 128 queries x DB_K = 128 keys of one (b, h) and streams the rows i through a ring
+// DB_Q = 256 queries x DB_K = 128 keys of one (b, h) and streams the rows i through a ring
 // of LDS stages: per row the waves copy Q, dO (its queries), K, V (its keys), lse and delta
 // straight from global memory into a stage (global_load_lds_dwordx4), and wave w computes
-// queries 32 (w % 4) .. +31 against keys 64 (w / 4) .. +63 (two 32 x 32 units) from LDS:
+// queries 64 (w % 4) .. +63 against keys 64 (w / 4) .. +63 (four 32 x 32 units) from LDS:
 //   S^T = K Q^T + C,  dP^T = V dO^T,  acc += P^T (dP^T - delta)
-// The bias tile C stays in registers for the whole loop.  Every sum over i runs in one
-// lane in row order: deterministic.
-constexpr int DB_Q = 128;
+// Four units per wave and row keep the per-row costs (the barrier, the LDS round trip that
+// all waves start together after it) small against the work.  The bias tiles C stay in
+// registers for the whole loop.  Every sum over i runs in one lane in row order:
+// deterministic.
+constexpr int DB_Q = 256;
 constexpr int DB_K = 128;
 constexpr int DB_WAVES = 8;
 constexpr int DB_THR = 64 * DB_WAVES;
 #ifndef TRI_ATTN_DB_STAGES
-#define TRI_ATTN_DB_STAGES 4
+#define TRI_ATTN_DB_STAGES 3
 #endif
 constexpr int DB_STAGES = TRI_ATTN_DB_STAGES;
 #ifndef TRI_ATTN_DB_TILE_J
@@ -681,16 +683,16 @@ constexpr int DB_STAGES = TRI_ATTN_DB_STAGES;
 #endif
 constexpr int DB_TILE_J = TRI_ATTN_DB_TILE_J;   // query tiles x key tiles one XCD works on together
 constexpr int DB_TILE_K = TRI_ATTN_DB_TILE_K;
-constexpr int NP_ALIGN = 128;                   // lse / delta rows padded to whole query tiles
-static_assert(DB_Q % NP_ALIGN == 0 || NP_ALIGN % DB_Q == 0, "a query tile never crosses the padding");
+constexpr int NP_ALIGN = 256;                   // lse / delta rows padded to whole query tiles
+static_assert(NP_ALIGN % DB_Q == 0 && NP_ALIGN % 128 == 0, "a query tile never crosses the padding");
 
 struct DbStage {
     __bf16 q[DB_Q][D];     // 64-byte rows, 16-byte chunks swizzled by kv_chunk()
     __bf16 g[DB_Q][D];     // dO rounded to bf16
     __bf16 k[DB_K][D];
     __bf16 v[DB_K][D];
-    float lse[DB_Q];
-    float dl[DB_Q];
+    float lse[DB_Q];       // nb = -lse log2(e)
+    float dl[DB_Q];        // delta
 };
 constexpr int DB_STAGE_BYTES = static_cast<int>(sizeof(DbStage));
 constexpr int DB_Q_OFF = static_cast<int>(offsetof(DbStage, q));
@@ -698,40 +700,67 @@ constexpr int DB_G_OFF = static_cast<int>(offsetof(DbStage, g));
 constexpr int DB_K_OFF = static_cast<int>(offsetof(DbStage, k));
 constexpr int DB_V_OFF = static_cast<int>(offsetof(DbStage, v));
 constexpr int DB_L_OFF = static_cast<int>(offsetof(DbStage, lse));
-// per wave and row: 4 pieces of 1 KB (16 rows of Q, dO, K or V) and 128 bytes of lse / delta
-constexpr int DB_COPIES = 5;
-static_assert(4 * DB_WAVES * 1024 == 4 * DB_Q * D * 2 && DB_Q == DB_K, "pieces of the four tensors");
-static_assert(DB_WAVES * 128 == 2 * DB_Q * 4, "lse / delta pieces");
+constexpr int DB_DL_OFF = static_cast<int>(offsetof(DbStage, dl));
+constexpr int DB_PQ = DB_Q * D * 2 / 1024;      // 1 KB pieces of Q (and of dO)
+constexpr int DB_PK = DB_K * D * 2 / 1024;      // 1 KB pieces of K (and of V)
+constexpr int DB_PIECES = (2 * DB_PQ + 2 * DB_PK) / DB_WAVES;   // per wave and row
+constexpr int DB_COPIES = DB_PIECES + 1;                        // + 256 bytes of lse or delta
+static_assert(DB_PIECES * DB_WAVES == 2 * DB_PQ + 2 * DB_PK, "whole pieces per wave");
+static_assert(DB_WAVES * 256 == 2 * DB_Q * 4, "lse / delta: 256 bytes per wave");
+static_assert(DB_STAGES >= 3 && DB_STAGES * sizeof(DbStage) <= 160 * 1024, "LDS ring");
+static_assert(DB_COPIES * (DB_STAGES - 2) <= 63, "vmcnt range");
+// offsets written into the operand reads below
+static_assert(DB_V_OFF - DB_K_OFF == 8192 && DB_G_OFF - DB_Q_OFF == 16384 && DB_DL_OFF - DB_L_OFF == 1024,
+              "stage layout of the dbias operand reads");
 __shared__ DbStage g_db[DB_STAGES];
 
-
+// Copy sources are a wave-uniform base (the piece's first row at row i = 0) plus a 32-bit
+// lane offset, the same for every piece (row lane / 4 of the piece, its swizzled part), so
+// the copies take the scalar-base address form; a piece that runs past the last position
+// (the last tile) takes per-lane offsets clamped to it.
 struct DbCtx {
-    const char* src[4];        // this wave's four pieces: row base of (b, i = 0, pos, h), part applied
-    uint32_t dst[4];           // byte offset of each piece inside a stage
-    int64_t row_step;          // bytes between rows i of one tensor
-    const char* ls_src;        // lse / delta piece of row 0 (lanes 0 .. 7), or null
-    int64_t ls_step;           // bytes between rows i of nbT
+    const char* src[DB_PIECES];   // this wave's pieces: (b, i = 0, first row of the piece, h)
+    int64_t first[DB_PIECES];     // position of the piece's first row
+    uint32_t dst[DB_PIECES];      // byte offset of each piece inside a stage
+    uint32_t off;                 // this lane's offset inside a piece
+    int64_t N, pos_bytes;         // positions, bytes between consecutive positions
+    int64_t row_step;             // bytes between rows i of one tensor
+    const char* ls_src;           // lse / delta piece of row 0 (lanes 0 .. 15)
+    int64_t ls_step;              // bytes between rows i of nbT
     uint32_t ls_dst;
 };
 
 __device__ __forceinline__ void db_stage(const DbCtx& cx, int64_t i, int slot, int lane) {
     char* base = reinterpret_cast<char*>(&g_db[slot]);
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
-        __builtin_amdgcn_global_load_lds(GPTR(cx.src[t] + i * cx.row_step), LPTR(base + cx.dst[t]), 16, 0, 0);
-    if (lane < 8) __builtin_amdgcn_global_load_lds(GPTR(cx.ls_src + i * cx.ls_step), LPTR(base + cx.ls_dst), 16, 0, 0);
+    for (int t = 0; t < DB_PIECES; ++t) {
+        const char* row = cx.src[t] + i * cx.row_step;
+        if (cx.first[t] + 15 < cx.N) {
+            uint32_t off = cx.off;
+            asm volatile("" : "+v"(off));
+            __builtin_amdgcn_global_load_lds(GPTR(row + off), LPTR(base + cx.dst[t]), 16, 0, 0);
+        } else {                             // padded rows read the last real one (a 64-bit address:
+            const int64_t pos = min(cx.first[t] + (lane >> 2), cx.N - 1);   // the piece may start past it)
+            __builtin_amdgcn_global_load_lds(GPTR(row + (pos - cx.first[t]) * cx.pos_bytes + (cx.off % 64)),
+                                             LPTR(base + cx.dst[t]), 16, 0, 0);
+        }
+    }
+    if (lane < 16) {
+        uint32_t off = static_cast<uint32_t>(lane * 16);
+        asm volatile("" : "+v"(off));
+        __builtin_amdgcn_global_load_lds(GPTR(cx.ls_src + i * cx.ls_step + off), LPTR(base + cx.ls_dst), 16, 0, 0);
+    }
 }
 
+// Barrier after which every wave's copies except those of the DB_STAGES - 2 newest rows
+// are complete; with `drain`, all of them.
 __device__ __forceinline__ void db_barrier_keep() {
-    static_assert(DB_STAGES == 3 || DB_STAGES == 4, "three or four stages");
-    static_assert(DB_COPIES == 5, "vmcnt below: the copies of the DB_STAGES - 2 newest rows stay in flight");
-    if constexpr (DB_STAGES == 3) asm volatile("s_waitcnt vmcnt(5)\n\ts_barrier" ::: "memory");
-    if constexpr (DB_STAGES == 4) asm volatile("s_waitcnt vmcnt(10)\n\ts_barrier" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(%c0)\n\ts_barrier" ::"i"(DB_COPIES * (DB_STAGES - 2)) : "memory");
 }
 
 __global__ void __launch_bounds__(DB_THR) bwd_dbias_lds(BwdProblem p, const float* img, const __bf16* g16,
                                                         const float* nbT, const float* deltaT, int n_jb, int nblk,
-                                                        int64_t NP, int n_t, int total) {
+                                                        int64_t NP, int n_tq, int n_tk, int total) {
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c = lane & 31, h2 = lane >> 5;
@@ -741,13 +770,13 @@ __global__ void __launch_bounds__(DB_THR) bwd_dbias_lds(BwdProblem p, const floa
     const int xcd = w % 8, slot = w / 8;
     const int base = total / 8, extra = total % 8;
     const int logical = xcd * base + (xcd < extra ? xcd : extra) + slot;
-    const int bh = logical / (n_t * n_t);
-    const int rem = logical - bh * n_t * n_t;
-    const int strip = rem / (DB_TILE_J * n_t);
-    const int nr = min(DB_TILE_J, n_t - strip * DB_TILE_J);
-    const int o = rem - strip * DB_TILE_J * n_t;
+    const int bh = logical / (n_tq * n_tk);
+    const int rem = logical - bh * n_tq * n_tk;
+    const int strip = rem / (DB_TILE_J * n_tk);
+    const int nr = min(DB_TILE_J, n_tq - strip * DB_TILE_J);
+    const int o = rem - strip * DB_TILE_J * n_tk;
     const int tile = o / (nr * DB_TILE_K);
-    const int nk = min(DB_TILE_K, n_t - tile * DB_TILE_K);
+    const int nk = min(DB_TILE_K, n_tk - tile * DB_TILE_K);
     const int o2 = o - tile * nr * DB_TILE_K;
     const int jt = strip * DB_TILE_J + o2 / nk;
     const int kt = tile * DB_TILE_K + o2 % nk;
@@ -757,36 +786,43 @@ __global__ void __launch_bounds__(DB_THR) bwd_dbias_lds(BwdProblem p, const floa
 
     DbCtx cx;
     {
-        // piece pi = 4 w + t: tensor pi / 8 (Q, dO, K, V), rows 16 (pi % 8) .. +15; lane l
-        // carries row l / 4, 16-byte slot l % 4, which holds logical part kv_chunk(row, slot)
+        // piece pi = DB_PIECES w + t: Q pieces first, then dO, K, V; piece rows 16 (local) ..
+        // +15; lane l carries row l / 4, 16-byte slot l % 4, which holds logical part
+        // kv_chunk(row, slot)
         const __bf16* tens[4] = {static_cast<const __bf16*>(p.q), g16, static_cast<const __bf16*>(p.k),
                                  static_cast<const __bf16*>(p.v)};
         const uint32_t offs[4] = {DB_Q_OFF, DB_G_OFF, DB_K_OFF, DB_V_OFF};
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int pi = 4 * wave + t, ten = pi >> 3, r = 16 * (pi & 7) + (lane >> 2);
-            int64_t pos = (ten < 2 ? j0 : k0) + r;
-            pos = pos < N ? pos : N - 1;                      // padded rows read a real one
-            const int part = kv_chunk(r, lane & 3);
-            cx.src[t] = reinterpret_cast<const char*>(tens[ten] + (b * p.I * N + pos) * HD + h * D + 8 * part);
-            cx.dst[t] = offs[ten] + (pi & 7) * 1024;
+        for (int t = 0; t < DB_PIECES; ++t) {
+            const int pi = DB_PIECES * wave + t;
+            const int ten = pi < DB_PQ ? 0 : pi < 2 * DB_PQ ? 1 : pi < 2 * DB_PQ + DB_PK ? 2 : 3;
+            const int local = pi - (ten < 2 ? ten * DB_PQ : 2 * DB_PQ + (ten - 2) * DB_PK);
+            cx.first[t] = (ten < 2 ? j0 : k0) + 16 * local;
+            cx.src[t] = reinterpret_cast<const char*>(tens[ten] + (b * p.I * N + cx.first[t]) * HD + h * D);
+            cx.dst[t] = offs[ten] + local * 1024;
         }
+        // the swizzle depends on bits 1, 2 of the row only, so it is the same in every piece
+        cx.off = static_cast<uint32_t>((lane >> 2) * HD * 2 + kv_chunk(lane >> 2, lane & 3) * 16);
+        cx.N = N;
+        cx.pos_bytes = HD * 2;
         cx.row_step = N * HD * 2;
-        // lse / delta: wave w < 4 copies lse of queries 32 w .. +31, wave w >= 4 delta of 32 (w - 4)
+        // lse / delta: wave w < 4 copies nb of queries 64 w .. +63, wave w >= 4 delta of 64 (w - 4)
         const float* ls = wave < 4 ? nbT : deltaT;
-        cx.ls_src = reinterpret_cast<const char*>(ls + (b * p.I * H + h) * NP + j0 + 32 * (wave & 3) + 4 * (lane & 7));
+        cx.ls_src = reinterpret_cast<const char*>(ls + (b * p.I * H + h) * NP + j0 + 64 * (wave & 3));
         cx.ls_step = H * NP * 4;
-        cx.ls_dst = DB_L_OFF + 128 * wave;
+        cx.ls_dst = DB_L_OFF + 256 * wave;
     }
 
-    const int qt = wave & 3, kp = wave >> 2;
-    const int64_t j = j0 + 32 * qt + c;
-    const bool jok = j < N;
-    // bias (+ mask) * sqrt(D) of this lane's query for the 16 keys of each unit's registers
-    f32x16 C[2];
+    const int qp = wave & 3, kp = wave >> 2;
+    // bias (+ mask) * sqrt(D) of this lane's queries for the 16 keys of each unit's registers;
+    // unit u = 2 qi + ki: queries 64 qp + 32 qi + c, keys 64 kp + 32 ki + ...
+    f32x16 C[4];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int64_t kb = k0 + 64 * kp + 32 * u;             // a multiple of 32: one image key block
+    for (int u = 0; u < 4; ++u) {
+        const int qi = u >> 1, ki = u & 1;
+        const int64_t j = j0 + 64 * qp + 32 * qi + c;
+        const bool jok = j < N;
+        const int64_t kb = k0 + 64 * kp + 32 * ki;             // a multiple of 32: one image key block
         if (kb >= N) {
             C[u] = f32x16{} - INFINITY;
             continue;
@@ -800,18 +836,19 @@ __global__ void __launch_bounds__(DB_THR) bwd_dbias_lds(BwdProblem p, const floa
             for (int e = 0; e < 4; ++e) C[u][4 * a + e] = x[e];
         }
     }
-    // LDS byte offsets of this lane's operand reads (stage 0); unit 1 is 32 rows (+2048) on
-    const int kr = 64 * kp + c, qr = 32 * qt + c;
+    // LDS byte offsets of this lane's operand reads (stage 0, tile 0 of each pair); the
+    // second tile of a pair is 32 rows (+2048) on
+    const int kr = 64 * kp + c, qr = 64 * qp + c;
     uint32_t ok[2], oq[2];
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
-        ok[m] = kr * 64 + kv_chunk(kr, 2 * m + h2) * 16;
-        oq[m] = qr * 64 + kv_chunk(qr, 2 * m + h2) * 16;
+        ok[m] = DB_K_OFF + kr * 64 + kv_chunk(kr, 2 * m + h2) * 16;
+        oq[m] = DB_Q_OFF + qr * 64 + kv_chunk(qr, 2 * m + h2) * 16;
     }
     const uint32_t ol = DB_L_OFF + qr * 4;
     const uint32_t st0 = LDS_ADDR(&g_db[0]);
 
-    f32x16 acc[2] = {};
+    f32x16 acc[4] = {};
     const int64_t I = p.I;
     // prologue: rows 0 .. DB_STAGES - 2 in flight, row 0 complete everywhere
     for (int64_t r = 0; r < DB_STAGES - 1 && r < I; ++r) db_stage(cx, r, static_cast<int>(r), lane);
@@ -823,53 +860,68 @@ __global__ void __launch_bounds__(DB_THR) bwd_dbias_lds(BwdProblem p, const floa
         const uint32_t st = st0 + static_cast<uint32_t>(i % DB_STAGES) * DB_STAGE_BYTES;
         const bool issue = i + DB_STAGES - 1 < I;
         if (issue) db_stage(cx, i + DB_STAGES - 1, static_cast<int>((i + DB_STAGES - 1) % DB_STAGES), lane);
-        u32x4 kk[4], vv[4], qq[2], gg[2];
-        float lse, dl;
+        // [tile][d-half]: K of key tile ki, V, Q of query tile qi, dO; nb and delta per query tile
+        u32x4 kk[2][2], vv[2][2], qq[2][2], gg[2][2];
+        float nb[2], dl[2];
         asm volatile(
-            "ds_read_b128 %0, %14 offset:%c18\n\t"
-            "ds_read_b128 %1, %15 offset:%c18\n\t"
-            "ds_read_b128 %2, %14 offset:%c19\n\t"
-            "ds_read_b128 %3, %15 offset:%c19\n\t"
-            "ds_read_b128 %4, %14 offset:%c20\n\t"
-            "ds_read_b128 %5, %15 offset:%c20\n\t"
-            "ds_read_b128 %6, %14 offset:%c21\n\t"
-            "ds_read_b128 %7, %15 offset:%c21\n\t"
-            "ds_read_b128 %8, %16 offset:%c22\n\t"
-            "ds_read_b128 %9, %17 offset:%c22\n\t"
-            "ds_read_b128 %10, %16 offset:%c23\n\t"
-            "ds_read_b128 %11, %17 offset:%c23\n\t"
-            "ds_read_b32 %12, %24\n\t"
-            "ds_read_b32 %13, %24 offset:%c25\n\t"
+            "ds_read_b128 %0, %20\n\t"
+            "ds_read_b128 %1, %21\n\t"
+            "ds_read_b128 %2, %20 offset:2048\n\t"
+            "ds_read_b128 %3, %21 offset:2048\n\t"
+            "ds_read_b128 %4, %22\n\t"
+            "ds_read_b128 %5, %23\n\t"
+            "ds_read_b128 %6, %22 offset:2048\n\t"
+            "ds_read_b128 %7, %23 offset:2048\n\t"
+            "ds_read_b128 %8, %20 offset:8192\n\t"
+            "ds_read_b128 %9, %21 offset:8192\n\t"
+            "ds_read_b128 %10, %20 offset:10240\n\t"
+            "ds_read_b128 %11, %21 offset:10240\n\t"
+            "ds_read_b128 %12, %22 offset:16384\n\t"
+            "ds_read_b128 %13, %23 offset:16384\n\t"
+            "ds_read_b128 %14, %22 offset:18432\n\t"
+            "ds_read_b128 %15, %23 offset:18432\n\t"
+            "ds_read_b32 %16, %24\n\t"
+            "ds_read_b32 %17, %24 offset:128\n\t"
+            "ds_read_b32 %18, %24 offset:1024\n\t"
+            "ds_read_b32 %19, %24 offset:1152\n\t"
             "s_waitcnt lgkmcnt(0)"
-            : "=&v"(kk[0]), "=&v"(kk[1]), "=&v"(kk[2]), "=&v"(kk[3]), "=&v"(vv[0]), "=&v"(vv[1]), "=&v"(vv[2]),
-              "=&v"(vv[3]), "=&v"(qq[0]), "=&v"(qq[1]), "=&v"(gg[0]), "=&v"(gg[1]), "=&v"(lse), "=&v"(dl)
-            : "v"(st + ok[0]), "v"(st + ok[1]), "v"(st + oq[0]), "v"(st + oq[1]), "i"(DB_K_OFF), "i"(DB_K_OFF + 2048),
-              "i"(DB_V_OFF), "i"(DB_V_OFF + 2048), "i"(DB_Q_OFF), "i"(DB_G_OFF), "v"(st + ol), "i"(DB_Q * 4));
-        const float nb = lse;   // already -lse log2(e)
+            : "=&v"(kk[0][0]), "=&v"(kk[0][1]), "=&v"(kk[1][0]), "=&v"(kk[1][1]), "=&v"(qq[0][0]), "=&v"(qq[0][1]),
+              "=&v"(qq[1][0]), "=&v"(qq[1][1]), "=&v"(vv[0][0]), "=&v"(vv[0][1]), "=&v"(vv[1][0]), "=&v"(vv[1][1]),
+              "=&v"(gg[0][0]), "=&v"(gg[0][1]), "=&v"(gg[1][0]), "=&v"(gg[1][1]), "=&v"(nb[0]), "=&v"(nb[1]),
+              "=&v"(dl[0]), "=&v"(dl[1])
+            : "v"(st + ok[0]), "v"(st + ok[1]), "v"(st + oq[0]), "v"(st + oq[1]), "v"(st + ol));
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            f32x16 S = mfma(__builtin_bit_cast(bf16x8, kk[2 * u]), __builtin_bit_cast(bf16x8, qq[0]), C[u]);
-            S = mfma(__builtin_bit_cast(bf16x8, kk[2 * u + 1]), __builtin_bit_cast(bf16x8, qq[1]), S);
-            f32x16 dP = mfma(__builtin_bit_cast(bf16x8, vv[2 * u]), __builtin_bit_cast(bf16x8, gg[0]), f32x16{});
-            dP = mfma(__builtin_bit_cast(bf16x8, vv[2 * u + 1]), __builtin_bit_cast(bf16x8, gg[1]), dP);
+        for (int u = 0; u < 4; ++u) {
+            const int qi = u >> 1, ki = u & 1;
+            // one unit's S and dP at a time (the registers hold the four bias tiles and sums):
+            // this unit's operands pass through an empty statement ordered after the previous
+            // unit's sums, so its products cannot be hoisted above that unit's work
+            asm volatile("" : "+v"(C[u]), "+v"(kk[ki][0]), "+v"(kk[ki][1]), "+v"(vv[ki][0]), "+v"(vv[ki][1]));
+            f32x16 S = mfma(__builtin_bit_cast(bf16x8, kk[ki][0]), __builtin_bit_cast(bf16x8, qq[qi][0]), C[u]);
+            S = mfma(__builtin_bit_cast(bf16x8, kk[ki][1]), __builtin_bit_cast(bf16x8, qq[qi][1]), S);
+            f32x16 dP = mfma(__builtin_bit_cast(bf16x8, vv[ki][0]), __builtin_bit_cast(bf16x8, gg[qi][0]), f32x16{});
+            dP = mfma(__builtin_bit_cast(bf16x8, vv[ki][1]), __builtin_bit_cast(bf16x8, gg[qi][1]), dP);
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-                acc[u][r] = fmaf(__builtin_amdgcn_exp2f(fmaf(S[r], kScale, nb)), dP[r] - dl, acc[u][r]);
+                acc[u][r] = fmaf(__builtin_amdgcn_exp2f(fmaf(S[r], kScale, nb[qi])), dP[r] - dl[qi], acc[u][r]);
+            asm volatile("" : "+v"(acc[u]));
         }
         if (issue)
             db_barrier_keep();
         else
             db_barrier_drain();
     }
-    if (jok) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int qi = u >> 1, ki = u & 1;
+        const int64_t j = j0 + 64 * qp + 32 * qi + c;
+        if (j >= N) continue;
         float* out = p.dbias + (bh * N + j) * N;
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t kk = k0 + 64 * kp + 32 * u + 8 * (r / 4) + 4 * h2 + (r % 4);
-                if (kk < N) out[kk] = acc[u][r];
-            }
+        for (int r = 0; r < 16; ++r) {
+            const int64_t kk = k0 + 64 * kp + 32 * ki + 8 * (r / 4) + 4 * h2 + (r % 4);
+            if (kk < N) out[kk] = acc[u][r];
+        }
     }
 }
 
@@ -988,12 +1040,12 @@ hipError_t launch_backward_mfma(const BwdProblem& p, void* workspace, hipStream_
                            static_cast<int>(total));
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    const int64_t n_t = (p.N + DB_Q - 1) / DB_Q;
-    const int64_t total = n_t * n_t * p.B * p.H;
+    const int64_t n_tq = (p.N + DB_Q - 1) / DB_Q, n_tk = (p.N + DB_K - 1) / DB_K;
+    const int64_t total = n_tq * n_tk * p.B * p.H;
     if (total > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(bwd_dbias_lds, dim3(static_cast<unsigned>(total)), dim3(DB_THR), 0, stream, p, img, g16, nbT,
-                       deltaT, static_cast<int>(n_jb), static_cast<int>(nblk), Ly.NP, static_cast<int>(n_t),
-                       static_cast<int>(total));
+                       deltaT, static_cast<int>(n_jb), static_cast<int>(nblk), Ly.NP, static_cast<int>(n_tq),
+                       static_cast<int>(n_tk), static_cast<int>(total));
     return hipGetLastError();
 }
 
