@@ -13,7 +13,7 @@
 //   bwd_prep_kernel   dout -> bf16 copy (the operand of the dP and dV products),
 //                     delta = dout . out per query, and delta, nb = -lse log2(e) and
 //                     nb' = (r_j - lse) sqrt(D) transposed to [b, i, h, j] (rows padded to
-//                     whole 128-query tiles).
+//                     whole 256-query tiles).
 //   bwd_dq_lds        2 lines x 128 queries per workgroup, 32-key blocks streamed through
 //                     an LDS ring (the forward's shape):
 //                       S^T = K Q^T + nb',  dP^T = V dO^T,  dS^T = P^T (dP^T - delta),
@@ -21,7 +21,7 @@
 //   bwd_dkdv_lds      2 lines x 128 keys per workgroup, 32-query blocks streamed, in the
 //                     orientation in which P and dS leave the accumulator as B operands:
 //                       S = Q K^T + nb',  dP = dO V^T,  dV^T += dO^T P,  dK^T += Q^T dS
-//   bwd_dbias_lds     128 queries x 128 keys of one (b, h) per workgroup, rows i streamed:
+//   bwd_dbias_lds     256 queries x 128 keys of one (b, h) per workgroup, rows i streamed:
 //                       dbias^T += dS^T of every row i (the bias is shared by all rows)
 // Every streaming kernel copies its operands straight from global memory into a ring of
 // LDS stages (global_load_lds_dwordx4, one barrier per block) and reads them from there;
