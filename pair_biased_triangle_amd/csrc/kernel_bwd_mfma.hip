@@ -667,10 +667,21 @@ __global__ void __launch_bounds__(DK_THR, 2) bwd_dkdv_lds(BwdProblem p, const _F
 // all waves start together after it) small against the work.  The bias tiles C stay in
 // registers for the whole loop.  Every sum over i runs in one lane in row order:
 // deterministic.
-constexpr int DB_Q = 256;
+#ifndef TRI_ATTN_DB_Q
+#define TRI_ATTN_DB_Q 256
+#endif
+#ifndef TRI_ATTN_DB_WAVES
+#define TRI_ATTN_DB_WAVES 8
+#endif
+#ifndef TRI_ATTN_DB_WG_PER_CU
+#define TRI_ATTN_DB_WG_PER_CU 1
+#endif
+constexpr int DB_Q = TRI_ATTN_DB_Q;
 constexpr int DB_K = 128;
-constexpr int DB_WAVES = 8;
+constexpr int DB_WAVES = TRI_ATTN_DB_WAVES;
 constexpr int DB_THR = 64 * DB_WAVES;
+constexpr int DB_NQP = DB_Q / 64;               // 64-query pairs of tiles; wave = (query pair, key pair)
+static_assert(DB_NQP * (DB_K / 64) == DB_WAVES, "one 64 x 64 block of four units per wave");
 #ifndef TRI_ATTN_DB_STAGES
 #define TRI_ATTN_DB_STAGES 3
 #endif
@@ -707,11 +718,10 @@ constexpr int DB_PIECES = (2 * DB_PQ + 2 * DB_PK) / DB_WAVES;   // per wave and 
 constexpr int DB_COPIES = DB_PIECES + 1;                        // + 256 bytes of lse or delta
 static_assert(DB_PIECES * DB_WAVES == 2 * DB_PQ + 2 * DB_PK, "whole pieces per wave");
 static_assert(DB_WAVES * 256 == 2 * DB_Q * 4, "lse / delta: 256 bytes per wave");
-static_assert(DB_STAGES >= 3 && DB_STAGES * sizeof(DbStage) <= 160 * 1024, "LDS ring");
+static_assert(DB_STAGES >= 2 && DB_STAGES * sizeof(DbStage) * TRI_ATTN_DB_WG_PER_CU <= 160 * 1024, "LDS ring");
 static_assert(DB_COPIES * (DB_STAGES - 2) <= 63, "vmcnt range");
-// offsets written into the operand reads below
-static_assert(DB_V_OFF - DB_K_OFF == 8192 && DB_G_OFF - DB_Q_OFF == 16384 && DB_DL_OFF - DB_L_OFF == 1024,
-              "stage layout of the dbias operand reads");
+// offset written into the operand reads below
+static_assert(DB_V_OFF - DB_K_OFF == 8192, "stage layout of the dbias operand reads");
 __shared__ DbStage g_db[DB_STAGES];
 
 // Copy sources are a wave-uniform base (the piece's first row at row i = 0) plus a 32-bit
@@ -755,10 +765,13 @@ __device__ __forceinline__ void db_stage(const DbCtx& cx, int64_t i, int slot, i
 // Barrier after which every wave's copies except those of the DB_STAGES - 2 newest rows
 // are complete; with `drain`, all of them.
 __device__ __forceinline__ void db_barrier_keep() {
-    asm volatile("s_waitcnt vmcnt(%c0)\n\ts_barrier" ::"i"(DB_COPIES * (DB_STAGES - 2)) : "memory");
+    if constexpr (DB_STAGES == 2)
+        db_barrier_drain();
+    else
+        asm volatile("s_waitcnt vmcnt(%c0)\n\ts_barrier" ::"i"(DB_COPIES * (DB_STAGES - 2)) : "memory");
 }
 
-__global__ void __launch_bounds__(DB_THR) bwd_dbias_lds(BwdProblem p, const float* img, const __bf16* g16,
+__global__ void __launch_bounds__(DB_THR, TRI_ATTN_DB_WG_PER_CU) bwd_dbias_lds(BwdProblem p, const float* img, const __bf16* g16,
                                                         const float* nbT, const float* deltaT, int n_jb, int nblk,
                                                         int64_t NP, int n_tq, int n_tk, int total) {
     const int tid = threadIdx.x;
@@ -806,14 +819,14 @@ __global__ void __launch_bounds__(DB_THR) bwd_dbias_lds(BwdProblem p, const floa
         cx.N = N;
         cx.pos_bytes = HD * 2;
         cx.row_step = N * HD * 2;
-        // lse / delta: wave w < 4 copies nb of queries 64 w .. +63, wave w >= 4 delta of 64 (w - 4)
-        const float* ls = wave < 4 ? nbT : deltaT;
-        cx.ls_src = reinterpret_cast<const char*>(ls + (b * p.I * H + h) * NP + j0 + 64 * (wave & 3));
+        // lse / delta: wave w < DB_NQP copies nb of queries 64 w .. +63, the others delta
+        const float* ls = wave < DB_NQP ? nbT : deltaT;
+        cx.ls_src = reinterpret_cast<const char*>(ls + (b * p.I * H + h) * NP + j0 + 64 * (wave % DB_NQP));
         cx.ls_step = H * NP * 4;
         cx.ls_dst = DB_L_OFF + 256 * wave;
     }
 
-    const int qp = wave & 3, kp = wave >> 2;
+    const int qp = wave % DB_NQP, kp = wave / DB_NQP;
     // bias (+ mask) * sqrt(D) of this lane's queries for the 16 keys of each unit's registers;
     // unit u = 2 qi + ki: queries 64 qp + 32 qi + c, keys 64 kp + 32 ki + ...
     f32x16 C[4];
@@ -876,20 +889,22 @@ __global__ void __launch_bounds__(DB_THR) bwd_dbias_lds(BwdProblem p, const floa
             "ds_read_b128 %9, %21 offset:8192\n\t"
             "ds_read_b128 %10, %20 offset:10240\n\t"
             "ds_read_b128 %11, %21 offset:10240\n\t"
-            "ds_read_b128 %12, %22 offset:16384\n\t"
-            "ds_read_b128 %13, %23 offset:16384\n\t"
-            "ds_read_b128 %14, %22 offset:18432\n\t"
-            "ds_read_b128 %15, %23 offset:18432\n\t"
+            "ds_read_b128 %12, %22 offset:%c25\n\t"
+            "ds_read_b128 %13, %23 offset:%c25\n\t"
+            "ds_read_b128 %14, %22 offset:%c26\n\t"
+            "ds_read_b128 %15, %23 offset:%c26\n\t"
             "ds_read_b32 %16, %24\n\t"
             "ds_read_b32 %17, %24 offset:128\n\t"
-            "ds_read_b32 %18, %24 offset:1024\n\t"
-            "ds_read_b32 %19, %24 offset:1152\n\t"
+            "ds_read_b32 %18, %24 offset:%c27\n\t"
+            "ds_read_b32 %19, %24 offset:%c28\n\t"
             "s_waitcnt lgkmcnt(0)"
             : "=&v"(kk[0][0]), "=&v"(kk[0][1]), "=&v"(kk[1][0]), "=&v"(kk[1][1]), "=&v"(qq[0][0]), "=&v"(qq[0][1]),
               "=&v"(qq[1][0]), "=&v"(qq[1][1]), "=&v"(vv[0][0]), "=&v"(vv[0][1]), "=&v"(vv[1][0]), "=&v"(vv[1][1]),
               "=&v"(gg[0][0]), "=&v"(gg[0][1]), "=&v"(gg[1][0]), "=&v"(gg[1][1]), "=&v"(nb[0]), "=&v"(nb[1]),
               "=&v"(dl[0]), "=&v"(dl[1])
-            : "v"(st + ok[0]), "v"(st + ok[1]), "v"(st + oq[0]), "v"(st + oq[1]), "v"(st + ol));
+            : "v"(st + ok[0]), "v"(st + ok[1]), "v"(st + oq[0]), "v"(st + oq[1]), "v"(st + ol),
+              "i"(DB_G_OFF - DB_Q_OFF), "i"(DB_G_OFF - DB_Q_OFF + 2048), "i"(DB_DL_OFF - DB_L_OFF),
+              "i"(DB_DL_OFF - DB_L_OFF + 128));
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int qi = u >> 1, ki = u & 1;

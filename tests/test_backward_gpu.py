@@ -71,6 +71,19 @@ def test_kernels_with_exact_statistics(torch_dev, dtype, I, N, D, bar):
         compare_rel(g, r, bar, f"{n} {dtype} D={D}")
 
 
+def test_several_batches_heads_and_tiles(torch_dev):
+    """B = 2, H = 3 and N = 520: three 256-query dbias tiles (the last one ragged), five
+    128-key tiles, and rows of the second batch element, with exact statistics."""
+    w, dout = case("bf16", 3, 520, 32, seed=77, mask_last=9, B=2, H=3)
+    say("[bwd] exact statistics bf16 B=2 H=3 I=3 N=520")
+    out, lse = oracle.tri_attn(w.q, w.k, w.v, w.bias, w.mask)
+    got = gpu_bwd(torch_dev, w, dout, torch_dev.from_numpy(out.astype(np.float32)).cuda(),
+                  torch_dev.from_numpy(lse.astype(np.float32)).cuda())
+    ref = oracle.tri_attn_bwd(w.q, w.k, w.v, w.bias, w.mask, dout)
+    for n, g, r in zip(NAMES, got, ref):
+        compare_rel(g, r, 1e-2, f"{n} bf16 B=2 H=3 N=520")
+
+
 @pytest.mark.parametrize("dtype,I,N,D,bar", [("bf16", 24, 160, 32, 2e-2), ("fp32", 12, 96, 32, 1e-4)])
 def test_end_to_end(torch_dev, dtype, I, N, D, bar):
     import pair_biased_triangle_amd as P
