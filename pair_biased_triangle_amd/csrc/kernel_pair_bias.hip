@@ -5,8 +5,9 @@
 // With a single line every bias value is used once, so the triangle kernel's prepass (a
 // reference maximum and an fp16 image: two reads of the bias, a write and a read of the
 // image) costs several times the attention itself.  Here the raw bf16 bias is copied
-// straight into LDS, once, and each query keeps the exact running maximum of its scores
-// (the online-normaliser form of the tiled-softmax merge).  The keys are cut into ranges
+// straight into LDS, once, and each query keeps a running reference of its scores
+// (the online-normaliser form of the tiled-softmax merge, the reference moved only when a
+// score passes it by more than 8 in log2 units).  The keys are cut into ranges
 // that run side by side; their partial states are joined by state_combine_kernel.
 //
 // A workgroup of 4 waves owns 128 queries of one (b, h) and one key range; wave w owns
@@ -16,7 +17,7 @@
 // the block's 32 mask values into a ring of LDS stages, then per wave:
 //     S^T = K Q^T                   two v_mfma_f32_32x32x16_bf16 (Q in registers)
 //     x   = (S / sqrt(D) + bias + mask) log2(e)         log2 units, absolute
-//     m'  = max(m, max_k x),  alpha = 2^(m - m'),  p = 2^(x - m')
+//     m'  = max_k x if it exceeds m by more than 8, else m;  alpha = 2^(m - m'),  p = 2^(x - m')
 //     O^T = alpha O^T + V^T P^T     two v_mfma_f32_32x32x16_bf16 on the bf16-rounded p
 //     l   = alpha l + sum_k p       over the rounded p
 // Operand layouts are those of the triangle kernel (kernel_bf16_mfma.hip).
@@ -45,7 +46,7 @@ constexpr int PQ = 128;               // queries per workgroup
 constexpr int PW = 4;                 // waves per workgroup, one 32-query tile each
 constexpr int PTHR = 64 * PW;
 #ifndef TRI_ATTN_PB_STAGES
-#define TRI_ATTN_PB_STAGES 4
+#define TRI_ATTN_PB_STAGES 3
 #endif
 #ifndef TRI_ATTN_PB_FILL
 #define TRI_ATTN_PB_FILL 512
@@ -57,6 +58,7 @@ constexpr int64_t FILL_WGS = TRI_ATTN_PB_FILL;  // workgroups wanted before spli
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kScale = 1.4426950408889634f / 5.656854249492381f;   // log2(e) / sqrt(32)
+constexpr float RESCALE_SLACK = 8.0f;           // log2 units a score may exceed the reference by
 
 // 16-byte chunk `part` of a 64-byte LDS row is stored at chunk kv_chunk(row, part)
 __host__ __device__ constexpr int kv_chunk(int row, int part) { return part ^ ((row >> 1) & 3); }
@@ -253,13 +255,20 @@ __global__ void __launch_bounds__(PTHR) pair_bias_direct_kernel(Problem p, float
 #pragma unroll
         for (int r = 1; r < 16; ++r) mx = fmaxf(mx, x[r]);
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mnew = fmaxf(mref, mx);
-        const float alpha = mref == -INFINITY ? 0.0f : exp2f(mref - mnew);
-        const float sh = mnew == -INFINITY ? 0.0f : mnew;
-        mref = mnew;
-        lsum *= alpha;
+        // The reference moves only when a score exceeds it by more than RESCALE_SLACK (log2
+        // units): p then stays below 2^RESCALE_SLACK, and the rescale of O and l (and its
+        // exponential) is skipped for the whole wave in the usual case.  Sums and the final
+        // normalisation use the same reference, so the result is unchanged up to rounding.
+        if (__any(mx > mref + RESCALE_SLACK)) {
+            const bool grow = mx > mref + RESCALE_SLACK;
+            const float mnew = grow ? mx : mref;
+            const float alpha = !grow ? 1.0f : (mref == -INFINITY ? 0.0f : exp2f(mref - mnew));
+            mref = mnew;
+            lsum *= alpha;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) O[r] *= alpha;
+            for (int r = 0; r < 16; ++r) O[r] *= alpha;
+        }
+        const float sh = mref == -INFINITY ? 0.0f : mref;
         f32x16 P;
 #pragma unroll
         for (int r = 0; r < 16; ++r) P[r] = __builtin_amdgcn_exp2f(x[r] - sh);
