@@ -293,7 +293,7 @@ int tri_attn_bwd(const void *q, const void *k, const void *v, const void *bias,
  * NULL.  It is the triangle operation with a single row (I == 1), with the same tiling
  * and rules.  With one row every bias value is used once, so for bf16, D == 32 and even N
  * the call (like any one-row tri_attn_fwd_rows call) runs a single-pass kernel that reads
- * the raw bias once with the exact running maximum instead of the fp16 image; its
+ * the raw bias once with a running reference per query instead of the fp16 image; its
  * workspace holds only the partial states of key ranges run side by side (none when one
  * range suffices).  Odd N takes the image path.
  */
