@@ -349,7 +349,7 @@ def test_pair_bias_attention(torch_dev, dtype, N, D, T, B):
 
 @pytest.mark.parametrize("N", [100, 640])
 def test_pair_bias_single_pass_extremes(torch_dev, N):
-    """The single-pass kernel keeps the exact running maximum: a bias jump of +60 on one key
+    """The single-pass kernel keeps a running reference: a bias jump of +60 on one key
     of some queries makes that key take all the weight, a batch element with every key
     masked gives out 0 and lse -inf, and the rest still matches the oracle."""
     import pair_biased_triangle_amd as P
@@ -370,3 +370,27 @@ def test_pair_bias_single_pass_extremes(torch_dev, N):
     assert np.all(o[1] == 0) and np.all(np.isneginf(l[1]))
     vv = W.bf16_bits_to_f32(w.v)[0, 0, N // 3, 2]                     # the value row of the dominant key
     np.testing.assert_allclose(o[0, 10:40, 2], np.broadcast_to(vv, (30, 32)), atol=1e-6)
+
+
+@pytest.mark.parametrize("N", [640, 2700])
+def test_pair_bias_single_pass_moving_reference(torch_dev, N):
+    """Bias ramps rising along the keys with a slope that differs per query (0 to 1.2 per
+    key block, in natural-log units, some falling instead), so that the single-pass kernel
+    moves its reference many times, at different blocks for different queries of a wave
+    (queries whose reference stays keep a factor of 1 inside the rescale branch); the
+    result matches the oracle."""
+    import pair_biased_triangle_amd as P
+    w = small("bf16", B=1, I=1, N=N, D=32, T=1, mask_last=3)
+    bias = W.bf16_bits_to_f32(w.bias)
+    keys = np.arange(N, dtype=np.float32) / 32.0                       # key blocks
+    slope = np.random.default_rng(5).uniform(-0.4, 1.2, size=(4, N)).astype(np.float32)
+    bias[0] += slope[:, :, None] * keys[None, None, :]
+    w.bias = W.f32_to_bf16_bits(bias)
+    say(f"[next] pair-bias single pass, moving reference, N={N}")
+    q, k, v, b, mask = dev_inputs(torch_dev, w)
+    shp = (1, N, 4, 32)
+    out, lse = P.pair_bias_attn_fwd(q.view(shp), k.view(shp), v.view(shp), b, mask, want_lse=True)
+    torch_dev.cuda.synchronize()
+    ref, ref_lse = oracle.tri_attn(w.q, w.k, w.v, w.bias, w.mask, n_key_tiles=1)
+    compare(out.cpu().numpy(), ref[:, 0], TOL["bf16"], "pair-bias moving reference out")
+    compare_lse(lse.cpu().numpy(), ref_lse[:, 0], TOL["bf16"], "pair-bias moving reference lse")
