@@ -34,9 +34,25 @@
  * computes q.k and P.V on bf16 matrix cores with fp32 accumulation; softmax statistics
  * are fp32 and the probabilities are rounded to bf16 (nearest even) only as the P.V
  * operand.  It takes bias + mask relative to each query's largest bias + mask over the
- * call's keys (softmax does not change when all scores of a query move together),
- * times sqrt(D) and rounded to fp16: every such value is <= 0, those below the fp16 range
- * become -inf (weight 0).  The fp32 path computes in fp32 throughout.
+ * call's keys (softmax does not change when all scores of a query move together), in
+ * log2 units, rounded to fp16: every such value is <= 0 and keeps 11 significant bits.
+ * The fp32 path computes in fp32 throughout.
+ *
+ * Accuracy envelope of the bf16 path.  The fp16 rounding of a bias value x log2 units
+ * below its query's largest is up to |x| 2^-11, so it is bounded by a span: every
+ * (b, h, block of 256 query columns) whose finite bias + mask values all lie within 32
+ * log2 units (about 22.2 nats) of their query's largest runs on the matrix cores, with
+ * at most 2^-7 log2 units of image rounding per score (max |error| against fp64 about
+ * 1e-3 to 5e-3 on N(0,1)-N(0,4) biases, about 4e-3 at the edge of the span when q.k
+ * puts the weight on the farthest keys); every other block is computed on the fp32 path
+ * with the bias unrounded, so the 1e-2 bf16 bar holds whatever the bias spread.
+ * Finite values more than 65520 log2 units (about 45,400 nats) below the largest are
+ * beyond fp16 and count as dropped keys (weight 0): such a key could only matter if its
+ * q.k / sqrt(D) made up that distance.  Hence a mask written into the bias or mask as
+ * a large finite negative number sends its blocks to the fp32 path when it lies within
+ * that range (e.g. -1e4) and not when it lies beyond it (e.g. -1e9); -inf is always free.
+ * The same envelope and routing apply to the matrix-core backward's dq, dk and dv (per
+ * (b, h)); its dbias kernel always adds the fp32 bias.
  *
  * Ownership and memory: every pointer is a device pointer owned by the caller; the
  * library keeps none of them after returning.  q, k, v, bias and mask are only read and

@@ -36,147 +36,162 @@ __device__ __forceinline__ float ld(const void* base, int64_t idx) {
 // probability of a score against the query's log-sum-exp (0 for a query with no key)
 __device__ __forceinline__ float prob(float s, float lse) { return lse == -INFINITY ? 0.0f : expf(s - lse); }
 
+// With `wide` set (the bf16 backward's span flags, n_wide per (b, h)), a workgroup works
+// only if its (b, h) has a flag set; rows i run blockIdx.y, blockIdx.y + gridDim.y, ...
+__device__ __forceinline__ bool skip_bh(const int* wide, int n_wide) {
+    if (!wide) return false;
+    int any = 0;
+    for (int t = 0; t < n_wide; ++t) any |= wide[static_cast<int64_t>(blockIdx.z) * n_wide + t];
+    return any == 0;
+}
+
 template <bool BF16, int DP>
-__global__ void __launch_bounds__(BT) bwd_dq_kernel(BwdProblem p) {
+__global__ void __launch_bounds__(BT) bwd_dq_kernel(BwdProblem p, const int* wide, int n_wide) {
+    if (skip_bh(wide, n_wide)) return;
     const int64_t N = p.N, H = p.H, D = p.D, I = p.I;
-    const int64_t i = blockIdx.y, b = blockIdx.z / H, h = blockIdx.z % H;
+    const int64_t b = blockIdx.z / H, h = blockIdx.z % H;
     const int64_t j = static_cast<int64_t>(blockIdx.x) * BT + threadIdx.x;
-    const int64_t row = (b * I + i) * N;      // flat (b, i, 0)
     const int tid = threadIdx.x;
     __shared__ float Ks[BKB][DP + 1];
     __shared__ float Vs[BKB][DP + 1];
     __shared__ float Bs[BT][BKB + 1];
+    for (int64_t i = blockIdx.y; i < I; i += gridDim.y) {
+        const int64_t row = (b * I + i) * N;      // flat (b, i, 0)
 
-    const bool live = j < N;
-    float q[DP], g[DP], dq[DP];
-    float delta = 0.0f;
-    const float lse = live ? p.lse[(row + j) * H + h] : -INFINITY;
+        const bool live = j < N;
+        float q[DP], g[DP], dq[DP];
+        float delta = 0.0f;
+        const float lse = live ? p.lse[(row + j) * H + h] : -INFINITY;
 #pragma unroll
-    for (int d = 0; d < DP; ++d) {
-        const bool ok = live && d < D;
-        const int64_t e = ((row + j) * H + h) * D + d;
-        q[d] = ok ? ld<BF16>(p.q, e) : 0.0f;
-        g[d] = ok ? p.dout[e] : 0.0f;
-        delta = fmaf(g[d], ok ? p.out[e] : 0.0f, delta);
-        dq[d] = 0.0f;
-    }
-    const float scale = 1.0f / sqrtf(static_cast<float>(D));
-    for (int64_t kb = 0; kb < N; kb += BKB) {
-        const int nk = static_cast<int>(N - kb < BKB ? N - kb : BKB);
-        __syncthreads();
-        for (int e = tid; e < BKB * DP; e += BT) {
-            const int kk = e / DP, d = e % DP;
-            const bool ok = kk < nk && d < D;
-            const int64_t off = ((row + kb + kk) * H + h) * D + d;
-            Ks[kk][d] = ok ? ld<BF16>(p.k, off) : 0.0f;
-            Vs[kk][d] = ok ? ld<BF16>(p.v, off) : 0.0f;
+        for (int d = 0; d < DP; ++d) {
+            const bool ok = live && d < D;
+            const int64_t e = ((row + j) * H + h) * D + d;
+            q[d] = ok ? ld<BF16>(p.q, e) : 0.0f;
+            g[d] = ok ? p.dout[e] : 0.0f;
+            delta = fmaf(g[d], ok ? p.out[e] : 0.0f, delta);
+            dq[d] = 0.0f;
         }
-        const int64_t j0 = static_cast<int64_t>(blockIdx.x) * BT;
-        for (int e = tid; e < BT * BKB; e += BT) {
-            const int jj = e / BKB, kk = e % BKB;
-            float bv = -INFINITY;
-            if (kk < nk && j0 + jj < N) {
-                bv = ld<BF16>(p.bias, ((b * H + h) * N + j0 + jj) * N + kb + kk);
-                if (p.mask) bv += p.mask[b * N + kb + kk];
+        const float scale = 1.0f / sqrtf(static_cast<float>(D));
+        for (int64_t kb = 0; kb < N; kb += BKB) {
+            const int nk = static_cast<int>(N - kb < BKB ? N - kb : BKB);
+            __syncthreads();
+            for (int e = tid; e < BKB * DP; e += BT) {
+                const int kk = e / DP, d = e % DP;
+                const bool ok = kk < nk && d < D;
+                const int64_t off = ((row + kb + kk) * H + h) * D + d;
+                Ks[kk][d] = ok ? ld<BF16>(p.k, off) : 0.0f;
+                Vs[kk][d] = ok ? ld<BF16>(p.v, off) : 0.0f;
             }
-            Bs[jj][kk] = bv;
-        }
-        __syncthreads();
-        for (int kk = 0; kk < nk; ++kk) {
-            float s = 0.0f, dp = 0.0f;
-#pragma unroll
-            for (int d = 0; d < DP; ++d) {
-                s = fmaf(q[d], Ks[kk][d], s);
-                dp = fmaf(g[d], Vs[kk][d], dp);
+            const int64_t j0 = static_cast<int64_t>(blockIdx.x) * BT;
+            for (int e = tid; e < BT * BKB; e += BT) {
+                const int jj = e / BKB, kk = e % BKB;
+                float bv = -INFINITY;
+                if (kk < nk && j0 + jj < N) {
+                    bv = ld<BF16>(p.bias, ((b * H + h) * N + j0 + jj) * N + kb + kk);
+                    if (p.mask) bv += p.mask[b * N + kb + kk];
+                }
+                Bs[jj][kk] = bv;
             }
-            const float pk = prob(s * scale + Bs[tid][kk], lse);
-            const float ds = pk * (dp - delta);
+            __syncthreads();
+            for (int kk = 0; kk < nk; ++kk) {
+                float s = 0.0f, dp = 0.0f;
 #pragma unroll
-            for (int d = 0; d < DP; ++d) dq[d] = fmaf(ds, Ks[kk][d], dq[d]);
+                for (int d = 0; d < DP; ++d) {
+                    s = fmaf(q[d], Ks[kk][d], s);
+                    dp = fmaf(g[d], Vs[kk][d], dp);
+                }
+                const float pk = prob(s * scale + Bs[tid][kk], lse);
+                const float ds = pk * (dp - delta);
+#pragma unroll
+                for (int d = 0; d < DP; ++d) dq[d] = fmaf(ds, Ks[kk][d], dq[d]);
+            }
         }
-    }
-    if (live) {
+        if (live) {
 #pragma unroll
-        for (int d = 0; d < DP; ++d)
-            if (d < D) p.dq[((row + j) * H + h) * D + d] = dq[d] * scale;
-    }
+            for (int d = 0; d < DP; ++d)
+                if (d < D) p.dq[((row + j) * H + h) * D + d] = dq[d] * scale;
+        }
+    }   // rows i
 }
 
 template <bool BF16, int DP>
-__global__ void __launch_bounds__(BT) bwd_dkdv_kernel(BwdProblem p) {
+__global__ void __launch_bounds__(BT) bwd_dkdv_kernel(BwdProblem p, const int* wide, int n_wide) {
+    if (skip_bh(wide, n_wide)) return;
     const int64_t N = p.N, H = p.H, D = p.D, I = p.I;
-    const int64_t i = blockIdx.y, b = blockIdx.z / H, h = blockIdx.z % H;
+    const int64_t b = blockIdx.z / H, h = blockIdx.z % H;
     const int64_t k0 = static_cast<int64_t>(blockIdx.x) * BT;
     const int64_t key = k0 + threadIdx.x;
-    const int64_t row = (b * I + i) * N;
     const int tid = threadIdx.x;
     __shared__ float Qs[BKB][DP + 1];
     __shared__ float Gs[BKB][DP + 1];
     __shared__ float Ls[BKB], Ds[BKB];
     __shared__ float Bs[BKB][BT + 1];
+    for (int64_t i = blockIdx.y; i < I; i += gridDim.y) {
+        const int64_t row = (b * I + i) * N;
 
-    const bool live = key < N;
-    float kv[DP], vv[DP], dk[DP], dv[DP];
+        const bool live = key < N;
+        float kv[DP], vv[DP], dk[DP], dv[DP];
 #pragma unroll
-    for (int d = 0; d < DP; ++d) {
-        const bool ok = live && d < D;
-        const int64_t e = ((row + key) * H + h) * D + d;
-        kv[d] = ok ? ld<BF16>(p.k, e) : 0.0f;
-        vv[d] = ok ? ld<BF16>(p.v, e) : 0.0f;
-        dk[d] = dv[d] = 0.0f;
-    }
-    const float mk = (live && p.mask) ? p.mask[b * N + key] : 0.0f;
-    const float scale = 1.0f / sqrtf(static_cast<float>(D));
-    for (int64_t jb = 0; jb < N; jb += BKB) {
-        const int nq = static_cast<int>(N - jb < BKB ? N - jb : BKB);
-        __syncthreads();
-        for (int e = tid; e < BKB * DP; e += BT) {
-            const int jj = e / DP, d = e % DP;
-            const bool ok = jj < nq && d < D;
-            const int64_t off = ((row + jb + jj) * H + h) * D + d;
-            Qs[jj][d] = ok ? ld<BF16>(p.q, off) : 0.0f;
-            Gs[jj][d] = ok ? p.dout[off] : 0.0f;
+        for (int d = 0; d < DP; ++d) {
+            const bool ok = live && d < D;
+            const int64_t e = ((row + key) * H + h) * D + d;
+            kv[d] = ok ? ld<BF16>(p.k, e) : 0.0f;
+            vv[d] = ok ? ld<BF16>(p.v, e) : 0.0f;
+            dk[d] = dv[d] = 0.0f;
         }
-        if (tid < BKB) {
-            float lse = -INFINITY, delta = 0.0f;
-            if (tid < nq) {
-                const int64_t qi = (row + jb + tid) * H + h;
-                lse = p.lse[qi];
-                for (int d = 0; d < D; ++d) delta = fmaf(p.dout[qi * D + d], p.out[qi * D + d], delta);
+        const float mk = (live && p.mask) ? p.mask[b * N + key] : 0.0f;
+        const float scale = 1.0f / sqrtf(static_cast<float>(D));
+        for (int64_t jb = 0; jb < N; jb += BKB) {
+            const int nq = static_cast<int>(N - jb < BKB ? N - jb : BKB);
+            __syncthreads();
+            for (int e = tid; e < BKB * DP; e += BT) {
+                const int jj = e / DP, d = e % DP;
+                const bool ok = jj < nq && d < D;
+                const int64_t off = ((row + jb + jj) * H + h) * D + d;
+                Qs[jj][d] = ok ? ld<BF16>(p.q, off) : 0.0f;
+                Gs[jj][d] = ok ? p.dout[off] : 0.0f;
             }
-            Ls[tid] = lse;
-            Ds[tid] = delta;
-        }
-        for (int e = tid; e < BKB * BT; e += BT) {
-            const int jj = e / BT, kk = e % BT;
-            Bs[jj][kk] = (jj < nq && k0 + kk < N) ? ld<BF16>(p.bias, ((b * H + h) * N + jb + jj) * N + k0 + kk) : 0.0f;
-        }
-        __syncthreads();
-        for (int jj = 0; jj < nq; ++jj) {
-            float s = 0.0f, dp = 0.0f;
+            if (tid < BKB) {
+                float lse = -INFINITY, delta = 0.0f;
+                if (tid < nq) {
+                    const int64_t qi = (row + jb + tid) * H + h;
+                    lse = p.lse[qi];
+                    for (int d = 0; d < D; ++d) delta = fmaf(p.dout[qi * D + d], p.out[qi * D + d], delta);
+                }
+                Ls[tid] = lse;
+                Ds[tid] = delta;
+            }
+            for (int e = tid; e < BKB * BT; e += BT) {
+                const int jj = e / BT, kk = e % BT;
+                Bs[jj][kk] = (jj < nq && k0 + kk < N) ? ld<BF16>(p.bias, ((b * H + h) * N + jb + jj) * N + k0 + kk) : 0.0f;
+            }
+            __syncthreads();
+            for (int jj = 0; jj < nq; ++jj) {
+                float s = 0.0f, dp = 0.0f;
 #pragma unroll
-            for (int d = 0; d < DP; ++d) {
-                s = fmaf(Qs[jj][d], kv[d], s);
-                dp = fmaf(Gs[jj][d], vv[d], dp);
-            }
-            const float pk = prob(s * scale + Bs[jj][tid] + mk, Ls[jj]);
-            const float ds = pk * (dp - Ds[jj]);
+                for (int d = 0; d < DP; ++d) {
+                    s = fmaf(Qs[jj][d], kv[d], s);
+                    dp = fmaf(Gs[jj][d], vv[d], dp);
+                }
+                const float pk = prob(s * scale + Bs[jj][tid] + mk, Ls[jj]);
+                const float ds = pk * (dp - Ds[jj]);
 #pragma unroll
-            for (int d = 0; d < DP; ++d) {
-                dk[d] = fmaf(ds, Qs[jj][d], dk[d]);
-                dv[d] = fmaf(pk, Gs[jj][d], dv[d]);
+                for (int d = 0; d < DP; ++d) {
+                    dk[d] = fmaf(ds, Qs[jj][d], dk[d]);
+                    dv[d] = fmaf(pk, Gs[jj][d], dv[d]);
+                }
             }
         }
-    }
-    if (live) {
+        if (live) {
 #pragma unroll
-        for (int d = 0; d < DP; ++d)
-            if (d < D) {
-                const int64_t e = ((row + key) * H + h) * D + d;
-                p.dk[e] = dk[d] * scale;
-                p.dv[e] = dv[d];
-            }
-    }
+            for (int d = 0; d < DP; ++d)
+                if (d < D) {
+                    const int64_t e = ((row + key) * H + h) * D + d;
+                    p.dk[e] = dk[d] * scale;
+                    p.dv[e] = dv[d];
+                }
+        }
+    }   // rows i
 }
 
 constexpr int TB = 64;            // (j, k) tile edge of the dbias kernel
@@ -280,10 +295,10 @@ template <bool BF16, int DP>
 hipError_t launch_dp(const BwdProblem& p, hipStream_t stream) {
     const unsigned nb = static_cast<unsigned>((p.N + BT - 1) / BT);
     const dim3 grid(nb, static_cast<unsigned>(p.I), static_cast<unsigned>(p.B * p.H));
-    hipLaunchKernelGGL((bwd_dq_kernel<BF16, DP>), grid, dim3(BT), 0, stream, p);
+    hipLaunchKernelGGL((bwd_dq_kernel<BF16, DP>), grid, dim3(BT), 0, stream, p, nullptr, 0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<BF16, DP>), grid, dim3(BT), 0, stream, p);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<BF16, DP>), grid, dim3(BT), 0, stream, p, nullptr, 0);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const unsigned nt = static_cast<unsigned>((p.N + TB - 1) / TB);
@@ -304,6 +319,19 @@ hipError_t launch_bf(const BwdProblem& p, hipStream_t stream) {
 hipError_t launch_backward(const BwdProblem& p, bool bf16, hipStream_t stream) {
     if ((p.N + TB - 1) / TB > 65535) return hipErrorInvalidConfiguration;
     return bf16 ? launch_bf<true>(p, stream) : launch_bf<false>(p, stream);
+}
+
+hipError_t launch_backward_wide(const BwdProblem& p, const int* wide, int n_wide, hipStream_t stream) {
+    if (p.D > 32) return hipErrorInvalidValue;
+    // usually no (b, h) is flagged: a small grid (rows walked in up to 64 slots) keeps the
+    // launch cheap when every workgroup returns
+    const unsigned nb = static_cast<unsigned>((p.N + BT - 1) / BT);
+    const dim3 grid(nb, static_cast<unsigned>(p.I < 64 ? p.I : 64), static_cast<unsigned>(p.B * p.H));
+    hipLaunchKernelGGL((bwd_dq_kernel<true, 32>), grid, dim3(BT), 0, stream, p, wide, n_wide);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<true, 32>), grid, dim3(BT), 0, stream, p, wide, n_wide);
+    return hipGetLastError();
 }
 
 }  // namespace tri_attn

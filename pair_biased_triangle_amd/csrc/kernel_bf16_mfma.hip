@@ -118,6 +118,10 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kSqrtD = 5.656854249492381f;   // sqrt(32), the scale of the backward's fp32 image
 constexpr float kScale = 1.4426950408889634f / 5.656854249492381f;   // log2(e) / sqrt(32): q.k -> log2 units
+// Widest span the fp16 image keeps below a query's reference: a stored value in
+// (-kImageSpan, 0] is rounded by at most 2^-7 log2 units.  A column block with any finite
+// value below it is handled by the fp32 kernel instead (see bias_image16_kernel).
+constexpr float kImageSpan = 32.0f;
 constexpr float kLo = 5.421010862427522e-20f;  // 2^-64
 constexpr float kHi = 1.8446744073709552e19f;  // 2^64
 
@@ -193,8 +197,10 @@ static_assert(BJ % IMG16_Q == 0, "an image workgroup fills part of one column bl
 // query's biases are a contiguous row, so one wave walks it with coalesced reads (one
 // partial).  Ending node: they are a column, so a wave holds 64 consecutive queries and the
 // keys are split into REF_KS chunks, each a partial maximum, over 4 waves of a workgroup.
+// The same launch clears the wide-span flag of every column block (one int per (b, h,
+// column block)), which bias_image16_kernel sets afterwards.
 constexpr int REF_KS = 16;
-__global__ void __launch_bounds__(256) bias_ref_kernel(Problem p, float* part, int64_t nqp) {
+__global__ void __launch_bounds__(256) bias_ref_kernel(Problem p, float* part, int64_t nqp, int* wide, int n_jb) {
     const int64_t bh = blockIdx.z, b = bh / p.H, BH = gridDim.z;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t NK = p.nkeys();
@@ -202,6 +208,7 @@ __global__ void __launch_bounds__(256) bias_ref_kernel(Problem p, float* part, i
     if (!p.ending) {
         const int64_t j = static_cast<int64_t>(blockIdx.x) * 4 + wave;
         if (j >= nqp) return;
+        if (j % BJ == 0 && lane == 0) wide[bh * n_jb + j / BJ] = 0;
         float mx = -INFINITY;
         if (j < p.N) {
             const uint16_t* row = bg + (bh * p.N + j) * p.N + p.k0;
@@ -239,6 +246,7 @@ __global__ void __launch_bounds__(256) bias_ref_kernel(Problem p, float* part, i
     }
     __shared__ float red[4][64];
     const int64_t j = static_cast<int64_t>(blockIdx.x) * 64 + lane;
+    if (blockIdx.y == 0 && threadIdx.x == 0 && j % BJ == 0) wide[bh * n_jb + j / BJ] = 0;
     const int64_t chunk = (NK + REF_KS - 1) / REF_KS;
     const int64_t lo = blockIdx.y * chunk, hi = min(NK, lo + chunk);
     float mx = -INFINITY;
@@ -263,9 +271,22 @@ __global__ void __launch_bounds__(256) bias_ref_kernel(Problem p, float* part, i
 // wave holds 64 consecutive queries, which for one key are 128 contiguous bytes.  r_j is
 // the largest of the n_part partial maxima (0 if every key is masked); with several
 // partials the workgroups of the first blocks also store r_j for the epilogue.
+//
+// Span guard.  fp16 rounds a value in (-2^e, -2^(e-1)] by up to 2^(e-12), so the image error
+// of a score grows with how far its bias lies below r_j.  The output error stays within
+// that of the bf16 probabilities only while every kept value lies within kImageSpan of
+// r_j.  A workgroup that writes a finite image value below -kImageSpan sets its column
+// block's flag in `wide`; the attention kernel then leaves that block to the fp32 kernel,
+// which adds the bias unrounded.  Values beyond fp16's range become -inf: keys more than
+// 65520 log2 units (about 45,400 nats) below the query's largest bias get weight 0.
 constexpr int IMG16_NB = 4;
+__device__ __forceinline__ bool beyond_span(_Float16 h) {
+    const float f = static_cast<float>(h);
+    return f < -kImageSpan && f > -INFINITY;
+}
+
 __global__ void __launch_bounds__(256) bias_image16_kernel(Problem p, const float* part, int n_part, _Float16* img,
-                                                           float* ref, int n_jb, int nblk) {
+                                                           float* ref, int n_jb, int nblk, int* wide) {
     const int g = blockIdx.x, n0 = blockIdx.y * IMG16_NB;
     const int64_t bh = blockIdx.z, b = bh / p.H, BH = gridDim.z;
     const int t = threadIdx.x;
@@ -282,7 +303,8 @@ __global__ void __launch_bounds__(256) bias_image16_kernel(Problem p, const floa
     if (n_part > 1 && n0 == 0 && pt == 0) ref[bh * nqp + j] = r;
 
     const BlockPlan plan(p.nkeys());
-    const int jb = static_cast<int>(j / BJ), jl = static_cast<int>(j % BJ);
+    const int jb = static_cast<int>(j / BJ), jl = static_cast<int>(j % BJ);   // jb is the workgroup's
+    bool spread = false;                                                     // (IMG16_Q divides BJ)
     _Float16* dst = img + (bh * n_jb + jb) * nblk * static_cast<int64_t>(IMG_HALVES) + jl * BK + kv_chunk(jl, pt) * 8;
     if (!p.ending) {
         // Starting node: the workgroup's blocks cover the contiguous keys k0 + kbeg .. + span
@@ -315,7 +337,9 @@ __global__ void __launch_bounds__(256) bias_image16_kernel(Problem p, const floa
                 const int kk = 2 * lane + h;
                 float x = 0.0f;
                 if (jr < p.N && kk < span) x = (__uint_as_float(static_cast<uint32_t>(rowp[kk]) << 16) + mk[h] - rj) * kLog2e;
-                if (kk < IMG16_NB * BK) rowbuf[rr][kk] = static_cast<_Float16>(x);
+                const _Float16 hx = static_cast<_Float16>(x);
+                spread = spread || beyond_span(hx);
+                if (kk < IMG16_NB * BK) rowbuf[rr][kk] = hx;
             }
         }
         __syncthreads();
@@ -332,6 +356,7 @@ __global__ void __launch_bounds__(256) bias_image16_kernel(Problem p, const floa
             }
             *reinterpret_cast<f16x8*>(dst + static_cast<int64_t>(n) * IMG_HALVES) = x;
         }
+        if (__syncthreads_or(spread) && t == 0) atomicOr(wide + bh * n_jb + jb, 1);
         return;
     }
     // the query's biases at key k0 + k: base[k * kstride] (a row, or a column for the ending node)
@@ -367,9 +392,13 @@ __global__ void __launch_bounds__(256) bias_image16_kernel(Problem p, const floa
         if (n0 + u >= nblk) break;
         f16x8 x;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = static_cast<_Float16>(val[u][e]);
+        for (int e = 0; e < 8; ++e) {
+            x[e] = static_cast<_Float16>(val[u][e]);
+            spread = spread || beyond_span(x[e]);
+        }
         *reinterpret_cast<f16x8*>(dst + static_cast<int64_t>(n0 + u) * IMG_HALVES) = x;
     }
+    if (__syncthreads_or(spread) && t == 0) atomicOr(wide + bh * n_jb + jb, 1);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -724,8 +753,11 @@ __device__ __forceinline__ void key_loop_exact(const Ctx& cx, const Lane& L, int
     for (int n = nb0; n < nb1; ++n) key_step<true>(cx, L, wave, lane, qB, s, n, nb1);
 }
 
+// A column block whose flag in `wide` is set (bias spread beyond kImageSpan) is left to the
+// fp32 kernel that runs after this one: nothing is written for it, except that in split-key
+// mode every split stores the empty state (the fp32 kernel then stores split 0's).
 __global__ void __launch_bounds__(NTHR, 2) bf16_mfma_kernel(Problem p, Strides sd, const _Float16* img, const float* ref,
-                                                         int n_jb, int n_rg, int nblk, int total) {
+                                                         const int* wide, int n_jb, int n_rg, int nblk, int total) {
     // XCD-aware remap: XCD x (= hardware id mod 8) walks a contiguous range of logical ids.
     const int w = blockIdx.x;
     const int xcd = w % NXCD, slot = w / NXCD;
@@ -808,6 +840,26 @@ __global__ void __launch_bounds__(NTHR, 2) bf16_mfma_kernel(Problem p, Strides s
         p.out += split * rows * D;
         p.st_m += split * rows;
         p.st_l += split * rows;
+    }
+
+    if (wide[static_cast<int64_t>(bh) * n_jb + jb]) {   // the fp32 kernel's block
+        if (n_split > 1) {
+#pragma unroll
+            for (int ri = 0; ri < RW; ++ri)
+#pragma unroll
+                for (int ti = 0; ti < TW; ++ti) {
+                    const int64_t i = i0 + row0 + ri, j = j0 + (tile0 + ti) * 32 + L.c;
+                    if (!(i < lines && j < p.N)) continue;
+                    const int64_t qo = bh_off + i * sd.line + j * sd.query;
+#pragma unroll
+                    for (int a = 0; a < 4; ++a) *reinterpret_cast<f32x4*>(p.out + qo + 8 * a + 4 * L.h2) = f32x4{};
+                    if (L.h2 == 0) {
+                        p.st_m[qo / D] = -INFINITY;
+                        p.st_l[qo / D] = 0.0f;
+                    }
+                }
+        }
+        return;
     }
 
     State s;
@@ -946,9 +998,10 @@ __global__ void __launch_bounds__(NTHR, 2) bf16_mfma_kernel(Problem p, Strides s
 }
 
 // Workspace of the forward: the fp16 image, then the references r_j (fp32, padded to
-// whole column blocks), then for the ending node REF_KS partial maxima per query, then in
-// split-key mode the partial states (acc, m, l of every query, per split); each part
-// 256-byte aligned.  The starting node's single partial maximum is r_j itself.
+// whole column blocks), the wide-span flag of every (b, h, column block) (int), then for
+// the ending node REF_KS partial maxima per query, then in split-key mode the partial
+// states (acc, m, l of every query, per split); each part 256-byte aligned.  The starting
+// node's single partial maximum is r_j itself.
 //
 // Split-key mode: a call whose grid would leave most of the chip idle (attention with
 // pair bias is one line; small N) cuts the key blocks into up to MAX_SPLIT ranges run side
@@ -959,7 +1012,7 @@ constexpr int64_t FILL_WGS = 512;           // two workgroups per compute unit
 struct FwdLayout {
     int64_t n_jb, nblk, nqp, n_rg, wgs, rows;
     int n_part, n_split;
-    size_t img_bytes, ref_off, part_off, split_off, total;
+    size_t img_bytes, ref_off, wide_off, part_off, split_off, total;
 };
 FwdLayout fwd_layout(const Problem& p) {
     FwdLayout L;
@@ -976,13 +1029,16 @@ FwdLayout fwd_layout(const Problem& p) {
         L.n_split = static_cast<int>(min(min(want, most), static_cast<int64_t>(MAX_SPLIT)));
         if (L.n_split < 2) L.n_split = 1;
     }
+    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
     L.img_bytes = static_cast<size_t>(p.B * p.H * L.n_jb * L.nblk) * IMG_HALVES * 2;
-    L.ref_off = (L.img_bytes + 255) / 256 * 256;
+    L.ref_off = up(L.img_bytes);
     const size_t ref_bytes = static_cast<size_t>(p.B * p.H * L.nqp) * 4;
-    L.part_off = L.ref_off + (ref_bytes + 255) / 256 * 256;
-    L.split_off = p.ending ? L.part_off + (ref_bytes * REF_KS + 255) / 256 * 256 : L.part_off;
+    L.wide_off = up(L.ref_off + ref_bytes);
+    const size_t wide_bytes = static_cast<size_t>(p.B * p.H * L.n_jb) * 4;
+    L.part_off = up(L.wide_off + wide_bytes);
+    L.split_off = p.ending ? up(L.part_off + ref_bytes * REF_KS) : L.part_off;
     L.total = L.n_split > 1 ? L.split_off + static_cast<size_t>(L.n_split * L.rows) * (D + 2) * 4
-                            : (p.ending ? L.part_off + ref_bytes * REF_KS : L.ref_off + ref_bytes);
+                            : (p.ending ? L.part_off + ref_bytes * REF_KS : L.wide_off + wide_bytes);
     return L;
 }
 
@@ -1013,17 +1069,19 @@ namespace {
 hipError_t launch_prepass(const Problem& p, const FwdLayout& Ly, void* workspace, int64_t n_qg, hipStream_t stream) {
     _Float16* img = static_cast<_Float16*>(workspace);
     float* ref = reinterpret_cast<float*>(static_cast<char*>(workspace) + Ly.ref_off);
+    int* wide = reinterpret_cast<int*>(static_cast<char*>(workspace) + Ly.wide_off);
     float* part = Ly.n_part > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + Ly.part_off) : ref;
     const unsigned bhs = static_cast<unsigned>(p.B * p.H);
     const dim3 ref_grid = p.ending ? dim3(static_cast<unsigned>(Ly.nqp / 64), REF_KS, bhs)
                                    : dim3(static_cast<unsigned>(Ly.nqp / 4), 1, bhs);
-    hipLaunchKernelGGL(bias_ref_kernel, ref_grid, dim3(256), 0, stream, p, part, Ly.nqp);
+    hipLaunchKernelGGL(bias_ref_kernel, ref_grid, dim3(256), 0, stream, p, part, Ly.nqp, wide,
+                       static_cast<int>(Ly.n_jb));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(bias_image16_kernel,
                        dim3(static_cast<unsigned>(n_qg), static_cast<unsigned>((Ly.nblk + IMG16_NB - 1) / IMG16_NB), bhs),
                        dim3(256), 0, stream, p, part, Ly.n_part, img, ref, static_cast<int>(Ly.n_jb),
-                       static_cast<int>(Ly.nblk));
+                       static_cast<int>(Ly.nblk), wide);
     return hipGetLastError();
 }
 }  // namespace
@@ -1036,7 +1094,8 @@ Prepass16 prepass16_layout(const Problem& p) {
     q.nqp = L.nqp;
     q.nblk = L.nblk;
     q.ref_off = L.ref_off;
-    q.bytes = L.ref_off + static_cast<size_t>(p.B * p.H * L.nqp) * 4;
+    q.wide_off = L.wide_off;
+    q.bytes = L.wide_off + static_cast<size_t>(p.B * p.H * L.n_jb) * 4;
     return q;
 }
 
@@ -1058,13 +1117,15 @@ hipError_t launch_bf16_mfma(const Problem& p, void* workspace, hipStream_t strea
         return hipErrorInvalidConfiguration;
     _Float16* img = static_cast<_Float16*>(workspace);
     float* ref = reinterpret_cast<float*>(static_cast<char*>(workspace) + Ly.ref_off);
+    const int* wide = reinterpret_cast<const int*>(static_cast<char*>(workspace) + Ly.wide_off);
     hipError_t e = launch_prepass(p, Ly, workspace, n_qg, stream);
     if (e != hipSuccess) return e;
     if (Ly.n_split == 1) {
         hipLaunchKernelGGL(bf16_mfma_kernel, dim3(static_cast<unsigned>(total)), dim3(NTHR), 0, stream, p, sd, img, ref,
-                           static_cast<int>(Ly.n_jb), static_cast<int>(n_rg), static_cast<int>(Ly.nblk),
+                           wide, static_cast<int>(Ly.n_jb), static_cast<int>(n_rg), static_cast<int>(Ly.nblk),
                            static_cast<int>(total));
-        return hipGetLastError();
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        return launch_general_wide(p, wide, BJ, stream);     // the column blocks beyond the span
     }
     // split-key mode: partial states of every split, then one join into out (and lse)
     float* acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + Ly.split_off);
@@ -1076,9 +1137,10 @@ hipError_t launch_bf16_mfma(const Problem& p, void* workspace, hipStream_t strea
     q.st_l = sl;
     q.lse = nullptr;
     hipLaunchKernelGGL(bf16_mfma_kernel, dim3(static_cast<unsigned>(total), static_cast<unsigned>(Ly.n_split)),
-                       dim3(NTHR), 0, stream, q, sd, img, ref, static_cast<int>(Ly.n_jb), static_cast<int>(n_rg),
+                       dim3(NTHR), 0, stream, q, sd, img, ref, wide, static_cast<int>(Ly.n_jb), static_cast<int>(n_rg),
                        static_cast<int>(Ly.nblk), static_cast<int>(total));
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = launch_general_wide(q, wide, BJ, stream)) != hipSuccess) return e;   // split 0's state
     return launch_state_combine(acc, sm, sl, Ly.n_split, Ly.rows, D, p.out, p.lse, stream);
 }
 

@@ -216,9 +216,17 @@ __device__ __forceinline__ void dq_barrier_keep() {
     asm volatile("s_waitcnt vmcnt(%c0)\n\ts_barrier" ::"i"(keep) : "memory");
 }
 
+// True when any column block of (b, h) holds bias beyond the fp16 image's span (the
+// prepass's flags): dq and dk/dv of that (b, h) are then left to the fp32 kernels.
+__device__ __forceinline__ bool any_wide(const int* wide, int64_t bh, int n) {
+    int any = 0;
+    for (int t = 0; t < n; ++t) any |= wide[bh * n + t];
+    return any != 0;
+}
+
 __global__ void __launch_bounds__(DQ_THR, 2) bwd_dq_lds(BwdProblem p, const _Float16* img16, const float* ref16,
-                                                     Prepass16 pre, const __bf16* g16, const float* delta, int n_jb,
-                                                     int n_rg, int nblk, int total) {
+                                                     Prepass16 pre, const int* wide, const __bf16* g16,
+                                                     const float* delta, int n_jb, int n_rg, int nblk, int total) {
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c = lane & 31, h2 = lane >> 5;
@@ -241,6 +249,7 @@ __global__ void __launch_bounds__(DQ_THR, 2) bwd_dq_lds(BwdProblem p, const _Flo
     const int64_t N = p.N, H = p.H, HD = H * D, I = p.I;
     const int64_t b = bh / H, h = bh % H;
     const int64_t i0 = static_cast<int64_t>(rg) * DQ_R, j0 = static_cast<int64_t>(jb) * IMG_BJ;
+    if (any_wide(wide, bh, static_cast<int>(pre.n_jb))) return;
 
     DqCtx cx;
     {
@@ -464,9 +473,10 @@ __device__ __forceinline__ void dk_stage(const DkCtx& cx, int n, int wave, int l
     if (lane < 8) __builtin_amdgcn_global_load_lds(GPTR(cx.ls_src + qb * 4), LPTR(lds + cx.ls_dst), 16, 0, 0);
 }
 
-__global__ void __launch_bounds__(DK_THR, 2) bwd_dkdv_lds(BwdProblem p, const _Float16* imgT16, const __bf16* g16,
-                                                       const float* nbT2, const float* deltaT, int n_kb, int n_rg,
-                                                       int nqblk, int64_t NP, int total) {
+__global__ void __launch_bounds__(DK_THR, 2) bwd_dkdv_lds(BwdProblem p, const _Float16* imgT16, const int* wide,
+                                                       int n_wide, const __bf16* g16, const float* nbT2,
+                                                       const float* deltaT, int n_kb, int n_rg, int nqblk, int64_t NP,
+                                                       int total) {
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c = lane & 31, h2 = lane >> 5;
@@ -487,6 +497,7 @@ __global__ void __launch_bounds__(DK_THR, 2) bwd_dkdv_lds(BwdProblem p, const _F
     const int64_t N = p.N, H = p.H, HD = H * D, I = p.I;
     const int64_t b = bh / H, h = bh % H;
     const int64_t i0 = static_cast<int64_t>(rg) * DK_R, k0 = static_cast<int64_t>(kb) * IMG_BJ;
+    if (any_wide(wide, bh, n_wide)) return;
 
     DkCtx cx;
     {
@@ -1016,6 +1027,7 @@ hipError_t launch_backward_mfma(const BwdProblem& p, void* workspace, hipStream_
     float* img = reinterpret_cast<float*>(ws + Ly.img);
     _Float16* img16 = reinterpret_cast<_Float16*>(ws + Ly.pre16);
     const float* ref16 = reinterpret_cast<const float*>(ws + Ly.pre16 + Ly.pre.ref_off);
+    const int* wide = reinterpret_cast<const int*>(ws + Ly.pre16 + Ly.pre.wide_off);
     _Float16* imgT16 = reinterpret_cast<_Float16*>(ws + Ly.imgT16);
     __bf16* g16 = reinterpret_cast<__bf16*>(ws + Ly.g16);
     float* delta = reinterpret_cast<float*>(ws + Ly.delta);
@@ -1042,19 +1054,21 @@ hipError_t launch_backward_mfma(const BwdProblem& p, void* workspace, hipStream_
         const int64_t total = n_jb * n_rg * p.B * p.H;
         if (total > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
         hipLaunchKernelGGL(bwd_dq_lds, dim3(static_cast<unsigned>(total)), dim3(DQ_THR), 0, stream, p, img16, ref16,
-                           Ly.pre, g16, delta, static_cast<int>(n_jb), static_cast<int>(n_rg), static_cast<int>(nblk),
-                           static_cast<int>(total));
+                           Ly.pre, wide, g16, delta, static_cast<int>(n_jb), static_cast<int>(n_rg),
+                           static_cast<int>(nblk), static_cast<int>(total));
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     {
         const int64_t n_rg = (p.I + DK_R - 1) / DK_R;
         const int64_t total = n_jb * n_rg * p.B * p.H;
         if (total > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-        hipLaunchKernelGGL(bwd_dkdv_lds, dim3(static_cast<unsigned>(total)), dim3(DK_THR), 0, stream, p, imgT16, g16,
-                           nbT2, deltaT, static_cast<int>(n_jb), static_cast<int>(n_rg), static_cast<int>(nblk), Ly.NP,
-                           static_cast<int>(total));
+        hipLaunchKernelGGL(bwd_dkdv_lds, dim3(static_cast<unsigned>(total)), dim3(DK_THR), 0, stream, p, imgT16, wide,
+                           static_cast<int>(Ly.pre.n_jb), g16, nbT2, deltaT, static_cast<int>(n_jb),
+                           static_cast<int>(n_rg), static_cast<int>(nblk), Ly.NP, static_cast<int>(total));
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
+    // dq and dk/dv of every (b, h) whose bias spans more than the fp16 image keeps
+    if ((e = launch_backward_wide(p, wide, static_cast<int>(Ly.pre.n_jb), stream)) != hipSuccess) return e;
     const int64_t n_tq = (p.N + DB_Q - 1) / DB_Q, n_tk = (p.N + DB_K - 1) / DB_K;
     const int64_t total = n_tq * n_tk * p.B * p.H;
     if (total > 0x7FFFFFFF) return hipErrorInvalidConfiguration;

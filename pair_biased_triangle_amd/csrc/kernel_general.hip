@@ -29,19 +29,25 @@ __device__ __forceinline__ float load_elem(const void* base, int64_t idx) {
     }
 }
 
+template <int DP>
+struct Tiles {
+    float K[GK][DP + 1];
+    float V[GK][DP + 1];
+    float B[GJ][GK + 1];
+};
+
+// One line r of the workgroup's 64 queries.
 template <bool BF16, int DP>
-__global__ void __launch_bounds__(GJ) general_kernel(Problem p, Strides st) {
+__device__ void general_line(const Problem& p, const Strides& st, int64_t r, Tiles<DP>& sh) {
     const int64_t N = p.N, H = p.H, D = p.D, NK = p.nkeys();
-    const int64_t r = blockIdx.y;                 // line (row i, or column j for the ending node)
     const int64_t b = blockIdx.z / H, h = blockIdx.z % H;
     const int64_t j0 = static_cast<int64_t>(blockIdx.x) * GJ;
     const int tid = threadIdx.x;
     const int64_t j = j0 + tid;                   // this thread's query
     const int64_t line = b * st.batch + r * st.line + h * D;   // element offset of (b, line r, head h)
-
-    __shared__ float Ks[GK][DP + 1];
-    __shared__ float Vs[GK][DP + 1];
-    __shared__ float Bs[GJ][GK + 1];
+    float (&Ks)[GK][DP + 1] = sh.K;
+    float (&Vs)[GK][DP + 1] = sh.V;
+    float (&Bs)[GJ][GK + 1] = sh.B;
 
     float q[DP], acc[DP];
 #pragma unroll
@@ -162,25 +168,53 @@ __global__ void __launch_bounds__(GJ) general_kernel(Problem p, Strides st) {
     }
 }
 
+// Lines blockIdx.y, blockIdx.y + gridDim.y, ...  With `wide` set, only workgroups whose
+// query column block (of wide_cols columns) is flagged do any work.
+template <bool BF16, int DP>
+__global__ void __launch_bounds__(GJ) general_kernel(Problem p, Strides st, const int* wide, int wide_cols) {
+    if (wide) {
+        const int64_t n_jb = (p.N + wide_cols - 1) / wide_cols;
+        const int64_t jb = static_cast<int64_t>(blockIdx.x) * GJ / wide_cols;
+        if (!wide[static_cast<int64_t>(blockIdx.z) * n_jb + jb]) return;
+    }
+    __shared__ Tiles<DP> sh;
+    const int64_t lines = p.ending ? p.N : p.I;   // rows i, or columns j for the ending node (I == N)
+    for (int64_t r = blockIdx.y; r < lines; r += gridDim.y) {
+        __syncthreads();                          // the previous line's last reads of the tiles
+        general_line<BF16, DP>(p, st, r, sh);
+    }
+}
+
 template <bool BF16>
-hipError_t launch_dp(const Problem& p, hipStream_t stream) {
-    // lines: I rows (starting node) or N columns (ending node, I == N)
-    const dim3 grid(static_cast<unsigned>((p.N + GJ - 1) / GJ), static_cast<unsigned>(p.ending ? p.N : p.I),
-                    static_cast<unsigned>(p.B * p.H));
+hipError_t launch_dp(const Problem& p, const int* wide, int wide_cols, unsigned line_slots, hipStream_t stream) {
+    const dim3 grid(static_cast<unsigned>((p.N + GJ - 1) / GJ), line_slots, static_cast<unsigned>(p.B * p.H));
     const Strides st = strides_of(p);
     if (p.D <= 16)
-        hipLaunchKernelGGL((general_kernel<BF16, 16>), grid, dim3(GJ), 0, stream, p, st);
+        hipLaunchKernelGGL((general_kernel<BF16, 16>), grid, dim3(GJ), 0, stream, p, st, wide, wide_cols);
     else if (p.D <= 32)
-        hipLaunchKernelGGL((general_kernel<BF16, 32>), grid, dim3(GJ), 0, stream, p, st);
+        hipLaunchKernelGGL((general_kernel<BF16, 32>), grid, dim3(GJ), 0, stream, p, st, wide, wide_cols);
     else
-        hipLaunchKernelGGL((general_kernel<BF16, 64>), grid, dim3(GJ), 0, stream, p, st);
+        hipLaunchKernelGGL((general_kernel<BF16, 64>), grid, dim3(GJ), 0, stream, p, st, wide, wide_cols);
     return hipGetLastError();
 }
+
+int64_t lines_of(const Problem& p) { return p.ending ? p.N : p.I; }
 
 }  // namespace
 
 hipError_t launch_general(const Problem& p, bool bf16, hipStream_t stream) {
-    return bf16 ? launch_dp<true>(p, stream) : launch_dp<false>(p, stream);
+    // one workgroup per (64 queries, line, (b, h))
+    const unsigned slots = static_cast<unsigned>(lines_of(p));
+    return bf16 ? launch_dp<true>(p, nullptr, GJ, slots, stream) : launch_dp<false>(p, nullptr, GJ, slots, stream);
+}
+
+hipError_t launch_general_wide(const Problem& p, const int* wide, int cols, hipStream_t stream) {
+    if (cols % GJ != 0) return hipErrorInvalidValue;
+    // Usually no block is flagged, so the grid is kept small (each workgroup walks up to
+    // 64 line slots' worth of lines) to make the launch cheap when every workgroup returns.
+    constexpr int64_t kLineSlots = 64;
+    const int64_t lines = lines_of(p);
+    return launch_dp<true>(p, wide, cols, static_cast<unsigned>(lines < kLineSlots ? lines : kLineSlots), stream);
 }
 
 }  // namespace tri_attn

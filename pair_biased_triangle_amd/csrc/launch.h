@@ -65,6 +65,9 @@ struct BwdProblem {
     int64_t B, H, I, N, D;
 };
 hipError_t launch_backward(const BwdProblem& p, bool bf16, hipStream_t stream);
+// dq, dk and dv of the fp32 kernels (bf16 inputs), only for the (b, h) whose n_wide flags
+// wide[(b*H + h) * n_wide + t] include a nonzero one; every other workgroup returns at once.
+hipError_t launch_backward_wide(const BwdProblem& p, const int* wide, int n_wide, hipStream_t stream);
 
 // bf16 inputs, D == 32: matrix-core forward.  `workspace` (16-byte aligned, at least
 // bf16_workspace_bytes(p) bytes) receives its fp16 bias image and per-query references.
@@ -76,9 +79,12 @@ hipError_t launch_bf16_mfma(const Problem& p, void* workspace, hipStream_t strea
 // (bias + mask - r_j) * log2(e), one cols x 32 tile per (b, h, column block jb, key block n)
 // at ((b*H + h) * n_jb + jb) * nblk + n (row jj = query jb*cols + jj, its 32 keys in the
 // matrix-core register order, 16-byte parts swizzled by row), then r_j as fp32 at
-// ref_off + ((b*H + h) * nqp + j) * 4 (nqp = n_jb * cols).
+// ref_off + ((b*H + h) * nqp + j) * 4 (nqp = n_jb * cols), then one int per (b, h, jb) at
+// wide_off + ((b*H + h) * n_jb + jb) * 4, nonzero when the column block holds a finite
+// image value more than the image's span below r_j (its fp16 rounding would exceed the
+// bound the matrix-core kernels assume; such blocks go to the fp32 kernels).
 struct Prepass16 {
-    size_t ref_off, bytes;
+    size_t ref_off, wide_off, bytes;
     int64_t n_jb, nqp, nblk;
     int cols;
 };
@@ -104,6 +110,10 @@ hipError_t launch_backward_mfma(const BwdProblem& p, void* workspace, hipStream_
 
 // Any D <= 64, fp32 or bf16 inputs: plain fp32 kernel.
 hipError_t launch_general(const Problem& p, bool bf16, hipStream_t stream);
+// The same kernel (bf16 inputs) restricted to the query column blocks of `cols` columns
+// whose flag wide[(b*H + h) * n_jb + jb] is nonzero (n_jb = ceil(N / cols)); every other
+// workgroup returns at once.  cols is a multiple of 64.
+hipError_t launch_general_wide(const Problem& p, const int* wide, int cols, hipStream_t stream);
 
 // Partial softmax states (state mode above), rows = B * I * N * H queries of D values:
 // (acc, m, l) <- merge((acc, m, l), (acc_t, m_t, l_t)), and out = acc / l, lse = m + ln l.

@@ -134,15 +134,16 @@ def test_out_overlapping_an_input(lib):
 def test_workspace_bytes(lib):
     # bf16 D=32: the fp16 image, B*H*ceil(N/256)*ceil(N/32)*256*32*2 bytes (256-column
     # blocks; 32-key blocks over the whole key range, whatever T), padded to 256 bytes, then
-    # one fp32 reference per (b, h, query column padded to a multiple of 256)
+    # one fp32 reference per (b, h, query column padded to a multiple of 256), then one int
+    # span flag per (b, h, column block)
     def need(B, H, N, blocks):
         img = B * H * -(-N // 256) * blocks * 256 * 32 * 2
-        return -(-img // 256) * 256 + B * H * -(-N // 256) * 256 * 4
+        return -(-img // 256) * 256 + B * H * -(-N // 256) * 256 * 4 + B * H * -(-N // 256) * 4
     assert lib.tri_attn_workspace_bytes(1, 4, 2700, 2700, 32, 8, BF16) == need(1, 4, 2700, 85)
     assert lib.tri_attn_workspace_bytes(1, 4, 2700, 2700, 32, 200, BF16) == need(1, 4, 2700, 85)
     assert lib.tri_attn_workspace_bytes(1, 4, 1024, 4096, 32, 8, BF16) == need(1, 4, 4096, 128)
     assert lib.tri_attn_workspace_bytes(2, 3, 5, 7, 32, 3, BF16) == need(2, 3, 7, 1)
-    assert need(1, 4, 2700, 85) == 4 * 11 * 85 * 16384 + 4 * 11 * 1024
+    assert need(1, 4, 2700, 85) == 4 * 11 * 85 * 16384 + 4 * 11 * 1024 + 4 * 11 * 4
     assert lib.tri_attn_workspace_bytes(1, 4, 64, 64, 32, 1, FP32) == 0
     assert lib.tri_attn_workspace_bytes(1, 4, 64, 64, 16, 1, BF16) == 0
     assert lib.tri_attn_workspace_bytes(1, 4, 64, 64, 32, 0, BF16) == E_TILES
@@ -166,7 +167,8 @@ def test_workspace_bytes_of_one_row_calls(lib):
     assert lib.tri_attn_workspace_bytes(3, 4, 1, 100, 32, 3, BF16) == 0 == single_pass(3, 4, 100)
     assert lib.tri_attn_workspace_bytes(2, 4, 1, 300, 32, 4, BF16) == single_pass(2, 4, 300) > 0
     odd = lib.tri_attn_workspace_bytes(1, 4, 1, 301, 32, 2, BF16)
-    assert odd == 4 * 2 * 10 * 256 * 32 * 2 + 4 * 2 * 256 * 4        # image (2 column blocks x 10 key blocks) + r_j
+    assert odd == 4 * 2 * 10 * 256 * 32 * 2 + 4 * 2 * 256 * 4 + 4 * 2 * 4   # image (2 column blocks x 10 key
+                                                                             # blocks) + r_j + span flags
     assert P.workspace_bytes(1, 4, 1, 2700, 32, 8, 1) == single_pass(1, 4, 2700)
 
 

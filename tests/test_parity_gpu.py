@@ -293,9 +293,9 @@ def test_caller_workspace_matches_pool_workspace(torch_dev):
 
 
 def test_bias_jump_is_exact(torch_dev):
-    """A bias far above the rest of its row (+120 nats) and one far below (-1000): the
-    bf16 path takes bias + mask relative to each query's largest value, so both stay
-    exact; the large key's value is returned."""
+    """A bias far above the rest of its row (+120 nats) and one far below (-1000): both
+    leave the fp16 image's span, so those column blocks are computed by the fp32 kernel;
+    the large key's value is returned."""
     torch = torch_dev
     cfg = W.custom_config(B=1, I=24, N=260, H=2, D=32, dtype="bf16", n_key_tiles=3, seed=15)
     w = W.make_inputs(cfg)
