@@ -1,0 +1,123 @@
+"""GPU parity at the sizes the benchmark times, for every pass it times.
+
+* complex_n1024 (N = 1024, four chains): the whole output tensor against the oracle.
+* The backward at N = 2700 (single_gpu_n2700): one tri_attn_bwd over all 2700 rows, as
+  `bench.py --pass bwd` runs it, compared on 16 sampled lines i (dq, dk, dv of a line
+  depend on that line alone).  The forward statistics of those lines are the oracle's, so
+  the bar is the kernels' own (1e-2 x max(1, max|oracle|)); the other lines keep the GPU
+  forward's.  dbias sums over every line, so it is checked through a row-share call:
+  the same 16 lines gathered into I = 16 (tri_attn_bwd on a row share returns the dbias
+  of its rows), against the oracle's dbias of those lines.
+* The split-tile ring at N = 2700, T = 8 (`bench.py --pass ring`): the first step's
+  state, six updates folded into it and the final step, on sampled query rows.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from tests.test_parity_gpu import TOL, compare, edge_rows, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch_dev():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import pair_biased_triangle_amd as P
+    P.load_library()
+    return torch
+
+
+@pytest.fixture(scope="module")
+def n2700(torch_dev):
+    """single_gpu_n2700 inputs on the host and on the device."""
+    w = W.make_inputs("single_gpu_n2700")
+    dev = tuple(to_dev(torch_dev, x) for x in (w.q, w.k, w.v, w.bias, w.mask))
+    return w, dev
+
+
+@pytest.mark.timeout(600)
+def test_complex_n1024_full(torch_dev):
+    import pair_biased_triangle_amd as P
+    w = W.make_inputs("complex_n1024")
+    cfg = w.cfg
+    say(f"[full] complex_n1024: whole tensor, T={cfg.n_key_tiles}")
+    q, k, v, bias, mask = (to_dev(torch_dev, x) for x in (w.q, w.k, w.v, w.bias, w.mask))
+    out = P.tri_attn_fwd(q, k, v, bias, mask, n_key_tiles=cfg.n_key_tiles)
+    torch_dev.cuda.synchronize()
+    got = out.cpu().numpy()
+    del out
+    ref, _ = oracle.tri_attn(w.q, w.k, w.v, w.bias, w.mask, n_key_tiles=cfg.n_key_tiles)
+    compare(got, ref, TOL["bf16"], "complex_n1024 full tensor")
+
+
+LINES = np.array([0, 1, 2, 127, 128, 255, 256, 1023, 1349, 1350, 2047, 2048, 2600, 2697, 2698, 2699])
+
+
+def compare_rel(got, ref, rel, what):
+    scale = max(1.0, float(np.max(np.abs(ref))))
+    compare(got, ref, rel * scale, f"{what} (bar {rel:g} x {scale:.3g})")
+
+
+@pytest.mark.timeout(900)
+def test_backward_n2700_sampled_lines(torch_dev, n2700):
+    import pair_biased_triangle_amd as P
+    torch = torch_dev
+    w, (q, k, v, bias, mask) = n2700
+    cfg = w.cfg
+    sel = lambda a: np.ascontiguousarray(a[:, LINES])
+    say(f"[full] backward N=2700: oracle on {len(LINES)} lines")
+    dout = torch.randn(q.shape, dtype=torch.float32, device="cuda", generator=torch.Generator("cuda").manual_seed(5))
+    dout_l = sel(dout.cpu().numpy())
+    wq, wk, wv = sel(w.q), sel(w.k), sel(w.v)
+    ref_out, ref_lse = oracle.tri_attn(wq, wk, wv, w.bias, w.mask)
+    ref = oracle.tri_attn_bwd(wq, wk, wv, w.bias, w.mask, dout_l)
+
+    say("[full] backward N=2700: all 2700 lines on the GPU (the benchmark's call)")
+    out, lse = P.tri_attn_fwd_lse(q, k, v, bias, mask, n_key_tiles=cfg.n_key_tiles)
+    idx = torch.from_numpy(LINES).cuda()
+    out[:, idx] = torch.from_numpy(ref_out.astype(np.float32)).cuda()
+    lse[:, idx] = torch.from_numpy(ref_lse.astype(np.float32)).cuda()
+    dq, dk, dv, dbias = P.tri_attn_bwd(q, k, v, bias, mask, out, lse, dout)
+    torch.cuda.synchronize()
+    del dbias, out, lse
+    for name, g, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref[:3]):
+        compare_rel(g[:, idx].cpu().numpy(), r, 1e-2, f"{name} N=2700, 16 lines of a full call")
+    del dq, dk, dv
+
+    say("[full] backward N=2700: the same 16 lines as one row share (dbias of those lines)")
+    share = [to_dev(torch, x) for x in (wq, wk, wv)]
+    g = P.tri_attn_bwd(*share, bias, mask, torch.from_numpy(ref_out.astype(np.float32)).cuda(),
+                       torch.from_numpy(ref_lse.astype(np.float32)).cuda(), torch.from_numpy(dout_l).cuda())
+    torch.cuda.synchronize()
+    for name, got, r in zip(("dq", "dk", "dv", "dbias"), g, ref):
+        compare_rel(got.cpu().numpy(), r, 1e-2, f"{name} N=2700 row share I=16")
+
+
+@pytest.mark.timeout(600)
+def test_ring_n2700_t8_sampled(torch_dev, n2700):
+    import pair_biased_triangle_amd as P
+    torch = torch_dev
+    w, (q, k, v, bias, mask) = n2700
+    cfg = w.cfg
+    B, I, N, H, D, T = cfg.B, cfg.I, cfg.N, cfg.H, cfg.D, cfg.n_key_tiles
+    bounds = [t * (N // T) + min(t, N % T) for t in range(T + 1)]
+    say(f"[full] ring N=2700: state, {T - 2} updates, final step")
+    acc, m, l = P.tri_attn_tile_state(q, k, v, bias, mask, key_begin=bounds[0], key_end=bounds[1])
+    for t in range(1, T - 1):
+        P.tri_attn_tile_state_update(q, k, v, bias, mask, key_begin=bounds[t], key_end=bounds[t + 1],
+                                     acc=acc, m=m, l=l)
+    out, lse = P.tri_attn_tile_state_final(q, k, v, bias, mask, key_begin=bounds[T - 1], key_end=bounds[T],
+                                           acc=acc, m=m, l=l, want_lse=True)
+    torch.cuda.synchronize()
+    del acc, m, l
+    rows = edge_rows(cfg, np.random.default_rng(17))
+    idx = torch.from_numpy(rows).cuda()
+    got = out.view(-1, H, D)[idx].cpu().numpy()
+    got_lse = lse.view(-1, H)[idx].cpu().numpy()
+    ref, ref_lse = oracle.tri_attn(w.q, w.k, w.v, w.bias, w.mask, n_key_tiles=T, rows=rows)
+    compare(got, ref, TOL["bf16"], f"ring out, {len(rows)} rows")
+    compare(got_lse, ref_lse, TOL["bf16"], f"ring lse, {len(rows)} rows")
