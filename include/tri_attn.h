@@ -113,7 +113,8 @@ typedef enum {
     TRI_ATTN_ERR_HIP = -7,          /* the HIP runtime refused an allocation or launch */
     TRI_ATTN_ERR_ALIAS = -8,        /* an output (or the workspace) overlaps an input or another output */
     TRI_ATTN_ERR_WORKSPACE = -9,    /* caller workspace smaller than tri_attn_workspace_bytes() */
-    TRI_ATTN_ERR_RANGE = -10        /* key range not within 0 <= key_begin < key_end <= N */
+    TRI_ATTN_ERR_RANGE = -10,       /* key range not within 0 <= key_begin < key_end <= N */
+    TRI_ATTN_ERR_SCRATCH = -11      /* workspace need above tri_attn_noalloc_scratch_bytes() */
 } tri_attn_status;
 
 /*
@@ -162,6 +163,26 @@ int tri_attn_fwd_rows_ws(const void *q, const void *k, const void *v, const void
                          int64_t B, int64_t H, int64_t I, int64_t N, int64_t D,
                          int32_t n_key_tiles, int32_t dtype,
                          void *workspace, int64_t workspace_bytes, void *stream);
+
+/*
+ * tri_attn_fwd_rows for callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): the workspace is a static device array
+ * of tri_attn_noalloc_scratch_bytes() bytes (64 MiB) inside the library, one per GPU, held
+ * from the loading of the library's code until the process ends.  This call allocates
+ * nothing and frees nothing.  Problems whose workspace (tri_attn_workspace_bytes()) exceeds
+ * the array are rejected with TRI_ATTN_ERR_SCRATCH before any device work; B = 1, H = 4
+ * fits up to N = I = 2816.  Every call on one GPU uses the same array and leaves its
+ * contents there (each call writes all it reads): calls that overlap in time on one GPU,
+ * from several streams or threads, race on it and must be serialised by the caller.
+ * Arguments, results and other errors as tri_attn_fwd_rows.
+ */
+int tri_attn_fwd_rows_noalloc(const void *q, const void *k, const void *v, const void *bias,
+                              const float *mask, float *out,
+                              int64_t B, int64_t H, int64_t I, int64_t N, int64_t D,
+                              int32_t n_key_tiles, int32_t dtype, void *stream);
+
+/* Size in bytes of the static scratch of tri_attn_fwd_rows_noalloc. */
+int64_t tri_attn_noalloc_scratch_bytes(void);
 
 /*
  * Forward that also returns the natural-log normaliser of every query,

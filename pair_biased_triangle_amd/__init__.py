@@ -20,9 +20,10 @@ STATUS = {
     0: "TRI_ATTN_OK", -1: "TRI_ATTN_ERR_NULL", -2: "TRI_ATTN_ERR_SHAPE", -3: "TRI_ATTN_ERR_DTYPE",
     -4: "TRI_ATTN_ERR_UNSUPPORTED", -5: "TRI_ATTN_ERR_ALIGN", -6: "TRI_ATTN_ERR_TILES",
     -7: "TRI_ATTN_ERR_HIP", -8: "TRI_ATTN_ERR_ALIAS", -9: "TRI_ATTN_ERR_WORKSPACE",
-    -10: "TRI_ATTN_ERR_RANGE",
+    -10: "TRI_ATTN_ERR_RANGE", -11: "TRI_ATTN_ERR_SCRATCH",
 }
 EXPORTS = ("tri_attn_fwd", "tri_attn_fwd_rows", "tri_attn_fwd_rows_ws", "tri_attn_workspace_bytes",
+           "tri_attn_fwd_rows_noalloc", "tri_attn_noalloc_scratch_bytes",
            "tri_attn_fwd_lse", "tri_attn_fwd_ending", "tri_attn_tile_state", "tri_attn_tile_state_update",
            "tri_attn_tile_state_final", "tri_attn_state_merge",
            "tri_attn_state_finalize", "pair_bias_attn_fwd", "tri_attn_bwd",
@@ -52,6 +53,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         L.tri_attn_fwd_rows.restype = ctypes.c_int
         L.tri_attn_fwd_rows_ws.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, i32, vp, i64, vp]
         L.tri_attn_fwd_rows_ws.restype = ctypes.c_int
+        L.tri_attn_fwd_rows_noalloc.argtypes = L.tri_attn_fwd_rows.argtypes
+        L.tri_attn_fwd_rows_noalloc.restype = ctypes.c_int
+        L.tri_attn_noalloc_scratch_bytes.argtypes = []
+        L.tri_attn_noalloc_scratch_bytes.restype = ctypes.c_int64
         L.tri_attn_fwd_lse.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, i32, vp]
         L.tri_attn_fwd_lse.restype = ctypes.c_int
         L.tri_attn_fwd_ending.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, vp]
@@ -189,6 +194,24 @@ def tri_attn_fwd_rows_ws(q, k, v, bias, mask=None, *, workspace, n_key_tiles: in
                                   B, H, I, N, D, int(n_key_tiles), dt, _ptr(workspace), nbytes,
                                   _stream_handle(stream)))
     return out
+
+
+def tri_attn_fwd_rows_noalloc(q, k, v, bias, mask=None, *, n_key_tiles: int = 1, out=None, stream=None):
+    """tri_attn_fwd_rows on the library's static device scratch: the library allocates
+    nothing (for callers that cannot).  Calls on one GPU must not overlap in time.  Raises
+    TRI_ATTN_ERR_SCRATCH when the problem needs more than noalloc_scratch_bytes().  Calls
+    tri_attn_fwd_rows_noalloc."""
+    L = load_library()
+    dt, out = _validate(q, k, v, bias, mask, out)
+    B, I, N, H, D = q.shape
+    _check(L.tri_attn_fwd_rows_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(mask), _ptr(out),
+                                       B, H, I, N, D, int(n_key_tiles), dt, _stream_handle(stream)))
+    return out
+
+
+def noalloc_scratch_bytes() -> int:
+    """Size of the static scratch behind tri_attn_fwd_rows_noalloc."""
+    return int(load_library().tri_attn_noalloc_scratch_bytes())
 
 
 def _per_query(out, shape, name, t):

@@ -127,6 +127,12 @@ hipError_t launch_state_combine(const float* acc, const float* m, const float* l
                                 int64_t D, float* out, float* lse, hipStream_t stream);
 
 
+// The allocation-free entry point's workspace: a static device array of
+// static_scratch_bytes() bytes; static_scratch() returns its address on the current device
+// (looked up once per device).
+size_t static_scratch_bytes();
+hipError_t static_scratch(void** out);
+
 // Start of key tile t when N keys are cut into T near-equal contiguous tiles
 // (the first N mod T tiles hold one key more).
 __host__ __device__ inline int64_t tile_start(int64_t t, int64_t N, int64_t T) {

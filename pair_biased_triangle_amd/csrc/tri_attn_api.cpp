@@ -84,6 +84,7 @@ struct Call {
     float* fin = nullptr;                  // with update: final output (state only read)
     void* ws = nullptr;                    // caller workspace when ws_bytes >= 0
     int64_t ws_bytes = -1;
+    bool static_ws = false;                // workspace: the library's static device scratch
 };
 
 struct Span {
@@ -182,6 +183,16 @@ int run(const Call& c, void* stream) {
         return e == hipSuccess ? TRI_ATTN_OK : hip_fail(e);
     }
     const int64_t need = static_cast<int64_t>(mfma_workspace_bytes(p));
+    if (c.static_ws) {      // the static scratch: no allocation, bounded size
+        if (need > static_cast<int64_t>(tri_attn::static_scratch_bytes())) return TRI_ATTN_ERR_SCRATCH;
+        void* scratch = nullptr;
+        if (need > 0) {
+            const hipError_t e = tri_attn::static_scratch(&scratch);
+            if (e != hipSuccess) return hip_fail(e);
+        }
+        const hipError_t e = launch_mfma(p, scratch, s);
+        return e == hipSuccess ? TRI_ATTN_OK : hip_fail(e);
+    }
     if (c.ws_bytes >= 0) {  // caller-provided workspace
         if (!c.ws) return TRI_ATTN_ERR_NULL;
         if (!aligned(c.ws, 16)) return TRI_ATTN_ERR_ALIGN;
@@ -261,6 +272,16 @@ int tri_attn_fwd_rows_ws(const void* q, const void* k, const void* v, const void
     c.ws_bytes = workspace_bytes;
     return run(c, stream);
 }
+
+int tri_attn_fwd_rows_noalloc(const void* q, const void* k, const void* v, const void* bias, const float* mask,
+                              float* out, int64_t B, int64_t H, int64_t I, int64_t N, int64_t D, int32_t n_key_tiles,
+                              int32_t dtype, void* stream) {
+    Call c = make_call(q, k, v, bias, mask, out, B, H, I, N, D, n_key_tiles, dtype);
+    c.static_ws = true;
+    return run(c, stream);
+}
+
+int64_t tri_attn_noalloc_scratch_bytes(void) { return static_cast<int64_t>(tri_attn::static_scratch_bytes()); }
 
 int tri_attn_fwd_lse(const void* q, const void* k, const void* v, const void* bias, const float* mask, float* out,
                      float* lse, int64_t B, int64_t H, int64_t I, int64_t N, int64_t D, int32_t n_key_tiles,
@@ -422,12 +443,13 @@ const char* tri_attn_status_string(int status) {
         case TRI_ATTN_ERR_ALIAS: return "an output or the workspace overlaps an input or another output";
         case TRI_ATTN_ERR_WORKSPACE: return "workspace smaller than tri_attn_workspace_bytes()";
         case TRI_ATTN_ERR_RANGE: return "key range outside 0 <= key_begin < key_end <= N";
+        case TRI_ATTN_ERR_SCRATCH: return "the problem needs more workspace than the static scratch of tri_attn_fwd_rows_noalloc (tri_attn_noalloc_scratch_bytes())";
         default: return "unknown status";
     }
 }
 
 int tri_attn_last_hip_error(void) { return g_last_hip_error; }
 
-int tri_attn_version(void) { return 10400; }
+int tri_attn_version(void) { return 10500; }
 
 }  // extern "C"

@@ -16,8 +16,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "tri_attn.h")
 
 FP32, BF16 = 0, 1
-OK, E_NULL, E_SHAPE, E_DTYPE, E_UNSUP, E_ALIGN, E_TILES, E_HIP, E_ALIAS, E_WS, E_RANGE = (
-    0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10)
+OK, E_NULL, E_SHAPE, E_DTYPE, E_UNSUP, E_ALIGN, E_TILES, E_HIP, E_ALIAS, E_WS, E_RANGE, E_SCRATCH = (
+    0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10, -11)
 NAME = r"(?:tri_attn_\w+|pair_bias_attn_\w+)"
 
 
@@ -45,9 +45,9 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.tri_attn_version() == 10400
+    assert lib.tri_attn_version() == 10500
     seen = set()
-    codes = (OK, E_NULL, E_SHAPE, E_DTYPE, E_UNSUP, E_ALIGN, E_TILES, E_HIP, E_ALIAS, E_WS, E_RANGE)
+    codes = (OK, E_NULL, E_SHAPE, E_DTYPE, E_UNSUP, E_ALIGN, E_TILES, E_HIP, E_ALIAS, E_WS, E_RANGE, E_SCRATCH)
     for code in codes:
         s = P.status_string(code)
         assert s and s != "unknown status"
@@ -173,6 +173,27 @@ def test_workspace_bytes_of_one_row_calls(lib):
 
 
 WS = fake(0x70000000)
+
+
+def call_noalloc(lib, I=64, N=64, **kw):
+    a = dict(q=Q, k=K, v=V, bias=BIAS, mask=None, out=OUT, B=1, H=4, D=32, T=1, dtype=BF16)
+    a.update(kw)
+    return lib.tri_attn_fwd_rows_noalloc(a["q"], a["k"], a["v"], a["bias"], a["mask"], a["out"], a["B"], a["H"], I, N,
+                                         a["D"], a["T"], a["dtype"], None)
+
+
+def test_noalloc_scratch_limit(lib):
+    # the static scratch is 64 MiB; a workspace need above it is refused before any device
+    # work (N = 4096: the fp16 image alone is 4 * 16 * 128 * 16 KB = 128 MiB)
+    assert lib.tri_attn_noalloc_scratch_bytes() == 64 << 20 == P.noalloc_scratch_bytes()
+    assert lib.tri_attn_workspace_bytes(1, 4, 64, 4096, 32, 1, BF16) > 64 << 20
+    assert call_noalloc(lib, I=64, N=4096) == E_SCRATCH
+    assert lib.tri_attn_workspace_bytes(1, 4, 2816, 2816, 32, 8, BF16) <= 64 << 20    # the stated limit
+    assert lib.tri_attn_workspace_bytes(1, 4, 2817, 2817, 32, 8, BF16) > 64 << 20
+    # the ordinary checks come first
+    assert call_noalloc(lib, I=64, N=4096, q=None) == E_NULL
+    assert call_noalloc(lib, I=64, N=4096, T=0) == E_TILES
+    assert call_noalloc(lib, I=64, N=4096, out=fake(0x60000008)) == E_ALIGN
 
 
 def call_ws(lib, ws=WS, nbytes=1 << 30, **kw):
