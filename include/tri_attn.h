@@ -64,13 +64,18 @@
  * multiple of 256, keys to a multiple of 32), plus,
  * for calls too small to fill the GPU (fewer than 512 workgroups of 2 rows x 256 columns
  * and at least 16 key blocks), the partial softmax states of up to 16 key ranges that run
- * side by side and are then joined (16 * 34 * B * I * N * H bytes at most).  Every entry
- * point except tri_attn_fwd_rows_ws, and the matrix-core backward, obtains its workspace
- * stream-ordered on `stream` (hipMallocFromPoolAsync / hipFreeAsync) from a memory pool the
- * library creates once per device; the pool keeps freed memory reserved for later calls
- * (up to the largest workspace used) until the process ends.  tri_attn_fwd_rows_ws takes
- * the workspace from the caller instead and allocates nothing.  The fp32 paths need no
- * workspace.
+ * side by side and are then joined (16 * 34 * B * I * N * H bytes at most).  Three ways
+ * to provide it:
+ *   - the caller: every entry point that needs a workspace has a *_ws form that takes one
+ *     (sized by tri_attn_call_workspace_bytes) and allocates nothing;
+ *   - a static 64 MiB device array inside the library: tri_attn_fwd_rows_noalloc;
+ *   - the library's pool: the entry points without a workspace argument (the operator's
+ *     own signature has none) obtain it stream-ordered on `stream`
+ *     (hipMallocFromPoolAsync / hipFreeAsync) from a memory pool the library creates once
+ *     per device; the pool keeps freed memory reserved for later calls, at most the
+ *     largest workspace in use at once, until tri_attn_pool_release() or the end of the
+ *     process (tri_attn_pool_reserved_bytes() reports it).
+ * The fp32 paths need no workspace.
  *
  * Streams: calls only enqueue work on `stream` (a hipStream_t; NULL is the null
  * stream) and return without synchronising.  A kernel fault surfaces at the caller's
@@ -307,8 +312,9 @@ int tri_attn_state_finalize(const float *acc, const float *m, const float *l,
  *   dq, dk, dv [B, I, N, H, D] and dbias [B, H, N, N]: binary32 results, overwritten.
  * bf16 inputs with D == 32 and out, dout, dq, dk, dv 16-byte aligned run on matrix
  * cores: dout, p and ds are rounded to bf16 as product operands, sums are fp32, and a
- * workspace (bias images, bf16 dout, per-query statistics) comes from the library pool as
- * described above.  Every other case computes in fp32, any D <= 64, with no workspace.
+ * workspace (bias images, bf16 dout, per-query statistics; tri_attn_call_workspace_bytes
+ * with TRI_ATTN_CALL_BWD) comes from the library pool as described above, or from the
+ * caller through tri_attn_bwd_ws.  Every other case computes in fp32, any D <= 64, with no workspace.
  * Both are deterministic (every sum is taken by one thread in a fixed order, no atomics).
  * A query with lse = -inf contributes nothing.  q, k, v, bias 16-byte aligned, the other
  * pointers 4-byte aligned; no result may overlap an input or another result.  Same error
@@ -338,6 +344,82 @@ int pair_bias_attn_fwd(const void *q, const void *k, const void *v, const void *
                        const float *mask, float *out, float *lse,
                        int64_t B, int64_t H, int64_t N, int64_t D,
                        int32_t n_key_tiles, int32_t dtype, void *stream);
+
+/*
+ * Caller-workspace forms.  Each *_ws entry point is its namesake with a caller-owned
+ * device workspace appended (workspace, workspace_bytes): 16-byte aligned, at least
+ * tri_attn_call_workspace_bytes() bytes for that call (NULL with 0 bytes when that is 0),
+ * not overlapping any input or result, overwritten by the call and not to be touched by
+ * other work until the call's kernels have finished on `stream`.  The library allocates
+ * nothing in these calls.  Extra errors as tri_attn_fwd_rows_ws: TRI_ATTN_ERR_WORKSPACE
+ * (too small or negative size), TRI_ATTN_ERR_NULL (NULL where bytes are needed),
+ * TRI_ATTN_ERR_ALIGN, TRI_ATTN_ERR_ALIAS.  Everything else as the namesake.
+ */
+int tri_attn_fwd_lse_ws(const void *q, const void *k, const void *v, const void *bias,
+                        const float *mask, float *out, float *lse,
+                        int64_t B, int64_t H, int64_t I, int64_t N, int64_t D,
+                        int32_t n_key_tiles, int32_t dtype,
+                        void *workspace, int64_t workspace_bytes, void *stream);
+int tri_attn_fwd_ending_ws(const void *q, const void *k, const void *v, const void *bias,
+                           const float *mask, float *out, float *lse,
+                           int64_t B, int64_t H, int64_t N, int64_t D,
+                           int32_t n_key_tiles, int32_t dtype,
+                           void *workspace, int64_t workspace_bytes, void *stream);
+int tri_attn_tile_state_ws(const void *q, const void *k, const void *v, const void *bias,
+                           const float *mask, float *acc, float *m, float *l,
+                           int64_t B, int64_t H, int64_t I, int64_t N, int64_t D,
+                           int64_t key_begin, int64_t key_end, int32_t ending, int32_t dtype,
+                           void *workspace, int64_t workspace_bytes, void *stream);
+int tri_attn_tile_state_update_ws(const void *q, const void *k, const void *v, const void *bias,
+                                  const float *mask, float *acc, float *m, float *l,
+                                  int64_t B, int64_t H, int64_t I, int64_t N, int64_t D,
+                                  int64_t key_begin, int64_t key_end, int32_t ending, int32_t dtype,
+                                  void *workspace, int64_t workspace_bytes, void *stream);
+int tri_attn_tile_state_final_ws(const void *q, const void *k, const void *v, const void *bias,
+                                 const float *mask, const float *acc, const float *m, const float *l,
+                                 float *out, float *lse,
+                                 int64_t B, int64_t H, int64_t I, int64_t N, int64_t D,
+                                 int64_t key_begin, int64_t key_end, int32_t ending, int32_t dtype,
+                                 void *workspace, int64_t workspace_bytes, void *stream);
+int pair_bias_attn_fwd_ws(const void *q, const void *k, const void *v, const void *bias,
+                          const float *mask, float *out, float *lse,
+                          int64_t B, int64_t H, int64_t N, int64_t D,
+                          int32_t n_key_tiles, int32_t dtype,
+                          void *workspace, int64_t workspace_bytes, void *stream);
+int tri_attn_bwd_ws(const void *q, const void *k, const void *v, const void *bias,
+                    const float *mask, const float *out, const float *lse, const float *dout,
+                    float *dq, float *dk, float *dv, float *dbias,
+                    int64_t B, int64_t H, int64_t I, int64_t N, int64_t D, int32_t dtype,
+                    void *workspace, int64_t workspace_bytes, void *stream);
+
+/* which call tri_attn_call_workspace_bytes sizes */
+typedef enum {
+    TRI_ATTN_CALL_FWD = 0,            /* tri_attn_fwd, _rows, _lse (and their _ws forms) */
+    TRI_ATTN_CALL_ENDING = 1,         /* tri_attn_fwd_ending (I == N) */
+    TRI_ATTN_CALL_STATE = 2,          /* tri_attn_tile_state, _update, _final, starting node */
+    TRI_ATTN_CALL_STATE_ENDING = 3,   /* the same, ending node (I == N) */
+    TRI_ATTN_CALL_PAIR_BIAS = 4,      /* pair_bias_attn_fwd (I == 1) */
+    TRI_ATTN_CALL_BWD = 5             /* tri_attn_bwd */
+} tri_attn_call;
+
+/*
+ * Workspace bytes (0 if none) of one call of kind `call` (a tri_attn_call) at these
+ * sizes; key_count is the number of keys of a ring step's range (state calls only, 1 to
+ * N; pass N otherwise).  For the backward it assumes the matrix-core path (16-byte
+ * aligned fp32 tensors).  Negative tri_attn_status on invalid sizes (the checks of the
+ * call itself that need no pointers).
+ */
+int64_t tri_attn_call_workspace_bytes(int32_t call, int64_t B, int64_t H, int64_t I, int64_t N,
+                                      int64_t D, int64_t key_count, int32_t dtype);
+
+/*
+ * The library's memory pool (used by the entry points that take no workspace argument):
+ * bytes it holds reserved on the current device (0 before its first use), and a release of
+ * every device pool's unused memory back to the driver (memory of calls still in flight on
+ * a stream stays until they finish).  TRI_ATTN_ERR_HIP on a HIP error.
+ */
+int64_t tri_attn_pool_reserved_bytes(void);
+int tri_attn_pool_release(void);
 
 /* Static, NUL-terminated description of a tri_attn_status (unknown codes included). */
 const char *tri_attn_status_string(int status);

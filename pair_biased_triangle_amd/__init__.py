@@ -15,6 +15,8 @@ LIB_PATH = os.path.join(PKG, "libtri_attn.so")
 
 # tri_attn_dtype
 TRI_ATTN_FP32, TRI_ATTN_BF16 = 0, 1
+# tri_attn_call (kinds of calls that tri_attn_call_workspace_bytes sizes)
+CALL_FWD, CALL_ENDING, CALL_STATE, CALL_STATE_ENDING, CALL_PAIR_BIAS, CALL_BWD = range(6)
 # tri_attn_status
 STATUS = {
     0: "TRI_ATTN_OK", -1: "TRI_ATTN_ERR_NULL", -2: "TRI_ATTN_ERR_SHAPE", -3: "TRI_ATTN_ERR_DTYPE",
@@ -24,6 +26,9 @@ STATUS = {
 }
 EXPORTS = ("tri_attn_fwd", "tri_attn_fwd_rows", "tri_attn_fwd_rows_ws", "tri_attn_workspace_bytes",
            "tri_attn_fwd_rows_noalloc", "tri_attn_noalloc_scratch_bytes",
+           "tri_attn_fwd_lse_ws", "tri_attn_fwd_ending_ws", "tri_attn_tile_state_ws", "tri_attn_tile_state_update_ws",
+           "tri_attn_tile_state_final_ws", "pair_bias_attn_fwd_ws", "tri_attn_bwd_ws",
+           "tri_attn_call_workspace_bytes", "tri_attn_pool_reserved_bytes", "tri_attn_pool_release",
            "tri_attn_fwd_lse", "tri_attn_fwd_ending", "tri_attn_tile_state", "tri_attn_tile_state_update",
            "tri_attn_tile_state_final", "tri_attn_state_merge",
            "tri_attn_state_finalize", "pair_bias_attn_fwd", "tri_attn_bwd",
@@ -77,6 +82,23 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         L.pair_bias_attn_fwd.restype = ctypes.c_int
         L.tri_attn_bwd.argtypes = [vp] * 12 + [i64, i64, i64, i64, i64, i32, vp]
         L.tri_attn_bwd.restype = ctypes.c_int
+        W = [vp, i64]   # workspace, workspace_bytes
+        L.tri_attn_fwd_lse_ws.argtypes = list(L.tri_attn_fwd_lse.argtypes)[:-1] + W + [vp]
+        L.tri_attn_fwd_ending_ws.argtypes = list(L.tri_attn_fwd_ending.argtypes)[:-1] + W + [vp]
+        L.tri_attn_tile_state_ws.argtypes = list(L.tri_attn_tile_state.argtypes)[:-1] + W + [vp]
+        L.tri_attn_tile_state_update_ws.argtypes = list(L.tri_attn_tile_state_update.argtypes)[:-1] + W + [vp]
+        L.tri_attn_tile_state_final_ws.argtypes = list(L.tri_attn_tile_state_final.argtypes)[:-1] + W + [vp]
+        L.pair_bias_attn_fwd_ws.argtypes = list(L.pair_bias_attn_fwd.argtypes)[:-1] + W + [vp]
+        L.tri_attn_bwd_ws.argtypes = list(L.tri_attn_bwd.argtypes)[:-1] + W + [vp]
+        for name in ("tri_attn_fwd_lse_ws", "tri_attn_fwd_ending_ws", "tri_attn_tile_state_ws",
+                     "tri_attn_tile_state_update_ws", "tri_attn_tile_state_final_ws", "pair_bias_attn_fwd_ws",
+                     "tri_attn_bwd_ws", "tri_attn_pool_release"):
+            getattr(L, name).restype = ctypes.c_int
+        L.tri_attn_pool_release.argtypes = []
+        L.tri_attn_pool_reserved_bytes.argtypes = []
+        L.tri_attn_pool_reserved_bytes.restype = ctypes.c_int64
+        L.tri_attn_call_workspace_bytes.argtypes = [i32, i64, i64, i64, i64, i64, i64, i32]
+        L.tri_attn_call_workspace_bytes.restype = ctypes.c_int64
         L.tri_attn_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i32, i32]
         L.tri_attn_workspace_bytes.restype = ctypes.c_int64
         L.tri_attn_status_string.argtypes = [ctypes.c_int]
@@ -144,33 +166,14 @@ def _validate(q, k, v, bias, mask, out):
     return dt, out
 
 
-def tri_attn_fwd_rows(q, k, v, bias, mask=None, *, n_key_tiles: int = 1, out=None, stream=None):
-    """Triangle attention for the query rows i held in q, k, v (one rank's row share).
-
-    q, k, v: [B, I, N, H, D] (bfloat16 or float32, device, contiguous); bias: [B, H, N, N]
-    of the same dtype; mask: [B, N] float32 additive or None.  Returns out [B, I, N, H, D]
-    float32 (written into ``out`` when given).  Enqueued on ``stream`` (default: torch's
-    current stream); nothing is synchronised.  Calls the C entry point tri_attn_fwd_rows.
-    """
-    L = load_library()
-    dt, out = _validate(q, k, v, bias, mask, out)
-    B, I, N, H, D = q.shape
-    _check(L.tri_attn_fwd_rows(_ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(mask), _ptr(out),
-                               B, H, I, N, D, int(n_key_tiles), dt, _stream_handle(stream)))
-    return out
-
-
-def tri_attn_fwd(q, k, v, bias, mask=None, *, n_key_tiles: int = 1, out=None, stream=None):
-    """Triangle attention over all N query rows: q, k, v are [B, N, N, H, D].  Calls the C
-    entry point tri_attn_fwd; otherwise as tri_attn_fwd_rows."""
-    L = load_library()
-    if q.dim() != 5 or q.shape[1] != q.shape[2]:
-        raise ValueError("tri_attn_fwd needs q of shape [B, N, N, H, D]; use tri_attn_fwd_rows for a row share")
-    dt, out = _validate(q, k, v, bias, mask, out)
-    B, _, N, H, D = q.shape
-    _check(L.tri_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(mask), _ptr(out),
-                          B, H, N, D, int(n_key_tiles), dt, _stream_handle(stream)))
-    return out
+def call_workspace_bytes(kind: int, B: int, H: int, I: int, N: int, D: int, key_count: int, dtype_code: int) -> int:
+    """Device workspace (bytes, 0 if none) of one call of kind ``kind`` (CALL_FWD, ...) at
+    these sizes; ``key_count`` is the number of keys of a ring step's range (state calls).
+    Calls tri_attn_call_workspace_bytes."""
+    n = load_library().tri_attn_call_workspace_bytes(int(kind), B, H, I, N, D, int(key_count), dtype_code)
+    if n < 0:
+        raise TriAttnError(int(n), status_string(int(n)))
+    return int(n)
 
 
 def workspace_bytes(B: int, H: int, I: int, N: int, D: int, n_key_tiles: int, dtype_code: int) -> int:
@@ -181,19 +184,92 @@ def workspace_bytes(B: int, H: int, I: int, N: int, D: int, n_key_tiles: int, dt
     return int(n)
 
 
-def tri_attn_fwd_rows_ws(q, k, v, bias, mask=None, *, workspace, n_key_tiles: int = 1, out=None, stream=None):
-    """tri_attn_fwd_rows with a caller-owned device workspace (a uint8 tensor of at least
-    workspace_bytes(...) bytes); the library allocates nothing.  Calls tri_attn_fwd_rows_ws."""
+def pool_reserved_bytes() -> int:
+    """Bytes the library's memory pool holds on the current device (tri_attn_pool_reserved_bytes)."""
+    n = load_library().tri_attn_pool_reserved_bytes()
+    if n < 0:
+        _check(int(n))
+    return int(n)
+
+
+def pool_release() -> None:
+    """Return the unused memory of the library's pools to the driver (tri_attn_pool_release)."""
+    _check(load_library().tri_attn_pool_release())
+
+
+LIBRARY = "library"   # workspace=LIBRARY: call the entry point without a workspace argument (library pool)
+
+
+def _workspace(workspace, kind, sizes, key_count, dt, device, stream):
+    """The (pointer, bytes) pair a *_ws entry point takes, plus the tensor to keep alive, or
+    None when the call should go to the entry point without a workspace (its pool).
+
+    workspace=None: a uint8 tensor of exactly the call's need from torch's allocator (the
+    library then allocates nothing); a tensor: used as given; LIBRARY: the pool."""
+    import torch
+    if isinstance(workspace, str):
+        if workspace != LIBRARY:
+            raise ValueError(f"workspace must be None, a device tensor or {LIBRARY!r}")
+        return None
+    B, H, I, N, D = sizes
+    if workspace is None:
+        need = call_workspace_bytes(kind, B, H, I, N, D, key_count, dt)
+        if need == 0:
+            return (None, 0), None
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+        if stream is not None and stream != torch.cuda.current_stream(device):
+            workspace.record_stream(stream)   # torch must not hand it out again before the call's kernels end
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    return (_ptr(workspace), workspace.numel() * workspace.element_size()), workspace
+
+
+def tri_attn_fwd_rows(q, k, v, bias, mask=None, *, n_key_tiles: int = 1, out=None, workspace=None, stream=None):
+    """Triangle attention for the query rows i held in q, k, v (one rank's row share).
+
+    q, k, v: [B, I, N, H, D] (bfloat16 or float32, device, contiguous); bias: [B, H, N, N]
+    of the same dtype; mask: [B, N] float32 additive or None.  Returns out [B, I, N, H, D]
+    float32 (written into ``out`` when given).  Enqueued on ``stream`` (default: torch's
+    current stream); nothing is synchronised.  The workspace comes from torch (``workspace``
+    None: the C entry point tri_attn_fwd_rows_ws, so the library allocates nothing), from
+    the caller (a uint8 device tensor), or from the library's pool (``workspace=LIBRARY``:
+    the C entry point tri_attn_fwd_rows).
+    """
     L = load_library()
     dt, out = _validate(q, k, v, bias, mask, out)
     B, I, N, H, D = q.shape
-    if workspace is None or not workspace.is_cuda or not workspace.is_contiguous():
-        raise ValueError("workspace must be a contiguous device tensor")
-    nbytes = workspace.numel() * workspace.element_size()
-    _check(L.tri_attn_fwd_rows_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(mask), _ptr(out),
-                                  B, H, I, N, D, int(n_key_tiles), dt, _ptr(workspace), nbytes,
-                                  _stream_handle(stream)))
+    ws = _workspace(workspace, CALL_FWD, (B, H, I, N, D), N, dt, q.device, stream)
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(mask), _ptr(out), B, H, I, N, D, int(n_key_tiles), dt)
+    if ws is None:
+        _check(L.tri_attn_fwd_rows(*args, _stream_handle(stream)))
+    else:
+        _check(L.tri_attn_fwd_rows_ws(*args, *ws[0], _stream_handle(stream)))
     return out
+
+
+def tri_attn_fwd(q, k, v, bias, mask=None, *, n_key_tiles: int = 1, out=None, workspace=None, stream=None):
+    """Triangle attention over all N query rows: q, k, v are [B, N, N, H, D].  With
+    ``workspace=LIBRARY`` it calls the C entry point tri_attn_fwd; otherwise as
+    tri_attn_fwd_rows (with I == N)."""
+    L = load_library()
+    if q.dim() != 5 or q.shape[1] != q.shape[2]:
+        raise ValueError("tri_attn_fwd needs q of shape [B, N, N, H, D]; use tri_attn_fwd_rows for a row share")
+    if isinstance(workspace, str) and workspace == LIBRARY:
+        dt, out = _validate(q, k, v, bias, mask, out)
+        B, _, N, H, D = q.shape
+        _check(L.tri_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(mask), _ptr(out),
+                              B, H, N, D, int(n_key_tiles), dt, _stream_handle(stream)))
+        return out
+    return tri_attn_fwd_rows(q, k, v, bias, mask, n_key_tiles=n_key_tiles, out=out, workspace=workspace, stream=stream)
+
+
+def tri_attn_fwd_rows_ws(q, k, v, bias, mask=None, *, workspace, n_key_tiles: int = 1, out=None, stream=None):
+    """tri_attn_fwd_rows with a caller-owned device workspace (a uint8 tensor of at least
+    workspace_bytes(...) bytes); the library allocates nothing.  Calls tri_attn_fwd_rows_ws."""
+    if workspace is None or isinstance(workspace, str):
+        raise ValueError("workspace must be a contiguous device tensor")
+    return tri_attn_fwd_rows(q, k, v, bias, mask, n_key_tiles=n_key_tiles, out=out, workspace=workspace,
+                             stream=stream)
 
 
 def tri_attn_fwd_rows_noalloc(q, k, v, bias, mask=None, *, n_key_tiles: int = 1, out=None, stream=None):
@@ -224,24 +300,31 @@ def _per_query(out, shape, name, t):
     return t
 
 
-def tri_attn_fwd_lse(q, k, v, bias, mask=None, *, n_key_tiles: int = 1, out=None, lse=None, stream=None):
+def tri_attn_fwd_lse(q, k, v, bias, mask=None, *, n_key_tiles: int = 1, out=None, lse=None, workspace=None,
+                     stream=None):
     """tri_attn_fwd_rows that also returns lse [B, I, N, H] (natural-log normaliser of every
-    query; -inf where no key survives).  Returns (out, lse).  Calls tri_attn_fwd_lse."""
+    query; -inf where no key survives).  Returns (out, lse).  Calls tri_attn_fwd_lse_ws (or
+    tri_attn_fwd_lse with workspace=LIBRARY)."""
     L = load_library()
     dt, out = _validate(q, k, v, bias, mask, out)
     B, I, N, H, D = q.shape
     lse = _per_query(out, (B, I, N, H), "lse", lse)
-    _check(L.tri_attn_fwd_lse(_ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(mask), _ptr(out), _ptr(lse),
-                              B, H, I, N, D, int(n_key_tiles), dt, _stream_handle(stream)))
+    ws = _workspace(workspace, CALL_FWD, (B, H, I, N, D), N, dt, q.device, stream)
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(mask), _ptr(out), _ptr(lse), B, H, I, N, D,
+            int(n_key_tiles), dt)
+    if ws is None:
+        _check(L.tri_attn_fwd_lse(*args, _stream_handle(stream)))
+    else:
+        _check(L.tri_attn_fwd_lse_ws(*args, *ws[0], _stream_handle(stream)))
     return out, lse
 
 
 def tri_attn_fwd_ending(q, k, v, bias, mask=None, *, n_key_tiles: int = 1, out=None, lse=None,
-                        want_lse: bool = False, stream=None):
+                        want_lse: bool = False, workspace=None, stream=None):
     """Ending-node triangle attention (attention along columns, bias transposed):
     out[b,i,j] = sum_k softmax_k(q[b,i,j].k[b,k,j]/sqrt(D) + bias[b,h,k,i] + mask[b,k]) v[b,k,j].
     q, k, v: [B, N, N, H, D].  Returns out, or (out, lse) when want_lse or lse is given.
-    Calls tri_attn_fwd_ending."""
+    Calls tri_attn_fwd_ending_ws (or tri_attn_fwd_ending with workspace=LIBRARY)."""
     L = load_library()
     if q.dim() != 5 or q.shape[1] != q.shape[2]:
         raise ValueError("tri_attn_fwd_ending needs q of shape [B, N, N, H, D]")
@@ -249,48 +332,64 @@ def tri_attn_fwd_ending(q, k, v, bias, mask=None, *, n_key_tiles: int = 1, out=N
     B, _, N, H, D = q.shape
     if want_lse or lse is not None:
         lse = _per_query(out, (B, N, N, H), "lse", lse)
-    _check(L.tri_attn_fwd_ending(_ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(mask), _ptr(out), _ptr(lse),
-                                 B, H, N, D, int(n_key_tiles), dt, _stream_handle(stream)))
+    ws = _workspace(workspace, CALL_ENDING, (B, H, N, N, D), N, dt, q.device, stream)
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(mask), _ptr(out), _ptr(lse), B, H, N, D, int(n_key_tiles), dt)
+    if ws is None:
+        _check(L.tri_attn_fwd_ending(*args, _stream_handle(stream)))
+    else:
+        _check(L.tri_attn_fwd_ending_ws(*args, *ws[0], _stream_handle(stream)))
     return (out, lse) if lse is not None else out
 
 
+def _ring_step(name, q, k, v, bias, mask, key_begin, key_end, ending, acc, m, l, extra, dt, workspace, stream):
+    L = load_library()
+    B, I, N, H, D = q.shape
+    kind = CALL_STATE_ENDING if ending else CALL_STATE
+    count = max(1, min(int(key_end), N) - max(int(key_begin), 0))   # invalid ranges are refused by the call itself
+    ws = _workspace(workspace, kind, (B, H, I, N, D), count, dt, q.device, stream)
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(mask), _ptr(acc), _ptr(m), _ptr(l), *extra,
+            B, H, I, N, D, int(key_begin), int(key_end), int(bool(ending)), dt)
+    if ws is None:
+        _check(getattr(L, name)(*args, _stream_handle(stream)))
+    else:
+        _check(getattr(L, name + "_ws")(*args, *ws[0], _stream_handle(stream)))
+
+
 def tri_attn_tile_state(q, k, v, bias, mask=None, *, key_begin: int, key_end: int, ending: bool = False,
-                        acc=None, m=None, l=None, stream=None):
+                        acc=None, m=None, l=None, workspace=None, stream=None):
     """Partial softmax state of the keys [key_begin, key_end) as one ring step: returns
     (acc [B, I, N, H, D] unnormalised, m [B, I, N, H] reference, l [B, I, N, H] normaliser).
-    Calls tri_attn_tile_state."""
-    L = load_library()
+    Calls tri_attn_tile_state_ws (or tri_attn_tile_state with workspace=LIBRARY)."""
     dt, acc = _validate(q, k, v, bias, mask, acc)
     B, I, N, H, D = q.shape
     m = _per_query(acc, (B, I, N, H), "m", m)
     l = _per_query(acc, (B, I, N, H), "l", l)
-    _check(L.tri_attn_tile_state(_ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(mask), _ptr(acc), _ptr(m), _ptr(l),
-                                 B, H, I, N, D, int(key_begin), int(key_end), int(bool(ending)), dt,
-                                 _stream_handle(stream)))
+    _ring_step("tri_attn_tile_state", q, k, v, bias, mask, key_begin, key_end, ending, acc, m, l, (), dt,
+               workspace, stream)
     return acc, m, l
 
 
 def tri_attn_tile_state_update(q, k, v, bias, mask=None, *, key_begin: int, key_end: int, acc, m, l,
-                               ending: bool = False, stream=None):
+                               ending: bool = False, workspace=None, stream=None):
     """Fold the keys [key_begin, key_end), as one ring step, into the running state
-    (acc, m, l) in place (l = 0 is the empty state).  Calls tri_attn_tile_state_update."""
-    L = load_library()
+    (acc, m, l) in place (l = 0 is the empty state).  Calls tri_attn_tile_state_update_ws
+    (or tri_attn_tile_state_update with workspace=LIBRARY)."""
     dt, acc = _validate(q, k, v, bias, mask, acc)
     B, I, N, H, D = q.shape
     m = _per_query(acc, (B, I, N, H), "m", m)
     l = _per_query(acc, (B, I, N, H), "l", l)
-    _check(L.tri_attn_tile_state_update(_ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(mask), _ptr(acc), _ptr(m),
-                                        _ptr(l), B, H, I, N, D, int(key_begin), int(key_end), int(bool(ending)), dt,
-                                        _stream_handle(stream)))
+    _ring_step("tri_attn_tile_state_update", q, k, v, bias, mask, key_begin, key_end, ending, acc, m, l, (), dt,
+               workspace, stream)
     return acc, m, l
 
 
 def tri_attn_tile_state_final(q, k, v, bias, mask=None, *, key_begin: int, key_end: int, acc, m, l,
-                              ending: bool = False, out=None, lse=None, want_lse: bool = False, stream=None):
+                              ending: bool = False, out=None, lse=None, want_lse: bool = False, workspace=None,
+                              stream=None):
     """The last ring step: fold the keys [key_begin, key_end) into the state (acc, m, l),
     which is only read, and return the finalised out [B, I, N, H, D] (and lse [B, I, N, H]
-    when asked).  Calls tri_attn_tile_state_final."""
-    L = load_library()
+    when asked).  Calls tri_attn_tile_state_final_ws (or tri_attn_tile_state_final with
+    workspace=LIBRARY)."""
     dt, acc = _validate(q, k, v, bias, mask, acc)
     _, out = _validate(q, k, v, bias, mask, out)
     B, I, N, H, D = q.shape
@@ -298,9 +397,8 @@ def tri_attn_tile_state_final(q, k, v, bias, mask=None, *, key_begin: int, key_e
     l = _per_query(acc, (B, I, N, H), "l", l)
     if want_lse or lse is not None:
         lse = _per_query(acc, (B, I, N, H), "lse", lse)
-    _check(L.tri_attn_tile_state_final(_ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(mask), _ptr(acc), _ptr(m), _ptr(l),
-                                       _ptr(out), _ptr(lse), B, H, I, N, D, int(key_begin), int(key_end),
-                                       int(bool(ending)), dt, _stream_handle(stream)))
+    _ring_step("tri_attn_tile_state_final", q, k, v, bias, mask, key_begin, key_end, ending, acc, m, l,
+               (_ptr(out), _ptr(lse)), dt, workspace, stream)
     return (out, lse) if lse is not None else out
 
 
@@ -341,9 +439,10 @@ def tri_attn_state_finalize(acc, m, l, *, out=None, lse=None, stream=None):
 
 
 def pair_bias_attn_fwd(q, k, v, bias, mask=None, *, n_key_tiles: int = 1, out=None, lse=None,
-                       want_lse: bool = False, stream=None):
+                       want_lse: bool = False, workspace=None, stream=None):
     """Attention with pair bias: q, k, v [B, N, H, D], bias [B, H, N, N], mask [B, N] or None.
-    Returns out [B, N, H, D] float32, or (out, lse [B, N, H]).  Calls pair_bias_attn_fwd."""
+    Returns out [B, N, H, D] float32, or (out, lse [B, N, H]).  Calls pair_bias_attn_fwd_ws
+    (or pair_bias_attn_fwd with workspace=LIBRARY)."""
     L = load_library()
     if q.dim() != 4:
         raise ValueError("pair_bias_attn_fwd needs q, k, v of shape [B, N, H, D]")
@@ -353,18 +452,23 @@ def pair_bias_attn_fwd(q, k, v, bias, mask=None, *, n_key_tiles: int = 1, out=No
     dt, out5 = _validate(q5, k5, v5, bias, mask, out5)
     if want_lse or lse is not None:
         lse = _per_query(out5, (B, N, H), "lse", lse)
-    _check(L.pair_bias_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(mask), _ptr(out5), _ptr(lse),
-                                B, H, N, D, int(n_key_tiles), dt, _stream_handle(stream)))
+    ws = _workspace(workspace, CALL_PAIR_BIAS, (B, H, 1, N, D), N, dt, q.device, stream)
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(mask), _ptr(out5), _ptr(lse), B, H, N, D, int(n_key_tiles), dt)
+    if ws is None:
+        _check(L.pair_bias_attn_fwd(*args, _stream_handle(stream)))
+    else:
+        _check(L.pair_bias_attn_fwd_ws(*args, *ws[0], _stream_handle(stream)))
     out = out5.view(B, N, H, D)
     return (out, lse) if lse is not None else out
 
 
-def tri_attn_bwd(q, k, v, bias, mask, out, lse, dout, *, stream=None):
+def tri_attn_bwd(q, k, v, bias, mask, out, lse, dout, *, workspace=None, stream=None):
     """Gradients of the starting-node operation for the upstream gradient dout.
 
     q, k, v, bias, mask: the forward's inputs; out, lse: its results (tri_attn_fwd_lse);
     dout: float32 shaped like q.  Returns (dq, dk, dv, dbias), float32; dbias [B, H, N, N]
-    is summed over the rows i held.  Calls tri_attn_bwd.
+    is summed over the rows i held.  Calls tri_attn_bwd_ws (or tri_attn_bwd with
+    workspace=LIBRARY).
     """
     import torch
     L = load_library()
@@ -375,8 +479,13 @@ def tri_attn_bwd(q, k, v, bias, mask, out, lse, dout, *, stream=None):
         raise ValueError("dout must be a contiguous float32 tensor shaped like q")
     dq, dk, dv = (torch.empty(q.shape, dtype=torch.float32, device=q.device) for _ in range(3))
     dbias = torch.empty((B, H, N, N), dtype=torch.float32, device=q.device)
-    _check(L.tri_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(mask), _ptr(out), _ptr(lse), _ptr(dout),
-                          _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbias), B, H, I, N, D, dt, _stream_handle(stream)))
+    ws = _workspace(workspace, CALL_BWD, (B, H, I, N, D), N, dt, q.device, stream)
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(mask), _ptr(out), _ptr(lse), _ptr(dout),
+            _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbias), B, H, I, N, D, dt)
+    if ws is None:
+        _check(L.tri_attn_bwd(*args, _stream_handle(stream)))
+    else:
+        _check(L.tri_attn_bwd_ws(*args, *ws[0], _stream_handle(stream)))
     return dq, dk, dv, dbias
 
 

@@ -131,15 +131,21 @@ tri_attn::Problem make_problem(const Call& c) {
 // Stream-ordered memory pool of the library, one per device, created on first use.  Its
 // release threshold is unlimited, so memory freed at the end of a call stays reserved for
 // the next one instead of going back to the driver at every synchronisation.
-hipError_t workspace_pool(hipMemPool_t* out) {
-    constexpr int kMaxDevices = 64;
-    static std::mutex mu;
-    static hipMemPool_t pools[kMaxDevices] = {};
+constexpr int kMaxDevices = 64;
+std::mutex g_pool_mu;
+hipMemPool_t g_pools[kMaxDevices] = {};
+
+hipError_t workspace_pool(hipMemPool_t* out, bool create = true) {
+    hipMemPool_t* pools = g_pools;
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
     if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-    std::lock_guard<std::mutex> lock(mu);
+    std::lock_guard<std::mutex> lock(g_pool_mu);
+    if (!pools[dev] && !create) {
+        *out = nullptr;
+        return hipSuccess;
+    }
     if (!pools[dev]) {
         hipMemPoolProps props = {};
         props.allocType = hipMemAllocationTypePinned;
@@ -194,7 +200,7 @@ int run(const Call& c, void* stream) {
         return e == hipSuccess ? TRI_ATTN_OK : hip_fail(e);
     }
     if (c.ws_bytes >= 0) {  // caller-provided workspace
-        if (!c.ws) return TRI_ATTN_ERR_NULL;
+        if (!c.ws && need > 0) return TRI_ATTN_ERR_NULL;
         if (!aligned(c.ws, 16)) return TRI_ATTN_ERR_ALIGN;
         if (c.ws_bytes < need) return TRI_ATTN_ERR_WORKSPACE;
         const Span others[] = {{c.out, qkv_elems * 4}, {c.q, qkv_elems * 2},  {c.k, qkv_elems * 2},
@@ -283,49 +289,186 @@ int tri_attn_fwd_rows_noalloc(const void* q, const void* k, const void* v, const
 
 int64_t tri_attn_noalloc_scratch_bytes(void) { return static_cast<int64_t>(tri_attn::static_scratch_bytes()); }
 
-int tri_attn_fwd_lse(const void* q, const void* k, const void* v, const void* bias, const float* mask, float* out,
-                     float* lse, int64_t B, int64_t H, int64_t I, int64_t N, int64_t D, int32_t n_key_tiles,
-                     int32_t dtype, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The forward-family calls with an optional caller workspace (ws_bytes < 0: the pool).
+int fwd_lse(const void* q, const void* k, const void* v, const void* bias, const float* mask, float* out, float* lse,
+            int64_t B, int64_t H, int64_t I, int64_t N, int64_t D, int32_t T, int32_t dtype, void* ws,
+            int64_t ws_bytes, void* stream) {
     if (!lse) return TRI_ATTN_ERR_NULL;
-    Call c = make_call(q, k, v, bias, mask, out, B, H, I, N, D, n_key_tiles, dtype);
+    Call c = make_call(q, k, v, bias, mask, out, B, H, I, N, D, T, dtype);
     c.lse = lse;
+    c.ws = ws;
+    c.ws_bytes = ws_bytes;
     return run(c, stream);
 }
 
-int tri_attn_fwd_ending(const void* q, const void* k, const void* v, const void* bias, const float* mask,
-                        float* out, float* lse, int64_t B, int64_t H, int64_t N, int64_t D, int32_t n_key_tiles,
-                        int32_t dtype, void* stream) {
-    Call c = make_call(q, k, v, bias, mask, out, B, H, N, N, D, n_key_tiles, dtype);
+int fwd_ending(const void* q, const void* k, const void* v, const void* bias, const float* mask, float* out, float* lse,
+               int64_t B, int64_t H, int64_t N, int64_t D, int32_t T, int32_t dtype, void* ws, int64_t ws_bytes,
+               void* stream) {
+    Call c = make_call(q, k, v, bias, mask, out, B, H, N, N, D, T, dtype);
     c.ending = true;
     c.lse = lse;
+    c.ws = ws;
+    c.ws_bytes = ws_bytes;
     return run(c, stream);
 }
 
-int tri_attn_tile_state(const void* q, const void* k, const void* v, const void* bias, const float* mask, float* acc,
-                        float* m, float* l, int64_t B, int64_t H, int64_t I, int64_t N, int64_t D, int64_t key_begin,
-                        int64_t key_end, int32_t ending, int32_t dtype, void* stream) {
-    if (!m || !l) return TRI_ATTN_ERR_NULL;
+// One ring step: `update` folds it into the state (acc, m, l); `fin`, with update, writes the
+// folded result there (and lse) and only reads the state.
+int ring_step(const void* q, const void* k, const void* v, const void* bias, const float* mask, float* acc, float* m,
+              float* l, float* fin, float* lse, bool update, int64_t B, int64_t H, int64_t I, int64_t N, int64_t D,
+              int64_t key_begin, int64_t key_end, int32_t ending, int32_t dtype, void* ws, int64_t ws_bytes,
+              void* stream) {
     Call c = make_call(q, k, v, bias, mask, acc, B, H, I, N, D, 1, dtype);
     c.key_begin = key_begin;
     c.key_end = key_end < 0 ? 0 : key_end;   // a negative end is an empty (invalid) range
     c.ending = ending != 0;
     c.st_m = m;
     c.st_l = l;
+    c.update = update;
+    c.fin = fin;
+    c.lse = lse;
+    c.ws = ws;
+    c.ws_bytes = ws_bytes;
     return run(c, stream);
+}
+
+int pair_bias(const void* q, const void* k, const void* v, const void* bias, const float* mask, float* out, float* lse,
+              int64_t B, int64_t H, int64_t N, int64_t D, int32_t T, int32_t dtype, void* ws, int64_t ws_bytes,
+              void* stream) {
+    // one sequence per batch element: the [B, N, H, D] tensors are [B, 1, N, H, D]
+    Call c = make_call(q, k, v, bias, mask, out, B, H, 1, N, D, T, dtype);
+    c.lse = lse;
+    c.ws = ws;
+    c.ws_bytes = ws_bytes;
+    return run(c, stream);
+}
+
+int bwd(const void* q, const void* k, const void* v, const void* bias, const float* mask, const float* out,
+        const float* lse, const float* dout, float* dq, float* dk, float* dv, float* dbias, int64_t B, int64_t H,
+        int64_t I, int64_t N, int64_t D, int32_t dtype, void* ws, int64_t ws_bytes, void* stream) {
+    if (!q || !k || !v || !bias || !out || !lse || !dout || !dq || !dk || !dv || !dbias) return TRI_ATTN_ERR_NULL;
+    int64_t qkv_elems = 0, bias_elems = 0;
+    const int st = check_sizes(B, H, I, N, D, 1, dtype, &qkv_elems, &bias_elems);
+    if (st != TRI_ATTN_OK) return st;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(bias, 16) || (mask && !aligned(mask, 4)) ||
+        !aligned(out, 4) || !aligned(lse, 4) || !aligned(dout, 4) || !aligned(dq, 4) || !aligned(dk, 4) ||
+        !aligned(dv, 4) || !aligned(dbias, 4))
+        return TRI_ATTN_ERR_ALIGN;
+    const int64_t esz = dtype == TRI_ATTN_BF16 ? 2 : 4;
+    const Span inputs[] = {{q, qkv_elems * esz},   {k, qkv_elems * esz},  {v, qkv_elems * esz},
+                           {bias, bias_elems * esz}, {mask, B * N * 4},     {out, qkv_elems * 4},
+                           {lse, qkv_elems / D * 4}, {dout, qkv_elems * 4}};
+    const Span outputs[] = {{dq, qkv_elems * 4}, {dk, qkv_elems * 4}, {dv, qkv_elems * 4}, {dbias, bias_elems * 4}};
+    for (int a = 0; a < 4; ++a) {
+        for (const Span& in : inputs)
+            if (in.p && overlaps(outputs[a].p, outputs[a].bytes, in.p, in.bytes)) return TRI_ATTN_ERR_ALIAS;
+        for (int o = a + 1; o < 4; ++o)
+            if (overlaps(outputs[a].p, outputs[a].bytes, outputs[o].p, outputs[o].bytes)) return TRI_ATTN_ERR_ALIAS;
+    }
+    const tri_attn::BwdProblem p{q, k, v, bias, mask, out, lse, dout, dq, dk, dv, dbias, B, H, I, N, D};
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    // matrix cores for bf16 with D == 32 when the fp32 tensors allow 16-byte accesses
+    const bool mfma = uses_matrix_cores(dtype, D) && aligned(out, 16) && aligned(dout, 16) && aligned(dq, 16) &&
+                      aligned(dk, 16) && aligned(dv, 16);
+    if (!mfma) {
+        const hipError_t e = tri_attn::launch_backward(p, dtype == TRI_ATTN_BF16, s);
+        return e == hipSuccess ? TRI_ATTN_OK : hip_fail(e);
+    }
+    const int64_t need = static_cast<int64_t>(tri_attn::bwd_mfma_workspace_bytes(p));
+    if (ws_bytes >= 0) {   // caller-provided workspace
+        if (!ws) return TRI_ATTN_ERR_NULL;
+        if (!aligned(ws, 16)) return TRI_ATTN_ERR_ALIGN;
+        if (ws_bytes < need) return TRI_ATTN_ERR_WORKSPACE;
+        for (const Span& o : inputs)
+            if (o.p && overlaps(ws, need, o.p, o.bytes)) return TRI_ATTN_ERR_ALIAS;
+        for (const Span& o : outputs)
+            if (overlaps(ws, need, o.p, o.bytes)) return TRI_ATTN_ERR_ALIAS;
+        const hipError_t e = tri_attn::launch_backward_mfma(p, ws, s);
+        return e == hipSuccess ? TRI_ATTN_OK : hip_fail(e);
+    }
+    hipMemPool_t pool = nullptr;
+    hipError_t e = workspace_pool(&pool);
+    if (e != hipSuccess) return hip_fail(e);
+    void* own = nullptr;
+    e = hipMallocFromPoolAsync(&own, static_cast<size_t>(need), pool, s);
+    if (e != hipSuccess) return hip_fail(e);
+    e = tri_attn::launch_backward_mfma(p, own, s);
+    const hipError_t ef = hipFreeAsync(own, s);
+    if (e != hipSuccess) return hip_fail(e);
+    if (ef != hipSuccess) return hip_fail(ef);
+    return TRI_ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int tri_attn_fwd_lse(const void* q, const void* k, const void* v, const void* bias, const float* mask, float* out,
+                     float* lse, int64_t B, int64_t H, int64_t I, int64_t N, int64_t D, int32_t n_key_tiles,
+                     int32_t dtype, void* stream) {
+    return fwd_lse(q, k, v, bias, mask, out, lse, B, H, I, N, D, n_key_tiles, dtype, nullptr, -1, stream);
+}
+
+int tri_attn_fwd_lse_ws(const void* q, const void* k, const void* v, const void* bias, const float* mask, float* out,
+                        float* lse, int64_t B, int64_t H, int64_t I, int64_t N, int64_t D, int32_t n_key_tiles,
+                        int32_t dtype, void* workspace, int64_t workspace_bytes, void* stream) {
+    if (workspace_bytes < 0) return TRI_ATTN_ERR_WORKSPACE;
+    return fwd_lse(q, k, v, bias, mask, out, lse, B, H, I, N, D, n_key_tiles, dtype, workspace, workspace_bytes,
+                   stream);
+}
+
+int tri_attn_fwd_ending(const void* q, const void* k, const void* v, const void* bias, const float* mask,
+                        float* out, float* lse, int64_t B, int64_t H, int64_t N, int64_t D, int32_t n_key_tiles,
+                        int32_t dtype, void* stream) {
+    return fwd_ending(q, k, v, bias, mask, out, lse, B, H, N, D, n_key_tiles, dtype, nullptr, -1, stream);
+}
+
+int tri_attn_fwd_ending_ws(const void* q, const void* k, const void* v, const void* bias, const float* mask,
+                           float* out, float* lse, int64_t B, int64_t H, int64_t N, int64_t D, int32_t n_key_tiles,
+                           int32_t dtype, void* workspace, int64_t workspace_bytes, void* stream) {
+    if (workspace_bytes < 0) return TRI_ATTN_ERR_WORKSPACE;
+    return fwd_ending(q, k, v, bias, mask, out, lse, B, H, N, D, n_key_tiles, dtype, workspace, workspace_bytes,
+                      stream);
+}
+
+int tri_attn_tile_state(const void* q, const void* k, const void* v, const void* bias, const float* mask, float* acc,
+                        float* m, float* l, int64_t B, int64_t H, int64_t I, int64_t N, int64_t D, int64_t key_begin,
+                        int64_t key_end, int32_t ending, int32_t dtype, void* stream) {
+    if (!m || !l) return TRI_ATTN_ERR_NULL;
+    return ring_step(q, k, v, bias, mask, acc, m, l, nullptr, nullptr, false, B, H, I, N, D, key_begin, key_end, ending,
+                     dtype, nullptr, -1, stream);
+}
+
+int tri_attn_tile_state_ws(const void* q, const void* k, const void* v, const void* bias, const float* mask,
+                           float* acc, float* m, float* l, int64_t B, int64_t H, int64_t I, int64_t N, int64_t D,
+                           int64_t key_begin, int64_t key_end, int32_t ending, int32_t dtype, void* workspace,
+                           int64_t workspace_bytes, void* stream) {
+    if (!m || !l) return TRI_ATTN_ERR_NULL;
+    if (workspace_bytes < 0) return TRI_ATTN_ERR_WORKSPACE;
+    return ring_step(q, k, v, bias, mask, acc, m, l, nullptr, nullptr, false, B, H, I, N, D, key_begin, key_end, ending,
+                     dtype, workspace, workspace_bytes, stream);
 }
 
 int tri_attn_tile_state_update(const void* q, const void* k, const void* v, const void* bias, const float* mask,
                                float* acc, float* m, float* l, int64_t B, int64_t H, int64_t I, int64_t N, int64_t D,
                                int64_t key_begin, int64_t key_end, int32_t ending, int32_t dtype, void* stream) {
     if (!m || !l) return TRI_ATTN_ERR_NULL;
-    Call c = make_call(q, k, v, bias, mask, acc, B, H, I, N, D, 1, dtype);
-    c.key_begin = key_begin;
-    c.key_end = key_end < 0 ? 0 : key_end;
-    c.ending = ending != 0;
-    c.st_m = m;
-    c.st_l = l;
-    c.update = true;
-    return run(c, stream);
+    return ring_step(q, k, v, bias, mask, acc, m, l, nullptr, nullptr, true, B, H, I, N, D, key_begin, key_end, ending,
+                     dtype, nullptr, -1, stream);
+}
+
+int tri_attn_tile_state_update_ws(const void* q, const void* k, const void* v, const void* bias, const float* mask,
+                                  float* acc, float* m, float* l, int64_t B, int64_t H, int64_t I, int64_t N,
+                                  int64_t D, int64_t key_begin, int64_t key_end, int32_t ending, int32_t dtype,
+                                  void* workspace, int64_t workspace_bytes, void* stream) {
+    if (!m || !l) return TRI_ATTN_ERR_NULL;
+    if (workspace_bytes < 0) return TRI_ATTN_ERR_WORKSPACE;
+    return ring_step(q, k, v, bias, mask, acc, m, l, nullptr, nullptr, true, B, H, I, N, D, key_begin, key_end, ending,
+                     dtype, workspace, workspace_bytes, stream);
 }
 
 int tri_attn_tile_state_final(const void* q, const void* k, const void* v, const void* bias, const float* mask,
@@ -334,16 +477,19 @@ int tri_attn_tile_state_final(const void* q, const void* k, const void* v, const
                               int32_t ending, int32_t dtype, void* stream) {
     if (!m || !l || !out) return TRI_ATTN_ERR_NULL;
     // the state is only read here; the kernels take it through the state pointers
-    Call c = make_call(q, k, v, bias, mask, const_cast<float*>(acc), B, H, I, N, D, 1, dtype);
-    c.key_begin = key_begin;
-    c.key_end = key_end < 0 ? 0 : key_end;
-    c.ending = ending != 0;
-    c.st_m = const_cast<float*>(m);
-    c.st_l = const_cast<float*>(l);
-    c.update = true;
-    c.fin = out;
-    c.lse = lse;
-    return run(c, stream);
+    return ring_step(q, k, v, bias, mask, const_cast<float*>(acc), const_cast<float*>(m), const_cast<float*>(l), out,
+                     lse, true, B, H, I, N, D, key_begin, key_end, ending, dtype, nullptr, -1, stream);
+}
+
+int tri_attn_tile_state_final_ws(const void* q, const void* k, const void* v, const void* bias, const float* mask,
+                                 const float* acc, const float* m, const float* l, float* out, float* lse, int64_t B,
+                                 int64_t H, int64_t I, int64_t N, int64_t D, int64_t key_begin, int64_t key_end,
+                                 int32_t ending, int32_t dtype, void* workspace, int64_t workspace_bytes,
+                                 void* stream) {
+    if (!m || !l || !out) return TRI_ATTN_ERR_NULL;
+    if (workspace_bytes < 0) return TRI_ATTN_ERR_WORKSPACE;
+    return ring_step(q, k, v, bias, mask, const_cast<float*>(acc), const_cast<float*>(m), const_cast<float*>(l), out,
+                     lse, true, B, H, I, N, D, key_begin, key_end, ending, dtype, workspace, workspace_bytes, stream);
 }
 
 int tri_attn_state_merge(float* acc, float* m, float* l, const float* acc_t, const float* m_t, const float* l_t,
@@ -380,54 +526,77 @@ int tri_attn_state_finalize(const float* acc, const float* m, const float* l, fl
 int tri_attn_bwd(const void* q, const void* k, const void* v, const void* bias, const float* mask, const float* out,
                  const float* lse, const float* dout, float* dq, float* dk, float* dv, float* dbias, int64_t B,
                  int64_t H, int64_t I, int64_t N, int64_t D, int32_t dtype, void* stream) {
-    if (!q || !k || !v || !bias || !out || !lse || !dout || !dq || !dk || !dv || !dbias) return TRI_ATTN_ERR_NULL;
-    int64_t qkv_elems = 0, bias_elems = 0;
-    const int st = check_sizes(B, H, I, N, D, 1, dtype, &qkv_elems, &bias_elems);
-    if (st != TRI_ATTN_OK) return st;
-    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(bias, 16) || (mask && !aligned(mask, 4)) ||
-        !aligned(out, 4) || !aligned(lse, 4) || !aligned(dout, 4) || !aligned(dq, 4) || !aligned(dk, 4) ||
-        !aligned(dv, 4) || !aligned(dbias, 4))
-        return TRI_ATTN_ERR_ALIGN;
-    const int64_t esz = dtype == TRI_ATTN_BF16 ? 2 : 4;
-    const Span inputs[] = {{q, qkv_elems * esz},   {k, qkv_elems * esz},  {v, qkv_elems * esz},
-                           {bias, bias_elems * esz}, {mask, B * N * 4},     {out, qkv_elems * 4},
-                           {lse, qkv_elems / D * 4}, {dout, qkv_elems * 4}};
-    const Span outputs[] = {{dq, qkv_elems * 4}, {dk, qkv_elems * 4}, {dv, qkv_elems * 4}, {dbias, bias_elems * 4}};
-    for (int a = 0; a < 4; ++a) {
-        for (const Span& in : inputs)
-            if (in.p && overlaps(outputs[a].p, outputs[a].bytes, in.p, in.bytes)) return TRI_ATTN_ERR_ALIAS;
-        for (int o = a + 1; o < 4; ++o)
-            if (overlaps(outputs[a].p, outputs[a].bytes, outputs[o].p, outputs[o].bytes)) return TRI_ATTN_ERR_ALIAS;
-    }
-    const tri_attn::BwdProblem p{q, k, v, bias, mask, out, lse, dout, dq, dk, dv, dbias, B, H, I, N, D};
-    const hipStream_t s = static_cast<hipStream_t>(stream);
-    // matrix cores for bf16 with D == 32 when the fp32 tensors allow 16-byte accesses
-    const bool mfma = uses_matrix_cores(dtype, D) && aligned(out, 16) && aligned(dout, 16) && aligned(dq, 16) &&
-                      aligned(dk, 16) && aligned(dv, 16);
-    if (!mfma) {
-        const hipError_t e = tri_attn::launch_backward(p, dtype == TRI_ATTN_BF16, s);
-        return e == hipSuccess ? TRI_ATTN_OK : hip_fail(e);
-    }
-    hipMemPool_t pool = nullptr;
-    hipError_t e = workspace_pool(&pool);
-    if (e != hipSuccess) return hip_fail(e);
-    void* own = nullptr;
-    e = hipMallocFromPoolAsync(&own, tri_attn::bwd_mfma_workspace_bytes(p), pool, s);
-    if (e != hipSuccess) return hip_fail(e);
-    e = tri_attn::launch_backward_mfma(p, own, s);
-    const hipError_t ef = hipFreeAsync(own, s);
-    if (e != hipSuccess) return hip_fail(e);
-    if (ef != hipSuccess) return hip_fail(ef);
-    return TRI_ATTN_OK;
+    return bwd(q, k, v, bias, mask, out, lse, dout, dq, dk, dv, dbias, B, H, I, N, D, dtype, nullptr, -1, stream);
+}
+
+int tri_attn_bwd_ws(const void* q, const void* k, const void* v, const void* bias, const float* mask, const float* out,
+                    const float* lse, const float* dout, float* dq, float* dk, float* dv, float* dbias, int64_t B,
+                    int64_t H, int64_t I, int64_t N, int64_t D, int32_t dtype, void* workspace,
+                    int64_t workspace_bytes, void* stream) {
+    if (workspace_bytes < 0) return TRI_ATTN_ERR_WORKSPACE;
+    return bwd(q, k, v, bias, mask, out, lse, dout, dq, dk, dv, dbias, B, H, I, N, D, dtype, workspace,
+               workspace_bytes, stream);
 }
 
 int pair_bias_attn_fwd(const void* q, const void* k, const void* v, const void* bias, const float* mask, float* out,
                        float* lse, int64_t B, int64_t H, int64_t N, int64_t D, int32_t n_key_tiles, int32_t dtype,
                        void* stream) {
-    // one sequence per batch element: the [B, N, H, D] tensors are [B, 1, N, H, D]
-    Call c = make_call(q, k, v, bias, mask, out, B, H, 1, N, D, n_key_tiles, dtype);
-    c.lse = lse;
-    return run(c, stream);
+    return pair_bias(q, k, v, bias, mask, out, lse, B, H, N, D, n_key_tiles, dtype, nullptr, -1, stream);
+}
+
+int pair_bias_attn_fwd_ws(const void* q, const void* k, const void* v, const void* bias, const float* mask, float* out,
+                          float* lse, int64_t B, int64_t H, int64_t N, int64_t D, int32_t n_key_tiles, int32_t dtype,
+                          void* workspace, int64_t workspace_bytes, void* stream) {
+    if (workspace_bytes < 0) return TRI_ATTN_ERR_WORKSPACE;
+    return pair_bias(q, k, v, bias, mask, out, lse, B, H, N, D, n_key_tiles, dtype, workspace, workspace_bytes, stream);
+}
+
+int64_t tri_attn_call_workspace_bytes(int32_t call, int64_t B, int64_t H, int64_t I, int64_t N, int64_t D,
+                                      int64_t key_count, int32_t dtype) {
+    if (call < TRI_ATTN_CALL_FWD || call > TRI_ATTN_CALL_BWD) return TRI_ATTN_ERR_SHAPE;
+    int64_t qkv_elems = 0, bias_elems = 0;
+    const int st = check_sizes(B, H, I, N, D, 1, dtype, &qkv_elems, &bias_elems);
+    if (st != TRI_ATTN_OK) return st;
+    const bool ending = call == TRI_ATTN_CALL_ENDING || call == TRI_ATTN_CALL_STATE_ENDING;
+    const bool state = call == TRI_ATTN_CALL_STATE || call == TRI_ATTN_CALL_STATE_ENDING;
+    if ((ending && I != N) || (call == TRI_ATTN_CALL_PAIR_BIAS && I != 1)) return TRI_ATTN_ERR_SHAPE;
+    if (state && (key_count < 1 || key_count > N)) return TRI_ATTN_ERR_RANGE;
+    if (!uses_matrix_cores(dtype, D)) return 0;
+    if (call == TRI_ATTN_CALL_BWD) {
+        const tri_attn::BwdProblem p{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                     nullptr, nullptr, nullptr, B, H, I, N, D};
+        return static_cast<int64_t>(tri_attn::bwd_mfma_workspace_bytes(p));
+    }
+    Call c = make_call(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, B, H, I, N, D, 1, dtype);
+    c.ending = ending;
+    if (state) {   // a state call's layout depends on how many keys its range holds, not where it starts
+        static float placeholder;
+        c.key_begin = 0;
+        c.key_end = key_count;
+        c.st_m = c.st_l = &placeholder;
+    }
+    return static_cast<int64_t>(mfma_workspace_bytes(make_problem(c)));
+}
+
+int64_t tri_attn_pool_reserved_bytes(void) {
+    hipMemPool_t pool = nullptr;
+    const hipError_t e = workspace_pool(&pool, false);
+    if (e != hipSuccess) return hip_fail(e);
+    if (!pool) return 0;
+    uint64_t reserved = 0;
+    const hipError_t ea = hipMemPoolGetAttribute(pool, hipMemPoolAttrReservedMemCurrent, &reserved);
+    if (ea != hipSuccess) return hip_fail(ea);
+    return static_cast<int64_t>(reserved);
+}
+
+int tri_attn_pool_release(void) {
+    std::lock_guard<std::mutex> lock(g_pool_mu);
+    for (hipMemPool_t pool : g_pools) {
+        if (!pool) continue;
+        const hipError_t e = hipMemPoolTrimTo(pool, 0);
+        if (e != hipSuccess) return hip_fail(e);
+    }
+    return TRI_ATTN_OK;
 }
 
 const char* tri_attn_status_string(int status) {

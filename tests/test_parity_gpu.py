@@ -283,7 +283,7 @@ def test_caller_workspace_matches_pool_workspace(torch_dev):
     need = P.workspace_bytes(2, 3, 21, 150, 32, 6, P.TRI_ATTN_BF16)
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
     say("[parity] caller workspace vs library pool")
-    a = P.tri_attn_fwd_rows(q, k, v, bias, mask, n_key_tiles=6)
+    a = P.tri_attn_fwd_rows(q, k, v, bias, mask, n_key_tiles=6, workspace=P.LIBRARY)
     b = P.tri_attn_fwd_rows_ws(q, k, v, bias, mask, workspace=ws, n_key_tiles=6)
     torch.cuda.synchronize()
     assert torch.equal(a, b)

@@ -41,7 +41,7 @@ def test_noalloc_matches_allocating_entry_point_twice(torch_dev):
     del b
     q, k, v, bias, mask = (to_dev(torch, x) for x in (w.q, w.k, w.v, w.bias, w.mask))
     say("[noalloc] call 1: N=2700, T=8, one wide column block")
-    ref1 = P.tri_attn_fwd_rows(q, k, v, bias, mask, n_key_tiles=cfg.n_key_tiles)
+    ref1 = P.tri_attn_fwd_rows(q, k, v, bias, mask, n_key_tiles=cfg.n_key_tiles, workspace=P.LIBRARY)
     got1 = P.tri_attn_fwd_rows_noalloc(q, k, v, bias, mask, n_key_tiles=cfg.n_key_tiles)
     torch.cuda.synchronize()
     assert torch.equal(got1, ref1), "call 1 differs from tri_attn_fwd_rows"
@@ -51,7 +51,7 @@ def test_noalloc_matches_allocating_entry_point_twice(torch_dev):
     w2 = W.make_inputs(small)
     q, k, v, bias, mask = (to_dev(torch, x) for x in (w2.q, w2.k, w2.v, w2.bias, w2.mask))
     say("[noalloc] call 2: B=2, I=40, N=300, H=3, narrow bias")
-    ref2 = P.tri_attn_fwd_rows(q, k, v, bias, mask, n_key_tiles=3)
+    ref2 = P.tri_attn_fwd_rows(q, k, v, bias, mask, n_key_tiles=3, workspace=P.LIBRARY)
     got2 = P.tri_attn_fwd_rows_noalloc(q, k, v, bias, mask, n_key_tiles=3)
     torch.cuda.synchronize()
     assert torch.equal(got2, ref2), "call 2 differs from tri_attn_fwd_rows"
