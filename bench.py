@@ -63,8 +63,10 @@ def kernel_source_digest() -> str:
     return h.hexdigest()
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per launch from the committed rocprofv3 --pmc summary, or None."""
+def measured_counters(workload: str):
+    """The committed rocprofv3 --pmc summary of the forward's dominant kernel on this
+    workload (HBM bytes per launch, clock, MFMA busy), or None when the kernel sources
+    changed since it was taken."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
@@ -73,7 +75,7 @@ def measured_traffic(workload: str):
     entry = rec.get(workload)
     if not entry or entry.get("kernel_source_sha256") != kernel_source_digest():
         return None
-    return int(entry["hbm_bytes_per_launch"])
+    return entry
 
 
 def to_dev(torch, a):
@@ -293,7 +295,8 @@ def main() -> int:
 
     flops = cfg.flops
     tflops = flops / (ms_per_step * 1e-3) / 1e12
-    traffic = measured_traffic(args.workload) if cfg.dtype == "bf16" else None
+    ctr = measured_counters(args.workload) if cfg.dtype == "bf16" else None
+    traffic = int(ctr["hbm_bytes_per_launch"]) if ctr else None
     roofline = {
         "bound": "mfma",
         "achieved": round(tflops, 3),
@@ -306,6 +309,11 @@ def main() -> int:
         "algorithmic_flops_per_launch": flops,
         "algorithmic_bytes_per_launch": cfg.algorithmic_bytes,
         "hbm_gbs_algorithmic": round(cfg.algorithmic_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        # from the committed counters of the same kernel source (None once it changed): the
+        # average clock under this load and the matrix-core busy share of SIMD cycles
+        "clock_ghz": ctr.get("clock_ghz") if ctr else None,
+        "mfma_busy_pct": ctr.get("mfma_busy_pct") if ctr else None,
+        "counters_source": ctr.get("source") if ctr else None,
     }
     result = {
         "metric": METRIC,
