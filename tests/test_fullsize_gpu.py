@@ -121,3 +121,41 @@ def test_ring_n2700_t8_sampled(torch_dev, n2700):
     ref, ref_lse = oracle.tri_attn(w.q, w.k, w.v, w.bias, w.mask, n_key_tiles=T, rows=rows)
     compare(got, ref, TOL["bf16"], f"ring out, {len(rows)} rows")
     compare(got_lse, ref_lse, TOL["bf16"], f"ring lse, {len(rows)} rows")
+
+
+@pytest.mark.timeout(600)
+def test_backward_n2700_dbias_of_all_rows(torch_dev, n2700):
+    """dbias of the full N = 2700 call sums dS over all 2700 rows, beyond what the oracle
+    can compute here; two properties that hold at any size check it.
+      * Every row of dbias sums to zero: sum_k ds_k = sum_k p_k (dp_k - delta) = 0,
+        because sum_k p_k dp_k = dout . out = delta and sum_k p_k = 1.  The bar is the
+        rounding of the 2700-term sums: 1e-2 of the largest |dbias| row sum of |values|.
+      * The dbias of the whole call is the sum of the dbias of two row shares (rows
+        [0, 1350) and [1350, 2700)), each a separate call: the cross-row reduction at full
+        size.  Bar: 1e-4 of max |dbias| (fp32 sums of 2700 terms, different order)."""
+    import pair_biased_triangle_amd as P
+    torch = torch_dev
+    w, (q, k, v, bias, mask) = n2700
+    cfg = w.cfg
+    say("[full] backward N=2700: dbias over all rows, then over two row shares")
+    out, lse = P.tri_attn_fwd_lse(q, k, v, bias, mask, n_key_tiles=cfg.n_key_tiles)
+    dout = torch.randn(q.shape, dtype=torch.float32, device="cuda", generator=torch.Generator("cuda").manual_seed(9))
+    full = P.tri_attn_bwd(q, k, v, bias, mask, out, lse, dout)[3]
+    torch.cuda.synchronize()
+    half = cfg.I // 2
+    parts = []
+    for lo, hi in ((0, half), (half, cfg.I)):
+        sl = lambda t: t[:, lo:hi].contiguous()
+        parts.append(P.tri_attn_bwd(sl(q), sl(k), sl(v), bias, mask, sl(out), sl(lse), sl(dout))[3])
+        torch.cuda.synchronize()
+    kept = slice(0, cfg.N - cfg.mask_last)            # masked keys get no gradient
+    row_sum = full[..., kept].double().sum(dim=-1)
+    row_abs = full[..., kept].double().abs().sum(dim=-1)
+    worst = float((row_sum.abs() / row_abs.clamp_min(1e-30)).max())
+    say(f"  dbias row sums: max |sum| / sum|.| = {worst:.3e} (bar 1e-2), max |dbias| = {float(full.abs().max()):.3g}")
+    assert worst <= 1e-2
+    assert torch.all(full[..., cfg.N - cfg.mask_last:] == 0), "a masked key got a bias gradient"
+    scale = float(full.abs().max())
+    diff = float((full.double() - parts[0].double() - parts[1].double()).abs().max())
+    say(f"  dbias(all rows) - dbias(rows < 1350) - dbias(rows >= 1350): max |diff| = {diff:.3e} (bar {1e-4 * scale:.3e})")
+    assert diff <= 1e-4 * scale
