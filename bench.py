@@ -169,7 +169,7 @@ def other_pass(args, torch, P, W, cfg) -> dict:
         work = 3 * B * N * H * D * s_in + B * H * N * N * s_in + (4 * B * N if mask is not None else 0) + 4 * B * N * H * D
         unit, peak, bound = "GB/s", PEAK_HBM_GBS, "hbm"
         metric = "attention with pair bias GB/s (q, k, v, bias read once, out written once)"
-        kernels = "bias_ref_kernel + bias_image16_kernel + bf16_mfma_kernel (one row, split-key) + state_combine_kernel"
+        kernels = "pair_bias_direct_kernel (one pass over the raw bias, split keys) + state_combine_kernel"
         extra["flops_per_call"] = 4.0 * B * H * N * N * D
         dtype = cfg.dtype
     else:   # ring
