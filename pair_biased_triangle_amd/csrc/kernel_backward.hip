@@ -37,7 +37,8 @@ __device__ __forceinline__ float ld(const void* base, int64_t idx) {
 __device__ __forceinline__ float prob(float s, float lse) { return lse == -INFINITY ? 0.0f : expf(s - lse); }
 
 // With `wide` set (the bf16 backward's span flags, n_wide per (b, h)), a workgroup works
-// only if its (b, h) has a flag set; rows i run blockIdx.y, blockIdx.y + gridDim.y, ...
+// only if its (b, h) (blockIdx.z) has a flag set; in dq and dk/dv rows i then run
+// blockIdx.y, blockIdx.y + gridDim.y, ...
 __device__ __forceinline__ bool skip_bh(const int* wide, int n_wide) {
     if (!wide) return false;
     int any = 0;
@@ -199,7 +200,8 @@ constexpr int TT = 4;             // pairs per thread along j and along k
 constexpr int TBT = (TB / TT) * (TB / TT);   // 256 threads
 
 template <bool BF16, int DP>
-__global__ void __launch_bounds__(TBT) bwd_dbias_kernel(BwdProblem p) {
+__global__ void __launch_bounds__(TBT) bwd_dbias_kernel(BwdProblem p, const int* wide, int n_wide) {
+    if (skip_bh(wide, n_wide)) return;
     const int64_t N = p.N, H = p.H, D = p.D, I = p.I;
     const int64_t b = blockIdx.z / H, h = blockIdx.z % H;
     const int64_t j0 = static_cast<int64_t>(blockIdx.y) * TB, k0 = static_cast<int64_t>(blockIdx.x) * TB;
@@ -303,7 +305,7 @@ hipError_t launch_dp(const BwdProblem& p, hipStream_t stream) {
     if (e != hipSuccess) return e;
     const unsigned nt = static_cast<unsigned>((p.N + TB - 1) / TB);
     hipLaunchKernelGGL((bwd_dbias_kernel<BF16, DP>), dim3(nt, nt, static_cast<unsigned>(p.B * p.H)), dim3(TBT), 0,
-                       stream, p);
+                       stream, p, nullptr, 0);
     return hipGetLastError();
 }
 
@@ -331,6 +333,10 @@ hipError_t launch_backward_wide(const BwdProblem& p, const int* wide, int n_wide
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_dkdv_kernel<true, 32>), grid, dim3(BT), 0, stream, p, wide, n_wide);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const unsigned nt = static_cast<unsigned>((p.N + TB - 1) / TB);
+    hipLaunchKernelGGL((bwd_dbias_kernel<true, 32>), dim3(nt, nt, static_cast<unsigned>(p.B * p.H)), dim3(TBT), 0,
+                       stream, p, wide, n_wide);
     return hipGetLastError();
 }
 

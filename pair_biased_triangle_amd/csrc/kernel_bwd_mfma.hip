@@ -6,23 +6,24 @@
 // each query's reference r_j (the forward's prepass, and bias_imageT16_kernel for its
 // transpose): x = (q.k + (r_j - lse) sqrt(D)) log2(e)/sqrt(D) + (bias + mask - r_j) log2(e)
 // is the score minus lse in log2 units, with (r_j - lse) sqrt(D) seeding the matrix
-// accumulator and the image taken by one v_fma_mix_f32.  dbias keeps the fp32 image
-// (bias + mask) sqrt(D) in registers for its whole loop.
+// accumulator and the image taken by one v_fma_mix_f32.  dbias takes the bias out of its
+// loop over rows: it sums 2^x' (dP - delta) with x' the score without the image term and
+// multiplies the sums by 2^((bias + mask - r_j) log2(e)) once, from the raw bias.
 //
 // Kernels, each owning the sums it produces (no atomics, deterministic):
 //   bwd_prep_kernel   dout -> bf16 copy (the operand of the dP and dV products),
-//                     delta = dout . out per query, and delta, nb = -lse log2(e) and
-//                     nb' = (r_j - lse) sqrt(D) transposed to [b, i, h, j] (rows padded to
-//                     whole 256-query tiles).
+//                     delta = dout . out per query, and -delta and nb' = (r_j - lse) sqrt(D)
+//                     transposed to [b, i, h, j] (rows padded to whole 256-query tiles).
 //   bwd_dq_lds        2 lines x 128 queries per workgroup, 32-key blocks streamed through
 //                     an LDS ring (the forward's shape):
-//                       S^T = K Q^T + nb',  dP^T = V dO^T,  dS^T = P^T (dP^T - delta),
+//                       S^T = K Q^T + nb',  dP^T = V dO^T - delta,  dS^T = P^T dP^T,
 //                       dQ^T += K^T dS^T
 //   bwd_dkdv_lds      2 lines x 128 keys per workgroup, 32-query blocks streamed, in the
 //                     orientation in which P and dS leave the accumulator as B operands:
-//                       S = Q K^T + nb',  dP = dO V^T,  dV^T += dO^T P,  dK^T += Q^T dS
+//                       S = Q K^T + nb',  dP = dO V^T - delta,  dV^T += dO^T P,  dK^T += Q^T dS
 //   bwd_dbias_lds     256 queries x 128 keys of one (b, h) per workgroup, rows i streamed:
-//                       dbias^T += dS^T of every row i (the bias is shared by all rows)
+//                       S^T = K Q^T,  dP^T = V dO^T - delta,  acc += 2^x'^T dP^T,
+//                       dbias^T = E^T acc at the end (the bias is shared by all rows)
 // Every streaming kernel copies its operands straight from global memory into a ring of
 // LDS stages (global_load_lds_dwordx4, one barrier per block) and reads them from there;
 // transposed operands come from ds_read_b64_tr_b16 on the natural [row][d] tiles.
@@ -87,22 +88,20 @@ __device__ __forceinline__ void to_bf16(const f32x16& x, bf16x8& lo, bf16x8& hi)
     hi = __builtin_convertvector(__builtin_shufflevector(x, x, 8, 9, 10, 11, 12, 13, 14, 15), bf16x8);
 }
 
-// -inf for a query without any finite score (its p is 0 everywhere), else -lse in log2 units
-__device__ __forceinline__ float neg_lse2(float lse) { return lse == -INFINITY ? -INFINITY : -lse * kLog2e; }
-
 // ---------------------------------------------------------------------------------------
 // One thread per (b, i, h, j) with j padded to NP: dout of query (b, i, j, h) rounded to
 // bf16, delta = dout . out, and, transposed to [b, i, h, j] so that the row-streaming
-// kernels copy whole rows, delta and nb = -lse log2(e) (the shift of the score in log2
-// units; -inf for a query without any finite score, and for the padded j, whose delta is 0).
+// kernels copy whole rows, -delta (the seed of their dP accumulators, which then hold
+// dP - delta) and nb' = (r_j - lse) sqrt(D) (the shift of the score against the query's
+// reference; -inf for a query without any finite score, and for the padded j, whose delta
+// is 0).
 // Eight lanes per query: lane `part` reads elements 4 part .. 4 part + 3 of dout and out,
 // so a wave reads 1 KB of contiguous rows per load; the partial dot products meet in three
 // shuffle steps.  Threads run over (line, query padded to NP, head, part); the padded
 // queries only write the padding of the transposed rows.
 constexpr int PREP_PARTS = D / 4;
-__global__ void __launch_bounds__(256) bwd_prep_kernel(BwdProblem p, __bf16* g16, float* delta, float* nbT,
-                                                       float* deltaT, int64_t NP, const float* ref16, int64_t nqp16,
-                                                       float* nbT2) {
+__global__ void __launch_bounds__(256) bwd_prep_kernel(BwdProblem p, __bf16* g16, float* delta, float* deltaT,
+                                                       int64_t NP, const float* ref16, int64_t nqp16, float* nbT2) {
     const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
     const int64_t total = p.B * p.I * NP * p.H * PREP_PARTS;   // whole groups of 8 lanes
     if (t >= total) return;
@@ -126,9 +125,8 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdProblem p, __bf16* g16
     if (part == 0) {
         const int64_t tt = (line * p.H + h) * NP + j;   // [b, i, h, j]
         if (real) delta[q] = dl;
-        deltaT[tt] = dl;
+        deltaT[tt] = -dl;                               // seeds the dP accumulators
         const float lse = real ? p.lse[q] : -INFINITY;
-        nbT[tt] = neg_lse2(lse);
         // (r_j - lse) sqrt(D): with the fp16 image relative to r_j, the score in log2 units is
         // (q.k + this) * log2(e)/sqrt(D) + image
         const int64_t b = line / p.I;
@@ -146,7 +144,7 @@ __device__ __forceinline__ void db_barrier_drain() { asm volatile("s_waitcnt vmc
 // 16 KB (K, V of its lines and its 128 rows of the forward's fp16 image tile, copied by
 // global_load_lds); two workgroups share a compute unit.  Wave w owns line w / 2 and query
 // tiles 2 (w % 2), +1; Q and dO of its queries stay in registers.  Per unit and block:
-//   S^T = K Q^T + nb',  dP^T = V dO^T,  dS^T = P^T (dP^T - delta),  dQ^T += K^T dS^T
+//   S^T = K Q^T + nb',  dP^T = V dO^T - delta,  dS^T = P^T dP^T,  dQ^T += K^T dS^T
 // with K^T read transposed from the staged [key][d] tile (ds_read_b64_tr_b16).
 #ifndef TRI_ATTN_DQ_WAVES
 #define TRI_ATTN_DQ_WAVES 4
@@ -314,11 +312,14 @@ __global__ void __launch_bounds__(DQ_THR, 2) bwd_dq_lds(BwdProblem p, const _Flo
 #pragma unroll
     for (int h = 0; h < 2; ++h) ac[h] = DQ_B_OFF + t0 * DQ_CTILE_BYTES + c * 64 + kv_chunk(c, 2 * h2 + h) * 16;
     const uint32_t st0 = LDS_ADDR(&g_dq[0]);
-    f32x16 nbs[2];                    // score accumulator seeds: (r_j - lse) sqrt(D) in every register
+    f32x16 nbs[2], ndl[2];            // accumulator seeds: (r_j - lse) sqrt(D) for S, -delta for dP
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) nbs[u][r] = nb[u];
+        for (int r = 0; r < 16; ++r) {
+            nbs[u][r] = nb[u];
+            ndl[u][r] = -dl[u];
+        }
 
     f32x16 dQ[2] = {};
     for (int n = 0; n < DQ_STAGES - 1 && n < nblk; ++n) dq_stage(cx, n, wave, lane);
@@ -358,13 +359,12 @@ __global__ void __launch_bounds__(DQ_THR, 2) bwd_dq_lds(BwdProblem p, const _Flo
         for (int u = 0; u < 2; ++u) {
             f32x16 S = mfma(__builtin_bit_cast(bf16x8, kk[0]), qB[u][0], nbs[u]);
             S = mfma(__builtin_bit_cast(bf16x8, kk[1]), qB[u][1], S);
-            f32x16 dP = mfma(__builtin_bit_cast(bf16x8, vv[0]), gB[u][0], f32x16{});
+            f32x16 dP = mfma(__builtin_bit_cast(bf16x8, vv[0]), gB[u][0], ndl[u]);   // dP - delta
             dP = mfma(__builtin_bit_cast(bf16x8, vv[1]), gB[u][1], dP);
             f32x16 dS;
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-                dS[r] = __builtin_amdgcn_exp2f(fmaf(S[r], kScale, half_of(cc[2 * u], cc[2 * u + 1], r))) *
-                        (dP[r] - dl[u]);
+                dS[r] = __builtin_amdgcn_exp2f(fmaf(S[r], kScale, half_of(cc[2 * u], cc[2 * u + 1], r))) * dP[r];
             bf16x8 s0, s1;
             to_bf16(dS, s0, s1);
             dQ[u] = mfma(kT[0], s0, dQ[u]);
@@ -395,11 +395,11 @@ __global__ void __launch_bounds__(DQ_THR, 2) bwd_dq_lds(BwdProblem p, const _Flo
 // dk, dv: a workgroup of 4 waves owns DK_R = 2 lines x 128 keys of one (b, h) and streams
 // 32-query blocks through a ring of 4 LDS stages (two workgroups per compute unit): Q and
 // dO of its lines, the 128 x 32 fp16 transposed tile (bias_imageT16_kernel: row = key, 32
-// queries, relative to each query's r_q) and nb' = (r_q - lse) sqrt(D), delta of the
+// queries, relative to each query's r_q) and nb' = (r_q - lse) sqrt(D), -delta of the
 // block's queries.  Wave w owns line w / 2 and key tiles 2 (w % 2), +1 (lane = key; K and
 // V of its keys stay in registers).  Per unit and block, in the orientation in which P and
 // dS leave the accumulator as the B operands of the next products:
-//   S = Q K^T + nb',  dP = dO V^T,  dS = P (dP - delta),  dV^T += dO^T P,  dK^T += Q^T dS
+//   S = Q K^T + nb',  dP = dO V^T - delta,  dS = P dP,  dV^T += dO^T P,  dK^T += Q^T dS
 // with Q^T, dO^T read transposed from the staged [query][d] tiles.  A dropped key
 // (masked, or past the end) gets zero gradients.
 #ifndef TRI_ATTN_DK_WAVES
@@ -514,7 +514,7 @@ __global__ void __launch_bounds__(DK_THR, 2) bwd_dkdv_lds(BwdProblem p, const _F
             cx.part_bytes[t] = kv_chunk(cx.q_local[t], lane & 3) * 16;
         }
         cx.img_wg = imgT16 + (static_cast<int64_t>(bh) * n_kb + kb) * nqblk * static_cast<int64_t>(IMG_BJ * 32);
-        // nb of line w (w < DK_R) or delta of line w - DK_R, 32 floats of the block in lanes 0 .. 7
+        // nb' of line w (w < DK_R) or -delta of line w - DK_R, 32 floats of the block in lanes 0 .. 7
         int64_t il = i0 + wave % DK_R;
         il = il < I ? il : I - 1;
         cx.ls_src = reinterpret_cast<const char*>((wave < DK_R ? nbT2 : deltaT) + ((b * I + il) * H + h) * NP + 4 * (lane & 7));
@@ -540,7 +540,7 @@ __global__ void __launch_bounds__(DK_THR, 2) bwd_dkdv_lds(BwdProblem p, const _F
     }
     // LDS byte offsets (stage 0) of this lane's reads: Q and dO rows (A of S and dP), the
     // transposed reads of Q and dO (A of dK, dV), the bias chunks of its first key tile
-    // (second tile +4096), and nb / delta of its 16 query rows 8a + 4 h2 + e
+    // (second tile +4096), and nb' / -delta of its 16 query rows 8a + 4 h2 + e
     uint32_t aq[2], at[4], ac[2];
 #pragma unroll
     for (int m = 0; m < 2; ++m) aq[m] = DK_Q_OFF + line * 2048 + c * 64 + kv_chunk(c, 2 * m + h2) * 16;
@@ -621,17 +621,20 @@ __global__ void __launch_bounds__(DK_THR, 2) bwd_dkdv_lds(BwdProblem p, const _F
                 for (int e = 0; e < 4; ++e) S[4 * a + e] = __uint_as_float(nn[a][e]);
             S = mfma(__builtin_bit_cast(bf16x8, qq[0]), kB[u][0], S);
             S = mfma(__builtin_bit_cast(bf16x8, qq[1]), kB[u][1], S);
-            f32x16 dP = mfma(__builtin_bit_cast(bf16x8, gg[0]), vB[u][0], f32x16{});
-            dP = mfma(__builtin_bit_cast(bf16x8, gg[1]), vB[u][1], dP);
-            // register r = 4a + e holds query row 8a + 4 h2 + e: nb and delta from nn[a][e], dd[a][e]
+            // register r = 4a + e holds query row 8a + 4 h2 + e: nb' and -delta from nn[a][e],
+            // dd[a][e] seed the two accumulators
+            f32x16 dP;
 #pragma unroll
             for (int a = 0; a < 4; ++a)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 4 * a + e;
-                    S[r] = __builtin_amdgcn_exp2f(fmaf(S[r], kScale, half_of(cc[0], cc[1], r)));
-                    dP[r] = S[r] * (dP[r] - __uint_as_float(dd[a][e]));
-                }
+                for (int e = 0; e < 4; ++e) dP[4 * a + e] = __uint_as_float(dd[a][e]);
+            dP = mfma(__builtin_bit_cast(bf16x8, gg[0]), vB[u][0], dP);
+            dP = mfma(__builtin_bit_cast(bf16x8, gg[1]), vB[u][1], dP);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                S[r] = __builtin_amdgcn_exp2f(fmaf(S[r], kScale, half_of(cc[0], cc[1], r)));
+                dP[r] = S[r] * dP[r];
+            }
             bf16x8 p0, p1, s0, s1;
             to_bf16(S, p0, p1);
             to_bf16(dP, s0, s1);
@@ -670,14 +673,18 @@ __global__ void __launch_bounds__(DK_THR, 2) bwd_dkdv_lds(BwdProblem p, const _F
 // ---------------------------------------------------------------------------------------
 // dbias[b, h, j, k] = sum over the rows i held of dS[i, j, k].  A workgroup of 8 waves owns
 // DB_Q = 256 queries x DB_K = 128 keys of one (b, h) and streams the rows i through a ring
-// of LDS stages: per row the waves copy Q, dO (its queries), K, V (its keys), lse and delta
+// of LDS stages: per row the waves copy Q, dO (its queries), K, V (its keys), nb' and -delta
 // straight from global memory into a stage (global_load_lds_dwordx4), and wave w computes
-// queries 64 (w % 4) .. +63 against keys 64 (w / 4) .. +63 (four 32 x 32 units) from LDS:
-//   S^T = K Q^T + C,  dP^T = V dO^T,  acc += P^T (dP^T - delta)
-// Four units per wave and row keep the per-row costs (the barrier, the LDS round trip that
-// all waves start together after it) small against the work.  The bias tiles C stay in
-// registers for the whole loop.  Every sum over i runs in one lane in row order:
-// deterministic.
+// queries 64 (w % 4) .. +63 against keys 64 (w / 4) .. +63 (four 32 x 32 units) from LDS.
+// The bias is the same in every row, so it leaves the loop: with r_j the query's reference
+// (the forward prepass's) and E[j, k] = 2^((bias + mask - r_j) log2(e)),
+//   p = 2^x' E,   x' = (q.k + (r_j - lse) sqrt(D)) log2(e) / sqrt(D),
+// and the loop sums acc = sum_i 2^x' (dP - delta) from S^T = K Q^T and dP^T = V dO^T alone;
+// dbias = E acc at the end (0 where E is 0: keys dropped by the mask).  Inside the image's
+// span (every finite (bias + mask - r_j) log2(e) >= -32, or the (b, h) is left to the fp32
+// kernel) a kept key has x' <= 32, so 2^x' stays finite.  Without bias registers a wave
+// issues the next unit's four products under the current unit's exponentials.  Every sum
+// over i runs in one lane in row order: deterministic.
 #ifndef TRI_ATTN_DB_Q
 #define TRI_ATTN_DB_Q 256
 #endif
@@ -713,8 +720,8 @@ struct DbStage {
     __bf16 g[DB_Q][D];     // dO rounded to bf16
     __bf16 k[DB_K][D];
     __bf16 v[DB_K][D];
-    float lse[DB_Q];       // nb = -lse log2(e)
-    float dl[DB_Q];        // delta
+    float lse[DB_Q];       // nb' = (r_j - lse) sqrt(D)
+    float dl[DB_Q];        // -delta
 };
 constexpr int DB_STAGE_BYTES = static_cast<int>(sizeof(DbStage));
 constexpr int DB_Q_OFF = static_cast<int>(offsetof(DbStage, q));
@@ -746,8 +753,8 @@ struct DbCtx {
     uint32_t off;                 // this lane's offset inside a piece
     int64_t N, pos_bytes;         // positions, bytes between consecutive positions
     int64_t row_step;             // bytes between rows i of one tensor
-    const char* ls_src;           // lse / delta piece of row 0 (lanes 0 .. 15)
-    int64_t ls_step;              // bytes between rows i of nbT
+    const char* ls_src;           // nb' / delta piece of row 0 (lanes 0 .. 15)
+    int64_t ls_step;              // bytes between rows i of nbT2
     uint32_t ls_dst;
 };
 
@@ -782,9 +789,92 @@ __device__ __forceinline__ void db_barrier_keep() {
         asm volatile("s_waitcnt vmcnt(%c0)\n\ts_barrier" ::"i"(DB_COPIES * (DB_STAGES - 2)) : "memory");
 }
 
-__global__ void __launch_bounds__(DB_THR, TRI_ATTN_DB_WG_PER_CU) bwd_dbias_lds(BwdProblem p, const float* img, const __bf16* g16,
-                                                        const float* nbT, const float* deltaT, int n_jb, int nblk,
-                                                        int64_t NP, int n_tq, int n_tk, int total) {
+// One row's operands of a wave: [tile][d-half] K of key tile ki, V, Q of query tile qi, dO;
+// nb' and -delta per query tile.
+struct DbOps {
+    u32x4 kk[2][2], vv[2][2], qq[2][2], gg[2][2];
+    float nb[2], dl[2];
+};
+
+// Reads a row's operands from its stage at `st` (LDS byte address) and waits for them.
+__device__ __forceinline__ void db_read(uint32_t st, const uint32_t (&ok)[2], const uint32_t (&oq)[2], uint32_t ol,
+                                        DbOps& o) {
+    asm volatile(
+        "ds_read_b128 %0, %20\n\t"
+        "ds_read_b128 %1, %21\n\t"
+        "ds_read_b128 %2, %20 offset:2048\n\t"
+        "ds_read_b128 %3, %21 offset:2048\n\t"
+        "ds_read_b128 %4, %22\n\t"
+        "ds_read_b128 %5, %23\n\t"
+        "ds_read_b128 %6, %22 offset:2048\n\t"
+        "ds_read_b128 %7, %23 offset:2048\n\t"
+        "ds_read_b128 %8, %20 offset:8192\n\t"
+        "ds_read_b128 %9, %21 offset:8192\n\t"
+        "ds_read_b128 %10, %20 offset:10240\n\t"
+        "ds_read_b128 %11, %21 offset:10240\n\t"
+        "ds_read_b128 %12, %22 offset:%c25\n\t"
+        "ds_read_b128 %13, %23 offset:%c25\n\t"
+        "ds_read_b128 %14, %22 offset:%c26\n\t"
+        "ds_read_b128 %15, %23 offset:%c26\n\t"
+        "ds_read_b32 %16, %24\n\t"
+        "ds_read_b32 %17, %24 offset:128\n\t"
+        "ds_read_b32 %18, %24 offset:%c27\n\t"
+        "ds_read_b32 %19, %24 offset:%c28\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(o.kk[0][0]), "=&v"(o.kk[0][1]), "=&v"(o.kk[1][0]), "=&v"(o.kk[1][1]), "=&v"(o.qq[0][0]),
+          "=&v"(o.qq[0][1]), "=&v"(o.qq[1][0]), "=&v"(o.qq[1][1]), "=&v"(o.vv[0][0]), "=&v"(o.vv[0][1]),
+          "=&v"(o.vv[1][0]), "=&v"(o.vv[1][1]), "=&v"(o.gg[0][0]), "=&v"(o.gg[0][1]), "=&v"(o.gg[1][0]),
+          "=&v"(o.gg[1][1]), "=&v"(o.nb[0]), "=&v"(o.nb[1]), "=&v"(o.dl[0]), "=&v"(o.dl[1])
+        : "v"(st + ok[0]), "v"(st + ok[1]), "v"(st + oq[0]), "v"(st + oq[1]), "v"(st + ol),
+          "i"(DB_G_OFF - DB_Q_OFF), "i"(DB_G_OFF - DB_Q_OFF + 2048), "i"(DB_DL_OFF - DB_L_OFF),
+          "i"(DB_DL_OFF - DB_L_OFF + 128));
+}
+
+// One row's four units u = 2 qi + ki: acc[u] += 2^x' (dP - delta).  Each unit's products are
+// issued one per chunk of four scores of the unit before it, so the matrix unit runs under
+// that unit's exponentials.
+__device__ __forceinline__ void db_row(const DbOps& o, f32x16 (&acc)[4]) {
+    const float nbs[2] = {o.nb[0] * kScale, o.nb[1] * kScale};   // (r_j - lse) log2(e); -inf stays -inf
+    const f32x16 zero = {};
+    f32x16 ndl[2];                                                // -delta: seeds dP, which then holds dP - delta
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        ndl[0][r] = o.dl[0];
+        ndl[1][r] = o.dl[1];
+    }
+    f32x16 S = mfma(__builtin_bit_cast(bf16x8, o.kk[0][0]), __builtin_bit_cast(bf16x8, o.qq[0][0]), zero);
+    f32x16 dP = mfma(__builtin_bit_cast(bf16x8, o.vv[0][0]), __builtin_bit_cast(bf16x8, o.gg[0][0]), ndl[0]);
+    S = mfma(__builtin_bit_cast(bf16x8, o.kk[0][1]), __builtin_bit_cast(bf16x8, o.qq[0][1]), S);
+    dP = mfma(__builtin_bit_cast(bf16x8, o.vv[0][1]), __builtin_bit_cast(bf16x8, o.gg[0][1]), dP);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int qi = u >> 1;
+        const int nq = (u + 1) >> 1, nk = (u + 1) & 1;   // the next unit's tiles
+        f32x16 Sn = zero, dPn = zero;
+#pragma unroll
+        for (int ch = 0; ch < 4; ++ch) {
+            if (u + 1 < 4) {
+                if (ch == 0) Sn = mfma(__builtin_bit_cast(bf16x8, o.kk[nk][0]), __builtin_bit_cast(bf16x8, o.qq[nq][0]), zero);
+                if (ch == 1) dPn = mfma(__builtin_bit_cast(bf16x8, o.vv[nk][0]), __builtin_bit_cast(bf16x8, o.gg[nq][0]), ndl[nq]);
+                if (ch == 2) Sn = mfma(__builtin_bit_cast(bf16x8, o.kk[nk][1]), __builtin_bit_cast(bf16x8, o.qq[nq][1]), Sn);
+                if (ch == 3) dPn = mfma(__builtin_bit_cast(bf16x8, o.vv[nk][1]), __builtin_bit_cast(bf16x8, o.gg[nq][1]), dPn);
+            }
+#pragma unroll
+            for (int r = 4 * ch; r < 4 * ch + 4; ++r)
+                acc[u][r] = fmaf(__builtin_amdgcn_exp2f(fmaf(S[r], kScale, nbs[qi])), dP[r], acc[u][r]);
+            asm volatile("" : "+v"(acc[u]));   // the sums are used only next row: keep them in this chunk
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        S = Sn;
+        dP = dPn;
+    }
+}
+
+__global__ void __launch_bounds__(DB_THR, TRI_ATTN_DB_WG_PER_CU) bwd_dbias_lds(BwdProblem p, const float* ref16, int64_t nqp16,
+                                                        const int* wide, int n_wide, const __bf16* g16,
+                                                        const float* nbT2, const float* deltaT, int64_t NP, int n_tq,
+                                                        int n_tk, int total) {
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c = lane & 31, h2 = lane >> 5;
@@ -807,6 +897,7 @@ __global__ void __launch_bounds__(DB_THR, TRI_ATTN_DB_WG_PER_CU) bwd_dbias_lds(B
     const int64_t N = p.N, H = p.H, HD = H * D;
     const int64_t b = bh / H, h = bh % H;
     const int64_t j0 = static_cast<int64_t>(jt) * DB_Q, k0 = static_cast<int64_t>(kt) * DB_K;
+    if (any_wide(wide, bh, n_wide)) return;   // left to the fp32 kernel (whole workgroup)
 
     DbCtx cx;
     {
@@ -830,36 +921,14 @@ __global__ void __launch_bounds__(DB_THR, TRI_ATTN_DB_WG_PER_CU) bwd_dbias_lds(B
         cx.N = N;
         cx.pos_bytes = HD * 2;
         cx.row_step = N * HD * 2;
-        // lse / delta: wave w < DB_NQP copies nb of queries 64 w .. +63, the others delta
-        const float* ls = wave < DB_NQP ? nbT : deltaT;
+        // nb' / -delta: wave w < DB_NQP copies nb' of queries 64 w .. +63, the others -delta
+        const float* ls = wave < DB_NQP ? nbT2 : deltaT;
         cx.ls_src = reinterpret_cast<const char*>(ls + (b * p.I * H + h) * NP + j0 + 64 * (wave % DB_NQP));
         cx.ls_step = H * NP * 4;
         cx.ls_dst = DB_L_OFF + 256 * wave;
     }
 
     const int qp = wave % DB_NQP, kp = wave / DB_NQP;
-    // bias (+ mask) * sqrt(D) of this lane's queries for the 16 keys of each unit's registers;
-    // unit u = 2 qi + ki: queries 64 qp + 32 qi + c, keys 64 kp + 32 ki + ...
-    f32x16 C[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int qi = u >> 1, ki = u & 1;
-        const int64_t j = j0 + 64 * qp + 32 * qi + c;
-        const bool jok = j < N;
-        const int64_t kb = k0 + 64 * kp + 32 * ki;             // a multiple of 32: one image key block
-        if (kb >= N) {
-            C[u] = f32x16{} - INFINITY;
-            continue;
-        }
-        const int jb = static_cast<int>((jok ? j : 0) / IMG_BJ), jj = static_cast<int>((jok ? j : 0) % IMG_BJ);
-        const float* t = img + ((bh * n_jb + jb) * static_cast<int64_t>(nblk) + kb / IMG_BK) * IMG_BJ * IMG_BK + jj * IMG_BK;
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-            const f32x4 x = *reinterpret_cast<const f32x4*>(t + img_chunk(jj, 2 * a + h2) * 4);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) C[u][4 * a + e] = x[e];
-        }
-    }
     // LDS byte offsets of this lane's operand reads (stage 0, tile 0 of each pair); the
     // second tile of a pair is 32 rows (+2048) on
     const int kr = 64 * kp + c, qr = 64 * qp + c;
@@ -873,6 +942,7 @@ __global__ void __launch_bounds__(DB_THR, TRI_ATTN_DB_WG_PER_CU) bwd_dbias_lds(B
     const uint32_t st0 = LDS_ADDR(&g_db[0]);
 
     f32x16 acc[4] = {};
+    DbOps ops;
     const int64_t I = p.I;
     // prologue: rows 0 .. DB_STAGES - 2 in flight, row 0 complete everywhere
     for (int64_t r = 0; r < DB_STAGES - 1 && r < I; ++r) db_stage(cx, r, static_cast<int>(r), lane);
@@ -884,69 +954,32 @@ __global__ void __launch_bounds__(DB_THR, TRI_ATTN_DB_WG_PER_CU) bwd_dbias_lds(B
         const uint32_t st = st0 + static_cast<uint32_t>(i % DB_STAGES) * DB_STAGE_BYTES;
         const bool issue = i + DB_STAGES - 1 < I;
         if (issue) db_stage(cx, i + DB_STAGES - 1, static_cast<int>((i + DB_STAGES - 1) % DB_STAGES), lane);
-        // [tile][d-half]: K of key tile ki, V, Q of query tile qi, dO; nb and delta per query tile
-        u32x4 kk[2][2], vv[2][2], qq[2][2], gg[2][2];
-        float nb[2], dl[2];
-        asm volatile(
-            "ds_read_b128 %0, %20\n\t"
-            "ds_read_b128 %1, %21\n\t"
-            "ds_read_b128 %2, %20 offset:2048\n\t"
-            "ds_read_b128 %3, %21 offset:2048\n\t"
-            "ds_read_b128 %4, %22\n\t"
-            "ds_read_b128 %5, %23\n\t"
-            "ds_read_b128 %6, %22 offset:2048\n\t"
-            "ds_read_b128 %7, %23 offset:2048\n\t"
-            "ds_read_b128 %8, %20 offset:8192\n\t"
-            "ds_read_b128 %9, %21 offset:8192\n\t"
-            "ds_read_b128 %10, %20 offset:10240\n\t"
-            "ds_read_b128 %11, %21 offset:10240\n\t"
-            "ds_read_b128 %12, %22 offset:%c25\n\t"
-            "ds_read_b128 %13, %23 offset:%c25\n\t"
-            "ds_read_b128 %14, %22 offset:%c26\n\t"
-            "ds_read_b128 %15, %23 offset:%c26\n\t"
-            "ds_read_b32 %16, %24\n\t"
-            "ds_read_b32 %17, %24 offset:128\n\t"
-            "ds_read_b32 %18, %24 offset:%c27\n\t"
-            "ds_read_b32 %19, %24 offset:%c28\n\t"
-            "s_waitcnt lgkmcnt(0)"
-            : "=&v"(kk[0][0]), "=&v"(kk[0][1]), "=&v"(kk[1][0]), "=&v"(kk[1][1]), "=&v"(qq[0][0]), "=&v"(qq[0][1]),
-              "=&v"(qq[1][0]), "=&v"(qq[1][1]), "=&v"(vv[0][0]), "=&v"(vv[0][1]), "=&v"(vv[1][0]), "=&v"(vv[1][1]),
-              "=&v"(gg[0][0]), "=&v"(gg[0][1]), "=&v"(gg[1][0]), "=&v"(gg[1][1]), "=&v"(nb[0]), "=&v"(nb[1]),
-              "=&v"(dl[0]), "=&v"(dl[1])
-            : "v"(st + ok[0]), "v"(st + ok[1]), "v"(st + oq[0]), "v"(st + oq[1]), "v"(st + ol),
-              "i"(DB_G_OFF - DB_Q_OFF), "i"(DB_G_OFF - DB_Q_OFF + 2048), "i"(DB_DL_OFF - DB_L_OFF),
-              "i"(DB_DL_OFF - DB_L_OFF + 128));
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int qi = u >> 1, ki = u & 1;
-            // one unit's S and dP at a time (the registers hold the four bias tiles and sums):
-            // this unit's operands pass through an empty statement ordered after the previous
-            // unit's sums, so its products cannot be hoisted above that unit's work
-            asm volatile("" : "+v"(C[u]), "+v"(kk[ki][0]), "+v"(kk[ki][1]), "+v"(vv[ki][0]), "+v"(vv[ki][1]));
-            f32x16 S = mfma(__builtin_bit_cast(bf16x8, kk[ki][0]), __builtin_bit_cast(bf16x8, qq[qi][0]), C[u]);
-            S = mfma(__builtin_bit_cast(bf16x8, kk[ki][1]), __builtin_bit_cast(bf16x8, qq[qi][1]), S);
-            f32x16 dP = mfma(__builtin_bit_cast(bf16x8, vv[ki][0]), __builtin_bit_cast(bf16x8, gg[qi][0]), f32x16{});
-            dP = mfma(__builtin_bit_cast(bf16x8, vv[ki][1]), __builtin_bit_cast(bf16x8, gg[qi][1]), dP);
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                acc[u][r] = fmaf(__builtin_amdgcn_exp2f(fmaf(S[r], kScale, nb[qi])), dP[r] - dl[qi], acc[u][r]);
-            asm volatile("" : "+v"(acc[u]));
-        }
+        db_read(st, ok, oq, ol, ops);
+        db_row(ops, acc);
         if (issue)
             db_barrier_keep();
         else
             db_barrier_drain();
     }
+    // dbias = E acc, E = 2^((bias + mask - r_j) log2(e)) from the raw bias; a key that E
+    // drops (the mask, or a query without any kept key) gets exactly 0
+    const uint16_t* braw = static_cast<const uint16_t*>(p.bias);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
         const int qi = u >> 1, ki = u & 1;
         const int64_t j = j0 + 64 * qp + 32 * qi + c;
         if (j >= N) continue;
+        const float rj = ref16[bh * nqp16 + j];
         float* out = p.dbias + (bh * N + j) * N;
+        const uint16_t* brow = braw + (bh * N + j) * N;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int64_t kk = k0 + 64 * kp + 32 * ki + 8 * (r / 4) + 4 * h2 + (r % 4);
-            if (kk < N) out[kk] = acc[u][r];
+            if (kk >= N) continue;
+            const float bv = __uint_as_float(static_cast<uint32_t>(brow[kk]) << 16);
+            const float mk = p.mask ? p.mask[b * N + kk] : 0.0f;
+            const float e = __builtin_amdgcn_exp2f((bv + mk - rj) * kLog2e);
+            out[kk] = e > 0.0f ? e * acc[u][r] : 0.0f;
         }
     }
 }
@@ -992,7 +1025,7 @@ struct BwdLayout {
     Problem fwd;            // the image problem: the bias and mask over all keys
     Prepass16 pre;          // the forward's prepass: fp16 image and r_j (dq, dk/dv)
     int64_t NP, nq;
-    size_t img, pre16, imgT16, g16, delta, nbT, nbT2, deltaT, total;   // byte offsets / total
+    size_t pre16, imgT16, g16, delta, nbT2, deltaT, total;   // byte offsets / total
 };
 
 BwdLayout bwd_layout(const BwdProblem& p) {
@@ -1004,13 +1037,11 @@ BwdLayout bwd_layout(const BwdProblem& p) {
     const size_t per_line = static_cast<size_t>(p.B * p.I * p.H * L.NP) * 4;
     const int64_t n_kt = (p.N + IMG_BJ - 1) / IMG_BJ, nqb = (p.N + 31) / 32;
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
-    L.img = 0;
-    L.pre16 = up(L.img + bias_image_bytes(L.fwd));
+    L.pre16 = 0;
     L.imgT16 = up(L.pre16 + L.pre.bytes);
     L.g16 = up(L.imgT16 + static_cast<size_t>(p.B * p.H * n_kt * nqb) * IMG_BJ * 32 * 2);
     L.delta = up(L.g16 + static_cast<size_t>(L.nq) * D * 2);
-    L.nbT = up(L.delta + static_cast<size_t>(L.nq) * 4);
-    L.nbT2 = L.nbT + per_line;
+    L.nbT2 = up(L.delta + static_cast<size_t>(L.nq) * 4);
     L.deltaT = L.nbT2 + per_line;
     L.total = L.deltaT + per_line;
     return L;
@@ -1024,14 +1055,12 @@ hipError_t launch_backward_mfma(const BwdProblem& p, void* workspace, hipStream_
     const int64_t n_jb = (p.N + IMG_BJ - 1) / IMG_BJ;
     const int64_t nblk = bias_image_blocks(Ly.fwd);      // 32-key blocks
     char* ws = static_cast<char*>(workspace);
-    float* img = reinterpret_cast<float*>(ws + Ly.img);
     _Float16* img16 = reinterpret_cast<_Float16*>(ws + Ly.pre16);
     const float* ref16 = reinterpret_cast<const float*>(ws + Ly.pre16 + Ly.pre.ref_off);
     const int* wide = reinterpret_cast<const int*>(ws + Ly.pre16 + Ly.pre.wide_off);
     _Float16* imgT16 = reinterpret_cast<_Float16*>(ws + Ly.imgT16);
     __bf16* g16 = reinterpret_cast<__bf16*>(ws + Ly.g16);
     float* delta = reinterpret_cast<float*>(ws + Ly.delta);
-    float* nbT = reinterpret_cast<float*>(ws + Ly.nbT);
     float* nbT2 = reinterpret_cast<float*>(ws + Ly.nbT2);
     float* deltaT = reinterpret_cast<float*>(ws + Ly.deltaT);
     const int64_t n_prep = p.B * p.I * p.H * Ly.NP * PREP_PARTS;
@@ -1041,13 +1070,12 @@ hipError_t launch_backward_mfma(const BwdProblem& p, void* workspace, hipStream_
         return hipErrorInvalidConfiguration;
     hipError_t e = launch_prepass16(Ly.fwd, ws + Ly.pre16, stream);
     if (e != hipSuccess) return e;
-    if ((e = launch_bias_image(Ly.fwd, img, stream)) != hipSuccess) return e;
     hipLaunchKernelGGL(bias_imageT16_kernel, dim3(static_cast<unsigned>(n_kt * nqb), static_cast<unsigned>(p.B * p.H)),
                        dim3(256), 0, stream, p, ref16, Ly.pre.nqp, imgT16, static_cast<int>(n_kt),
                        static_cast<int>(nqb));
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(bwd_prep_kernel, dim3(static_cast<unsigned>((n_prep + 255) / 256)), dim3(256), 0, stream, p, g16,
-                       delta, nbT, deltaT, Ly.NP, ref16, Ly.pre.nqp, nbT2);
+                       delta, deltaT, Ly.NP, ref16, Ly.pre.nqp, nbT2);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     {
         const int64_t n_rg = (p.I + DQ_R - 1) / DQ_R;
@@ -1067,13 +1095,13 @@ hipError_t launch_backward_mfma(const BwdProblem& p, void* workspace, hipStream_
                            static_cast<int>(n_rg), static_cast<int>(nblk), Ly.NP, static_cast<int>(total));
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    // dq and dk/dv of every (b, h) whose bias spans more than the fp16 image keeps
+    // dq, dk/dv and dbias of every (b, h) whose bias spans more than the fp16 image keeps
     if ((e = launch_backward_wide(p, wide, static_cast<int>(Ly.pre.n_jb), stream)) != hipSuccess) return e;
     const int64_t n_tq = (p.N + DB_Q - 1) / DB_Q, n_tk = (p.N + DB_K - 1) / DB_K;
     const int64_t total = n_tq * n_tk * p.B * p.H;
     if (total > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(bwd_dbias_lds, dim3(static_cast<unsigned>(total)), dim3(DB_THR), 0, stream, p, img, g16, nbT,
-                       deltaT, static_cast<int>(n_jb), static_cast<int>(nblk), Ly.NP, static_cast<int>(n_tq),
+    hipLaunchKernelGGL(bwd_dbias_lds, dim3(static_cast<unsigned>(total)), dim3(DB_THR), 0, stream, p, ref16, Ly.pre.nqp,
+                       wide, static_cast<int>(Ly.pre.n_jb), g16, nbT2, deltaT, Ly.NP, static_cast<int>(n_tq),
                        static_cast<int>(n_tk), static_cast<int>(total));
     return hipGetLastError();
 }

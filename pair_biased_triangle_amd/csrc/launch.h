@@ -65,8 +65,9 @@ struct BwdProblem {
     int64_t B, H, I, N, D;
 };
 hipError_t launch_backward(const BwdProblem& p, bool bf16, hipStream_t stream);
-// dq, dk and dv of the fp32 kernels (bf16 inputs), only for the (b, h) whose n_wide flags
-// wide[(b*H + h) * n_wide + t] include a nonzero one; every other workgroup returns at once.
+// dq, dk, dv and dbias of the fp32 kernels (bf16 inputs), only for the (b, h) whose n_wide
+// flags wide[(b*H + h) * n_wide + t] include a nonzero one; every other workgroup returns
+// at once.
 hipError_t launch_backward_wide(const BwdProblem& p, const int* wide, int n_wide, hipStream_t stream);
 
 // bf16 inputs, D == 32: matrix-core forward.  `workspace` (16-byte aligned, at least
@@ -103,8 +104,9 @@ int64_t bias_image_blocks(const Problem& p);   // nblk
 size_t bias_image_bytes(const Problem& p);
 hipError_t launch_bias_image(const Problem& p, float* img, hipStream_t stream);
 
-// Backward on matrix cores (bf16, D == 32).  Workspace: the bias image (keys in one tile),
-// dout rounded to bf16 and delta = dout . out per query; bwd_mfma_workspace_bytes() bytes.
+// Backward on matrix cores (bf16, D == 32).  Workspace: the forward's prepass (fp16 image,
+// references, span flags), the transposed fp16 image, dout rounded to bf16, delta = dout .
+// out per query and the per-row statistics; bwd_mfma_workspace_bytes() bytes.
 size_t bwd_mfma_workspace_bytes(const BwdProblem& p);
 hipError_t launch_backward_mfma(const BwdProblem& p, void* workspace, hipStream_t stream);
 
