@@ -127,57 +127,63 @@ __global__ void __launch_bounds__(ST_THR) state_finalize_kernel(const float* acc
 // Join n_split partial states stored split after split (acc [n_split][rows][D], m and l
 // [n_split][rows]) into out = acc / l and lse = m + ln l of the merged state, in one pass:
 // the merge rule applied to all splits at once, m* = max m_s, l = sum e^(m_s - m*) l_s.
-// A workgroup owns CB_Q queries, so that small joins still spread over the chip.
+// A thread owns 4 (VEC) or 1 consecutive elements of one query and issues every load it
+// needs (each split's m, l and acc elements) before using any, so the join costs one
+// memory round trip; the threads of a query repeat its m and l loads (cache hits).
 constexpr int MAX_COMBINE = 16;
-constexpr int CB_Q = 16;
-constexpr int CB_THR = 128;
+constexpr int CB_THR = 256;
 template <bool VEC>
 __global__ void __launch_bounds__(CB_THR) state_combine_kernel(const float* acc, const float* m, const float* l,
                                                                int n_split, int64_t rows, int D, float* out,
                                                                float* lse) {
-    __shared__ float fac[MAX_COMBINE][CB_Q];
-    const int64_t q0 = static_cast<int64_t>(blockIdx.x) * CB_Q;
-    const int nq = static_cast<int>(rows - q0 < CB_Q ? rows - q0 : CB_Q);
-    const int tid = threadIdx.x;
-    if (tid < nq) {
-        const int64_t q = q0 + tid;
-        float mx = -INFINITY;
-        for (int s = 0; s < n_split; ++s)
-            if (l[s * rows + q] > 0.0f) mx = fmaxf(mx, m[s * rows + q]);
-        float lt = 0.0f;
-        for (int s = 0; s < n_split; ++s) {
-            const float ls = l[s * rows + q];
-            const float f = ls > 0.0f ? expf(m[s * rows + q] - mx) : 0.0f;
-            fac[s][tid] = f;
-            lt += f * ls;
-        }
-        const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-        for (int s = 0; s < n_split; ++s) fac[s][tid] *= inv;
-        if (lse) lse[q] = lt > 0.0f ? mx + logf(lt) : -INFINITY;
-    }
-    __syncthreads();
-    const int64_t e0 = q0 * D;
-    const int ne = nq * D;
-    if constexpr (VEC) {
-        for (int e = tid; e < ne / 4; e += CB_THR) {
-            const int qq = 4 * e / D;
-            f32x4 x = {};
-#pragma unroll 4
-            for (int s = 0; s < n_split; ++s) {
-                const f32x4 a = reinterpret_cast<const f32x4*>(acc + s * rows * D + e0)[e];
+    constexpr int W = VEC ? 4 : 1;
+    const int per_q = D / W;                          // threads per query (D % W == 0)
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * CB_THR + threadIdx.x;
+    if (t >= rows * per_q) return;
+    const int64_t q = t / per_q;
+    const int part = static_cast<int>(t - q * per_q);
+    float ms[MAX_COMBINE], ls[MAX_COMBINE];
+    float a[MAX_COMBINE][W];
 #pragma unroll
-                for (int c = 0; c < 4; ++c) x[c] = fmaf(fac[s][qq], a[c], x[c]);
+    for (int s = 0; s < MAX_COMBINE; ++s) {
+        if (s < n_split) {
+            ms[s] = m[s * rows + q];
+            ls[s] = l[s * rows + q];
+            const float* src = acc + (s * rows + q) * D + part * W;
+            if constexpr (VEC) {
+                const f32x4 v = *reinterpret_cast<const f32x4*>(src);
+#pragma unroll
+                for (int c = 0; c < W; ++c) a[s][c] = v[c];
+            } else {
+                a[s][0] = *src;
             }
-            reinterpret_cast<f32x4*>(out + e0)[e] = x;
-        }
-    } else {
-        for (int e = tid; e < ne; e += CB_THR) {
-            const int qq = e / D;
-            float x = 0.0f;
-            for (int s = 0; s < n_split; ++s) x = fmaf(fac[s][qq], acc[s * rows * D + e0 + e], x);
-            out[e0 + e] = x;
+        } else {
+            ms[s] = -INFINITY;
+            ls[s] = 0.0f;
+#pragma unroll
+            for (int c = 0; c < W; ++c) a[s][c] = 0.0f;
         }
     }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < MAX_COMBINE; ++s)
+        if (ls[s] > 0.0f) mx = fmaxf(mx, ms[s]);
+    float lt = 0.0f, x[W] = {};
+#pragma unroll
+    for (int s = 0; s < MAX_COMBINE; ++s) {
+        const float f = ls[s] > 0.0f ? expf(ms[s] - mx) : 0.0f;
+        lt += f * ls[s];
+#pragma unroll
+        for (int c = 0; c < W; ++c) x[c] = fmaf(f, a[s][c], x[c]);
+    }
+    const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+    float* dst = out + q * D + part * W;
+    if constexpr (VEC) {
+        *reinterpret_cast<f32x4*>(dst) = f32x4{x[0] * inv, x[1] * inv, x[2] * inv, x[3] * inv};
+    } else {
+        *dst = x[0] * inv;
+    }
+    if (lse && part == 0) lse[q] = lt > 0.0f ? mx + logf(lt) : -INFINITY;
 }
 
 }  // namespace
@@ -216,8 +222,11 @@ hipError_t launch_state_finalize(const float* acc, const float* m, const float* 
 
 hipError_t launch_state_combine(const float* acc, const float* m, const float* l, int n_split, int64_t rows,
                                 int64_t D, float* out, float* lse, hipStream_t stream) {
-    const int64_t blocks = (rows + CB_Q - 1) / CB_Q;
-    if (blocks > 0x7FFFFFFF || n_split < 1 || n_split > MAX_COMBINE) return hipErrorInvalidConfiguration;
+    if (D < 1 || n_split < 1 || n_split > MAX_COMBINE) return hipErrorInvalidConfiguration;
+    const int64_t threads = rows * (vec_ok(D, acc, out) ? D / 4 : D);
+    const int64_t blocks = (threads + CB_THR - 1) / CB_THR;
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    if (blocks == 0) return hipSuccess;
     // every split's accumulator block is rows * D floats: 16-byte aligned when D % 4 == 0
     if (vec_ok(D, acc, out))
         hipLaunchKernelGGL(state_combine_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(CB_THR), 0, stream,
