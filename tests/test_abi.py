@@ -153,16 +153,17 @@ def test_workspace_bytes(lib):
 
 def test_workspace_bytes_of_one_row_calls(lib):
     # one row (attention with pair bias), bf16, D=32, even N: the single-pass kernel's key-range
-    # states, S splits of [rows][D] accumulators plus m and l per row (S so that about 512
-    # workgroups of 128 queries run, at most 16, each split at least 4 key blocks); none
-    # when one range suffices; odd N goes through the fp16 image
+    # states, S splits of [rows][D] accumulators plus m and l per row (S = as many ranges of
+    # the B*H*ceil(N/128) query-block workgroups as one round of 768 resident workgroups
+    # holds, at most 16, each split at least 4 key blocks); none when one range suffices;
+    # odd N goes through the fp16 image
     def single_pass(B, H, N):
         n_qb, nblk, rows = -(-N // 128), -(-N // 32), B * N * H
-        s = min(-(-512 // (B * H * n_qb)), nblk // 4, 16)
+        s = min(768 // (B * H * n_qb), nblk // 4, 16)
         if s < 2:
             return 0
         return s * rows * 32 * 4 + -(-(s * rows * 4) // 256) * 256 + s * rows * 4
-    assert single_pass(1, 4, 2700) == 6 * 10800 * 32 * 4 + 259328 + 6 * 10800 * 4
+    assert single_pass(1, 4, 2700) == 8 * 10800 * 32 * 4 + 345600 + 8 * 10800 * 4
     assert lib.tri_attn_workspace_bytes(1, 4, 1, 2700, 32, 8, BF16) == single_pass(1, 4, 2700)
     assert lib.tri_attn_workspace_bytes(3, 4, 1, 100, 32, 3, BF16) == 0 == single_pass(3, 4, 100)
     assert lib.tri_attn_workspace_bytes(2, 4, 1, 300, 32, 4, BF16) == single_pass(2, 4, 300) > 0
