@@ -29,6 +29,7 @@
 
 #include <cmath>
 #include <cstddef>
+#include <type_traits>
 
 namespace tri_attn {
 namespace {
@@ -381,22 +382,25 @@ __global__ void __launch_bounds__(PTHR, TRI_ATTN_PB_OCC) pair_bias_direct_kernel
         pb_barrier_keep();
     else
         pb_barrier_drain();
-    for (int n = nb0; n < nb1; ++n) {
+    auto step = [&](int n, auto tail) {
+        constexpr bool TAIL = decltype(tail)::value;
         const uint32_t st = st0 + static_cast<uint32_t>(n % PSTAGE) * PB_STAGE_BYTES;
         const bool issue = n + PSTAGE - 1 < nb1;
         if (issue) pb_stage(cx, n + PSTAGE - 1, wave, lane);
         PbOps o;
         pb_read<MASK>(st, ak, av, ab, am, o);
         const f32x16 S = pb_scores(o, qB);
-        if (BK * (n + 1) <= N)
-            pb_soft<MASK, false>(o, S, h2, BK, O, mref, lsum);
-        else
-            pb_soft<MASK, true>(o, S, h2, N - BK * n, O, mref, lsum);
+        pb_soft<MASK, TAIL>(o, S, h2, TAIL ? N - BK * n : BK, O, mref, lsum);
         if (issue)
             pb_barrier_keep();
         else
             pb_barrier_drain();
-    }
+    };
+    // only the last block of the call can run past the last key: it leaves the loop, so the
+    // loop body has one code path for O
+    const int nfull = min(nb1, N / BK);
+    for (int n = nb0; n < nfull; ++n) step(n, std::false_type{});
+    for (int n = max(nb0, nfull); n < nb1; ++n) step(n, std::true_type{});
 
     // lanes l and l ^ 32 hold disjoint keys of the same query; register r holds
     // d = 8 (r / 4) + 4 h2 + r % 4
