@@ -394,3 +394,21 @@ def test_pair_bias_single_pass_moving_reference(torch_dev, N):
     ref, ref_lse = oracle.tri_attn(w.q, w.k, w.v, w.bias, w.mask, n_key_tiles=1)
     compare(out.cpu().numpy(), ref[:, 0], TOL["bf16"], "pair-bias moving reference out")
     compare_lse(lse.cpu().numpy(), ref_lse[:, 0], TOL["bf16"], "pair-bias moving reference lse")
+
+
+@pytest.mark.parametrize("N", [100, 640, 2700])
+def test_pair_bias_without_mask(torch_dev, N):
+    """The single-pass kernel's maskless form (mask = None): one key range at N = 100, whole
+    32-key blocks only at N = 640, ranges joined by the combine and a last block past the
+    last key at N = 2700."""
+    import pair_biased_triangle_amd as P
+    w = small("bf16", B=1, I=1, N=N, D=32, T=1, mask_last=0)
+    assert w.mask is None
+    say(f"[next] pair-bias without a mask, N={N}")
+    q, k, v, bias, _ = dev_inputs(torch_dev, w)
+    shp = (1, N, 4, 32)
+    out, lse = P.pair_bias_attn_fwd(q.view(shp), k.view(shp), v.view(shp), bias, None, want_lse=True)
+    torch_dev.cuda.synchronize()
+    ref, ref_lse = oracle.tri_attn(w.q, w.k, w.v, w.bias, None, n_key_tiles=1)
+    compare(out.cpu().numpy(), ref[:, 0], TOL["bf16"], "pair-bias without mask out")
+    compare_lse(lse.cpu().numpy(), ref_lse[:, 0], TOL["bf16"], "pair-bias without mask lse")
