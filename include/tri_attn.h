@@ -334,11 +334,12 @@ int tri_attn_bwd(const void *q, const void *k, const void *v, const void *bias,
  *     out[b,j,h,:]   = sum_k softmax_k(s)_k * v[b,k,h,:]
  * q, k, v, out [B, N, H, D]; bias [B, H, N, N]; mask [B, N] or NULL; lse [B, N, H] or
  * NULL.  It is the triangle operation with a single row (I == 1), with the same tiling
- * and rules.  With one row every bias value is used once, so for bf16, D == 32 and even N
- * the call (like any one-row tri_attn_fwd_rows call) runs a single-pass kernel that reads
- * the raw bias once with a running reference per query instead of the fp16 image; its
- * workspace holds only the partial states of key ranges run side by side (none when one
- * range suffices).  Odd N takes the image path.
+ * and rules.  With one row every bias value is used once, so for bf16, D == 32, even N up
+ * to 46340 and a 16-byte aligned bias the call (like any one-row tri_attn_fwd_rows call)
+ * runs a single-pass kernel that reads the raw bias once with a running reference per
+ * query instead of the fp16 image; its workspace holds only the partial states of key
+ * ranges run side by side (none when one range suffices).  Other one-row calls take the
+ * image path.
  */
 int pair_bias_attn_fwd(const void *q, const void *k, const void *v, const void *bias,
                        const float *mask, float *out, float *lse,
