@@ -152,3 +152,33 @@ def test_autograd_function(torch_dev):
     ref = oracle.tri_attn_bwd(w.q, w.k, w.v, w.bias, w.mask, dout)
     for n, x, r in zip(NAMES, (q, k, v, bias), ref):
         compare_rel(x.grad.cpu().numpy(), r, 1e-4, f"autograd {n}")
+
+
+@pytest.mark.parametrize("deep", [False, True])
+def test_soft_mask_and_shifted_bias(torch_dev, deep):
+    """A mask of finite values (keys in [-4, 0], none dropped) and one head's bias shifted
+    by +50: the matrix-core dbias multiplies its row sums by 2^((bias + mask - r_j) log2 e)
+    at the end, so a mask that is neither 0 nor -inf and a bias far from 0 both pass
+    through that factor.  With `deep`, every seventh key's mask is -30 instead: finite
+    values further below the row's reference than the fp16 bias image spans, which sends
+    those columns to the fp32 kernels.  Exact statistics, bf16 bar."""
+    import pair_biased_triangle_amd as P
+    t = torch_dev
+    w = W.make_inputs(W.custom_config(B=1, I=8, N=300, H=4, D=32, dtype="bf16", n_key_tiles=1, seed=91,
+                                      sigma_bias=1.0, mask_last=0))
+    bias = W.bf16_bits_to_f32(w.bias)
+    bias[0, 2] += 50.0
+    w.bias = W.f32_to_bf16_bits(bias)
+    mask = (-4.0 * np.random.default_rng(92).random((1, 300))).astype(np.float32)
+    if deep:
+        mask[0, ::7] = -30.0
+    dout = np.random.default_rng(93).standard_normal(w.q.shape).astype(np.float32)
+    say(f"[bwd] soft mask{' with deep keys' if deep else ''}, head 2 shifted by +50, bf16 I=8 N=300")
+    out, lse = oracle.tri_attn(w.q, w.k, w.v, w.bias, mask)
+    q, k, v, b = (to_dev(t, x) for x in (w.q, w.k, w.v, w.bias))
+    g = P.tri_attn_bwd(q, k, v, b, to_dev(t, mask), t.from_numpy(out.astype(np.float32)).cuda(),
+                       t.from_numpy(lse.astype(np.float32)).cuda(), t.from_numpy(dout).cuda())
+    t.cuda.synchronize()
+    ref = oracle.tri_attn_bwd(w.q, w.k, w.v, w.bias, mask, dout)
+    for n, a, r in zip(NAMES, (x.cpu().numpy() for x in g), ref):
+        compare_rel(a, r, 1e-2, f"soft mask{' deep' if deep else ''} {n} bf16")
