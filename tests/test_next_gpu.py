@@ -412,3 +412,36 @@ def test_pair_bias_without_mask(torch_dev, N):
     ref, ref_lse = oracle.tri_attn(w.q, w.k, w.v, w.bias, None, n_key_tiles=1)
     compare(out.cpu().numpy(), ref[:, 0], TOL["bf16"], "pair-bias without mask out")
     compare_lse(lse.cpu().numpy(), ref_lse[:, 0], TOL["bf16"], "pair-bias without mask lse")
+
+
+@pytest.mark.timeout(600)
+def test_pair_bias_largest_single_pass_size(torch_dev):
+    """The largest N the single-pass kernel takes (46340: its copies address one (b, h)
+    bias slab of N * N * 2 bytes with 32-bit offsets, so rows past j = 23170 lie more than
+    2^31 bytes into it).  Each sampled query gets +30 on one key spread over the whole
+    range, so its output is essentially that key's value and any misaddressed bias row or
+    key shows; compared with the oracle on those queries."""
+    import pair_biased_triangle_amd as P
+    N = 46340
+    w = W.make_inputs(W.custom_config(B=1, I=1, N=N, H=1, D=32, dtype="bf16", n_key_tiles=1, seed=97,
+                                      sigma_bias=2.0, mask_last=6))
+    rows = np.array([0, 1, 127, 128, 23170, 23171, 33000, 40000, 46211, 46338, 46339])
+    keys = (rows * 7919 + 11) % (N - 6)
+    bias = w.bias.reshape(N, N)
+    sel = W.bf16_bits_to_f32(bias[rows, keys]) + 30.0
+    bias[rows, keys] = W.f32_to_bf16_bits(sel)
+    ws = P.call_workspace_bytes(P.CALL_PAIR_BIAS, 1, 1, 1, N, 32, N, P.TRI_ATTN_BF16)
+    assert ws < 64 << 20, f"{ws} bytes of workspace: not the single-pass kernel's partial states"
+    say(f"[next] pair-bias at N={N} (single pass, {ws} bytes of workspace)")
+    q, k, v, b, mask = dev_inputs(torch_dev, w)
+    shp = (1, N, 1, 32)
+    out, lse = P.pair_bias_attn_fwd(q.view(shp), k.view(shp), v.view(shp), b, mask, want_lse=True)
+    torch_dev.cuda.synchronize()
+    del b
+    ref, ref_lse = oracle.tri_attn(w.q, w.k, w.v, w.bias, w.mask, n_key_tiles=1, rows=rows)
+    got = out.view(N, 1, 32)[torch_dev.from_numpy(rows).cuda()].cpu().numpy()
+    got_lse = lse.view(N, 1)[torch_dev.from_numpy(rows).cuda()].cpu().numpy()
+    compare(got, ref, TOL["bf16"], f"pair-bias N={N}, {len(rows)} queries")
+    compare_lse(got_lse, ref_lse, TOL["bf16"], f"pair-bias lse N={N}")
+    vk = W.bf16_bits_to_f32(w.v.reshape(N, 32)[keys])
+    assert np.max(np.abs(got[:, 0] - vk)) < 0.1, "a query's output is not its heavy key's value"
