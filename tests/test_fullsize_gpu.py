@@ -159,3 +159,86 @@ def test_backward_n2700_dbias_of_all_rows(torch_dev, n2700):
     diff = float((full.double() - parts[0].double() - parts[1].double()).abs().max())
     say(f"  dbias(all rows) - dbias(rows < 1350) - dbias(rows >= 1350): max |diff| = {diff:.3e} (bar {1e-4 * scale:.3e})")
     assert diff <= 1e-4 * scale
+
+
+
+N4200 = (4200, 4, 32, 8)          # N = I, H, D, key tiles
+
+
+@pytest.fixture(scope="module")
+def n4200(torch_dev):
+    """A square problem larger than any benchmarked one: N = I = 4200 (H = 4, D = 32), whose
+    q, k, v, out and gradients hold 2.26e9 elements each, so lines from i = 3995 on start
+    past 2^31 elements (and 2^32 bytes of bf16).  Inputs from a seeded device generator."""
+    torch = torch_dev
+    N, H, D, _ = N4200
+    g = torch.Generator("cuda").manual_seed(4200)
+    q, k, v = (torch.randn((1, N, N, H, D), dtype=torch.bfloat16, device="cuda", generator=g) for _ in range(3))
+    bias = torch.randn((1, H, N, N), dtype=torch.bfloat16, device="cuda", generator=g)
+    mask = torch.zeros((1, N), dtype=torch.float32, device="cuda")
+    mask[:, N - 30:] = -float("inf")
+    return q, k, v, bias, mask
+
+
+def bf16_host(torch, t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+@pytest.mark.timeout(600)
+def test_forward_square_n4200_past_2_31_elements(torch_dev, n4200):
+    """The oracle on sampled queries of lines on both sides of the 2^31-element boundary;
+    each line's output depends on its own q, k, v and the shared bias only."""
+    import pair_biased_triangle_amd as P
+    torch = torch_dev
+    N, H, D, T = N4200
+    q, k, v, bias, mask = n4200
+    say(f"[full] forward N=I={N}: one call over {N * N * H * D:.3g} elements per tensor")
+    out = P.tri_attn_fwd(q, k, v, bias, mask, n_key_tiles=T)
+    torch.cuda.synchronize()
+    lines = [0, 1, 2047, 3994, 3995, 3996, 4199]
+    cols = np.array([0, 1, 255, 256, 2100, 4170, 4199])
+    idx = torch.tensor(lines, device="cuda")
+    qs, ks, vs = (bf16_host(torch, t[:, idx]) for t in (q, k, v))
+    got = out[:, idx][:, :, torch.from_numpy(cols).cuda()].cpu().numpy()
+    del out
+    rows = np.array([i * N + j for i in range(len(lines)) for j in cols])
+    ref, _ = oracle.tri_attn(qs, ks, vs, bf16_host(torch, bias), mask.cpu().numpy(), n_key_tiles=T, rows=rows)
+    compare(got.reshape(-1, H, D), ref, TOL["bf16"], f"N={N} forward, {len(rows)} queries of {len(lines)} lines")
+
+
+@pytest.mark.timeout(900)
+def test_backward_square_n4200_past_2_31_elements(torch_dev, n4200):
+    """The backward over all 4200 lines: dq, dk, dv of lines on both sides of the 2^31-element
+    boundary against the oracle (the forward statistics of those lines are the oracle's, so
+    the bar is the kernels' own, 1e-2 x max(1, max|oracle|)), and dbias, a sum over every
+    line, through its zero row sums."""
+    import pair_biased_triangle_amd as P
+    torch = torch_dev
+    N, H, D, T = N4200
+    q, k, v, bias, mask = n4200
+    lines = [1, 3994, 3995, 4199]
+    idx = torch.tensor(lines, device="cuda")
+    qs, ks, vs = (bf16_host(torch, t[:, idx]) for t in (q, k, v))
+    bias_h, mask_h = bf16_host(torch, bias), mask.cpu().numpy()
+    dout = torch.randn(q.shape, dtype=torch.float32, device="cuda", generator=torch.Generator("cuda").manual_seed(42))
+    dout_s = dout[:, idx].cpu().numpy()
+    say(f"[full] backward N=I={N}: oracle on {len(lines)} lines")
+    ref_out, ref_lse = oracle.tri_attn(qs, ks, vs, bias_h, mask_h)
+    ref = oracle.tri_attn_bwd(qs, ks, vs, bias_h, mask_h, dout_s)
+    say(f"[full] backward N=I={N}: all lines on the GPU")
+    out, lse = P.tri_attn_fwd_lse(q, k, v, bias, mask, n_key_tiles=T)
+    out[:, idx] = torch.from_numpy(ref_out.astype(np.float32)).cuda()
+    lse[:, idx] = torch.from_numpy(ref_lse.astype(np.float32)).cuda()
+    dq, dk, dv, dbias = P.tri_attn_bwd(q, k, v, bias, mask, out, lse, dout)
+    torch.cuda.synchronize()
+    del out, lse, dout
+    for name, g_, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref[:3]):
+        compare_rel(g_[:, idx].cpu().numpy(), r, 1e-2, f"{name} N={N}, {len(lines)} lines of a full call")
+    del dq, dk, dv
+    kept = slice(0, N - 30)
+    row_sum = dbias[..., kept].double().sum(dim=-1)
+    row_abs = dbias[..., kept].double().abs().sum(dim=-1)
+    worst = float((row_sum.abs() / row_abs.clamp_min(1e-30)).max())
+    say(f"  dbias row sums: max |sum| / sum|.| = {worst:.3e} (bar 1e-2)")
+    assert worst <= 1e-2
+    assert torch.all(dbias[..., N - 30:] == 0), "a masked key got a bias gradient"
