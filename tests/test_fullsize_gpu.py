@@ -242,3 +242,57 @@ def test_backward_square_n4200_past_2_31_elements(torch_dev, n4200):
     say(f"  dbias row sums: max |sum| / sum|.| = {worst:.3e} (bar 1e-2)")
     assert worst <= 1e-2
     assert torch.all(dbias[..., N - 30:] == 0), "a masked key got a bias gradient"
+
+
+@pytest.mark.timeout(600)
+def test_ending_square_n4200_past_2_31_elements(torch_dev, n4200):
+    """The ending node on the same problem: line j is a column, its keys (k, j) lie N * H * D
+    elements apart, and outputs of rows i >= 3995 lie past 2^31 elements; the oracle's
+    ending orientation on sampled (i, j)."""
+    import pair_biased_triangle_amd as P
+    torch = torch_dev
+    N, H, D, T = N4200
+    q, k, v, bias, mask = n4200
+    say(f"[full] ending node N={N}")
+    out = P.tri_attn_fwd_ending(q, k, v, bias, mask, n_key_tiles=T)
+    torch.cuda.synchronize()
+    ii = np.array([0, 1, 2047, 3994, 3995, 4199])
+    jj = np.array([0, 255, 256, 2100, 4199])
+    rows = np.array([i * N + j for i in ii for j in jj])
+    got = out.view(-1, H, D)[torch.from_numpy(rows).cuda()].cpu().numpy()
+    del out
+    ref, _ = oracle.tri_attn(bf16_host(torch, q), bf16_host(torch, k), bf16_host(torch, v), bf16_host(torch, bias),
+                             mask.cpu().numpy(), n_key_tiles=T, rows=rows, ending=True)
+    compare(got, ref, TOL["bf16"], f"N={N} ending, {len(rows)} queries")
+
+
+@pytest.mark.timeout(600)
+def test_ring_square_n4200_past_2_31_elements(torch_dev, n4200):
+    """The split-tile ring on the same problem (first state, six updates, final step): the
+    states hold 2.26e9 accumulator elements; sampled queries of lines on both sides of the
+    boundary against the oracle."""
+    import pair_biased_triangle_amd as P
+    torch = torch_dev
+    N, H, D, T = N4200
+    q, k, v, bias, mask = n4200
+    bounds = [t * (N // T) + min(t, N % T) for t in range(T + 1)]
+    say(f"[full] ring N={N}: state, {T - 2} updates, final step")
+    acc, m, l = P.tri_attn_tile_state(q, k, v, bias, mask, key_begin=bounds[0], key_end=bounds[1])
+    for t in range(1, T - 1):
+        P.tri_attn_tile_state_update(q, k, v, bias, mask, key_begin=bounds[t], key_end=bounds[t + 1], acc=acc, m=m, l=l)
+    out, lse = P.tri_attn_tile_state_final(q, k, v, bias, mask, key_begin=bounds[T - 1], key_end=bounds[T],
+                                           acc=acc, m=m, l=l, want_lse=True)
+    torch.cuda.synchronize()
+    del acc, m, l
+    lines = [2, 3995, 4199]
+    cols = np.array([0, 256, 4199])
+    idx = torch.tensor(lines, device="cuda")
+    cidx = torch.from_numpy(cols).cuda()
+    got = out[:, idx][:, :, cidx].cpu().numpy().reshape(-1, H, D)
+    got_lse = lse[:, idx][:, :, cidx].cpu().numpy().reshape(-1, H)
+    del out, lse
+    qs, ks, vs = (bf16_host(torch, t[:, idx]) for t in (q, k, v))
+    rows = np.array([i * N + j for i in range(len(lines)) for j in cols])
+    ref, ref_lse = oracle.tri_attn(qs, ks, vs, bf16_host(torch, bias), mask.cpu().numpy(), n_key_tiles=T, rows=rows)
+    compare(got, ref, TOL["bf16"], f"N={N} ring out, {len(rows)} queries")
+    compare(got_lse, ref_lse, TOL["bf16"], f"N={N} ring lse")
