@@ -184,26 +184,37 @@ struct DqCtx {
     uint32_t kv_lds[2];
     int key_local[2];
     int part_bytes[2];
+    uint32_t lane_off[2];      // key_local * key_bytes + part_bytes: the lane's source offset in a block
     const _Float16* img_wg;    // this workgroup's 128 rows of the fp16 image tile of key block 0
     int64_t img_blk;           // halves between the tiles of consecutive key blocks
     int64_t key_bytes;
     int last_key;
 };
 
+// Copy sources are a wave-uniform base (the block's first key, the block's image tile) plus
+// a 32-bit lane offset fixed for the loop, so the copies take the scalar-base address form;
+// only the last, partial block clamps its padded keys to the last real one.  The empty asm
+// statements keep the compiler from folding the offsets into 64-bit vector pointers.
 __device__ __forceinline__ void dq_stage(const DqCtx& cx, int n, int wave, int lane) {
     char* lds = reinterpret_cast<char*>(&g_dq[n % DQ_STAGES]);
     const int kb = 32 * n;
+    const int lim = cx.last_key - kb;   // last real key of the block, block-relative
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-        const int rel = min(kb + cx.key_local[t], cx.last_key) - kb;   // padded keys read a real key
-        const char* src = cx.kv_row[t] + static_cast<int64_t>(kb) * cx.key_bytes + rel * cx.key_bytes + cx.part_bytes[t];
-        __builtin_amdgcn_global_load_lds(GPTR(src), LPTR(lds + cx.kv_lds[t]), 16, 0, 0);
+        uint32_t off = cx.lane_off[t];
+        if (lim < 31)
+            off = static_cast<uint32_t>(min(cx.key_local[t], lim) * static_cast<int>(cx.key_bytes) + cx.part_bytes[t]);
+        asm volatile("" : "+v"(off));
+        const char* base = cx.kv_row[t] + static_cast<int64_t>(kb) * cx.key_bytes;
+        __builtin_amdgcn_global_load_lds(GPTR(base + off), LPTR(lds + cx.kv_lds[t]), 16, 0, 0);
     }
-    const char* src = reinterpret_cast<const char*>(cx.img_wg + n * cx.img_blk) + lane * 16;
+    const char* tile = reinterpret_cast<const char*>(cx.img_wg + n * cx.img_blk);
 #pragma unroll
     for (int t = 0; t < DQ_BIAS_PER_WAVE; ++t) {
         const int base = (DQ_BIAS_PER_WAVE * wave + t) * 1024;
-        __builtin_amdgcn_global_load_lds(GPTR(src + base), LPTR(lds + DQ_B_OFF + base), 16, 0, 0);
+        uint32_t off = static_cast<uint32_t>(lane * 16 + base);
+        asm volatile("" : "+v"(off));
+        __builtin_amdgcn_global_load_lds(GPTR(tile + off), LPTR(lds + DQ_B_OFF + base), 16, 0, 0);
     }
 }
 
@@ -263,6 +274,7 @@ __global__ void __launch_bounds__(DQ_THR, 2) bwd_dq_lds(BwdProblem p, const _Flo
             cx.kv_lds[t] = (kv ? DQ_V_OFF : DQ_K_OFF) + line * DQ_LINE_BYTES + t * 1024;
             cx.key_local[t] = 16 * t + (lane >> 2);
             cx.part_bytes[t] = kv_chunk(cx.key_local[t], lane & 3) * 16;
+            cx.lane_off[t] = static_cast<uint32_t>(cx.key_local[t] * cx.key_bytes + cx.part_bytes[t]);
         }
         // the prepass tiles hold pre.cols queries; this block's 128 are rows (jb % sub) * 128 on
         const int sub = pre.cols / IMG_BJ;
@@ -448,29 +460,43 @@ struct DkCtx {
     uint32_t qg_lds[2];
     int q_local[2];
     int part_bytes[2];
+    uint32_t lane_off[2];      // q_local * q_bytes + part_bytes: the lane's source offset in a block
     const _Float16* img_wg;    // this workgroup's fp16 transposed tiles, nqblk consecutive 128 x 32 tiles
-    const char* ls_src;        // nb or delta piece of query block 0 (lanes 0 .. 7)
+    const char* ls_src;        // nb or delta row of the line at query 0 (wave-uniform)
+    uint32_t ls_off;           // this lane's byte offset from it (lanes 0 .. 7)
     uint32_t ls_dst;
     int64_t q_bytes;
     int last_q;
 };
 
+// Copy sources in the scalar-base form, as dq_stage's; only the last, partial block clamps
+// its padded queries to the last real one.
 __device__ __forceinline__ void dk_stage(const DkCtx& cx, int n, int wave, int lane) {
     char* lds = reinterpret_cast<char*>(&g_dk[n % DK_STAGES]);
     const int qb = 32 * n;
+    const int lim = cx.last_q - qb;   // last real query of the block, block-relative
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-        const int rel = min(qb + cx.q_local[t], cx.last_q) - qb;    // padded queries read a real one
-        const char* src = cx.qg_row[t] + static_cast<int64_t>(qb) * cx.q_bytes + rel * cx.q_bytes + cx.part_bytes[t];
-        __builtin_amdgcn_global_load_lds(GPTR(src), LPTR(lds + cx.qg_lds[t]), 16, 0, 0);
+        uint32_t off = cx.lane_off[t];
+        if (lim < 31)
+            off = static_cast<uint32_t>(min(cx.q_local[t], lim) * static_cast<int>(cx.q_bytes) + cx.part_bytes[t]);
+        asm volatile("" : "+v"(off));
+        const char* base = cx.qg_row[t] + static_cast<int64_t>(qb) * cx.q_bytes;
+        __builtin_amdgcn_global_load_lds(GPTR(base + off), LPTR(lds + cx.qg_lds[t]), 16, 0, 0);
     }
-    const char* src = reinterpret_cast<const char*>(cx.img_wg + static_cast<int64_t>(n) * IMG_BJ * 32) + lane * 16;
+    const char* tile = reinterpret_cast<const char*>(cx.img_wg + static_cast<int64_t>(n) * IMG_BJ * 32);
 #pragma unroll
     for (int t = 0; t < DK_BIAS_PER_WAVE; ++t) {
         const int base = (DK_BIAS_PER_WAVE * wave + t) * 1024;
-        __builtin_amdgcn_global_load_lds(GPTR(src + base), LPTR(lds + DK_B_OFF + base), 16, 0, 0);
+        uint32_t off = static_cast<uint32_t>(lane * 16 + base);
+        asm volatile("" : "+v"(off));
+        __builtin_amdgcn_global_load_lds(GPTR(tile + off), LPTR(lds + DK_B_OFF + base), 16, 0, 0);
     }
-    if (lane < 8) __builtin_amdgcn_global_load_lds(GPTR(cx.ls_src + qb * 4), LPTR(lds + cx.ls_dst), 16, 0, 0);
+    if (lane < 8) {
+        uint32_t off = cx.ls_off;
+        asm volatile("" : "+v"(off));
+        __builtin_amdgcn_global_load_lds(GPTR(cx.ls_src + qb * 4 + off), LPTR(lds + cx.ls_dst), 16, 0, 0);
+    }
 }
 
 __global__ void __launch_bounds__(DK_THR, 2) bwd_dkdv_lds(BwdProblem p, const _Float16* imgT16, const int* wide,
@@ -512,12 +538,14 @@ __global__ void __launch_bounds__(DK_THR, 2) bwd_dkdv_lds(BwdProblem p, const _F
             cx.qg_lds[t] = (qg ? DK_G_OFF : DK_Q_OFF) + sline * 2048 + t * 1024;
             cx.q_local[t] = 16 * t + (lane >> 2);
             cx.part_bytes[t] = kv_chunk(cx.q_local[t], lane & 3) * 16;
+            cx.lane_off[t] = static_cast<uint32_t>(cx.q_local[t] * cx.q_bytes + cx.part_bytes[t]);
         }
         cx.img_wg = imgT16 + (static_cast<int64_t>(bh) * n_kb + kb) * nqblk * static_cast<int64_t>(IMG_BJ * 32);
         // nb' of line w (w < DK_R) or -delta of line w - DK_R, 32 floats of the block in lanes 0 .. 7
         int64_t il = i0 + wave % DK_R;
         il = il < I ? il : I - 1;
-        cx.ls_src = reinterpret_cast<const char*>((wave < DK_R ? nbT2 : deltaT) + ((b * I + il) * H + h) * NP + 4 * (lane & 7));
+        cx.ls_src = reinterpret_cast<const char*>((wave < DK_R ? nbT2 : deltaT) + ((b * I + il) * H + h) * NP);
+        cx.ls_off = static_cast<uint32_t>(16 * (lane & 7));
         cx.ls_dst = DK_N_OFF + 128 * wave;
         cx.last_q = static_cast<int>(N - 1);
     }
