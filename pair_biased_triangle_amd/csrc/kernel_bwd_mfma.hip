@@ -307,7 +307,7 @@ __global__ void __launch_bounds__(DQ_THR, 2) bwd_dq_lds(BwdProblem p, const _Flo
         dl[u] = ok ? delta[qi] : 0.0f;
     }
     // LDS byte offsets (stage 0) of this lane's reads: K and V rows (A of S and dP), the
-    // transposed K reads (A of dQ), the bias chunks of its first tile (second tile +4096)
+    // transposed K reads (A of dQ), the bias chunks of its first tile (second tile +2048)
     uint32_t ak[2], at[4], ac[2];
 #pragma unroll
     for (int m = 0; m < 2; ++m) ak[m] = DQ_K_OFF + line * DQ_LINE_BYTES + c * 64 + kv_chunk(c, 2 * m + h2) * 16;
@@ -568,7 +568,7 @@ __global__ void __launch_bounds__(DK_THR, 2) bwd_dkdv_lds(BwdProblem p, const _F
     }
     // LDS byte offsets (stage 0) of this lane's reads: Q and dO rows (A of S and dP), the
     // transposed reads of Q and dO (A of dK, dV), the bias chunks of its first key tile
-    // (second tile +4096), and nb' / -delta of its 16 query rows 8a + 4 h2 + e
+    // (second tile +2048), and nb' / -delta of its 16 query rows 8a + 4 h2 + e
     uint32_t aq[2], at[4], ac[2];
 #pragma unroll
     for (int m = 0; m < 2; ++m) aq[m] = DK_Q_OFF + line * 2048 + c * 64 + kv_chunk(c, 2 * m + h2) * 16;
@@ -597,35 +597,41 @@ __global__ void __launch_bounds__(DK_THR, 2) bwd_dkdv_lds(BwdProblem p, const _F
         const uint32_t st = st0 + static_cast<uint32_t>(n % DK_STAGES) * DK_STAGE_BYTES;
         const bool issue = n + DK_STAGES - 1 < nqblk;
         if (issue) dk_stage(cx, n + DK_STAGES - 1, wave, lane);
-        u32x4 qq[2], gg[2], nn[4], dd[4];
+        u32x4 qq[2], gg[2], nn[4], dd[4], cc[2][2];
         u32x2 tq[4], tg[4];
         asm volatile(
-            "ds_read_b128 %0, %20\n\t"
-            "ds_read_b128 %1, %21\n\t"
-            "ds_read_b128 %2, %20 offset:%c27\n\t"
-            "ds_read_b128 %3, %21 offset:%c27\n\t"
-            "ds_read_b64_tr_b16 %4, %22\n\t"
-            "ds_read_b64_tr_b16 %5, %23\n\t"
-            "ds_read_b64_tr_b16 %6, %24\n\t"
-            "ds_read_b64_tr_b16 %7, %25\n\t"
-            "ds_read_b64_tr_b16 %8, %22 offset:%c27\n\t"
-            "ds_read_b64_tr_b16 %9, %23 offset:%c27\n\t"
-            "ds_read_b64_tr_b16 %10, %24 offset:%c27\n\t"
-            "ds_read_b64_tr_b16 %11, %25 offset:%c27\n\t"
-            "ds_read_b128 %12, %26\n\t"
-            "ds_read_b128 %13, %26 offset:32\n\t"
-            "ds_read_b128 %14, %26 offset:64\n\t"
-            "ds_read_b128 %15, %26 offset:96\n\t"
-            "ds_read_b128 %16, %26 offset:%c28\n\t"
-            "ds_read_b128 %17, %26 offset:%c29\n\t"
-            "ds_read_b128 %18, %26 offset:%c30\n\t"
-            "ds_read_b128 %19, %26 offset:%c31\n\t"
+            "ds_read_b128 %0, %24\n\t"
+            "ds_read_b128 %1, %25\n\t"
+            "ds_read_b128 %2, %24 offset:%c33\n\t"
+            "ds_read_b128 %3, %25 offset:%c33\n\t"
+            "ds_read_b64_tr_b16 %4, %26\n\t"
+            "ds_read_b64_tr_b16 %5, %27\n\t"
+            "ds_read_b64_tr_b16 %6, %28\n\t"
+            "ds_read_b64_tr_b16 %7, %29\n\t"
+            "ds_read_b64_tr_b16 %8, %26 offset:%c33\n\t"
+            "ds_read_b64_tr_b16 %9, %27 offset:%c33\n\t"
+            "ds_read_b64_tr_b16 %10, %28 offset:%c33\n\t"
+            "ds_read_b64_tr_b16 %11, %29 offset:%c33\n\t"
+            "ds_read_b128 %12, %30\n\t"
+            "ds_read_b128 %13, %30 offset:32\n\t"
+            "ds_read_b128 %14, %30 offset:64\n\t"
+            "ds_read_b128 %15, %30 offset:96\n\t"
+            "ds_read_b128 %16, %30 offset:%c34\n\t"
+            "ds_read_b128 %17, %30 offset:%c35\n\t"
+            "ds_read_b128 %18, %30 offset:%c36\n\t"
+            "ds_read_b128 %19, %30 offset:%c37\n\t"
+            "ds_read_b128 %20, %31\n\t"
+            "ds_read_b128 %21, %32\n\t"
+            "ds_read_b128 %22, %31 offset:2048\n\t"
+            "ds_read_b128 %23, %32 offset:2048\n\t"
             "s_waitcnt lgkmcnt(0)"
             : "=&v"(qq[0]), "=&v"(qq[1]), "=&v"(gg[0]), "=&v"(gg[1]), "=&v"(tq[0]), "=&v"(tq[1]), "=&v"(tq[2]),
               "=&v"(tq[3]), "=&v"(tg[0]), "=&v"(tg[1]), "=&v"(tg[2]), "=&v"(tg[3]), "=&v"(nn[0]), "=&v"(nn[1]),
-              "=&v"(nn[2]), "=&v"(nn[3]), "=&v"(dd[0]), "=&v"(dd[1]), "=&v"(dd[2]), "=&v"(dd[3])
+              "=&v"(nn[2]), "=&v"(nn[3]), "=&v"(dd[0]), "=&v"(dd[1]), "=&v"(dd[2]), "=&v"(dd[3]), "=&v"(cc[0][0]),
+              "=&v"(cc[0][1]), "=&v"(cc[1][0]), "=&v"(cc[1][1])
             : "v"(st + aq[0]), "v"(st + aq[1]), "v"(st + at[0]), "v"(st + at[1]), "v"(st + at[2]), "v"(st + at[3]),
-              "v"(st + an), "i"(DK_GQ), "i"(DK_DN), "i"(DK_DN + 32), "i"(DK_DN + 64), "i"(DK_DN + 96));
+              "v"(st + an), "v"(st + ac[0]), "v"(st + ac[1]), "i"(DK_GQ), "i"(DK_DN), "i"(DK_DN + 32), "i"(DK_DN + 64),
+              "i"(DK_DN + 96));
         bf16x8 qT[2], gT[2];
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
@@ -634,13 +640,6 @@ __global__ void __launch_bounds__(DK_THR, 2) bwd_dkdv_lds(BwdProblem p, const _F
         }
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-            u32x4 cc[2];
-            asm volatile(
-                "ds_read_b128 %0, %2\n\t"
-                "ds_read_b128 %1, %3\n\t"
-                "s_waitcnt lgkmcnt(0)"
-                : "=&v"(cc[0]), "=&v"(cc[1])
-                : "v"(st + ac[0] + 2048 * u), "v"(st + ac[1] + 2048 * u));
             // the score accumulator starts from (r_q - lse) sqrt(D) of each query row
             f32x16 S;
 #pragma unroll
@@ -660,7 +659,7 @@ __global__ void __launch_bounds__(DK_THR, 2) bwd_dkdv_lds(BwdProblem p, const _F
             dP = mfma(__builtin_bit_cast(bf16x8, gg[1]), vB[u][1], dP);
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                S[r] = __builtin_amdgcn_exp2f(fmaf(S[r], kScale, half_of(cc[0], cc[1], r)));
+                S[r] = __builtin_amdgcn_exp2f(fmaf(S[r], kScale, half_of(cc[u][0], cc[u][1], r)));
                 dP[r] = S[r] * dP[r];
             }
             bf16x8 p0, p1, s0, s1;
