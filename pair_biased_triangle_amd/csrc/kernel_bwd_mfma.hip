@@ -12,7 +12,8 @@
 //
 // Kernels, each owning the sums it produces (no atomics, deterministic):
 //   bwd_prep_kernel   dout -> bf16 copy (the operand of the dP and dV products),
-//                     delta = dout . out per query, and -delta and nb' = (r_j - lse) sqrt(D)
+//                     delta = dout . out per query from that rounded dout, and -delta and
+//                     nb' = (r_j - lse) sqrt(D)
 //                     transposed to [b, i, h, j] (rows padded to whole 256-query tiles).
 //   bwd_dq_lds        2 lines x 128 queries per workgroup, 32-key blocks streamed through
 //                     an LDS ring (the forward's shape):
@@ -111,12 +112,16 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdProblem p, __bf16* g16
     const int64_t q = (line * p.N + (real ? j : 0)) * p.H + h;
     float dl = 0.0f;
     if (real) {
+        // delta from the same bf16-rounded dout that the dP products use: dS = P (dP - delta)
+        // is then the gradient for that rounded dout, and its rows still sum to zero
+        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
         const f32x4 g = *reinterpret_cast<const f32x4*>(p.dout + q * D + 4 * part);
         const f32x4 o = *reinterpret_cast<const f32x4*>(p.out + q * D + 4 * part);
+        const bf16x4 gb = __builtin_convertvector(g, bf16x4);
+        const f32x4 gr = __builtin_convertvector(gb, f32x4);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dl = fmaf(g[e], o[e], dl);
-        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-        *reinterpret_cast<bf16x4*>(g16 + q * D + 4 * part) = __builtin_convertvector(g, bf16x4);
+        for (int e = 0; e < 4; ++e) dl = fmaf(gr[e], o[e], dl);
+        *reinterpret_cast<bf16x4*>(g16 + q * D + 4 * part) = gb;
     }
     static_assert(PREP_PARTS == 8, "three shuffle steps");
     dl += __shfl_xor(dl, 1);

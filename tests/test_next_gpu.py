@@ -445,3 +445,48 @@ def test_pair_bias_largest_single_pass_size(torch_dev):
     compare_lse(got_lse, ref_lse, TOL["bf16"], f"pair-bias lse N={N}")
     vk = W.bf16_bits_to_f32(w.v.reshape(N, 32)[keys])
     assert np.max(np.abs(got[:, 0] - vk)) < 0.1, "a query's output is not its heavy key's value"
+
+
+@pytest.mark.parametrize("N", [1, 2])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_degenerate_sizes(torch_dev, dtype, N):
+    """One or two tokens through the entry points beyond the forward: attention with pair
+    bias (N = 2 is the smallest the single pass takes, N = 1 goes through the image), the
+    ending node, the ring with one key per step and the backward (with a single key every
+    probability is 1, so the oracle's dq, dk and dbias vanish and dv is dout)."""
+    import pair_biased_triangle_amd as P
+    t = torch_dev
+    say(f"[next] degenerate sizes {dtype} N={N}")
+    w = small(dtype, B=2, I=N, N=N, H=2, D=32, T=N, mask_last=0)
+    q, k, v, bias, mask = dev_inputs(t, w)
+    ref, ref_lse = oracle.tri_attn(w.q, w.k, w.v, w.bias, w.mask, n_key_tiles=N, ending=True)
+    out = P.tri_attn_fwd_ending(q, k, v, bias, mask, n_key_tiles=N)
+    t.cuda.synchronize()
+    compare(out.cpu().numpy(), ref, TOL[dtype], f"ending N={N}")
+    ref, ref_lse = oracle.tri_attn(w.q, w.k, w.v, w.bias, w.mask, n_key_tiles=N)
+    acc, m, l = P.tri_attn_tile_state(q, k, v, bias, mask, key_begin=0, key_end=1)
+    if N == 2:
+        out, lse = P.tri_attn_tile_state_final(q, k, v, bias, mask, key_begin=1, key_end=2, acc=acc, m=m, l=l,
+                                               want_lse=True)
+    else:
+        out, lse = P.tri_attn_state_finalize(acc, m, l)
+    t.cuda.synchronize()
+    compare(out.cpu().numpy(), ref, TOL[dtype], f"ring N={N}")
+    compare_lse(lse.cpu().numpy(), ref_lse, TOL[dtype], f"ring lse N={N}")
+    pb = small(dtype, B=2, I=1, N=N, H=2, D=32, T=1, mask_last=0)
+    q1, k1, v1, b1, _ = dev_inputs(t, pb)
+    shp = (2, N, 2, 32)
+    out, lse = P.pair_bias_attn_fwd(q1.view(shp), k1.view(shp), v1.view(shp), b1, None, want_lse=True)
+    t.cuda.synchronize()
+    pref, pref_lse = oracle.tri_attn(pb.q, pb.k, pb.v, pb.bias, None)
+    compare(out.cpu().numpy(), pref[:, 0], TOL[dtype], f"pair bias N={N}")
+    compare_lse(lse.cpu().numpy(), pref_lse[:, 0], TOL[dtype], f"pair bias lse N={N}")
+    dout = np.random.default_rng(5).standard_normal(w.q.shape).astype(np.float32)
+    fo, fl = oracle.tri_attn(w.q, w.k, w.v, w.bias, w.mask)
+    g = P.tri_attn_bwd(q, k, v, bias, mask, t.from_numpy(fo.astype(np.float32)).cuda(),
+                       t.from_numpy(fl.astype(np.float32)).cuda(), t.from_numpy(dout).cuda())
+    t.cuda.synchronize()
+    gref = oracle.tri_attn_bwd(w.q, w.k, w.v, w.bias, w.mask, dout)
+    bar = 1e-2 if dtype == "bf16" else 1e-4
+    for name, a, r in zip(("dq", "dk", "dv", "dbias"), (x.cpu().numpy() for x in g), gref):
+        compare(a, r, bar * max(1.0, float(np.max(np.abs(r)))), f"backward {name} N={N}")
