@@ -1,9 +1,10 @@
 """GPU parity on seeded random shapes: a fixed list of problems drawn from a seeded
 generator (batch, rows, tokens, heads, head size, dtype, key tiles, bias scale and a
 random mask with some keys dropped and, now and then, every key of a batch element),
-each run through the forward, the log-sum-exp, the ending node (square ones), attention
-with pair bias (one row) and the backward, and compared element by element with the
-fp64 oracle on the same inputs.  Bars as everywhere: 1e-5 (fp32) and 1e-2 (bf16) on
+each run through the forward, the log-sum-exp, the allocation-free forward (when its
+scratch suffices), the ring of T steps, the ending node (square ones), attention with pair
+bias (one row) and the backward, and compared element by element with the fp64 oracle on
+the same inputs.  Bars as everywhere: 1e-5 (fp32) and 1e-2 (bf16) on
 outputs and lse; the backward's as in test_backward_gpu.py (exact statistics).
 """
 import numpy as np
@@ -80,6 +81,26 @@ def test_random_shape(torch_dev, case):
     compare(out.cpu().numpy(), ref, tol, "forward")
     compare(out2.cpu().numpy(), ref, tol, "forward with lse")
     compare_lse(lse.cpu().numpy(), ref_lse, tol, "lse")
+    if P.workspace_bytes(c.B, c.H, c.I, c.N, c.D, T, P.TRI_ATTN_BF16 if c.dtype == "bf16" else P.TRI_ATTN_FP32) <= \
+            P.noalloc_scratch_bytes():
+        on = P.tri_attn_fwd_rows_noalloc(q, k, v, bias, m, n_key_tiles=T)
+        t.cuda.synchronize()
+        compare(on.cpu().numpy(), ref, tol, "forward without allocation")
+    # the ring: T tile states folded by updates, the last step finalising
+    bounds = [s * (c.N // T) + min(s, c.N % T) for s in range(T + 1)]
+    if T == 1:
+        acc, ms, ls = P.tri_attn_tile_state(q, k, v, bias, m, key_begin=0, key_end=c.N)
+        orng, lrng = P.tri_attn_state_finalize(acc, ms, ls)
+    else:
+        acc, ms, ls = P.tri_attn_tile_state(q, k, v, bias, m, key_begin=bounds[0], key_end=bounds[1])
+        for s in range(1, T - 1):
+            P.tri_attn_tile_state_update(q, k, v, bias, m, key_begin=bounds[s], key_end=bounds[s + 1], acc=acc, m=ms,
+                                         l=ls)
+        orng, lrng = P.tri_attn_tile_state_final(q, k, v, bias, m, key_begin=bounds[T - 1], key_end=bounds[T],
+                                                 acc=acc, m=ms, l=ls, want_lse=True)
+    t.cuda.synchronize()
+    compare(orng.cpu().numpy(), ref, tol, "ring")
+    compare_lse(lrng.cpu().numpy(), ref_lse, tol, "ring lse")
     if c.I == c.N:
         oe = P.tri_attn_fwd_ending(q, k, v, bias, m, n_key_tiles=T)
         t.cuda.synchronize()
