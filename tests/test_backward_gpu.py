@@ -182,3 +182,25 @@ def test_soft_mask_and_shifted_bias(torch_dev, deep):
     ref = oracle.tri_attn_bwd(w.q, w.k, w.v, w.bias, mask, dout)
     for n, a, r in zip(NAMES, (x.cpu().numpy() for x in g), ref):
         compare_rel(a, r, 1e-2, f"soft mask{' deep' if deep else ''} {n} bf16")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_dbias_rows_sum_to_zero(torch_dev, dtype):
+    """sum_k ds_k = sum_k p_k (dp_k - delta) = 0 when delta = dout . out and out = sum_k p_k v_k.
+    Fed the oracle's exact statistics, the matrix-core path forms delta from the same
+    bf16-rounded dout as its dP products, so each dbias row sums to zero up to fp32
+    rounding, far inside the gradient's own bar: |row sum| <= 1e-4 of the row's sum of
+    magnitudes (the fp32 path likewise)."""
+    import pair_biased_triangle_amd as P
+    t = torch_dev
+    w, dout = case(dtype, 8, 300, 32, seed=95, mask_last=7)
+    out, lse = oracle.tri_attn(w.q, w.k, w.v, w.bias, w.mask)
+    say(f"[bwd] dbias row sums, {dtype}")
+    q, k, v, b, m = (to_dev(t, x) for x in (w.q, w.k, w.v, w.bias, w.mask))
+    g = P.tri_attn_bwd(q, k, v, b, m, t.from_numpy(out.astype(np.float32)).cuda(),
+                       t.from_numpy(lse.astype(np.float32)).cuda(), t.from_numpy(dout).cuda())
+    t.cuda.synchronize()
+    db = g[3].cpu().numpy().astype(np.float64)
+    worst = float(np.max(np.abs(db.sum(axis=-1)) / np.maximum(np.abs(db).sum(axis=-1), 1e-30)))
+    say(f"  max |row sum| / sum |.| = {worst:.3e} (bar 1e-4)")
+    assert worst <= 1e-4
