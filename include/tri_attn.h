@@ -311,10 +311,12 @@ int tri_attn_state_finalize(const float *acc, const float *m, const float *l,
  *   (tri_attn_fwd_lse);  dout [B, I, N, H, D] binary32;
  *   dq, dk, dv [B, I, N, H, D] and dbias [B, H, N, N]: binary32 results, overwritten.
  * bf16 inputs with D == 32 and out, dout, dq, dk, dv 16-byte aligned run on matrix
- * cores: dout, p and ds are rounded to bf16 as product operands, sums are fp32, and a
- * workspace (bias images, bf16 dout, per-query statistics; tri_attn_call_workspace_bytes
- * with TRI_ATTN_CALL_BWD) comes from the library pool as described above, or from the
- * caller through tri_attn_bwd_ws.  Every other case computes in fp32, any D <= 64, with no workspace.
+ * cores: dout, p and ds are rounded to bf16 as product operands (delta from the same
+ * rounded dout), sums are fp32, and a workspace (bias images, bf16 dout and head-major
+ * copies of q, k, v, [B, H, I, N, D], per-query statistics: about 4 B H N^2 + 8 B I N H D
+ * bytes; tri_attn_call_workspace_bytes with TRI_ATTN_CALL_BWD)
+ * comes from the library pool as described above, or from the caller through
+ * tri_attn_bwd_ws.  Every other case computes in fp32, any D <= 64, with no workspace.
  * Both are deterministic (every sum is taken by one thread in a fixed order, no atomics).
  * A query with lse = -inf contributes nothing.  q, k, v, bias 16-byte aligned, the other
  * pointers 4-byte aligned; no result may overlap an input or another result.  Same error

@@ -110,6 +110,7 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdProblem p, __bf16* g16
     const int64_t qh = t / PREP_PARTS, h = qh % p.H, lj = qh / p.H, j = lj % NP, line = lj / NP;
     const bool real = j < p.N;
     const int64_t q = (line * p.N + (real ? j : 0)) * p.H + h;
+    const int64_t qhm = ((line / p.I * p.H + h) * p.I + line % p.I) * p.N + j;   // head-major position of g16
     float dl = 0.0f;
     if (real) {
         // delta from the same bf16-rounded dout that the dP products use: dS = P (dP - delta)
@@ -121,7 +122,7 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdProblem p, __bf16* g16
         const f32x4 gr = __builtin_convertvector(gb, f32x4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) dl = fmaf(gr[e], o[e], dl);
-        *reinterpret_cast<bf16x4*>(g16 + q * D + 4 * part) = gb;
+        *reinterpret_cast<bf16x4*>(g16 + qhm * D + 4 * part) = gb;
     }
     static_assert(PREP_PARTS == 8, "three shuffle steps");
     dl += __shfl_xor(dl, 1);
@@ -137,6 +138,26 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdProblem p, __bf16* g16
         const int64_t b = line / p.I;
         nbT2[tt] = lse == -INFINITY ? -INFINITY : (ref16[(b * p.H + h) * nqp16 + j] - lse) * kSqrtD;
     }
+}
+
+// q, k, v copied head-major, [B, H, I, N, D]: the streaming kernels then copy each head's
+// rows as contiguous 64-byte runs instead of 64 bytes out of every 256 (the other heads'
+// bytes share their lines).  Thread t moves 16 bytes: part t % 4 of head (t / 4) % H of
+// position t / (4 H), so a wave reads 1 KB of contiguous positions and writes 256
+// contiguous bytes per head; grid.y picks q, k or v.  (5.6 GB moved at N = 2700, about
+// 1.9 ms: near the bandwidth the other streaming kernels see.)
+__global__ void __launch_bounds__(256) bwd_headmajor_kernel(BwdProblem p, __bf16* qh, __bf16* kh, __bf16* vh) {
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    const int64_t total = p.B * p.I * p.N * p.H * 4;
+    if (t >= total) return;
+    const int part = static_cast<int>(t & 3);
+    const int64_t h = (t >> 2) % p.H, pos = (t >> 2) / p.H;   // pos = (b * I + i) * N + j
+    const int64_t IN = p.I * p.N, b = pos / IN, rem = pos - b * IN;
+    const __bf16* src = blockIdx.y == 0 ? static_cast<const __bf16*>(p.q) : blockIdx.y == 1 ? static_cast<const __bf16*>(p.k)
+                                                                                             : static_cast<const __bf16*>(p.v);
+    __bf16* dst = blockIdx.y == 0 ? qh : blockIdx.y == 1 ? kh : vh;
+    *reinterpret_cast<u32x4*>(dst + ((b * p.H + h) * IN + rem) * D + 8 * part) =
+        *reinterpret_cast<const u32x4*>(src + (pos * p.H + h) * D + 8 * part);
 }
 
 #define GPTR(p) ((const __attribute__((address_space(1))) void*)(p))
@@ -240,6 +261,7 @@ __device__ __forceinline__ bool any_wide(const int* wide, int64_t bh, int n) {
 
 __global__ void __launch_bounds__(DQ_THR, 2) bwd_dq_lds(BwdProblem p, const _Float16* img16, const float* ref16,
                                                      Prepass16 pre, const int* wide, const __bf16* g16,
+                                                     const __bf16* kh, const __bf16* vh,
                                                      const float* delta, int n_jb, int n_rg, int nblk, int total) {
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -267,15 +289,14 @@ __global__ void __launch_bounds__(DQ_THR, 2) bwd_dq_lds(BwdProblem p, const _Flo
 
     DqCtx cx;
     {
-        cx.key_bytes = HD * 2;
+        cx.key_bytes = D * 2;   // head-major copies: one head's keys 64 bytes apart
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             // piece 2 w + t: line w / 2, K (w even) or V (w odd), keys 16 t .. +15
             const int line = wave >> 1, kv = wave & 1;
             int64_t i = i0 + line;
             i = i < I ? i : I - 1;                       // padded lines read a real line (never stored)
-            cx.kv_row[t] = reinterpret_cast<const char*>(static_cast<const __bf16*>(kv ? p.v : p.k) +
-                                                         ((b * I + i) * N) * HD + h * D);
+            cx.kv_row[t] = reinterpret_cast<const char*>((kv ? vh : kh) + (((b * H + h) * I + i) * N) * D);
             cx.kv_lds[t] = (kv ? DQ_V_OFF : DQ_K_OFF) + line * DQ_LINE_BYTES + t * 1024;
             cx.key_local[t] = 16 * t + (lane >> 2);
             cx.part_bytes[t] = kv_chunk(cx.key_local[t], lane & 3) * 16;
@@ -303,7 +324,7 @@ __global__ void __launch_bounds__(DQ_THR, 2) bwd_dq_lds(BwdProblem p, const _Flo
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
             qB[u][m] = frag(q, qo + 16 * m + 8 * h2, ok);
-            gB[u][m] = frag(g16, qo + 16 * m + 8 * h2, ok);
+            gB[u][m] = frag(g16, (((b * H + h) * I + i) * N + j) * D + 16 * m + 8 * h2, ok);
         }
         const int64_t qi = ((b * I + i) * N + j) * H + h;
         const float lse = ok ? p.lse[qi] : -INFINITY;
@@ -505,7 +526,8 @@ __device__ __forceinline__ void dk_stage(const DkCtx& cx, int n, int wave, int l
 }
 
 __global__ void __launch_bounds__(DK_THR, 2) bwd_dkdv_lds(BwdProblem p, const _Float16* imgT16, const int* wide,
-                                                       int n_wide, const __bf16* g16, const float* nbT2,
+                                                       int n_wide, const __bf16* g16, const __bf16* qh,
+                                                       const float* nbT2,
                                                        const float* deltaT, int n_kb, int n_rg, int nqblk, int64_t NP,
                                                        int total) {
     const int tid = threadIdx.x;
@@ -532,14 +554,13 @@ __global__ void __launch_bounds__(DK_THR, 2) bwd_dkdv_lds(BwdProblem p, const _F
 
     DkCtx cx;
     {
-        cx.q_bytes = HD * 2;
+        cx.q_bytes = D * 2;   // head-major copies: one head's queries 64 bytes apart
         const int sline = wave >> 1, qg = wave & 1;   // pieces of wave w: line w / 2, Q (w even) or dO, both halves
         int64_t i = i0 + sline;
         i = i < I ? i : I - 1;                         // padded lines read a real line (never stored)
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            cx.qg_row[t] = reinterpret_cast<const char*>((qg ? g16 : static_cast<const __bf16*>(p.q)) +
-                                                         ((b * I + i) * N) * HD + h * D);
+            cx.qg_row[t] = reinterpret_cast<const char*>((qg ? g16 : qh) + (((b * H + h) * I + i) * N) * D);
             cx.qg_lds[t] = (qg ? DK_G_OFF : DK_Q_OFF) + sline * 2048 + t * 1024;
             cx.q_local[t] = 16 * t + (lane >> 2);
             cx.part_bytes[t] = kv_chunk(cx.q_local[t], lane & 3) * 16;
@@ -905,6 +926,7 @@ __device__ __forceinline__ void db_row(const DbOps& o, f32x16 (&acc)[4]) {
 
 __global__ void __launch_bounds__(DB_THR, TRI_ATTN_DB_WG_PER_CU) bwd_dbias_lds(BwdProblem p, const float* ref16, int64_t nqp16,
                                                         const int* wide, int n_wide, const __bf16* g16,
+                                                        const __bf16* qh, const __bf16* kh, const __bf16* vh,
                                                         const float* nbT2, const float* deltaT, int64_t NP, int n_tq,
                                                         int n_tk, int total) {
     const int tid = threadIdx.x;
@@ -936,8 +958,7 @@ __global__ void __launch_bounds__(DB_THR, TRI_ATTN_DB_WG_PER_CU) bwd_dbias_lds(B
         // piece pi = DB_PIECES w + t: Q pieces first, then dO, K, V; piece rows 16 (local) ..
         // +15; lane l carries row l / 4, 16-byte slot l % 4, which holds logical part
         // kv_chunk(row, slot)
-        const __bf16* tens[4] = {static_cast<const __bf16*>(p.q), g16, static_cast<const __bf16*>(p.k),
-                                 static_cast<const __bf16*>(p.v)};
+        const __bf16* tens[4] = {qh, g16, kh, vh};   // head-major copies
         const uint32_t offs[4] = {DB_Q_OFF, DB_G_OFF, DB_K_OFF, DB_V_OFF};
 #pragma unroll
         for (int t = 0; t < DB_PIECES; ++t) {
@@ -945,14 +966,14 @@ __global__ void __launch_bounds__(DB_THR, TRI_ATTN_DB_WG_PER_CU) bwd_dbias_lds(B
             const int ten = pi < DB_PQ ? 0 : pi < 2 * DB_PQ ? 1 : pi < 2 * DB_PQ + DB_PK ? 2 : 3;
             const int local = pi - (ten < 2 ? ten * DB_PQ : 2 * DB_PQ + (ten - 2) * DB_PK);
             cx.first[t] = (ten < 2 ? j0 : k0) + 16 * local;
-            cx.src[t] = reinterpret_cast<const char*>(tens[ten] + (b * p.I * N + cx.first[t]) * HD + h * D);
+            cx.src[t] = reinterpret_cast<const char*>(tens[ten] + ((b * H + h) * p.I * N + cx.first[t]) * D);
             cx.dst[t] = offs[ten] + local * 1024;
         }
         // the swizzle depends on bits 1, 2 of the row only, so it is the same in every piece
-        cx.off = static_cast<uint32_t>((lane >> 2) * HD * 2 + kv_chunk(lane >> 2, lane & 3) * 16);
+        cx.off = static_cast<uint32_t>((lane >> 2) * D * 2 + kv_chunk(lane >> 2, lane & 3) * 16);
         cx.N = N;
-        cx.pos_bytes = HD * 2;
-        cx.row_step = N * HD * 2;
+        cx.pos_bytes = D * 2;
+        cx.row_step = N * D * 2;
         // nb' / -delta: wave w < DB_NQP copies nb' of queries 64 w .. +63, the others -delta
         const float* ls = wave < DB_NQP ? nbT2 : deltaT;
         cx.ls_src = reinterpret_cast<const char*>(ls + (b * p.I * H + h) * NP + j0 + 64 * (wave % DB_NQP));
@@ -1057,7 +1078,7 @@ struct BwdLayout {
     Problem fwd;            // the image problem: the bias and mask over all keys
     Prepass16 pre;          // the forward's prepass: fp16 image and r_j (dq, dk/dv)
     int64_t NP, nq;
-    size_t pre16, imgT16, g16, delta, nbT2, deltaT, total;   // byte offsets / total
+    size_t pre16, imgT16, g16, qh, kh, vh, delta, nbT2, deltaT, total;   // byte offsets / total
 };
 
 BwdLayout bwd_layout(const BwdProblem& p) {
@@ -1072,7 +1093,10 @@ BwdLayout bwd_layout(const BwdProblem& p) {
     L.pre16 = 0;
     L.imgT16 = up(L.pre16 + L.pre.bytes);
     L.g16 = up(L.imgT16 + static_cast<size_t>(p.B * p.H * n_kt * nqb) * IMG_BJ * 32 * 2);
-    L.delta = up(L.g16 + static_cast<size_t>(L.nq) * D * 2);
+    L.qh = up(L.g16 + static_cast<size_t>(L.nq) * D * 2);
+    L.kh = up(L.qh + static_cast<size_t>(L.nq) * D * 2);
+    L.vh = up(L.kh + static_cast<size_t>(L.nq) * D * 2);
+    L.delta = up(L.vh + static_cast<size_t>(L.nq) * D * 2);
     L.nbT2 = up(L.delta + static_cast<size_t>(L.nq) * 4);
     L.deltaT = L.nbT2 + per_line;
     L.total = L.deltaT + per_line;
@@ -1092,6 +1116,9 @@ hipError_t launch_backward_mfma(const BwdProblem& p, void* workspace, hipStream_
     const int* wide = reinterpret_cast<const int*>(ws + Ly.pre16 + Ly.pre.wide_off);
     _Float16* imgT16 = reinterpret_cast<_Float16*>(ws + Ly.imgT16);
     __bf16* g16 = reinterpret_cast<__bf16*>(ws + Ly.g16);
+    __bf16* qh = reinterpret_cast<__bf16*>(ws + Ly.qh);
+    __bf16* kh = reinterpret_cast<__bf16*>(ws + Ly.kh);
+    __bf16* vh = reinterpret_cast<__bf16*>(ws + Ly.vh);
     float* delta = reinterpret_cast<float*>(ws + Ly.delta);
     float* nbT2 = reinterpret_cast<float*>(ws + Ly.nbT2);
     float* deltaT = reinterpret_cast<float*>(ws + Ly.deltaT);
@@ -1109,12 +1136,15 @@ hipError_t launch_backward_mfma(const BwdProblem& p, void* workspace, hipStream_
     hipLaunchKernelGGL(bwd_prep_kernel, dim3(static_cast<unsigned>((n_prep + 255) / 256)), dim3(256), 0, stream, p, g16,
                        delta, deltaT, Ly.NP, ref16, Ly.pre.nqp, nbT2);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int64_t n_hm = (p.B * p.I * p.N * p.H * 4 + 255) / 256;   // within n_prep's bound checked above
+    hipLaunchKernelGGL(bwd_headmajor_kernel, dim3(static_cast<unsigned>(n_hm), 3), dim3(256), 0, stream, p, qh, kh, vh);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     {
         const int64_t n_rg = (p.I + DQ_R - 1) / DQ_R;
         const int64_t total = n_jb * n_rg * p.B * p.H;
         if (total > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
         hipLaunchKernelGGL(bwd_dq_lds, dim3(static_cast<unsigned>(total)), dim3(DQ_THR), 0, stream, p, img16, ref16,
-                           Ly.pre, wide, g16, delta, static_cast<int>(n_jb), static_cast<int>(n_rg),
+                           Ly.pre, wide, g16, kh, vh, delta, static_cast<int>(n_jb), static_cast<int>(n_rg),
                            static_cast<int>(nblk), static_cast<int>(total));
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
@@ -1123,7 +1153,7 @@ hipError_t launch_backward_mfma(const BwdProblem& p, void* workspace, hipStream_
         const int64_t total = n_jb * n_rg * p.B * p.H;
         if (total > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
         hipLaunchKernelGGL(bwd_dkdv_lds, dim3(static_cast<unsigned>(total)), dim3(DK_THR), 0, stream, p, imgT16, wide,
-                           static_cast<int>(Ly.pre.n_jb), g16, nbT2, deltaT, static_cast<int>(n_jb),
+                           static_cast<int>(Ly.pre.n_jb), g16, qh, nbT2, deltaT, static_cast<int>(n_jb),
                            static_cast<int>(n_rg), static_cast<int>(nblk), Ly.NP, static_cast<int>(total));
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
@@ -1133,7 +1163,7 @@ hipError_t launch_backward_mfma(const BwdProblem& p, void* workspace, hipStream_
     const int64_t total = n_tq * n_tk * p.B * p.H;
     if (total > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(bwd_dbias_lds, dim3(static_cast<unsigned>(total)), dim3(DB_THR), 0, stream, p, ref16, Ly.pre.nqp,
-                       wide, static_cast<int>(Ly.pre.n_jb), g16, nbT2, deltaT, Ly.NP, static_cast<int>(n_tq),
+                       wide, static_cast<int>(Ly.pre.n_jb), g16, qh, kh, vh, nbT2, deltaT, Ly.NP, static_cast<int>(n_tq),
                        static_cast<int>(n_tk), static_cast<int>(total));
     return hipGetLastError();
 }
