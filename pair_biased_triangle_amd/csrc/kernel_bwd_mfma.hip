@@ -11,10 +11,13 @@
 // multiplies the sums by 2^((bias + mask - r_j) log2(e)) once, from the raw bias.
 //
 // Kernels, each owning the sums it produces (no atomics, deterministic):
-//   bwd_prep_kernel   dout -> bf16 copy (the operand of the dP and dV products),
-//                     delta = dout . out per query from that rounded dout, and -delta and
-//                     nb' = (r_j - lse) sqrt(D)
+//   bwd_prep_kernel   dout -> bf16 copy, head-major [B, H, I, N, D] (the operand of the dP
+//                     and dV products), delta = dout . out per query from that rounded
+//                     dout, and -delta and nb' = (r_j - lse) sqrt(D)
 //                     transposed to [b, i, h, j] (rows padded to whole 256-query tiles).
+//   bwd_headmajor_kernel
+//                     q, k, v -> head-major copies [B, H, I, N, D], which the three
+//                     streaming kernels below copy into LDS (each head's rows contiguous).
 //   bwd_dq_lds        2 lines x 128 queries per workgroup, 32-key blocks streamed through
 //                     an LDS ring (the forward's shape):
 //                       S^T = K Q^T + nb',  dP^T = V dO^T - delta,  dS^T = P^T dP^T,
