@@ -951,7 +951,7 @@ __global__ void __launch_bounds__(DB_THR, TRI_ATTN_DB_WG_PER_CU) bwd_dbias_lds(B
     const int o2 = o - tile * nr * DB_TILE_K;
     const int jt = strip * DB_TILE_J + o2 / nk;
     const int kt = tile * DB_TILE_K + o2 % nk;
-    const int64_t N = p.N, H = p.H, HD = H * D;
+    const int64_t N = p.N, H = p.H;
     const int64_t b = bh / H, h = bh % H;
     const int64_t j0 = static_cast<int64_t>(jt) * DB_Q, k0 = static_cast<int64_t>(kt) * DB_K;
     if (any_wide(wide, bh, n_wide)) return;   // left to the fp32 kernel (whole workgroup)
