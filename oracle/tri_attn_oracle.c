@@ -377,3 +377,88 @@ int oracle_tri_attn_bwd(const void *q, const void *k, const void *v, const void 
     }
     return failed ? ORACLE_ERR_NOMEM : ORACLE_OK;
 }
+
+/*
+ * dbias of selected query columns: dbias[b, h, j, k] = sum over every row i of ds_k for the
+ * query (b, i, j, h), with p, dp, delta and ds as written above oracle_tri_attn_bwd, for j
+ * in cols[0 .. n_cols-1] only (so that a column sum over all N rows of a large problem
+ * costs O(I N D) per column instead of the whole backward).  out [B, H, n_cols, N] doubles,
+ * overwritten.  One OpenMP task per (b, h, column); each sum over rows runs in one thread
+ * in row order.  A row whose query has no finite score contributes nothing.
+ */
+int oracle_tri_attn_dbias_cols(const void *q, const void *k, const void *v, const void *bias,
+                               const float *mask, const float *dout, int dtype,
+                               int64_t B, int64_t H, int64_t I, int64_t N, int64_t D,
+                               const int64_t *cols, int64_t n_cols, double *out)
+{
+    if (!q || !k || !v || !bias || !dout || !cols || !out || n_cols < 1)
+        return ORACLE_ERR_ARG;
+    if (B < 1 || H < 1 || I < 1 || N < 1 || D < 1 || I > N)
+        return ORACLE_ERR_ARG;
+    if (dtype != ORACLE_DTYPE_FP32 && dtype != ORACLE_DTYPE_BF16)
+        return ORACLE_ERR_ARG;
+    for (int64_t c = 0; c < n_cols; ++c)
+        if (cols[c] < 0 || cols[c] >= N)
+            return ORACLE_ERR_ARG;
+    const double inv_sqrt_d = 1.0 / sqrt((double)D);
+    for (int64_t e = 0; e < B * H * n_cols * N; ++e)
+        out[e] = 0.0;
+    int failed = 0;
+
+#pragma omp parallel
+    {
+        double *p = (double *)malloc((size_t)N * sizeof(double));
+        double *dp = (double *)malloc((size_t)N * sizeof(double));
+        const int ok = p && dp;
+        if (!ok) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t t = 0; t < B * H * n_cols; ++t) {
+            if (!ok)
+                continue;
+            const int64_t c = t % n_cols, bh = t / n_cols, b = bh / H, h = bh % H, j = cols[c];
+            double *row = out + t * N;
+            for (int64_t i = 0; i < I; ++i) {
+                const int64_t line = (b * I + i) * N;     /* flat (b, i, j=0) */
+                const int64_t q_off = ((line + j) * H + h) * D;
+                double mx = -INFINITY;
+                for (int64_t kk = 0; kk < N; ++kk) {
+                    const int64_t k_off = ((line + kk) * H + h) * D;
+                    double dot = 0.0;
+                    for (int64_t d = 0; d < D; ++d)
+                        dot += widen(q, q_off + d, dtype) * widen(k, k_off + d, dtype);
+                    double sc = dot * inv_sqrt_d + widen(bias, ((b * H + h) * N + j) * N + kk, dtype);
+                    if (mask)
+                        sc += (double)mask[b * N + kk];
+                    p[kk] = sc;
+                    if (sc > mx)
+                        mx = sc;
+                }
+                if (mx == -INFINITY)
+                    continue;
+                double l = 0.0;
+                for (int64_t kk = 0; kk < N; ++kk) {
+                    p[kk] = exp(p[kk] - mx);
+                    l += p[kk];
+                }
+                double delta = 0.0;
+                for (int64_t kk = 0; kk < N; ++kk) {
+                    p[kk] /= l;
+                    const int64_t v_off = ((line + kk) * H + h) * D;
+                    double dot = 0.0;
+                    for (int64_t d = 0; d < D; ++d)
+                        dot += (double)dout[q_off + d] * widen(v, v_off + d, dtype);
+                    dp[kk] = dot;
+                    delta += p[kk] * dot;
+                }
+                for (int64_t kk = 0; kk < N; ++kk)
+                    row[kk] += p[kk] * (dp[kk] - delta);
+            }
+        }
+        free(p);
+        free(dp);
+    }
+    return failed ? ORACLE_ERR_NOMEM : ORACLE_OK;
+}

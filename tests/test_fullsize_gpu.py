@@ -7,7 +7,8 @@
   the bar is the kernels' own (1e-2 x max(1, max|oracle|)); the other lines keep the GPU
   forward's.  dbias sums over every line, so it is checked through a row-share call:
   the same 16 lines gathered into I = 16 (tri_attn_bwd on a row share returns the dbias
-  of its rows), against the oracle's dbias of those lines.
+  of its rows), against the oracle's dbias of those lines; and the full call's dbias,
+  summed over all 2700 rows, on eight query columns against the oracle's column form.
 * The split-tile ring at N = 2700, T = 8 (`bench.py --pass ring`): the first step's
   state, six updates folded into it and the final step, on sampled query rows.
 """
@@ -160,6 +161,30 @@ def test_backward_n2700_dbias_of_all_rows(torch_dev, n2700):
     say(f"  dbias(all rows) - dbias(rows < 1350) - dbias(rows >= 1350): max |diff| = {diff:.3e} (bar {1e-4 * scale:.3e})")
     assert diff <= 1e-4 * scale
 
+
+
+@pytest.mark.timeout(900)
+def test_backward_n2700_dbias_columns_over_all_rows(torch_dev, n2700):
+    """dbias of the benchmark's full call (every one of the 2700 rows summed, from the GPU
+    forward's out and lse) against the oracle's column form (dS summed over all rows in
+    fp64, pinned to autograd) on eight query columns j: the first, tile and row-share
+    edges, the last kept key's column and the last one, all heads and keys.  Bar: the
+    backward's own, 1e-2 x max(1, max|oracle|)."""
+    import pair_biased_triangle_amd as P
+    torch = torch_dev
+    w, (q, k, v, bias, mask) = n2700
+    cfg = w.cfg
+    cols = [0, 1, 255, 256, 1350, 2047, cfg.N - cfg.mask_last - 1, cfg.N - 1]
+    say(f"[full] backward N=2700: dbias over all rows on columns {cols}")
+    out, lse = P.tri_attn_fwd_lse(q, k, v, bias, mask, n_key_tiles=cfg.n_key_tiles)
+    dout = torch.randn(q.shape, dtype=torch.float32, device="cuda", generator=torch.Generator("cuda").manual_seed(11))
+    dbias = P.tri_attn_bwd(q, k, v, bias, mask, out, lse, dout)[3]
+    torch.cuda.synchronize()
+    got = dbias[:, :, cols].cpu().numpy()
+    del dbias, out, lse
+    ref = oracle.tri_attn_dbias_cols(w.q, w.k, w.v, w.bias, w.mask, dout.cpu().numpy(), cols)
+    compare_rel(got, ref, 1e-2, "dbias N=2700, 8 columns summed over 2700 rows")
+    assert np.all(got[..., cfg.N - cfg.mask_last:] == 0), "a masked key got a bias gradient"
 
 
 N4200 = (4200, 4, 32, 8)          # N = I, H, D, key tiles

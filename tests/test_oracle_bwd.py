@@ -104,3 +104,24 @@ def test_fully_masked_row_has_no_gradient(oracle_mod):
     dout = rng.standard_normal(q.shape).astype(np.float32)
     for g in oracle_mod.tri_attn_bwd(q, k, v, bias, mask, dout):
         assert np.all(g == 0)
+
+
+@pytest.mark.parametrize("shape,masked,cols", [(dict(B=1, I=4, N=11, H=2, D=8), (), (0, 5, 10)),
+                                               (dict(B=2, I=5, N=17, H=3, D=16), (0, 9, 16), (16, 3, 3, 8))])
+def test_dbias_columns_match_autograd(oracle_mod, shape, masked, cols):
+    """The column form of dbias (summed over every row) against torch autograd, and a
+    batch element whose keys are all masked contributes nothing."""
+    rng = np.random.default_rng(93)
+    q, k, v, bias, mask = rand_case(rng, masked=masked, sigma_b=2.0, **shape)
+    if shape["B"] > 1:
+        mask = np.zeros((shape["B"], shape["N"]), dtype=np.float32) if mask is None else mask.copy()
+        mask[1, :] = -np.inf
+    dout = rng.standard_normal(q.shape).astype(np.float32)
+    got = oracle_mod.tri_attn_dbias_cols(q, k, v, bias, mask, dout, list(cols))
+    if shape["B"] > 1:
+        assert np.all(got[1] == 0)
+        ref = autograd_reference(q[:1], k[:1], v[:1], bias[:1], mask[:1], dout[:1])[3]
+        got = got[:1]
+    else:
+        ref = autograd_reference(q, k, v, bias, mask, dout)[3]
+    np.testing.assert_allclose(got, ref[:, :, list(cols)], rtol=0, atol=1e-12)

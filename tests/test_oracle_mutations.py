@@ -68,6 +68,10 @@ MUTATIONS = {
                               "dv[kv_off + d] += ds * (double)dout[q_off + d];"),
     "bwd_dbias_not_summed_over_rows": ("dbias[((b * H + h) * N + j) * N + kk] += ds;",
                                        "dbias[((b * H + h) * N + j) * N + kk] = ds;"),
+    # dbias of selected query columns
+    "dbias_cols_delta_dropped": ("row[kk] += p[kk] * (dp[kk] - delta);", "row[kk] += p[kk] * dp[kk];"),
+    "dbias_cols_last_row_only": ("row[kk] += p[kk] * (dp[kk] - delta);", "row[kk] = p[kk] * (dp[kk] - delta);"),
+    "dbias_cols_wrong_column": ("h = bh % H, j = cols[c];", "h = bh % H, j = cols[(c + 1) % n_cols];"),
 }
 
 
@@ -161,8 +165,12 @@ def battery(lib_path) -> list[str]:
         from tests.test_oracle_bwd import autograd_reference
         dout = rng.standard_normal(q.shape).astype(np.float32)
         got = oracle.tri_attn_bwd(q, k, v, bias, mask, dout, lib_path=lib_path)
-        for g, r in zip(got, autograd_reference(q, k, v, bias, mask, dout)):
+        ref = autograd_reference(q, k, v, bias, mask, dout)
+        for g, r in zip(got, ref):
             np.testing.assert_allclose(g, r, rtol=0, atol=1e-12)
+        cols = [0, 7, 22]
+        got = oracle.tri_attn_dbias_cols(q, k, v, bias, mask, dout, cols, lib_path=lib_path)
+        np.testing.assert_allclose(got, ref[3][:, :, cols], rtol=0, atol=1e-12)
 
     with np.errstate(all="ignore"):
         for name, fn in [("sdpa", sdpa), ("tiles", tiles), ("shifts", shifts),
