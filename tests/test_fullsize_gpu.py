@@ -11,6 +11,9 @@
   summed over all 2700 rows, on eight query columns against the oracle's column form.
 * The split-tile ring at N = 2700, T = 8 (`bench.py --pass ring`): the first step's
   state, six updates folded into it and the final step, on sampled query rows.
+* One rank's share of a ring over a large assembly (ring_share_n4096_i1024: 1,024 rows of
+  N = 4,096): the eight-step ring on sampled rows, and the backward (dq, dk, dv of four
+  lines, dbias of the share on six query columns).
 """
 import numpy as np
 import pytest
@@ -185,6 +188,81 @@ def test_backward_n2700_dbias_columns_over_all_rows(torch_dev, n2700):
     ref = oracle.tri_attn_dbias_cols(w.q, w.k, w.v, w.bias, w.mask, dout.cpu().numpy(), cols)
     compare_rel(got, ref, 1e-2, "dbias N=2700, 8 columns summed over 2700 rows")
     assert np.all(got[..., cfg.N - cfg.mask_last:] == 0), "a masked key got a bias gradient"
+
+
+@pytest.fixture(scope="module")
+def share4096(torch_dev):
+    """ring_share_n4096_i1024 inputs (one rank's 1,024 rows of N = 4,096) on host and device."""
+    w = W.make_inputs("ring_share_n4096_i1024")
+    dev = tuple(to_dev(torch_dev, x) for x in (w.q, w.k, w.v, w.bias, w.mask))
+    return w, dev
+
+
+@pytest.mark.timeout(600)
+def test_ring_share_n4096_t8_sampled(torch_dev, share4096):
+    """The rank's share of a ring as the workload describes it: its 1,024 rows against
+    all 4,096 keys in 8 key tiles folded by the ring-step entry points (first step, six
+    updates, final step), on sampled rows against the oracle's tiled forward."""
+    import pair_biased_triangle_amd as P
+    torch = torch_dev
+    w, (q, k, v, bias, mask) = share4096
+    cfg = w.cfg
+    B, I, N, H, D, T = cfg.B, cfg.I, cfg.N, cfg.H, cfg.D, cfg.n_key_tiles
+    bounds = [t * (N // T) + min(t, N % T) for t in range(T + 1)]
+    say(f"[full] ring share I=1024 N=4096: state, {T - 2} updates, final step")
+    acc, m, l = P.tri_attn_tile_state(q, k, v, bias, mask, key_begin=bounds[0], key_end=bounds[1])
+    for t in range(1, T - 1):
+        P.tri_attn_tile_state_update(q, k, v, bias, mask, key_begin=bounds[t], key_end=bounds[t + 1],
+                                     acc=acc, m=m, l=l)
+    out, lse = P.tri_attn_tile_state_final(q, k, v, bias, mask, key_begin=bounds[T - 1], key_end=bounds[T],
+                                           acc=acc, m=m, l=l, want_lse=True)
+    torch.cuda.synchronize()
+    del acc, m, l
+    rows = edge_rows(cfg, np.random.default_rng(19))
+    idx = torch.from_numpy(rows).cuda()
+    got = out.view(-1, H, D)[idx].cpu().numpy()
+    got_lse = lse.view(-1, H)[idx].cpu().numpy()
+    ref, ref_lse = oracle.tri_attn(w.q, w.k, w.v, w.bias, w.mask, n_key_tiles=T, rows=rows)
+    compare(got, ref, TOL["bf16"], f"ring share out, {len(rows)} rows")
+    compare(got_lse, ref_lse, TOL["bf16"], f"ring share lse, {len(rows)} rows")
+
+
+@pytest.mark.timeout(900)
+def test_backward_ring_share_n4096(torch_dev, share4096):
+    """The backward of the rank's share (I = 1024 rows, N = 4096): dq, dk, dv of four
+    lines (their forward statistics the oracle's, bar the kernels' own 1e-2 x
+    max(1, max|oracle|)) and dbias, summed over the share's 1,024 rows (the share's part of
+    the bias gradient), on six query columns against the oracle's column form, end to end
+    from the GPU forward's out and lse."""
+    import pair_biased_triangle_amd as P
+    torch = torch_dev
+    w, (q, k, v, bias, mask) = share4096
+    cfg = w.cfg
+    lines = np.array([0, 511, 1000, 1023])
+    sel = lambda a: np.ascontiguousarray(a[:, lines])
+    dout = torch.randn(q.shape, dtype=torch.float32, device="cuda", generator=torch.Generator("cuda").manual_seed(13))
+    dout_h = dout.cpu().numpy()
+    say("[full] backward ring share I=1024 N=4096: oracle on 4 lines")
+    wq, wk, wv = sel(w.q), sel(w.k), sel(w.v)
+    ref_out, ref_lse = oracle.tri_attn(wq, wk, wv, w.bias, w.mask)
+    ref = oracle.tri_attn_bwd(wq, wk, wv, w.bias, w.mask, sel(dout_h))
+    out, lse = P.tri_attn_fwd_lse(q, k, v, bias, mask, n_key_tiles=cfg.n_key_tiles)
+    idx = torch.from_numpy(lines).cuda()
+    out_e, lse_e = out.clone(), lse.clone()           # end to end, for dbias
+    out[:, idx] = torch.from_numpy(ref_out.astype(np.float32)).cuda()
+    lse[:, idx] = torch.from_numpy(ref_lse.astype(np.float32)).cuda()
+    dq, dk, dv, _ = P.tri_attn_bwd(q, k, v, bias, mask, out, lse, dout)
+    torch.cuda.synchronize()
+    for name, g, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref[:3]):
+        compare_rel(g[:, idx].cpu().numpy(), r, 1e-2, f"{name} I=1024 N=4096, 4 lines of a full call")
+    del dq, dk, dv, out, lse
+    cols = [0, 67, 68, 2048, 4079, 4095]
+    dbias = P.tri_attn_bwd(q, k, v, bias, mask, out_e, lse_e, dout)[3]
+    torch.cuda.synchronize()
+    got = dbias[:, :, cols].cpu().numpy()
+    del dbias
+    refc = oracle.tri_attn_dbias_cols(w.q, w.k, w.v, w.bias, w.mask, dout_h, cols)
+    compare_rel(got, refc, 1e-2, "dbias I=1024 N=4096, 6 columns summed over 1024 rows")
 
 
 N4200 = (4200, 4, 32, 8)          # N = I, H, D, key tiles
