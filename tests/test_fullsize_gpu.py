@@ -190,6 +190,27 @@ def test_backward_n2700_dbias_columns_over_all_rows(torch_dev, n2700):
     assert np.all(got[..., cfg.N - cfg.mask_last:] == 0), "a masked key got a bias gradient"
 
 
+@pytest.mark.timeout(600)
+def test_ending_n2700_sampled(torch_dev, n2700):
+    """The ending node on the benchmark's workload, as `bench.py --pass ending` runs it:
+    with the lse, on sampled (i, j) against the oracle's ending orientation."""
+    import pair_biased_triangle_amd as P
+    torch = torch_dev
+    w, (q, k, v, bias, mask) = n2700
+    cfg = w.cfg
+    say("[full] ending node N=2700")
+    out, lse = P.tri_attn_fwd_ending(q, k, v, bias, mask, n_key_tiles=cfg.n_key_tiles, want_lse=True)
+    torch.cuda.synchronize()
+    rows = edge_rows(cfg, np.random.default_rng(23))
+    idx = torch.from_numpy(rows).cuda()
+    got = out.view(-1, cfg.H, cfg.D)[idx].cpu().numpy()
+    got_lse = lse.view(-1, cfg.H)[idx].cpu().numpy()
+    ref, ref_lse = oracle.tri_attn(w.q, w.k, w.v, w.bias, w.mask, n_key_tiles=cfg.n_key_tiles, rows=rows,
+                                   ending=True)
+    compare(got, ref, TOL["bf16"], f"ending out, {len(rows)} rows")
+    compare(got_lse, ref_lse, TOL["bf16"], f"ending lse, {len(rows)} rows")
+
+
 @pytest.fixture(scope="module")
 def share4096(torch_dev):
     """ring_share_n4096_i1024 inputs (one rank's 1,024 rows of N = 4,096) on host and device."""
